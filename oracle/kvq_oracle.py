@@ -1,0 +1,416 @@
+"""CPU oracle for the dynamically quantized paged KV cache and the attention
+that reads it.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The HIP library
+(``sub_byte_quantized_amd``) never imports, links or calls anything here, and
+nothing here imports it.
+
+Plain numpy. The quantize-on-write steps are an *encoding*, so they are written
+as the method's steps in order, in float32 (the precision the codes are decided
+in on both sides). Attention has a plain definition (softmax attention over the
+dequantized, un-rotated keys and values), so it is that definition written out
+in float64.
+
+Sources (web pages; cited by title and section):
+
+* [P1] FastDeploy PR 5173, "[Feature] support dynamic int2 quantization cache
+  kv" -- sections "Motivation" and the pull-request overview: a 2-bit KV cache
+  whose scales are computed at run time, written by an encoder/decoder cache
+  write kernel and read by an attention kernel.
+* [P2] prhub summary of vLLM PR 40835, "INT4 per-token-head KV cache
+  quantization for the Triton backend" -- sections 功能与动机 (motivation:
+  two 4-bit values per byte, randomized Hadamard transform, asymmetric
+  quantization with a zero point), 实现拆解 (implementation: the write kernel
+  applies the RHT, computes one scale and zero point per token and head, and
+  packs nibbles; the read kernel unpacks, dequantizes and attends), 关键源码片段
+  (the cache shape snippet).
+* [P3] FastDeploy PR 7718, "Optimize AppendAttention for discrete head-wise
+  block_idx" -- sections Motivation (head-wise block table, logical
+  [batch, kv_head, block], physical [batch*kv_heads, max_blocks]) and
+  Modifications / correctness gates (-1 marks an evicted sliding-window block;
+  such rows are skipped before any K/V pointer is formed).
+* [P4] vllm-ascend-quantized-kv-cache 0.2.0rc2 package description, section
+  运行机制 (decode dequantizes inside attention; prefill gathers and
+  dequantizes the paged cache).
+* [P5] FastDeploy PR 7757, "fix cache_manager_v1 allocating kv cache with wrong
+  dtype" -- section 修复: every quantized cache is stored as uint8.
+
+Readings where the pages are silent (each also listed in the design doc):
+
+* INT4/INT2 codes are unsigned in [0, L], L = 2^b - 1; the zero point is the
+  real-valued row minimum, x_hat = c*s + z.  INT8 is symmetric, s = absmax/127,
+  codes in [-127, 127] stored as two's complement bytes.
+* Rounding is round-half-to-even (np.rint); s and 1/s are correctly rounded
+  float32 divisions; (y - z) and the product by 1/s are separate float32 ops.
+* A row whose scale is zero, subnormal or NaN gets all-zero codes.
+* The rotation is y = (1/sqrt(D)) * H_D * (d (.) x), H_D the Sylvester Hadamard
+  matrix in natural order, d the caller's +-1 signs; K and V are both rotated,
+  and the attention output is rotated back once.
+* Element 2j of a row goes to the low nibble of byte j; for INT2 element 4j+k
+  goes to bits 2k..2k+1 of byte j.
+* A token position p of sequence b attends (decode) to positions j < L_b that
+  lie in a non-evicted block and, for a windowed kv head, j >= L_b - W.
+  kv head = q head // (Hq/Hkv).  An empty allowed set gives output 0.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+INT8_SYM = 0
+INT4_ASYM = 1
+INT2_ASYM = 2
+MODES = (INT8_SYM, INT4_ASYM, INT2_ASYM)
+BITS = {INT8_SYM: 8, INT4_ASYM: 4, INT2_ASYM: 2}
+# number of quantization steps: codes span [0, L] (asymmetric) or [-L, L]
+LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3}
+META_FLOATS = {INT8_SYM: 1, INT4_ASYM: 2, INT2_ASYM: 2}
+
+_F32 = np.float32
+_FLT_MIN = _F32(2.0 ** -126)
+
+
+# --------------------------------------------------------------------------
+# Layout  ([P2] 关键源码片段: the packed row holds head_size*b/8 code bytes;
+#          [P5] 修复: storage dtype is uint8 for every quantized mode)
+# --------------------------------------------------------------------------
+def row_code_bytes(mode: int, head_dim: int) -> int:
+    """Packed code bytes of one (token, kv head) row: head_dim * b / 8."""
+    return head_dim * BITS[mode] // 8
+
+
+def plane_shapes(mode: int, head_dim: int, num_kv_heads: int, block_size: int,
+                 num_blocks: int):
+    """Shapes of one code plane and one meta plane (K and V each have both).
+
+    codes: uint8 [num_blocks, Hkv, block_size, P]
+    meta : float32 [num_blocks, Hkv, block_size, M], M = 1 (s) or 2 (s, z)
+    """
+    P = row_code_bytes(mode, head_dim)
+    M = META_FLOATS[mode]
+    return ((num_blocks, num_kv_heads, block_size, P),
+            (num_blocks, num_kv_heads, block_size, M))
+
+
+# --------------------------------------------------------------------------
+# Hadamard rotation ([P2] 功能与动机 / 实现拆解: RHT before quantization)
+# --------------------------------------------------------------------------
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """H[i, j] = (-1)^popcount(i & j): the Sylvester matrix in natural order."""
+    assert n > 0 and n & (n - 1) == 0
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    bits = i & j
+    pop = np.zeros_like(bits)
+    while np.any(bits):
+        pop += bits & 1
+        bits >>= 1
+    return np.where(pop % 2 == 0, 1, -1).astype(np.int64)
+
+
+def fwht(x: np.ndarray) -> np.ndarray:
+    """Unnormalized fast Walsh-Hadamard transform along the last axis.
+
+    Stages h = 1, 2, 4, ..., D/2; each stage maps the pair (i, i+h), i with bit
+    h clear, to (x_i + x_{i+h}, x_i - x_{i+h}).  Arithmetic stays in x's dtype
+    (float32 for the stored-code path, float64 for checks), so the float32
+    result is fully specified by this stage order.
+    """
+    x = np.array(x, copy=True)
+    D = x.shape[-1]
+    assert D & (D - 1) == 0
+    lead = x.shape[:-1]
+    h = 1
+    while h < D:
+        y = x.reshape(lead + (D // (2 * h), 2, h))
+        a = y[..., 0, :]
+        b = y[..., 1, :]
+        x = np.stack([a + b, a - b], axis=-2).reshape(lead + (D,))
+        h *= 2
+    return x
+
+
+def inv_sqrt_f32(D: int) -> np.float32:
+    """float32 rounding of 1/sqrt(D)."""
+    return _F32(1.0 / math.sqrt(D))
+
+
+def rotate_f32(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """y = fl32( FWHT32(d (.) x) * fl32(1/sqrt(D)) ), rows along the last axis.
+
+    The sign flip is exact; the FWHT is the float32 stage sequence of fwht();
+    the normalization is one float32 multiply per element.
+    """
+    x = np.asarray(x, dtype=_F32)
+    d = np.asarray(signs, dtype=_F32)
+    y = fwht(x * d)
+    return (y * inv_sqrt_f32(x.shape[-1])).astype(_F32)
+
+
+def rotate_dense_f64(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """Check path: (1/sqrt(D)) * H @ (d (.) x) with a dense float64 H."""
+    D = x.shape[-1]
+    H = sylvester_hadamard(D).astype(np.float64)
+    xd = np.asarray(x, np.float64) * np.asarray(signs, np.float64)
+    return (xd @ H.T) / math.sqrt(D)
+
+
+def unrotate_f64(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """R^T x with R = (1/sqrt(D)) H diag(d):  (1/sqrt(D)) * d (.) (H x), float64."""
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    return fwht(x) * np.asarray(signs, np.float64) / math.sqrt(D)
+
+
+# --------------------------------------------------------------------------
+# Per-token-head quantization ([P2] 功能与动机 / 实现拆解: one scale and zero
+# point per (token, head); [P1] Motivation: 2-bit codes, scales at run time)
+# --------------------------------------------------------------------------
+def quantize_rows(y: np.ndarray, mode: int):
+    """Quantize float32 rows y [R, D] -> (codes int32 [R, D], s f32 [R], z f32 [R]).
+
+    INT8 (symmetric): a = max|y|, s = a / 127, z = 0,
+      c = clamp(rint(y * inv), -127, 127) with inv = 1/s.
+    INT4 / INT2 (asymmetric): mn = min y, mx = max y, s = (mx - mn) / L,
+      z = mn, c = clamp(rint((y - mn) * inv), 0, L).
+    Rows with s == 0, subnormal s or NaN s get all-zero codes.
+    """
+    y = np.asarray(y, dtype=_F32)
+    L = _F32(LEVELS[mode])
+    if mode == INT8_SYM:
+        a = np.max(np.abs(y), axis=-1)
+        s = (a / L).astype(_F32)
+        z = np.zeros_like(s)
+        base = y
+        lo, hi = -LEVELS[mode], LEVELS[mode]
+    else:
+        mn = np.min(y, axis=-1)
+        mx = np.max(y, axis=-1)
+        s = ((mx - mn) / L).astype(_F32)
+        z = mn.astype(_F32)
+        base = (y - mn[..., None]).astype(_F32)
+        lo, hi = 0, LEVELS[mode]
+    ok = s >= _FLT_MIN  # False for 0, subnormal and NaN
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        inv = np.where(ok, _F32(1.0) / np.where(ok, s, _F32(1.0)), _F32(0.0)).astype(_F32)
+        t = (base * inv[..., None]).astype(_F32)
+    c = np.clip(np.rint(t), lo, hi)
+    c = np.where(ok[..., None], c, 0).astype(np.int32)
+    return c, s, z
+
+
+def dequant_rows_f64(codes: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """x_hat = c * s + z in float64 (z = 0 for INT8)."""
+    return (np.asarray(codes, np.float64) * np.asarray(s, np.float64)[..., None]
+            + np.asarray(z, np.float64)[..., None])
+
+
+# --------------------------------------------------------------------------
+# Packing ([P2] 实现拆解: pack/unpack of 4-bit values, two per byte;
+#          [P1]: 2-bit codes, four per byte)
+# --------------------------------------------------------------------------
+def pack_codes(codes: np.ndarray, mode: int) -> np.ndarray:
+    """codes [..., D] -> uint8 [..., D*b/8]."""
+    c = np.asarray(codes, np.int64)
+    if mode == INT8_SYM:
+        return (c & 0xFF).astype(np.uint8)
+    b = BITS[mode]
+    per = 8 // b
+    D = c.shape[-1]
+    g = (c & ((1 << b) - 1)).reshape(c.shape[:-1] + (D // per, per))
+    out = np.zeros(g.shape[:-1], dtype=np.int64)
+    for k in range(per):
+        out |= g[..., k] << (b * k)
+    return out.astype(np.uint8)
+
+
+def unpack_codes(packed: np.ndarray, mode: int, head_dim: int) -> np.ndarray:
+    """uint8 [..., D*b/8] -> int32 codes [..., D] (INT8 sign-extended)."""
+    p = np.asarray(packed, np.uint8).astype(np.int64)
+    if mode == INT8_SYM:
+        return np.where(p >= 128, p - 256, p).astype(np.int32)
+    b = BITS[mode]
+    per = 8 // b
+    parts = [(p >> (b * k)) & ((1 << b) - 1) for k in range(per)]
+    out = np.stack(parts, axis=-1).reshape(p.shape[:-1] + (p.shape[-1] * per,))
+    assert out.shape[-1] == head_dim
+    return out.astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Quantize-on-write into the paged layout  ([P2] 实现拆解 item 2: RHT, then
+# scale and zero per token and head, then pack and store; [P3] Motivation:
+# per-head block rows)
+# --------------------------------------------------------------------------
+def encode_rows(x_bf16_as_f32: np.ndarray, mode: int, signs=None):
+    """Steps O1-O5 on rows [R, D]: rotation (optional), stats, codes, packing.
+
+    Returns (packed uint8 [R, P], s f32 [R], z f32 [R], codes int32 [R, D]).
+    """
+    x = np.asarray(x_bf16_as_f32, dtype=_F32)
+    y = rotate_f32(x, signs) if signs is not None else x
+    codes, s, z = quantize_rows(y, mode)
+    return pack_codes(codes, mode), s, z, codes
+
+
+def write_cache(k: np.ndarray, v: np.ndarray, mode: int, block_size: int,
+                k_codes: np.ndarray, k_meta: np.ndarray,
+                v_codes: np.ndarray, v_meta: np.ndarray,
+                slot_mapping=None, slot_mapping_headwise=None, signs=None):
+    """Quantize the rows of k, v [T, Hkv, D] (float32 images of bf16) and store
+    them at their slots (step O6).
+
+    slot_mapping [T] (the same slot for every kv head) or slot_mapping_headwise
+    [T, Hkv]; slot = block * block_size + offset; a negative slot skips the row.
+    Planes are modified in place.
+    """
+    T, Hkv, D = k.shape
+    if (slot_mapping is None) == (slot_mapping_headwise is None):
+        raise ValueError("exactly one slot mapping")
+    if slot_mapping_headwise is None:
+        slots = np.repeat(np.asarray(slot_mapping, np.int64)[:, None], Hkv, axis=1)
+    else:
+        slots = np.asarray(slot_mapping_headwise, np.int64).reshape(T, Hkv)
+    for src, codes_pl, meta_pl in ((k, k_codes, k_meta), (v, v_codes, v_meta)):
+        packed, s, z, _ = encode_rows(np.asarray(src, _F32).reshape(T * Hkv, D), mode, signs)
+        packed = packed.reshape(T, Hkv, -1)
+        s = s.reshape(T, Hkv)
+        z = z.reshape(T, Hkv)
+        tt, hh = np.nonzero(slots >= 0)
+        sl = slots[tt, hh]
+        blk, off = sl // block_size, sl % block_size
+        codes_pl[blk, hh, off, :] = packed[tt, hh]
+        meta_pl[blk, hh, off, 0] = s[tt, hh]
+        if mode != INT8_SYM:
+            meta_pl[blk, hh, off, 1] = z[tt, hh]
+
+
+# --------------------------------------------------------------------------
+# Reading the cache back ([P4] 运行机制: gather and dequantize the paged cache;
+# [P3] correctness gates: -1 rows are skipped, never dereferenced)
+# --------------------------------------------------------------------------
+def table_row(b: int, h: int, num_kv_heads: int, block_tables=None,
+              block_tables_headwise=None) -> np.ndarray:
+    """Block-id row walked by (sequence b, kv head h): the uniform row b, or the
+    head-wise row b*Hkv + h."""
+    if block_tables_headwise is not None:
+        return np.asarray(block_tables_headwise)[b * num_kv_heads + h]
+    return np.asarray(block_tables)[b]
+
+
+def gather_head(b: int, h: int, n_pos: int, mode: int, head_dim: int,
+                block_size: int, num_kv_heads: int,
+                k_codes, k_meta, v_codes, v_meta, signs=None,
+                block_tables=None, block_tables_headwise=None):
+    """Dequantized, un-rotated K and V (float64 [n_pos, D]) of positions
+    0..n_pos-1 of (b, h), plus a bool [n_pos] that is False for positions in an
+    evicted (-1) block.  Evicted rows are returned as zeros and never read."""
+    row = table_row(b, h, num_kv_heads, block_tables, block_tables_headwise)
+    pos = np.arange(n_pos)
+    ids = np.asarray(row, np.int64)[pos // block_size] if n_pos else np.zeros(0, np.int64)
+    present = ids >= 0
+    K = np.zeros((n_pos, head_dim))
+    V = np.zeros((n_pos, head_dim))
+    if np.any(present):
+        bi = ids[present]
+        off = pos[present] % block_size
+        for pl_c, pl_m, out in ((k_codes, k_meta, K), (v_codes, v_meta, V)):
+            codes = unpack_codes(pl_c[bi, h, off, :], mode, head_dim)
+            s = pl_m[bi, h, off, 0]
+            z = pl_m[bi, h, off, 1] if mode != INT8_SYM else np.zeros_like(s)
+            xhat = dequant_rows_f64(codes, s, z)
+            out[present] = unrotate_f64(xhat, signs) if signs is not None else xhat
+    return K, V, present
+
+
+def _attend(qs: np.ndarray, K: np.ndarray, V: np.ndarray, allowed: np.ndarray,
+            scale: float) -> np.ndarray:
+    """Plain softmax attention in float64.  qs [n, D]; allowed [n, Lk] bool.
+    Rows with no allowed key give 0."""
+    out = np.zeros((qs.shape[0], V.shape[1]))
+    if K.shape[0] == 0:
+        return out
+    logits = scale * (np.asarray(qs, np.float64) @ K.T)
+    logits = np.where(allowed, logits, -np.inf)
+    m = np.max(logits, axis=1, keepdims=True)
+    has = np.isfinite(m[:, 0])
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.where(allowed, np.exp(logits - m), 0.0)
+    l = p.sum(axis=1, keepdims=True)
+    out[has] = (p[has] @ V) / l[has]
+    return out
+
+
+def decode_attention(q, seq_lens, mode: int, head_dim: int, block_size: int,
+                     num_kv_heads: int, k_codes, k_meta, v_codes, v_meta,
+                     softmax_scale: float, signs=None, block_tables=None,
+                     block_tables_headwise=None, window=None, pairs=None):
+    """Step O9: one query token per sequence, q [B, Hq, D] (float images of
+    bf16).  Returns float64 [B, Hq, D].
+
+    If ``pairs`` is given (list of (b, kv_head)), only those are computed and
+    the rest of the output stays NaN.
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, D = q.shape
+    G = Hq // num_kv_heads
+    out = np.full((B, Hq, D), np.nan)
+    todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(num_kv_heads)]
+    for b, h in todo:
+        L = int(seq_lens[b])
+        K, V, present = gather_head(b, h, L, mode, head_dim, block_size, num_kv_heads,
+                                    k_codes, k_meta, v_codes, v_meta, signs,
+                                    block_tables, block_tables_headwise)
+        allowed = present.copy()
+        W = int(window[h]) if window is not None else 0
+        if W > 0:
+            allowed &= np.arange(L) >= L - W
+        qs = q[b, h * G:(h + 1) * G]
+        out[b, h * G:(h + 1) * G] = _attend(qs, K, V, np.broadcast_to(allowed, (G, L)),
+                                             softmax_scale)
+    return out
+
+
+def prefill_attention(q, cu_seqlens_q, seq_lens, mode: int, head_dim: int,
+                      block_size: int, num_kv_heads: int, k_codes, k_meta, v_codes,
+                      v_meta, softmax_scale: float, signs=None, block_tables=None,
+                      block_tables_headwise=None, window=None, pairs=None,
+                      rows=None):
+    """Step O10: chunked prefill.  q [Tq, Hq, D]; sequence b owns query rows
+    cu[b]..cu[b+1]-1, which sit at positions L_b - n_b + i (n_b = new tokens).
+    Query at position p attends to keys j <= p that are present and, for a
+    windowed kv head, j >= p - W + 1.  Returns float64 [Tq, Hq, D].
+
+    ``pairs`` restricts the (b, kv_head) pairs computed; ``rows`` (an int array
+    of query indices within each sequence) restricts the query rows.
+    """
+    q = np.asarray(q, np.float64)
+    Tq, Hq, D = q.shape
+    G = Hq // num_kv_heads
+    out = np.full((Tq, Hq, D), np.nan)
+    B = len(seq_lens)
+    todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(num_kv_heads)]
+    for b, h in todo:
+        L = int(seq_lens[b])
+        q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        n = q1 - q0
+        if n == 0:
+            continue
+        K, V, present = gather_head(b, h, L, mode, head_dim, block_size, num_kv_heads,
+                                    k_codes, k_meta, v_codes, v_meta, signs,
+                                    block_tables, block_tables_headwise)
+        idx = np.arange(n) if rows is None else np.asarray([r for r in rows if r < n], np.int64)
+        if idx.size == 0:
+            continue
+        pos = (L - n + idx)[:, None]
+        j = np.arange(L)[None, :]
+        allowed = (j <= pos) & present[None, :]
+        W = int(window[h]) if window is not None else 0
+        if W > 0:
+            allowed &= j >= pos - W + 1
+        for g in range(G):
+            hq = h * G + g
+            out[q0 + idx, hq] = _attend(q[q0 + idx, hq], K, V, allowed, softmax_scale)
+    return out

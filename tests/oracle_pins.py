@@ -1,0 +1,434 @@
+"""Pins for the CPU oracle: each ``check_*(o)`` takes an oracle module and
+raises AssertionError when the oracle disagrees with something fixed outside
+it (a closed form, a library routine, an invariant, brute force, or a fact the
+pages state).  ``test_oracle_pins.py`` runs them on the oracle; the mutation
+tests run them on copies of the oracle with a planted mistake and require that
+at least one pin fails.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.linalg
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+F32 = np.float32
+MODES = (0, 1, 2)
+
+
+def _bf16_rows(shape, seed, scale=1.0, offset=0.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g) * scale + offset
+    return x.to(torch.bfloat16).float().numpy()
+
+
+# ---------------------------------------------------------------- packing ---
+def check_pack_exhaustive(o):
+    """Every byte value survives unpack -> pack, for each mode (INT4: two
+    codes per byte, INT2: four, INT8: one signed code)."""
+    allb = np.arange(256, dtype=np.uint8)
+    for mode, D in ((1, 2), (2, 4), (0, 1)):
+        rows = allb.reshape(256, 1)
+        codes = o.unpack_codes(rows, mode, D)
+        assert codes.shape == (256, D)
+        back = o.pack_codes(codes, mode)
+        assert np.array_equal(back, rows), f"mode {mode} byte round trip"
+    # INT8: two's complement value of every byte
+    c = o.unpack_codes(allb.reshape(256, 1), 0, 1)[:, 0]
+    assert np.array_equal(c, np.where(allb >= 128, allb.astype(int) - 256, allb))
+
+
+def check_pack_positions(o):
+    """Element 2j -> low nibble of byte j; element 4j+k -> bits 2k..2k+1."""
+    for j in range(8):
+        c = np.zeros(8, int); c[j] = 15
+        p = o.pack_codes(c[None], 1)[0]
+        exp = np.zeros(4, int); exp[j // 2] = 0x0F if j % 2 == 0 else 0xF0
+        assert np.array_equal(p, exp), f"INT4 element {j}"
+        c = np.zeros(16, int); c[j] = 3
+        p = o.pack_codes(c[None], 2)[0]
+        exp = np.zeros(4, int); exp[j // 4] = 3 << (2 * (j % 4))
+        assert np.array_equal(p, exp), f"INT2 element {j}"
+
+
+def check_pack_random_roundtrip(o):
+    r = np.random.default_rng(7)
+    for mode, lo, hi in ((0, -127, 127), (1, 0, 15), (2, 0, 3)):
+        c = r.integers(lo, hi + 1, size=(50, 128))
+        assert np.array_equal(o.unpack_codes(o.pack_codes(c, mode), mode, 128), c)
+
+
+# --------------------------------------------------------------- hadamard ---
+def check_hadamard_matrix(o):
+    for n in (2, 8, 64, 128):
+        H = o.sylvester_hadamard(n)
+        assert np.array_equal(H @ H.T, n * np.eye(n, dtype=np.int64)), f"H H^T = nI, n={n}"
+        assert np.array_equal(H, scipy.linalg.hadamard(n)), f"Sylvester order, n={n}"
+
+
+def check_fwht_is_hadamard(o):
+    """FWHT of each basis vector is the matching column of scipy's H."""
+    for n in (4, 64, 128):
+        E = np.eye(n)
+        assert np.array_equal(o.fwht(E), scipy.linalg.hadamard(n).T.astype(float))
+
+
+def check_fwht_involution(o):
+    r = np.random.default_rng(3)
+    x = r.standard_normal((20, 128))
+    assert np.allclose(o.fwht(o.fwht(x)), 128 * x, rtol=0, atol=1e-10)
+
+
+def check_rotation_orthogonal(o):
+    r = np.random.default_rng(4)
+    for n in (64, 128):
+        d = np.where(r.integers(0, 2, n) == 1, 1.0, -1.0)
+        R = scipy.linalg.hadamard(n) * d[None, :] / math.sqrt(n)   # H diag(d) / sqrt(n)
+        assert np.allclose(R.T @ R, np.eye(n), atol=1e-12)
+        x = r.standard_normal((5, n))
+        # rotate (dense check path) and unrotate agree with R and R^T
+        assert np.allclose(o.rotate_dense_f64(x, d), x @ R.T, atol=1e-12)
+        assert np.allclose(o.unrotate_f64(x @ R.T, d), x, atol=1e-12)
+
+
+def check_rotate_f32_accuracy(o):
+    """The float32 FWHT path is within its rounding bound of the exact
+    rotation: log2(D) * sqrt(D) * 2^-24 * max|x| + 2^-24 |y|."""
+    r = np.random.default_rng(5)
+    u = 2.0 ** -24
+    for n in (64, 128):
+        d = np.where(r.integers(0, 2, n) == 1, 1.0, -1.0).astype(F32)
+        x = _bf16_rows((64, n), 11 + n, scale=3.0)
+        y32 = o.rotate_f32(x, d).astype(np.float64)
+        R = scipy.linalg.hadamard(n) * d.astype(float)[None, :] / math.sqrt(n)
+        y = x.astype(np.float64) @ R.T
+        bound = math.log2(n) * math.sqrt(n) * u * np.abs(x).max(axis=1, keepdims=True) + u * np.abs(y)
+        assert np.all(np.abs(y32 - y) <= 1.01 * bound)
+        assert y32.dtype == np.float64 and o.rotate_f32(x, d).dtype == F32
+
+
+# ---------------------------------------------------------- quantization ---
+def check_quant_ranges_and_error(o):
+    """Codes lie in [0, L] / [-127, 127]; reconstruction error <= s/2 (plus
+    the float32 slack of 1/s and the product)."""
+    for mode in MODES:
+        for seed, (sc, off) in enumerate(((1.0, 0.0), (10.0, 3.0), (1e-3, -5.0))):
+            y = _bf16_rows((200, 128), 100 + seed, scale=sc, offset=off)
+            c, s, z = o.quantize_rows(y, mode)
+            L = o.LEVELS[mode]
+            lo = -L if mode == 0 else 0
+            assert c.min() >= lo and c.max() <= L
+            if mode == 0:
+                assert np.all(z == 0)
+                assert np.array_equal(s, (np.abs(y).max(axis=1) / F32(127)).astype(F32))
+            else:
+                assert np.array_equal(z, y.min(axis=1))
+                assert np.array_equal(s, ((y.max(axis=1) - y.min(axis=1)) / F32(L)).astype(F32))
+            xh = o.dequant_rows_f64(c, s, z)
+            err = np.abs(xh - y.astype(np.float64))
+            assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 1e-5)), mode
+
+
+def check_quant_nearest(o):
+    """Each code is the nearest grid point to the exact value (y-z)/s, up to
+    float32 ties: |t - c| <= 0.5 + 1e-5."""
+    for mode in MODES:
+        y = _bf16_rows((300, 64), 200 + mode, scale=2.0)
+        c, s, z = o.quantize_rows(y, mode)
+        t = (y.astype(np.float64) - z[:, None]) / s[:, None].astype(np.float64)
+        L = o.LEVELS[mode]
+        lo = -L if mode == 0 else 0
+        assert np.all(np.abs(np.clip(t, lo, L) - c) <= 0.5 + 1e-5)
+
+
+def check_quant_grid_rows(o):
+    """Rows on an exact power-of-two grid reconstruct exactly: s = 2^-e,
+    codes = the grid indices, x_hat = y."""
+    r = np.random.default_rng(9)
+    for mode in MODES:
+        L = o.LEVELS[mode]
+        for e in (-3, 0, 4):
+            if mode == 0:
+                k = r.integers(-L, L + 1, size=(40, 128))
+                k[:, 0] = L * np.where(r.integers(0, 2, 40) == 1, 1, -1)
+                y = (k * 2.0 ** -e).astype(F32)
+            else:
+                k = r.integers(0, L + 1, size=(40, 128))
+                k[:, 0], k[:, 1] = 0, L
+                m = r.integers(-1000, 1001, size=(40, 1))     # grid offset, a multiple of 2^-e
+                y = ((m + k) * 2.0 ** -e).astype(F32)
+            c, s, z = o.quantize_rows(y, mode)
+            assert np.all(s == F32(2.0 ** -e)), (mode, e)
+            assert np.array_equal(c, k), (mode, e)
+            assert np.array_equal(o.dequant_rows_f64(c, s, z), y.astype(np.float64))
+
+
+def check_quant_degenerate(o):
+    for mode in MODES:
+        y = np.full((3, 64), F32(0.75), F32)
+        y[1] = 0.0
+        y[2] = F32(-2.5)
+        c, s, z = o.quantize_rows(y, mode)
+        if mode == 0:
+            # only the zero row is degenerate for absmax; a constant row maps to +-127
+            assert s[1] == 0 and np.all(c[1] == 0)
+            assert np.all(c[0] == 127) and np.all(c[2] == -127)
+        else:
+            assert np.all(c == 0)
+            assert np.all(s == 0) and np.array_equal(z, y[:, 0])
+            assert np.array_equal(o.dequant_rows_f64(c, s, z), y.astype(np.float64))
+        tiny = np.zeros((1, 64), F32); tiny[0, 0] = F32(2.0 ** -140)
+        c, s, z = o.quantize_rows(tiny, mode)
+        assert np.all(c == 0)
+
+
+# ------------------------------------------------------------------ layout ---
+def check_layout_facts(o):
+    with open(os.path.join(HERE, "golden", "layout_facts.json")) as f:
+        g = json.load(f)
+    assert o.row_code_bytes(1, g["int4_data_head_size"]["head_size"]) == g["int4_data_head_size"]["data_head_size"]
+    assert o.row_code_bytes(0, g["int8_data_head_size"]["head_size"]) == g["int8_data_head_size"]["data_head_size"]
+    assert o.META_FLOATS[0] * 4 == g["scale_bytes_per_token_head"]["value"]
+    assert o.row_code_bytes(1, 128) / o.row_code_bytes(0, 128) == g["int4_over_int8_code_bytes"]["value"]
+    assert 128 // o.row_code_bytes(2, 128) == g["int2_codes_per_byte"]["value"]
+
+
+def _tiny_cache(o, mode, D=64, bs=16, Hkv=2, lens=(37, 100), seed=0, rotate=True):
+    r = np.random.default_rng(seed)
+    nblk = [(L + bs - 1) // bs for L in lens]
+    nb = sum(nblk) + 3
+    perm = r.permutation(nb)
+    bt = np.full((len(lens), max(nblk)), -1, np.int64)
+    k0 = 0
+    for b, n in enumerate(nblk):
+        bt[b, :n] = perm[k0:k0 + n]
+        k0 += n
+    T = sum(lens)
+    tok_seq = np.repeat(np.arange(len(lens)), lens)
+    tok_pos = np.concatenate([np.arange(L) for L in lens])
+    slots = bt[tok_seq, tok_pos // bs] * bs + tok_pos % bs
+    k = _bf16_rows((T, Hkv, D), 1000 + seed)
+    v = _bf16_rows((T, Hkv, D), 2000 + seed, offset=0.5)
+    signs = np.where(r.integers(0, 2, D) == 1, 1.0, -1.0).astype(F32) if rotate else None
+    cs, ms = o.plane_shapes(mode, D, Hkv, bs, nb)
+    planes = [np.full(cs, 0xFF, np.uint8), np.full(ms, np.nan, F32),
+              np.full(cs, 0xFF, np.uint8), np.full(ms, np.nan, F32)]
+    o.write_cache(k, v, mode, bs, *planes, slot_mapping=slots, signs=signs)
+    return dict(k=k, v=v, bt=bt, slots=slots, planes=planes, signs=signs, lens=np.array(lens),
+                D=D, bs=bs, Hkv=Hkv, nb=nb, used=perm[:k0], tok_seq=tok_seq, tok_pos=tok_pos)
+
+
+def check_paged_roundtrip(o):
+    """Writing through a shuffled block table and reading back through it
+    gives the rows encoded densely; unused blocks keep their poison."""
+    for mode in MODES:
+        t = _tiny_cache(o, mode)
+        kc, km, vc, vm = t["planes"]
+        for src, pc, pm in ((t["k"], kc, km), (t["v"], vc, vm)):
+            T, Hkv, D = src.shape
+            packed, s, z, _ = o.encode_rows(src.reshape(T * Hkv, D), mode, t["signs"])
+            blk, off = t["slots"] // t["bs"], t["slots"] % t["bs"]
+            for h in range(Hkv):
+                assert np.array_equal(pc[blk, h, off], packed.reshape(T, Hkv, -1)[:, h])
+                assert np.array_equal(pm[blk, h, off, 0], s.reshape(T, Hkv)[:, h])
+                if mode != 0:
+                    assert np.array_equal(pm[blk, h, off, 1], z.reshape(T, Hkv)[:, h])
+        unused = np.setdiff1d(np.arange(t["nb"]), t["used"])
+        assert np.all(kc[unused] == 0xFF) and np.all(np.isnan(km[unused]))
+
+
+def check_gather_matches_dense(o):
+    """gather_head through the table equals dequantize(unrotate(encode(row)))
+    computed row by row with the dense float64 R^T."""
+    t = _tiny_cache(o, 1)
+    kc, km, vc, vm = t["planes"]
+    D, bs, Hkv = t["D"], t["bs"], t["Hkv"]
+    R = scipy.linalg.hadamard(D) * t["signs"].astype(float)[None, :] / math.sqrt(D)
+    for b, L in enumerate(t["lens"]):
+        for h in range(Hkv):
+            K, V, pres = o.gather_head(b, h, int(L), 1, D, bs, Hkv, kc, km, vc, vm,
+                                       t["signs"], block_tables=t["bt"])
+            assert pres.all()
+            rows = np.nonzero(t["tok_seq"] == b)[0]
+            for src, got in ((t["k"], K), (t["v"], V)):
+                packed, s, z, codes = o.encode_rows(src[rows, h], 1, t["signs"])
+                xh = codes * s[:, None].astype(float) + z[:, None].astype(float)
+                assert np.allclose(got, xh @ R, atol=1e-12)
+
+
+# --------------------------------------------------------------- attention ---
+def _sdpa64(q, K, V, mask, scale):
+    qt = torch.as_tensor(q, dtype=torch.float64)[None, None]
+    kt = torch.as_tensor(K, dtype=torch.float64)[None, None]
+    vt = torch.as_tensor(V, dtype=torch.float64)[None, None]
+    m = torch.as_tensor(mask)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)[0, 0].numpy()
+
+
+def check_decode_vs_sdpa(o):
+    """Decode equals torch's float64 scaled_dot_product_attention over the
+    gathered K/V, with the window mask, for every mode."""
+    for mode in MODES:
+        t = _tiny_cache(o, mode, seed=mode)
+        kc, km, vc, vm = t["planes"]
+        D, bs, Hkv = t["D"], t["bs"], t["Hkv"]
+        Hq = 4
+        q = _bf16_rows((2, Hq, D), 77 + mode)
+        win = np.array([0, 20], np.int32)
+        out = o.decode_attention(q, t["lens"], mode, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                                 signs=t["signs"], block_tables=t["bt"], window=win)
+        for b, L in enumerate(t["lens"]):
+            for hq in range(Hq):
+                h = hq // (Hq // Hkv)
+                K, V, _ = o.gather_head(b, h, int(L), mode, D, bs, Hkv, kc, km, vc, vm,
+                                        t["signs"], block_tables=t["bt"])
+                mask = np.ones((1, L), bool)
+                if win[h] > 0:
+                    mask[0, :L - win[h]] = False
+                ref = _sdpa64(q[b, hq][None], K, V, mask, 0.125)[0]
+                assert np.allclose(out[b, hq], ref, atol=1e-12, rtol=1e-12), (mode, b, hq)
+
+
+def check_decode_closed_forms(o):
+    """All keys equal -> output = mean of the values; L = 1 -> output = v_0;
+    q = 0 -> mean of the values; identical q within a GQA group -> identical
+    outputs; different q heads of one group see the same keys."""
+    D, bs, Hkv, Hq = 64, 16, 2, 4
+    nb = 6
+    cs, ms = o.plane_shapes(1, D, Hkv, bs, nb)
+    kc = np.zeros(cs, np.uint8); vc = np.zeros(cs, np.uint8)
+    km = np.zeros(ms, F32); vm = np.zeros(ms, F32)
+    r = np.random.default_rng(1)
+    L = 40
+    T = L
+    k = np.tile(_bf16_rows((1, Hkv, D), 5), (T, 1, 1))         # all keys equal
+    v = _bf16_rows((T, Hkv, D), 6)
+    bt = np.array([[4, 0, 2], [5, 1, 3]], np.int64)
+    slots = bt[0, np.arange(T) // bs] * bs + np.arange(T) % bs
+    o.write_cache(k, v, 1, bs, kc, km, vc, vm, slot_mapping=slots, signs=None)
+    q = _bf16_rows((1, Hq, D), 8)
+    q[0, 1] = q[0, 0]
+    out = o.decode_attention(q, np.array([L]), 1, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                             block_tables=bt[:1])
+    for hq in range(Hq):
+        h = hq // 2
+        _, V, _ = o.gather_head(0, h, L, 1, D, bs, Hkv, kc, km, vc, vm, None, block_tables=bt[:1])
+        assert np.allclose(out[0, hq], V.mean(axis=0), atol=1e-12)
+    assert np.array_equal(out[0, 0], out[0, 1])
+    # q = 0 with distinct keys -> mean
+    k2 = _bf16_rows((T, Hkv, D), 9)
+    o.write_cache(k2, v, 1, bs, kc, km, vc, vm, slot_mapping=slots)
+    out0 = o.decode_attention(np.zeros((1, Hq, D)), np.array([L]), 1, D, bs, Hkv, kc, km, vc, vm,
+                              0.125, block_tables=bt[:1])
+    _, V0, _ = o.gather_head(0, 0, L, 1, D, bs, Hkv, kc, km, vc, vm, None, block_tables=bt[:1])
+    assert np.allclose(out0[0, 0], V0.mean(axis=0), atol=1e-12)
+    # L = 1 -> v_0 exactly (dequantized)
+    out1 = o.decode_attention(q, np.array([1]), 1, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                              block_tables=bt[:1])
+    v_first = o.gather_head(0, 1, 1, 1, D, bs, Hkv, kc, km, vc, vm, None, block_tables=bt[:1])[1][0]
+    assert np.allclose(out1[0, 3], v_first, atol=1e-14)
+    # empty allowed set -> 0
+    outE = o.decode_attention(q, np.array([0]), 1, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                              block_tables=bt[:1])
+    assert np.all(outE == 0)
+
+
+def check_rotation_identity(o):
+    """Attending in rotated space with a pre-rotated query and rotating the
+    output back equals the oracle's un-rotate-then-attend path."""
+    t = _tiny_cache(o, 1, seed=3)
+    kc, km, vc, vm = t["planes"]
+    D, bs, Hkv = t["D"], t["bs"], t["Hkv"]
+    d = t["signs"].astype(float)
+    R = scipy.linalg.hadamard(D) * d[None, :] / math.sqrt(D)
+    q = _bf16_rows((2, 4, D), 31)
+    out = o.decode_attention(q, t["lens"], 1, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                             signs=t["signs"], block_tables=t["bt"])
+    for b, L in enumerate(t["lens"]):
+        for hq in range(4):
+            h = hq // 2
+            Kr, Vr, _ = o.gather_head(b, h, int(L), 1, D, bs, Hkv, kc, km, vc, vm, None,
+                                      block_tables=t["bt"])   # rotated-space x_hat
+            qr = R @ q[b, hq].astype(float)
+            lg = 0.125 * (Kr @ qr)
+            p = np.exp(lg - lg.max()); p /= p.sum()
+            o_rot = p @ Vr
+            assert np.allclose(R.T @ o_rot, out[b, hq], atol=1e-12)
+
+
+def check_headwise_equivalence(o):
+    """A head-wise table whose rows all equal the uniform row gives the same
+    output; -1 only on blocks wholly outside the window equals the window mask
+    alone."""
+    t = _tiny_cache(o, 2, seed=5)
+    kc, km, vc, vm = t["planes"]
+    D, bs, Hkv = t["D"], t["bs"], t["Hkv"]
+    q = _bf16_rows((2, 4, D), 41)
+    win = np.array([24, 0], np.int32)
+    base = o.decode_attention(q, t["lens"], 2, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                              signs=t["signs"], block_tables=t["bt"], window=win)
+    hw = np.repeat(t["bt"], Hkv, axis=0)
+    same = o.decode_attention(q, t["lens"], 2, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                              signs=t["signs"], block_tables_headwise=hw, window=win)
+    assert np.array_equal(base, same)
+    hw2 = hw.copy()
+    for b, L in enumerate(t["lens"]):
+        start = L - win[0]
+        for j in range(hw2.shape[1]):
+            if (j + 1) * bs <= start:
+                hw2[b * Hkv + 0, j] = -1
+    ev = o.decode_attention(q, t["lens"], 2, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                            signs=t["signs"], block_tables_headwise=hw2, window=win)
+    assert np.allclose(ev, base, atol=1e-13)
+    # evicting a block inside the window removes exactly its tokens
+    hw3 = hw.copy()
+    hw3[1 * Hkv + 1, 2] = -1      # seq 1, kv head 1 (full), block 2
+    ev3 = o.decode_attention(q, t["lens"], 2, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                             signs=t["signs"], block_tables_headwise=hw3, window=win)
+    L1 = int(t["lens"][1])
+    K, V, _ = o.gather_head(1, 1, L1, 2, D, bs, Hkv, kc, km, vc, vm, t["signs"], block_tables=t["bt"])
+    mask = np.ones((1, L1), bool)
+    mask[0, 2 * bs:3 * bs] = False
+    for hq in (2, 3):
+        ref = _sdpa64(q[1, hq][None], K, V, mask, 0.125)[0]
+        assert np.allclose(ev3[1, hq], ref, atol=1e-12)
+
+
+def check_prefill_vs_bruteforce(o):
+    """Chunked prefill equals a per-query loop of SDPA with the causal and
+    window masks; its last row equals decode with the same query."""
+    t = _tiny_cache(o, 1, seed=6)
+    kc, km, vc, vm = t["planes"]
+    D, bs, Hkv = t["D"], t["bs"], t["Hkv"]
+    lens = t["lens"]
+    n_new = np.array([5, 17])
+    cu = np.concatenate([[0], np.cumsum(n_new)])
+    q = _bf16_rows((int(cu[-1]), 4, D), 51)
+    win = np.array([0, 30], np.int32)
+    out = o.prefill_attention(q, cu, lens, 1, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                              signs=t["signs"], block_tables=t["bt"], window=win)
+    for b, L in enumerate(lens):
+        for h in range(Hkv):
+            K, V, _ = o.gather_head(b, h, int(L), 1, D, bs, Hkv, kc, km, vc, vm, t["signs"],
+                                    block_tables=t["bt"])
+            for i in range(n_new[b]):
+                p = L - n_new[b] + i
+                mask = np.zeros((1, L), bool)
+                mask[0, :p + 1] = True
+                if win[h] > 0:
+                    mask[0, :max(0, p - win[h] + 1)] = False
+                for g in range(2):
+                    hq = 2 * h + g
+                    ref = _sdpa64(q[cu[b] + i, hq][None], K, V, mask, 0.125)[0]
+                    assert np.allclose(out[cu[b] + i, hq], ref, atol=1e-12)
+    last = q[cu[1:] - 1]
+    dec = o.decode_attention(last, lens, 1, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                             signs=t["signs"], block_tables=t["bt"], window=win)
+    assert np.allclose(dec, out[cu[1:] - 1], atol=1e-13)
+
+
+ALL = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

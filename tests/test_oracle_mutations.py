@@ -1,0 +1,55 @@
+"""Plant a plausible mistake in a copy of the oracle (CPU only) and require
+that at least one pin fails: the pins are strong enough to catch a dropped
+term, a wrong sign or index, or a transposed operand."""
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "kvq_oracle.py")
+
+MUTATIONS = {
+    "fwht_sign": ("np.stack([a + b, a - b], axis=-2)", "np.stack([a + b, b - a], axis=-2)"),
+    "fwht_pairing": ("y = x.reshape(lead + (D // (2 * h), 2, h))", "y = x.reshape(lead + (D // (2 * h), h, 2)).swapaxes(-1, -2)"),
+    "no_normalization": ("return (y * inv_sqrt_f32(x.shape[-1])).astype(_F32)", "return y.astype(_F32)"),
+    "unrotate_no_signs": ("return fwht(x) * np.asarray(signs, np.float64) / math.sqrt(D)", "return fwht(x) / math.sqrt(D)"),
+    "floor_not_rint": ("c = np.clip(np.rint(t), lo, hi)", "c = np.clip(np.floor(t), lo, hi)"),
+    "zero_is_max": ("z = mn.astype(_F32)", "z = mx.astype(_F32)"),
+    "int4_levels_16": ("LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3}", "LEVELS = {INT8_SYM: 127, INT4_ASYM: 16, INT2_ASYM: 3}"),
+    "int8_levels_128": ("LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3}", "LEVELS = {INT8_SYM: 128, INT4_ASYM: 15, INT2_ASYM: 3}"),
+    "nibble_order": ("out |= g[..., k] << (b * k)", "out |= g[..., k] << (b * (per - 1 - k))"),
+    "int8_no_sign_extend": ("return np.where(p >= 128, p - 256, p).astype(np.int32)", "return p.astype(np.int32)"),
+    "dequant_wrong": ("return (np.asarray(codes, np.float64) * np.asarray(s, np.float64)[..., None]\n            + np.asarray(z, np.float64)[..., None])",
+                      "return ((np.asarray(codes, np.float64) + np.asarray(z, np.float64)[..., None])\n            * np.asarray(s, np.float64)[..., None])"),
+    "gqa_map": ("qs = q[b, h * G:(h + 1) * G]", "qs = q[b, h::num_kv_heads]"),
+    "window_off_by_one": ("allowed &= np.arange(L) >= L - W", "allowed &= np.arange(L) > L - W"),
+    "causal_strict": ("allowed = (j <= pos) & present[None, :]", "allowed = (j < pos) & present[None, :]"),
+    "prefill_window_off_by_one": ("allowed &= j >= pos - W + 1", "allowed &= j >= pos - W"),
+    "evicted_read": ("present = ids >= 0", "present = ids >= -1"),
+    "headwise_row": ("return np.asarray(block_tables_headwise)[b * num_kv_heads + h]", "return np.asarray(block_tables_headwise)[h * num_kv_heads + b]"),
+    "scale_dropped": ("logits = scale * (np.asarray(qs, np.float64) @ K.T)", "logits = np.asarray(qs, np.float64) @ K.T"),
+    "slot_offset": ("blk, off = sl // block_size, sl % block_size", "blk, off = sl // block_size, (sl + 1) % block_size"),
+}
+
+
+def _mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    mod = _mutant(*MUTATIONS[name])
+    caught = []
+    for check in pins.ALL:
+        try:
+            check(mod)
+        except Exception:   # AssertionError, or a crash the mistake causes
+            caught.append(check.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
