@@ -1,0 +1,189 @@
+/*
+ * kvq.h -- C ABI of libkvq: a dynamically quantized paged KV cache and the
+ * attention that reads it, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages (cited by title and section):
+ *  - FastDeploy PR 5173 "[Feature] support dynamic int2 quantization cache kv"
+ *    (Motivation; pull-request overview): a 2-bit KV cache with run-time
+ *    scales, written by encoder/decoder cache-write kernels and read by an
+ *    attention kernel; no scales come from checkpoints.
+ *  - prhub summary of vLLM PR 40835 "INT4 per-token-head KV cache quantization
+ *    for the Triton backend" (功能与动机; 实现拆解; 关键源码片段): a write
+ *    entry point (reshape-and-cache) that applies a randomized Hadamard
+ *    transform, computes one scale and zero point per (token, kv head) and
+ *    packs two 4-bit codes per byte; a read entry point (unified attention)
+ *    that unpacks, dequantizes and attends; uint8 storage.
+ *  - FastDeploy PR 7718 "Optimize AppendAttention for discrete head-wise
+ *    block_idx" (Motivation; Modifications; correctness gates): an optional,
+ *    additive head-wise block table [batch*kv_heads, max_blocks] whose -1
+ *    entries are evicted sliding-window blocks that are skipped before any
+ *    K/V address is formed; int32 index tensors; the GQA head-divisibility
+ *    check raises instead of asserting.
+ *  - FastDeploy PR 7757 "fix cache_manager_v1 allocating kv cache with wrong
+ *    dtype" (问题描述; 修复): every quantized cache is uint8; a storage
+ *    dtype/size mismatch must be reported, not crash.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked (device) are HIP device pointers; (host) are host
+ *    pointers.  The caller owns every buffer and keeps it alive until the work
+ *    queued on `stream` has finished.  The library allocates no device memory
+ *    and keeps no pointer after returning.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    Every launch is asynchronous on it.
+ *  - Arguments are validated on the host before anything is launched.  A
+ *    status other than KVQ_OK means nothing was launched; kvq_last_error()
+ *    then returns a message (thread-local, valid until the next call on the
+ *    same thread).  The library never aborts.
+ *  - Values the host cannot see (device-side seq_lens, block ids, slots) are
+ *    the caller's contract: block ids must be < num_blocks or negative (table
+ *    entries) and slots < num_blocks*block_size or negative (slot mappings).
+ *
+ * Cache layout (one code plane and one meta plane each for K and for V):
+ *    codes: uint8   [num_blocks, num_kv_heads, block_size, P]
+ *           P = head_dim * b / 8, b = 8, 4, 2 bits
+ *    meta : float32 [num_blocks, num_kv_heads, block_size, M]
+ *           M = 1 (INT8: scale) or 2 (INT4/INT2: scale, zero point)
+ *  A (token, kv head) row of codes is contiguous.  INT4 puts element 2j in the
+ *  low nibble of byte j; INT2 puts element 4j+k in bits 2k..2k+1 of byte j;
+ *  INT8 stores two's complement codes in [-127, 127].  Reconstruction:
+ *  x_hat = c*s (INT8) or c*s + z (INT4/INT2), in the rotated basis when the
+ *  cache has a rotation.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = 1,        /* an argument is invalid (NULL, out of range, inconsistent) */
+  KVQ_EUNSUPPORTED = 2,  /* valid but not built (e.g. head_dim 96, GQA group > 16) */
+  KVQ_ENOSPACE = 3,      /* the workspace is smaller than the *_workspace_size result */
+  KVQ_EHIP = 4           /* the HIP runtime reported an error at launch */
+} kvq_status;
+
+/* Quantization modes.  INT8: per-token-head symmetric, s = max|y| / 127.
+ * INT4 / INT2: per-token-head asymmetric, s = (max y - min y) / L,
+ * z = min y, L = 15 / 3, codes = clamp(rint((y - z) / s), 0, L), computed as
+ * (y - z) * (1/s) in float32 with round-half-to-even.  A row whose scale is
+ * zero or subnormal gets all-zero codes. */
+typedef enum { KVQ_INT8_SYM = 0, KVQ_INT4_ASYM = 1, KVQ_INT2_ASYM = 2 } kvq_mode;
+
+typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 } kvq_out_dtype;
+
+typedef struct {
+  int32_t mode;            /* kvq_mode */
+  int32_t head_dim;        /* D: 64 or 128 */
+  int32_t num_kv_heads;    /* Hkv >= 1 */
+  int32_t block_size;      /* tokens per block: a multiple of 16, 16..1024 */
+  int64_t num_blocks;      /* physical blocks in each plane, >= 1 */
+  /* (device) [head_dim] float32 of +1.0f / -1.0f, or NULL for no rotation.
+   * With signs d, every K and V row x is stored as the codes of
+   * y = (1/sqrt(D)) * H_D (d .* x), H_D the Sylvester Hadamard matrix in
+   * natural order; attention pre-rotates the query with the same matrix and
+   * rotates its output back, so results are in the original basis. */
+  const float* rot_signs;
+} kvq_cache_desc;
+
+typedef struct {
+  uint64_t code_bytes;       /* bytes of one code plane (the K plane; V is equal) */
+  uint64_t meta_bytes;       /* bytes of one meta plane */
+  uint32_t row_code_bytes;   /* P */
+  uint32_t row_meta_floats;  /* M */
+} kvq_layout;
+
+/* Sizes of the planes the caller must allocate for `desc` (host only, no GPU
+ * needed).  Cache allocation from these sizes rules out the storage-dtype
+ * mismatch of FastDeploy PR 7757 by construction. */
+kvq_status kvq_query_layout(const kvq_cache_desc* desc, kvq_layout* out /* host */);
+
+/* Quantize-on-write (vLLM PR 40835 summary, 实现拆解 item 2; FastDeploy PR
+ * 5173 encoder/decoder cache write).  For each token t < num_tokens and kv
+ * head h: read the bf16 rows key[t, h, :] and value[t, h, :], rotate them
+ * (if desc->rot_signs), compute the per-row scale (and zero point), round,
+ * pack and store codes and meta at slot = slot_mapping[t] (or
+ * slot_mapping_headwise[t*Hkv + h]): block = slot / block_size,
+ * offset = slot % block_size.  A negative slot skips the row.
+ *   key, value       (device) bf16, row (t, h) at t*tok_stride + h*D elements
+ *   *_tok_stride     elements between consecutive tokens, >= Hkv*D
+ *   slot_mapping     (device) int64 [num_tokens], or NULL
+ *   slot_mapping_headwise (device) int64 [num_tokens, Hkv], or NULL;
+ *                    exactly one of the two slot mappings is non-NULL
+ *                    (num_tokens == 0 is a no-op that reads no argument)
+ *   k_codes, v_codes (device) uint8 planes; k_meta, v_meta (device) float32
+ * Two tokens mapped to the same (slot, head) in one call race. */
+kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc,
+                                 const void* key, const void* value,
+                                 int64_t key_tok_stride, int64_t value_tok_stride,
+                                 const int64_t* slot_mapping,
+                                 const int64_t* slot_mapping_headwise,
+                                 int32_t num_tokens,
+                                 uint8_t* k_codes, float* k_meta,
+                                 uint8_t* v_codes, float* v_meta,
+                                 void* stream);
+
+/* Workspace bytes kvq_paged_decode_attention needs for these sizes (host
+ * only).  max_seq_len is the largest seq_lens entry the call will see. */
+kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t max_seq_len,
+                                     size_t* bytes /* host */);
+
+/* Zero a decode workspace once after allocating it (asynchronous on
+ * `stream`).  Decode keeps per-(sequence, kv head) completion counters at
+ * the start of the workspace; every decode call leaves them at zero again,
+ * so a workspace needs this only once.  Calls that share a workspace must be
+ * ordered (same stream or synchronized). */
+kvq_status kvq_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Paged decode attention (vLLM PR 40835 summary, 实现拆解 item 2: unpack,
+ * dequantize, attend; FastDeploy PR 7718: optional head-wise table with -1
+ * skips).  One query token per sequence; for sequence b, q head hq and kv
+ * head h = hq / (Hq/Hkv) the output is softmax attention of query[b, hq] over
+ * the dequantized, un-rotated keys/values of positions j < seq_lens[b] that
+ * lie in a non-evicted block and, if window && window[h] > 0, satisfy
+ * j >= seq_lens[b] - window[h].  No allowed position => output 0.
+ *   out          (device) [B, Hq, D] float32 (KVQ_OUT_F32) or bf16 (KVQ_OUT_BF16)
+ *   query        (device) bf16 [B, Hq, D]
+ *   block_tables (device) int32 [B, max_blocks_per_seq], or NULL
+ *   block_tables_headwise (device) int32 [B*Hkv, max_blocks_per_seq], or NULL;
+ *                exactly one is non-NULL; row b*Hkv + h serves kv head h;
+ *                an entry < 0 marks an evicted block (never read)
+ *   seq_lens     (device) int32 [B], positions cached for each sequence
+ *                (the current token included), each <= max_seq_len
+ *   max_seq_len  host upper bound on seq_lens, <= max_blocks_per_seq*block_size
+ *   window       (device) int32 [Hkv], <= 0 = full context; or NULL
+ *   softmax_scale  logits scale (usually 1/sqrt(D)); finite
+ *   workspace    (device) >= kvq_decode_workspace_size bytes, 256-byte
+ *                aligned, zeroed once by kvq_workspace_init
+ * Calls sharing one workspace must not overlap in time. */
+kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc,
+                                      void* out, int32_t out_dtype,
+                                      const void* query,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      const uint8_t* k_codes, const float* k_meta,
+                                      const uint8_t* v_codes, const float* v_meta,
+                                      const int32_t* block_tables,
+                                      const int32_t* block_tables_headwise,
+                                      int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t max_seq_len,
+                                      const int32_t* window,
+                                      float softmax_scale,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/* Thread-local message for the last non-OK status ("" if none). */
+const char* kvq_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,274 @@
+// libkvq host side: argument validation, cache layout, split planning and
+// kernel launches behind the C ABI of include/kvq.h.
+//
+// Validation mirrors the interface facts of the pages: int32 index tensors and
+// a head-divisibility check that reports instead of asserting (FastDeploy PR
+// 7718, Modifications), an additive optional head-wise table (same PR,
+// Motivation), uint8 storage whose size comes from the layout query (FastDeploy
+// PR 7757, 修复), and no static scales (FastDeploy PR 5173, overview).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvq_status ok() {
+  g_err[0] = '\0';
+  return KVQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+kvq_status check_desc(const kvq_cache_desc* d) {
+  if (!d) return fail(KVQ_EINVAL, "desc is NULL");
+  if (d->mode < KVQ_INT8_SYM || d->mode > KVQ_INT2_ASYM)
+    return fail(KVQ_EINVAL, "mode %d is not a kvq_mode", d->mode);
+  if (d->head_dim != 64 && d->head_dim != 128) {
+    if (d->head_dim > 0 && (d->head_dim & (d->head_dim - 1)) == 0)
+      return fail(KVQ_EUNSUPPORTED, "head_dim %d: only 64 and 128 are built", d->head_dim);
+    return fail(KVQ_EINVAL, "head_dim %d must be a power of two (64 or 128)", d->head_dim);
+  }
+  if (d->num_kv_heads < 1) return fail(KVQ_EINVAL, "num_kv_heads %d < 1", d->num_kv_heads);
+  if (d->block_size < 16 || d->block_size > 1024 || d->block_size % 16 != 0)
+    return fail(KVQ_EINVAL, "block_size %d must be a multiple of 16 in [16, 1024]", d->block_size);
+  if (d->num_blocks < 1) return fail(KVQ_EINVAL, "num_blocks %lld < 1", (long long)d->num_blocks);
+  if (d->rot_signs && !aligned(d->rot_signs, 16))
+    return fail(KVQ_EINVAL, "rot_signs must be 16-byte aligned");
+  return KVQ_OK;
+}
+
+kvq_status check_planes(const uint8_t* kc, const float* km, const uint8_t* vc, const float* vm) {
+  if (!kc || !km || !vc || !vm) return fail(KVQ_EINVAL, "a cache plane pointer is NULL");
+  if (!aligned(kc, 16) || !aligned(km, 16) || !aligned(vc, 16) || !aligned(vm, 16))
+    return fail(KVQ_EINVAL, "cache planes must be 16-byte aligned");
+  return KVQ_OK;
+}
+
+float inv_sqrt_f32(int d) { return (float)(1.0 / std::sqrt((double)d)); }
+
+struct DecodePlan {
+  int chunks_per_split;
+  int max_splits;
+  size_t counter_bytes;
+  size_t partial_bytes;
+  size_t total() const { return counter_bytes + partial_bytes; }
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Split-KV plan: split each (sequence, kv head)'s active range into runs of
+// chunks so that the launch holds a few thousand waves (>> 256 CUs) whatever
+// the batch.  Deterministic in its inputs, so the workspace query and the
+// call agree.
+DecodePlan plan_decode(const kvq_cache_desc* d, int num_seqs, int num_q_heads, int max_seq_len) {
+  DecodePlan pl{};
+  const long long max_chunks = (max_seq_len + kvq::kChunk - 1) / kvq::kChunk;
+  const long long units = (long long)num_seqs * d->num_kv_heads * (max_chunks > 0 ? max_chunks : 1);
+  long long target = 4096;
+  if (const char* e = std::getenv("KVQ_DECODE_TARGET_WAVES")) {
+    const long long t = std::atoll(e);
+    if (t > 0) target = t;
+  }
+  long long cps = (units + target - 1) / target;
+  if (cps < 4) cps = 4;
+  if (const char* e = std::getenv("KVQ_DECODE_CHUNKS_PER_SPLIT")) {
+    const long long c = std::atoll(e);
+    if (c > 0) cps = c;
+  }
+  if (max_chunks > 0 && cps > max_chunks) cps = max_chunks;
+  if (cps < 1) cps = 1;
+  long long ms = max_chunks > 0 ? (max_chunks + cps - 1) / cps : 1;
+  if (ms < 1) ms = 1;
+  pl.chunks_per_split = (int)cps;
+  pl.max_splits = (int)ms;
+  if (ms > 1) {
+    pl.counter_bytes = round_up((size_t)num_seqs * d->num_kv_heads * sizeof(uint32_t), 256);
+    pl.partial_bytes = (size_t)num_seqs * num_q_heads * ms * (d->head_dim + 4) * sizeof(float);
+  }
+  return pl;
+}
+
+kvq_status check_decode_sizes(const kvq_cache_desc* d, int num_seqs, int num_q_heads, int max_seq_len) {
+  if (num_seqs < 0) return fail(KVQ_EINVAL, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > 65535) return fail(KVQ_EUNSUPPORTED, "num_seqs %d > 65535", num_seqs);
+  if (num_q_heads < 1) return fail(KVQ_EINVAL, "num_q_heads %d < 1", num_q_heads);
+  if (num_q_heads % d->num_kv_heads != 0)
+    return fail(KVQ_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                d->num_kv_heads);
+  if (num_q_heads / d->num_kv_heads > 16)
+    return fail(KVQ_EUNSUPPORTED, "GQA group %d > 16 is not built", num_q_heads / d->num_kv_heads);
+  if (d->num_kv_heads > 65535) return fail(KVQ_EUNSUPPORTED, "num_kv_heads > 65535");
+  if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len %d < 0", max_seq_len);
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_query_layout(const kvq_cache_desc* desc, kvq_layout* out) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_EINVAL, "out is NULL");
+  const uint32_t P = (uint32_t)kvq::row_bytes(desc->mode, desc->head_dim);
+  const uint32_t M = (uint32_t)kvq::mode_meta(desc->mode);
+  const uint64_t rows = (uint64_t)desc->num_blocks * desc->num_kv_heads * desc->block_size;
+  out->row_code_bytes = P;
+  out->row_meta_floats = M;
+  out->code_bytes = rows * P;
+  out->meta_bytes = rows * M * sizeof(float);
+  return ok();
+}
+
+kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc, const void* key, const void* value,
+                                 int64_t key_tok_stride, int64_t value_tok_stride,
+                                 const int64_t* slot_mapping, const int64_t* slot_mapping_headwise,
+                                 int32_t num_tokens, uint8_t* k_codes, float* k_meta,
+                                 uint8_t* v_codes, float* v_meta, void* stream) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (num_tokens < 0) return fail(KVQ_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return ok();  // nothing is read or written
+  if ((slot_mapping == nullptr) == (slot_mapping_headwise == nullptr))
+    return fail(KVQ_EINVAL, "exactly one of slot_mapping and slot_mapping_headwise must be non-NULL");
+  st = check_planes(k_codes, k_meta, v_codes, v_meta);
+  if (st != KVQ_OK) return st;
+  const int D = desc->head_dim, H = desc->num_kv_heads;
+  {
+    if (!key || !value) return fail(KVQ_EINVAL, "key or value is NULL");
+    if (key_tok_stride < (int64_t)H * D || value_tok_stride < (int64_t)H * D)
+      return fail(KVQ_EINVAL, "token strides (%lld, %lld) must be >= num_kv_heads*head_dim = %d",
+                  (long long)key_tok_stride, (long long)value_tok_stride, H * D);
+    if (key_tok_stride % 8 != 0 || value_tok_stride % 8 != 0 || !aligned(key, 16) || !aligned(value, 16))
+      return fail(KVQ_EINVAL, "key/value must be 16-byte aligned with token strides a multiple of 8");
+  }
+  kvq::WriteParams p{};
+  p.key = static_cast<const uint16_t*>(key);
+  p.value = static_cast<const uint16_t*>(value);
+  p.key_stride = key_tok_stride;
+  p.value_stride = value_tok_stride;
+  p.slot = slot_mapping;
+  p.slot_hw = slot_mapping_headwise;
+  p.total_rows = 2 * (int64_t)num_tokens * H;
+  p.hkv = H;
+  p.block_size = desc->block_size;
+  p.k_codes = k_codes;
+  p.k_meta = k_meta;
+  p.v_codes = v_codes;
+  p.v_meta = v_meta;
+  p.signs = desc->rot_signs;
+  p.inv_sqrt_d = inv_sqrt_f32(D);
+  hipError_t e = kvq::launch_write(desc->mode, D, desc->rot_signs != nullptr, p,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_EHIP, "write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_seq_len, size_t* bytes) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  st = check_decode_sizes(desc, num_seqs, num_q_heads, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (!bytes) return fail(KVQ_EINVAL, "bytes is NULL");
+  *bytes = plan_decode(desc, num_seqs, num_q_heads, max_seq_len).total();
+  return ok();
+}
+
+kvq_status kvq_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return ok();
+  if (!workspace) return fail(KVQ_EINVAL, "workspace is NULL");
+  if (!aligned(workspace, 256) || workspace_bytes % 16 != 0)
+    return fail(KVQ_EINVAL, "workspace must be 256-byte aligned and a multiple of 16 bytes");
+  hipError_t e = kvq::launch_fill_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_EHIP, "workspace init: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
+                                      const void* query, int32_t num_seqs, int32_t num_q_heads,
+                                      const uint8_t* k_codes, const float* k_meta,
+                                      const uint8_t* v_codes, const float* v_meta,
+                                      const int32_t* block_tables, const int32_t* block_tables_headwise,
+                                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                      int32_t max_seq_len, const int32_t* window, float softmax_scale,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  st = check_decode_sizes(desc, num_seqs, num_q_heads, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16)
+    return fail(KVQ_EINVAL, "out_dtype %d is not a kvq_out_dtype", out_dtype);
+  if ((block_tables == nullptr) == (block_tables_headwise == nullptr))
+    return fail(KVQ_EINVAL, "exactly one of block_tables and block_tables_headwise must be non-NULL");
+  if (max_blocks_per_seq < 1) return fail(KVQ_EINVAL, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * desc->block_size)
+    return fail(KVQ_EINVAL, "max_seq_len %d exceeds max_blocks_per_seq*block_size = %lld", max_seq_len,
+                (long long)max_blocks_per_seq * desc->block_size);
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is not finite");
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !seq_lens) return fail(KVQ_EINVAL, "out, query or seq_lens is NULL");
+  if (!aligned(out, 16)) return fail(KVQ_EINVAL, "out must be 16-byte aligned");
+  st = check_planes(k_codes, k_meta, v_codes, v_meta);
+  if (st != KVQ_OK) return st;
+  const DecodePlan pl = plan_decode(desc, num_seqs, num_q_heads, max_seq_len);
+  if (pl.total() > 0) {
+    if (!workspace) return fail(KVQ_EINVAL, "workspace is NULL (%zu bytes needed)", pl.total());
+    if (workspace_bytes < pl.total())
+      return fail(KVQ_ENOSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total());
+    if (!aligned(workspace, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
+  }
+  kvq::DecodeParams p{};
+  p.k_codes = k_codes;
+  p.k_meta = k_meta;
+  p.v_codes = v_codes;
+  p.v_meta = v_meta;
+  p.q = static_cast<const uint16_t*>(query);
+  p.out = out;
+  p.headwise = block_tables_headwise != nullptr;
+  p.tables = p.headwise ? block_tables_headwise : block_tables;
+  p.seq_lens = seq_lens;
+  p.window = window;
+  p.signs = desc->rot_signs;
+  p.counters = pl.total() > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
+  p.partials = pl.total() > 0
+                   ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counter_bytes)
+                   : nullptr;
+  p.qscale = softmax_scale * 1.4426950408889634f;
+  p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
+  p.max_blocks = max_blocks_per_seq;
+  p.block_size = desc->block_size;
+  p.hq = num_q_heads;
+  p.hkv = desc->num_kv_heads;
+  p.group = num_q_heads / desc->num_kv_heads;
+  p.chunks_per_split = pl.chunks_per_split;
+  p.max_splits = pl.max_splits;
+  p.out_bf16 = out_dtype == KVQ_OUT_BF16;
+  hipError_t e = kvq::launch_decode(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p, num_seqs,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* kvq_last_error(void) { return g_err; }
+
+int32_t kvq_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal declarations shared by the libkvq host code and its HIP kernels.
+// Not part of the C ABI (include/kvq.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// Codes per byte and metadata floats per row, by mode (0 INT8, 1 INT4, 2 INT2).
+__host__ __device__ constexpr int mode_bits(int mode) { return mode == 0 ? 8 : (mode == 1 ? 4 : 2); }
+__host__ __device__ constexpr int mode_meta(int mode) { return mode == 0 ? 1 : 2; }
+__host__ __device__ constexpr int mode_levels(int mode) { return mode == 0 ? 127 : (mode == 1 ? 15 : 3); }
+__host__ __device__ constexpr int row_bytes(int mode, int d) { return d * mode_bits(mode) / 8; }
+
+// Positions processed together by the decode kernel: two 16-token MFMA tiles.
+constexpr int kChunk = 32;
+
+struct WriteParams {
+  const uint16_t* key;      // bf16
+  const uint16_t* value;    // bf16
+  int64_t key_stride;       // elements between tokens
+  int64_t value_stride;
+  const int64_t* slot;      // [T] or nullptr
+  const int64_t* slot_hw;   // [T, Hkv] or nullptr
+  int64_t total_rows;       // 2 * T * Hkv
+  int32_t hkv;
+  int32_t block_size;
+  uint8_t* k_codes;
+  float* k_meta;
+  uint8_t* v_codes;
+  float* v_meta;
+  const float* signs;       // [D] or nullptr
+  float inv_sqrt_d;         // float32 rounding of 1/sqrt(D)
+};
+
+struct DecodeParams {
+  const uint8_t* k_codes;
+  const float* k_meta;
+  const uint8_t* v_codes;
+  const float* v_meta;
+  const uint16_t* q;            // bf16 [B, Hq, D]
+  void* out;                    // [B, Hq, D]
+  const int32_t* tables;        // [B, max_blocks] or [B*Hkv, max_blocks]
+  const int32_t* seq_lens;      // [B]
+  const int32_t* window;        // [Hkv] or nullptr
+  const float* signs;           // [D] or nullptr
+  float* partials;              // [B, Hq, max_splits, D + 4]
+  uint32_t* counters;           // [B, Hkv]
+  float qscale;                 // softmax_scale * log2(e)
+  float inv_sqrt_d;
+  int32_t headwise;
+  int32_t max_blocks;
+  int32_t block_size;
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;                // Hq / Hkv
+  int32_t chunks_per_split;
+  int32_t max_splits;
+  int32_t out_bf16;
+};
+
+hipError_t launch_write(int mode, int d, bool rot, const WriteParams& p, hipStream_t s);
+hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, int num_seqs,
+                         hipStream_t s);
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+
+}  // namespace kvq

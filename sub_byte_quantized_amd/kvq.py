@@ -1,0 +1,185 @@
+"""Python binding of libkvq with the C ABI's names.
+
+Argument marshalling only: tensors are checked for dtype, device and
+contiguity, their data pointers and the current HIP stream are passed to the
+library, and a non-OK status raises KvqError with the library's message.
+Every step of the computation runs in the library's HIP kernels.  PyTorch is
+used for device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (KVQ_INT2_ASYM, KVQ_INT4_ASYM, KVQ_INT8_SYM, KVQ_OUT_BF16,  # noqa: F401
+                   KVQ_OUT_F32)
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_lib.STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != _lib.KVQ_OK:
+        raise KvqError(status, _lib.load().kvq_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, device=None, contiguous=True):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a HIP device, got {device}")
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+@dataclasses.dataclass
+class CacheDesc:
+    mode: int
+    head_dim: int
+    num_kv_heads: int
+    block_size: int
+    num_blocks: int
+    rot_signs: Optional[torch.Tensor] = None   # float32 [head_dim] of +-1, on the device
+
+    def c(self) -> _lib.CacheDesc:
+        if self.rot_signs is not None:
+            _need(self.rot_signs, "rot_signs", torch.float32)
+        return _lib.CacheDesc(int(self.mode), int(self.head_dim), int(self.num_kv_heads),
+                              int(self.block_size), int(self.num_blocks),
+                              None if self.rot_signs is None else self.rot_signs.data_ptr())
+
+
+def kvq_query_layout(desc: CacheDesc) -> dict:
+    out = _lib.Layout()
+    d = desc.c()
+    _check(_lib.load().kvq_query_layout(ctypes.byref(d), ctypes.byref(out)))
+    return dict(code_bytes=out.code_bytes, meta_bytes=out.meta_bytes,
+                row_code_bytes=out.row_code_bytes, row_meta_floats=out.row_meta_floats)
+
+
+def alloc_cache(desc: CacheDesc, device, poison: bool = False):
+    """Allocate (k_codes, k_meta, v_codes, v_meta) at the sizes
+    kvq_query_layout reports: uint8 [nb, Hkv, bs, P] and float32
+    [nb, Hkv, bs, M].  ``poison`` fills codes with 0xFF and meta with NaN."""
+    lay = kvq_query_layout(desc)
+    P, M = lay["row_code_bytes"], lay["row_meta_floats"]
+    shape_c = (desc.num_blocks, desc.num_kv_heads, desc.block_size, P)
+    shape_m = (desc.num_blocks, desc.num_kv_heads, desc.block_size, M)
+    planes = []
+    for _ in range(2):
+        c = torch.empty(shape_c, dtype=torch.uint8, device=device)
+        m = torch.empty(shape_m, dtype=torch.float32, device=device)
+        assert c.numel() == lay["code_bytes"] and m.numel() * 4 == lay["meta_bytes"]
+        if poison:
+            c.fill_(0xFF)
+            m.fill_(float("nan"))
+        planes += [c, m]
+    return tuple(planes)
+
+
+def kvq_reshape_and_cache(desc: CacheDesc, key: torch.Tensor, value: torch.Tensor,
+                          k_codes: torch.Tensor, k_meta: torch.Tensor,
+                          v_codes: torch.Tensor, v_meta: torch.Tensor,
+                          slot_mapping: Optional[torch.Tensor] = None,
+                          slot_mapping_headwise: Optional[torch.Tensor] = None) -> None:
+    """Quantize bf16 key/value [T, Hkv, D] into the paged cache."""
+    dev = k_codes.device
+    for t, n in ((key, "key"), (value, "value")):
+        _need(t, n, torch.bfloat16, dev, contiguous=False)
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != desc.head_dim:
+            raise ValueError(f"{n} must be [T, Hkv, D] with heads and D contiguous")
+    if key.shape != value.shape:
+        raise ValueError("key and value shapes differ")
+    _need(slot_mapping, "slot_mapping", torch.int64, dev)
+    _need(slot_mapping_headwise, "slot_mapping_headwise", torch.int64, dev)
+    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (v_codes, "v_codes", torch.uint8),
+                     (k_meta, "k_meta", torch.float32), (v_meta, "v_meta", torch.float32)):
+        _need(t, n, dt, dev)
+    d = desc.c()
+    _check(_lib.load().kvq_reshape_and_cache(
+        ctypes.byref(d), _ptr(key), _ptr(value), key.stride(0), value.stride(0),
+        _ptr(slot_mapping), _ptr(slot_mapping_headwise), int(key.shape[0]),
+        _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta), _stream(dev)))
+
+
+def kvq_decode_workspace_size(desc: CacheDesc, num_seqs: int, num_q_heads: int,
+                              max_seq_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    d = desc.c()
+    _check(_lib.load().kvq_decode_workspace_size(ctypes.byref(d), int(num_seqs), int(num_q_heads),
+                                                 int(max_seq_len), ctypes.byref(n)))
+    return int(n.value)
+
+
+def kvq_workspace_init(workspace: torch.Tensor) -> None:
+    _need(workspace, "workspace", torch.uint8)
+    _check(_lib.load().kvq_workspace_init(_ptr(workspace), workspace.numel(), _stream(workspace.device)))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A device workspace of at least ``nbytes`` (rounded to 256), zeroed by
+    kvq_workspace_init."""
+    n = max(256, (int(nbytes) + 255) // 256 * 256)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    kvq_workspace_init(ws)
+    return ws
+
+
+def kvq_paged_decode_attention(desc: CacheDesc, query: torch.Tensor,
+                               k_codes: torch.Tensor, k_meta: torch.Tensor,
+                               v_codes: torch.Tensor, v_meta: torch.Tensor,
+                               seq_lens: torch.Tensor, max_seq_len: int,
+                               block_tables: Optional[torch.Tensor] = None,
+                               block_tables_headwise: Optional[torch.Tensor] = None,
+                               window: Optional[torch.Tensor] = None,
+                               softmax_scale: Optional[float] = None,
+                               out: Optional[torch.Tensor] = None,
+                               out_dtype: torch.dtype = torch.float32,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention for query [B, Hq, D] (bf16); returns out [B, Hq, D]."""
+    dev = query.device
+    _need(query, "query", torch.bfloat16, dev)
+    B, Hq, D = query.shape
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(block_tables_headwise, "block_tables_headwise", torch.int32, dev)
+    _need(window, "window", torch.int32, dev)
+    tab = block_tables if block_tables is not None else block_tables_headwise
+    max_blocks = int(tab.shape[1]) if tab is not None else 0
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
+    _need(out, "out", out.dtype, dev)
+    odt = {torch.float32: KVQ_OUT_F32, torch.bfloat16: KVQ_OUT_BF16}[out.dtype]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = alloc_workspace(kvq_decode_workspace_size(desc, B, Hq, max_seq_len), dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    d = desc.c()
+    _check(_lib.load().kvq_paged_decode_attention(
+        ctypes.byref(d), _ptr(out), odt, _ptr(query), int(B), int(Hq),
+        _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
+        _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
+        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale),
+        _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out

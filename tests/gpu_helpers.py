@@ -1,0 +1,99 @@
+"""Shared helpers for the GPU parity tests: build a workload, write it with
+the HIP path into a poisoned cache, and run the oracle on the GPU's stored
+planes (so attention parity does not depend on write parity)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+import sub_byte_quantized_amd as kvq
+
+# Attention acceptance on float32 output (max-abs, mean-abs).
+ATOL_MAX = 2e-3
+ATOL_MEAN = 2e-4
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def desc_of(spec, case, num_blocks=None):
+    return kvq.CacheDesc(spec.mode, spec.D, spec.Hkv, spec.bs,
+                         num_blocks or case.tables.num_blocks, case.rot_signs)
+
+
+def build(spec, device=None, write=True, case=None):
+    """Case on the device, poisoned planes, every position written by the HIP
+    write kernel.  Returns (case, desc, planes)."""
+    device = device or dev()
+    case = case or synth.make_case(spec, device)
+    d = desc_of(spec, case)
+    planes = kvq.alloc_cache(d, device, poison=True)
+    if write:
+        kvq.kvq_reshape_and_cache(d, case.k, case.v, *planes, slot_mapping=case.slot_mapping,
+                                  slot_mapping_headwise=case.slot_mapping_headwise)
+    torch.cuda.synchronize()
+    return case, d, planes
+
+
+def host(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def host_planes(planes):
+    return [host(p) for p in planes]
+
+
+def f32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def oracle_decode(spec, case, planes_np, pairs=None):
+    return oracle.decode_attention(
+        f32(case.q), host(case.seq_lens), spec.mode, spec.D, spec.bs, spec.Hkv,
+        *planes_np, case.softmax_scale, signs=host(case.rot_signs),
+        block_tables=host(case.block_tables), block_tables_headwise=host(case.block_tables_headwise),
+        window=host(case.window), pairs=pairs)
+
+
+def gpu_decode(spec, case, d, planes, **kw):
+    return kvq.kvq_paged_decode_attention(
+        d, case.q, *planes, case.seq_lens, int(case.seq_lens.max().item()),
+        block_tables=case.block_tables, block_tables_headwise=case.block_tables_headwise,
+        window=case.window, softmax_scale=case.softmax_scale, **kw)
+
+
+def assert_close(got, ref, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    mask = ~np.isnan(ref)
+    assert mask.any()
+    assert np.all(np.isfinite(got[mask])), f"{what}: non-finite output"
+    err = np.abs(got[mask] - ref[mask])
+    mx, mean = float(err.max()), float(err.mean())
+    print(f"[parity] {what}: max-abs {mx:.3e} mean-abs {mean:.3e} over {mask.sum()} values")
+    assert mx <= ATOL_MAX and mean <= ATOL_MEAN, f"{what}: max-abs {mx:.3e} mean-abs {mean:.3e}"
+
+
+def compare_codes(spec, got_codes, ref_codes, rotated, what=""):
+    """Packed codes: bit-exact without rotation; with rotation at most 0.01 %
+    of elements may differ, each by one step."""
+    if not rotated:
+        assert np.array_equal(got_codes, ref_codes), f"{what}: codes differ"
+        return
+    g = oracle.unpack_codes(got_codes, spec.mode, spec.D).astype(np.int64)
+    r = oracle.unpack_codes(ref_codes, spec.mode, spec.D).astype(np.int64)
+    diff = np.abs(g - r)
+    n_bad = int((diff > 0).sum())
+    print(f"[parity] {what}: {n_bad} of {diff.size} codes differ (max step {int(diff.max())})")
+    assert diff.max() <= 1 and n_bad <= 1e-4 * diff.size, f"{what}: {n_bad} codes differ"
+
+
+def compare_meta(got, ref, what=""):
+    """Scales and zero points within 1e-6 relative (absolute floor 1e-30)."""
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    tol = 1e-6 * np.abs(ref.astype(np.float64)) + 1e-30
+    bad = err > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} meta values differ; worst {err.max():.3e}"

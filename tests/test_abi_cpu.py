@@ -1,0 +1,140 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+symbol include/kvq.h declares, and rejects invalid arguments before any HIP
+call (FastDeploy PR 7718 Modifications: checks report instead of asserting;
+FastDeploy PR 7757 修复: sizes come from the layout query)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from sub_byte_quantized_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvq_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def desc(mode=1, D=128, H=4, bs=64, nb=10, signs=None):
+    return _lib.CacheDesc(mode, D, H, bs, nb, signs)
+
+
+def test_header_lists_entry_points():
+    names = header_functions()
+    for n in ("kvq_query_layout", "kvq_reshape_and_cache", "kvq_paged_decode_attention",
+              "kvq_decode_workspace_size", "kvq_workspace_init", "kvq_last_error"):
+        assert n in names
+
+
+def test_exports_every_header_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks {name}"
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("D", [64, 128])
+def test_layout_matches_formula(lib, mode, D):
+    d = desc(mode, D, H=3, bs=32, nb=7)
+    out = _lib.Layout()
+    assert lib.kvq_query_layout(ctypes.byref(d), ctypes.byref(out)) == 0
+    cshape, mshape = oracle.plane_shapes(mode, D, 3, 32, 7)
+    assert out.row_code_bytes == cshape[-1] == D * {0: 8, 1: 4, 2: 2}[mode] // 8
+    assert out.row_meta_floats == mshape[-1]
+    assert out.code_bytes == 7 * 3 * 32 * cshape[-1]
+    assert out.meta_bytes == 7 * 3 * 32 * mshape[-1] * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mode=3), _lib.KVQ_EINVAL), (dict(mode=-1), _lib.KVQ_EINVAL),
+    (dict(D=96), _lib.KVQ_EINVAL), (dict(D=256), _lib.KVQ_EUNSUPPORTED), (dict(D=0), _lib.KVQ_EINVAL),
+    (dict(H=0), _lib.KVQ_EINVAL), (dict(bs=8), _lib.KVQ_EINVAL), (dict(bs=40), _lib.KVQ_EINVAL),
+    (dict(nb=0), _lib.KVQ_EINVAL)])
+def test_layout_rejects(lib, kw, status):
+    out = _lib.Layout()
+    d = desc(**kw)
+    assert lib.kvq_query_layout(ctypes.byref(d), ctypes.byref(out)) == status
+    assert lib.kvq_last_error().decode()
+    assert lib.kvq_query_layout(None, ctypes.byref(out)) == _lib.KVQ_EINVAL
+
+
+def test_write_validation(lib):
+    d = desc()
+    P = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
+    # neither / both slot mappings
+    assert lib.kvq_reshape_and_cache(ctypes.byref(d), P, P, 512, 512, None, None, 4, P, P, P, P, None) == _lib.KVQ_EINVAL
+    assert lib.kvq_reshape_and_cache(ctypes.byref(d), P, P, 512, 512, P, P, 4, P, P, P, P, None) == _lib.KVQ_EINVAL
+    # null plane
+    assert lib.kvq_reshape_and_cache(ctypes.byref(d), P, P, 512, 512, P, None, 4, None, P, P, P, None) == _lib.KVQ_EINVAL
+    # stride below Hkv*D
+    assert lib.kvq_reshape_and_cache(ctypes.byref(d), P, P, 100, 512, P, None, 4, P, P, P, P, None) == _lib.KVQ_EINVAL
+    assert "stride" in lib.kvq_last_error().decode()
+    # negative token count
+    assert lib.kvq_reshape_and_cache(ctypes.byref(d), P, P, 512, 512, P, None, -1, P, P, P, P, None) == _lib.KVQ_EINVAL
+    # zero tokens: OK and nothing launched
+    assert lib.kvq_reshape_and_cache(ctypes.byref(d), P, P, 512, 512, P, None, 0, P, P, P, P, None) == _lib.KVQ_OK
+
+
+def _decode(lib, d, **kw):
+    P = ctypes.c_void_p(4096)
+    a = dict(out=P, odt=0, q=P, B=2, Hq=8, kc=P, km=P, vc=P, vm=P, bt=P, bth=None, mb=4, sl=P, msl=200,
+             win=None, scale=0.125, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.kvq_paged_decode_attention(ctypes.byref(d), a["out"], a["odt"], a["q"], a["B"], a["Hq"],
+                                          a["kc"], a["km"], a["vc"], a["vm"], a["bt"], a["bth"], a["mb"],
+                                          a["sl"], a["msl"], a["win"], a["scale"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation(lib):
+    d = desc(H=4, bs=64)
+    P = ctypes.c_void_p(4096)
+    assert _decode(lib, d, Hq=6) == _lib.KVQ_EINVAL                 # GQA divisibility
+    assert "multiple" in lib.kvq_last_error().decode()
+    assert _decode(lib, d, Hq=4 * 17) == _lib.KVQ_EUNSUPPORTED      # group > 16
+    assert _decode(lib, d, bt=None, bth=None) == _lib.KVQ_EINVAL    # no table
+    assert _decode(lib, d, bt=P, bth=P) == _lib.KVQ_EINVAL          # both tables
+    assert _decode(lib, d, msl=4 * 64 + 1) == _lib.KVQ_EINVAL       # beyond the table
+    assert _decode(lib, d, odt=5) == _lib.KVQ_EINVAL
+    assert _decode(lib, d, scale=float("nan")) == _lib.KVQ_EINVAL
+    assert _decode(lib, d, q=None) == _lib.KVQ_EINVAL
+    assert _decode(lib, d, B=-1) == _lib.KVQ_EINVAL
+    assert _decode(lib, d, kc=None) == _lib.KVQ_EINVAL
+    assert _decode(lib, d, out=ctypes.c_void_p(4098)) == _lib.KVQ_EINVAL   # misaligned
+    assert _decode(lib, d, B=0) == _lib.KVQ_OK                      # nothing to do
+    need = ctypes.c_size_t()
+    assert lib.kvq_decode_workspace_size(ctypes.byref(d), 2, 8, 200, ctypes.byref(need)) == 0
+    if need.value:
+        assert _decode(lib, d, wsb=need.value - 1) == _lib.KVQ_ENOSPACE
+        assert _decode(lib, d, ws=None) == _lib.KVQ_EINVAL
+
+
+def test_workspace_size_grows_with_work(lib):
+    d = desc(H=8, bs=64)
+    sizes = []
+    for msl in (64, 4096, 131072):
+        n = ctypes.c_size_t()
+        assert lib.kvq_decode_workspace_size(ctypes.byref(d), 4, 32, msl, ctypes.byref(n)) == 0
+        sizes.append(n.value)
+        assert n.value % 16 == 0
+    assert sizes[0] <= sizes[1] <= sizes[2]
+
+
+def test_workspace_init_validation(lib):
+    assert lib.kvq_workspace_init(None, 0, None) == _lib.KVQ_OK
+    assert lib.kvq_workspace_init(None, 256, None) == _lib.KVQ_EINVAL
+    assert lib.kvq_workspace_init(ctypes.c_void_p(4096 + 16), 256, None) == _lib.KVQ_EINVAL
+
+
+def test_version(lib):
+    assert lib.kvq_version() >= 100
