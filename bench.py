@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized paged KV cache on one MI355X.
+
+A step is one decode step of the workload: quantize-on-write of the step's
+new token of every sequence (kvq_reshape_and_cache), then paged decode
+attention of every sequence over its whole cache (kvq_paged_decode_attention).
+The default workload is the INT8 per-token-head symmetric decode (batch 32,
+32 q / 8 kv heads, head_dim 128, block 64, seq_lens ~U[1024, 8192], 4 outlier
+channels x10); --config selects the others.  The cache is built once (untimed)
+and copied into enough replicas (>= 1.2 GB in total) that steps cycle through
+memory larger than the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  ``value`` is decode effective KV GB/s of the whole
+step: the algorithmic bytes decode reads (packed codes + fp32 scale/zero of
+attended tokens, plus queries, outputs and block-table entries) divided by
+the step time.  ``roofline`` is the decode kernel alone, timed with HIP
+events on the stream it runs on.  ``write`` reports quantize-write tokens/s
+on a whole-cache fill.  ``cpu_baseline`` times the oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import sub_byte_quantized_amd as kvq  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+DECODE_SRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc", "kvq_decode.hip")
+
+
+def sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def decode_algo_bytes(spec, case):
+    """Algorithmic bytes one decode launch reads and writes: codes + meta of
+    every attended token (positions inside the window, in non-evicted blocks,
+    below seq_len), the block-table entries walked, queries and outputs."""
+    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
+    M = 1 if spec.mode == 0 else 2
+    row = 2 * (P + 4 * M)
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    win = None if case.window is None else case.window.cpu().numpy()
+    bt = None if case.block_tables is None else case.block_tables.cpu().numpy()
+    bth = None if case.block_tables_headwise is None else case.block_tables_headwise.cpu().numpy()
+    tokens = 0
+    entries = 0
+    for b, L in enumerate(lens):
+        for h in range(spec.Hkv):
+            W = int(win[h]) if win is not None else 0
+            start = L - W if (W > 0 and L > W) else 0
+            row_ids = bth[b * spec.Hkv + h] if bth is not None else bt[b]
+            if L <= 0:
+                continue
+            j0, j1 = start // spec.bs, (L - 1) // spec.bs
+            ids = row_ids[j0:j1 + 1]
+            entries += len(ids)
+            pos = np.arange(j0 * spec.bs, (j1 + 1) * spec.bs)
+            keep = (pos >= start) & (pos < L) & np.repeat(ids >= 0, spec.bs)
+            tokens += int(keep.sum())
+    kv = tokens * row
+    q = spec.B * spec.Hq * spec.D * 2
+    out = spec.B * spec.Hq * spec.D * 4
+    return kv + q + out + 4 * entries + 4 * spec.B, kv, tokens
+
+
+def write_bytes_per_token(spec):
+    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
+    M = 1 if spec.mode == 0 else 2
+    slot = 8 * (spec.Hkv if spec.headwise else 1)
+    return spec.Hkv * 2 * (spec.D * 2 + P + 4 * M) + slot
+
+
+def build_workload(spec, dev):
+    case = synth.make_case(spec, dev)
+    d = kvq.CacheDesc(spec.mode, spec.D, spec.Hkv, spec.bs, case.tables.num_blocks, case.rot_signs)
+    planes = kvq.alloc_cache(d, dev, poison=True)
+    kvq.kvq_reshape_and_cache(d, case.k, case.v, *planes, slot_mapping=case.slot_mapping,
+                              slot_mapping_headwise=case.slot_mapping_headwise)
+    # the step's new tokens: the last position of each sequence
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    last = np.cumsum(lens) - 1
+    li = torch.as_tensor(last, device=dev)
+    new = dict(k=case.k[li].contiguous(), v=case.v[li].contiguous(),
+               sm=None if case.slot_mapping is None else case.slot_mapping[li].contiguous(),
+               smh=None if case.slot_mapping_headwise is None else case.slot_mapping_headwise[li].contiguous())
+    torch.cuda.synchronize()
+    return case, d, planes, new
+
+
+def time_events(fn, reps):
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def cpu_baseline(spec, case, planes, seconds):
+    """The oracle, as it stands, on a bounded sample of the same decode: as
+    many (sequence, kv head) pairs as fit in ``seconds``."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    host_planes = [p.cpu().numpy() for p in planes]
+    q = case.q.float().cpu().numpy()
+    lens = case.seq_lens.cpu().numpy()
+    bt = None if case.block_tables is None else case.block_tables.cpu().numpy()
+    bth = None if case.block_tables_headwise is None else case.block_tables_headwise.cpu().numpy()
+    win = None if case.window is None else case.window.cpu().numpy()
+    signs = None if case.rot_signs is None else case.rot_signs.cpu().numpy()
+    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
+    M = 1 if spec.mode == 0 else 2
+    r = np.random.default_rng(0)
+    order = [(int(b), int(h)) for b, h in zip(r.permutation(np.repeat(np.arange(spec.B), spec.Hkv)),
+                                                np.tile(np.arange(spec.Hkv), spec.B))]
+    done, nbytes = 0, 0
+    t0 = time.perf_counter()
+    for b, h in order:
+        oracle.decode_attention(q, lens, spec.mode, spec.D, spec.bs, spec.Hkv, *host_planes,
+                                case.softmax_scale, signs=signs, block_tables=bt,
+                                block_tables_headwise=bth, window=win, pairs=[(b, h)])
+        W = int(win[h]) if win is not None else 0
+        L = int(lens[b])
+        nbytes += (min(L, W) if W > 0 else L) * 2 * (P + 4 * M)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    # oracle write on a token sample
+    tw0 = time.perf_counter()
+    nt = 2048
+    k = case.k[:nt].float().cpu().numpy()
+    v = case.v[:nt].float().cpu().numpy()
+    for src in (k, v):
+        oracle.encode_rows(src.reshape(-1, spec.D), spec.mode, signs)
+    tw = time.perf_counter() - tw0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {spec.B * spec.Hkv} (sequence, kv head) decode pairs in {dt:.1f} s "
+                      f"(float64 attention over the GPU's stored planes); write: {nt} tokens in {tw:.2f} s",
+            "write_tokens_per_s": round(nt / tw, 1)}
+
+
+def load_traffic(name):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    if it is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        j = json.load(f)
+    if j.get("kernel_source_sha") != sha(DECODE_SRC):
+        return None
+    return j.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas cycled (0 = enough for 1.2 GB)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["step", "copy"], default="step",
+                    help="copy: time a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build measures the kernel "
+              "on one GPU's share; see DESIGN.md for how the path shards.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    kvq.load_library()
+
+    if args.mode == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms = time_events(lambda i: dst.copy_(src), max(1, args.steps))
+        print(json.dumps({"mode": "copy", "bytes": n, "ms": ms, "GBps": [2 * n / (m * 1e6) for m in ms]}))
+        return
+
+    spec = synth.CONFIGS[args.config]
+    t_setup = time.perf_counter()
+    case, d, planes, new = build_workload(spec, dev)
+    cache_bytes = sum(p.numel() * p.element_size() for p in planes)
+    R = args.replicas or max(1, min(16, math.ceil(max(1.2e9, 4 * MALL_BYTES) / cache_bytes)))
+    replicas = [planes] + [tuple(p.clone() for p in planes) for _ in range(R - 1)]
+    max_len = int(case.seq_lens.max().item())
+    ws = kvq.alloc_workspace(kvq.kvq_decode_workspace_size(d, spec.B, spec.Hq, max_len), dev)
+    out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
+    algo, kv_bytes, tokens = decode_algo_bytes(spec, case)
+    setup_s = time.perf_counter() - t_setup
+
+    def write(i):
+        rp = replicas[i % R]
+        kvq.kvq_reshape_and_cache(d, new["k"], new["v"], *rp, slot_mapping=new["sm"],
+                                  slot_mapping_headwise=new["smh"])
+
+    def decode(i):
+        rp = replicas[i % R]
+        kvq.kvq_paged_decode_attention(d, case.q, *rp, case.seq_lens, max_len,
+                                       block_tables=case.block_tables,
+                                       block_tables_headwise=case.block_tables_headwise,
+                                       window=case.window, softmax_scale=case.softmax_scale,
+                                       out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        write(i)
+        decode(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, events around each kernel
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        write(i)
+        ev[i][1].record()
+        decode(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    write_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    dec_avg = float(np.mean(dec_ms))
+
+    # quantize-write throughput: whole-cache fill into a scratch replica
+    T = case.k.shape[0]
+    scratch = replicas[-1]
+
+    def fill(i):
+        kvq.kvq_reshape_and_cache(d, case.k, case.v, *scratch, slot_mapping=case.slot_mapping,
+                                  slot_mapping_headwise=case.slot_mapping_headwise)
+
+    fill(0)
+    fill_ms = time_events(fill, 5)
+    fill_avg = float(np.mean(fill_ms))
+    wb = write_bytes_per_token(spec)
+
+    result = {
+        "metric": "decode-attn effective KV GB/s (% HBM peak); quantize-write tokens/s",
+        "value": round(algo / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {0: "int8 codes, bf16 mfma, fp32 accumulate", 1: "int4 codes, bf16 mfma, fp32 accumulate",
+                  2: "int2 codes, bf16 mfma, fp32 accumulate"}[spec.mode],
+        "data": "synthetic (seeded)",
+        "config": {"workload": spec.name, "batch": spec.B, "q_heads": spec.Hq, "kv_heads": spec.Hkv,
+                   "head_dim": spec.D, "block_size": spec.bs, "mode": ["int8_sym", "int4_asym", "int2_asym"][spec.mode],
+                   "rotation": spec.rotate, "tokens_cached": int(T), "kv_tokens_attended": tokens,
+                   "cache_replicas": R, "parallelism": "single GPU"},
+        "hbm_frac_of_step": round(algo / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel",
+                     "achieved": round(algo / (dec_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(algo / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(f"decode_{spec.name}_counters.json"),
+                     "algorithmic_bytes_per_launch": int(algo), "kv_bytes_per_launch": int(kv_bytes),
+                     "avg_launch_us": round(dec_avg * 1e3, 3)},
+        "write": {"step_write_us": round(float(np.mean(write_ms)) * 1e3, 3), "step_tokens": spec.B,
+                  "fill_tokens": int(T), "fill_us": round(fill_avg * 1e3, 2),
+                  "tokens_per_s": round(T / (fill_avg * 1e-3), 1),
+                  "bytes_per_token": wb, "GBps": round(T * wb / (fill_avg * 1e-3) / 1e9, 2),
+                  "frac": round(T * wb / (fill_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, case, planes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -80,7 +80,7 @@ typedef struct {
   int32_t mode;            /* kvq_mode */
   int32_t head_dim;        /* D: 64 or 128 */
   int32_t num_kv_heads;    /* Hkv >= 1 */
-  int32_t block_size;      /* tokens per block: a multiple of 16, 16..1024 */
+  int32_t block_size;      /* tokens per block: a power of two, 16..1024 */
   int64_t num_blocks;      /* physical blocks in each plane, >= 1 */
   /* (device) [head_dim] float32 of +1.0f / -1.0f, or NULL for no rotation.
    * With signs d, every K and V row x is stored as the codes of
@@ -133,11 +133,9 @@ kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t num_seq
                                      int32_t num_q_heads, int32_t max_seq_len,
                                      size_t* bytes /* host */);
 
-/* Zero a decode workspace once after allocating it (asynchronous on
- * `stream`).  Decode keeps per-(sequence, kv head) completion counters at
- * the start of the workspace; every decode call leaves them at zero again,
- * so a workspace needs this only once.  Calls that share a workspace must be
- * ordered (same stream or synchronized). */
+/* Zero a workspace (asynchronous on `stream`; 256-byte aligned, size a
+ * multiple of 16).  Decode does not need a zeroed workspace; this is a
+ * convenience for callers that want deterministic contents. */
 kvq_status kvq_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Paged decode attention (vLLM PR 40835 summary, 实现拆解 item 2: unpack,
@@ -159,7 +157,9 @@ kvq_status kvq_workspace_init(void* workspace, size_t workspace_bytes, void* str
  *   window       (device) int32 [Hkv], <= 0 = full context; or NULL
  *   softmax_scale  logits scale (usually 1/sqrt(D)); finite
  *   workspace    (device) >= kvq_decode_workspace_size bytes, 256-byte
- *                aligned, zeroed once by kvq_workspace_init
+ *                aligned (may be NULL when that size is 0); holds the
+ *                per-split partial results between the two kernels a call
+ *                launches when a sequence is split
  * Calls sharing one workspace must not overlap in time. */
 kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc,
                                       void* out, int32_t out_dtype,

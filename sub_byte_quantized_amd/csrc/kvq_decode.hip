@@ -4,37 +4,53 @@
 // per-token-head KV cache quantization for the Triton backend", 实现拆解
 // item 2: unpack, dequantize, attend), the head-wise block-table walk of
 // FastDeploy PR 7718 ("Optimize AppendAttention for discrete head-wise
-// block_idx": per-head rows, -1 entries skipped before any K/V address is
-// formed), and the decode-side dequantization inside attention described in
+// block_idx": per-head rows; -1 entries are skipped before any K/V address is
+// formed), and decode-side dequantization inside attention as described for
 // the vllm-ascend-quantized-kv-cache package (运行机制).
 //
-// What is computed, per (sequence b, q head hq, kv head h = hq / G):
-//   out = R^T softmax_j(scale * q'.k_hat_j) v_hat_j ,  q' = R q
-// where k_hat/v_hat are the stored codes dequantized in the rotated basis
-// (x_hat = c*s + z) and R the cache's rotation (identity without signs).
-// The dot products never dequantize element by element:
-//   q'.k_hat_t = s_t (q'.c_t) + z_t sum(q')
-//   sum_t w_t v_hat_t = sum_t (p_t s_t) c_t + (sum_t p_t z_t) 1
-// and both contractions run on MFMA (v_mfma_f32_16x16x32_bf16) with the codes
-// as exact bf16 integers 128 + c (built with one and-or per two codes), the
-// query and the weights split into bf16 hi + lo, and the 128 offset removed by
-// seeding the accumulators with -128 * (sum of the other operand).
+// Per (sequence b, q head hq, kv head h = hq / G) it computes
+//   out = R^T sum_j softmax_j(scale * q'.k_hat_j) v_hat_j ,   q' = R q,
+// k_hat / v_hat the stored codes dequantized in the rotated basis
+// (x_hat = c*s + z) and R the cache's rotation (identity without signs),
+// without dequantizing element by element:
+//   q'.k_hat_t      = s_t (q'.c_t) + z_t sum(q')
+//   sum_t w_t v_hat_t = sum_t (p_t s_t) c_t + (sum_t p_t z_t) 1 .
+// q'.c runs on v_mfma_i32_16x16x64_i8: the codes are int8 operands as they
+// are (INT8) or after two or three bit operations per 16 codes (INT4/INT2),
+// and q' is split into three int8 pieces (scale S: q' ~ S (a + b/2^7 +
+// c/2^14), |a| <= 127, |b|, |c| <= 64), so the products accumulate exactly in
+// int32.  sum_t w_t c_t runs on v_mfma_f32_16x16x32_bf16 with the codes as
+// exact bf16 integers 128 + c (one and-or per two codes) and w split into
+// bf16 hi + lo; one extra MFMA per d-tile, a constant -128 operand against the
+// weight sum in three bf16 pieces, cancels the 128 offset.
 //
-// Work split: one wave per (split, kv head, sequence).  A split is a run of
-// 32-position chunks of the sequence's active range (positions inside the
-// window).  Each chunk is two 16-token MFMA tiles; a tile lies in one cache
-// block (block_size is a multiple of 16) and is skipped when its block id is
-// negative or it lies outside [window start, seq_len).
-//   K pass  A = codes [16 tokens x 32 d]     lane (token, d-group)
-//           B = q'    [32 d x 16 heads]      lane (head,  d-group)
-//           C = scores[16 tokens x 16 heads] lane (head, 4 tokens)
-//   V pass  A = codes^T [16 d x 32 tokens]   lane (d-group, 8 tokens)
-//           B = w^T   [32 tokens x 16 heads] lane (head, 8 tokens): the K
-//                       pass's C registers of two tiles, no shuffle needed
-//           C = acc   [16 d x 16 heads]      lane (head, 4 d-slots)
-// Heads beyond G carry zeros.  With more than one split, every wave writes
-// (m, l, acc) to the workspace, and the last wave of a (sequence, kv head)
-// (device-scope counter) combines them, applies R^T and stores.
+// Layout of one 64-position tile (four 16-token sub-tiles sigma = 0..3).
+// MFMA columns n = 0..15 are (head g, phase phi) = (n / PHI, n % PHI), PHI the
+// largest power of two <= 16/G (at most 4), so G*PHI of the 16 columns carry
+// work instead of G.  Lane l has r = l % 16 and q = l / 16.
+//   K pass, K-tile tau (4/PHI per tile, sub-tiles tau*PHI .. +PHI-1):
+//     A  codes  [16 tokens x 64 k] int8  lane (token r of sub-tile
+//                                   tau*PHI + q*PHI/4, d-range q % (4/PHI))
+//     B  q' piece [64 k x 16 cols] int8  from LDS; zero unless the lane
+//                                   group's phase equals the column's phase
+//     C  scores [16 tokens x 16 cols] int32, lane (col r, tokens 4q..4q+3)
+//   V pass, k-steps u = 0, 1 (sub-tiles 2u, 2u+1):
+//     A  codes^T [16 d x 32 tokens]  lane (d-group r, tokens 16(2u+j/4)+4q+j%4)
+//     B  w^T     [32 tokens x 16 cols] the K pass's C registers, zero where the
+//                                   column's phase does not own the sub-tile
+//     C  acc     [16 d x 16 cols]   lane (col r, d-slots 4q..4q+3)
+//   Columns of one head are summed at the end (phases partition the tokens).
+//
+// Work split: one 256-thread workgroup (4 waves) per (split, kv head,
+// sequence); a split is a run of tiles of the sequence's active range (the
+// window), interleaved over the waves.  Each wave keeps its own online-softmax
+// state, issues the next tile's loads before computing the current one, and
+// rescales its accumulators only when a head's running maximum grows by more
+// than 2^8.  The workgroup combines its waves in LDS; with one split it
+// finishes (normalize, R^T, store), otherwise it writes (m, l, acc) to the
+// workspace and decode_reduce_kernel, launched next on the same stream,
+// combines the splits and finishes (stream order makes the partials visible;
+// no device-scope fence or atomic is needed).
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -44,13 +60,34 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr uint32_t kMagic = 0x43004300u;  // bf16 128.0 in both halves
+constexpr float kRescale = 8.0f;          // log2 of the growth that forces a rescale
+constexpr int kWaves = 4;
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x4_t mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a), __builtin_bit_cast(i32x4_t, b),
+                                               c, 0, 0, 0);
+}
+
+// (x & m) | (c & ~m).  With m and c held in VGPRs this is one v_bitop3_b32
+// (with literal or scalar constants the compiler emits an and plus an or).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | (c & ~m); }
+
+// Copy a wave-uniform value into a VGPR the optimizer cannot fold back into a
+// scalar or a literal.  Used once per kernel for the and_or() constants; the
+// result only feeds ordinary VALU instructions.
+__device__ __forceinline__ uint32_t to_vgpr(uint32_t x) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "s"(x));
+  return r;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -60,81 +97,81 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Pack two exact small integers held as floats into a bf16 pair (truncation
-// of the low mantissa bits is exact for values < 256).
+// Two exact small integers held as floats -> bf16 pair (the dropped mantissa
+// bits are zero for values < 256).
 __device__ __forceinline__ uint32_t pack_exact(float a, float b) {
   return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
-// d index held by MFMA k-slot j of lane group kg in k-step k (K pass); the
-// same map lays out the query operand.  It follows the unpacking order below.
-template <int MODE, int D>
-__device__ __forceinline__ int kmap(int kg, int k, int j) {
-  const int base = kg * (D / 4);
-  if constexpr (MODE == 1) return base + 8 * k + (j >> 1) + 4 * (j & 1);
-  else if constexpr (MODE == 2) return base + 16 * (k >> 1) + 4 * (k & 1) + (j >> 1) + 8 * (j & 1);
-  else return base + 8 * k + j;
-}
-
-// Number of dwords a lane loads from one K row (P/4 bytes) and from one V row
-// (P/16 bytes, at least one dword register).
-template <int MODE, int D> struct Geo {
-  static constexpr int P = row_bytes(MODE, D);
-  static constexpr int KW = P / 16;              // dwords of K codes per lane per tile
-  static constexpr int VB = P / 16;              // bytes of V codes per lane per token
+template <int MODE, int D, int PHI>
+struct Geo {
+  static constexpr int P = row_bytes(MODE, D);   // packed bytes per row
+  static constexpr int M = mode_meta(MODE);      // meta floats per row
+  static constexpr int NKT = 4 / PHI;            // K-tiles per 64-position tile
+  static constexpr int SUBD = D * PHI / 4;       // d values per lane group per K-tile
+  static constexpr int KS = SUBD / 16;           // int8 MFMA k-steps per K-tile
+  static constexpr int KB = SUBD * mode_bits(MODE) / 8;  // K bytes a lane loads per K-tile
+  static constexpr int KW = KB / 4;              // ... in dwords
+  static constexpr int KSW = KW / KS;            // ... per k-step
+  static constexpr int VB = P / 16;              // V bytes a lane loads per token
   static constexpr int VW = VB >= 4 ? VB / 4 : 1;
-  static constexpr int KSTEPS = D / 32;
-  static constexpr int DT = D / 16;              // d-tiles of the V pass
-  static constexpr int M = mode_meta(MODE);
+  static constexpr int DT = D / 16;              // V-pass d-tiles
 };
 
-// K-pass A operand: exact bf16 (128 + c) of the 8 codes of k-step k.
-template <int MODE, int D>
-__device__ __forceinline__ u32x4_t unpack_k(const uint32_t* kc, int k) {
+// d held by byte j (0..15) of the int8 operand of k-step s for lane-group
+// d-range `sub` (K pass); the query pieces in LDS are laid out in this order.
+template <int MODE, int D, int PHI>
+__device__ __forceinline__ int kmap(int sub, int s, int j) {
+  const int base = sub * Geo<MODE, D, PHI>::SUBD + 16 * s;
+  if constexpr (MODE == 1) return base + 8 * ((j >> 2) >> 1) + 2 * (j & 3) + ((j >> 2) & 1);
+  else if constexpr (MODE == 2) return base + 4 * (j & 3) + (j >> 2);
+  else return base + j;
+}
+
+// K-pass int8 A operand of k-step s (16 codes) from the lane's K-tile dwords.
+template <int MODE, int KSW>
+__device__ __forceinline__ u32x4_t unpack_k(const uint32_t* kc, int s, uint32_t m4, uint32_t m2) {
   u32x4_t a;
   if constexpr (MODE == 1) {
-    const uint32_t x = kc[k];
-    a[0] = (x & 0x000F000Fu) | kMagic;
-    a[1] = ((x >> 4) & 0x000F000Fu) | kMagic;
-    a[2] = ((x >> 8) & 0x000F000Fu) | kMagic;
-    a[3] = ((x >> 12) & 0x000F000Fu) | kMagic;
+    const uint32_t x0 = kc[2 * s], x1 = kc[2 * s + 1];
+    a[0] = x0 & m4;
+    a[1] = (x0 >> 4) & m4;
+    a[2] = x1 & m4;
+    a[3] = (x1 >> 4) & m4;
   } else if constexpr (MODE == 2) {
-    const uint32_t x = kc[k >> 1] >> (8 * (k & 1));
-    a[0] = (x & 0x00030003u) | kMagic;
-    a[1] = ((x >> 2) & 0x00030003u) | kMagic;
-    a[2] = ((x >> 4) & 0x00030003u) | kMagic;
-    a[3] = ((x >> 6) & 0x00030003u) | kMagic;
+    const uint32_t x = kc[s];
+    a[0] = x & m2;
+    a[1] = (x >> 2) & m2;
+    a[2] = (x >> 4) & m2;
+    a[3] = (x >> 6) & m2;
   } else {
-    const uint32_t x0 = kc[2 * k] ^ 0x80808080u, x1 = kc[2 * k + 1] ^ 0x80808080u;
-    a[0] = pack_exact((float)(x0 & 0xffu), (float)((x0 >> 8) & 0xffu));
-    a[1] = pack_exact((float)((x0 >> 16) & 0xffu), (float)(x0 >> 24));
-    a[2] = pack_exact((float)(x1 & 0xffu), (float)((x1 >> 8) & 0xffu));
-    a[3] = pack_exact((float)((x1 >> 16) & 0xffu), (float)(x1 >> 24));
+    a[0] = kc[4 * s]; a[1] = kc[4 * s + 1]; a[2] = kc[4 * s + 2]; a[3] = kc[4 * s + 3];
   }
   return a;
 }
 
-// V-pass A operand for d-tile dt: token slots 0..7 (pairs 2p, 2p+1) of the
-// lane's d = d-group*(D/16) + dt, as exact bf16 (128 + c).
-template <int MODE, int D, int DTI>
-__device__ __forceinline__ u32x4_t unpack_v(const uint32_t (*vc)[Geo<MODE, D>::VW]) {
+// V-pass A operand for d-tile DTI: token slots j = 0..7 (pairs 2p, 2p+1) of
+// the lane's d = r*(D/16) + DTI, from vc[j][*].
+template <int MODE, int VW, int DTI>
+__device__ __forceinline__ u32x4_t unpack_v(const uint32_t (*vc)[VW], uint32_t magic, uint32_t n4,
+                                            uint32_t n2) {
   u32x4_t a;
   if constexpr (MODE == 1) {
-    constexpr int b = DTI >> 1;
-    constexpr uint32_t sel = (uint32_t)b | (0x0Cu << 8) | ((uint32_t)(4 + b) << 16) | (0x0Cu << 24);
+    constexpr uint32_t b = DTI >> 1;
+    constexpr uint32_t sel = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint32_t y = __builtin_amdgcn_perm(vc[2 * p + 1][0], vc[2 * p][0], sel);
-      a[p] = (((DTI & 1) ? (y >> 4) : y) & 0x000F000Fu) | kMagic;
+      a[p] = and_or((DTI & 1) ? (y >> 4) : y, n4, magic);
     }
   } else if constexpr (MODE == 2) {
-    constexpr int b = DTI >> 2;
+    constexpr uint32_t b = DTI >> 2;
     constexpr int sh = 2 * (DTI & 3);
-    constexpr uint32_t sel = (uint32_t)b | (0x0Cu << 8) | ((uint32_t)(4 + b) << 16) | (0x0Cu << 24);
+    constexpr uint32_t sel = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint32_t y = __builtin_amdgcn_perm(vc[2 * p + 1][0], vc[2 * p][0], sel);
-      a[p] = ((y >> sh) & 0x00030003u) | kMagic;
+      a[p] = and_or(sh ? (y >> sh) : y, n2, magic);
     }
   } else {
     constexpr int w = DTI >> 2;
@@ -148,32 +185,30 @@ __device__ __forceinline__ u32x4_t unpack_v(const uint32_t (*vc)[Geo<MODE, D>::V
   return a;
 }
 
-template <int MODE, int D, int DTI>
+template <int MODE, int VW, int DT, int DTI>
 struct VPass {
-  __device__ __forceinline__ static void run(const uint32_t (*vc)[Geo<MODE, D>::VW], u32x4_t bhi,
-                                             u32x4_t blo, f32x4_t* acc) {
-    const u32x4_t a = unpack_v<MODE, D, DTI>(vc);
-    acc[DTI] = mfma(a, bhi, acc[DTI]);
-    acc[DTI] = mfma(a, blo, acc[DTI]);
-    VPass<MODE, D, DTI + 1>::run(vc, bhi, blo, acc);
+  __device__ __forceinline__ static void run(const uint32_t (*vc)[VW], u32x4_t bh, u32x4_t bl,
+                                             f32x4_t* acc, uint32_t magic, uint32_t n4, uint32_t n2) {
+    const u32x4_t a = unpack_v<MODE, VW, DTI>(vc, magic, n4, n2);
+    acc[DTI] = mfma(a, bh, acc[DTI]);
+    acc[DTI] = mfma(a, bl, acc[DTI]);
+    VPass<MODE, VW, DT, DTI + 1>::run(vc, bh, bl, acc, magic, n4, n2);
   }
 };
-template <int MODE, int D>
-struct VPass<MODE, D, D / 16> {
-  __device__ __forceinline__ static void run(const uint32_t (*)[Geo<MODE, D>::VW], u32x4_t,
-                                             u32x4_t, f32x4_t*) {}
+template <int MODE, int VW, int DT>
+struct VPass<MODE, VW, DT, DT> {
+  __device__ __forceinline__ static void run(const uint32_t (*)[VW], u32x4_t, u32x4_t, f32x4_t*, uint32_t,
+                                             uint32_t, uint32_t) {}
 };
 
 template <int N>
 __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src) {
-  if constexpr (N == 32) {
-    const uint4 a = reinterpret_cast<const uint4*>(src)[0];
-    const uint4 b = reinterpret_cast<const uint4*>(src)[1];
-    dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
-    dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
-  } else if constexpr (N == 16) {
-    const uint4 a = *reinterpret_cast<const uint4*>(src);
-    dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int i = 0; i < N / 16; ++i) {
+      const uint4 a = reinterpret_cast<const uint4*>(src)[i];
+      dst[4 * i] = a.x; dst[4 * i + 1] = a.y; dst[4 * i + 2] = a.z; dst[4 * i + 3] = a.w;
+    }
   } else if constexpr (N == 8) {
     const uint2 a = *reinterpret_cast<const uint2*>(src);
     dst[0] = a.x; dst[1] = a.y;
@@ -186,356 +221,572 @@ __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src) {
   }
 }
 
-template <int N>
-__device__ __forceinline__ void zero_words(uint32_t* dst) {
+// Rows and validity of one tile's four 16-token sub-tiles (wave-uniform).
+struct TileInfo {
+  int pos0;                 // first position of the tile
+  int row0, row1, row2, row3;  // plane row of the sub-tile's first token; 0 when invalid
+  uint32_t valid;           // bit sigma: sub-tile has a block and meets [start, L)
+};
+
+__device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int tile, int te, int L, int start,
+                                              int bs_log2, int hkv, int h) {
+  TileInfo t;
+  t.pos0 = tile * 64;
+  t.valid = 0;
+  int row[4];
 #pragma unroll
-  for (int i = 0; i < N; ++i) dst[i] = 0u;
+  for (int s = 0; s < 4; ++s) {
+    const int pos = t.pos0 + 16 * s;
+    const bool in = tile < te && pos < L && pos + 15 >= start;
+    const int id = __builtin_amdgcn_readfirstlane(ids[in ? (pos >> bs_log2) - blk0 : 0]);
+    const bool ok = in && id >= 0;
+    t.valid |= ok ? 1u << s : 0u;
+    row[s] = ok ? ((id * hkv + h) << bs_log2) + (pos & ((1 << bs_log2) - 1)) : 0;
+  }
+  t.row0 = row[0]; t.row1 = row[1]; t.row2 = row[2]; t.row3 = row[3];
+  return t;
 }
 
-// In-lane + cross-lane (xor 16, xor 32) FWHT over the D values of one head
-// held as v[e], e = 0..D/4-1, by the four lanes l%16 = g, l/16 = q, with
-// d = q*(D/4) + e; then d .* / sqrt(D).  Only the orthogonal map matters here
-// (tolerance-checked), not a particular rounding sequence.
-template <int D>
-__device__ __forceinline__ void inverse_rotate(float* v, int q, const float* signs, float inv_sqrt_d) {
-  constexpr int E = D / 4;
-#pragma unroll
-  for (int hh = 1; hh < E; hh <<= 1) {
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      if (!(i & hh)) {
-        const float a = v[i], b = v[i + hh];
-        v[i] = a + b;
-        v[i + hh] = a - b;
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 16; m <= 32; m <<= 1) {
-    const bool upper = ((q * 16) & m) != 0;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const float o = __shfl_xor(v[i], m);
-      v[i] = upper ? (o - v[i]) : (v[i] + o);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < E; ++i) v[i] = v[i] * signs[q * E + i] * inv_sqrt_d;
+// Row of sub-tile sigma (sigma may differ per lane).  An invalid sub-tile
+// reads row 0, which is always addressable; its data is masked out of the
+// scores and gets zero weight.
+__device__ __forceinline__ int pick_row(const TileInfo& t, int sigma) {
+  return sigma == 0 ? t.row0 : (sigma == 1 ? t.row1 : (sigma == 2 ? t.row2 : t.row3));
 }
 
-template <int D>
-__device__ __forceinline__ void store_out(const DecodeParams& p, int64_t orow, int q, const float* v) {
-  constexpr int E = D / 4;
-  if (p.out_bf16) {
-    uint32_t* o = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.out) + orow * D + q * E);
+template <int MODE, int D, int PHI>
+struct Buf {
+  using Gm = Geo<MODE, D, PHI>;
+  uint32_t k[Gm::NKT][Gm::KW];
+  uint32_t v[16][Gm::VW];
+  float km[Gm::NKT][4 * Gm::M];
+  float vm[Gm::NKT][4 * Gm::M];
+};
+
+template <int MODE, int D, int PHI>
+__device__ __forceinline__ void issue_loads(Buf<MODE, D, PHI>& b, const TileInfo& t, const DecodeParams& p,
+                                            int r, int q, int phi_col) {
+  using Gm = Geo<MODE, D, PHI>;
+  constexpr int P = Gm::P, M = Gm::M;
+  const int phi_grp = q * PHI / 4;          // phase of this lane group (K pass)
+  const int sub = q % (4 / PHI);            // d-range of this lane group (K pass)
 #pragma unroll
-    for (int i = 0; i < E / 8; ++i) {
-      uint4 w;
-      w.x = pack_bf16(v[8 * i + 0], v[8 * i + 1]);
-      w.y = pack_bf16(v[8 * i + 2], v[8 * i + 3]);
-      w.z = pack_bf16(v[8 * i + 4], v[8 * i + 5]);
-      w.w = pack_bf16(v[8 * i + 6], v[8 * i + 7]);
-      reinterpret_cast<uint4*>(o)[i] = w;
+  for (int tau = 0; tau < Gm::NKT; ++tau) {
+    const int kr = pick_row(t, tau * PHI + phi_grp) + r;
+    load_bytes<Gm::KB>(b.k[tau], p.k_codes + (int64_t)kr * P + sub * Gm::KB);
+    const int mr = pick_row(t, tau * PHI + phi_col) + 4 * q;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const float4 a = reinterpret_cast<const float4*>(p.k_meta + (int64_t)mr * M)[i];
+      const float4 c = reinterpret_cast<const float4*>(p.v_meta + (int64_t)mr * M)[i];
+      b.km[tau][4 * i] = a.x; b.km[tau][4 * i + 1] = a.y; b.km[tau][4 * i + 2] = a.z; b.km[tau][4 * i + 3] = a.w;
+      b.vm[tau][4 * i] = c.x; b.vm[tau][4 * i + 1] = c.y; b.vm[tau][4 * i + 2] = c.z; b.vm[tau][4 * i + 3] = c.w;
     }
-  } else {
-    float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + orow * D + q * E);
+  }
+  const int voff = 4 * q * P + r * Gm::VB;
 #pragma unroll
-    for (int i = 0; i < E / 4; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  for (int s = 0; s < 4; ++s) {
+    const int row = s == 0 ? t.row0 : (s == 1 ? t.row1 : (s == 2 ? t.row2 : t.row3));
+    const uint8_t* base = p.v_codes + (int64_t)row * P;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_bytes<Gm::VB>(b.v[4 * s + i], base + voff + i * P);
   }
 }
 
-template <int MODE, int D, bool ROT>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
-  using Gm = Geo<MODE, D>;
-  constexpr int P = Gm::P;
+struct WaveState {
+  float m;     // running reference maximum (log2 units) of the lane's head
+  float l;     // lane partial sum of p
+  float z;     // lane partial sum of p * z_V
+};
+
+struct LaneConst {
+  const int8_t* qa;    // query pieces of this lane's B operand rows (LDS)
+  const int8_t* qb;
+  const int8_t* qc;
+  float qs;            // piece scale S of the column's head
+  float q1;            // sum of the column head's represented q'
+  int q;
+  int phi_col;
+  bool head_ok;
+  uint32_t magic, n4, n2;   // bf16 128.0 pair; nibble and crumb masks of a bf16 pair
+};
+
+template <int MODE, int D, int PHI>
+__device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const TileInfo& t, WaveState& st,
+                                             f32x4_t* acc, const LaneConst& lc, int L, int start) {
+  using Gm = Geo<MODE, D, PHI>;
   constexpr int M = Gm::M;
-  constexpr int KS = Gm::KSTEPS;
-  constexpr int E = D / 4;            // output values per lane
-  __shared__ float qs[16][D];
+  const int q = lc.q, phi_col = lc.phi_col;
+  // ---- K pass: int32 (a, b, c) dot products of the query pieces with the codes
+  float sc[Gm::NKT][4];
+#pragma unroll
+  for (int tau = 0; tau < Gm::NKT; ++tau) {
+    i32x4_t ia = {0, 0, 0, 0}, ib = {0, 0, 0, 0}, ic = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < Gm::KS; ++s) {
+      const u32x4_t a = unpack_k<MODE, Gm::KSW>(b.k[tau], s, 0x0F0F0F0Fu, 0x03030303u);
+      const uint4 xa = *reinterpret_cast<const uint4*>(lc.qa + 16 * s);
+      const uint4 xb = *reinterpret_cast<const uint4*>(lc.qb + 16 * s);
+      const uint4 xc = *reinterpret_cast<const uint4*>(lc.qc + 16 * s);
+      ia = mfma_i8(a, u32x4_t{xa.x, xa.y, xa.z, xa.w}, ia);
+      ib = mfma_i8(a, u32x4_t{xb.x, xb.y, xb.z, xb.w}, ib);
+      ic = mfma_i8(a, u32x4_t{xc.x, xc.y, xc.z, xc.w}, ic);
+    }
+    const int sg = tau * PHI + phi_col;
+    const bool tv = lc.head_ok && ((t.valid >> sg) & 1u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = t.pos0 + 16 * sg + 4 * q + i;
+      const float raw = (float)((ia[i] << 7) + ib[i]) * 0.0078125f + (float)ic[i] * 6.103515625e-05f;
+      const float s = M == 2 ? b.km[tau][2 * i] : b.km[tau][i];
+      const float z = M == 2 ? b.km[tau][2 * i + 1] : 0.0f;
+      const float v = (s * lc.qs) * raw + z * lc.q1;
+      sc[tau][i] = (tv && pos < L && pos >= start) ? v : kNegInf;
+    }
+  }
+  // ---- tile maximum of the head: lane values, lane groups q, phases of the head
+  float tmax = kNegInf;
+#pragma unroll
+  for (int tau = 0; tau < Gm::NKT; ++tau)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[tau][i]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+#pragma unroll
+  for (int m = 1; m < PHI; m <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, m));
+  if (__any(tmax > st.m + kRescale)) {
+    const float mn = fmaxf(st.m, tmax);
+    const float alpha = mn == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
+    st.m = mn;
+    st.l *= alpha;
+    st.z *= alpha;
+#pragma unroll
+    for (int i = 0; i < Gm::DT; ++i) acc[i] *= alpha;
+  }
+  const float mu = st.m == kNegInf ? 0.0f : st.m;
+
+  // ---- probabilities and V weights w = p * s_V as bf16 hi + lo pairs
+  uint32_t wh[Gm::NKT][2], wl[Gm::NKT][2];
+  float wsum = 0.0f;
+#pragma unroll
+  for (int tau = 0; tau < Gm::NKT; ++tau) {
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      float w2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float pr = __builtin_amdgcn_exp2f(sc[tau][i + e] - mu);
+        const float sv = M == 2 ? b.vm[tau][2 * (i + e)] : b.vm[tau][i + e];
+        const float zv = M == 2 ? b.vm[tau][2 * (i + e) + 1] : 0.0f;
+        const bool live = pr > 0.0f;
+        st.l += pr;
+        st.z += live ? pr * zv : 0.0f;
+        w2[e] = live ? pr * sv : 0.0f;
+      }
+      const uint32_t hi = pack_bf16(w2[0], w2[1]);
+      const uint32_t lo = pack_bf16(w2[0] - bf16_lo(hi), w2[1] - bf16_hi(hi));
+      wh[tau][i / 2] = hi;
+      wl[tau][i / 2] = lo;
+      wsum += (bf16_lo(hi) + bf16_lo(lo)) + (bf16_hi(hi) + bf16_hi(lo));
+    }
+  }
+  // ---- offset: acc -= 128 * (sum of the column's weights), as one MFMA per
+  // d-tile against the sum split into three bf16 pieces
+  wsum += __shfl_xor(wsum, 16);
+  wsum += __shfl_xor(wsum, 32);
+  {
+    const __bf16 w0 = (__bf16)wsum;
+    const float r1 = wsum - (float)w0;
+    const __bf16 w1 = (__bf16)r1;
+    const __bf16 w2 = (__bf16)(r1 - (float)w1);
+    const uint32_t d0 = q == 0 ? ((uint32_t)__builtin_bit_cast(uint16_t, w0) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16)) : 0u;
+    const uint32_t d1 = q == 0 ? (uint32_t)__builtin_bit_cast(uint16_t, w2) : 0u;
+    const u32x4_t bw = {d0, d1, 0u, 0u};
+    const u32x4_t neg128 = {0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u};
+#pragma unroll
+    for (int i = 0; i < Gm::DT; ++i) acc[i] = mfma(neg128, bw, acc[i]);
+  }
+
+  // ---- V pass: k-step u covers sub-tiles 2u (slots 0..3) and 2u+1 (slots 4..7)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    u32x4_t bh, bl;
+    if constexpr (PHI == 1) {
+      bh = u32x4_t{wh[2 * u][0], wh[2 * u][1], wh[2 * u + 1][0], wh[2 * u + 1][1]};
+      bl = u32x4_t{wl[2 * u][0], wl[2 * u][1], wl[2 * u + 1][0], wl[2 * u + 1][1]};
+    } else {
+      // the lane owns sub-tile 2u + phi_col % 2 of this k-step (PHI == 2: from
+      // K-tile u; PHI == 4: only when phi_col / 2 == u, from its one K-tile)
+      const int tau = PHI == 2 ? u : 0;
+      const bool own = PHI == 2 ? true : (phi_col >> 1) == u;
+      const bool first = (phi_col & 1) == 0;
+      const uint32_t h0 = own ? wh[tau][0] : 0u, h1 = own ? wh[tau][1] : 0u;
+      const uint32_t l0 = own ? wl[tau][0] : 0u, l1 = own ? wl[tau][1] : 0u;
+      bh = first ? u32x4_t{h0, h1, 0u, 0u} : u32x4_t{0u, 0u, h0, h1};
+      bl = first ? u32x4_t{l0, l1, 0u, 0u} : u32x4_t{0u, 0u, l0, l1};
+    }
+    VPass<MODE, Gm::VW, Gm::DT, 0>::run(b.v + 8 * u, bh, bl, acc, lc.magic, lc.n4, lc.n2);
+  }
+}
+
+// FWHT of `rows` rows of D floats in LDS (Sylvester, natural order), all
+// threads of the workgroup; ends with a barrier.
+template <int D>
+__device__ __forceinline__ void lds_fwht(float (*x)[D], int rows, int tid) {
+  for (int hh = 1; hh < D; hh <<= 1) {
+    for (int e = tid; e < rows * (D / 2); e += 64 * kWaves) {
+      const int g = e / (D / 2), k = e - g * (D / 2);
+      const int i = (k / hh) * 2 * hh + (k % hh);
+      const float a = x[g][i], bb = x[g][i + hh];
+      x[g][i] = a + bb;
+      x[g][i + hh] = a - bb;
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_rows(const DecodeParams& p, float (*fin)[D], int G, int64_t orow0,
+                                           int tid, bool rot) {
+  for (int e = tid; e < G * D; e += 64 * kWaves) {
+    const int g = e / D, d = e - g * D;
+    float v = fin[g][d];
+    if (rot) v = v * p.signs[d] * p.inv_sqrt_d;
+    if (p.out_bf16)
+      reinterpret_cast<__bf16*>(p.out)[(orow0 + g) * D + d] = (__bf16)v;
+    else
+      reinterpret_cast<float*>(p.out)[(orow0 + g) * D + d] = v;
+  }
+}
+
+template <int D>
+struct Smem {
+  union {
+    struct {
+      int8_t qa[17][D];     // query pieces in k-slot order; row 16 = zeros
+      int8_t qb[17][D];
+      int8_t qc[17][D];
+      float qf[16][D];      // prologue scratch: R q * scale * log2(e)
+    } pro;
+    struct {
+      float acc[kWaves][16][D];
+      float ml[kWaves][16][2];
+    } comb;
+    float fin[16][D];
+  };
+  float qs[16];
+  float q1[16];
+  int32_t ids[kMaxSplitBlocks];   // block ids of the split's range
+};
+
+template <int MODE, int D, int PHI, bool ROT>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  using Gm = Geo<MODE, D, PHI>;
+  __shared__ Smem<D> sm;
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int r16 = lane & 15;
-  const int kg = lane >> 4;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int q = lane >> 4;
   const int G = p.group;
   const int hkv = p.hkv;
-  const int bs = p.block_size;
 
   const int L = p.seq_lens[b];
   const int W = p.window ? p.window[h] : 0;
   const int start = (W > 0 && L > W) ? L - W : 0;
-  const int c0 = start / kChunk;
-  const int c1 = (L + kChunk - 1) / kChunk;
-  const int n_chunks = L > 0 ? c1 - c0 : 0;
-  const int cps = p.chunks_per_split;
-  const int n_splits = n_chunks > 0 ? (n_chunks + cps - 1) / cps : 1;
+  const int t0 = start / 64;
+  const int t1 = (L + 63) / 64;
+  const int n_tiles = L > 0 ? t1 - t0 : 0;
+  const int tps = p.chunks_per_split;   // tiles per split
+  const int n_splits = n_tiles > 0 ? (n_tiles + tps - 1) / tps : 1;
   if (split >= n_splits) return;
-  const int cb = c0 + split * cps;
-  const int ce = min(c1, cb + cps);
+  const int tb = t0 + split * tps;
+  const int te = min(t1, tb + tps);
   const int32_t* trow = p.tables + (int64_t)(p.headwise ? b * hkv + h : b) * p.max_blocks;
+  const int64_t orow0 = (int64_t)b * p.hq + h * G;
 
-  // ---- query prologue: q'' = R q * scale * log2(e), split into bf16 hi + lo
-  for (int e = lane; e < G * D; e += 64) {
+  // ---- block ids of the split's positions [64 tb, min(64 te, L)) into LDS
+  const int blk0 = (tb * 64) >> p.block_size_log2;
+  {
+    const int last_pos = min(te * 64, L) - 1;
+    const int n_ids = last_pos >= tb * 64 ? (last_pos >> p.block_size_log2) - blk0 + 1 : 0;
+    for (int i = tid; i < n_ids; i += 64 * kWaves) sm.ids[i] = trow[blk0 + i];
+    if (n_ids == 0 && tid == 0) sm.ids[0] = -1;
+  }
+
+  // ---- prologue: q' = R q * scale * log2(e), then int8 pieces in k-slot order
+  for (int e = tid; e < G * D; e += 64 * kWaves) {
     const int g = e / D, d = e - g * D;
-    float v = __uint_as_float((uint32_t)p.q[((int64_t)b * p.hq + h * G + g) * D + d] << 16);
+    float v = __uint_as_float((uint32_t)p.q[(orow0 + g) * D + d] << 16);
     if constexpr (ROT) v *= p.signs[d];
-    qs[g][d] = v;
+    sm.pro.qf[g][d] = v;
   }
   __syncthreads();
-  if constexpr (ROT) {
-    for (int hh = 1; hh < D; hh <<= 1) {
-      for (int e = lane; e < G * (D / 2); e += 64) {
-        const int g = e / (D / 2), k = e - g * (D / 2);
-        const int i = (k / hh) * 2 * hh + (k % hh);
-        const float a = qs[g][i], bb = qs[g][i + hh];
-        qs[g][i] = a + bb;
-        qs[g][i + hh] = a - bb;
-      }
-      __syncthreads();
-    }
-  }
+  if constexpr (ROT) lds_fwht<D>(sm.pro.qf, G, tid);
   const float qmul = ROT ? p.qscale * p.inv_sqrt_d : p.qscale;
-  u32x4_t bqh[KS], bql[KS];
-  float q1 = 0.0f;
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float v0 = 0.0f, v1 = 0.0f;
-      if (r16 < G) {
-        v0 = qs[r16][kmap<MODE, D>(kg, k, 2 * jj)] * qmul;
-        v1 = qs[r16][kmap<MODE, D>(kg, k, 2 * jj + 1)] * qmul;
+  for (int g = wave; g < 17; g += kWaves) {
+    if (g >= G) {
+      for (int pos = lane; pos < D; pos += 64) {
+        sm.pro.qa[g][pos] = 0; sm.pro.qb[g][pos] = 0; sm.pro.qc[g][pos] = 0;
       }
-      const uint32_t hi = pack_bf16(v0, v1);
-      const uint32_t lo = pack_bf16(v0 - bf16_lo(hi), v1 - bf16_hi(hi));
-      bqh[k][jj] = hi;
-      bql[k][jj] = lo;
-      q1 += (bf16_lo(hi) + bf16_lo(lo)) + (bf16_hi(hi) + bf16_hi(lo));
+      continue;
+    }
+    float mx = 0.0f;
+    for (int d = lane; d < D; d += 64) mx = fmaxf(mx, fabsf(sm.pro.qf[g][d] * qmul));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    const float S = mx / 127.0f;
+    const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
+    float sa = 0.0f, sb = 0.0f, sc = 0.0f;
+    for (int pos = lane; pos < D; pos += 64) {
+      const int sub = pos / Gm::SUBD, rem = pos - sub * Gm::SUBD;
+      const float v = sm.pro.qf[g][kmap<MODE, D, PHI>(sub, rem >> 4, rem & 15)] * qmul;
+      const float t = fminf(fmaxf(v * invS, -127.0f), 127.0f);
+      const float a = __builtin_rintf(t);
+      const float r1 = (t - a) * 128.0f;
+      const float bq = __builtin_rintf(r1);
+      const float cq = __builtin_rintf((r1 - bq) * 128.0f);
+      sm.pro.qa[g][pos] = (int8_t)a;
+      sm.pro.qb[g][pos] = (int8_t)bq;
+      sm.pro.qc[g][pos] = (int8_t)cq;
+      sa += a; sb += bq; sc += cq;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      sa += __shfl_xor(sa, m);
+      sb += __shfl_xor(sb, m);
+      sc += __shfl_xor(sc, m);
+    }
+    if (lane == 0) {
+      sm.qs[g] = S;
+      sm.q1[g] = S * (sa + sb * 0.0078125f + sc * 6.103515625e-05f);
     }
   }
-  q1 += __shfl_xor(q1, 16);
-  q1 += __shfl_xor(q1, 32);
-  const float koff = -128.0f * q1;
+  __syncthreads();
 
-  // ---- main loop over chunks
-  float m_run = kNegInf;
-  float l_run = 0.0f;   // per-lane partial sum of p
-  float z_run = 0.0f;   // per-lane partial sum of p * z_V
+  // ---- per-lane constants
+  LaneConst lc;
+  const int g_col = r / PHI;            // head of this lane's MFMA column
+  lc.q = q;
+  lc.phi_col = r % PHI;                 // phase of this lane's MFMA column
+  lc.head_ok = g_col < G;
+  const int phi_grp = q * PHI / 4;      // phase of this lane group (K pass)
+  const int sub = q % (4 / PHI);
+  const int brow = (lc.head_ok && phi_grp == lc.phi_col) ? g_col : 16;
+  lc.qa = &sm.pro.qa[brow][sub * Gm::SUBD];
+  lc.qb = &sm.pro.qb[brow][sub * Gm::SUBD];
+  lc.qc = &sm.pro.qc[brow][sub * Gm::SUBD];
+  lc.qs = lc.head_ok ? sm.qs[g_col] : 0.0f;
+  lc.q1 = lc.head_ok ? sm.q1[g_col] : 0.0f;
+  lc.magic = to_vgpr(p.bits_magic);
+  lc.n4 = to_vgpr(p.bits_n4);
+  lc.n2 = to_vgpr(p.bits_n2);
+
+  WaveState st{kNegInf, 0.0f, 0.0f};
   f32x4_t acc[Gm::DT];
 #pragma unroll
   for (int i = 0; i < Gm::DT; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int c = cb; c < ce; ++c) {
-    int tpos[2];
-    int64_t rbase[2];   // row index of the tile's first token in the planes
-    bool tok[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      tpos[mt] = c * kChunk + 16 * mt;
-      tok[mt] = false;
-      rbase[mt] = 0;
-      if (tpos[mt] < L && tpos[mt] + 15 >= start) {
-        const int id = trow[tpos[mt] / bs];
-        if (id >= 0) {
-          tok[mt] = true;
-          rbase[mt] = ((int64_t)id * hkv + h) * bs + (tpos[mt] % bs);
-        }
-      }
+  // ---- tiles tb + wave, tb + wave + 4, ...: two buffers, loads one tile ahead.
+  // Every half-iteration issues the same loads (a tile past the split end is
+  // invalid and reads row 0), so the wait counts before each compute are exact
+  // and cover only the tile being computed.
+  {
+    const int bl = p.block_size_log2;
+    const int32_t* ids = sm.ids;
+    Buf<MODE, D, PHI> ba, bb;
+    int tile = tb + wave;
+    TileInfo ta = tile_info(ids, blk0, tile, te, L, start, bl, hkv, h);
+    TileInfo tn = tile_info(ids, blk0, tile + kWaves, te, L, start, bl, hkv, h);
+    issue_loads<MODE, D, PHI>(ba, ta, p, r, q, lc.phi_col);
+    for (; tile < te; tile += 2 * kWaves) {
+      issue_loads<MODE, D, PHI>(bb, tn, p, r, q, lc.phi_col);
+      const TileInfo t2 = tile_info(ids, blk0, tile + 2 * kWaves, te, L, start, bl, hkv, h);
+      if (ta.valid) compute_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
+      issue_loads<MODE, D, PHI>(ba, t2, p, r, q, lc.phi_col);
+      const TileInfo t3 = tile_info(ids, blk0, tile + 3 * kWaves, te, L, start, bl, hkv, h);
+      if (tn.valid) compute_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
+      ta = t2;
+      tn = t3;
     }
-    if (!tok[0] && !tok[1]) continue;
-
-    // loads: K codes (lane = token r16, bytes kg*P/4..), V codes (lane =
-    // d-group r16, token slots j), K/V meta (lane = head, tokens 4kg..4kg+3)
-    uint32_t kc[2][Gm::KW];
-    uint32_t vc[8][Gm::VW];
-    float km[2][4 * M], vm[2][4 * M];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      if (tok[mt]) {
-        load_bytes<P / 4>(kc[mt], p.k_codes + (rbase[mt] + r16) * P + kg * (P / 4));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          load_bytes<Gm::VB>(vc[4 * mt + i], p.v_codes + (rbase[mt] + 4 * kg + i) * P + r16 * Gm::VB);
-        const float* kmp = p.k_meta + (rbase[mt] + 4 * kg) * M;
-        const float* vmp = p.v_meta + (rbase[mt] + 4 * kg) * M;
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-          const float4 a = reinterpret_cast<const float4*>(kmp)[i];
-          const float4 bb = reinterpret_cast<const float4*>(vmp)[i];
-          km[mt][4 * i] = a.x; km[mt][4 * i + 1] = a.y; km[mt][4 * i + 2] = a.z; km[mt][4 * i + 3] = a.w;
-          vm[mt][4 * i] = bb.x; vm[mt][4 * i + 1] = bb.y; vm[mt][4 * i + 2] = bb.z; vm[mt][4 * i + 3] = bb.w;
-        }
-      } else {
-        zero_words<Gm::KW>(kc[mt]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zero_words<Gm::VW>(vc[4 * mt + i]);
-#pragma unroll
-        for (int i = 0; i < 4 * M; ++i) { km[mt][i] = 0.0f; vm[mt][i] = 0.0f; }
-      }
-    }
-
-    // K pass: raw[mt][i] = sum_d q''_d (128 + c_d) - 128 sum q'' for token 4kg+i
-    f32x4_t sc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4_t a = {koff, koff, koff, koff};
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const u32x4_t ak = unpack_k<MODE, D>(kc[mt], k);
-        a = mfma(ak, bqh[k], a);
-        a = mfma(ak, bql[k], a);
-      }
-      sc[mt] = a;
-    }
-
-    // scores (log2 units), masks, chunk max per head
-    float s2[2][4];
-    float cmax = kNegInf;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = tpos[mt] + 4 * kg + i;
-        const bool valid = tok[mt] && pos < L && pos >= start && r16 < G;
-        const float s = M == 2 ? km[mt][2 * i] : km[mt][i];
-        const float z = M == 2 ? km[mt][2 * i + 1] : 0.0f;
-        const float v = s * sc[mt][i] + z * q1;
-        s2[mt][i] = valid ? v : kNegInf;
-        cmax = fmaxf(cmax, s2[mt][i]);
-      }
-    }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-
-    // probabilities, V weights w = p * s_V (bf16 hi + lo), zero-point term
-    uint32_t whi[4], wlo[4];
-    float lsum = 0.0f, zsum = 0.0f, wsum = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        float w2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float pr = __builtin_amdgcn_exp2f(s2[mt][i + e] - m_use);
-          const float sv = M == 2 ? vm[mt][2 * (i + e)] : vm[mt][i + e];
-          const float zv = M == 2 ? vm[mt][2 * (i + e) + 1] : 0.0f;
-          const bool live = pr > 0.0f;
-          lsum += pr;
-          zsum += live ? pr * zv : 0.0f;
-          w2[e] = live ? pr * sv : 0.0f;
-        }
-        const uint32_t hi = pack_bf16(w2[0], w2[1]);
-        const uint32_t lo = pack_bf16(w2[0] - bf16_lo(hi), w2[1] - bf16_hi(hi));
-        whi[2 * mt + i / 2] = hi;
-        wlo[2 * mt + i / 2] = lo;
-        wsum += (bf16_lo(hi) + bf16_lo(lo)) + (bf16_hi(hi) + bf16_hi(lo));
-      }
-    }
-    l_run = l_run * alpha + lsum;
-    z_run = z_run * alpha + zsum;
-    wsum += __shfl_xor(wsum, 16);
-    wsum += __shfl_xor(wsum, 32);
-    const float voff = -128.0f * wsum;
-#pragma unroll
-    for (int i = 0; i < Gm::DT; ++i) {
-      acc[i][0] = acc[i][0] * alpha + voff;
-      acc[i][1] = acc[i][1] * alpha + voff;
-      acc[i][2] = acc[i][2] * alpha + voff;
-      acc[i][3] = acc[i][3] * alpha + voff;
-    }
-    const u32x4_t bwh = {whi[0], whi[1], whi[2], whi[3]};
-    const u32x4_t bwl = {wlo[0], wlo[1], wlo[2], wlo[3]};
-    VPass<MODE, D, 0>::run(vc, bwh, bwl, acc);
-    m_run = m_new;
   }
 
-  // ---- split epilogue
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  z_run += __shfl_xor(z_run, 16);
-  z_run += __shfl_xor(z_run, 32);
-  // lane (head g = r16, q = kg) holds d = (4q + i)*(D/16) + dt  ->  e = i*(D/16) + dt
-  float v[E];
+  // ---- wave epilogue: sum the phases of a head, then l and z over lane groups
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int m = 1; m < PHI; m <<= 1) {
 #pragma unroll
-    for (int dt = 0; dt < Gm::DT; ++dt) v[i * Gm::DT + dt] = acc[dt][i] + z_run;
+    for (int i = 0; i < Gm::DT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += __shfl_xor(acc[i][j], m);
+    st.l += __shfl_xor(st.l, m);
+    st.z += __shfl_xor(st.z, m);
+  }
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+  st.z += __shfl_xor(st.z, 16);
+  st.z += __shfl_xor(st.z, 32);
+  __syncthreads();   // the prologue area becomes the combine area
+  if (lc.head_ok && lc.phi_col == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int dt = 0; dt < Gm::DT; ++dt) sm.comb.acc[wave][g_col][(4 * q + i) * Gm::DT + dt] = acc[dt][i] + st.z;
+    if (q == 0) {
+      sm.comb.ml[wave][g_col][0] = st.m;
+      sm.comb.ml[wave][g_col][1] = st.l;
+    }
+  }
+  __syncthreads();
 
-  const int g = r16;
-  const int64_t orow = (int64_t)b * p.hq + h * G + g;
-  if (n_splits == 1) {
-    const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  // ---- workgroup combine: each thread owns (g, d) pairs
+  constexpr int PER = (16 * D + 64 * kWaves - 1) / (64 * kWaves);
+  float val[PER];
+  float lsum[PER];
+  float mmax[PER];
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = l_run > 0.0f ? v[i] * inv_l : 0.0f;
-    if constexpr (ROT) inverse_rotate<D>(v, kg, p.signs, p.inv_sqrt_d);
-    if (g < G) store_out<D>(p, orow, kg, v);
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid + k * 64 * kWaves;
+    val[k] = 0.0f; lsum[k] = 0.0f; mmax[k] = kNegInf;
+    if (e < G * D) {
+      const int g = e / D, d = e - g * D;
+      float mx = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.comb.ml[w][g][0]);
+      const float mu = mx == kNegInf ? 0.0f : mx;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm.comb.ml[w][g][0] - mu);
+        val[k] += f * sm.comb.acc[w][g][d];
+        lsum[k] += f * sm.comb.ml[w][g][1];
+      }
+      mmax[k] = mx;
+    }
+  }
+  __syncthreads();
+
+  if (n_splits == 1) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + k * 64 * kWaves;
+      if (e < G * D) sm.fin[e / D][e % D] = lsum[k] > 0.0f ? val[k] / lsum[k] : 0.0f;
+    }
+    __syncthreads();
+    if constexpr (ROT) lds_fwht<D>(sm.fin, G, tid);
+    store_rows<D>(p, sm.fin, G, orow0, tid, ROT);
     return;
   }
 
-  float* rec = p.partials + (orow * p.max_splits + split) * (D + 4);
-  if (g < G) {
-    if (kg == 0) *reinterpret_cast<float2*>(rec) = make_float2(m_run, l_run);
-    float4* dst = reinterpret_cast<float4*>(rec + 4 + kg * E);
+  // ---- several splits: publish (m, l, acc); decode_reduce_kernel combines
 #pragma unroll
-    for (int i = 0; i < E / 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-  }
-  __threadfence();
-  uint32_t* ctr = p.counters + (int64_t)b * hkv + h;
-  uint32_t old = 0;
-  if (lane == 0) old = atomicAdd(ctr, 1u);
-  old = __shfl(old, 0);
-  if (old != (uint32_t)(n_splits - 1)) return;
-  __threadfence();
-  if (lane == 0) atomicExch(ctr, 0u);
-
-  // last wave: combine the splits of every head of this kv head
-  const float* base = p.partials + orow * p.max_splits * (D + 4);
-  float mx = kNegInf;
-  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, g < G ? base[s * (D + 4)] : kNegInf);
-  const float mu = mx == kNegInf ? 0.0f : mx;
-  float ltot = 0.0f;
-#pragma unroll
-  for (int i = 0; i < E; ++i) v[i] = 0.0f;
-  if (g < G) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float* r = base + s * (D + 4);
-      const float2 ml = *reinterpret_cast<const float2*>(r);
-      const float wgt = __builtin_amdgcn_exp2f(ml.x - mu);
-      ltot += wgt * ml.y;
-      const float4* src = reinterpret_cast<const float4*>(r + 4 + kg * E);
-#pragma unroll
-      for (int i = 0; i < E / 4; ++i) {
-        const float4 a = src[i];
-        v[4 * i] += wgt * a.x;
-        v[4 * i + 1] += wgt * a.y;
-        v[4 * i + 2] += wgt * a.z;
-        v[4 * i + 3] += wgt * a.w;
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid + k * 64 * kWaves;
+    if (e < G * D) {
+      const int g = e / D, d = e - g * D;
+      float* rec = p.partials + ((orow0 + g) * p.max_splits + split) * (D + 4);
+      rec[4 + d] = val[k];
+      if (d == 0) {
+        rec[0] = mmax[k];
+        rec[1] = lsum[k];
       }
     }
   }
-  const float inv_l = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+}
+
+// Cross-split combine, launched after decode_kernel on the same stream when a
+// (sequence, kv head) can have several splits: one workgroup per (sequence,
+// kv head) merges the splits' (m, l, acc) of its G heads, normalizes, applies
+// R^T and stores.
+template <int D, bool ROT>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
+  __shared__ float fin[16][D];
+  __shared__ float wgt[16][kMaxReduceSplits];
+  __shared__ float inv_l[16];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int G = p.group;
+  const int L = p.seq_lens[b];
+  const int W = p.window ? p.window[h] : 0;
+  const int start = (W > 0 && L > W) ? L - W : 0;
+  const int n_tiles = L > 0 ? (L + 63) / 64 - start / 64 : 0;
+  const int tps = p.chunks_per_split;
+  const int n_splits = n_tiles > 0 ? (n_tiles + tps - 1) / tps : 1;
+  if (n_splits == 1) return;   // decode_kernel already stored this (sequence, kv head)
+  const int64_t orow0 = (int64_t)b * p.hq + h * G;
+  // weights exp2(m_s - M) of every (head, split), and 1 / sum_s w_s l_s
+  for (int g = tid >> 6; g < G; g += 4) {
+    const int lane = tid & 63;
+    const float* base = p.partials + (orow0 + g) * p.max_splits * (D + 4);
+    float mx = kNegInf;
+    for (int s = lane; s < n_splits; s += 64) mx = fmaxf(mx, base[s * (D + 4)]);
 #pragma unroll
-  for (int i = 0; i < E; ++i) v[i] = ltot > 0.0f ? v[i] * inv_l : 0.0f;
-  if constexpr (ROT) inverse_rotate<D>(v, kg, p.signs, p.inv_sqrt_d);
-  if (g < G) store_out<D>(p, orow, kg, v);
+    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    const float mu = mx == kNegInf ? 0.0f : mx;
+    float l = 0.0f;
+    for (int s = lane; s < n_splits; s += 64) {
+      const float w = __builtin_amdgcn_exp2f(base[s * (D + 4)] - mu);
+      wgt[g][s] = w;
+      l += w * base[s * (D + 4) + 1];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) l += __shfl_xor(l, m);
+    if (lane == 0) inv_l[g] = l > 0.0f ? 1.0f / l : 0.0f;
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += 256) {
+    const int g = e / D, d = e - g * D;
+    const float* base = p.partials + (orow0 + g) * p.max_splits * (D + 4) + 4 + d;
+    float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
+    int s = 0;
+    for (; s + 4 <= n_splits; s += 4) {
+      v0 += wgt[g][s] * base[s * (D + 4)];
+      v1 += wgt[g][s + 1] * base[(s + 1) * (D + 4)];
+      v2 += wgt[g][s + 2] * base[(s + 2) * (D + 4)];
+      v3 += wgt[g][s + 3] * base[(s + 3) * (D + 4)];
+    }
+    for (; s < n_splits; ++s) v0 += wgt[g][s] * base[s * (D + 4)];
+    fin[g][d] = ((v0 + v1) + (v2 + v3)) * inv_l[g];
+  }
+  __syncthreads();
+  if constexpr (ROT) {
+    for (int hh = 1; hh < D; hh <<= 1) {
+      for (int e = tid; e < G * (D / 2); e += 256) {
+        const int g = e / (D / 2), k = e - g * (D / 2);
+        const int i = (k / hh) * 2 * hh + (k % hh);
+        const float a = fin[g][i], bb = fin[g][i + hh];
+        fin[g][i] = a + bb;
+        fin[g][i + hh] = a - bb;
+      }
+      __syncthreads();
+    }
+  }
+  store_rows<D>(p, fin, G, orow0, tid, ROT);
+}
+
+template <int MODE, int D, int PHI, bool ROT>
+hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, hipStream_t s) {
+  hipLaunchKernelGGL((decode_kernel<MODE, D, PHI, ROT>), dim3(p.max_splits, p.hkv, num_seqs),
+                     dim3(64 * kWaves), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_splits == 1) return e;
+  hipLaunchKernelGGL((decode_reduce_kernel<D, ROT>), dim3(p.hkv, num_seqs), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 template <int MODE, int D, bool ROT>
-hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<MODE, D, ROT>), dim3(p.max_splits, p.hkv, num_seqs), dim3(64), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_decode_p(const DecodeParams& p, int n, hipStream_t s) {
+  if (p.group * 4 <= 16) return launch_decode_t<MODE, D, 4, ROT>(p, n, s);
+  if (p.group * 2 <= 16) return launch_decode_t<MODE, D, 2, ROT>(p, n, s);
+  return launch_decode_t<MODE, D, 1, ROT>(p, n, s);
 }
 
 template <int MODE>
 hipError_t launch_decode_m(int d, bool rot, const DecodeParams& p, int n, hipStream_t s) {
-  if (d == 64) return rot ? launch_decode_t<MODE, 64, true>(p, n, s) : launch_decode_t<MODE, 64, false>(p, n, s);
-  return rot ? launch_decode_t<MODE, 128, true>(p, n, s) : launch_decode_t<MODE, 128, false>(p, n, s);
+  if (d == 64) return rot ? launch_decode_p<MODE, 64, true>(p, n, s) : launch_decode_p<MODE, 64, false>(p, n, s);
+  return rot ? launch_decode_p<MODE, 128, true>(p, n, s) : launch_decode_p<MODE, 128, false>(p, n, s);
 }
 
 }  // namespace

@@ -46,9 +46,11 @@ kvq_status check_desc(const kvq_cache_desc* d) {
     return fail(KVQ_EINVAL, "head_dim %d must be a power of two (64 or 128)", d->head_dim);
   }
   if (d->num_kv_heads < 1) return fail(KVQ_EINVAL, "num_kv_heads %d < 1", d->num_kv_heads);
-  if (d->block_size < 16 || d->block_size > 1024 || d->block_size % 16 != 0)
-    return fail(KVQ_EINVAL, "block_size %d must be a multiple of 16 in [16, 1024]", d->block_size);
+  if (d->block_size < 16 || d->block_size > 1024 || (d->block_size & (d->block_size - 1)) != 0)
+    return fail(KVQ_EINVAL, "block_size %d must be a power of two in [16, 1024]", d->block_size);
   if (d->num_blocks < 1) return fail(KVQ_EINVAL, "num_blocks %lld < 1", (long long)d->num_blocks);
+  if ((long long)d->num_blocks * d->num_kv_heads * d->block_size > 0x7fffffffLL)
+    return fail(KVQ_EUNSUPPORTED, "num_blocks*num_kv_heads*block_size must stay below 2^31 rows");
   if (d->rot_signs && !aligned(d->rot_signs, 16))
     return fail(KVQ_EINVAL, "rot_signs must be 16-byte aligned");
   return KVQ_OK;
@@ -66,42 +68,45 @@ float inv_sqrt_f32(int d) { return (float)(1.0 / std::sqrt((double)d)); }
 struct DecodePlan {
   int chunks_per_split;
   int max_splits;
-  size_t counter_bytes;
   size_t partial_bytes;
-  size_t total() const { return counter_bytes + partial_bytes; }
+  size_t total() const { return partial_bytes; }
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Split-KV plan: split each (sequence, kv head)'s active range into runs of
-// chunks so that the launch holds a few thousand waves (>> 256 CUs) whatever
-// the batch.  Deterministic in its inputs, so the workspace query and the
-// call agree.
+// 64-position tiles, one 4-wave workgroup per run, so that the launch holds a
+// few thousand workgroups (>> 256 CUs) whatever the batch while each wave
+// still gets several tiles to pipeline.  Deterministic in its inputs, so the
+// workspace query and the call agree.
 DecodePlan plan_decode(const kvq_cache_desc* d, int num_seqs, int num_q_heads, int max_seq_len) {
   DecodePlan pl{};
-  const long long max_chunks = (max_seq_len + kvq::kChunk - 1) / kvq::kChunk;
-  const long long units = (long long)num_seqs * d->num_kv_heads * (max_chunks > 0 ? max_chunks : 1);
-  long long target = 4096;
-  if (const char* e = std::getenv("KVQ_DECODE_TARGET_WAVES")) {
+  const long long max_tiles = (max_seq_len + kvq::kTile - 1) / kvq::kTile;
+  const long long units = (long long)num_seqs * d->num_kv_heads * (max_tiles > 0 ? max_tiles : 1);
+  long long target = 2048;
+  if (const char* e = std::getenv("KVQ_DECODE_TARGET_WGS")) {
     const long long t = std::atoll(e);
     if (t > 0) target = t;
   }
-  long long cps = (units + target - 1) / target;
-  if (cps < 4) cps = 4;
-  if (const char* e = std::getenv("KVQ_DECODE_CHUNKS_PER_SPLIT")) {
+  long long tps = (units + target - 1) / target;
+  if (tps < 8) tps = 8;
+  if (const char* e = std::getenv("KVQ_DECODE_TILES_PER_SPLIT")) {
     const long long c = std::atoll(e);
-    if (c > 0) cps = c;
+    if (c > 0) tps = c;
   }
-  if (max_chunks > 0 && cps > max_chunks) cps = max_chunks;
-  if (cps < 1) cps = 1;
-  long long ms = max_chunks > 0 ? (max_chunks + cps - 1) / cps : 1;
+  // the combine kernel handles at most kMaxReduceSplits splits
+  if (max_tiles > (long long)kvq::kMaxReduceSplits * tps)
+    tps = (max_tiles + kvq::kMaxReduceSplits - 1) / kvq::kMaxReduceSplits;
+  if (max_tiles > 0 && tps > max_tiles) tps = max_tiles;
+  // the block ids of one split must fit the kernel's LDS table
+  const long long tps_cap = ((long long)(kvq::kMaxSplitBlocks - 1) * d->block_size) / kvq::kTile;
+  if (tps > tps_cap) tps = tps_cap;
+  if (tps < 1) tps = 1;
+  long long ms = max_tiles > 0 ? (max_tiles + tps - 1) / tps : 1;
   if (ms < 1) ms = 1;
-  pl.chunks_per_split = (int)cps;
+  pl.chunks_per_split = (int)tps;
   pl.max_splits = (int)ms;
-  if (ms > 1) {
-    pl.counter_bytes = round_up((size_t)num_seqs * d->num_kv_heads * sizeof(uint32_t), 256);
-    pl.partial_bytes = (size_t)num_seqs * num_q_heads * ms * (d->head_dim + 4) * sizeof(float);
-  }
+  if (ms > 1) pl.partial_bytes = round_up((size_t)num_seqs * num_q_heads * ms * (d->head_dim + 4) * sizeof(float), 256);
   return pl;
 }
 
@@ -247,20 +252,21 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
   p.seq_lens = seq_lens;
   p.window = window;
   p.signs = desc->rot_signs;
-  p.counters = pl.total() > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
-  p.partials = pl.total() > 0
-                   ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counter_bytes)
-                   : nullptr;
+  p.partials = pl.total() > 0 ? static_cast<float*>(workspace) : nullptr;
   p.qscale = softmax_scale * 1.4426950408889634f;
   p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
   p.max_blocks = max_blocks_per_seq;
   p.block_size = desc->block_size;
+  p.block_size_log2 = __builtin_ctz((unsigned)desc->block_size);
   p.hq = num_q_heads;
   p.hkv = desc->num_kv_heads;
   p.group = num_q_heads / desc->num_kv_heads;
   p.chunks_per_split = pl.chunks_per_split;
   p.max_splits = pl.max_splits;
   p.out_bf16 = out_dtype == KVQ_OUT_BF16;
+  p.bits_magic = 0x43004300u;
+  p.bits_n4 = 0x000F000Fu;
+  p.bits_n2 = 0x00030003u;
   hipError_t e = kvq::launch_decode(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p, num_seqs,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_EHIP, "decode launch: %s", hipGetErrorString(e));

@@ -13,8 +13,12 @@ __host__ __device__ constexpr int mode_meta(int mode) { return mode == 0 ? 1 : 2
 __host__ __device__ constexpr int mode_levels(int mode) { return mode == 0 ? 127 : (mode == 1 ? 15 : 3); }
 __host__ __device__ constexpr int row_bytes(int mode, int d) { return d * mode_bits(mode) / 8; }
 
-// Positions processed together by the decode kernel: two 16-token MFMA tiles.
-constexpr int kChunk = 32;
+// Positions the decode kernel processes as one tile (four 16-token MFMA tiles).
+constexpr int kTile = 64;
+// Most block ids one decode split may span (held in LDS).
+constexpr int kMaxSplitBlocks = 1024;
+// Most splits one (sequence, kv head) may have (the combine kernel's LDS).
+constexpr int kMaxReduceSplits = 512;
 
 struct WriteParams {
   const uint16_t* key;      // bf16
@@ -46,18 +50,21 @@ struct DecodeParams {
   const int32_t* window;        // [Hkv] or nullptr
   const float* signs;           // [D] or nullptr
   float* partials;              // [B, Hq, max_splits, D + 4]
-  uint32_t* counters;           // [B, Hkv]
   float qscale;                 // softmax_scale * log2(e)
   float inv_sqrt_d;
   int32_t headwise;
   int32_t max_blocks;
   int32_t block_size;
+  int32_t block_size_log2;
   int32_t hq;
   int32_t hkv;
   int32_t group;                // Hq / Hkv
-  int32_t chunks_per_split;
+  int32_t chunks_per_split;     // 64-position tiles per split
   int32_t max_splits;
   int32_t out_bf16;
+  uint32_t bits_magic;          // 0x43004300: bf16 128.0 in both halves
+  uint32_t bits_n4;             // 0x000F000F
+  uint32_t bits_n2;             // 0x00030003
 };
 
 hipError_t launch_write(int mode, int d, bool rot, const WriteParams& p, hipStream_t s);

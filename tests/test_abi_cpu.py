@@ -59,7 +59,7 @@ def test_layout_matches_formula(lib, mode, D):
 @pytest.mark.parametrize("kw,status", [
     (dict(mode=3), _lib.KVQ_EINVAL), (dict(mode=-1), _lib.KVQ_EINVAL),
     (dict(D=96), _lib.KVQ_EINVAL), (dict(D=256), _lib.KVQ_EUNSUPPORTED), (dict(D=0), _lib.KVQ_EINVAL),
-    (dict(H=0), _lib.KVQ_EINVAL), (dict(bs=8), _lib.KVQ_EINVAL), (dict(bs=40), _lib.KVQ_EINVAL),
+    (dict(H=0), _lib.KVQ_EINVAL), (dict(bs=8), _lib.KVQ_EINVAL), (dict(bs=40), _lib.KVQ_EINVAL), (dict(bs=48), _lib.KVQ_EINVAL),
     (dict(nb=0), _lib.KVQ_EINVAL)])
 def test_layout_rejects(lib, kw, status):
     out = _lib.Layout()

@@ -85,13 +85,13 @@ def test_decode_repeatable_and_split_invariant(monkeypatch):
     case, d, planes = gh.build(spec)
     outs = []
     for cps in ("1", "3", "1000"):
-        monkeypatch.setenv("KVQ_DECODE_CHUNKS_PER_SPLIT", cps)
+        monkeypatch.setenv("KVQ_DECODE_TILES_PER_SPLIT", cps)
         o1 = gh.gpu_decode(spec, case, d, planes)
         o2 = gh.gpu_decode(spec, case, d, planes)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2), f"repeat differs at cps={cps}"
         outs.append(o1.cpu().numpy())
-    monkeypatch.delenv("KVQ_DECODE_CHUNKS_PER_SPLIT")
+    monkeypatch.delenv("KVQ_DECODE_TILES_PER_SPLIT")
     ref = gh.oracle_decode(spec, case, gh.host_planes(planes))
     for o in outs:
         gh.assert_close(o, ref, "split-count")
