@@ -90,6 +90,34 @@ __device__ __forceinline__ uint32_t to_vgpr(uint32_t x) {
   return r;
 }
 
+// Cross-lane reductions without LDS round trips.  v_permlane16_swap /
+// v_permlane32_swap applied to (x, x) return x and its partner lane l^16 /
+// l^32 in the two results; DPP quad_perm gives lanes l^1 and l^2.  Both lanes
+// of a pair compute the same commutative op on the same two values, so they
+// agree bit for bit.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// lane l ^ M for M = 1 or 2 (within a quad)
+template <int M>
+__device__ __forceinline__ float quad_xor(float x) {
+  constexpr int sel = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), sel, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
@@ -350,10 +378,9 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
   for (int tau = 0; tau < Gm::NKT; ++tau)
 #pragma unroll
     for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[tau][i]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-#pragma unroll
-  for (int m = 1; m < PHI; m <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, m));
+  tmax = max_xor32(max_xor16(tmax));
+  if constexpr (PHI >= 2) tmax = __builtin_fmaxf(tmax, quad_xor<1>(tmax));
+  if constexpr (PHI >= 4) tmax = __builtin_fmaxf(tmax, quad_xor<2>(tmax));
   if (__any(tmax > st.m + kRescale)) {
     const float mn = fmaxf(st.m, tmax);
     const float alpha = mn == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
@@ -392,8 +419,7 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
   }
   // ---- offset: acc -= 128 * (sum of the column's weights), as one MFMA per
   // d-tile against the sum split into three bf16 pieces
-  wsum += __shfl_xor(wsum, 16);
-  wsum += __shfl_xor(wsum, 32);
+  wsum = add_xor32(add_xor16(wsum));
   {
     const __bf16 w0 = (__bf16)wsum;
     const float r1 = wsum - (float)w0;
@@ -464,9 +490,9 @@ template <int D>
 struct Smem {
   union {
     struct {
-      int8_t qa[17][D];     // query pieces in k-slot order; row 16 = zeros
-      int8_t qb[17][D];
-      int8_t qc[17][D];
+      int8_t qa[17][D + 16];  // query pieces in k-slot order; row 16 = zeros
+      int8_t qb[17][D + 16];  // (16 bytes of padding keep rows on distinct banks)
+      int8_t qc[17][D + 16];
       float qf[16][D];      // prologue scratch: R q * scale * log2(e)
     } pro;
     struct {
@@ -480,8 +506,14 @@ struct Smem {
   int32_t ids[kMaxSplitBlocks];   // block ids of the split's range
 };
 
+// Two waves per SIMD (two workgroups per CU) where the registers fit without
+// spilling, so one workgroup's prologue and epilogue overlap another's tiles.
+template <int MODE, int D, int PHI>
+constexpr int decode_waves_per_simd() { return (PHI == 1 || (MODE == 0 && D == 128 && PHI < 4)) ? 1 : 2; }
+
 template <int MODE, int D, int PHI, bool ROT>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<MODE, D, PHI>())))
+void decode_kernel(DecodeParams p) {
   using Gm = Geo<MODE, D, PHI>;
   __shared__ Smem<D> sm;
 
@@ -510,7 +542,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const int32_t* trow = p.tables + (int64_t)(p.headwise ? b * hkv + h : b) * p.max_blocks;
   const int64_t orow0 = (int64_t)b * p.hq + h * G;
 
-  // ---- block ids of the split's positions [64 tb, min(64 te, L)) into LDS
+  // ---- block ids of the split's positions [64 tb, min(64 te, L)) and the raw
+  // query rows into LDS
   const int blk0 = (tb * 64) >> p.block_size_log2;
   {
     const int last_pos = min(te * 64, L) - 1;
@@ -518,8 +551,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     for (int i = tid; i < n_ids; i += 64 * kWaves) sm.ids[i] = trow[blk0 + i];
     if (n_ids == 0 && tid == 0) sm.ids[0] = -1;
   }
-
-  // ---- prologue: q' = R q * scale * log2(e), then int8 pieces in k-slot order
   for (int e = tid; e < G * D; e += 64 * kWaves) {
     const int g = e / D, d = e - g * D;
     float v = __uint_as_float((uint32_t)p.q[(orow0 + g) * D + d] << 16);
@@ -527,6 +558,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     sm.pro.qf[g][d] = v;
   }
   __syncthreads();
+
+  // ---- first tiles' loads go out before the query prologue, which they do
+  // not depend on, so their latency overlaps it
+  const int bl = p.block_size_log2;
+  Buf<MODE, D, PHI> ba, bb;
+  int tile = tb + wave;
+  TileInfo ta = tile_info(sm.ids, blk0, tile, te, L, start, bl, hkv, h);
+  TileInfo tn = tile_info(sm.ids, blk0, tile + kWaves, te, L, start, bl, hkv, h);
+  const int phi_col0 = r % PHI;
+  issue_loads<MODE, D, PHI>(ba, ta, p, r, q, phi_col0);
+
+  // ---- query prologue: q' = R q * scale * log2(e), then int8 pieces in
+  // k-slot order
   if constexpr (ROT) lds_fwht<D>(sm.pro.qf, G, tid);
   const float qmul = ROT ? p.qscale * p.inv_sqrt_d : p.qscale;
   for (int g = wave; g < 17; g += kWaves) {
@@ -596,40 +640,36 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   // Every half-iteration issues the same loads (a tile past the split end is
   // invalid and reads row 0), so the wait counts before each compute are exact
   // and cover only the tile being computed.
-  {
-    const int bl = p.block_size_log2;
-    const int32_t* ids = sm.ids;
-    Buf<MODE, D, PHI> ba, bb;
-    int tile = tb + wave;
-    TileInfo ta = tile_info(ids, blk0, tile, te, L, start, bl, hkv, h);
-    TileInfo tn = tile_info(ids, blk0, tile + kWaves, te, L, start, bl, hkv, h);
-    issue_loads<MODE, D, PHI>(ba, ta, p, r, q, lc.phi_col);
-    for (; tile < te; tile += 2 * kWaves) {
-      issue_loads<MODE, D, PHI>(bb, tn, p, r, q, lc.phi_col);
-      const TileInfo t2 = tile_info(ids, blk0, tile + 2 * kWaves, te, L, start, bl, hkv, h);
-      if (ta.valid) compute_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
-      issue_loads<MODE, D, PHI>(ba, t2, p, r, q, lc.phi_col);
-      const TileInfo t3 = tile_info(ids, blk0, tile + 3 * kWaves, te, L, start, bl, hkv, h);
-      if (tn.valid) compute_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
-      ta = t2;
-      tn = t3;
-    }
+  for (; tile < te; tile += 2 * kWaves) {
+    issue_loads<MODE, D, PHI>(bb, tn, p, r, q, lc.phi_col);
+    const TileInfo t2 = tile_info(sm.ids, blk0, tile + 2 * kWaves, te, L, start, bl, hkv, h);
+    if (ta.valid) compute_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
+    issue_loads<MODE, D, PHI>(ba, t2, p, r, q, lc.phi_col);
+    const TileInfo t3 = tile_info(sm.ids, blk0, tile + 3 * kWaves, te, L, start, bl, hkv, h);
+    if (tn.valid) compute_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
+    ta = t2;
+    tn = t3;
   }
 
   // ---- wave epilogue: sum the phases of a head, then l and z over lane groups
-#pragma unroll
-  for (int m = 1; m < PHI; m <<= 1) {
+  if constexpr (PHI >= 2) {
 #pragma unroll
     for (int i = 0; i < Gm::DT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] += __shfl_xor(acc[i][j], m);
-    st.l += __shfl_xor(st.l, m);
-    st.z += __shfl_xor(st.z, m);
+      for (int j = 0; j < 4; ++j) acc[i][j] += quad_xor<1>(acc[i][j]);
+    st.l += quad_xor<1>(st.l);
+    st.z += quad_xor<1>(st.z);
   }
-  st.l += __shfl_xor(st.l, 16);
-  st.l += __shfl_xor(st.l, 32);
-  st.z += __shfl_xor(st.z, 16);
-  st.z += __shfl_xor(st.z, 32);
+  if constexpr (PHI >= 4) {
+#pragma unroll
+    for (int i = 0; i < Gm::DT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += quad_xor<2>(acc[i][j]);
+    st.l += quad_xor<2>(st.l);
+    st.z += quad_xor<2>(st.z);
+  }
+  st.l = add_xor32(add_xor16(st.l));
+  st.z = add_xor32(add_xor16(st.z));
   __syncthreads();   // the prologue area becomes the combine area
   if (lc.head_ok && lc.phi_col == 0) {
 #pragma unroll
