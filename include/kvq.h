@@ -176,6 +176,42 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc,
                                       void* workspace, size_t workspace_bytes,
                                       void* stream);
 
+/* Chunked-prefill attention (vLLM PR 40835 summary, 实现拆解 item 2; the
+ * vllm-ascend-quantized-kv-cache package, 运行机制: prefill reads the paged
+ * quantized cache; FastDeploy PR 7718: head-wise table with -1 skips and
+ * per-head sliding windows).  Sequence b owns the query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; its n_b = cu_seqlens_q[b+1] -
+ * cu_seqlens_q[b] new tokens are already written to the cache (call
+ * kvq_reshape_and_cache first) and sit at positions L_b - n_b + i, L_b =
+ * seq_lens[b].  Row (i, q head hq) attends, over kv head h = hq / (Hq/Hkv), to
+ * the dequantized, un-rotated keys/values of positions j <= L_b - n_b + i that
+ * lie in a non-evicted block and, if window && window[h] > 0, satisfy
+ * j >= L_b - n_b + i - window[h] + 1.  No allowed position => output 0.
+ *   out          (device) [total_q, Hq, D] float32 or bf16 (out_dtype)
+ *   query        (device) bf16 [total_q, Hq, D]
+ *   cu_seqlens_q (device) int32 [num_seqs + 1], non-decreasing, from 0
+ *   max_q_len    host upper bound on every n_b (sizes the grid; rows past it
+ *                are not computed)
+ *   seq_lens     (device) int32 [num_seqs], each >= n_b and <= max_seq_len
+ *   block tables, window, softmax_scale and the cache planes as for
+ *   kvq_paged_decode_attention.  No workspace: every launch covers the whole
+ *   key range of its rows.  GQA groups up to 128. */
+kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc,
+                                       void* out, int32_t out_dtype,
+                                       const void* query,
+                                       const int32_t* cu_seqlens_q,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t max_q_len,
+                                       const uint8_t* k_codes, const float* k_meta,
+                                       const uint8_t* v_codes, const float* v_meta,
+                                       const int32_t* block_tables,
+                                       const int32_t* block_tables_headwise,
+                                       int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, int32_t max_seq_len,
+                                       const int32_t* window,
+                                       float softmax_scale,
+                                       void* stream);
+
 /* Thread-local message for the last non-OK status ("" if none). */
 const char* kvq_last_error(void);
 

@@ -1,0 +1,106 @@
+// Device helpers shared by the libkvq HIP kernels (gfx950): MFMA wrappers,
+// cross-lane reductions, bf16 packing and raw byte loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr uint32_t kMagic = 0x43004300u;  // bf16 128.0 in both halves
+constexpr float kRescale = 8.0f;          // log2 of the growth that forces a rescale
+
+__device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x4_t mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a), __builtin_bit_cast(i32x4_t, b),
+                                               c, 0, 0, 0);
+}
+
+// (x & m) | (c & ~m).  With m and c held in VGPRs this is one v_bitop3_b32
+// (with literal or scalar constants the compiler emits an and plus an or).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | (c & ~m); }
+
+// Copy a wave-uniform value into a VGPR the optimizer cannot fold back into a
+// scalar or a literal.  Used once per kernel for the and_or() constants; the
+// result only feeds ordinary VALU instructions.
+__device__ __forceinline__ uint32_t to_vgpr(uint32_t x) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "s"(x));
+  return r;
+}
+
+// Cross-lane reductions without LDS round trips.  v_permlane16_swap /
+// v_permlane32_swap applied to (x, x) return x and its partner lane l^16 /
+// l^32 in the two results; DPP quad_perm gives lanes l^1 and l^2.  Both lanes
+// of a pair compute the same commutative op on the same two values, so they
+// agree bit for bit.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// lane l ^ M for M = 1 or 2 (within a quad)
+template <int M>
+__device__ __forceinline__ float quad_xor(float x) {
+  constexpr int sel = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), sel, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two exact small integers held as floats -> bf16 pair (the dropped mantissa
+// bits are zero for values < 256).
+__device__ __forceinline__ uint32_t pack_exact(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+template <int N>
+__device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src) {
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int i = 0; i < N / 16; ++i) {
+      const uint4 a = reinterpret_cast<const uint4*>(src)[i];
+      dst[4 * i] = a.x; dst[4 * i + 1] = a.y; dst[4 * i + 2] = a.z; dst[4 * i + 3] = a.w;
+    }
+  } else if constexpr (N == 8) {
+    const uint2 a = *reinterpret_cast<const uint2*>(src);
+    dst[0] = a.x; dst[1] = a.y;
+  } else if constexpr (N == 4) {
+    dst[0] = *reinterpret_cast<const uint32_t*>(src);
+  } else if constexpr (N == 2) {
+    dst[0] = *reinterpret_cast<const uint16_t*>(src);
+  } else {
+    dst[0] = *src;
+  }
+}
+
+}  // namespace
+}  // namespace kvq

@@ -88,8 +88,12 @@ DecodePlan plan_decode(const kvq_cache_desc* d, int num_seqs, int num_q_heads, i
     const long long t = std::atoll(e);
     if (t > 0) target = t;
   }
+  // Each split pays a fixed prologue (query pieces, block ids) and, when a
+  // sequence has several, a partial record plus the combine kernel; on MI355X
+  // fewer, longer splits win until the grid no longer covers the CUs, so a
+  // split spans at least 128 tiles (8192 positions).
   long long tps = (units + target - 1) / target;
-  if (tps < 8) tps = 8;
+  if (tps < 128) tps = 128;
   if (const char* e = std::getenv("KVQ_DECODE_TILES_PER_SPLIT")) {
     const long long c = std::atoll(e);
     if (c > 0) tps = c;
@@ -270,6 +274,74 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
   hipError_t e = kvq::launch_decode(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p, num_seqs,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
+                                       const void* query, const int32_t* cu_seqlens_q, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_q_len,
+                                       const uint8_t* k_codes, const float* k_meta,
+                                       const uint8_t* v_codes, const float* v_meta,
+                                       const int32_t* block_tables, const int32_t* block_tables_headwise,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                       int32_t max_seq_len, const int32_t* window, float softmax_scale,
+                                       void* stream) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (num_seqs < 0) return fail(KVQ_EINVAL, "num_seqs %d < 0", num_seqs);
+  if (num_q_heads < 1) return fail(KVQ_EINVAL, "num_q_heads %d < 1", num_q_heads);
+  if (num_q_heads % desc->num_kv_heads != 0)
+    return fail(KVQ_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                desc->num_kv_heads);
+  const int group = num_q_heads / desc->num_kv_heads;
+  if (group > 128) return fail(KVQ_EUNSUPPORTED, "GQA group %d > 128 is not built", group);
+  if (max_q_len < 0) return fail(KVQ_EINVAL, "max_q_len %d < 0", max_q_len);
+  if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len %d < 0", max_seq_len);
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16)
+    return fail(KVQ_EINVAL, "out_dtype %d is not a kvq_out_dtype", out_dtype);
+  if ((block_tables == nullptr) == (block_tables_headwise == nullptr))
+    return fail(KVQ_EINVAL, "exactly one of block_tables and block_tables_headwise must be non-NULL");
+  if (max_blocks_per_seq < 1) return fail(KVQ_EINVAL, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * desc->block_size)
+    return fail(KVQ_EINVAL, "max_seq_len %d exceeds max_blocks_per_seq*block_size = %lld", max_seq_len,
+                (long long)max_blocks_per_seq * desc->block_size);
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is not finite");
+  if (num_seqs == 0 || max_q_len == 0) return ok();
+  if (!out || !query || !cu_seqlens_q || !seq_lens)
+    return fail(KVQ_EINVAL, "out, query, cu_seqlens_q or seq_lens is NULL");
+  st = check_planes(k_codes, k_meta, v_codes, v_meta);
+  if (st != KVQ_OK) return st;
+  const int tq = 128 / group;
+  const long long n_qtiles = ((long long)max_q_len + tq - 1) / tq;
+  const long long n_work = n_qtiles * desc->num_kv_heads * (long long)num_seqs;
+  if (n_work > 0x7fffff00LL) return fail(KVQ_EUNSUPPORTED, "prefill grid of %lld workgroups", n_work);
+  kvq::PrefillParams p{};
+  p.k_codes = k_codes;
+  p.k_meta = k_meta;
+  p.v_codes = v_codes;
+  p.v_meta = v_meta;
+  p.q = static_cast<const uint16_t*>(query);
+  p.out = out;
+  p.cu_q = cu_seqlens_q;
+  p.seq_lens = seq_lens;
+  p.headwise = block_tables_headwise != nullptr;
+  p.tables = p.headwise ? block_tables_headwise : block_tables;
+  p.window = window;
+  p.signs = desc->rot_signs;
+  p.qscale = softmax_scale * 1.4426950408889634f;
+  p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
+  p.max_blocks = max_blocks_per_seq;
+  p.block_size_log2 = __builtin_ctz((unsigned)desc->block_size);
+  p.hq = num_q_heads;
+  p.hkv = desc->num_kv_heads;
+  p.group = group;
+  p.tq = tq;
+  p.n_qtiles = (int)n_qtiles;
+  p.n_work = (int)n_work;
+  p.out_bf16 = out_dtype == KVQ_OUT_BF16;
+  hipError_t e = kvq::launch_prefill(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_EHIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -67,9 +67,36 @@ struct DecodeParams {
   uint32_t bits_n2;             // 0x00030003
 };
 
+struct PrefillParams {
+  const uint8_t* k_codes;
+  const float* k_meta;
+  const uint8_t* v_codes;
+  const float* v_meta;
+  const uint16_t* q;            // bf16 [Tq, Hq, D]
+  void* out;                    // [Tq, Hq, D]
+  const int32_t* cu_q;          // [B + 1]
+  const int32_t* seq_lens;      // [B]
+  const int32_t* tables;        // [B, max_blocks] or [B*Hkv, max_blocks]
+  const int32_t* window;        // [Hkv] or nullptr
+  const float* signs;           // [D] or nullptr
+  float qscale;                 // softmax_scale * log2(e)
+  float inv_sqrt_d;
+  int32_t headwise;
+  int32_t max_blocks;
+  int32_t block_size_log2;
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;                // Hq / Hkv
+  int32_t tq;                   // query tokens per workgroup = 128 / group
+  int32_t n_qtiles;             // ceil(max_q_len / tq)
+  int32_t n_work;               // n_qtiles * hkv * num_seqs
+  int32_t out_bf16;
+};
+
 hipError_t launch_write(int mode, int d, bool rot, const WriteParams& p, hipStream_t s);
 hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, int num_seqs,
                          hipStream_t s);
+hipError_t launch_prefill(int mode, int d, bool rot, const PrefillParams& p, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 }  // namespace kvq

@@ -1,0 +1,558 @@
+// Chunked-prefill attention over the quantized paged cache.
+//
+// Follows the read half of the prhub summary of vLLM PR 40835 ("INT4
+// per-token-head KV cache quantization for the Triton backend", 实现拆解
+// item 2: unpack, dequantize, attend), prefill over a gathered and
+// dequantized paged cache as described for the vllm-ascend-quantized-kv-cache
+// package (运行机制), and the head-wise block-table walk with -1 skips and the
+// per-head sliding window of FastDeploy PR 7718 ("Optimize AppendAttention for
+// discrete head-wise block_idx").
+//
+// Sequence b appends n_b query tokens that sit at positions L_b - n_b + i
+// (their K/V rows are already in the cache).  Query row (token i, q head hq)
+// attends to the cached positions j <= L_b - n_b + i whose block is present
+// and, for a windowed kv head, j >= L_b - n_b + i - W + 1:
+//   out = R^T sum_j softmax_j(scale * q'.k_hat_j) v_hat_j ,  q' = R q.
+// As in decode, nothing is dequantized element by element:
+//   q'.k_hat_j = s_j (q'.c_j) + z_j sum(q')
+//   sum_j p_j v_hat_j = sum_j (p_j s_j) c_j + sum_j p_j z_j .
+//
+// Work split: one 256-thread workgroup (4 waves) per (query tile, kv head,
+// sequence); a query tile is floor(128 / G) consecutive tokens times the G q
+// heads of the kv head, 128 rows (token-major), 32 per wave.  The workgroup
+// walks 64-position key tiles from the earliest window start of its rows to
+// its last row's position.  Each tile is staged through LDS once for all
+// waves: K as int8 codes in k-slot order (two or three bit operations per 16
+// codes for INT4 / INT2), V transposed to [d][position] as exact bf16
+// integers c, and per-position (s_K, z_K, s_V, z_V).  The next tile's global
+// loads are in flight while the current tile is computed.
+//
+// Per wave and tile (lane l: r = l % 16, q = l / 16):
+//   S^T = K Q^T on v_mfma_i32_16x16x64_i8
+//     A  codes [16 positions x 64 k] from LDS, position 16 kb + r
+//     B  query pieces [64 k x 16 rows] in registers; q' * scale * log2(e) is
+//        split into two int8 pieces (q' ~ S (a + b / 2^7), |a| <= 127,
+//        |b| <= 64) that accumulate exactly in int32
+//     C  lane (row r, positions 16 kb + 4 q + i)
+//   O += W V on v_mfma_f32_16x16x32_bf16, W = p * s_V as bf16 hi + lo
+//     A  W [16 rows x 32 positions]: the C registers of two key blocks
+//     B  V^T [32 positions x 16 d] from LDS, the position order matching A
+//     C  lane (d 16 db + r, rows 4 q + i)
+// The online softmax keeps one reference maximum per row (log2 units) and
+// rescales only when a row's maximum grows by more than 2^8.
+#include "kvq_internal.h"
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kPWaves = 4;
+constexpr int kPRows = 128;   // query rows per workgroup
+constexpr int kPKeys = 64;    // positions per key tile
+
+template <int MODE, int D>
+struct PGeo {
+  static constexpr int P = row_bytes(MODE, D);             // packed bytes per row
+  static constexpr int M = mode_meta(MODE);                // meta floats per row
+  static constexpr int DC = D / 4;                         // d per K-staging thread
+  static constexpr int KNW = DC * mode_bits(MODE) / 32;    // K code dwords per staging thread
+  static constexpr int DPT = D / 16;                       // d per V-staging thread
+  static constexpr int VNB = DPT * mode_bits(MODE) / 8;    // V bytes per position per thread
+  static constexpr int VNW = VNB >= 4 ? VNB / 4 : 1;
+  static constexpr int KS = D / 64;                        // int8 k-steps
+  static constexpr int DB = D / 16;                        // d-blocks of the PV product
+  static constexpr int KROW = D + 16;                      // LDS K row stride, bytes
+  static constexpr int VROW = 2 * kPKeys + 16;             // LDS V^T row stride, bytes
+};
+
+// d of k-slot c (0 .. DC-1) inside a K-staging chunk, for the order the
+// staging threads write: INT4 puts the low nibbles of the chunk's dwords
+// first, then the high ones; INT2 puts its four 2-bit planes one after the
+// other.
+template <int MODE, int D>
+__device__ __forceinline__ int kslot_d(int s) {
+  constexpr int DC = PGeo<MODE, D>::DC;
+  const int base = (s / DC) * DC, c = s % DC;
+  if constexpr (MODE == 1) {
+    const int pl = c / (DC / 2), rem = c % (DC / 2);
+    return base + 8 * (rem >> 2) + 2 * (rem & 3) + pl;
+  } else if constexpr (MODE == 2) {
+    const int pl = c / (DC / 4), rem = c % (DC / 4);
+    return base + 16 * (rem >> 2) + 4 * (rem & 3) + pl;
+  } else {
+    return s;
+  }
+}
+
+template <int MODE, int D>
+struct PBuf {
+  using Gp = PGeo<MODE, D>;
+  int8_t k[kPKeys][Gp::KROW];        // int8 codes, k-slot order
+  uint16_t vt[D][Gp::VROW / 2];      // bf16 c, [d][position slot]
+  float sk[kPKeys];
+  float zk[kPKeys];
+  float sv[kPKeys];
+  float zv[kPKeys];
+  int32_t ok[kPKeys];                // position present and within the tile range
+};
+
+template <int MODE, int D>
+struct PSmem {
+  union {
+    float qf[kPRows][D + 4];         // prologue: R q; epilogue: rows before R^T
+    PBuf<MODE, D> buf[2];
+  };
+  float rs[kPRows];                  // max |q' * scale * log2(e)| of each row
+  float r1[kPRows];                  // sum of the row's represented q'
+};
+
+// Registers a staging thread carries from the global loads to the LDS stores.
+template <int MODE, int D>
+struct Stage {
+  using Gp = PGeo<MODE, D>;
+  uint32_t k[Gp::KNW];
+  uint32_t v[4][Gp::VNW];
+  float sk, zk, sv, zv;
+  int ok;
+};
+
+__device__ __forceinline__ int plane_row(const int32_t* trow, int j, int khi, int bs_log2, int hkv, int h,
+                                         int* ok) {
+  int id = -1;
+  if (j <= khi) id = trow[j >> bs_log2];
+  *ok = id >= 0;
+  return id >= 0 ? ((id * hkv + h) << bs_log2) + (j & ((1 << bs_log2) - 1)) : 0;
+}
+
+// Global loads of key tile `tau` into registers.  Thread t stages K codes of
+// position t / 4, d-chunk t % 4 (and the meta of the position when t % 4 ==
+// 0) and V codes of positions 4 (t / 16) .. +3, d = DPT (t % 16) .. +DPT-1.
+// A position that is absent (evicted block, past the range) reads row 0,
+// which always exists; it is masked by `ok`.
+template <int MODE, int D>
+__device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillParams& p, const int32_t* trow,
+                                           int tau, int khi, int h, int tid) {
+  using Gp = PGeo<MODE, D>;
+  const int n = tid >> 2, qd = tid & 3;
+  int ok;
+  const int row = plane_row(trow, tau * kPKeys + n, khi, p.block_size_log2, p.hkv, h, &ok);
+  load_bytes<Gp::KNW * 4>(st.k, p.k_codes + (int64_t)row * Gp::P + qd * (Gp::KNW * 4));
+  st.ok = ok;
+  if (qd == 0) {
+    st.sk = p.k_meta[(int64_t)row * Gp::M];
+    st.zk = Gp::M == 2 ? p.k_meta[(int64_t)row * Gp::M + 1] : 0.0f;
+    st.sv = p.v_meta[(int64_t)row * Gp::M];
+    st.zv = Gp::M == 2 ? p.v_meta[(int64_t)row * Gp::M + 1] : 0.0f;
+  }
+  // V rows of positions 4 kq + i come from the K-staging lanes 16 kq + 4 i
+  // (qd == 0), which sit in this thread's wave.
+  const int kq = tid >> 4, wd = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int vr = __shfl(row, (16 * kq + 4 * i) & 63);
+    load_bytes<Gp::VNB>(st.v[i], p.v_codes + (int64_t)vr * Gp::P + wd * Gp::VNB);
+  }
+}
+
+// Unpack the staged registers into LDS buffer `b`.
+template <int MODE, int D>
+__device__ __forceinline__ void stage_store(const Stage<MODE, D>& st, PBuf<MODE, D>& b, int tid) {
+  using Gp = PGeo<MODE, D>;
+  const int n = tid >> 2, qd = tid & 3;
+  // K: int8 codes, k-slot order
+  uint32_t kc[Gp::DC / 4];
+  if constexpr (MODE == 1) {
+#pragma unroll
+    for (int i = 0; i < Gp::KNW; ++i) {
+      kc[i] = st.k[i] & 0x0F0F0F0Fu;
+      kc[Gp::KNW + i] = (st.k[i] >> 4) & 0x0F0F0F0Fu;
+    }
+  } else if constexpr (MODE == 2) {
+#pragma unroll
+    for (int pl = 0; pl < 4; ++pl)
+#pragma unroll
+      for (int i = 0; i < Gp::KNW; ++i) kc[pl * Gp::KNW + i] = (st.k[i] >> (2 * pl)) & 0x03030303u;
+  } else {
+#pragma unroll
+    for (int i = 0; i < Gp::KNW; ++i) kc[i] = st.k[i];
+  }
+  uint4* kd = reinterpret_cast<uint4*>(&b.k[n][qd * Gp::DC]);
+#pragma unroll
+  for (int i = 0; i < Gp::DC / 16; ++i) kd[i] = make_uint4(kc[4 * i], kc[4 * i + 1], kc[4 * i + 2], kc[4 * i + 3]);
+  if (qd == 0) {
+    b.sk[n] = st.ok ? st.sk : 0.0f;
+    b.zk[n] = st.ok ? st.zk : 0.0f;
+    b.sv[n] = st.ok ? st.sv : 0.0f;
+    b.zv[n] = st.ok ? st.zv : 0.0f;
+    b.ok[n] = st.ok;
+  }
+  // V: positions 4 kq .. 4 kq + 3 -> slots of the PV operand order, as exact
+  // bf16 integers c (no offset: the accumulator then holds only the signal,
+  // whose fp32 rounding does not grow with an offset over long contexts)
+  const int kq = tid >> 4, wd = tid & 15;
+  const int kq7 = kq & 7;
+  const int slot = 32 * (kq >> 3) + 8 * (kq7 & 3) + 4 * (kq7 >> 2);
+  constexpr int BITS = mode_bits(MODE);
+#pragma unroll
+  for (int e = 0; e < Gp::DPT; ++e) {
+    float c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wv = st.v[i][(e * BITS) >> 5];
+      const int sh = (e * BITS) & 31;
+      if constexpr (MODE == 0)
+        c[i] = (float)(int32_t)(int8_t)(uint8_t)(wv >> sh);
+      else
+        c[i] = (float)((wv >> sh) & ((1u << BITS) - 1u));
+    }
+    *reinterpret_cast<uint2*>(&b.vt[Gp::DPT * wd + e][slot]) = make_uint2(pack_exact(c[0], c[1]),
+                                                                          pack_exact(c[2], c[3]));
+  }
+}
+
+template <int MODE, int D>
+constexpr int prefill_waves_per_simd() { return 2; }
+
+template <int MODE, int D, bool ROT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<MODE, D>())))
+void prefill_kernel(PrefillParams p) {
+  using Gp = PGeo<MODE, D>;
+  __shared__ PSmem<MODE, D> sm;
+
+  // ---- work item: consecutive items (the query tiles of one (sequence, kv
+  // head)) land on one XCD, whose L2 then serves their shared key tiles
+  const int nb = gridDim.x;                       // a multiple of 8
+  const int bid = blockIdx.x;
+  const int w_item = (bid & 7) * (nb >> 3) + (bid >> 3);
+  if (w_item >= p.n_work) return;
+  const int qt = w_item % p.n_qtiles;
+  const int hb = w_item / p.n_qtiles;
+  const int h = hb % p.hkv;
+  const int b = hb / p.hkv;
+
+  const int q0 = p.cu_q[b];
+  const int nq = p.cu_q[b + 1] - q0;
+  const int G = p.group;
+  const int tq = p.tq;
+  const int tok0 = qt * tq;
+  if (tok0 >= nq) return;
+  const int ntok = min(tq, nq - tok0);
+  const int nrows = ntok * G;
+  const int L = min(p.seq_lens[b], p.max_blocks << p.block_size_log2);
+  const int W = p.window ? p.window[h] : 0;
+  const int pbase = L - nq + tok0;                // position of the tile's first token
+  const int khi = pbase + ntok - 1;               // last position any row may see
+  const int klo = W > 0 ? max(0, pbase - W + 1) : 0;
+  const int tau0 = klo / kPKeys;
+  const int tau1 = khi >= 0 ? khi / kPKeys : -1;  // inclusive; none when khi < 0
+  const int32_t* trow = p.tables + (int64_t)(p.headwise ? b * p.hkv + h : b) * p.max_blocks;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+
+  // ---- first key tile's loads overlap the query prologue
+  Stage<MODE, D> stg;
+  if (tau0 <= tau1) stage_load<MODE, D>(stg, p, trow, tau0, khi, h, tid);
+
+  // ---- query prologue: rows (token t, head g) -> R q
+  for (int e = tid; e < kPRows * D; e += 64 * kPWaves) {
+    const int row = e / D, d = e - row * D;
+    float v = 0.0f;
+    if (row < nrows) {
+      const int t = row / G, g = row - t * G;
+      v = __uint_as_float((uint32_t)p.q[((int64_t)(q0 + tok0 + t) * p.hq + h * G + g) * D + d] << 16);
+      if constexpr (ROT) v *= p.signs[d];
+    }
+    sm.qf[row][d] = v;
+  }
+  __syncthreads();
+  if constexpr (ROT) {
+    for (int hh = 1; hh < D; hh <<= 1) {
+      for (int e = tid; e < kPRows * (D / 2); e += 64 * kPWaves) {
+        const int g = e / (D / 2), k = e - g * (D / 2);
+        const int i = (k / hh) * 2 * hh + (k % hh);
+        const float a = sm.qf[g][i], c = sm.qf[g][i + hh];
+        sm.qf[g][i] = a + c;
+        sm.qf[g][i + hh] = a - c;
+      }
+      __syncthreads();
+    }
+  }
+  const float qmul = ROT ? p.qscale * p.inv_sqrt_d : p.qscale;
+  // piece scale and represented sum per row (each wave its own 32 rows)
+  for (int i = 0; i < 32; ++i) {
+    const int row = 32 * wave + i;
+    float mx = 0.0f;
+    for (int d = lane; d < D; d += 64) mx = fmaxf(mx, fabsf(sm.qf[row][d] * qmul));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
+    float sa = 0.0f, sb = 0.0f;
+    for (int d = lane; d < D; d += 64) {
+      const float t = fminf(fmaxf(sm.qf[row][d] * qmul * invS, -127.0f), 127.0f);
+      const float a = __builtin_rintf(t);
+      sa += a;
+      sb += __builtin_rintf((t - a) * 128.0f);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      sa += __shfl_xor(sa, m);
+      sb += __shfl_xor(sb, m);
+    }
+    if (lane == 0) {
+      sm.rs[row] = mx;
+      sm.r1[row] = (mx / 127.0f) * (sa + sb * 0.0078125f);
+    }
+  }
+  __syncthreads();
+  // B operands: lane (row r of block rb, k-slots 64 ks + 16 q .. +15)
+  u32x4_t qa[2][Gp::KS], qb[2][Gp::KS];
+  float sp[2], qp[2];
+  int rpos[2], rlo[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = 32 * wave + 16 * rb + r;
+    const float mx = sm.rs[row];
+    const float S = mx / 127.0f;
+    const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;   // as in the pass above
+#pragma unroll
+    for (int ks = 0; ks < Gp::KS; ++ks) {
+      uint32_t wa[4], wb[4];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        uint32_t pa = 0, pb = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = kslot_d<MODE, D>(64 * ks + 16 * q + 4 * j4 + j);
+          const float t = fminf(fmaxf(sm.qf[row][d] * qmul * invS, -127.0f), 127.0f);
+          const float a = __builtin_rintf(t);
+          const float c = __builtin_rintf((t - a) * 128.0f);
+          pa |= ((uint32_t)(int32_t)a & 0xffu) << (8 * j);
+          pb |= ((uint32_t)(int32_t)c & 0xffu) << (8 * j);
+        }
+        wa[j4] = pa;
+        wb[j4] = pb;
+      }
+      qa[rb][ks] = u32x4_t{wa[0], wa[1], wa[2], wa[3]};
+      qb[rb][ks] = u32x4_t{wb[0], wb[1], wb[2], wb[3]};
+    }
+    // logit (log2 units) = sp * x, x = s_K raw + z_K qp, raw = 128 A + B
+    sp[rb] = S > 0.0f ? S * 0.0078125f : 1.0f;
+    qp[rb] = S > 0.0f ? sm.r1[row] / sp[rb] : 0.0f;
+    const bool live = row < nrows;
+    rpos[rb] = live ? pbase + row / G : -1;
+    rlo[rb] = W > 0 ? rpos[rb] - W + 1 : INT32_MIN;
+  }
+  // wave-uniform position range of the wave's live rows
+  const int wrow0 = 32 * wave;
+  const bool wave_live = wrow0 < nrows;
+  const int wpos_lo = pbase + wrow0 / G;
+  const int wpos_hi = pbase + (min(wrow0 + 31, nrows - 1)) / G;
+  __syncthreads();   // qf is dead; the buffers may be written
+
+  if (tau0 <= tau1) stage_store<MODE, D>(stg, sm.buf[0], tid);
+  __syncthreads();
+
+  float m_[2] = {kNegInf, kNegInf}, l_[2] = {0.0f, 0.0f}, z_[2] = {0.0f, 0.0f};
+  f32x4_t o[2][Gp::DB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int db = 0; db < Gp::DB; ++db) o[rb][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int tau = tau0; tau <= tau1; ++tau) {
+    const PBuf<MODE, D>& cb = sm.buf[(tau - tau0) & 1];
+    const bool more = tau < tau1;
+    if (more) stage_load<MODE, D>(stg, p, trow, tau + 1, khi, h, tid);
+
+    const int pos0 = tau * kPKeys;
+    const bool active = wave_live && pos0 <= wpos_hi && (W <= 0 || pos0 + kPKeys - 1 >= wpos_lo - W + 1);
+    if (active) {
+      const bool all_ok = __all(cb.ok[lane] != 0);
+      const bool full = all_ok && pos0 + kPKeys - 1 <= wpos_lo && (W <= 0 || pos0 >= wpos_hi - W + 1);
+      // ---- S^T = K Q^T, two int32 accumulators (pieces a and b)
+      float x[4][2][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        i32x4_t ia[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, ib[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+        for (int ks = 0; ks < Gp::KS; ++ks) {
+          const uint4 av = *reinterpret_cast<const uint4*>(&cb.k[16 * kb + r][64 * ks + 16 * q]);
+          const u32x4_t a = u32x4_t{av.x, av.y, av.z, av.w};
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            ia[rb] = mfma_i8(a, qa[rb][ks], ia[rb]);
+            ib[rb] = mfma_i8(a, qb[rb][ks], ib[rb]);
+          }
+        }
+        const float4 sk4 = *reinterpret_cast<const float4*>(&cb.sk[16 * kb + 4 * q]);
+        const float4 zk4 = *reinterpret_cast<const float4*>(&cb.zk[16 * kb + 4 * q]);
+        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
+        const float zkv[4] = {zk4.x, zk4.y, zk4.z, zk4.w};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float raw = (float)((ia[rb][i] << 7) + ib[rb][i]);
+            x[kb][rb][i] = __builtin_fmaf(raw, skv[i], zkv[i] * qp[rb]);
+          }
+      }
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int4 ok4 = *reinterpret_cast<const int4*>(&cb.ok[16 * kb + 4 * q]);
+          const int okv[4] = {ok4.x, ok4.y, ok4.z, ok4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = pos0 + 16 * kb + 4 * q + i;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              const bool keep = okv[i] != 0 && j <= rpos[rb] && j >= rlo[rb];
+              x[kb][rb][i] = keep ? x[kb][rb][i] : kNegInf;
+            }
+          }
+        }
+      }
+      // ---- row maxima (log2 units) and lazy rescale
+      float tm[2];
+      bool grow = false;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kb][rb][i]);
+        mx = max_xor32(max_xor16(mx));
+        tm[rb] = mx * sp[rb];
+        grow |= tm[rb] > m_[rb] + kRescale;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float mn = fmaxf(m_[rb], tm[rb]);
+          const float alpha = mn == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_[rb] - mn);
+          m_[rb] = mn;
+          l_[rb] *= alpha;
+          z_[rb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float ai = __shfl(alpha, 4 * q + i);
+#pragma unroll
+            for (int db = 0; db < Gp::DB; ++db) o[rb][db][i] *= ai;
+          }
+        }
+      }
+      // ---- p = 2^(logit - m), W = p s_V as bf16 hi + lo in PV A-operand order
+      u32x4_t wh[2][2], wl[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mu = m_[rb] == kNegInf ? 0.0f : m_[rb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const float4 sv4 = *reinterpret_cast<const float4*>(&cb.sv[16 * kb + 4 * q]);
+          const float4 zv4 = *reinterpret_cast<const float4*>(&cb.zv[16 * kb + 4 * q]);
+          const float svv[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
+          const float zvv[4] = {zv4.x, zv4.y, zv4.z, zv4.w};
+          float wv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][rb][i], sp[rb], -mu));
+            l_[rb] += pr;
+            z_[rb] = __builtin_fmaf(pr, zvv[i], z_[rb]);
+            wv[i] = pr * svv[i];
+          }
+          const uint32_t h0 = pack_bf16(wv[0], wv[1]), h1 = pack_bf16(wv[2], wv[3]);
+          const uint32_t l0 = pack_bf16(wv[0] - bf16_lo(h0), wv[1] - bf16_hi(h0));
+          const uint32_t l1 = pack_bf16(wv[2] - bf16_lo(h1), wv[3] - bf16_hi(h1));
+          const int s = kb >> 1, half = 2 * (kb & 1);
+          wh[s][rb][half] = h0; wh[s][rb][half + 1] = h1;
+          wl[s][rb][half] = l0; wl[s][rb][half + 1] = l1;
+        }
+      }
+      // ---- O += W V
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int db = 0; db < Gp::DB; ++db) {
+          const uint4 bv = *reinterpret_cast<const uint4*>(&cb.vt[16 * db + r][32 * s + 8 * q]);
+          const u32x4_t bb = u32x4_t{bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            o[rb][db] = mfma(wh[s][rb], bb, o[rb][db]);
+            o[rb][db] = mfma(wl[s][rb], bb, o[rb][db]);
+          }
+        }
+    }
+    if (more) stage_store<MODE, D>(stg, sm.buf[(tau + 1 - tau0) & 1], tid);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalize into LDS rows, R^T, store
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float lt = add_xor32(add_xor16(l_[rb]));
+    const float zt = add_xor32(add_xor16(z_[rb]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(lt, 4 * q + i);
+      const float zi = __shfl(zt, 4 * q + i);
+      const float inv = li > 0.0f ? 1.0f / li : 0.0f;
+      const int row = 32 * wave + 16 * rb + 4 * q + i;
+#pragma unroll
+      for (int db = 0; db < Gp::DB; ++db) sm.qf[row][16 * db + r] = (o[rb][db][i] + zi) * inv;
+    }
+  }
+  __syncthreads();
+  if constexpr (ROT) {
+    for (int hh = 1; hh < D; hh <<= 1) {
+      for (int e = tid; e < nrows * (D / 2); e += 64 * kPWaves) {
+        const int g = e / (D / 2), k = e - g * (D / 2);
+        const int i = (k / hh) * 2 * hh + (k % hh);
+        const float a = sm.qf[g][i], c = sm.qf[g][i + hh];
+        sm.qf[g][i] = a + c;
+        sm.qf[g][i + hh] = a - c;
+      }
+      __syncthreads();
+    }
+  }
+  for (int e = tid; e < nrows * D; e += 64 * kPWaves) {
+    const int row = e / D, d = e - row * D;
+    const int t = row / G, g = row - t * G;
+    float v = sm.qf[row][d];
+    if constexpr (ROT) v = v * p.signs[d] * p.inv_sqrt_d;
+    const int64_t o_idx = ((int64_t)(q0 + tok0 + t) * p.hq + h * G + g) * D + d;
+    if (p.out_bf16)
+      reinterpret_cast<__bf16*>(p.out)[o_idx] = (__bf16)v;
+    else
+      reinterpret_cast<float*>(p.out)[o_idx] = v;
+  }
+}
+
+template <int MODE, int D, bool ROT>
+hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
+  const int grid = (p.n_work + 7) / 8 * 8;
+  hipLaunchKernelGGL((prefill_kernel<MODE, D, ROT>), dim3(grid), dim3(64 * kPWaves), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(int mode, int d, bool rot, const PrefillParams& p, hipStream_t s) {
+#define KVQ_PREFILL_CASE(M_, D_)                                                           \
+  if (mode == M_ && d == D_) return rot ? launch_prefill_t<M_, D_, true>(p, s)           \
+                                        : launch_prefill_t<M_, D_, false>(p, s);
+  KVQ_PREFILL_CASE(0, 64)
+  KVQ_PREFILL_CASE(0, 128)
+  KVQ_PREFILL_CASE(1, 64)
+  KVQ_PREFILL_CASE(1, 128)
+  KVQ_PREFILL_CASE(2, 64)
+  KVQ_PREFILL_CASE(2, 128)
+#undef KVQ_PREFILL_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

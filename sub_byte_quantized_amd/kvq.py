@@ -183,3 +183,45 @@ def kvq_paged_decode_attention(desc: CacheDesc, query: torch.Tensor,
         _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale),
         _ptr(workspace), workspace.numel(), _stream(dev)))
     return out
+
+
+def kvq_paged_prefill_attention(desc: CacheDesc, query: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                max_q_len: int,
+                                k_codes: torch.Tensor, k_meta: torch.Tensor,
+                                v_codes: torch.Tensor, v_meta: torch.Tensor,
+                                seq_lens: torch.Tensor, max_seq_len: int,
+                                block_tables: Optional[torch.Tensor] = None,
+                                block_tables_headwise: Optional[torch.Tensor] = None,
+                                window: Optional[torch.Tensor] = None,
+                                softmax_scale: Optional[float] = None,
+                                out: Optional[torch.Tensor] = None,
+                                out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Chunked-prefill attention for query [total_q, Hq, D] (bf16) with
+    sequence b owning rows cu_seqlens_q[b]..cu_seqlens_q[b+1]-1; returns out
+    [total_q, Hq, D]."""
+    dev = query.device
+    _need(query, "query", torch.bfloat16, dev)
+    Tq, Hq, D = query.shape
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(block_tables_headwise, "block_tables_headwise", torch.int32, dev)
+    _need(window, "window", torch.int32, dev)
+    B = int(seq_lens.shape[0])
+    if cu_seqlens_q.shape[0] != B + 1:
+        raise KvqError(1, f"cu_seqlens_q has {cu_seqlens_q.shape[0]} entries, {B + 1} expected")
+    tab = block_tables if block_tables is not None else block_tables_headwise
+    max_blocks = int(tab.shape[1]) if tab is not None else 0
+    if out is None:
+        out = torch.empty((Tq, Hq, D), dtype=out_dtype, device=dev)
+    _need(out, "out", out.dtype, dev)
+    odt = {torch.float32: KVQ_OUT_F32, torch.bfloat16: KVQ_OUT_BF16}[out.dtype]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    d = desc.c()
+    _check(_lib.load().kvq_paged_prefill_attention(
+        ctypes.byref(d), _ptr(out), odt, _ptr(query), _ptr(cu_seqlens_q), B, int(Hq), int(max_q_len),
+        _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
+        _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
+        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale), _stream(dev)))
+    return out

@@ -97,3 +97,41 @@ def compare_meta(got, ref, what=""):
     tol = 1e-6 * np.abs(ref.astype(np.float64)) + 1e-30
     bad = err > tol
     assert not bad.any(), f"{what}: {int(bad.sum())} meta values differ; worst {err.max():.3e}"
+
+
+def prefill_inputs(spec, n_new, device=None, stream=60):
+    """Seeded prefill queries for sequences 0..len(n_new)-1: q [sum n_new,
+    Hq, D] bf16 and cu_seqlens_q [len(n_new)+1] int32."""
+    device = device or dev()
+    n_new = np.asarray(n_new, np.int64)
+    q = synth.bf16_normal((int(n_new.sum()), spec.Hq, spec.D), spec.cfg, stream, device)
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32), device=device)
+    return q, cu
+
+
+def prefill_tables(case, nseq):
+    """Tables, seq_lens of the first nseq sequences (row slices)."""
+    spec = case.spec
+    bt = None if case.block_tables is None else case.block_tables[:nseq].contiguous()
+    bth = None if case.block_tables_headwise is None else case.block_tables_headwise[:nseq * spec.Hkv].contiguous()
+    return bt, bth, case.seq_lens[:nseq].contiguous()
+
+
+def gpu_prefill(spec, case, d, planes, q, cu, max_q_len=None, **kw):
+    nseq = int(cu.shape[0]) - 1
+    bt, bth, sl = prefill_tables(case, nseq)
+    if max_q_len is None:
+        max_q_len = int((cu[1:] - cu[:-1]).max().item()) if nseq else 0
+    return kvq.kvq_paged_prefill_attention(
+        d, q, cu, max_q_len, *planes, sl, int(case.seq_lens.max().item()),
+        block_tables=bt, block_tables_headwise=bth, window=case.window,
+        softmax_scale=case.softmax_scale, **kw)
+
+
+def oracle_prefill(spec, case, planes_np, q, cu, pairs=None, rows=None):
+    nseq = int(cu.shape[0]) - 1
+    bt, bth, sl = prefill_tables(case, nseq)
+    return oracle.prefill_attention(
+        f32(q), host(cu), host(sl), spec.mode, spec.D, spec.bs, spec.Hkv, *planes_np,
+        case.softmax_scale, signs=host(case.rot_signs), block_tables=host(bt),
+        block_tables_headwise=host(bth), window=host(case.window), pairs=pairs, rows=rows)

@@ -33,7 +33,8 @@ def desc(mode=1, D=128, H=4, bs=64, nb=10, signs=None):
 def test_header_lists_entry_points():
     names = header_functions()
     for n in ("kvq_query_layout", "kvq_reshape_and_cache", "kvq_paged_decode_attention",
-              "kvq_decode_workspace_size", "kvq_workspace_init", "kvq_last_error"):
+              "kvq_decode_workspace_size", "kvq_workspace_init", "kvq_paged_prefill_attention",
+              "kvq_last_error"):
         assert n in names
 
 
@@ -117,6 +118,36 @@ def test_decode_validation(lib):
     if need.value:
         assert _decode(lib, d, wsb=need.value - 1) == _lib.KVQ_ENOSPACE
         assert _decode(lib, d, ws=None) == _lib.KVQ_EINVAL
+
+
+def _prefill(lib, d, **kw):
+    P = ctypes.c_void_p(4096)
+    a = dict(out=P, odt=0, q=P, cu=P, B=2, Hq=8, mq=64, kc=P, km=P, vc=P, vm=P, bt=P, bth=None, mb=4, sl=P,
+             msl=200, win=None, scale=0.125)
+    a.update(kw)
+    return lib.kvq_paged_prefill_attention(ctypes.byref(d), a["out"], a["odt"], a["q"], a["cu"], a["B"], a["Hq"],
+                                           a["mq"], a["kc"], a["km"], a["vc"], a["vm"], a["bt"], a["bth"],
+                                           a["mb"], a["sl"], a["msl"], a["win"], a["scale"], None)
+
+
+def test_prefill_validation(lib):
+    d = desc(H=4, bs=64)
+    P = ctypes.c_void_p(4096)
+    assert _prefill(lib, d, Hq=6) == _lib.KVQ_EINVAL                 # GQA divisibility
+    assert "multiple" in lib.kvq_last_error().decode()
+    assert _prefill(lib, d, Hq=4 * 129) == _lib.KVQ_EUNSUPPORTED     # group > 128
+    assert _prefill(lib, d, bt=None, bth=None) == _lib.KVQ_EINVAL    # no table
+    assert _prefill(lib, d, bt=P, bth=P) == _lib.KVQ_EINVAL          # both tables
+    assert _prefill(lib, d, msl=4 * 64 + 1) == _lib.KVQ_EINVAL       # beyond the table
+    assert _prefill(lib, d, odt=7) == _lib.KVQ_EINVAL
+    assert _prefill(lib, d, scale=float("inf")) == _lib.KVQ_EINVAL
+    assert _prefill(lib, d, mq=-1) == _lib.KVQ_EINVAL
+    assert _prefill(lib, d, cu=None) == _lib.KVQ_EINVAL
+    assert _prefill(lib, d, vm=None) == _lib.KVQ_EINVAL
+    assert _prefill(lib, d, B=-3) == _lib.KVQ_EINVAL
+    assert _prefill(lib, d, B=0) == _lib.KVQ_OK                      # nothing to do
+    assert _prefill(lib, d, mq=0) == _lib.KVQ_OK
+    assert _prefill(lib, desc(D=96)) == _lib.KVQ_EINVAL
 
 
 def test_workspace_size_grows_with_work(lib):
