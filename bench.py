@@ -46,10 +46,11 @@ def sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def decode_algo_bytes(spec, case):
-    """Algorithmic bytes one decode launch reads and writes: codes + meta of
-    every attended token (positions inside the window, in non-evicted blocks,
-    below seq_len), the block-table entries walked, queries and outputs."""
+def decode_algo_bytes(spec, case, first=0):
+    """Algorithmic bytes one decode launch over sequences first..B-1 reads and
+    writes: codes + meta of every attended token (positions inside the
+    window, in non-evicted blocks, below seq_len), the block-table entries
+    walked, queries and outputs."""
     P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
     M = 1 if spec.mode == 0 else 2
     row = 2 * (P + 4 * M)
@@ -59,7 +60,8 @@ def decode_algo_bytes(spec, case):
     bth = None if case.block_tables_headwise is None else case.block_tables_headwise.cpu().numpy()
     tokens = 0
     entries = 0
-    for b, L in enumerate(lens):
+    for b in range(first, spec.B):
+        L = int(lens[b])
         for h in range(spec.Hkv):
             W = int(win[h]) if win is not None else 0
             start = L - W if (W > 0 and L > W) else 0
@@ -72,10 +74,42 @@ def decode_algo_bytes(spec, case):
             pos = np.arange(j0 * spec.bs, (j1 + 1) * spec.bs)
             keep = (pos >= start) & (pos < L) & np.repeat(ids >= 0, spec.bs)
             tokens += int(keep.sum())
+    nb = spec.B - first
     kv = tokens * row
-    q = spec.B * spec.Hq * spec.D * 2
-    out = spec.B * spec.Hq * spec.D * 4
-    return kv + q + out + 4 * entries + 4 * spec.B, kv, tokens
+    q = nb * spec.Hq * spec.D * 2
+    out = nb * spec.Hq * spec.D * 4
+    return kv + q + out + 4 * entries + 4 * nb, kv, tokens
+
+
+def prefill_work(spec, case):
+    """Useful work of the mixed step's chunked prefill: unmasked (query row,
+    key) pairs over the first n_prefill sequences (query i of sequence b at
+    p = L - n + i sees keys j <= p in present blocks and, for a windowed kv
+    head, j >= p - W + 1), times the G q heads; flops = 4 D per pair (q.k and
+    p.v); KV bytes = codes + meta of the positions any row of the chunk sees."""
+    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
+    M = 1 if spec.mode == 0 else 2
+    row = 2 * (P + 4 * M)
+    G = spec.Hq // spec.Hkv
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    cu = case.cu_seqlens_q.cpu().numpy().astype(np.int64)
+    win = None if case.window is None else case.window.cpu().numpy()
+    bt = None if case.block_tables is None else case.block_tables.cpu().numpy()
+    bth = None if case.block_tables_headwise is None else case.block_tables_headwise.cpu().numpy()
+    pairs = 0
+    kv_pos = 0
+    for b in range(spec.n_prefill):
+        L, n = int(lens[b]), int(cu[b + 1] - cu[b])
+        for h in range(spec.Hkv):
+            ids = (bth[b * spec.Hkv + h] if bth is not None else bt[b])[:(L + spec.bs - 1) // spec.bs]
+            present = np.repeat(ids >= 0, spec.bs)[:L].astype(np.int64)
+            csum = np.concatenate([[0], np.cumsum(present)])       # csum[j] = present positions < j
+            p = L - n + np.arange(n)
+            W = int(win[h]) if win is not None else 0
+            lo = np.maximum(p - W + 1, 0) if W > 0 else np.zeros_like(p)
+            pairs += int((csum[p + 1] - csum[lo]).sum()) * G
+            kv_pos += int(csum[L] - csum[lo[0]])
+    return pairs, 4 * spec.D * pairs, kv_pos * row
 
 
 def write_bytes_per_token(spec):
@@ -91,9 +125,12 @@ def build_workload(spec, dev):
     planes = kvq.alloc_cache(d, dev, poison=True)
     kvq.kvq_reshape_and_cache(d, case.k, case.v, *planes, slot_mapping=case.slot_mapping,
                               slot_mapping_headwise=case.slot_mapping_headwise)
-    # the step's new tokens: the last position of each sequence
+    # the step's new tokens: the last n_b positions of sequence b (one for a
+    # decode sequence, the chunk for a prefill sequence)
     lens = case.seq_lens.cpu().numpy().astype(np.int64)
-    last = np.cumsum(lens) - 1
+    n_new = synth.new_tokens_of(spec)
+    ends = np.cumsum(lens)
+    last = np.concatenate([np.arange(e - n, e) for e, n in zip(ends, n_new)])
     li = torch.as_tensor(last, device=dev)
     new = dict(k=case.k[li].contiguous(), v=case.v[li].contiguous(),
                sm=None if case.slot_mapping is None else case.slot_mapping[li].contiguous(),
@@ -174,12 +211,157 @@ def load_traffic(name):
     return j.get("hbm_bytes_per_launch")
 
 
+def oracle_prefill_sample(spec, case, planes, seconds):
+    """The oracle's chunked prefill on a bounded sample: rows of one
+    (sequence, kv head) pair, counted as unmasked pairs x 4 D flops."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    b, h = 0, spec.Hkv - 1          # a full-context head
+    bth = case.block_tables_headwise.cpu().numpy() if case.block_tables_headwise is not None else None
+    bt = case.block_tables.cpu().numpy() if case.block_tables is not None else None
+    ids = oracle.table_row(b, h, spec.Hkv, bt, bth)
+    ids = np.unique(ids[ids >= 0])
+    idx = torch.as_tensor(ids, device=planes[0].device)
+    small = [p[idx].cpu().numpy() for p in planes]
+    remap = np.full(case.tables.num_blocks, -1, np.int64)
+    remap[ids] = np.arange(len(ids))
+    bth2 = None if bth is None else np.where(bth >= 0, remap[np.maximum(bth, 0)], -1)
+    bt2 = None if bt is None else np.where(bt >= 0, remap[np.maximum(bt, 0)], -1)
+    q = case.q_prefill.float().cpu().numpy()
+    cu = case.cu_seqlens_q.cpu().numpy()
+    lens = case.seq_lens.cpu().numpy()
+    win = None if case.window is None else case.window.cpu().numpy()
+    signs = None if case.rot_signs is None else case.rot_signs.cpu().numpy()
+    n = int(cu[1] - cu[0])
+    L = int(lens[0])
+    G = spec.Hq // spec.Hkv
+    rows, pairs, t0 = 0, 0, time.perf_counter()
+    while rows < n and time.perf_counter() - t0 < seconds:
+        r = np.arange(rows, min(n, rows + 8))
+        oracle.prefill_attention(q, cu[:2], lens[:1], spec.mode, spec.D, spec.bs, spec.Hkv, *small,
+                                 case.softmax_scale, signs=signs, block_tables=bt2, block_tables_headwise=bth2,
+                                 window=win, pairs=[(b, h)], rows=r)
+        pairs += int(sum(L - n + i + 1 for i in r)) * G
+        rows = int(r[-1]) + 1
+    dt = time.perf_counter() - t0
+    return {"value": round(4 * spec.D * pairs / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{rows} of {n} query rows of sequence {b}, kv head {h} ({G} q heads) of the chunked "
+                      f"prefill in {dt:.1f} s (float64 attention over the GPU's stored planes)"}
+
+
+def run_mixed(args, spec, dev):
+    """The mixed step: quantize-write of every sequence's new tokens (the
+    chunk of each prefill sequence, one token of each decode sequence),
+    chunked-prefill attention of the prefill sequences, decode attention of
+    the others.  Prefill is MFMA work, so its roofline is TFLOP/s against the
+    dense bf16 peak; decode is reported as effective KV GB/s."""
+    t_setup = time.perf_counter()
+    case, d, planes, new = build_workload(spec, dev)
+    npf = spec.n_prefill
+    Hkv = spec.Hkv
+    max_len = int(case.seq_lens.max().item())
+    # decode part: sequences npf..B-1
+    dq = case.q[npf:].contiguous()
+    dsl = case.seq_lens[npf:].contiguous()
+    dbt = None if case.block_tables is None else case.block_tables[npf:].contiguous()
+    dbth = None if case.block_tables_headwise is None else case.block_tables_headwise[npf * Hkv:].contiguous()
+    ws = kvq.alloc_workspace(kvq.kvq_decode_workspace_size(d, spec.B - npf, spec.Hq, max_len), dev)
+    dout = torch.empty((spec.B - npf, spec.Hq, spec.D), dtype=torch.float32, device=dev)
+    # prefill part: sequences 0..npf-1
+    psl = case.seq_lens[:npf].contiguous()
+    pbt = None if case.block_tables is None else case.block_tables[:npf].contiguous()
+    pbth = None if case.block_tables_headwise is None else case.block_tables_headwise[:npf * Hkv].contiguous()
+    pout = torch.empty(case.q_prefill.shape, dtype=torch.float32, device=dev)
+    max_q = int(spec.prefill_new)
+    d_algo, d_kv, d_tokens = decode_algo_bytes(spec, case, first=npf)
+    pairs, flops, p_kv = prefill_work(spec, case)
+    setup_s = time.perf_counter() - t_setup
+
+    def write(i):
+        kvq.kvq_reshape_and_cache(d, new["k"], new["v"], *planes, slot_mapping=new["sm"],
+                                  slot_mapping_headwise=new["smh"])
+
+    def prefill(i):
+        kvq.kvq_paged_prefill_attention(d, case.q_prefill, case.cu_seqlens_q, max_q, *planes, psl, max_len,
+                                        block_tables=pbt, block_tables_headwise=pbth, window=case.window,
+                                        softmax_scale=case.softmax_scale, out=pout)
+
+    def decode(i):
+        kvq.kvq_paged_decode_attention(d, dq, *planes, dsl, max_len, block_tables=dbt,
+                                       block_tables_headwise=dbth, window=case.window,
+                                       softmax_scale=case.softmax_scale, out=dout, workspace=ws)
+
+    for i in range(args.warmup):
+        write(i)
+        prefill(i)
+        decode(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        write(i)
+        ev[i][1].record()
+        prefill(i)
+        ev[i][2].record()
+        decode(i)
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    w_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    p_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    d_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    T = int(new["k"].shape[0])
+    wb = write_bytes_per_token(spec)
+    p_tf = flops / (p_ms * 1e-3) / 1e12
+    d_gbs = d_algo / (d_ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode-attn effective KV GB/s (% HBM peak); quantize-write tokens/s",
+        "value": round(d_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
+        "data": "synthetic (seeded)",
+        "config": {"workload": spec.name, "batch": spec.B, "prefill_seqs": npf, "prefill_new_tokens": max_q,
+                   "decode_seqs": spec.B - npf, "q_heads": spec.Hq, "kv_heads": spec.Hkv, "head_dim": spec.D,
+                   "block_size": spec.bs, "mode": ["int8_sym", "int4_asym", "int2_asym"][spec.mode],
+                   "rotation": spec.rotate, "window": list(spec.window or []), "headwise_table": spec.headwise,
+                   "seq_len": max_len, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(p_tf, 2),
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(p_tf / 2500.0, 4), "traffic": None,
+                     "useful_pairs": pairs, "flops_per_launch": flops, "kv_bytes_per_launch": p_kv,
+                     "avg_launch_us": round(p_ms * 1e3, 2)},
+        "decode": {"kernel": "decode_kernel", "achieved_GBps": round(d_gbs, 2),
+                   "frac": round(d_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": int(d_algo),
+                   "kv_tokens_attended": d_tokens, "avg_launch_us": round(d_ms * 1e3, 2)},
+        "write": {"step_tokens": T, "step_write_us": round(w_ms * 1e3, 2),
+                  "tokens_per_s": round(T / (w_ms * 1e-3), 1), "bytes_per_token": wb,
+                  "GBps": round(T * wb / (w_ms * 1e-3) / 1e9, 2)},
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = oracle_prefill_sample(spec, case, planes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas cycled (0 = enough for 1.2 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -206,6 +388,8 @@ def main():
         return
 
     spec = synth.CONFIGS[args.config]
+    if spec.n_prefill:
+        return run_mixed(args, spec, dev)
     t_setup = time.perf_counter()
     case, d, planes, new = build_workload(spec, dev)
     cache_bytes = sum(p.numel() * p.element_size() for p in planes)

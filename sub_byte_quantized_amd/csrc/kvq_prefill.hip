@@ -87,13 +87,12 @@ __device__ __forceinline__ int kslot_d(int s) {
 template <int MODE, int D>
 struct PBuf {
   using Gp = PGeo<MODE, D>;
-  int8_t k[kPKeys][Gp::KROW];        // int8 codes, k-slot order
-  uint16_t vt[D][Gp::VROW / 2];      // bf16 c, [d][position slot]
-  float sk[kPKeys];
-  float zk[kPKeys];
-  float sv[kPKeys];
-  float zv[kPKeys];
-  int32_t ok[kPKeys];                // position present and within the tile range
+  u32x4_t k[kPKeys][Gp::KROW / 16];    // int8 codes, k-slot order
+  u32x4_t vt[D + 16][Gp::VROW / 16];   // bf16 c, [d][position slot]; rows D..D+3: see stage_store
+  f32x4_t sk[kPKeys / 4];              // per position, four to a vector
+  f32x4_t zk[kPKeys / 4];
+  f32x4_t sv[kPKeys / 4];
+  i32x4_t ok[kPKeys / 4];              // position present and within the tile range
 };
 
 template <int MODE, int D>
@@ -126,7 +125,7 @@ __device__ __forceinline__ int plane_row(const int32_t* trow, int j, int khi, in
 
 // Global loads of key tile `tau` into registers.  Thread t stages K codes of
 // position t / 4, d-chunk t % 4 (and the meta of the position when t % 4 ==
-// 0) and V codes of positions 4 (t / 16) .. +3, d = DPT (t % 16) .. +DPT-1.
+// 0) and V codes of positions 4 (t % 16) .. +3, d = DPT (t / 16) .. +DPT-1.
 // A position that is absent (evicted block, past the range) reads row 0,
 // which always exists; it is masked by `ok`.
 template <int MODE, int D>
@@ -144,12 +143,17 @@ __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillPara
     st.sv = p.v_meta[(int64_t)row * Gp::M];
     st.zv = Gp::M == 2 ? p.v_meta[(int64_t)row * Gp::M + 1] : 0.0f;
   }
-  // V rows of positions 4 kq + i come from the K-staging lanes 16 kq + 4 i
-  // (qd == 0), which sit in this thread's wave.
-  const int kq = tid >> 4, wd = tid & 15;
+  // V: positions 4 kq .. 4 kq + 3 (one block: block sizes are >= 16),
+  // d = DPT wd .. DPT wd + DPT - 1, with kq = t % 16 so that the 16 lanes of
+  // a group write one whole V^T row in LDS (no bank conflicts).
+  const int kq = tid & 15, wd = tid >> 4;
+  const int j0 = tau * kPKeys + 4 * kq;
+  const int bs_log2 = p.block_size_log2;
+  const int vid = j0 <= khi ? trow[j0 >> bs_log2] : -1;
+  const int vrow0 = ((max(vid, 0) * p.hkv + h) << bs_log2) + (j0 & ((1 << bs_log2) - 1));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int vr = __shfl(row, (16 * kq + 4 * i) & 63);
+    const int vr = (vid >= 0 && j0 + i <= khi) ? vrow0 + i : 0;
     load_bytes<Gp::VNB>(st.v[i], p.v_codes + (int64_t)vr * Gp::P + wd * Gp::VNB);
   }
 }
@@ -176,38 +180,211 @@ __device__ __forceinline__ void stage_store(const Stage<MODE, D>& st, PBuf<MODE,
 #pragma unroll
     for (int i = 0; i < Gp::KNW; ++i) kc[i] = st.k[i];
   }
-  uint4* kd = reinterpret_cast<uint4*>(&b.k[n][qd * Gp::DC]);
 #pragma unroll
-  for (int i = 0; i < Gp::DC / 16; ++i) kd[i] = make_uint4(kc[4 * i], kc[4 * i + 1], kc[4 * i + 2], kc[4 * i + 3]);
+  for (int i = 0; i < Gp::DC / 16; ++i)
+    b.k[n][qd * (Gp::DC / 16) + i] = u32x4_t{kc[4 * i], kc[4 * i + 1], kc[4 * i + 2], kc[4 * i + 3]};
   if (qd == 0) {
-    b.sk[n] = st.ok ? st.sk : 0.0f;
-    b.zk[n] = st.ok ? st.zk : 0.0f;
-    b.sv[n] = st.ok ? st.sv : 0.0f;
-    b.zv[n] = st.ok ? st.zv : 0.0f;
-    b.ok[n] = st.ok;
+    // The PV product also yields the row sums l = sum p and Z = sum p z_V
+    // through four extra V^T rows holding 1/s_V and z_V/s_V as bf16 hi + lo
+    // (W = p s_V).  A row with a zero or subnormal scale has all-zero codes,
+    // so any s_V reconstructs it; 1 keeps the extra rows finite.
+    const float sv = st.sv >= 1.17549435e-38f ? st.sv : 1.0f;
+    const float u = st.ok ? __builtin_amdgcn_rcpf(sv) : 0.0f;
+    const float t = st.ok ? st.zv * u : 0.0f;
+    const __bf16 uh = (__bf16)u, th = (__bf16)t;
+    const __bf16 ul = (__bf16)(u - (float)uh), tl = (__bf16)(t - (float)th);
+    const int kq7 = (n >> 2) & 7;
+    const int nslot = 32 * (n >> 5) + 8 * (kq7 & 3) + 4 * (kq7 >> 2) + (n & 3);
+    reinterpret_cast<__bf16*>(&b.vt[D + 0][0])[nslot] = uh;
+    reinterpret_cast<__bf16*>(&b.vt[D + 1][0])[nslot] = ul;
+    reinterpret_cast<__bf16*>(&b.vt[D + 2][0])[nslot] = th;
+    reinterpret_cast<__bf16*>(&b.vt[D + 3][0])[nslot] = tl;
+    b.sk[n >> 2][n & 3] = st.ok ? st.sk : 0.0f;
+    b.zk[n >> 2][n & 3] = st.ok ? st.zk : 0.0f;
+    b.sv[n >> 2][n & 3] = st.ok ? sv : 0.0f;
+    b.ok[n >> 2][n & 3] = st.ok;
   }
   // V: positions 4 kq .. 4 kq + 3 -> slots of the PV operand order, as exact
   // bf16 integers c (no offset: the accumulator then holds only the signal,
   // whose fp32 rounding does not grow with an offset over long contexts)
-  const int kq = tid >> 4, wd = tid & 15;
+  const int kq = tid & 15, wd = tid >> 4;
   const int kq7 = kq & 7;
   const int slot = 32 * (kq >> 3) + 8 * (kq7 & 3) + 4 * (kq7 >> 2);
+  // codes into bytes, then one v_cvt_f32_ubyte per code: byte b of plane
+  // word pw[pl][w] holds the code of d = DPT*wd + e with (INT8) e = 4 w + b,
+  // (INT4) e = 8 w + 2 b + pl, (INT2) e = 16 w + 4 b + pl
   constexpr int BITS = mode_bits(MODE);
+  constexpr int NPL = 8 / BITS;                       // code planes per byte
+  constexpr int NW = (Gp::DPT * BITS + 31) / 32;      // dwords per position
+  float c[4][Gp::DPT];
 #pragma unroll
-  for (int e = 0; e < Gp::DPT; ++e) {
-    float c[4];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t wv = st.v[i][(e * BITS) >> 5];
-      const int sh = (e * BITS) & 31;
-      if constexpr (MODE == 0)
-        c[i] = (float)(int32_t)(int8_t)(uint8_t)(wv >> sh);
-      else
-        c[i] = (float)((wv >> sh) & ((1u << BITS) - 1u));
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) {
+        const uint32_t x = MODE == 0 ? (st.v[i][w] ^ 0x80808080u)
+                                     : ((st.v[i][w] >> (BITS * pl)) & (MODE == 1 ? 0x0F0F0F0Fu : 0x03030303u));
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int e = (32 / BITS) * w + NPL * bb + pl;
+          if (e < Gp::DPT) c[i][e] = MODE == 0 ? (float)((x >> (8 * bb)) & 0xffu) - 128.0f
+                                               : (float)((x >> (8 * bb)) & 0xffu);
+        }
+      }
+#pragma unroll
+  for (int e = 0; e < Gp::DPT; ++e)
+    reinterpret_cast<uint2*>(&b.vt[Gp::DPT * wd + e][0])[slot >> 2] =
+        make_uint2(pack_exact(c[0][e], c[1][e]), pack_exact(c[2][e], c[3][e]));
+}
+
+template <int MODE, int D>
+struct WaveCtx {
+  using Gp = PGeo<MODE, D>;
+  u32x4_t qa[2][Gp::KS], qb[2][Gp::KS];   // query pieces, B-operand layout
+  f32x4_t o[2][Gp::DB + 1];               // output accumulators (C layout); block DB: l, Z
+  float m[2];                             // reference max (log2 units)
+  float sp[2], qp[2];                     // logit = sp * (s_K raw + z_K qp)
+  int rpos[2], rlo[2];                    // row position and window start
+  int W, wpos_lo, wpos_hi;
+  bool wave_live;
+  int lane, r, q;
+};
+
+// One key tile: global loads of the next tile, this tile's compute from
+// buffer PAR, the next tile's LDS stores into the other buffer, barrier.
+template <int MODE, int D, int PAR>
+__device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& wc, Stage<MODE, D>& stg,
+                                          const PrefillParams& p, const int32_t* trow, int tau, int tau1,
+                                          int khi, int h, int tid) {
+  using Gp = PGeo<MODE, D>;
+  const PBuf<MODE, D>& cb = sm.buf[PAR];
+  const bool more = tau < tau1;
+  if (more) stage_load<MODE, D>(stg, p, trow, tau + 1, khi, h, tid);
+  const int W = wc.W, r = wc.r, q = wc.q;
+    const int pos0 = tau * kPKeys;
+    const bool active = wc.wave_live && pos0 <= wc.wpos_hi && (W <= 0 || pos0 + kPKeys - 1 >= wc.wpos_lo - W + 1);
+    if (active) {
+      const bool all_ok = __all(cb.ok[wc.lane >> 2][wc.lane & 3] != 0);
+      const bool full = all_ok && pos0 + kPKeys - 1 <= wc.wpos_lo && (W <= 0 || pos0 >= wc.wpos_hi - W + 1);
+      // ---- S^T = K Q^T, two int32 accumulators (pieces a and b)
+      float x[4][2][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        i32x4_t ia[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, ib[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+        for (int ks = 0; ks < Gp::KS; ++ks) {
+          const u32x4_t a = cb.k[16 * kb + r][4 * ks + q];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            ia[rb] = mfma_i8(a, wc.qa[rb][ks], ia[rb]);
+            ib[rb] = mfma_i8(a, wc.qb[rb][ks], ib[rb]);
+          }
+        }
+        const f32x4_t skv = cb.sk[4 * kb + q];
+        const f32x4_t zkv = cb.zk[4 * kb + q];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float raw = (float)((ia[rb][i] << 7) + ib[rb][i]);
+            x[kb][rb][i] = __builtin_fmaf(raw, skv[i], zkv[i] * wc.qp[rb]);
+          }
+      }
+      if (__builtin_expect(!full, 0)) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const i32x4_t okv = cb.ok[4 * kb + q];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = pos0 + 16 * kb + 4 * q + i;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              const bool keep = okv[i] != 0 && j <= wc.rpos[rb] && j >= wc.rlo[rb];
+              x[kb][rb][i] = keep ? x[kb][rb][i] : kNegInf;
+            }
+          }
+        }
+      }
+      // ---- row maxima (log2 units) and lazy rescale
+      float tm[2];
+      bool grow = false;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kb][rb][i]);
+        mx = max_xor32(max_xor16(mx));
+        tm[rb] = mx * wc.sp[rb];
+        grow |= tm[rb] > wc.m[rb] + kRescale;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float mn = fmaxf(wc.m[rb], tm[rb]);
+          const float alpha = mn == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(wc.m[rb] - mn);
+          wc.m[rb] = mn;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float ai = __shfl(alpha, 4 * q + i);
+#pragma unroll
+            for (int db = 0; db <= Gp::DB; ++db) wc.o[rb][db][i] *= ai;
+          }
+        }
+      }
+      // ---- p = 2^(logit - m), W = p s_V as bf16 hi + lo in PV A-operand
+      // order (slab s = positions 32 s .. 32 s + 31)
+      u32x4_t wh[2][2], wl[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mu = wc.m[rb] == kNegInf ? 0.0f : wc.m[rb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const f32x4_t svv = cb.sv[4 * kb + q];
+          float wv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            wv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][rb][i], wc.sp[rb], -mu)) * svv[i];
+          // hi = w with the low 16 bits cleared (exact bf16), lo = w - hi
+          // (exact in fp32) rounded to bf16: together 16 significant bits
+          float th[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) th[i] = __uint_as_float(__float_as_uint(wv[i]) & 0xffff0000u);
+          const int s = kb >> 1, hf = 2 * (kb & 1);
+          wh[s][rb][hf] = __builtin_amdgcn_perm(__float_as_uint(th[1]), __float_as_uint(th[0]), 0x07060302u);
+          wh[s][rb][hf + 1] = __builtin_amdgcn_perm(__float_as_uint(th[3]), __float_as_uint(th[2]), 0x07060302u);
+          wl[s][rb][hf] = pack_bf16(wv[0] - th[0], wv[1] - th[1]);
+          wl[s][rb][hf + 1] = pack_bf16(wv[2] - th[2], wv[3] - th[3]);
+        }
+      }
+      // ---- O += W V, V operands read one d-block ahead of their MFMAs
+      u32x4_t b0 = cb.vt[r][q], b1 = cb.vt[r][4 + q];
+#pragma unroll
+      for (int db = 0; db <= Gp::DB; ++db) {
+        u32x4_t n0 = b0, n1 = b1;
+        if (db < Gp::DB) {
+          n0 = cb.vt[16 * (db + 1) + r][q];
+          n1 = cb.vt[16 * (db + 1) + r][4 + q];
+        }
+        // keep the next operands' reads ahead of this block's MFMAs (the
+        // scheduler otherwise sinks them next to their use and exposes the
+        // LDS latency)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          wc.o[rb][db] = mfma(wh[0][rb], b0, wc.o[rb][db]);
+          wc.o[rb][db] = mfma(wl[0][rb], b0, wc.o[rb][db]);
+          wc.o[rb][db] = mfma(wh[1][rb], b1, wc.o[rb][db]);
+          wc.o[rb][db] = mfma(wl[1][rb], b1, wc.o[rb][db]);
+        }
+        b0 = n0;
+        b1 = n1;
+      }
     }
-    *reinterpret_cast<uint2*>(&b.vt[Gp::DPT * wd + e][slot]) = make_uint2(pack_exact(c[0], c[1]),
-                                                                          pack_exact(c[2], c[3]));
-  }
+  if (more) stage_store<MODE, D>(stg, sm.buf[PAR ^ 1], tid);
+  __syncthreads();
 }
 
 template <int MODE, int D>
@@ -352,158 +529,47 @@ void prefill_kernel(PrefillParams p) {
   const int wpos_lo = pbase + wrow0 / G;
   const int wpos_hi = pbase + (min(wrow0 + 31, nrows - 1)) / G;
   __syncthreads();   // qf is dead; the buffers may be written
+  // extra V^T rows D+4 .. D+15 feed unused output columns: keep them zero
+  for (int e = tid; e < 2 * 12 * (Gp::VROW / 16); e += 64 * kPWaves) {
+    const int bsel = e / (12 * (Gp::VROW / 16)), rem = e - bsel * (12 * (Gp::VROW / 16));
+    sm.buf[bsel].vt[D + 4 + rem / (Gp::VROW / 16)][rem % (Gp::VROW / 16)] = u32x4_t{0u, 0u, 0u, 0u};
+  }
 
   if (tau0 <= tau1) stage_store<MODE, D>(stg, sm.buf[0], tid);
   __syncthreads();
 
-  float m_[2] = {kNegInf, kNegInf}, l_[2] = {0.0f, 0.0f}, z_[2] = {0.0f, 0.0f};
-  f32x4_t o[2][Gp::DB];
+  WaveCtx<MODE, D> wc{};
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < 2; ++rb) {
+    wc.m[rb] = kNegInf;
+    wc.sp[rb] = sp[rb]; wc.qp[rb] = qp[rb]; wc.rpos[rb] = rpos[rb]; wc.rlo[rb] = rlo[rb];
 #pragma unroll
-    for (int db = 0; db < Gp::DB; ++db) o[rb][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ks = 0; ks < Gp::KS; ++ks) { wc.qa[rb][ks] = qa[rb][ks]; wc.qb[rb][ks] = qb[rb][ks]; }
+#pragma unroll
+    for (int db = 0; db <= Gp::DB; ++db) wc.o[rb][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  wc.W = W; wc.wave_live = wave_live; wc.wpos_lo = wpos_lo; wc.wpos_hi = wpos_hi;
+  wc.lane = lane; wc.r = r; wc.q = q;
 
-  for (int tau = tau0; tau <= tau1; ++tau) {
-    const PBuf<MODE, D>& cb = sm.buf[(tau - tau0) & 1];
-    const bool more = tau < tau1;
-    if (more) stage_load<MODE, D>(stg, p, trow, tau + 1, khi, h, tid);
-
-    const int pos0 = tau * kPKeys;
-    const bool active = wave_live && pos0 <= wpos_hi && (W <= 0 || pos0 + kPKeys - 1 >= wpos_lo - W + 1);
-    if (active) {
-      const bool all_ok = __all(cb.ok[lane] != 0);
-      const bool full = all_ok && pos0 + kPKeys - 1 <= wpos_lo && (W <= 0 || pos0 >= wpos_hi - W + 1);
-      // ---- S^T = K Q^T, two int32 accumulators (pieces a and b)
-      float x[4][2][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        i32x4_t ia[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, ib[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-#pragma unroll
-        for (int ks = 0; ks < Gp::KS; ++ks) {
-          const uint4 av = *reinterpret_cast<const uint4*>(&cb.k[16 * kb + r][64 * ks + 16 * q]);
-          const u32x4_t a = u32x4_t{av.x, av.y, av.z, av.w};
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            ia[rb] = mfma_i8(a, qa[rb][ks], ia[rb]);
-            ib[rb] = mfma_i8(a, qb[rb][ks], ib[rb]);
-          }
-        }
-        const float4 sk4 = *reinterpret_cast<const float4*>(&cb.sk[16 * kb + 4 * q]);
-        const float4 zk4 = *reinterpret_cast<const float4*>(&cb.zk[16 * kb + 4 * q]);
-        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
-        const float zkv[4] = {zk4.x, zk4.y, zk4.z, zk4.w};
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float raw = (float)((ia[rb][i] << 7) + ib[rb][i]);
-            x[kb][rb][i] = __builtin_fmaf(raw, skv[i], zkv[i] * qp[rb]);
-          }
-      }
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int4 ok4 = *reinterpret_cast<const int4*>(&cb.ok[16 * kb + 4 * q]);
-          const int okv[4] = {ok4.x, ok4.y, ok4.z, ok4.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = pos0 + 16 * kb + 4 * q + i;
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-              const bool keep = okv[i] != 0 && j <= rpos[rb] && j >= rlo[rb];
-              x[kb][rb][i] = keep ? x[kb][rb][i] : kNegInf;
-            }
-          }
-        }
-      }
-      // ---- row maxima (log2 units) and lazy rescale
-      float tm[2];
-      bool grow = false;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kb][rb][i]);
-        mx = max_xor32(max_xor16(mx));
-        tm[rb] = mx * sp[rb];
-        grow |= tm[rb] > m_[rb] + kRescale;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const float mn = fmaxf(m_[rb], tm[rb]);
-          const float alpha = mn == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_[rb] - mn);
-          m_[rb] = mn;
-          l_[rb] *= alpha;
-          z_[rb] *= alpha;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float ai = __shfl(alpha, 4 * q + i);
-#pragma unroll
-            for (int db = 0; db < Gp::DB; ++db) o[rb][db][i] *= ai;
-          }
-        }
-      }
-      // ---- p = 2^(logit - m), W = p s_V as bf16 hi + lo in PV A-operand order
-      u32x4_t wh[2][2], wl[2][2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float mu = m_[rb] == kNegInf ? 0.0f : m_[rb];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const float4 sv4 = *reinterpret_cast<const float4*>(&cb.sv[16 * kb + 4 * q]);
-          const float4 zv4 = *reinterpret_cast<const float4*>(&cb.zv[16 * kb + 4 * q]);
-          const float svv[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
-          const float zvv[4] = {zv4.x, zv4.y, zv4.z, zv4.w};
-          float wv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][rb][i], sp[rb], -mu));
-            l_[rb] += pr;
-            z_[rb] = __builtin_fmaf(pr, zvv[i], z_[rb]);
-            wv[i] = pr * svv[i];
-          }
-          const uint32_t h0 = pack_bf16(wv[0], wv[1]), h1 = pack_bf16(wv[2], wv[3]);
-          const uint32_t l0 = pack_bf16(wv[0] - bf16_lo(h0), wv[1] - bf16_hi(h0));
-          const uint32_t l1 = pack_bf16(wv[2] - bf16_lo(h1), wv[3] - bf16_hi(h1));
-          const int s = kb >> 1, half = 2 * (kb & 1);
-          wh[s][rb][half] = h0; wh[s][rb][half + 1] = h1;
-          wl[s][rb][half] = l0; wl[s][rb][half + 1] = l1;
-        }
-      }
-      // ---- O += W V
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int db = 0; db < Gp::DB; ++db) {
-          const uint4 bv = *reinterpret_cast<const uint4*>(&cb.vt[16 * db + r][32 * s + 8 * q]);
-          const u32x4_t bb = u32x4_t{bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            o[rb][db] = mfma(wh[s][rb], bb, o[rb][db]);
-            o[rb][db] = mfma(wl[s][rb], bb, o[rb][db]);
-          }
-        }
-    }
-    if (more) stage_store<MODE, D>(stg, sm.buf[(tau + 1 - tau0) & 1], tid);
-    __syncthreads();
+  // two tiles per iteration so that each buffer's LDS offsets are constants
+  for (int tau = tau0; tau <= tau1; tau += 2) {
+    tile_step<MODE, D, 0>(sm, wc, stg, p, trow, tau, tau1, khi, h, tid);
+    if (tau + 1 > tau1) break;
+    tile_step<MODE, D, 1>(sm, wc, stg, p, trow, tau + 1, tau1, khi, h, tid);
   }
 
   // ---- epilogue: normalize into LDS rows, R^T, store
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const float lt = add_xor32(add_xor16(l_[rb]));
-    const float zt = add_xor32(add_xor16(z_[rb]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float li = __shfl(lt, 4 * q + i);
-      const float zi = __shfl(zt, 4 * q + i);
+      // l and Z of row 4 q + i: columns 0 + 1 and 2 + 3 of the extra block
+      const float li = __shfl(wc.o[rb][Gp::DB][i], 16 * q) + __shfl(wc.o[rb][Gp::DB][i], 16 * q + 1);
+      const float zi = __shfl(wc.o[rb][Gp::DB][i], 16 * q + 2) + __shfl(wc.o[rb][Gp::DB][i], 16 * q + 3);
       const float inv = li > 0.0f ? 1.0f / li : 0.0f;
       const int row = 32 * wave + 16 * rb + 4 * q + i;
 #pragma unroll
-      for (int db = 0; db < Gp::DB; ++db) sm.qf[row][16 * db + r] = (o[rb][db][i] + zi) * inv;
+      for (int db = 0; db < Gp::DB; ++db) sm.qf[row][16 * db + r] = (wc.o[rb][db][i] + zi) * inv;
     }
   }
   __syncthreads();
