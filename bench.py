@@ -38,12 +38,17 @@ import sub_byte_quantized_amd as kvq  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
-DECODE_SRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc", "kvq_decode.hip")
+CSRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc")
+# sources that define the decode kernels (the counter summary is tied to them)
+DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h")]
 
 
-def sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def decode_algo_bytes(spec, case, first=0):
