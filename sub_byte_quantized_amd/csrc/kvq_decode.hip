@@ -17,9 +17,9 @@
 //   sum_t w_t v_hat_t = sum_t (p_t s_t) c_t + (sum_t p_t z_t) 1 .
 // q'.c runs on v_mfma_i32_16x16x64_i8: the codes are int8 operands as they
 // are (INT8) or after two or three bit operations per 16 codes (INT4/INT2),
-// and q' is split into three int8 pieces (scale S: q' ~ S (a + b/2^7 +
-// c/2^14), |a| <= 127, |b|, |c| <= 64), so the products accumulate exactly in
-// int32.  sum_t w_t c_t runs on v_mfma_f32_16x16x32_bf16 with the codes as
+// and q' is split into two int8 pieces (scale S: q' ~ S (a + b/2^7),
+// |a| <= 127, |b| <= 64, within 2^-15 of max|q'|), so the products
+// accumulate exactly in int32.  sum_t w_t c_t runs on v_mfma_f32_16x16x32_bf16 with the codes as
 // exact bf16 integers 128 + c (one and-or per two codes) and w split into
 // bf16 hi + lo; one extra MFMA per d-tile, a constant -128 operand against the
 // weight sum in three bf16 pieces, cancels the 128 offset.
@@ -239,46 +239,54 @@ struct WaveState {
 struct LaneConst {
   const int8_t* qa;    // query pieces of this lane's B operand rows (LDS)
   const int8_t* qb;
-  const int8_t* qc;
-  float qs;            // piece scale S of the column's head
-  float q1;            // sum of the column head's represented q'
+  float sp;            // log2 logit per unit of x (S/128 of the column's head)
+  float q1r;           // sum of the column head's pieces, 128 a + b
   int q;
   int phi_col;
   bool head_ok;
   uint32_t magic, n4, n2;   // bf16 128.0 pair; nibble and crumb masks of a bf16 pair
 };
 
+// full: every position of the tile is present and inside [start, L), so no
+// score needs a mask (wave-uniform; the masking sits behind a branch).
 template <int MODE, int D, int PHI>
 __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const TileInfo& t, WaveState& st,
-                                             f32x4_t* acc, const LaneConst& lc, int L, int start) {
+                                             f32x4_t* acc, const LaneConst& lc, int L, int start, bool full) {
   using Gm = Geo<MODE, D, PHI>;
   constexpr int M = Gm::M;
   const int q = lc.q, phi_col = lc.phi_col;
-  // ---- K pass: int32 (a, b, c) dot products of the query pieces with the codes
+  // ---- K pass: int32 (a, b) dot products of the query pieces with the codes;
+  // x = s_K (128 a + b).c + z_K q1r, the log2 logit being sp * x
   float sc[Gm::NKT][4];
 #pragma unroll
   for (int tau = 0; tau < Gm::NKT; ++tau) {
-    i32x4_t ia = {0, 0, 0, 0}, ib = {0, 0, 0, 0}, ic = {0, 0, 0, 0};
+    i32x4_t ia = {0, 0, 0, 0}, ib = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < Gm::KS; ++s) {
       const u32x4_t a = unpack_k<MODE, Gm::KSW>(b.k[tau], s, 0x0F0F0F0Fu, 0x03030303u);
       const uint4 xa = *reinterpret_cast<const uint4*>(lc.qa + 16 * s);
       const uint4 xb = *reinterpret_cast<const uint4*>(lc.qb + 16 * s);
-      const uint4 xc = *reinterpret_cast<const uint4*>(lc.qc + 16 * s);
       ia = mfma_i8(a, u32x4_t{xa.x, xa.y, xa.z, xa.w}, ia);
       ib = mfma_i8(a, u32x4_t{xb.x, xb.y, xb.z, xb.w}, ib);
-      ic = mfma_i8(a, u32x4_t{xc.x, xc.y, xc.z, xc.w}, ic);
     }
-    const int sg = tau * PHI + phi_col;
-    const bool tv = lc.head_ok && ((t.valid >> sg) & 1u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pos = t.pos0 + 16 * sg + 4 * q + i;
-      const float raw = (float)((ia[i] << 7) + ib[i]) * 0.0078125f + (float)ic[i] * 6.103515625e-05f;
+      const float raw = (float)((ia[i] << 7) + ib[i]);
       const float s = M == 2 ? b.km[tau][2 * i] : b.km[tau][i];
       const float z = M == 2 ? b.km[tau][2 * i + 1] : 0.0f;
-      const float v = (s * lc.qs) * raw + z * lc.q1;
-      sc[tau][i] = (tv && pos < L && pos >= start) ? v : kNegInf;
+      sc[tau][i] = __builtin_fmaf(raw, s, z * lc.q1r);
+    }
+  }
+  if (__builtin_expect(!full, 0)) {
+#pragma unroll
+    for (int tau = 0; tau < Gm::NKT; ++tau) {
+      const int sg = tau * PHI + phi_col;
+      const bool tv = (t.valid >> sg) & 1u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = t.pos0 + 16 * sg + 4 * q + i;
+        sc[tau][i] = (tv && pos < L && pos >= start) ? sc[tau][i] : kNegInf;
+      }
     }
   }
   // ---- tile maximum of the head: lane values, lane groups q, phases of the head
@@ -287,7 +295,7 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
   for (int tau = 0; tau < Gm::NKT; ++tau)
 #pragma unroll
     for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[tau][i]);
-  tmax = max_xor32(max_xor16(tmax));
+  tmax = max_xor32(max_xor16(tmax)) * lc.sp;
   if constexpr (PHI >= 2) tmax = __builtin_fmaxf(tmax, quad_xor<1>(tmax));
   if constexpr (PHI >= 4) tmax = __builtin_fmaxf(tmax, quad_xor<2>(tmax));
   if (__any(tmax > st.m + kRescale)) {
@@ -311,13 +319,16 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
       float w2[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const float pr = __builtin_amdgcn_exp2f(sc[tau][i + e] - mu);
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[tau][i + e], lc.sp, -mu));
         const float sv = M == 2 ? b.vm[tau][2 * (i + e)] : b.vm[tau][i + e];
         const float zv = M == 2 ? b.vm[tau][2 * (i + e) + 1] : 0.0f;
-        const bool live = pr > 0.0f;
         st.l += pr;
-        st.z += live ? pr * zv : 0.0f;
-        w2[e] = live ? pr * sv : 0.0f;
+        // a masked position may sit on an absent row whose meta is not
+        // finite: its weight must be an exact zero, not 0 * NaN
+        const float svm = full ? sv : (pr > 0.0f ? sv : 0.0f);
+        const float zvm = full ? zv : (pr > 0.0f ? zv : 0.0f);
+        if constexpr (M == 2) st.z = __builtin_fmaf(pr, zvm, st.z);
+        w2[e] = pr * svm;
       }
       const uint32_t hi = pack_bf16(w2[0], w2[1]);
       const uint32_t lo = pack_bf16(w2[0] - bf16_lo(hi), w2[1] - bf16_hi(hi));
@@ -365,6 +376,14 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
   }
 }
 
+template <int MODE, int D, int PHI>
+__device__ __forceinline__ void run_tile(const Buf<MODE, D, PHI>& b, const TileInfo& t, WaveState& st,
+                                         f32x4_t* acc, const LaneConst& lc, int L, int start) {
+  if (!t.valid) return;
+  const bool full = t.valid == 0xFu && t.pos0 >= start && t.pos0 + 64 <= L;
+  compute_tile<MODE, D, PHI>(b, t, st, acc, lc, L, start, full);
+}
+
 // FWHT of `rows` rows of D floats in LDS (Sylvester, natural order), all
 // threads of the workgroup; ends with a barrier.
 template <int D>
@@ -401,7 +420,6 @@ struct Smem {
     struct {
       int8_t qa[17][D + 16];  // query pieces in k-slot order; row 16 = zeros
       int8_t qb[17][D + 16];  // (16 bytes of padding keep rows on distinct banks)
-      int8_t qc[17][D + 16];
       float qf[16][D];      // prologue scratch: R q * scale * log2(e)
     } pro;
     struct {
@@ -410,8 +428,8 @@ struct Smem {
     } comb;
     float fin[16][D];
   };
-  float qs[16];
-  float q1[16];
+  float qs[16];   // sp: log2 logit per unit of x, (max|q'| / 127) / 128
+  float q1[16];   // q1r: sum over d of 128 a + b
   int32_t ids[kMaxSplitBlocks];   // block ids of the split's range
 };
 
@@ -485,7 +503,7 @@ void decode_kernel(DecodeParams p) {
   for (int g = wave; g < 17; g += kWaves) {
     if (g >= G) {
       for (int pos = lane; pos < D; pos += 64) {
-        sm.pro.qa[g][pos] = 0; sm.pro.qb[g][pos] = 0; sm.pro.qc[g][pos] = 0;
+        sm.pro.qa[g][pos] = 0; sm.pro.qb[g][pos] = 0;
       }
       continue;
     }
@@ -493,31 +511,24 @@ void decode_kernel(DecodeParams p) {
     for (int d = lane; d < D; d += 64) mx = fmaxf(mx, fabsf(sm.pro.qf[g][d] * qmul));
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    const float S = mx / 127.0f;
+    // q' ~ (S / 128) (128 a + b), S = max|q'| / 127, |a| <= 127, |b| <= 64
     const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
-    float sa = 0.0f, sb = 0.0f, sc = 0.0f;
+    float sab = 0.0f;
     for (int pos = lane; pos < D; pos += 64) {
       const int sub = pos / Gm::SUBD, rem = pos - sub * Gm::SUBD;
       const float v = sm.pro.qf[g][kmap<MODE, D, PHI>(sub, rem >> 4, rem & 15)] * qmul;
       const float t = fminf(fmaxf(v * invS, -127.0f), 127.0f);
       const float a = __builtin_rintf(t);
-      const float r1 = (t - a) * 128.0f;
-      const float bq = __builtin_rintf(r1);
-      const float cq = __builtin_rintf((r1 - bq) * 128.0f);
+      const float bq = __builtin_rintf((t - a) * 128.0f);
       sm.pro.qa[g][pos] = (int8_t)a;
       sm.pro.qb[g][pos] = (int8_t)bq;
-      sm.pro.qc[g][pos] = (int8_t)cq;
-      sa += a; sb += bq; sc += cq;
+      sab += 128.0f * a + bq;           // exact: |sum| < 2^24
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      sa += __shfl_xor(sa, m);
-      sb += __shfl_xor(sb, m);
-      sc += __shfl_xor(sc, m);
-    }
+    for (int m = 32; m >= 1; m >>= 1) sab += __shfl_xor(sab, m);
     if (lane == 0) {
-      sm.qs[g] = S;
-      sm.q1[g] = S * (sa + sb * 0.0078125f + sc * 6.103515625e-05f);
+      sm.qs[g] = mx > 0.0f ? (mx / 127.0f) * 0.0078125f : 1.0f;
+      sm.q1[g] = sab;
     }
   }
   __syncthreads();
@@ -533,9 +544,8 @@ void decode_kernel(DecodeParams p) {
   const int brow = (lc.head_ok && phi_grp == lc.phi_col) ? g_col : 16;
   lc.qa = &sm.pro.qa[brow][sub * Gm::SUBD];
   lc.qb = &sm.pro.qb[brow][sub * Gm::SUBD];
-  lc.qc = &sm.pro.qc[brow][sub * Gm::SUBD];
-  lc.qs = lc.head_ok ? sm.qs[g_col] : 0.0f;
-  lc.q1 = lc.head_ok ? sm.q1[g_col] : 0.0f;
+  lc.sp = lc.head_ok ? sm.qs[g_col] : 1.0f;
+  lc.q1r = lc.head_ok ? sm.q1[g_col] : 0.0f;
   lc.magic = to_vgpr(p.bits_magic);
   lc.n4 = to_vgpr(p.bits_n4);
   lc.n2 = to_vgpr(p.bits_n2);
@@ -552,10 +562,10 @@ void decode_kernel(DecodeParams p) {
   for (; tile < te; tile += 2 * kWaves) {
     issue_loads<MODE, D, PHI>(bb, tn, p, r, q, lc.phi_col);
     const TileInfo t2 = tile_info(sm.ids, blk0, tile + 2 * kWaves, te, L, start, bl, hkv, h);
-    if (ta.valid) compute_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
+    run_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
     issue_loads<MODE, D, PHI>(ba, t2, p, r, q, lc.phi_col);
     const TileInfo t3 = tile_info(sm.ids, blk0, tile + 3 * kWaves, te, L, start, bl, hkv, h);
-    if (tn.valid) compute_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
+    run_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
     ta = t2;
     tn = t3;
   }
