@@ -165,11 +165,28 @@ struct TileInfo {
   uint32_t valid;           // bit sigma: sub-tile has a block and meets [start, L)
 };
 
+// CB: block_size >= 64, so a tile lies in one block and its sub-tile rows
+// are row0 + 16 s (one block id per tile; an evicted block reads rows 0..63,
+// which exist because every block slice has at least 64 rows).
+template <bool CB>
 __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int tile, int te, int L, int start,
                                               int bs_log2, int hkv, int h) {
   TileInfo t;
   t.pos0 = tile * 64;
   t.valid = 0;
+  if constexpr (CB) {
+    const bool in = tile < te;
+    const int id = __builtin_amdgcn_readfirstlane(ids[in ? (t.pos0 >> bs_log2) - blk0 : 0]);
+    const bool okb = in && id >= 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int pos = t.pos0 + 16 * s;
+      t.valid |= (okb && pos < L && pos + 15 >= start) ? 1u << s : 0u;
+    }
+    t.row0 = okb ? ((id * hkv + h) << bs_log2) + (t.pos0 & ((1 << bs_log2) - 1)) : 0;
+    t.row1 = t.row0 + 16; t.row2 = t.row0 + 32; t.row3 = t.row0 + 48;
+    return t;
+  }
   int row[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -200,13 +217,39 @@ struct Buf {
   float vm[Gm::NKT][4 * Gm::M];
 };
 
-template <int MODE, int D, int PHI>
+template <int MODE, int D, int PHI, bool CB>
 __device__ __forceinline__ void issue_loads(Buf<MODE, D, PHI>& b, const TileInfo& t, const DecodeParams& p,
                                             int r, int q, int phi_col) {
   using Gm = Geo<MODE, D, PHI>;
   constexpr int P = Gm::P, M = Gm::M;
   const int phi_grp = q * PHI / 4;          // phase of this lane group (K pass)
   const int sub = q % (4 / PHI);            // d-range of this lane group (K pass)
+  if constexpr (CB) {
+    // uniform tile bases (scalar) + per-lane constant 32-bit offsets
+    const uint8_t* kb = p.k_codes + (int64_t)t.row0 * P;
+    const uint8_t* vb = p.v_codes + (int64_t)t.row0 * P;
+    const float* kmb = p.k_meta + (int64_t)t.row0 * M;
+    const float* vmb = p.v_meta + (int64_t)t.row0 * M;
+#pragma unroll
+    for (int tau = 0; tau < Gm::NKT; ++tau) {
+      const uint32_t ko = (uint32_t)((16 * (tau * PHI + phi_grp) + r) * P + sub * Gm::KB);
+      load_bytes<Gm::KB>(b.k[tau], kb + ko);
+      const uint32_t mo = (uint32_t)((16 * (tau * PHI + phi_col) + 4 * q) * M);
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const float4 a = reinterpret_cast<const float4*>(kmb + mo)[i];
+        const float4 c = reinterpret_cast<const float4*>(vmb + mo)[i];
+        b.km[tau][4 * i] = a.x; b.km[tau][4 * i + 1] = a.y; b.km[tau][4 * i + 2] = a.z; b.km[tau][4 * i + 3] = a.w;
+        b.vm[tau][4 * i] = c.x; b.vm[tau][4 * i + 1] = c.y; b.vm[tau][4 * i + 2] = c.z; b.vm[tau][4 * i + 3] = c.w;
+      }
+    }
+    const uint32_t vo = (uint32_t)(4 * q * P + r * Gm::VB);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_bytes<Gm::VB>(b.v[4 * s + i], vb + vo + (16 * s + i) * P);
+    return;
+  }
 #pragma unroll
   for (int tau = 0; tau < Gm::NKT; ++tau) {
     const int kr = pick_row(t, tau * PHI + phi_grp) + r;
@@ -438,7 +481,7 @@ struct Smem {
 template <int MODE, int D, int PHI>
 constexpr int decode_waves_per_simd() { return (PHI == 1 || (MODE == 0 && D == 128 && PHI < 4)) ? 1 : 2; }
 
-template <int MODE, int D, int PHI, bool ROT>
+template <int MODE, int D, int PHI, bool ROT, bool CB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<MODE, D, PHI>())))
 void decode_kernel(DecodeParams p) {
   using Gm = Geo<MODE, D, PHI>;
@@ -491,10 +534,10 @@ void decode_kernel(DecodeParams p) {
   const int bl = p.block_size_log2;
   Buf<MODE, D, PHI> ba, bb;
   int tile = tb + wave;
-  TileInfo ta = tile_info(sm.ids, blk0, tile, te, L, start, bl, hkv, h);
-  TileInfo tn = tile_info(sm.ids, blk0, tile + kWaves, te, L, start, bl, hkv, h);
+  TileInfo ta = tile_info<CB>(sm.ids, blk0, tile, te, L, start, bl, hkv, h);
+  TileInfo tn = tile_info<CB>(sm.ids, blk0, tile + kWaves, te, L, start, bl, hkv, h);
   const int phi_col0 = r % PHI;
-  issue_loads<MODE, D, PHI>(ba, ta, p, r, q, phi_col0);
+  issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col0);
 
   // ---- query prologue: q' = R q * scale * log2(e), then int8 pieces in
   // k-slot order
@@ -560,11 +603,11 @@ void decode_kernel(DecodeParams p) {
   // invalid and reads row 0), so the wait counts before each compute are exact
   // and cover only the tile being computed.
   for (; tile < te; tile += 2 * kWaves) {
-    issue_loads<MODE, D, PHI>(bb, tn, p, r, q, lc.phi_col);
-    const TileInfo t2 = tile_info(sm.ids, blk0, tile + 2 * kWaves, te, L, start, bl, hkv, h);
+    issue_loads<MODE, D, PHI, CB>(bb, tn, p, r, q, lc.phi_col);
+    const TileInfo t2 = tile_info<CB>(sm.ids, blk0, tile + 2 * kWaves, te, L, start, bl, hkv, h);
     run_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
-    issue_loads<MODE, D, PHI>(ba, t2, p, r, q, lc.phi_col);
-    const TileInfo t3 = tile_info(sm.ids, blk0, tile + 3 * kWaves, te, L, start, bl, hkv, h);
+    issue_loads<MODE, D, PHI, CB>(ba, t2, p, r, q, lc.phi_col);
+    const TileInfo t3 = tile_info<CB>(sm.ids, blk0, tile + 3 * kWaves, te, L, start, bl, hkv, h);
     run_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
     ta = t2;
     tn = t3;
@@ -727,8 +770,12 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
 
 template <int MODE, int D, int PHI, bool ROT>
 hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<MODE, D, PHI, ROT>), dim3(p.max_splits, p.hkv, num_seqs),
-                     dim3(64 * kWaves), 0, s, p);
+  if (p.block_size >= 64)
+    hipLaunchKernelGGL((decode_kernel<MODE, D, PHI, ROT, true>), dim3(p.max_splits, p.hkv, num_seqs),
+                       dim3(64 * kWaves), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<MODE, D, PHI, ROT, false>), dim3(p.max_splits, p.hkv, num_seqs),
+                       dim3(64 * kWaves), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_splits == 1) return e;
   hipLaunchKernelGGL((decode_reduce_kernel<D, ROT>), dim3(p.hkv, num_seqs), dim3(256), 0, s, p);
