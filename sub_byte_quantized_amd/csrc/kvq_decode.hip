@@ -320,6 +320,16 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
       sc[tau][i] = __builtin_fmaf(raw, s, z * lc.q1r);
     }
   }
+  // V meta of the lane's positions; a masked position may sit on an absent
+  // or unwritten row whose meta is not finite, so its weight inputs are zeroed
+  float svv[Gm::NKT][4], zvv[Gm::NKT][4];
+#pragma unroll
+  for (int tau = 0; tau < Gm::NKT; ++tau)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      svv[tau][i] = M == 2 ? b.vm[tau][2 * i] : b.vm[tau][i];
+      zvv[tau][i] = M == 2 ? b.vm[tau][2 * i + 1] : 0.0f;
+    }
   if (__builtin_expect(!full, 0)) {
 #pragma unroll
     for (int tau = 0; tau < Gm::NKT; ++tau) {
@@ -328,7 +338,10 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pos = t.pos0 + 16 * sg + 4 * q + i;
-        sc[tau][i] = (tv && pos < L && pos >= start) ? sc[tau][i] : kNegInf;
+        const bool keep = tv && pos < L && pos >= start;
+        sc[tau][i] = keep ? sc[tau][i] : kNegInf;
+        svv[tau][i] = keep ? svv[tau][i] : 0.0f;
+        zvv[tau][i] = keep ? zvv[tau][i] : 0.0f;
       }
     }
   }
@@ -363,21 +376,19 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[tau][i + e], lc.sp, -mu));
-        const float sv = M == 2 ? b.vm[tau][2 * (i + e)] : b.vm[tau][i + e];
-        const float zv = M == 2 ? b.vm[tau][2 * (i + e) + 1] : 0.0f;
         st.l += pr;
-        // a masked position may sit on an absent row whose meta is not
-        // finite: its weight must be an exact zero, not 0 * NaN
-        const float svm = full ? sv : (pr > 0.0f ? sv : 0.0f);
-        const float zvm = full ? zv : (pr > 0.0f ? zv : 0.0f);
-        if constexpr (M == 2) st.z = __builtin_fmaf(pr, zvm, st.z);
-        w2[e] = pr * svm;
+        if constexpr (M == 2) st.z = __builtin_fmaf(pr, zvv[tau][i + e], st.z);
+        w2[e] = pr * svv[tau][i + e];
       }
-      const uint32_t hi = pack_bf16(w2[0], w2[1]);
-      const uint32_t lo = pack_bf16(w2[0] - bf16_lo(hi), w2[1] - bf16_hi(hi));
+      // hi = w with the low 16 bits cleared (exact bf16), lo = w - hi (exact)
+      // rounded to bf16; the represented weights hi + lo feed the offset sum
+      const float h0 = __uint_as_float(__float_as_uint(w2[0]) & 0xffff0000u);
+      const float h1 = __uint_as_float(__float_as_uint(w2[1]) & 0xffff0000u);
+      const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(h1), __float_as_uint(h0), 0x07060302u);
+      const uint32_t lo = pack_bf16(w2[0] - h0, w2[1] - h1);
       wh[tau][i / 2] = hi;
       wl[tau][i / 2] = lo;
-      wsum += (bf16_lo(hi) + bf16_lo(lo)) + (bf16_hi(hi) + bf16_hi(lo));
+      wsum += (h0 + bf16_lo(lo)) + (h1 + bf16_hi(lo));
     }
   }
   // ---- offset: acc -= 128 * (sum of the column's weights), as one MFMA per
@@ -477,9 +488,12 @@ struct Smem {
 };
 
 // Two waves per SIMD (two workgroups per CU) where the registers fit without
-// spilling, so one workgroup's prologue and epilogue overlap another's tiles.
+// spilling, so one workgroup's prologue and epilogue overlap another's tiles;
+// three for INT2 with four phases, whose tiles are the lightest.
 template <int MODE, int D, int PHI>
-constexpr int decode_waves_per_simd() { return (PHI == 1 || (MODE == 0 && D == 128 && PHI < 4)) ? 1 : 2; }
+constexpr int decode_waves_per_simd() {
+  return (PHI == 1 || (MODE == 0 && D == 128 && PHI < 4)) ? 1 : ((MODE == 2 && PHI == 4) ? 3 : 2);
+}
 
 template <int MODE, int D, int PHI, bool ROT, bool CB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<MODE, D, PHI>())))
