@@ -128,14 +128,19 @@ kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc,
                                  void* stream);
 
 /* Workspace bytes kvq_paged_decode_attention needs for these sizes (host
- * only).  max_seq_len is the largest seq_lens entry the call will see. */
+ * only).  max_seq_len is the largest seq_lens entry the call will see.  The
+ * workspace holds one counter per (sequence, kv head) and the partial
+ * softmax states of pairs that several workgroups share; its size grows with
+ * num_seqs * kv heads and the GQA group, not with max_seq_len (except for
+ * very long batches). */
 kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t num_seqs,
                                      int32_t num_q_heads, int32_t max_seq_len,
                                      size_t* bytes /* host */);
 
 /* Zero a workspace (asynchronous on `stream`; 256-byte aligned, size a
- * multiple of 16).  Decode does not need a zeroed workspace; this is a
- * convenience for callers that want deterministic contents. */
+ * multiple of 16).  A decode workspace must be zeroed once before its first
+ * use (this call, or any other zero fill); every decode call leaves its
+ * counters at zero again, so later calls need no init. */
 kvq_status kvq_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Paged decode attention (vLLM PR 40835 summary, 实现拆解 item 2: unpack,
@@ -157,10 +162,10 @@ kvq_status kvq_workspace_init(void* workspace, size_t workspace_bytes, void* str
  *   window       (device) int32 [Hkv], <= 0 = full context; or NULL
  *   softmax_scale  logits scale (usually 1/sqrt(D)); finite
  *   workspace    (device) >= kvq_decode_workspace_size bytes, 256-byte
- *                aligned (may be NULL when that size is 0); holds the
- *                per-split partial results between the two kernels a call
- *                launches when a sequence is split
- * Calls sharing one workspace must not overlap in time. */
+ *                aligned, zeroed before its first use (kvq_workspace_init);
+ *                holds per-pair counters, zero again when the call ends, and
+ *                the partial results of pairs several workgroups share
+ * Calls sharing one workspace must not overlap in time.  One kernel launch. */
 kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc,
                                       void* out, int32_t out_dtype,
                                       const void* query,

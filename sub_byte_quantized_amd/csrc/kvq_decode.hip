@@ -41,23 +41,22 @@
 //     C  acc     [16 d x 16 cols]   lane (col r, d-slots 4q..4q+3)
 //   Columns of one head are summed at the end (phases partition the tokens).
 //
-// Work split: one 256-thread workgroup (4 waves) per (split, kv head,
-// sequence); a split is a run of tiles of the sequence's active range (the
-// window), interleaved over the waves.  Each wave keeps its own online-softmax
-// state, issues the next tile's loads before computing the current one, and
-// rescales its accumulators only when a head's running maximum grows by more
-// than 2^8.  The workgroup combines its waves in LDS; with one split it
-// finishes (normalize, R^T, store), otherwise it writes (m, l, acc) to the
-// workspace and decode_reduce_kernel, launched next on the same stream,
-// combines the splits and finishes (stream order makes the partials visible;
-// no device-scope fence or atomic is needed).
+// Work split: a persistent grid of 256-thread workgroups (4 waves) takes
+// equal shares of all (sequence, kv head) pairs' tiles concatenated (see
+// decode_kernel); a share's piece of one pair is a segment, whose tiles are
+// interleaved over the waves.  Each wave keeps its own online-softmax
+// state, issues the next tile's loads before computing the current one (also
+// across segment ends), and rescales its accumulators only when a head's
+// running maximum grows by more than 2^8.  The workgroup combines its waves
+// in LDS; a whole pair is finished there (normalize, R^T, store), a cut one
+// is published as (m, l, acc) to the workspace and merged by whichever of
+// its workgroups counts in last.
 #include "kvq_internal.h"
 #include "kvq_device.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kWaves = 4;
 
 template <int MODE, int D, int PHI>
 struct Geo {
@@ -71,6 +70,11 @@ struct Geo {
   static constexpr int KSW = KW / KS;            // ... per k-step
   static constexpr int VB = P / 16;              // V bytes a lane loads per token
   static constexpr int VW = VB >= 4 ? VB / 4 : 1;
+  // VB < 4: a lane loads the aligned dword that holds its VB bytes of a
+  // token (whole dwords: every bit of the loaded register stays live, so no
+  // narrowing or zero-extension has to wait for the data) and picks its
+  // bytes with a per-lane byte selector
+  static constexpr bool NARROW = VB < 4;
   static constexpr int DT = D / 16;              // V-pass d-tiles
 };
 
@@ -108,11 +112,22 @@ __device__ __forceinline__ u32x4_t unpack_k(const uint32_t* kc, int s, uint32_t 
 
 // V-pass A operand for d-tile DTI: token slots j = 0..7 (pairs 2p, 2p+1) of
 // the lane's d = r*(D/16) + DTI, from vc[j][*].
-template <int MODE, int VW, int DTI>
+template <int MODE, int VW, int DTI, bool NARROW>
 __device__ __forceinline__ u32x4_t unpack_v(const uint32_t (*vc)[VW], uint32_t magic, uint32_t n4,
-                                            uint32_t n2) {
+                                            uint32_t n2, uint32_t vsel) {
   u32x4_t a;
-  if constexpr (MODE == 1) {
+  if constexpr (NARROW) {
+    // vsel picks byte 0 of the lane's bytes in each of the two dwords; byte
+    // b of them is vsel + b in both selector fields
+    constexpr uint32_t b = MODE == 1 ? DTI >> 1 : DTI >> 2;
+    constexpr int sh = MODE == 1 ? 4 * (DTI & 1) : 2 * (DTI & 3);
+    const uint32_t sel = vsel + b * 0x00010001u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t y = __builtin_amdgcn_perm(vc[2 * p + 1][0], vc[2 * p][0], sel);
+      a[p] = and_or(sh ? (y >> sh) : y, MODE == 1 ? n4 : n2, magic);
+    }
+  } else if constexpr (MODE == 1) {
     constexpr uint32_t b = DTI >> 1;
     constexpr uint32_t sel = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);
 #pragma unroll
@@ -141,22 +156,22 @@ __device__ __forceinline__ u32x4_t unpack_v(const uint32_t (*vc)[VW], uint32_t m
   return a;
 }
 
-template <int MODE, int VW, int DT, int DTI>
+template <int MODE, int VW, int DT, int DTI, bool NARROW>
 struct VPass {
   __device__ __forceinline__ static void run(const uint32_t (*vc)[VW], u32x4_t bh, u32x4_t bl,
-                                             f32x4_t* acc, uint32_t magic, uint32_t n4, uint32_t n2) {
-    const u32x4_t a = unpack_v<MODE, VW, DTI>(vc, magic, n4, n2);
+                                             f32x4_t* acc, uint32_t magic, uint32_t n4, uint32_t n2,
+                                             uint32_t vsel) {
+    const u32x4_t a = unpack_v<MODE, VW, DTI, NARROW>(vc, magic, n4, n2, vsel);
     acc[DTI] = mfma(a, bh, acc[DTI]);
     acc[DTI] = mfma(a, bl, acc[DTI]);
-    VPass<MODE, VW, DT, DTI + 1>::run(vc, bh, bl, acc, magic, n4, n2);
+    VPass<MODE, VW, DT, DTI + 1, NARROW>::run(vc, bh, bl, acc, magic, n4, n2, vsel);
   }
 };
-template <int MODE, int VW, int DT>
-struct VPass<MODE, VW, DT, DT> {
+template <int MODE, int VW, int DT, bool NARROW>
+struct VPass<MODE, VW, DT, DT, NARROW> {
   __device__ __forceinline__ static void run(const uint32_t (*)[VW], u32x4_t, u32x4_t, f32x4_t*, uint32_t,
-                                             uint32_t, uint32_t) {}
+                                             uint32_t, uint32_t, uint32_t) {}
 };
-
 
 // Rows and validity of one tile's four 16-token sub-tiles (wave-uniform).
 struct TileInfo {
@@ -243,11 +258,11 @@ __device__ __forceinline__ void issue_loads(Buf<MODE, D, PHI>& b, const TileInfo
         b.vm[tau][4 * i] = c.x; b.vm[tau][4 * i + 1] = c.y; b.vm[tau][4 * i + 2] = c.z; b.vm[tau][4 * i + 3] = c.w;
       }
     }
-    const uint32_t vo = (uint32_t)(4 * q * P + r * Gm::VB);
+    const uint32_t vo = (uint32_t)(4 * q * P + ((r * Gm::VB) & ~3));   // NARROW: the aligned dword
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) load_bytes<Gm::VB>(b.v[4 * s + i], vb + vo + (16 * s + i) * P);
+      for (int i = 0; i < 4; ++i) load_bytes<Gm::NARROW ? 4 : Gm::VB>(b.v[4 * s + i], vb + vo + (16 * s + i) * P);
     return;
   }
 #pragma unroll
@@ -263,13 +278,13 @@ __device__ __forceinline__ void issue_loads(Buf<MODE, D, PHI>& b, const TileInfo
       b.vm[tau][4 * i] = c.x; b.vm[tau][4 * i + 1] = c.y; b.vm[tau][4 * i + 2] = c.z; b.vm[tau][4 * i + 3] = c.w;
     }
   }
-  const int voff = 4 * q * P + r * Gm::VB;
+  const int voff = 4 * q * P + ((r * Gm::VB) & ~3);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int row = s == 0 ? t.row0 : (s == 1 ? t.row1 : (s == 2 ? t.row2 : t.row3));
     const uint8_t* base = p.v_codes + (int64_t)row * P;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_bytes<Gm::VB>(b.v[4 * s + i], base + voff + i * P);
+    for (int i = 0; i < 4; ++i) load_bytes<Gm::NARROW ? 4 : Gm::VB>(b.v[4 * s + i], base + voff + i * P);
   }
 }
 
@@ -288,6 +303,7 @@ struct LaneConst {
   int phi_col;
   bool head_ok;
   uint32_t magic, n4, n2;   // bf16 128.0 pair; nibble and crumb masks of a bf16 pair
+  uint32_t vsel;            // NARROW V rows: byte selector of the lane's first byte
 };
 
 // full: every position of the tile is present and inside [start, L), so no
@@ -426,7 +442,7 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
       bh = first ? u32x4_t{h0, h1, 0u, 0u} : u32x4_t{0u, 0u, h0, h1};
       bl = first ? u32x4_t{l0, l1, 0u, 0u} : u32x4_t{0u, 0u, l0, l1};
     }
-    VPass<MODE, Gm::VW, Gm::DT, 0>::run(b.v + 8 * u, bh, bl, acc, lc.magic, lc.n4, lc.n2);
+    VPass<MODE, Gm::VW, Gm::DT, 0, Gm::NARROW>::run(b.v + 8 * u, bh, bl, acc, lc.magic, lc.n4, lc.n2, lc.vsel);
   }
 }
 
@@ -438,384 +454,802 @@ __device__ __forceinline__ void run_tile(const Buf<MODE, D, PHI>& b, const TileI
   compute_tile<MODE, D, PHI>(b, t, st, acc, lc, L, start, full);
 }
 
-// FWHT of `rows` rows of D floats in LDS (Sylvester, natural order), all
-// threads of the workgroup; ends with a barrier.
-template <int D>
-__device__ __forceinline__ void lds_fwht(float (*x)[D], int rows, int tid) {
-  for (int hh = 1; hh < D; hh <<= 1) {
-    for (int e = tid; e < rows * (D / 2); e += 64 * kWaves) {
-      const int g = e / (D / 2), k = e - g * (D / 2);
-      const int i = (k / hh) * 2 * hh + (k % hh);
-      const float a = x[g][i], bb = x[g][i + hh];
-      x[g][i] = a + bb;
-      x[g][i + hh] = a - bb;
-    }
-    __syncthreads();
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_rows(const DecodeParams& p, float (*fin)[D], int G, int64_t orow0,
-                                           int tid, bool rot) {
-  for (int e = tid; e < G * D; e += 64 * kWaves) {
-    const int g = e / D, d = e - g * D;
-    float v = fin[g][d];
-    if (rot) v = v * p.signs[d] * p.inv_sqrt_d;
-    if (p.out_bf16)
-      reinterpret_cast<__bf16*>(p.out)[(orow0 + g) * D + d] = (__bf16)v;
-    else
-      reinterpret_cast<float*>(p.out)[(orow0 + g) * D + d] = v;
-  }
-}
-
-template <int D>
-struct Smem {
-  union {
-    struct {
-      int8_t qa[17][D + 16];  // query pieces in k-slot order; row 16 = zeros
-      int8_t qb[17][D + 16];  // (16 bytes of padding keep rows on distinct banks)
-      float qf[16][D];      // prologue scratch: R q * scale * log2(e)
-    } pro;
-    struct {
-      float acc[kWaves][16][D];
-      float ml[kWaves][16][2];
-    } comb;
-    float fin[16][D];
-  };
-  float qs[16];   // sp: log2 logit per unit of x, (max|q'| / 127) / 128
-  float q1[16];   // q1r: sum over d of 128 a + b
-  int32_t ids[kMaxSplitBlocks];   // block ids of the split's range
-};
-
-// Two waves per SIMD (two workgroups per CU) where the registers fit without
-// spilling, so one workgroup's prologue and epilogue overlap another's tiles;
-// three for INT2 with four phases, whose tiles are the lightest.
+// Waves per SIMD, i.e. resident four-wave workgroups per CU: two where the
+// registers fit without spilling, so one workgroup's prologue and epilogue
+// overlap another's tiles; three for INT2 with four phases, whose tiles are
+// the lightest; one where a tile needs the whole register file.
 template <int MODE, int D, int PHI>
 constexpr int decode_waves_per_simd() {
   return (PHI == 1 || (MODE == 0 && D == 128 && PHI < 4)) ? 1 : ((MODE == 2 && PHI == 4) ? 3 : 2);
 }
 
-template <int MODE, int D, int PHI, bool ROT, bool CB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<MODE, D, PHI>())))
-void decode_kernel(DecodeParams p) {
-  using Gm = Geo<MODE, D, PHI>;
-  __shared__ Smem<D> sm;
+// Waves per workgroup.
+template <int MODE, int D, int PHI>
+constexpr int decode_wg_waves() { return 4; }
 
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const int lane = tid & 63;
-  const int r = lane & 15;
-  const int q = lane >> 4;
-  const int G = p.group;
-  const int hkv = p.hkv;
+// ---------------------------------------------------------------------------
+// Whole rows of D values, one row per wave: lane holds d = E*lane + e with
+// E = D/64.
 
-  const int L = p.seq_lens[b];
-  const int W = p.window ? p.window[h] : 0;
-  const int start = (W > 0 && L > W) ? L - W : 0;
-  const int t0 = start / 64;
-  const int t1 = (L + 63) / 64;
-  const int n_tiles = L > 0 ? t1 - t0 : 0;
-  const int tps = p.chunks_per_split;   // tiles per split
-  const int n_splits = n_tiles > 0 ? (n_tiles + tps - 1) / tps : 1;
-  if (split >= n_splits) return;
-  const int tb = t0 + split * tps;
-  const int te = min(t1, tb + tps);
-  const int32_t* trow = p.tables + (int64_t)(p.headwise ? b * hkv + h : b) * p.max_blocks;
-  const int64_t orow0 = (int64_t)b * p.hq + h * G;
-
-  // ---- block ids of the split's positions [64 tb, min(64 te, L)) and the raw
-  // query rows into LDS
-  const int blk0 = (tb * 64) >> p.block_size_log2;
-  {
-    const int last_pos = min(te * 64, L) - 1;
-    const int n_ids = last_pos >= tb * 64 ? (last_pos >> p.block_size_log2) - blk0 + 1 : 0;
-    for (int i = tid; i < n_ids; i += 64 * kWaves) sm.ids[i] = trow[blk0 + i];
-    if (n_ids == 0 && tid == 0) sm.ids[0] = -1;
+// In-register Sylvester FWHT of one row (natural order, unnormalized).  The
+// stages h = 1, 2, ..., D/2 run in that order: stage h maps the pair
+// (d, d + h), bit h of d clear, to (x_d + x_{d+h}, x_d - x_{d+h}); within the
+// lane for h < E, across lanes (lane ^ h/E) otherwise.
+template <int D>
+__device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane) {
+  constexpr int E = D / 64;
+  if constexpr (E == 2) {
+    const float a = x[0], b = x[1];
+    x[0] = a + b;
+    x[1] = a - b;
   }
-  for (int e = tid; e < G * D; e += 64 * kWaves) {
-    const int g = e / D, d = e - g * D;
-    float v = __uint_as_float((uint32_t)p.q[(orow0 + g) * D + d] << 16);
-    if constexpr (ROT) v *= p.signs[d];
-    sm.pro.qf[g][d] = v;
-  }
-  __syncthreads();
-
-  // ---- first tiles' loads go out before the query prologue, which they do
-  // not depend on, so their latency overlaps it
-  const int bl = p.block_size_log2;
-  Buf<MODE, D, PHI> ba, bb;
-  int tile = tb + wave;
-  TileInfo ta = tile_info<CB>(sm.ids, blk0, tile, te, L, start, bl, hkv, h);
-  TileInfo tn = tile_info<CB>(sm.ids, blk0, tile + kWaves, te, L, start, bl, hkv, h);
-  const int phi_col0 = r % PHI;
-  issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col0);
-
-  // ---- query prologue: q' = R q * scale * log2(e), then int8 pieces in
-  // k-slot order
-  if constexpr (ROT) lds_fwht<D>(sm.pro.qf, G, tid);
-  const float qmul = ROT ? p.qscale * p.inv_sqrt_d : p.qscale;
-  for (int g = wave; g < 17; g += kWaves) {
-    if (g >= G) {
-      for (int pos = lane; pos < D; pos += 64) {
-        sm.pro.qa[g][pos] = 0; sm.pro.qb[g][pos] = 0;
-      }
-      continue;
-    }
-    float mx = 0.0f;
-    for (int d = lane; d < D; d += 64) mx = fmaxf(mx, fabsf(sm.pro.qf[g][d] * qmul));
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    // q' ~ (S / 128) (128 a + b), S = max|q'| / 127, |a| <= 127, |b| <= 64
-    const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
-    float sab = 0.0f;
-    for (int pos = lane; pos < D; pos += 64) {
-      const int sub = pos / Gm::SUBD, rem = pos - sub * Gm::SUBD;
-      const float v = sm.pro.qf[g][kmap<MODE, D, PHI>(sub, rem >> 4, rem & 15)] * qmul;
-      const float t = fminf(fmaxf(v * invS, -127.0f), 127.0f);
-      const float a = __builtin_rintf(t);
-      const float bq = __builtin_rintf((t - a) * 128.0f);
-      sm.pro.qa[g][pos] = (int8_t)a;
-      sm.pro.qb[g][pos] = (int8_t)bq;
-      sab += 128.0f * a + bq;           // exact: |sum| < 2^24
-    }
+  for (int hl = 1; hl < 64; hl <<= 1) {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) sab += __shfl_xor(sab, m);
-    if (lane == 0) {
-      sm.qs[g] = mx > 0.0f ? (mx / 127.0f) * 0.0078125f : 1.0f;
-      sm.q1[g] = sab;
-    }
-  }
-  __syncthreads();
-
-  // ---- per-lane constants
-  LaneConst lc;
-  const int g_col = r / PHI;            // head of this lane's MFMA column
-  lc.q = q;
-  lc.phi_col = r % PHI;                 // phase of this lane's MFMA column
-  lc.head_ok = g_col < G;
-  const int phi_grp = q * PHI / 4;      // phase of this lane group (K pass)
-  const int sub = q % (4 / PHI);
-  const int brow = (lc.head_ok && phi_grp == lc.phi_col) ? g_col : 16;
-  lc.qa = &sm.pro.qa[brow][sub * Gm::SUBD];
-  lc.qb = &sm.pro.qb[brow][sub * Gm::SUBD];
-  lc.sp = lc.head_ok ? sm.qs[g_col] : 1.0f;
-  lc.q1r = lc.head_ok ? sm.q1[g_col] : 0.0f;
-  lc.magic = to_vgpr(p.bits_magic);
-  lc.n4 = to_vgpr(p.bits_n4);
-  lc.n2 = to_vgpr(p.bits_n2);
-
-  WaveState st{kNegInf, 0.0f, 0.0f};
-  f32x4_t acc[Gm::DT];
-#pragma unroll
-  for (int i = 0; i < Gm::DT; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // ---- tiles tb + wave, tb + wave + 4, ...: two buffers, loads one tile ahead.
-  // Every half-iteration issues the same loads (a tile past the split end is
-  // invalid and reads row 0), so the wait counts before each compute are exact
-  // and cover only the tile being computed.
-  for (; tile < te; tile += 2 * kWaves) {
-    issue_loads<MODE, D, PHI, CB>(bb, tn, p, r, q, lc.phi_col);
-    const TileInfo t2 = tile_info<CB>(sm.ids, blk0, tile + 2 * kWaves, te, L, start, bl, hkv, h);
-    run_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
-    issue_loads<MODE, D, PHI, CB>(ba, t2, p, r, q, lc.phi_col);
-    const TileInfo t3 = tile_info<CB>(sm.ids, blk0, tile + 3 * kWaves, te, L, start, bl, hkv, h);
-    run_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
-    ta = t2;
-    tn = t3;
-  }
-
-  // ---- wave epilogue: sum the phases of a head, then l and z over lane groups
-  if constexpr (PHI >= 2) {
-#pragma unroll
-    for (int i = 0; i < Gm::DT; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] += quad_xor<1>(acc[i][j]);
-    st.l += quad_xor<1>(st.l);
-    st.z += quad_xor<1>(st.z);
-  }
-  if constexpr (PHI >= 4) {
-#pragma unroll
-    for (int i = 0; i < Gm::DT; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] += quad_xor<2>(acc[i][j]);
-    st.l += quad_xor<2>(st.l);
-    st.z += quad_xor<2>(st.z);
-  }
-  st.l = add_xor32(add_xor16(st.l));
-  st.z = add_xor32(add_xor16(st.z));
-  __syncthreads();   // the prologue area becomes the combine area
-  if (lc.head_ok && lc.phi_col == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int dt = 0; dt < Gm::DT; ++dt) sm.comb.acc[wave][g_col][(4 * q + i) * Gm::DT + dt] = acc[dt][i] + st.z;
-    if (q == 0) {
-      sm.comb.ml[wave][g_col][0] = st.m;
-      sm.comb.ml[wave][g_col][1] = st.l;
-    }
-  }
-  __syncthreads();
-
-  // ---- workgroup combine: each thread owns (g, d) pairs
-  constexpr int PER = (16 * D + 64 * kWaves - 1) / (64 * kWaves);
-  float val[PER];
-  float lsum[PER];
-  float mmax[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e = tid + k * 64 * kWaves;
-    val[k] = 0.0f; lsum[k] = 0.0f; mmax[k] = kNegInf;
-    if (e < G * D) {
-      const int g = e / D, d = e - g * D;
-      float mx = kNegInf;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.comb.ml[w][g][0]);
-      const float mu = mx == kNegInf ? 0.0f : mx;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = __builtin_amdgcn_exp2f(sm.comb.ml[w][g][0] - mu);
-        val[k] += f * sm.comb.acc[w][g][d];
-        lsum[k] += f * sm.comb.ml[w][g][1];
-      }
-      mmax[k] = mx;
-    }
-  }
-  __syncthreads();
-
-  if (n_splits == 1) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int e = tid + k * 64 * kWaves;
-      if (e < G * D) sm.fin[e / D][e % D] = lsum[k] > 0.0f ? val[k] / lsum[k] : 0.0f;
-    }
-    __syncthreads();
-    if constexpr (ROT) lds_fwht<D>(sm.fin, G, tid);
-    store_rows<D>(p, sm.fin, G, orow0, tid, ROT);
-    return;
-  }
-
-  // ---- several splits: publish (m, l, acc); decode_reduce_kernel combines
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e = tid + k * 64 * kWaves;
-    if (e < G * D) {
-      const int g = e / D, d = e - g * D;
-      float* rec = p.partials + ((orow0 + g) * p.max_splits + split) * (D + 4);
-      rec[4 + d] = val[k];
-      if (d == 0) {
-        rec[0] = mmax[k];
-        rec[1] = lsum[k];
-      }
+    for (int e = 0; e < E; ++e) {
+      const float y = __shfl_xor(x[e], hl);
+      x[e] = (lane & hl) ? y - x[e] : x[e] + y;
     }
   }
 }
 
-// Cross-split combine, launched after decode_kernel on the same stream when a
-// (sequence, kv head) can have several splits: one workgroup per (sequence,
-// kv head) merges the splits' (m, l, acc) of its G heads, normalizes, applies
-// R^T and stores.
+// The lane's E bf16 values of a query row, as loaded (one dword or one short).
+template <int D>
+__device__ __forceinline__ uint32_t load_qrow(const uint16_t* src, int lane) {
+  if constexpr (D == 128) return reinterpret_cast<const uint32_t*>(src)[lane];
+  else return src[lane];
+}
+
+// One query row: q' = R q * scale * log2(e), then its two int8 pieces in
+// k-slot order (q' ~ (S/128)(128 a + b), S = max|q'|/127, |a| <= 127,
+// |b| <= 64), sp = S/128 and q1r = sum(128 a + b).  `scratch` is the wave's
+// own D floats of LDS (written and read back by the same wave, in order).
+template <int MODE, int D, int PHI, bool ROT>
+__device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, float* scratch, int8_t* qa,
+                                           int8_t* qb, float* qs, float* q1, int lane) {
+  using Gm = Geo<MODE, D, PHI>;
+  constexpr int E = D / 64;
+  float x[E];
+  if constexpr (E == 2) {
+    x[0] = __uint_as_float(raw << 16);
+    x[1] = __uint_as_float(raw & 0xffff0000u);
+  } else {
+    x[0] = __uint_as_float(raw << 16);
+  }
+  if constexpr (ROT) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] *= p.signs[E * lane + e];
+    wave_fwht<D>(x, lane);
+  }
+  const float qmul = ROT ? p.qscale * p.inv_sqrt_d : p.qscale;
+  float mx = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] *= qmul;
+    mx = fmaxf(mx, fabsf(x[e]));
+    scratch[E * lane + e] = x[e];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
+  float sab = 0.0f;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int pos = lane + 64 * j;
+    const int sub = pos / Gm::SUBD, rem = pos - sub * Gm::SUBD;
+    const float v = scratch[kmap<MODE, D, PHI>(sub, rem >> 4, rem & 15)];
+    const float t = fminf(fmaxf(v * invS, -127.0f), 127.0f);
+    const float a = __builtin_rintf(t);
+    const float bq = __builtin_rintf((t - a) * 128.0f);
+    qa[pos] = (int8_t)a;
+    qb[pos] = (int8_t)bq;
+    sab += 128.0f * a + bq;           // exact: |sum| < 2^24
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) sab += __shfl_xor(sab, m);
+  if (lane == 0) {
+    *qs = mx > 0.0f ? (mx / 127.0f) * 0.0078125f : 1.0f;
+    *q1 = sab;
+  }
+}
+
+// One output row from its D normalized values in LDS: R^T (FWHT, signs,
+// 1/sqrt(D)) when rotated, then float32 or bf16 stores.
 template <int D, bool ROT>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
-  __shared__ float fin[16][D];
-  __shared__ float wgt[16][kMaxReduceSplits];
-  __shared__ float inv_l[16];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int G = p.group;
-  const int L = p.seq_lens[b];
+__device__ __forceinline__ void finish_row(const DecodeParams& p, const float* src, int64_t orow, int lane) {
+  constexpr int E = D / 64;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = src[E * lane + e];
+  if constexpr (ROT) {
+    wave_fwht<D>(x, lane);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = x[e] * p.signs[E * lane + e] * p.inv_sqrt_d;
+  }
+  if (p.out_bf16) {
+    __bf16* o = reinterpret_cast<__bf16*>(p.out) + orow * D + E * lane;
+    if constexpr (E == 2) *reinterpret_cast<uint32_t*>(o) = pack_bf16(x[0], x[1]);
+    else o[0] = (__bf16)x[0];
+  } else {
+    float* o = reinterpret_cast<float*>(p.out) + orow * D + E * lane;
+    if constexpr (E == 2) *reinterpret_cast<float2*>(o) = make_float2(x[0], x[1]);
+    else o[0] = x[0];
+  }
+}
+
+constexpr int kPrefChunk = 1024;   // pairs whose tile prefix one LDS pass holds
+
+// A workgroup's piece of one (sequence, kv head) pair's tile range.
+struct SegRec {
+  int b, h;          // sequence, kv head
+  int tb, te;        // tiles [tb, te) of the pair (tile t = positions 64t ..)
+  int L, start;      // attended positions [start, L)
+  int ids_off;       // LDS ids[ids_off + j] = table entry blk0 + j
+  int blk0;
+  int n_ids;
+  int slot;          // partial slot, or -1: the segment is the whole pair
+  int pad[2];
+};
+
+template <int D, int PHI, int NWV>
+struct Smem {
+  static constexpr int GM = 16 / PHI;   // most heads of a kv head's group (G * PHI <= 16)
+  static constexpr int NS = 32 / GM;    // segments of one batch (their pieces stay in LDS)
+  static constexpr int QW = D + 16;     // piece row stride: 16 bytes of padding spread banks
+  alignas(16) int8_t qa[NS][GM][QW];    // query pieces in k-slot order
+  alignas(16) int8_t qb[NS][GM][QW];
+  alignas(16) int8_t qzero[QW];         // B rows of columns without work
+  float qs[NS][GM];                     // sp: (max|q'| / 127) / 128
+  float q1[NS][GM];                     // q1r: sum over d of 128 a + b
+  SegRec seg[NS];
+  int32_t ids[kMaxSplitBlocks];         // block ids of the batch's segments
+  union {
+    struct {
+      float acc[NWV][GM][D];
+      float ml[NWV][GM][2];
+    } comb;                             // per-wave (m, l, acc) of a segment
+    struct {
+      float fin[GM][D];                 // normalized rows before R^T
+      float cw[GM][64];                 // piece merge: factor of each piece
+    } fw;
+    float qrow[NWV][D];                 // query prologue scratch, one row per wave
+  };
+  float cm[GM];                         // piece merge: max m, 1 / l
+  float cl[GM];
+  int32_t pref[kPrefChunk + 1];         // inclusive tile prefix of a chunk of pairs
+  int32_t plen[kPrefChunk];             // its pairs' attended end L and start
+  int32_t pst[kPrefChunk];
+  int32_t part[64 * NWV];
+  int32_t pend[2][3];                   // pieces this workgroup published: pair, s0, s1
+  int32_t flag;
+};
+
+// Tiles of (sequence b, kv head h): 64-position tiles from the window start
+// (or 0) to seq_len; *t0 = first tile, *L = attended end, *start = begin.
+__device__ __forceinline__ int pair_geo(const DecodeParams& p, int pair, int* t0, int* L, int* start) {
+  const int b = pair / p.hkv, h = pair - b * p.hkv;
+  const int l = min(p.seq_lens[b], p.max_blocks << p.block_size_log2);
   const int W = p.window ? p.window[h] : 0;
-  const int start = (W > 0 && L > W) ? L - W : 0;
-  const int n_tiles = L > 0 ? (L + 63) / 64 - start / 64 : 0;
-  const int tps = p.chunks_per_split;
-  const int n_splits = n_tiles > 0 ? (n_tiles + tps - 1) / tps : 1;
-  if (n_splits == 1) return;   // decode_kernel already stored this (sequence, kv head)
-  const int64_t orow0 = (int64_t)b * p.hq + h * G;
-  // weights exp2(m_s - M) of every (head, split), and 1 / sum_s w_s l_s
-  for (int g = tid >> 6; g < G; g += 4) {
-    const int lane = tid & 63;
-    const float* base = p.partials + (orow0 + g) * p.max_splits * (D + 4);
+  const int s = (W > 0 && l > W) ? l - W : 0;
+  *t0 = s / 64;
+  *L = l;
+  *start = s;
+  return l > 0 ? (l + 63) / 64 - s / 64 : 0;
+}
+
+// The share partition: workgroup w takes tiles [w T / nw, (w + 1) T / nw)
+// of the T concatenated tiles (nw <= T, so no share is empty).
+struct Part {
+  int T, nw;
+  __device__ int start(int w) const { return (int)(((int64_t)T * w) / nw); }
+  // workgroup whose share holds tile x (0 <= x < T)
+  __device__ int owner(int x) const {
+    int w = (int)(((int64_t)x * nw) / T);
+    while (w + 1 < nw && start(w + 1) <= x) ++w;
+    while (w > 0 && start(w) > x) --w;
+    return w;
+  }
+};
+
+// Wave priority for the rounds of a persistent grid: with several
+// workgroups per CU (dispatch rounds of ncu workgroups), the SIMDs' issue
+// arbitration favours the oldest waves, so the last round's shares would
+// finish well after the first's; instead each wave's priority rotates
+// (0, 1, 2, ... per tile pair), offset by its round, and the rounds take
+// turns at the top.
+__device__ __forceinline__ void set_prio(int k) {
+  if (k == 0) __builtin_amdgcn_s_setprio(0);
+  else if (k == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(2);
+}
+
+// Workgroups in the partition: never more than tiles.
+__device__ __forceinline__ int active_wgs(int grid, int T) { return max(1, min(grid, T)); }
+
+// Tiles of one segment that wave `wave` computes: tb + wave + 4 i, padded to
+// an even count (the pad is past te, hence invalid) so the two load buffers
+// keep their roles across segments.
+__device__ __forceinline__ int wave_tiles2(int n, int wave) {
+  const int k = n > wave ? (n - wave + 3) >> 2 : 0;
+  return k + (k & 1);
+}
+
+// The wave's next tile to load, walking its tiles of the batch's segments in
+// order (wave-uniform, scalar registers).
+struct Cursor {
+  int ls, li, nseg;
+  int tb, te, off, blk0, L, start, h, n2;
+};
+
+template <int D, int PHI, int NWV>
+__device__ __forceinline__ void cursor_seek(Cursor& c, const Smem<D, PHI, NWV>& sm, int wave) {
+  for (; c.ls < c.nseg; ++c.ls) {
+    const SegRec& s = sm.seg[c.ls];
+    c.tb = __builtin_amdgcn_readfirstlane(s.tb);
+    c.te = __builtin_amdgcn_readfirstlane(s.te);
+    c.n2 = wave_tiles2(c.te - c.tb, wave);
+    if (c.n2 > 0) {
+      c.off = __builtin_amdgcn_readfirstlane(s.ids_off);
+      c.blk0 = __builtin_amdgcn_readfirstlane(s.blk0);
+      c.L = __builtin_amdgcn_readfirstlane(s.L);
+      c.start = __builtin_amdgcn_readfirstlane(s.start);
+      c.h = __builtin_amdgcn_readfirstlane(s.h);
+      return;
+    }
+  }
+}
+
+template <bool CB, int D, int PHI, int NWV>
+__device__ __forceinline__ TileInfo cursor_info(const Cursor& c, const Smem<D, PHI, NWV>& sm, int wave, int bl,
+                                                int hkv) {
+  if (c.ls >= c.nseg) {
+    TileInfo t;
+    t.pos0 = 0; t.row0 = 0; t.row1 = 0; t.row2 = 0; t.row3 = 0; t.valid = 0;
+    return t;
+  }
+  return tile_info<CB>(sm.ids + c.off, c.blk0, c.tb + wave + 4 * c.li, c.te, c.L, c.start, bl, hkv, c.h);
+}
+
+template <int D, int PHI, int NWV>
+__device__ __forceinline__ void cursor_next(Cursor& c, const Smem<D, PHI, NWV>& sm, int wave) {
+  if (++c.li < c.n2) return;
+  c.li = 0;
+  ++c.ls;
+  cursor_seek(c, sm, wave);
+}
+
+// Pieces cross workgroups (and XCDs, whose L2s are not coherent with each
+// other): they are stored and loaded with device scope, so they go to and
+// come from the device-coherent level instead of a stale L2 line, and no
+// cache-wide writeback or invalidate is needed.
+__device__ __forceinline__ void store_dev(float* a, float v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the published pieces of one pair (slots slot0 .. slot0 + n - 1),
+// normalize, R^T and store.  All threads; ends with the rows stored.
+template <int D, int PHI, int NWV, bool ROT>
+__device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI, NWV>& sm, int slot0, int n,
+                                             int64_t orow0, int tid) {
+  constexpr int NT = 64 * NWV;
+  const int G = p.group;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t stride = (int64_t)G * (D + 4);   // floats between consecutive pieces
+  // per head: M = max_s m_s and 1 / sum_s 2^(m_s - M) l_s
+  for (int g = wave; g < G; g += NWV) {
+    const float* base = p.partials + ((int64_t)slot0 * G + g) * (D + 4);
     float mx = kNegInf;
-    for (int s = lane; s < n_splits; s += 64) mx = fmaxf(mx, base[s * (D + 4)]);
+    for (int s = lane; s < n; s += 64) mx = fmaxf(mx, load_dev(base + s * stride));
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
     const float mu = mx == kNegInf ? 0.0f : mx;
     float l = 0.0f;
-    for (int s = lane; s < n_splits; s += 64) {
-      const float w = __builtin_amdgcn_exp2f(base[s * (D + 4)] - mu);
-      wgt[g][s] = w;
-      l += w * base[s * (D + 4) + 1];
-    }
+    for (int s = lane; s < n; s += 64)
+      l += __builtin_amdgcn_exp2f(load_dev(base + s * stride) - mu) * load_dev(base + s * stride + 1);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) l += __shfl_xor(l, m);
-    if (lane == 0) inv_l[g] = l > 0.0f ? 1.0f / l : 0.0f;
-  }
-  __syncthreads();
-  for (int e = tid; e < G * D; e += 256) {
-    const int g = e / D, d = e - g * D;
-    const float* base = p.partials + (orow0 + g) * p.max_splits * (D + 4) + 4 + d;
-    float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
-    int s = 0;
-    for (; s + 4 <= n_splits; s += 4) {
-      v0 += wgt[g][s] * base[s * (D + 4)];
-      v1 += wgt[g][s + 1] * base[(s + 1) * (D + 4)];
-      v2 += wgt[g][s + 2] * base[(s + 2) * (D + 4)];
-      v3 += wgt[g][s + 3] * base[(s + 3) * (D + 4)];
+    if (lane == 0) {
+      sm.cm[g] = mu;
+      sm.cl[g] = l > 0.0f ? 1.0f / l : 0.0f;
     }
-    for (; s < n_splits; ++s) v0 += wgt[g][s] * base[s * (D + 4)];
-    fin[g][d] = ((v0 + v1) + (v2 + v3)) * inv_l[g];
   }
   __syncthreads();
-  if constexpr (ROT) {
-    for (int hh = 1; hh < D; hh <<= 1) {
-      for (int e = tid; e < G * (D / 2); e += 256) {
-        const int g = e / (D / 2), k = e - g * (D / 2);
-        const int i = (k / hh) * 2 * hh + (k % hh);
-        const float a = fin[g][i], bb = fin[g][i + hh];
-        fin[g][i] = a + bb;
-        fin[g][i + hh] = a - bb;
+  // out = sum_s (2^(m_s - M) / l) acc_s, 64 pieces at a time, each piece's
+  // factor staged in LDS and the pieces' values requested eight at a time
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int cnt = min(64, n - s0);
+    for (int g = wave; g < G; g += NWV) {
+      if (lane < cnt) {
+        const float* base = p.partials + ((int64_t)(slot0 + s0 + lane) * G + g) * (D + 4);
+        sm.fw.cw[g][lane] = __builtin_amdgcn_exp2f(load_dev(base) - sm.cm[g]) * sm.cl[g];
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * D; e += NT) {
+      const int g = e / D, d = e - g * D;
+      const float* base = p.partials + ((int64_t)(slot0 + s0) * G + g) * (D + 4) + 4 + d;
+      float v = s0 == 0 ? 0.0f : sm.fw.fin[g][d];
+      int j = 0;
+      for (; j + 8 <= cnt; j += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = load_dev(base + (j + u) * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v = __builtin_fmaf(sm.fw.cw[g][j + u], x[u], v);
+      }
+      for (; j < cnt; ++j) v = __builtin_fmaf(sm.fw.cw[g][j], load_dev(base + j * stride), v);
+      sm.fw.fin[g][d] = v;
+    }
+    __syncthreads();
+  }
+  for (int g = wave; g < G; g += NWV) finish_row<D, ROT>(p, sm.fw.fin[g], orow0 + g, lane);
+}
+
+// Inclusive tile prefix of pairs [c0, c0 + cn) into pref[1 .. cn] (pref[0] =
+// 0); returns the chunk's tile total.  All threads of the workgroup; each
+// thread takes a run of consecutive pairs, the runs are scanned within the
+// wave by shuffles and across the waves in LDS.  Ends with a barrier.
+template <int NWV>
+__device__ __forceinline__ int scan_chunk(const DecodeParams& p, int32_t* pref, int32_t* plen, int32_t* pst,
+                                          int32_t* part, int c0, int cn, int tid) {
+  constexpr int NT = 64 * NWV;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per = (cn + NT - 1) / NT;
+  int run = 0;
+  for (int k = 0; k < per; ++k) {
+    const int i = tid * per + k;
+    if (i < cn) {
+      int t0, L, s;
+      run += pair_geo(p, c0 + i, &t0, &L, &s);
+      pref[i + 1] = run;
+      plen[i] = L;
+      pst[i] = s;
+    }
+  }
+  int x = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) part[wave] = x;
+  __syncthreads();
+  int before = x - run;
+  for (int v = 0; v < wave; ++v) before += part[v];
+  int tot = 0;
+#pragma unroll
+  for (int v = 0; v < NWV; ++v) tot += part[v];
+  for (int k = 0; k < per; ++k) {
+    const int i = tid * per + k;
+    if (i < cn) pref[i + 1] += before;
+  }
+  if (tid == 0) pref[0] = 0;
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(tot);
+}
+
+// First pair of a chunk whose range ends after tile x (cn if none).
+__device__ __forceinline__ int first_after(const int32_t* pref, int cn, int cbase, int x) {
+  int lo = 0, hi = cn;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (cbase + __builtin_amdgcn_readfirstlane(pref[mid + 1]) <= x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Stream-K decode: a persistent grid of n_wgs workgroups.  The (sequence, kv
+// head) pairs' tile ranges are concatenated in pair order (T tiles in all);
+// workgroup w takes tiles [w T / NW, (w + 1) T / NW): the tail of one pair,
+// some whole pairs, the head of another.  Each piece of a pair is a segment.
+// Segments go in batches: the batch's block ids and query pieces are staged
+// in LDS first; then every wave walks its tiles of all the batch's segments
+// as one stream with one tile of look-ahead, so the loads of a segment's
+// first tile are in flight while the previous segment is combined.  A whole
+// pair is finished in place; a cut one writes (m, l, acc) to slot
+// first_wg(pair) + pair + (w - first_wg(pair)) of the workspace and, at the
+// end, bumps the pair's counter: the workgroup that brings it to the pieces'
+// count merges them and resets it to zero.  Every workgroup scans the pairs'
+// tile counts itself; there is no other launch and no waiting on another
+// workgroup.
+template <int MODE, int D, int PHI, bool ROT, bool CB, int NWV>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<MODE, D, PHI>())))
+void decode_kernel(DecodeParams p) {
+  using Sm = Smem<D, PHI, NWV>;
+  using Gm = Geo<MODE, D, PHI>;
+  constexpr int NT = 64 * NWV, NS = Sm::NS;
+  __shared__ Sm sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, r = lane & 15, q = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = p.num_pairs, G = p.group, hkv = p.hkv, bl = p.block_size_log2;
+  const int w = blockIdx.x;
+
+  // ---- tile prefix of the first chunk of pairs; total tiles
+  for (int i = tid; i < Sm::QW; i += NT) sm.qzero[i] = 0;
+  int cn = min(kPrefChunk, P);
+  int ctot = scan_chunk<NWV>(p, sm.pref, sm.plen, sm.pst, sm.part, 0, cn, tid);
+  int T = ctot;
+  if (P > cn) {
+    int my = 0;
+    for (int i = cn + tid; i < P; i += NT) {
+      int t0, L, s;
+      my += pair_geo(p, i, &t0, &L, &s);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) my += __shfl_xor(my, m);
+    if (lane == 0) sm.part[wave] = my;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) T += __builtin_amdgcn_readfirstlane(sm.part[i]);
+    __syncthreads();
+  }
+  Part part;
+  part.T = T;
+  part.nw = active_wgs(gridDim.x, T);
+  const int nw = part.nw;
+  if (w >= nw) return;
+  const int a_my = part.start(w), e_my = part.start(w + 1);
+
+  // ---- pairs without tiles (an empty sequence) get zero rows; pair i falls
+  // to workgroup i % nw
+  for (int i = w + tid * nw; i < P; i += NT * nw) {
+    int t0, L, s;
+    if (pair_geo(p, i, &t0, &L, &s) == 0) {
+      const int b = i / hkv, h = i - b * hkv;
+      const int64_t o = ((int64_t)b * p.hq + h * G) * D;
+      for (int e = 0; e < G * D; ++e) {
+        if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[o + e] = (__bf16)0.0f;
+        else reinterpret_cast<float*>(p.out)[o + e] = 0.0f;
+      }
+    }
+  }
+
+  // ---- per-lane constants of the MFMA columns
+  const int g_col = r / PHI;            // head of this lane's MFMA column
+  const int phi_col = r % PHI;          // phase of this lane's MFMA column
+  const int phi_grp = q * PHI / 4;      // phase of this lane group (K pass)
+  const int sub = q % (4 / PHI);
+  const uint32_t magic = to_vgpr(p.bits_magic), n4 = to_vgpr(p.bits_n4), n2m = to_vgpr(p.bits_n2);
+  // byte (r * VB) % 4 of the dword in both selector fields, zero bytes between
+  const uint32_t vsel0 = (uint32_t)((r * Gm::VB) & 3);
+  const uint32_t vsel = vsel0 | 0x0C00u | ((4u + vsel0) << 16) | 0x0C000000u;
+
+  // chunk of pairs whose prefix is in LDS: pairs [c0, c0 + cn), cbase tiles
+  // before it, ci the next pair to look at
+  int c0 = 0, cbase = 0;
+  int x = a_my;          // next tile of the share
+  int ci = first_after(sm.pref, cn, cbase, x);
+  int npend = 0;
+  Buf<MODE, D, PHI> ba, bb;
+  // rotating wave priority (see set_prio)
+  const int prio_rounds = p.prio_rot ? min(3, (int)(gridDim.x / p.ncu)) : 1;
+  int prio_phase = prio_rounds > 1 ? (w / p.ncu) % prio_rounds : 0;
+
+  while (x < e_my) {
+    // ---- a batch: up to NS segments whose block ids fit the LDS table
+    __syncthreads();   // every wave is done with the previous batch's records
+    int nseg = 0, ids_used = 0;
+    while (nseg < NS && x < e_my) {
+      if (ci >= cn) {
+        c0 += cn;
+        cbase += ctot;
+        cn = min(kPrefChunk, P - c0);
+        if (cn <= 0) {   // no pair left (cannot happen while x < T)
+          x = e_my;
+          break;
+        }
+        __syncthreads();   // earlier readers of pref / part are done
+        ctot = scan_chunk<NWV>(p, sm.pref, sm.plen, sm.pst, sm.part, c0, cn, tid);
+        ci = first_after(sm.pref, cn, cbase, x);
+        continue;
+      }
+      const int s0 = cbase + __builtin_amdgcn_readfirstlane(sm.pref[ci]);
+      const int s1 = cbase + __builtin_amdgcn_readfirstlane(sm.pref[ci + 1]);
+      if (s1 <= x) {
+        ++ci;
+        continue;
+      }
+      const int pair = c0 + ci;
+      const int L = __builtin_amdgcn_readfirstlane(sm.plen[ci]);
+      const int start = __builtin_amdgcn_readfirstlane(sm.pst[ci]);
+      const int t0 = start / 64;
+      const int e = min(s1, e_my);
+      const int tb = t0 + (x - s0), te = t0 + (e - s0);
+      const int blk0 = (tb * 64) >> bl;
+      const int n_ids = ((min(te * 64, L) - 1) >> bl) - blk0 + 1;
+      if (ids_used + n_ids > kMaxSplitBlocks) {
+        if (nseg > 0) break;
+        x = e_my;   // cannot happen for a launch the host sized; give up the share
+        break;
+      }
+      const bool whole = x == s0 && e == s1;
+      if (tid == 0) {
+        SegRec& s = sm.seg[nseg];
+        s.b = pair / hkv;
+        s.h = pair - s.b * hkv;
+        s.tb = tb;
+        s.te = te;
+        s.L = L;
+        s.start = start;
+        s.ids_off = ids_used;
+        s.blk0 = blk0;
+        s.n_ids = n_ids;
+        s.slot = whole ? -1 : pair + w;
+        if (!whole && npend < 2) {
+          sm.pend[npend][0] = pair;
+          sm.pend[npend][1] = s0;
+          sm.pend[npend][2] = s1;
+        }
+      }
+      npend = min(2, npend + (whole ? 0 : 1));   // a share cuts at most two pairs
+      ids_used += n_ids;
+      ++nseg;
+      x = e;
+      if (x == s1) ++ci;
+    }
+    if (nseg == 0) break;
+    __syncthreads();   // records visible; the previous batch's LDS reads are done
+
+    // ---- batch prologue: block ids (into LDS) and query rows (into
+    // registers) are all requested before anything waits on them.  Thread
+    // index opaque to the compiler, as in the segment epilogue.
+    int pt = threadIdx.x;
+    asm volatile("" : "+v"(pt));
+    const int plane = pt & 63;
+    uint32_t raw[NS * Sm::GM / NWV];
+    int idv[kMaxSplitBlocks / NT];
+#pragma unroll
+    for (int u = 0; u < kMaxSplitBlocks / NT; ++u) {
+      const int j = pt + u * NT;
+      idv[u] = 0;
+      if (j < ids_used) {
+        int k = 0;
+        while (k + 1 < nseg && sm.seg[k + 1].ids_off <= j) ++k;
+        const SegRec& s = sm.seg[k];
+        const int32_t* trow = p.tables + (int64_t)(p.headwise ? s.b * hkv + s.h : s.b) * p.max_blocks;
+        idv[u] = trow[s.blk0 + (j - s.ids_off)];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NS * Sm::GM / NWV; ++i) {
+      const int rr = wave + i * NWV;
+      raw[i] = 0;
+      if (rr < nseg * G) {
+        const int k = rr / G, g = rr - k * G;
+        const int b = __builtin_amdgcn_readfirstlane(sm.seg[k].b), h = __builtin_amdgcn_readfirstlane(sm.seg[k].h);
+        raw[i] = load_qrow<D>(p.q + ((int64_t)b * p.hq + h * G + g) * D, plane);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxSplitBlocks / NT; ++u) {
+      const int j = pt + u * NT;
+      if (j < ids_used) sm.ids[j] = idv[u];
+    }
+    __syncthreads();
+
+    // the wave's first tile goes out before the query prologue
+    Cursor cur;
+    cur.ls = 0;
+    cur.li = 0;
+    cur.nseg = nseg;
+    cursor_seek(cur, sm, wave);
+    TileInfo ta = cursor_info<CB>(cur, sm, wave, bl, hkv);
+    cursor_next(cur, sm, wave);
+    issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
+
+#pragma unroll
+    for (int i = 0; i < NS * Sm::GM / NWV; ++i) {
+      const int rr = wave + i * NWV;
+      if (rr < nseg * G) {
+        const int k = rr / G, g = rr - k * G;
+        prep_query<MODE, D, PHI, ROT>(p, raw[i], sm.qrow[wave], sm.qa[k][g], sm.qb[k][g], &sm.qs[k][g],
+                                      &sm.q1[k][g], plane);
+      }
+    }
+    __syncthreads();
+
+    // ---- the stream: segment by segment, look-ahead across segment ends
+    for (int k = 0; k < nseg; ++k) {
+      const SegRec& sr = sm.seg[k];
+      const int L = __builtin_amdgcn_readfirstlane(sr.L);
+      const int start = __builtin_amdgcn_readfirstlane(sr.start);
+      const int n2 = wave_tiles2(__builtin_amdgcn_readfirstlane(sr.te) - __builtin_amdgcn_readfirstlane(sr.tb),
+                                 wave);
+      LaneConst lc;
+      lc.q = q;
+      lc.phi_col = phi_col;
+      lc.head_ok = g_col < G;
+      const bool brow = lc.head_ok && phi_grp == phi_col;
+      lc.qa = brow ? &sm.qa[k][g_col][sub * Gm::SUBD] : &sm.qzero[sub * Gm::SUBD];
+      lc.qb = brow ? &sm.qb[k][g_col][sub * Gm::SUBD] : &sm.qzero[sub * Gm::SUBD];
+      lc.sp = lc.head_ok ? sm.qs[k][g_col] : 1.0f;
+      lc.q1r = lc.head_ok ? sm.q1[k][g_col] : 0.0f;
+      lc.magic = magic;
+      lc.n4 = n4;
+      lc.n2 = n2m;
+      lc.vsel = vsel;
+
+      WaveState st{kNegInf, 0.0f, 0.0f};
+      f32x4_t acc[Gm::DT];
+#pragma unroll
+      for (int i = 0; i < Gm::DT; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+      for (int it = 0; it < n2; it += 2) {
+        if (prio_rounds > 1) {
+          set_prio(prio_phase);
+          prio_phase = prio_phase + 1 == prio_rounds ? 0 : prio_phase + 1;
+        }
+        const TileInfo tn = cursor_info<CB>(cur, sm, wave, bl, hkv);
+        cursor_next(cur, sm, wave);
+        issue_loads<MODE, D, PHI, CB>(bb, tn, p, r, q, phi_col);
+        run_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
+        const TileInfo t2 = cursor_info<CB>(cur, sm, wave, bl, hkv);
+        cursor_next(cur, sm, wave);
+        issue_loads<MODE, D, PHI, CB>(ba, t2, p, r, q, phi_col);
+        run_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
+        ta = t2;
+      }
+
+      // ---- segment epilogue: sum the phases of a head, then l and z over
+      // lane groups; combine the waves in LDS
+      if constexpr (PHI >= 2) {
+#pragma unroll
+        for (int i = 0; i < Gm::DT; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] += quad_xor<1>(acc[i][j]);
+        st.l += quad_xor<1>(st.l);
+        st.z += quad_xor<1>(st.z);
+      }
+      if constexpr (PHI >= 4) {
+#pragma unroll
+        for (int i = 0; i < Gm::DT; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] += quad_xor<2>(acc[i][j]);
+        st.l += quad_xor<2>(st.l);
+        st.z += quad_xor<2>(st.z);
+      }
+      st.l = add_xor32(add_xor16(st.l));
+      st.z = add_xor32(add_xor16(st.z));
+      // thread index the compiler cannot see through: the combine's
+      // lane-dependent addresses are formed here, not hoisted out of the
+      // segment loop and held across the tiles
+      int et = threadIdx.x;
+      asm volatile("" : "+v"(et));
+      const int elane = et & 63;
+      __syncthreads();   // the combine area is free
+      if (lc.head_ok && phi_col == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int dt = 0; dt < Gm::DT; ++dt) sm.comb.acc[wave][g_col][(4 * q + i) * Gm::DT + dt] = acc[dt][i] + st.z;
+        if (q == 0) {
+          sm.comb.ml[wave][g_col][0] = st.m;
+          sm.comb.ml[wave][g_col][1] = st.l;
+        }
+      }
+      __syncthreads();
+
+      constexpr int PER = (Sm::GM * D + NT - 1) / NT;
+      float val[PER], lsum[PER], mmax[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int e = et + j * NT;
+        val[j] = 0.0f; lsum[j] = 0.0f; mmax[j] = kNegInf;
+        if (e < G * D) {
+          const int g = e / D, d = e - g * D;
+          float mx = kNegInf;
+#pragma unroll
+          for (int v = 0; v < NWV; ++v) mx = fmaxf(mx, sm.comb.ml[v][g][0]);
+          const float mu = mx == kNegInf ? 0.0f : mx;
+#pragma unroll
+          for (int v = 0; v < NWV; ++v) {
+            const float f = __builtin_amdgcn_exp2f(sm.comb.ml[v][g][0] - mu);
+            val[j] += f * sm.comb.acc[v][g][d];
+            lsum[j] += f * sm.comb.ml[v][g][1];
+          }
+          mmax[j] = mx;
+        }
+      }
+      const int slot = __builtin_amdgcn_readfirstlane(sr.slot);
+      const int b = __builtin_amdgcn_readfirstlane(sr.b), h = __builtin_amdgcn_readfirstlane(sr.h);
+      const int64_t orow0 = (int64_t)b * p.hq + h * G;
+      if (slot < 0) {
+        __syncthreads();   // fin overlays the combine area
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int e = et + j * NT;
+          if (e < G * D) sm.fw.fin[e / D][e % D] = lsum[j] > 0.0f ? val[j] / lsum[j] : 0.0f;
+        }
+        __syncthreads();
+        for (int g = wave; g < G; g += NWV) finish_row<D, ROT>(p, sm.fw.fin[g], orow0 + g, elane);
+      } else {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int e = et + j * NT;
+          if (e < G * D) {
+            const int g = e / D, d = e - g * D;
+            float* rec = p.partials + ((int64_t)slot * G + g) * (D + 4);
+            store_dev(rec + 4 + d, val[j]);
+            if (d == 0) {
+              store_dev(rec, mmax[j]);
+              store_dev(rec + 1, lsum[j]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- published pieces: count them in; the last of a pair merges it
+  if (npend > 0) {
+    // the pieces' device-scope stores are complete before any count
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    for (int i = 0; i < npend; ++i) {
+      const int pair = __builtin_amdgcn_readfirstlane(sm.pend[i][0]);
+      const int s0 = __builtin_amdgcn_readfirstlane(sm.pend[i][1]);
+      const int s1 = __builtin_amdgcn_readfirstlane(sm.pend[i][2]);
+      const int fw = part.owner(s0), lw = part.owner(s1 - 1);
+      if (tid == 0) sm.flag = atomicAdd(p.counters + pair, 1) == lw - fw;
+      __syncthreads();
+      if (__builtin_amdgcn_readfirstlane(sm.flag)) {
+        const int b = pair / hkv, h = pair - b * hkv;
+        merge_pieces<D, PHI, NWV, ROT>(p, sm, pair + fw, lw - fw + 1, (int64_t)b * p.hq + h * G, tid);
+        if (tid == 0) atomicExch(p.counters + pair, 0);
       }
       __syncthreads();
     }
   }
-  store_rows<D>(p, fin, G, orow0, tid, ROT);
 }
 
 template <int MODE, int D, int PHI, bool ROT>
-hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, hipStream_t s) {
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+  constexpr int NWV = decode_wg_waves<MODE, D, PHI>();
   if (p.block_size >= 64)
-    hipLaunchKernelGGL((decode_kernel<MODE, D, PHI, ROT, true>), dim3(p.max_splits, p.hkv, num_seqs),
-                       dim3(64 * kWaves), 0, s, p);
+    hipLaunchKernelGGL((decode_kernel<MODE, D, PHI, ROT, true, NWV>), dim3(p.n_wgs), dim3(64 * NWV), 0, s, p);
   else
-    hipLaunchKernelGGL((decode_kernel<MODE, D, PHI, ROT, false>), dim3(p.max_splits, p.hkv, num_seqs),
-                       dim3(64 * kWaves), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.max_splits == 1) return e;
-  hipLaunchKernelGGL((decode_reduce_kernel<D, ROT>), dim3(p.hkv, num_seqs), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((decode_kernel<MODE, D, PHI, ROT, false, NWV>), dim3(p.n_wgs), dim3(64 * NWV), 0, s, p);
   return hipGetLastError();
 }
 
 template <int MODE, int D, bool ROT>
-hipError_t launch_decode_p(const DecodeParams& p, int n, hipStream_t s) {
-  if (p.group * 4 <= 16) return launch_decode_t<MODE, D, 4, ROT>(p, n, s);
-  if (p.group * 2 <= 16) return launch_decode_t<MODE, D, 2, ROT>(p, n, s);
-  return launch_decode_t<MODE, D, 1, ROT>(p, n, s);
+hipError_t launch_decode_p(const DecodeParams& p, hipStream_t s) {
+  if (p.group * 4 <= 16) return launch_decode_t<MODE, D, 4, ROT>(p, s);
+  if (p.group * 2 <= 16) return launch_decode_t<MODE, D, 2, ROT>(p, s);
+  return launch_decode_t<MODE, D, 1, ROT>(p, s);
 }
 
 template <int MODE>
-hipError_t launch_decode_m(int d, bool rot, const DecodeParams& p, int n, hipStream_t s) {
-  if (d == 64) return rot ? launch_decode_p<MODE, 64, true>(p, n, s) : launch_decode_p<MODE, 64, false>(p, n, s);
-  return rot ? launch_decode_p<MODE, 128, true>(p, n, s) : launch_decode_p<MODE, 128, false>(p, n, s);
+hipError_t launch_decode_m(int d, bool rot, const DecodeParams& p, hipStream_t s) {
+  if (d == 64) return rot ? launch_decode_p<MODE, 64, true>(p, s) : launch_decode_p<MODE, 64, false>(p, s);
+  return rot ? launch_decode_p<MODE, 128, true>(p, s) : launch_decode_p<MODE, 128, false>(p, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, int num_seqs, hipStream_t s) {
+int decode_wgs_per_cu(int mode, int d, int group) {
+  const int phi = group * 4 <= 16 ? 4 : (group * 2 <= 16 ? 2 : 1);
+  // four-wave workgroups: one wave per SIMD each
+#define KVQ_W(M_, D_, P_) if (mode == M_ && d == D_ && phi == P_) return decode_waves_per_simd<M_, D_, P_>();
+  KVQ_W(0, 64, 4) KVQ_W(0, 64, 2) KVQ_W(0, 64, 1) KVQ_W(0, 128, 4) KVQ_W(0, 128, 2) KVQ_W(0, 128, 1)
+  KVQ_W(1, 64, 4) KVQ_W(1, 64, 2) KVQ_W(1, 64, 1) KVQ_W(1, 128, 4) KVQ_W(1, 128, 2) KVQ_W(1, 128, 1)
+  KVQ_W(2, 64, 4) KVQ_W(2, 64, 2) KVQ_W(2, 64, 1) KVQ_W(2, 128, 4) KVQ_W(2, 128, 2) KVQ_W(2, 128, 1)
+#undef KVQ_W
+  return 4;
+}
+
+hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, hipStream_t s) {
   switch (mode) {
-    case 0: return launch_decode_m<0>(d, rot, p, num_seqs, s);
-    case 1: return launch_decode_m<1>(d, rot, p, num_seqs, s);
-    default: return launch_decode_m<2>(d, rot, p, num_seqs, s);
+    case 0: return launch_decode_m<0>(d, rot, p, s);
+    case 1: return launch_decode_m<1>(d, rot, p, s);
+    default: return launch_decode_m<2>(d, rot, p, s);
   }
 }
 

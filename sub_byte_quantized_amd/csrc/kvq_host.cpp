@@ -65,52 +65,55 @@ kvq_status check_planes(const uint8_t* kc, const float* km, const uint8_t* vc, c
 
 float inv_sqrt_f32(int d) { return (float)(1.0 / std::sqrt((double)d)); }
 
+// Compute units of the current device (the MI355X's 256 when there is no
+// device to ask, as in a host-only size query).
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return kvq::kNumCUs;
+  }
+  return n;
+}
+
+int env_flag(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  return e ? std::atoi(e) : dflt;
+}
+
 struct DecodePlan {
-  int chunks_per_split;
-  int max_splits;
+  int n_wgs;
+  size_t counter_bytes;
   size_t partial_bytes;
-  size_t total() const { return partial_bytes; }
+  size_t total() const { return counter_bytes + partial_bytes; }
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split-KV plan: split each (sequence, kv head)'s active range into runs of
-// 64-position tiles, one 4-wave workgroup per run, so that the launch holds a
-// few thousand workgroups (>> 256 CUs) whatever the batch while each wave
-// still gets several tiles to pipeline.  Deterministic in its inputs, so the
-// workspace query and the call agree.
+// Stream-K plan: a persistent grid of as many workgroups as fit on the
+// MI355X at once (256 CUs times the variant's resident workgroups per CU)
+// shares all pairs' tiles equally; more workgroups only when a
+// share could span more blocks than one segment's LDS table holds.  The
+// workspace holds one piece counter per pair (zero between calls) and one
+// (m, l, acc) record per (piece, head): at most n_wgs + pairs pieces.
+// Deterministic in its inputs.
 DecodePlan plan_decode(const kvq_cache_desc* d, int num_seqs, int num_q_heads, int max_seq_len) {
   DecodePlan pl{};
   const long long max_tiles = (max_seq_len + kvq::kTile - 1) / kvq::kTile;
-  const long long units = (long long)num_seqs * d->num_kv_heads * (max_tiles > 0 ? max_tiles : 1);
-  long long target = 2048;
-  if (const char* e = std::getenv("KVQ_DECODE_TARGET_WGS")) {
+  const long long pairs = (long long)num_seqs * d->num_kv_heads;
+  const long long seg_cap = ((long long)(kvq::kMaxSplitBlocks - 1) * d->block_size) / kvq::kTile - 1;
+  long long nw = (long long)num_cus() * kvq::decode_wgs_per_cu(d->mode, d->head_dim, num_q_heads / d->num_kv_heads);
+  if (const char* e = std::getenv("KVQ_DECODE_WGS")) {
     const long long t = std::atoll(e);
-    if (t > 0) target = t;
+    if (t > 0) nw = t;
   }
-  // Each split pays a fixed prologue (query pieces, block ids) and, when a
-  // sequence has several, a partial record plus the combine kernel; on MI355X
-  // fewer, longer splits win until the grid no longer covers the CUs, so a
-  // split spans at least 128 tiles (8192 positions).
-  long long tps = (units + target - 1) / target;
-  if (tps < 128) tps = 128;
-  if (const char* e = std::getenv("KVQ_DECODE_TILES_PER_SPLIT")) {
-    const long long c = std::atoll(e);
-    if (c > 0) tps = c;
-  }
-  // the combine kernel handles at most kMaxReduceSplits splits
-  if (max_tiles > (long long)kvq::kMaxReduceSplits * tps)
-    tps = (max_tiles + kvq::kMaxReduceSplits - 1) / kvq::kMaxReduceSplits;
-  if (max_tiles > 0 && tps > max_tiles) tps = max_tiles;
-  // the block ids of one split must fit the kernel's LDS table
-  const long long tps_cap = ((long long)(kvq::kMaxSplitBlocks - 1) * d->block_size) / kvq::kTile;
-  if (tps > tps_cap) tps = tps_cap;
-  if (tps < 1) tps = 1;
-  long long ms = max_tiles > 0 ? (max_tiles + tps - 1) / tps : 1;
-  if (ms < 1) ms = 1;
-  pl.chunks_per_split = (int)tps;
-  pl.max_splits = (int)ms;
-  if (ms > 1) pl.partial_bytes = round_up((size_t)num_seqs * num_q_heads * ms * (d->head_dim + 4) * sizeof(float), 256);
+  const long long need = (pairs * max_tiles + seg_cap - 1) / seg_cap + 1;
+  if (nw < need) nw = need;
+  pl.n_wgs = (int)nw;
+  const int G = num_q_heads / d->num_kv_heads;
+  pl.counter_bytes = round_up((size_t)pairs * sizeof(int32_t), 256);
+  pl.partial_bytes = round_up((size_t)(nw + pairs) * G * (d->head_dim + 4) * sizeof(float), 256);
   return pl;
 }
 
@@ -125,6 +128,9 @@ kvq_status check_decode_sizes(const kvq_cache_desc* d, int num_seqs, int num_q_h
     return fail(KVQ_EUNSUPPORTED, "GQA group %d > 16 is not built", num_q_heads / d->num_kv_heads);
   if (d->num_kv_heads > 65535) return fail(KVQ_EUNSUPPORTED, "num_kv_heads > 65535");
   if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len %d < 0", max_seq_len);
+  // the decode schedule counts all tiles of the batch in int32
+  if ((long long)num_seqs * d->num_kv_heads * ((max_seq_len + kvq::kTile - 1) / kvq::kTile) >= 0x7fffffffLL)
+    return fail(KVQ_EUNSUPPORTED, "num_seqs*num_kv_heads*ceil(max_seq_len/64) must stay below 2^31 tiles");
   return KVQ_OK;
 }
 
@@ -238,12 +244,10 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
   st = check_planes(k_codes, k_meta, v_codes, v_meta);
   if (st != KVQ_OK) return st;
   const DecodePlan pl = plan_decode(desc, num_seqs, num_q_heads, max_seq_len);
-  if (pl.total() > 0) {
-    if (!workspace) return fail(KVQ_EINVAL, "workspace is NULL (%zu bytes needed)", pl.total());
-    if (workspace_bytes < pl.total())
-      return fail(KVQ_ENOSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total());
-    if (!aligned(workspace, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
-  }
+  if (!workspace) return fail(KVQ_EINVAL, "workspace is NULL (%zu bytes needed)", pl.total());
+  if (workspace_bytes < pl.total())
+    return fail(KVQ_ENOSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total());
+  if (!aligned(workspace, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
   kvq::DecodeParams p{};
   p.k_codes = k_codes;
   p.k_meta = k_meta;
@@ -256,7 +260,8 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
   p.seq_lens = seq_lens;
   p.window = window;
   p.signs = desc->rot_signs;
-  p.partials = pl.total() > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.counters = static_cast<int32_t*>(workspace);
+  p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counter_bytes);
   p.qscale = softmax_scale * 1.4426950408889634f;
   p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
   p.max_blocks = max_blocks_per_seq;
@@ -265,13 +270,15 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
   p.hq = num_q_heads;
   p.hkv = desc->num_kv_heads;
   p.group = num_q_heads / desc->num_kv_heads;
-  p.chunks_per_split = pl.chunks_per_split;
-  p.max_splits = pl.max_splits;
+  p.num_pairs = num_seqs * desc->num_kv_heads;
+  p.n_wgs = pl.n_wgs;
+  p.ncu = num_cus();
+  p.prio_rot = env_flag("KVQ_DECODE_PRIO", 1);
   p.out_bf16 = out_dtype == KVQ_OUT_BF16;
   p.bits_magic = 0x43004300u;
   p.bits_n4 = 0x000F000Fu;
   p.bits_n2 = 0x00030003u;
-  hipError_t e = kvq::launch_decode(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p, num_seqs,
+  hipError_t e = kvq::launch_decode(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_EHIP, "decode launch: %s", hipGetErrorString(e));
   return ok();

@@ -15,10 +15,11 @@ __host__ __device__ constexpr int row_bytes(int mode, int d) { return d * mode_b
 
 // Positions the decode kernel processes as one tile (four 16-token MFMA tiles).
 constexpr int kTile = 64;
-// Most block ids one decode split may span (held in LDS).
+// Most block ids one decode segment may span (held in LDS).
 constexpr int kMaxSplitBlocks = 1024;
-// Most splits one (sequence, kv head) may have (the combine kernel's LDS).
-constexpr int kMaxReduceSplits = 512;
+// CUs of an MI355X: the persistent decode grid is this times the resident
+// workgroups per CU.
+constexpr int kNumCUs = 256;
 
 struct WriteParams {
   const uint16_t* key;      // bf16
@@ -49,7 +50,8 @@ struct DecodeParams {
   const int32_t* seq_lens;      // [B]
   const int32_t* window;        // [Hkv] or nullptr
   const float* signs;           // [D] or nullptr
-  float* partials;              // [B, Hq, max_splits, D + 4]
+  float* partials;              // [n_wgs + num_pairs][group][D + 4] pieces (m, l, pad, pad, acc)
+  int32_t* counters;            // [num_pairs] pieces counted in; zero between calls
   float qscale;                 // softmax_scale * log2(e)
   float inv_sqrt_d;
   int32_t headwise;
@@ -59,8 +61,10 @@ struct DecodeParams {
   int32_t hq;
   int32_t hkv;
   int32_t group;                // Hq / Hkv
-  int32_t chunks_per_split;     // 64-position tiles per split
-  int32_t max_splits;
+  int32_t num_pairs;            // B * Hkv
+  int32_t n_wgs;                // persistent decode workgroups
+  int32_t ncu;                  // compute units (workgroups of one dispatch round)
+  int32_t prio_rot;             // 1: dispatch rounds take turns at the top wave priority
   int32_t out_bf16;
   uint32_t bits_magic;          // 0x43004300: bf16 128.0 in both halves
   uint32_t bits_n4;             // 0x000F000F
@@ -94,8 +98,9 @@ struct PrefillParams {
 };
 
 hipError_t launch_write(int mode, int d, bool rot, const WriteParams& p, hipStream_t s);
-hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, int num_seqs,
-                         hipStream_t s);
+// Resident decode workgroups per CU for this variant (its waves per SIMD).
+int decode_wgs_per_cu(int mode, int d, int group);
+hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, hipStream_t s);
 hipError_t launch_prefill(int mode, int d, bool rot, const PrefillParams& p, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 

@@ -84,14 +84,16 @@ def test_decode_repeatable_and_split_invariant(monkeypatch):
     spec = synth.small_spec(name="splits", cfg=463, mode=2, rotate=True, lens=[2000, 45, 700], B=3)
     case, d, planes = gh.build(spec)
     outs = []
-    for cps in ("1", "3", "1000"):
-        monkeypatch.setenv("KVQ_DECODE_TILES_PER_SPLIT", cps)
+    # workgroup counts: one share per pair or fewer, shares cutting pairs at
+    # odd places, more workgroups than tiles (the partition then shrinks)
+    for nwg in ("1", "3", "7", "1000"):
+        monkeypatch.setenv("KVQ_DECODE_WGS", nwg)
         o1 = gh.gpu_decode(spec, case, d, planes)
         o2 = gh.gpu_decode(spec, case, d, planes)
         torch.cuda.synchronize()
-        assert torch.equal(o1, o2), f"repeat differs at cps={cps}"
+        assert torch.equal(o1, o2), f"repeat differs at {nwg} workgroups"
         outs.append(o1.cpu().numpy())
-    monkeypatch.delenv("KVQ_DECODE_TILES_PER_SPLIT")
+    monkeypatch.delenv("KVQ_DECODE_WGS")
     ref = gh.oracle_decode(spec, case, gh.host_planes(planes))
     for o in outs:
         gh.assert_close(o, ref, "split-count")
