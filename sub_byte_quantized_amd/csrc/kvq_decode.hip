@@ -463,9 +463,14 @@ constexpr int decode_waves_per_simd() {
   return (PHI == 1 || (MODE == 0 && D == 128 && PHI < 4)) ? 1 : ((MODE == 2 && PHI == 4) ? 3 : 2);
 }
 
-// Waves per workgroup.
+// Waves per workgroup.  INT4 and INT2: all of a CU's waves in one
+// workgroup (one per SIMD per round), so no two workgroups on a CU compete
+// and the waves of a SIMD take turns at the top priority; INT8, whose tiles
+// are the heaviest in bytes: four-wave workgroups, several per CU, so one
+// workgroup's segment barriers and prologue overlap another's loads
+// (measured faster for each).
 template <int MODE, int D, int PHI>
-constexpr int decode_wg_waves() { return 4; }
+constexpr int decode_wg_waves() { return MODE != 0 ? 4 * decode_waves_per_simd<MODE, D, PHI>() : 4; }
 
 // ---------------------------------------------------------------------------
 // Whole rows of D values, one row per wave: lane holds d = E*lane + e with
@@ -610,18 +615,15 @@ struct Smem {
     } comb;                             // per-wave (m, l, acc) of a segment
     struct {
       float fin[GM][D];                 // normalized rows before R^T
-      float cw[GM][64];                 // piece merge: factor of each piece
     } fw;
     float qrow[NWV][D];                 // query prologue scratch, one row per wave
   };
-  float cm[GM];                         // piece merge: max m, 1 / l
-  float cl[GM];
   int32_t pref[kPrefChunk + 1];         // inclusive tile prefix of a chunk of pairs
   int32_t plen[kPrefChunk];             // its pairs' attended end L and start
   int32_t pst[kPrefChunk];
   int32_t part[64 * NWV];
   int32_t pend[2][3];                   // pieces this workgroup published: pair, s0, s1
-  int32_t flag;
+  int32_t pflag[2];                     // this workgroup counted the last piece in
 };
 
 // Tiles of (sequence b, kv head h): 64-position tiles from the window start
@@ -637,30 +639,48 @@ __device__ __forceinline__ int pair_geo(const DecodeParams& p, int pair, int* t0
   return l > 0 ? (l + 63) / 64 - s / 64 : 0;
 }
 
-// The share partition: workgroup w takes tiles [w T / nw, (w + 1) T / nw)
-// of the T concatenated tiles (nw <= T, so no share is empty).
+// The share partition: workgroup w takes tiles [start(w), start(w + 1)) of
+// the T concatenated tiles.  Workgroups of dispatch round r (ids r*ncu ..
+// r*ncu + ncu - 1, one per CU) start streaming a few microseconds after the
+// rounds before them on the same CU (their prologues queue behind the older
+// waves), so round r's shares are K*r tiles shorter than round 0's, the
+// average kept at T / nw: share_r = T/nw + K (nr - 1)/2 - K r.  Equal shares
+// (K = 0) when nw is not a whole number of rounds or the shares would get
+// short.
 struct Part {
-  int T, nw;
-  __device__ int start(int w) const { return (int)(((int64_t)T * w) / nw); }
+  int T, nw, ncu, nr, K;
+  __device__ int start(int w) const {
+    if (K == 0) return (int)(((int64_t)T * w) / nw);
+    // 2 nw * (sum of the shares before w), exact in int64
+    const int r = w / ncu;
+    const int64_t c2 = 2LL * w * T +
+                       (int64_t)K * nw * ((int64_t)w * (nr - 1) - (int64_t)ncu * r * (r - 1) - 2LL * (w - r * ncu) * r);
+    return (int)(c2 / (2LL * nw));
+  }
   // workgroup whose share holds tile x (0 <= x < T)
   __device__ int owner(int x) const {
-    int w = (int)(((int64_t)x * nw) / T);
-    while (w + 1 < nw && start(w + 1) <= x) ++w;
-    while (w > 0 && start(w) > x) --w;
-    return w;
+    int lo = 0, hi = nw - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start(mid) <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
   }
 };
 
 // Wave priority for the rounds of a persistent grid: with several
 // workgroups per CU (dispatch rounds of ncu workgroups), the SIMDs' issue
 // arbitration favours the oldest waves, so the last round's shares would
-// finish well after the first's; instead each wave's priority rotates
-// (0, 1, 2, ... per tile pair), offset by its round, and the rounds take
-// turns at the top.
+// finish well after the first's.  Instead, while streaming tiles, each
+// wave's priority rotates (0, 1, 2, ... per tile pair), offset by its round,
+// so the rounds take turns at the top; the short latency-bound phases
+// (prologue, segment epilogues, merging) run at priority 3, above any
+// streaming wave, so they never wait behind another workgroup's tiles.
 __device__ __forceinline__ void set_prio(int k) {
   if (k == 0) __builtin_amdgcn_s_setprio(0);
   else if (k == 1) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(2);
+  else if (k == 2) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(3);
 }
 
 // Workgroups in the partition: never more than tiles.
@@ -669,8 +689,9 @@ __device__ __forceinline__ int active_wgs(int grid, int T) { return max(1, min(g
 // Tiles of one segment that wave `wave` computes: tb + wave + 4 i, padded to
 // an even count (the pad is past te, hence invalid) so the two load buffers
 // keep their roles across segments.
+template <int NWV>
 __device__ __forceinline__ int wave_tiles2(int n, int wave) {
-  const int k = n > wave ? (n - wave + 3) >> 2 : 0;
+  const int k = n > wave ? (n - wave + NWV - 1) / NWV : 0;
   return k + (k & 1);
 }
 
@@ -687,7 +708,7 @@ __device__ __forceinline__ void cursor_seek(Cursor& c, const Smem<D, PHI, NWV>& 
     const SegRec& s = sm.seg[c.ls];
     c.tb = __builtin_amdgcn_readfirstlane(s.tb);
     c.te = __builtin_amdgcn_readfirstlane(s.te);
-    c.n2 = wave_tiles2(c.te - c.tb, wave);
+    c.n2 = wave_tiles2<NWV>(c.te - c.tb, wave);
     if (c.n2 > 0) {
       c.off = __builtin_amdgcn_readfirstlane(s.ids_off);
       c.blk0 = __builtin_amdgcn_readfirstlane(s.blk0);
@@ -707,7 +728,7 @@ __device__ __forceinline__ TileInfo cursor_info(const Cursor& c, const Smem<D, P
     t.pos0 = 0; t.row0 = 0; t.row1 = 0; t.row2 = 0; t.row3 = 0; t.valid = 0;
     return t;
   }
-  return tile_info<CB>(sm.ids + c.off, c.blk0, c.tb + wave + 4 * c.li, c.te, c.L, c.start, bl, hkv, c.h);
+  return tile_info<CB>(sm.ids + c.off, c.blk0, c.tb + wave + NWV * c.li, c.te, c.L, c.start, bl, hkv, c.h);
 }
 
 template <int D, int PHI, int NWV>
@@ -730,7 +751,10 @@ __device__ __forceinline__ float load_dev(const float* a) {
 }
 
 // Merge the published pieces of one pair (slots slot0 .. slot0 + n - 1),
-// normalize, R^T and store.  All threads; ends with the rows stored.
+// normalize, R^T and store.  All threads.  Each thread folds its (head, d)
+// values over the pieces in slot order with the online-softmax update,
+// requesting eight pieces' (m, l, acc) at a time, so a merge of up to eight
+// pieces waits on memory once.
 template <int D, int PHI, int NWV, bool ROT>
 __device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI, NWV>& sm, int slot0, int n,
                                              int64_t orow0, int tid) {
@@ -738,53 +762,37 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI,
   const int G = p.group;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t stride = (int64_t)G * (D + 4);   // floats between consecutive pieces
-  // per head: M = max_s m_s and 1 / sum_s 2^(m_s - M) l_s
-  for (int g = wave; g < G; g += NWV) {
+  for (int e = tid; e < G * D; e += NT) {
+    const int g = e / D, d = e - g * D;
     const float* base = p.partials + ((int64_t)slot0 * G + g) * (D + 4);
-    float mx = kNegInf;
-    for (int s = lane; s < n; s += 64) mx = fmaxf(mx, load_dev(base + s * stride));
+    float M = kNegInf, l = 0.0f, v = 0.0f;
+    for (int s = 0; s < n; s += 8) {
+      const int c = min(8, n - s);
+      float pm[8], pl[8], pa[8];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    const float mu = mx == kNegInf ? 0.0f : mx;
-    float l = 0.0f;
-    for (int s = lane; s < n; s += 64)
-      l += __builtin_amdgcn_exp2f(load_dev(base + s * stride) - mu) * load_dev(base + s * stride + 1);
+      for (int u = 0; u < 8; ++u) {
+        if (u < c) {
+          const float* rec = base + (s + u) * stride;
+          pm[u] = load_dev(rec);
+          pl[u] = load_dev(rec + 1);
+          pa[u] = load_dev(rec + 4 + d);
+        }
+      }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) l += __shfl_xor(l, m);
-    if (lane == 0) {
-      sm.cm[g] = mu;
-      sm.cl[g] = l > 0.0f ? 1.0f / l : 0.0f;
+      for (int u = 0; u < 8; ++u) {
+        if (u < c) {
+          const float mn = fmaxf(M, pm[u]);
+          const float fo = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - mn);
+          const float fn = pm[u] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(pm[u] - mn);
+          v = v * fo + pa[u] * fn;
+          l = l * fo + pl[u] * fn;
+          M = mn;
+        }
+      }
     }
+    sm.fw.fin[g][d] = l > 0.0f ? v / l : 0.0f;
   }
   __syncthreads();
-  // out = sum_s (2^(m_s - M) / l) acc_s, 64 pieces at a time, each piece's
-  // factor staged in LDS and the pieces' values requested eight at a time
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int cnt = min(64, n - s0);
-    for (int g = wave; g < G; g += NWV) {
-      if (lane < cnt) {
-        const float* base = p.partials + ((int64_t)(slot0 + s0 + lane) * G + g) * (D + 4);
-        sm.fw.cw[g][lane] = __builtin_amdgcn_exp2f(load_dev(base) - sm.cm[g]) * sm.cl[g];
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < G * D; e += NT) {
-      const int g = e / D, d = e - g * D;
-      const float* base = p.partials + ((int64_t)(slot0 + s0) * G + g) * (D + 4) + 4 + d;
-      float v = s0 == 0 ? 0.0f : sm.fw.fin[g][d];
-      int j = 0;
-      for (; j + 8 <= cnt; j += 8) {
-        float x[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = load_dev(base + (j + u) * stride);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v = __builtin_fmaf(sm.fw.cw[g][j + u], x[u], v);
-      }
-      for (; j < cnt; ++j) v = __builtin_fmaf(sm.fw.cw[g][j], load_dev(base + j * stride), v);
-      sm.fw.fin[g][d] = v;
-    }
-    __syncthreads();
-  }
   for (int g = wave; g < G; g += NWV) finish_row<D, ROT>(p, sm.fw.fin[g], orow0 + g, lane);
 }
 
@@ -862,12 +870,16 @@ void decode_kernel(DecodeParams p) {
   using Sm = Smem<D, PHI, NWV>;
   using Gm = Geo<MODE, D, PHI>;
   constexpr int NT = 64 * NWV, NS = Sm::NS;
+  constexpr int QR = (NS * Sm::GM + NWV - 1) / NWV;      // query rows per wave in a batch prologue
+  constexpr int IDR = (kMaxSplitBlocks + NT - 1) / NT;    // block ids per thread
   __shared__ Sm sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = p.num_pairs, G = p.group, hkv = p.hkv, bl = p.block_size_log2;
   const int w = blockIdx.x;
+
+  if (p.prio_rot) set_prio(3);
 
   // ---- tile prefix of the first chunk of pairs; total tiles
   for (int i = tid; i < Sm::QW; i += NT) sm.qzero[i] = 0;
@@ -891,6 +903,10 @@ void decode_kernel(DecodeParams p) {
   Part part;
   part.T = T;
   part.nw = active_wgs(gridDim.x, T);
+  part.ncu = p.ncu;
+  part.nr = part.nw / p.ncu;
+  part.K = (part.nw % p.ncu == 0 && part.nr > 1 && (int64_t)T >= (int64_t)part.nw * (p.share_skew * part.nr + 1))
+               ? p.share_skew : 0;
   const int nw = part.nw;
   if (w >= nw) return;
   const int a_my = part.start(w), e_my = part.start(w + 1);
@@ -927,8 +943,10 @@ void decode_kernel(DecodeParams p) {
   int npend = 0;
   Buf<MODE, D, PHI> ba, bb;
   // rotating wave priority (see set_prio)
-  const int prio_rounds = p.prio_rot ? min(3, (int)(gridDim.x / p.ncu)) : 1;
-  int prio_phase = prio_rounds > 1 ? (w / p.ncu) % prio_rounds : 0;
+  // (rounds: the workgroup's own waves per SIMD, waves i, i + 4, ... sharing
+  // SIMD i % 4, or else the grid's dispatch rounds)
+  const int prio_rounds = !p.prio_rot ? 1 : (NWV > 4 ? NWV / 4 : min(3, (int)(gridDim.x / p.ncu)));
+  int prio_phase = prio_rounds > 1 ? (NWV > 4 ? wave / 4 : w / p.ncu) % prio_rounds : 0;
 
   while (x < e_my) {
     // ---- a batch: up to NS segments whose block ids fit the LDS table
@@ -1001,10 +1019,10 @@ void decode_kernel(DecodeParams p) {
     int pt = threadIdx.x;
     asm volatile("" : "+v"(pt));
     const int plane = pt & 63;
-    uint32_t raw[NS * Sm::GM / NWV];
-    int idv[kMaxSplitBlocks / NT];
+    uint32_t raw[QR];
+    int idv[IDR];
 #pragma unroll
-    for (int u = 0; u < kMaxSplitBlocks / NT; ++u) {
+    for (int u = 0; u < IDR; ++u) {
       const int j = pt + u * NT;
       idv[u] = 0;
       if (j < ids_used) {
@@ -1016,7 +1034,7 @@ void decode_kernel(DecodeParams p) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < NS * Sm::GM / NWV; ++i) {
+    for (int i = 0; i < QR; ++i) {
       const int rr = wave + i * NWV;
       raw[i] = 0;
       if (rr < nseg * G) {
@@ -1026,7 +1044,7 @@ void decode_kernel(DecodeParams p) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < kMaxSplitBlocks / NT; ++u) {
+    for (int u = 0; u < IDR; ++u) {
       const int j = pt + u * NT;
       if (j < ids_used) sm.ids[j] = idv[u];
     }
@@ -1043,7 +1061,7 @@ void decode_kernel(DecodeParams p) {
     issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
 
 #pragma unroll
-    for (int i = 0; i < NS * Sm::GM / NWV; ++i) {
+    for (int i = 0; i < QR; ++i) {
       const int rr = wave + i * NWV;
       if (rr < nseg * G) {
         const int k = rr / G, g = rr - k * G;
@@ -1058,8 +1076,8 @@ void decode_kernel(DecodeParams p) {
       const SegRec& sr = sm.seg[k];
       const int L = __builtin_amdgcn_readfirstlane(sr.L);
       const int start = __builtin_amdgcn_readfirstlane(sr.start);
-      const int n2 = wave_tiles2(__builtin_amdgcn_readfirstlane(sr.te) - __builtin_amdgcn_readfirstlane(sr.tb),
-                                 wave);
+      const int n2 = wave_tiles2<NWV>(__builtin_amdgcn_readfirstlane(sr.te) -
+                                      __builtin_amdgcn_readfirstlane(sr.tb), wave);
       LaneConst lc;
       lc.q = q;
       lc.phi_col = phi_col;
@@ -1094,6 +1112,8 @@ void decode_kernel(DecodeParams p) {
         run_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
         ta = t2;
       }
+
+      if (prio_rounds > 1) set_prio(3);
 
       // ---- segment epilogue: sum the phases of a head, then l and z over
       // lane groups; combine the waves in LDS
@@ -1192,19 +1212,22 @@ void decode_kernel(DecodeParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
+    // one lane per published piece: all counts go out together
+    if (tid < npend) {
+      const int fw = part.owner(sm.pend[tid][1]), lw = part.owner(sm.pend[tid][2] - 1);
+      sm.pflag[tid] = atomicAdd(p.counters + sm.pend[tid][0], 1) == lw - fw;
+    }
+    __syncthreads();
     for (int i = 0; i < npend; ++i) {
-      const int pair = __builtin_amdgcn_readfirstlane(sm.pend[i][0]);
-      const int s0 = __builtin_amdgcn_readfirstlane(sm.pend[i][1]);
-      const int s1 = __builtin_amdgcn_readfirstlane(sm.pend[i][2]);
-      const int fw = part.owner(s0), lw = part.owner(s1 - 1);
-      if (tid == 0) sm.flag = atomicAdd(p.counters + pair, 1) == lw - fw;
-      __syncthreads();
-      if (__builtin_amdgcn_readfirstlane(sm.flag)) {
+      if (__builtin_amdgcn_readfirstlane(sm.pflag[i])) {
+        const int pair = __builtin_amdgcn_readfirstlane(sm.pend[i][0]);
+        const int fw = part.owner(__builtin_amdgcn_readfirstlane(sm.pend[i][1]));
+        const int lw = part.owner(__builtin_amdgcn_readfirstlane(sm.pend[i][2]) - 1);
         const int b = pair / hkv, h = pair - b * hkv;
         merge_pieces<D, PHI, NWV, ROT>(p, sm, pair + fw, lw - fw + 1, (int64_t)b * p.hq + h * G, tid);
         if (tid == 0) atomicExch(p.counters + pair, 0);
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
 }
@@ -1236,8 +1259,7 @@ hipError_t launch_decode_m(int d, bool rot, const DecodeParams& p, hipStream_t s
 
 int decode_wgs_per_cu(int mode, int d, int group) {
   const int phi = group * 4 <= 16 ? 4 : (group * 2 <= 16 ? 2 : 1);
-  // four-wave workgroups: one wave per SIMD each
-#define KVQ_W(M_, D_, P_) if (mode == M_ && d == D_ && phi == P_) return decode_waves_per_simd<M_, D_, P_>();
+#define KVQ_W(M_, D_, P_) if (mode == M_ && d == D_ && phi == P_) return 4 * decode_waves_per_simd<M_, D_, P_>() / decode_wg_waves<M_, D_, P_>();
   KVQ_W(0, 64, 4) KVQ_W(0, 64, 2) KVQ_W(0, 64, 1) KVQ_W(0, 128, 4) KVQ_W(0, 128, 2) KVQ_W(0, 128, 1)
   KVQ_W(1, 64, 4) KVQ_W(1, 64, 2) KVQ_W(1, 64, 1) KVQ_W(1, 128, 4) KVQ_W(1, 128, 2) KVQ_W(1, 128, 1)
   KVQ_W(2, 64, 4) KVQ_W(2, 64, 2) KVQ_W(2, 64, 1) KVQ_W(2, 128, 4) KVQ_W(2, 128, 2) KVQ_W(2, 128, 1)

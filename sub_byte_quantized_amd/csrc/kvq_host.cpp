@@ -274,6 +274,7 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
   p.n_wgs = pl.n_wgs;
   p.ncu = num_cus();
   p.prio_rot = env_flag("KVQ_DECODE_PRIO", 1);
+  p.share_skew = env_flag("KVQ_DECODE_SKEW", 0);
   p.out_bf16 = out_dtype == KVQ_OUT_BF16;
   p.bits_magic = 0x43004300u;
   p.bits_n4 = 0x000F000Fu;
