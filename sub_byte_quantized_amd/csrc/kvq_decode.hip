@@ -1043,22 +1043,32 @@ void decode_kernel(DecodeParams p) {
         raw[i] = load_qrow<D>(p.q + ((int64_t)b * p.hq + h * G + g) * D, plane);
       }
     }
+    // the wave's first tile goes out now, its block ids read from the table
+    // itself (scalar loads), so its data is on the way while the block ids
+    // and query rows above come back and the query pieces are made
+    Cursor cur;
+    cur.ls = 0;
+    cur.li = 0;
+    cur.nseg = nseg;
+    cursor_seek(cur, sm, wave);
+    TileInfo ta;
+    if (cur.ls < nseg) {
+      const int b0 = __builtin_amdgcn_readfirstlane(sm.seg[cur.ls].b);
+      const int32_t* trow = p.tables + (int64_t)(p.headwise ? b0 * hkv + cur.h : b0) * p.max_blocks;
+      ta = tile_info<CB>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te, cur.L, cur.start, bl,
+                         hkv, cur.h);
+    } else {
+      ta = cursor_info<CB>(cur, sm, wave, bl, hkv);
+    }
+    cursor_next(cur, sm, wave);
+    issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
+
 #pragma unroll
     for (int u = 0; u < IDR; ++u) {
       const int j = pt + u * NT;
       if (j < ids_used) sm.ids[j] = idv[u];
     }
     __syncthreads();
-
-    // the wave's first tile goes out before the query prologue
-    Cursor cur;
-    cur.ls = 0;
-    cur.li = 0;
-    cur.nseg = nseg;
-    cursor_seek(cur, sm, wave);
-    TileInfo ta = cursor_info<CB>(cur, sm, wave, bl, hkv);
-    cursor_next(cur, sm, wave);
-    issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
 
 #pragma unroll
     for (int i = 0; i < QR; ++i) {
