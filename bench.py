@@ -13,8 +13,12 @@ memory larger than the 256 MB Infinity Cache.
 Prints ONE JSON line.  ``value`` is decode effective KV GB/s of the whole
 step: the algorithmic bytes decode reads (packed codes + fp32 scale/zero of
 attended tokens, plus queries, outputs and block-table entries) divided by
-the step time.  ``roofline`` is the decode kernel alone, timed with HIP
-events on the stream it runs on.  ``write`` reports quantize-write tokens/s
+the step time.  ``roofline`` is the decode kernel alone: after the timed
+steps, ``steps`` back-to-back decode launches between two HIP events on the
+stream it runs on, divided by ``steps`` (``in_step_launch_us`` is the same
+kernel bracketed inside the steps, which adds the launch gap after the
+write).  ``write``
+reports quantize-write tokens/s
 on a whole-cache fill.  ``cpu_baseline`` times the oracle on a bounded sample.
 """
 from __future__ import annotations
@@ -39,8 +43,10 @@ import sub_byte_quantized_amd as kvq  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc")
-# sources that define the decode kernels (the counter summary is tied to them)
+# sources that define the decode and prefill kernels (a counter summary is
+# tied to them)
 DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h")]
+PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")]
 
 
 def sha(paths):
@@ -155,6 +161,20 @@ def time_events(fn, reps):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
+def time_span(fn, reps):
+    """Mean duration of `reps` back-to-back calls: one HIP event before the
+    first and one after the last, on the current stream (the kernels' own)."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(reps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
 def cpu_baseline(spec, case, planes, seconds):
     """The oracle, as it stands, on a bounded sample of the same decode: as
     many (sequence, kv head) pairs as fit in ``seconds``."""
@@ -203,15 +223,15 @@ def cpu_baseline(spec, case, planes, seconds):
             "write_tokens_per_s": round(nt / tw, 1)}
 
 
-def load_traffic(name):
-    """HBM bytes per decode launch from the committed counter summary, or None
-    if it is missing or was taken on a different kernel source."""
+def load_traffic(name, srcs=DECODE_SRC):
+    """HBM bytes per launch from the committed counter summary, or None if it
+    is missing or was taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         j = json.load(f)
-    if j.get("kernel_source_sha") != sha(DECODE_SRC):
+    if j.get("kernel_source_sha") != sha(srcs):
         return None
     return j.get("hbm_bytes_per_launch")
 
@@ -320,8 +340,11 @@ def run_mixed(args, spec, dev):
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     w_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    p_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    d_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    p_step_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    d_step_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    # each kernel alone: back-to-back launches between two HIP events
+    p_ms = time_span(prefill, args.steps)
+    d_ms = time_span(decode, args.steps)
     T = int(new["k"].shape[0])
     wb = write_bytes_per_token(spec)
     p_tf = flops / (p_ms * 1e-3) / 1e12
@@ -345,12 +368,15 @@ def run_mixed(args, spec, dev):
                    "rotation": spec.rotate, "window": list(spec.window or []), "headwise_table": spec.headwise,
                    "seq_len": max_len, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(p_tf, 2),
-                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(p_tf / 2500.0, 4), "traffic": None,
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(p_tf / 2500.0, 4),
+                     "traffic": load_traffic(f"prefill_{spec.name}_counters.json", PREFILL_SRC),
                      "useful_pairs": pairs, "flops_per_launch": flops, "kv_bytes_per_launch": p_kv,
-                     "avg_launch_us": round(p_ms * 1e3, 2)},
+                     "avg_launch_us": round(p_ms * 1e3, 2), "launches": args.steps,
+                     "in_step_launch_us": round(p_step_ms * 1e3, 2)},
         "decode": {"kernel": "decode_kernel", "achieved_GBps": round(d_gbs, 2),
                    "frac": round(d_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": int(d_algo),
-                   "kv_tokens_attended": d_tokens, "avg_launch_us": round(d_ms * 1e3, 2)},
+                   "kv_tokens_attended": d_tokens, "avg_launch_us": round(d_ms * 1e3, 2),
+                   "in_step_launch_us": round(d_step_ms * 1e3, 2)},
         "write": {"step_tokens": T, "step_write_us": round(w_ms * 1e3, 2),
                   "tokens_per_s": round(T / (w_ms * 1e-3), 1), "bytes_per_token": wb,
                   "GBps": round(T * wb / (w_ms * 1e-3) / 1e9, 2)},
@@ -439,7 +465,12 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     write_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    dec_avg = float(np.mean(dec_ms))
+    step_dec_avg = float(np.mean(dec_ms))
+    # the decode kernel alone: `steps` back-to-back launches over the
+    # replicas between two HIP events on the stream it runs on (the host
+    # stays ahead of the GPU, so the span is the kernels and the gaps between
+    # them)
+    dec_avg = time_span(decode, args.steps)
 
     # quantize-write throughput: whole-cache fill into a scratch replica
     T = case.k.shape[0]
@@ -478,7 +509,8 @@ def main():
                      "frac": round(algo / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(f"decode_{spec.name}_counters.json"),
                      "algorithmic_bytes_per_launch": int(algo), "kv_bytes_per_launch": int(kv_bytes),
-                     "avg_launch_us": round(dec_avg * 1e3, 3)},
+                     "avg_launch_us": round(dec_avg * 1e3, 3), "launches": args.steps,
+                     "in_step_launch_us": round(step_dec_avg * 1e3, 3)},
         "write": {"step_write_us": round(float(np.mean(write_ms)) * 1e3, 3), "step_tokens": spec.B,
                   "fill_tokens": int(T), "fill_us": round(fill_avg * 1e3, 2),
                   "tokens_per_s": round(T / (fill_avg * 1e-3), 1),
