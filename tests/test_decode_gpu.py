@@ -208,3 +208,38 @@ def _sampled(cfg, n_pairs=12):
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_decode_full_config_sampled(cfg):
     _sampled(cfg)
+
+
+def _many_pair_lens(seed, n):
+    """Lengths for a batch with more (sequence, kv head) pairs than one LDS
+    scan chunk holds: some empty, most short, a fifth long enough that a few
+    segments fill the per-batch block-id table (block 16)."""
+    r = np.random.default_rng([seed, 7])
+    kind = r.random(n)
+    return [0 if k < 0.1 else int(r.integers(1, 201)) if k < 0.8 else int(r.integers(2000, 3001)) for k in kind]
+
+
+@pytest.mark.parametrize("mode,bs", [(1, 16), (0, 64), (2, 64)])
+def test_decode_many_pairs_chunks_and_batches(monkeypatch, mode, bs):
+    """1200 pairs (several prefix chunks), shares holding hundreds of
+    segments (many segment batches, some cut short by the block-id table),
+    empty sequences in between; default grid and a 7-workgroup grid."""
+    spec = synth.small_spec(name=f"many-m{mode}-b{bs}", cfg=470 + mode, mode=mode, rotate=mode != 0, bs=bs,
+                            B=300, Hkv=4, Hq=8, lens=_many_pair_lens(470 + mode, 300))
+    print(f"[case] decode {spec.name}", flush=True)
+    case, d, planes = gh.build(spec)
+    ref = gh.oracle_decode(spec, case, gh.host_planes(planes))
+    for nwg in (None, "7"):
+        if nwg is None:
+            monkeypatch.delenv("KVQ_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("KVQ_DECODE_WGS", nwg)
+        o1 = gh.gpu_decode(spec, case, d, planes)
+        o2 = gh.gpu_decode(spec, case, d, planes)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"repeat differs ({nwg} workgroups)"
+        o = o1.cpu().numpy()
+        lens = np.asarray(spec.lens)
+        assert np.all(o[lens == 0] == 0)
+        gh.assert_close(o, ref, f"{spec.name} wgs={nwg}")
+    monkeypatch.delenv("KVQ_DECODE_WGS", raising=False)
