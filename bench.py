@@ -13,13 +13,14 @@ memory larger than the 256 MB Infinity Cache.
 Prints ONE JSON line.  ``value`` is decode effective KV GB/s of the whole
 step: the algorithmic bytes decode reads (packed codes + fp32 scale/zero of
 attended tokens, plus queries, outputs and block-table entries) divided by
-the step time.  ``roofline`` is the decode kernel alone: after the timed
-steps, ``steps`` back-to-back decode launches between two HIP events on the
-stream it runs on, divided by ``steps`` (``in_step_launch_us`` is the same
-kernel bracketed inside the steps, which adds the launch gap after the
-write).  ``write``
-reports quantize-write tokens/s
-on a whole-cache fill.  ``cpu_baseline`` times the oracle on a bounded sample.
+the step time, the step's two kernels launched back to back (``--graph``
+replays them from one HIP graph per cache replica instead).  ``roofline`` is
+the decode kernel alone: after the
+timed steps, ``steps`` back-to-back eager decode launches between two HIP
+events on the stream it runs on, divided by ``steps`` (``in_step_launch_us``
+is the same kernel bracketed by events after the write, which adds the
+launch gap).  ``write`` reports quantize-write tokens/s on a whole-cache
+fill.  ``cpu_baseline`` times the oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -326,9 +327,17 @@ def run_mixed(args, spec, dev):
         prefill(i)
         decode(i)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: exactly `steps` steps, the three kernels back to back
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        write(i)
+        prefill(i)
+        decode(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the kernels inside a step, bracketed by events
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record()
         write(i)
@@ -338,7 +347,6 @@ def run_mixed(args, spec, dev):
         decode(i)
         ev[i][3].record()
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     w_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     p_step_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     d_step_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
@@ -396,6 +404,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas cycled (0 = enough for 1.2 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the step from a HIP graph instead of launching it")
     ap.add_argument("--mode", choices=["step", "copy"], default="step",
                     help="copy: time a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -450,10 +459,38 @@ def main():
         decode(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, events around each kernel
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # --graph: one HIP graph per cache replica (write, then decode), replayed
+    # (measured slower than eager launches for this two-kernel step)
+    graphs = None
+    if args.graph:
+        graphs = []
+        for k in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                write(k)
+                decode(k)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+
+    def step(i):
+        if graphs is not None:
+            graphs[i % R].replay()
+        else:
+            write(i)
+            decode(i)
+
+    # timed region: exactly `steps` steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    # the two kernels inside a step, bracketed by events (eager launches)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record()
         write(i)
@@ -461,8 +498,6 @@ def main():
         decode(i)
         ev[i][2].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
     write_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
     step_dec_avg = float(np.mean(dec_ms))
@@ -502,7 +537,8 @@ def main():
         "config": {"workload": spec.name, "batch": spec.B, "q_heads": spec.Hq, "kv_heads": spec.Hkv,
                    "head_dim": spec.D, "block_size": spec.bs, "mode": ["int8_sym", "int4_asym", "int2_asym"][spec.mode],
                    "rotation": spec.rotate, "tokens_cached": int(T), "kv_tokens_attended": tokens,
-                   "cache_replicas": R, "parallelism": "single GPU"},
+                   "cache_replicas": R, "parallelism": "single GPU",
+                   "step_launch": "eager" if graphs is None else "hip graph per replica"},
         "hbm_frac_of_step": round(algo / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "decode_kernel",
                      "achieved": round(algo / (dec_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
