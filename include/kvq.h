@@ -181,6 +181,46 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc,
                                       void* workspace, size_t workspace_bytes,
                                       void* stream);
 
+/* One decode step in one launch: the quantize-on-write of each sequence's
+ * new token followed by paged decode attention (the decoder's cache write and
+ * attention of FastDeploy PR 5173, Modifications, and the append-then-attend
+ * shape of FastDeploy PR 7718; the write and read halves of the vLLM PR 40835
+ * summary, 实现拆解 item 2).  The result equals kvq_reshape_and_cache of the
+ * B tokens followed by kvq_paged_decode_attention, codes and output bit for
+ * bit.
+ *   key, value   (device) bf16 [B, Hkv, D] rows, token b belongs to sequence
+ *                b; token strides in elements (>= Hkv*D, multiple of 8),
+ *                16-byte aligned
+ *   slot_mapping (device) int64 [B], or slot_mapping_headwise int64 [B, Hkv];
+ *                exactly one non-NULL.  A slot < 0 skips that token (or head).
+ *                A written slot must be the one the block table gives position
+ *                seq_lens[b] - 1 of sequence b (and head h when head-wise):
+ *                the workgroup that attends that position writes it first; a
+ *                slot anywhere else leaves the attention's view of it undefined.
+ *                Sequences with seq_lens[b] = 0 have no new token and nothing
+ *                is written for them.
+ * Every other argument, the workspace and the errors are those of
+ * kvq_paged_decode_attention (the planes are written, so they are not const).
+ * Calls sharing one workspace must not overlap in time.  One kernel launch. */
+kvq_status kvq_decode_step(const kvq_cache_desc* desc,
+                           void* out, int32_t out_dtype,
+                           const void* query,
+                           int32_t num_seqs, int32_t num_q_heads,
+                           const void* key, const void* value,
+                           int64_t key_tok_stride, int64_t value_tok_stride,
+                           const int64_t* slot_mapping,
+                           const int64_t* slot_mapping_headwise,
+                           uint8_t* k_codes, float* k_meta,
+                           uint8_t* v_codes, float* v_meta,
+                           const int32_t* block_tables,
+                           const int32_t* block_tables_headwise,
+                           int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t max_seq_len,
+                           const int32_t* window,
+                           float softmax_scale,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Chunked-prefill attention (vLLM PR 40835 summary, 实现拆解 item 2; the
  * vllm-ascend-quantized-kv-cache package, 运行机制: prefill reads the paged
  * quantized cache; FastDeploy PR 7718: head-wise table with -1 skips and

@@ -53,6 +53,7 @@
 // its workgroups counts in last.
 #include "kvq_internal.h"
 #include "kvq_device.h"
+#include "kvq_write_row.h"
 
 namespace kvq {
 namespace {
@@ -1013,11 +1014,39 @@ void decode_kernel(DecodeParams p) {
     if (nseg == 0) break;
     __syncthreads();   // records visible; the previous batch's LDS reads are done
 
-    // ---- batch prologue: block ids (into LDS) and query rows (into
-    // registers) are all requested before anything waits on them.  Thread
-    // index opaque to the compiler, as in the segment epilogue.
-    int pt = threadIdx.x;
+    // ---- fused step: the new token (position L - 1) of every pair whose
+    // last tile is in this batch is quantized and stored, K and V rows by one
+    // lane group each, and the stores complete before any of the batch's
+    // tiles is read.  Only this workgroup reads that tile, so no other
+    // workgroup has to wait for it.
+    int pt = threadIdx.x;   // thread index opaque to the compiler, as in the segment epilogue
     asm volatile("" : "+v"(pt));
+    if (p.fused) {
+      bool any = false;
+      for (int k = 0; k < nseg; ++k) {
+        const int te = __builtin_amdgcn_readfirstlane(sm.seg[k].te);
+        const int Lk = __builtin_amdgcn_readfirstlane(sm.seg[k].L);
+        any = any || (Lk > 0 && te - 1 == (Lk - 1) >> 6);
+      }
+      if (any) {
+        constexpr int LPR = D / 8;
+        const int grp = pt / LPR;
+        if (grp < 2 * nseg) {
+          const SegRec& sr = sm.seg[grp >> 1];
+          if (sr.L > 0 && sr.te - 1 == (sr.L - 1) >> 6) {
+            const int64_t slot = p.wp.slot_hw ? p.wp.slot_hw[(int64_t)sr.b * hkv + sr.h] : p.wp.slot[sr.b];
+            write_row<MODE, D, ROT>(p.wp, sr.b, sr.h, grp & 1, slot, pt % LPR);
+          }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __syncthreads();
+      }
+    }
+
+    // ---- batch prologue: block ids (into LDS) and query rows (into
+    // registers) are all requested before anything waits on them.
     const int plane = pt & 63;
     uint32_t raw[QR];
     int idv[IDR];

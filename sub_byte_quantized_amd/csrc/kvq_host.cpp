@@ -134,6 +134,88 @@ kvq_status check_decode_sizes(const kvq_cache_desc* d, int num_seqs, int num_q_h
   return KVQ_OK;
 }
 
+kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
+                                      const void* query, int32_t num_seqs, int32_t num_q_heads,
+                                      const uint8_t* k_codes, const float* k_meta,
+                                      const uint8_t* v_codes, const float* v_meta,
+                                      const int32_t* block_tables, const int32_t* block_tables_headwise,
+                                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                      int32_t max_seq_len, const int32_t* window, float softmax_scale,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      const kvq::WriteParams* wp) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  st = check_decode_sizes(desc, num_seqs, num_q_heads, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16)
+    return fail(KVQ_EINVAL, "out_dtype %d is not a kvq_out_dtype", out_dtype);
+  if ((block_tables == nullptr) == (block_tables_headwise == nullptr))
+    return fail(KVQ_EINVAL, "exactly one of block_tables and block_tables_headwise must be non-NULL");
+  if (max_blocks_per_seq < 1) return fail(KVQ_EINVAL, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * desc->block_size)
+    return fail(KVQ_EINVAL, "max_seq_len %d exceeds max_blocks_per_seq*block_size = %lld", max_seq_len,
+                (long long)max_blocks_per_seq * desc->block_size);
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is not finite");
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !seq_lens) return fail(KVQ_EINVAL, "out, query or seq_lens is NULL");
+  if (!aligned(out, 16)) return fail(KVQ_EINVAL, "out must be 16-byte aligned");
+  st = check_planes(k_codes, k_meta, v_codes, v_meta);
+  if (st != KVQ_OK) return st;
+  const DecodePlan pl = plan_decode(desc, num_seqs, num_q_heads, max_seq_len);
+  if (!workspace) return fail(KVQ_EINVAL, "workspace is NULL (%zu bytes needed)", pl.total());
+  if (workspace_bytes < pl.total())
+    return fail(KVQ_ENOSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total());
+  if (!aligned(workspace, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
+  kvq::DecodeParams p{};
+  p.k_codes = k_codes;
+  p.k_meta = k_meta;
+  p.v_codes = v_codes;
+  p.v_meta = v_meta;
+  p.q = static_cast<const uint16_t*>(query);
+  p.out = out;
+  p.headwise = block_tables_headwise != nullptr;
+  p.tables = p.headwise ? block_tables_headwise : block_tables;
+  p.seq_lens = seq_lens;
+  p.window = window;
+  p.signs = desc->rot_signs;
+  p.counters = static_cast<int32_t*>(workspace);
+  p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counter_bytes);
+  p.qscale = softmax_scale * 1.4426950408889634f;
+  p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
+  p.max_blocks = max_blocks_per_seq;
+  p.block_size = desc->block_size;
+  p.block_size_log2 = __builtin_ctz((unsigned)desc->block_size);
+  p.hq = num_q_heads;
+  p.hkv = desc->num_kv_heads;
+  p.group = num_q_heads / desc->num_kv_heads;
+  p.num_pairs = num_seqs * desc->num_kv_heads;
+  p.n_wgs = pl.n_wgs;
+  p.ncu = num_cus();
+  p.prio_rot = env_flag("KVQ_DECODE_PRIO", 1);
+  p.share_skew = env_flag("KVQ_DECODE_SKEW", 0);
+  p.out_bf16 = out_dtype == KVQ_OUT_BF16;
+  p.bits_magic = 0x43004300u;
+  p.bits_n4 = 0x000F000Fu;
+  p.bits_n2 = 0x00030003u;
+  if (wp) {
+    p.fused = 1;
+    p.wp = *wp;
+    p.wp.k_codes = const_cast<uint8_t*>(k_codes);
+    p.wp.k_meta = const_cast<float*>(k_meta);
+    p.wp.v_codes = const_cast<uint8_t*>(v_codes);
+    p.wp.v_meta = const_cast<float*>(v_meta);
+    p.wp.hkv = desc->num_kv_heads;
+    p.wp.block_size = desc->block_size;
+    p.wp.signs = desc->rot_signs;
+    p.wp.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
+    p.wp.total_rows = 2 * (int64_t)num_seqs * desc->num_kv_heads;
+  }
+  hipError_t e = kvq::launch_decode(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,64 +307,42 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
                                       int32_t max_seq_len, const int32_t* window, float softmax_scale,
                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(desc, out, out_dtype, query, num_seqs, num_q_heads, k_codes, k_meta, v_codes, v_meta,
+                     block_tables, block_tables_headwise, max_blocks_per_seq, seq_lens, max_seq_len, window,
+                     softmax_scale, workspace, workspace_bytes, stream, nullptr);
+}
+
+kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* out, int32_t out_dtype, const void* query,
+                           int32_t num_seqs, int32_t num_q_heads, const void* key, const void* value,
+                           int64_t key_tok_stride, int64_t value_tok_stride, const int64_t* slot_mapping,
+                           const int64_t* slot_mapping_headwise, uint8_t* k_codes, float* k_meta,
+                           uint8_t* v_codes, float* v_meta, const int32_t* block_tables,
+                           const int32_t* block_tables_headwise, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t max_seq_len, const int32_t* window,
+                           float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
   kvq_status st = check_desc(desc);
   if (st != KVQ_OK) return st;
-  st = check_decode_sizes(desc, num_seqs, num_q_heads, max_seq_len);
-  if (st != KVQ_OK) return st;
-  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16)
-    return fail(KVQ_EINVAL, "out_dtype %d is not a kvq_out_dtype", out_dtype);
-  if ((block_tables == nullptr) == (block_tables_headwise == nullptr))
-    return fail(KVQ_EINVAL, "exactly one of block_tables and block_tables_headwise must be non-NULL");
-  if (max_blocks_per_seq < 1) return fail(KVQ_EINVAL, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
-  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * desc->block_size)
-    return fail(KVQ_EINVAL, "max_seq_len %d exceeds max_blocks_per_seq*block_size = %lld", max_seq_len,
-                (long long)max_blocks_per_seq * desc->block_size);
-  if (!std::isfinite(softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is not finite");
-  if (num_seqs == 0) return ok();
-  if (!out || !query || !seq_lens) return fail(KVQ_EINVAL, "out, query or seq_lens is NULL");
-  if (!aligned(out, 16)) return fail(KVQ_EINVAL, "out must be 16-byte aligned");
-  st = check_planes(k_codes, k_meta, v_codes, v_meta);
-  if (st != KVQ_OK) return st;
-  const DecodePlan pl = plan_decode(desc, num_seqs, num_q_heads, max_seq_len);
-  if (!workspace) return fail(KVQ_EINVAL, "workspace is NULL (%zu bytes needed)", pl.total());
-  if (workspace_bytes < pl.total())
-    return fail(KVQ_ENOSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total());
-  if (!aligned(workspace, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
-  kvq::DecodeParams p{};
-  p.k_codes = k_codes;
-  p.k_meta = k_meta;
-  p.v_codes = v_codes;
-  p.v_meta = v_meta;
-  p.q = static_cast<const uint16_t*>(query);
-  p.out = out;
-  p.headwise = block_tables_headwise != nullptr;
-  p.tables = p.headwise ? block_tables_headwise : block_tables;
-  p.seq_lens = seq_lens;
-  p.window = window;
-  p.signs = desc->rot_signs;
-  p.counters = static_cast<int32_t*>(workspace);
-  p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counter_bytes);
-  p.qscale = softmax_scale * 1.4426950408889634f;
-  p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
-  p.max_blocks = max_blocks_per_seq;
-  p.block_size = desc->block_size;
-  p.block_size_log2 = __builtin_ctz((unsigned)desc->block_size);
-  p.hq = num_q_heads;
-  p.hkv = desc->num_kv_heads;
-  p.group = num_q_heads / desc->num_kv_heads;
-  p.num_pairs = num_seqs * desc->num_kv_heads;
-  p.n_wgs = pl.n_wgs;
-  p.ncu = num_cus();
-  p.prio_rot = env_flag("KVQ_DECODE_PRIO", 1);
-  p.share_skew = env_flag("KVQ_DECODE_SKEW", 0);
-  p.out_bf16 = out_dtype == KVQ_OUT_BF16;
-  p.bits_magic = 0x43004300u;
-  p.bits_n4 = 0x000F000Fu;
-  p.bits_n2 = 0x00030003u;
-  hipError_t e = kvq::launch_decode(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p,
-                                    static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(KVQ_EHIP, "decode launch: %s", hipGetErrorString(e));
-  return ok();
+  if (num_seqs > 0) {
+    if ((slot_mapping == nullptr) == (slot_mapping_headwise == nullptr))
+      return fail(KVQ_EINVAL, "exactly one of slot_mapping and slot_mapping_headwise must be non-NULL");
+    const int D = desc->head_dim, H = desc->num_kv_heads;
+    if (!key || !value) return fail(KVQ_EINVAL, "key or value is NULL");
+    if (key_tok_stride < (int64_t)H * D || value_tok_stride < (int64_t)H * D)
+      return fail(KVQ_EINVAL, "token strides (%lld, %lld) must be >= num_kv_heads*head_dim = %d",
+                  (long long)key_tok_stride, (long long)value_tok_stride, H * D);
+    if (key_tok_stride % 8 != 0 || value_tok_stride % 8 != 0 || !aligned(key, 16) || !aligned(value, 16))
+      return fail(KVQ_EINVAL, "key/value must be 16-byte aligned with token strides a multiple of 8");
+  }
+  kvq::WriteParams w{};
+  w.key = static_cast<const uint16_t*>(key);
+  w.value = static_cast<const uint16_t*>(value);
+  w.key_stride = key_tok_stride;
+  w.value_stride = value_tok_stride;
+  w.slot = slot_mapping;
+  w.slot_hw = slot_mapping_headwise;
+  return decode_impl(desc, out, out_dtype, query, num_seqs, num_q_heads, k_codes, k_meta, v_codes, v_meta,
+                     block_tables, block_tables_headwise, max_blocks_per_seq, seq_lens, max_seq_len, window,
+                     softmax_scale, workspace, workspace_bytes, stream, &w);
 }
 
 kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, int32_t out_dtype,

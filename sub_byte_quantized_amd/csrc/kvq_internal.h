@@ -70,6 +70,8 @@ struct DecodeParams {
   uint32_t bits_magic;          // 0x43004300: bf16 128.0 in both halves
   uint32_t bits_n4;             // 0x000F000F
   uint32_t bits_n2;             // 0x00030003
+  int32_t fused;                // 1: write each sequence's new token first (wp)
+  WriteParams wp;               // the new tokens: token b = sequence b
 };
 
 struct PrefillParams {

@@ -1,0 +1,145 @@
+// One cache row of the quantize-on-write (the arithmetic the cache format
+// defines, in the order of the prhub summary of vLLM PR 40835, 实现拆解 item
+// 2): bf16 row -> optional rotation -> scale (and zero) -> round -> pack ->
+// paged store.  Shared by the write kernel and the fused decode step.
+//
+// The D/8 lanes lr = 0 .. D/8-1 of one aligned lane group call it together
+// (converged: the FWHT and the statistics are shuffles within the group);
+// each lane owns 8 consecutive elements.  Row (token t, kv head h, K if kv =
+// 0 else V) goes to `slot` (block * block_size + offset); slot < 0 computes
+// nothing visible.
+#pragma once
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+template <int MODE, int D, bool ROT>
+__device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h, int kv, int64_t slot, int lr) {
+#pragma clang fp contract(off)
+  constexpr int LPR = D / 8;             // lanes per row
+  constexpr int P = row_bytes(MODE, D);  // packed bytes per row
+  constexpr int BPL = P / LPR;           // packed bytes per lane
+  constexpr int M = mode_meta(MODE);
+  constexpr float kLevels = (float)mode_levels(MODE);
+  const int hkv = p.hkv;
+  const bool active = slot >= 0;
+
+  float x[8];
+  if (active) {
+    const uint16_t* src = kv ? p.value + t * p.value_stride : p.key + t * p.key_stride;
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + (int64_t)h * D + lr * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+  }
+
+  if constexpr (ROT) {
+    const float4 s0 = *reinterpret_cast<const float4*>(p.signs + lr * 8);
+    const float4 s1 = *reinterpret_cast<const float4*>(p.signs + lr * 8 + 4);
+    x[0] *= s0.x; x[1] *= s0.y; x[2] *= s0.z; x[3] *= s0.w;
+    x[4] *= s1.x; x[5] *= s1.y; x[6] *= s1.z; x[7] *= s1.w;
+    // in-lane butterflies, pairs (i, i + hh) with bit hh of i clear
+#pragma unroll
+    for (int hh = 1; hh < 8; hh <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (!(i & hh)) {
+          const float a = x[i], b = x[i + hh];
+          x[i] = a + b;
+          x[i + hh] = a - b;
+        }
+      }
+    }
+    // cross-lane butterflies: element stride 8*m lives m lanes away
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) {
+      const bool upper = (lr & m) != 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float o = __shfl_xor(x[i], m);
+        x[i] = upper ? (o - x[i]) : (x[i] + o);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = x[i] * p.inv_sqrt_d;
+  }
+
+  float s, z;
+  if constexpr (MODE == 0) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) a = fmaxf(a, __shfl_xor(a, m));
+    s = a / kLevels;
+    z = 0.0f;
+  } else {
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      mn = fminf(mn, x[i]);
+      mx = fmaxf(mx, x[i]);
+    }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, m));
+      mx = fmaxf(mx, __shfl_xor(mx, m));
+    }
+    s = (mx - mn) / kLevels;
+    z = mn;
+  }
+
+  // zero, subnormal or NaN scale: all-zero codes
+  const bool ok = s >= 1.17549435e-38f;
+  const float inv = ok ? 1.0f / s : 0.0f;
+  constexpr float lo = MODE == 0 ? -kLevels : 0.0f;
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float tq = MODE == 0 ? x[i] * inv : (x[i] - z) * inv;
+    const float r = fminf(fmaxf(__builtin_rintf(tq), lo), kLevels);
+    c[i] = ok ? (uint32_t)(int32_t)r : 0u;
+  }
+
+  if (!active) return;
+  const int64_t blk = slot / p.block_size;
+  const int64_t off = slot - blk * p.block_size;
+  const int64_t ridx = (blk * hkv + h) * p.block_size + off;
+  uint8_t* codes = (kv ? p.v_codes : p.k_codes) + ridx * P + lr * BPL;
+  float* meta = (kv ? p.v_meta : p.k_meta) + ridx * M;
+
+  if constexpr (MODE == 0) {
+    uint2 w;
+    w.x = (c[0] & 0xffu) | ((c[1] & 0xffu) << 8) | ((c[2] & 0xffu) << 16) | ((c[3] & 0xffu) << 24);
+    w.y = (c[4] & 0xffu) | ((c[5] & 0xffu) << 8) | ((c[6] & 0xffu) << 16) | ((c[7] & 0xffu) << 24);
+    *reinterpret_cast<uint2*>(codes) = w;
+  } else if constexpr (MODE == 1) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= c[i] << (4 * i);
+    *reinterpret_cast<uint32_t*>(codes) = w;
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= c[i] << (2 * i);
+    *reinterpret_cast<uint16_t*>(codes) = (uint16_t)w;
+  }
+  if (lr == 0) {
+    if constexpr (M == 1) {
+      meta[0] = s;
+    } else {
+      *reinterpret_cast<float2*>(meta) = make_float2(s, z);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace kvq

@@ -185,6 +185,62 @@ def kvq_paged_decode_attention(desc: CacheDesc, query: torch.Tensor,
     return out
 
 
+def kvq_decode_step(desc: CacheDesc, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                    k_codes: torch.Tensor, k_meta: torch.Tensor,
+                    v_codes: torch.Tensor, v_meta: torch.Tensor,
+                    seq_lens: torch.Tensor, max_seq_len: int,
+                    slot_mapping: Optional[torch.Tensor] = None,
+                    slot_mapping_headwise: Optional[torch.Tensor] = None,
+                    block_tables: Optional[torch.Tensor] = None,
+                    block_tables_headwise: Optional[torch.Tensor] = None,
+                    window: Optional[torch.Tensor] = None,
+                    softmax_scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None,
+                    out_dtype: torch.dtype = torch.float32,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step in one launch: quantize-on-write of each sequence's
+    new token (key/value [B, Hkv, D] bf16, token b at slot_mapping[b], which
+    must be position seq_lens[b] - 1 of sequence b's table), then decode
+    attention of query [B, Hq, D]; returns out [B, Hq, D]."""
+    dev = query.device
+    _need(query, "query", torch.bfloat16, dev)
+    B, Hq, D = query.shape
+    for t, n in ((key, "key"), (value, "value")):
+        _need(t, n, torch.bfloat16, dev, contiguous=False)
+        if t.dim() != 3 or t.shape[0] != B or t.stride(2) != 1 or t.stride(1) != desc.head_dim:
+            raise ValueError(f"{n} must be [B, Hkv, D] with heads and D contiguous")
+    _need(slot_mapping, "slot_mapping", torch.int64, dev)
+    _need(slot_mapping_headwise, "slot_mapping_headwise", torch.int64, dev)
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(block_tables_headwise, "block_tables_headwise", torch.int32, dev)
+    _need(window, "window", torch.int32, dev)
+    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (v_codes, "v_codes", torch.uint8),
+                     (k_meta, "k_meta", torch.float32), (v_meta, "v_meta", torch.float32)):
+        _need(t, n, dt, dev)
+    tab = block_tables if block_tables is not None else block_tables_headwise
+    max_blocks = int(tab.shape[1]) if tab is not None else 0
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
+    _need(out, "out", out.dtype, dev)
+    odt = {torch.float32: KVQ_OUT_F32, torch.bfloat16: KVQ_OUT_BF16}[out.dtype]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = alloc_workspace(kvq_decode_workspace_size(desc, B, Hq, max_seq_len), dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    d = desc.c()
+    _check(_lib.load().kvq_decode_step(
+        ctypes.byref(d), _ptr(out), odt, _ptr(query), int(B), int(Hq),
+        _ptr(key), _ptr(value), key.stride(0), value.stride(0),
+        _ptr(slot_mapping), _ptr(slot_mapping_headwise),
+        _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
+        _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
+        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale),
+        _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
 def kvq_paged_prefill_attention(desc: CacheDesc, query: torch.Tensor, cu_seqlens_q: torch.Tensor,
                                 max_q_len: int,
                                 k_codes: torch.Tensor, k_meta: torch.Tensor,

@@ -34,7 +34,7 @@ def test_header_lists_entry_points():
     names = header_functions()
     for n in ("kvq_query_layout", "kvq_reshape_and_cache", "kvq_paged_decode_attention",
               "kvq_decode_workspace_size", "kvq_workspace_init", "kvq_paged_prefill_attention",
-              "kvq_last_error"):
+              "kvq_decode_step", "kvq_last_error"):
         assert n in names
 
 
