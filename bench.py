@@ -2,8 +2,9 @@
 """Benchmark of the quantized paged KV cache on one MI355X.
 
 A step is one decode step of the workload: quantize-on-write of the step's
-new token of every sequence (kvq_reshape_and_cache), then paged decode
-attention of every sequence over its whole cache (kvq_paged_decode_attention).
+new token of every sequence, then paged decode attention of every sequence
+over its whole cache, both in one launch (kvq_decode_step; ``--unfused``
+runs kvq_reshape_and_cache then kvq_paged_decode_attention instead).
 The default workload is the INT8 per-token-head symmetric decode (batch 32,
 32 q / 8 kv heads, head_dim 128, block 64, seq_lens ~U[1024, 8192], 4 outlier
 channels x10); --config selects the others.  The cache is built once (untimed)
@@ -13,14 +14,14 @@ memory larger than the 256 MB Infinity Cache.
 Prints ONE JSON line.  ``value`` is decode effective KV GB/s of the whole
 step: the algorithmic bytes decode reads (packed codes + fp32 scale/zero of
 attended tokens, plus queries, outputs and block-table entries) divided by
-the step time, the step's two kernels launched back to back (``--graph``
-replays them from one HIP graph per cache replica instead).  ``roofline`` is
-the decode kernel alone: after the
-timed steps, ``steps`` back-to-back eager decode launches between two HIP
-events on the stream it runs on, divided by ``steps`` (``in_step_launch_us``
-is the same kernel bracketed by events after the write, which adds the
-launch gap).  ``write`` reports quantize-write tokens/s on a whole-cache
-fill.  ``cpu_baseline`` times the oracle on a bounded sample.
+the step time, steps launched back to back (``--graph`` replays each from a
+HIP graph instead).  ``roofline`` is the step's kernel alone: after the
+timed steps, ``steps`` back-to-back launches between two HIP events on the
+stream it runs on, divided by ``steps``; its algorithmic bytes add the new
+tokens' write (bf16 rows read, codes + meta + slots).  ``decode_only`` is
+kvq_paged_decode_attention timed the same way, ``write.step_write_us`` the
+step's write alone.  ``write`` also reports quantize-write tokens/s on a
+whole-cache fill.  ``cpu_baseline`` times the oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -405,6 +406,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step from a HIP graph instead of launching it")
+    ap.add_argument("--unfused", action="store_true", help="run the step as write then decode (two launches)")
     ap.add_argument("--mode", choices=["step", "copy"], default="step",
                     help="copy: time a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -454,21 +456,31 @@ def main():
                                        window=case.window, softmax_scale=case.softmax_scale,
                                        out=out, workspace=ws)
 
-    for i in range(args.warmup):
+    def fused(i):
+        rp = replicas[i % R]
+        kvq.kvq_decode_step(d, case.q, new["k"], new["v"], *rp, case.seq_lens, max_len,
+                            slot_mapping=new["sm"], slot_mapping_headwise=new["smh"],
+                            block_tables=case.block_tables, block_tables_headwise=case.block_tables_headwise,
+                            window=case.window, softmax_scale=case.softmax_scale, out=out, workspace=ws)
+
+    def two_calls(i):
         write(i)
         decode(i)
+
+    one = two_calls if args.unfused else fused
+    for i in range(args.warmup):
+        one(i)
     torch.cuda.synchronize()
 
-    # --graph: one HIP graph per cache replica (write, then decode), replayed
-    # (measured slower than eager launches for this two-kernel step)
+    # --graph: one HIP graph per cache replica holding the step, replayed
+    # (measured slower than eager launches for the two-kernel step)
     graphs = None
     if args.graph:
         graphs = []
         for k in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                write(k)
-                decode(k)
+                one(k)
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % R].replay()
@@ -478,8 +490,7 @@ def main():
         if graphs is not None:
             graphs[i % R].replay()
         else:
-            write(i)
-            decode(i)
+            one(i)
 
     # timed region: exactly `steps` steps
     torch.cuda.synchronize()
@@ -489,23 +500,18 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    # the two kernels inside a step, bracketed by events (eager launches)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record()
-        write(i)
-        ev[i][1].record()
-        decode(i)
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    write_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    step_dec_avg = float(np.mean(dec_ms))
-    # the decode kernel alone: `steps` back-to-back launches over the
-    # replicas between two HIP events on the stream it runs on (the host
-    # stays ahead of the GPU, so the span is the kernels and the gaps between
-    # them)
-    dec_avg = time_span(decode, args.steps)
+    # the step's kernel alone (the fused write + decode; with --unfused the
+    # decode): `steps` back-to-back launches over the replicas between two
+    # HIP events on the stream it runs on (the host stays ahead of the GPU,
+    # so the span is the kernels and the gaps between them)
+    step_kernel = decode if args.unfused else fused
+    dec_avg = time_span(step_kernel, args.steps)
+    # for reference: decode alone and the step's write alone, same way
+    dec_only_avg = time_span(decode, args.steps)
+    step_write_avg = time_span(write, args.steps)
+    wb = write_bytes_per_token(spec)
+    step_write_bytes = spec.B * wb
+    k_algo = algo if args.unfused else algo + step_write_bytes
 
     # quantize-write throughput: whole-cache fill into a scratch replica
     T = case.k.shape[0]
@@ -518,7 +524,6 @@ def main():
     fill(0)
     fill_ms = time_events(fill, 5)
     fill_avg = float(np.mean(fill_ms))
-    wb = write_bytes_per_token(spec)
 
     result = {
         "metric": "decode-attn effective KV GB/s (% HBM peak); quantize-write tokens/s",
@@ -538,16 +543,19 @@ def main():
                    "head_dim": spec.D, "block_size": spec.bs, "mode": ["int8_sym", "int4_asym", "int2_asym"][spec.mode],
                    "rotation": spec.rotate, "tokens_cached": int(T), "kv_tokens_attended": tokens,
                    "cache_replicas": R, "parallelism": "single GPU",
+                   "step": "write + decode, two launches" if args.unfused else "fused write + decode, one launch",
                    "step_launch": "eager" if graphs is None else "hip graph per replica"},
         "hbm_frac_of_step": round(algo / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel",
-                     "achieved": round(algo / (dec_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(algo / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel" + ("" if args.unfused else " (fused step: new-token write + decode)"),
+                     "achieved": round(k_algo / (dec_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_algo / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(f"decode_{spec.name}_counters.json"),
-                     "algorithmic_bytes_per_launch": int(algo), "kv_bytes_per_launch": int(kv_bytes),
-                     "avg_launch_us": round(dec_avg * 1e3, 3), "launches": args.steps,
-                     "in_step_launch_us": round(step_dec_avg * 1e3, 3)},
-        "write": {"step_write_us": round(float(np.mean(write_ms)) * 1e3, 3), "step_tokens": spec.B,
+                     "algorithmic_bytes_per_launch": int(k_algo), "kv_bytes_per_launch": int(kv_bytes),
+                     "avg_launch_us": round(dec_avg * 1e3, 3), "launches": args.steps},
+        "decode_only": {"avg_launch_us": round(dec_only_avg * 1e3, 3),
+                        "achieved": round(algo / (dec_only_avg * 1e-3) / 1e9, 2),
+                        "algorithmic_bytes_per_launch": int(algo)},
+        "write": {"step_write_us": round(step_write_avg * 1e3, 3), "step_tokens": spec.B,
                   "fill_tokens": int(T), "fill_us": round(fill_avg * 1e3, 2),
                   "tokens_per_s": round(T / (fill_avg * 1e-3), 1),
                   "bytes_per_token": wb, "GBps": round(T * wb / (fill_avg * 1e-3) / 1e9, 2),

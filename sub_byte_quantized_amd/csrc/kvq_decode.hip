@@ -348,13 +348,19 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
       zvv[tau][i] = M == 2 ? b.vm[tau][2 * i + 1] : 0.0f;
     }
   if (__builtin_expect(!full, 0)) {
+    // the lane index re-derived here (mbcnt, from no register), so this rare
+    // path's per-lane masks and offsets are not hoisted out of the tile loop,
+    // where they would hold registers or spill
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int qm = ln >> 4, pm = (ln & 15) % PHI;
 #pragma unroll
     for (int tau = 0; tau < Gm::NKT; ++tau) {
-      const int sg = tau * PHI + phi_col;
+      const int sg = tau * PHI + pm;
       const bool tv = (t.valid >> sg) & 1u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int pos = t.pos0 + 16 * sg + 4 * q + i;
+        const int pos = t.pos0 + 16 * sg + 4 * qm + i;
         const bool keep = tv && pos < L && pos >= start;
         sc[tau][i] = keep ? sc[tau][i] : kNegInf;
         svv[tau][i] = keep ? svv[tau][i] : 0.0f;
@@ -1014,40 +1020,50 @@ void decode_kernel(DecodeParams p) {
     if (nseg == 0) break;
     __syncthreads();   // records visible; the previous batch's LDS reads are done
 
-    // ---- fused step: the new token (position L - 1) of every pair whose
-    // last tile is in this batch is quantized and stored, K and V rows by one
-    // lane group each, and the stores complete before any of the batch's
-    // tiles is read.  Only this workgroup reads that tile, so no other
-    // workgroup has to wait for it.
     int pt = threadIdx.x;   // thread index opaque to the compiler, as in the segment epilogue
     asm volatile("" : "+v"(pt));
+    const int plane = pt & 63;
+
+    // fused step: does this batch hold the last tile of a pair (the tile with
+    // the new token at position L - 1)?
+    bool wr = false;
     if (p.fused) {
-      bool any = false;
       for (int k = 0; k < nseg; ++k) {
         const int te = __builtin_amdgcn_readfirstlane(sm.seg[k].te);
         const int Lk = __builtin_amdgcn_readfirstlane(sm.seg[k].L);
-        any = any || (Lk > 0 && te - 1 == (Lk - 1) >> 6);
-      }
-      if (any) {
-        constexpr int LPR = D / 8;
-        const int grp = pt / LPR;
-        if (grp < 2 * nseg) {
-          const SegRec& sr = sm.seg[grp >> 1];
-          if (sr.L > 0 && sr.te - 1 == (sr.L - 1) >> 6) {
-            const int64_t slot = p.wp.slot_hw ? p.wp.slot_hw[(int64_t)sr.b * hkv + sr.h] : p.wp.slot[sr.b];
-            write_row<MODE, D, ROT>(p.wp, sr.b, sr.h, grp & 1, slot, pt % LPR);
-          }
-        }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __syncthreads();
+        wr = wr || (Lk > 0 && te - 1 == (Lk - 1) >> 6);
       }
     }
 
+    // ---- the wave's first tile goes out first, its block ids read from the
+    // table itself (scalar loads), so its data is on the way while the rest
+    // of the prologue runs; a tile holding a new token waits until after the
+    // barrier that follows the token's store
+    Cursor cur;
+    cur.ls = 0;
+    cur.li = 0;
+    cur.nseg = nseg;
+    cursor_seek(cur, sm, wave);
+    TileInfo ta;
+    // the last wave writes the new tokens, so only it waits on stores; its
+    // first tile, and any wave's first tile that holds a new token, go out
+    // after the barrier
+    const bool writer = wr && wave == NWV - 1;
+    const bool defer = writer ||
+                       (wr && cur.ls < nseg && cur.L > 0 && cur.tb + wave + NWV * cur.li == (cur.L - 1) >> 6);
+    if (cur.ls < nseg) {
+      const int b0 = __builtin_amdgcn_readfirstlane(sm.seg[cur.ls].b);
+      const int32_t* trow = p.tables + (int64_t)(p.headwise ? b0 * hkv + cur.h : b0) * p.max_blocks;
+      ta = tile_info<CB>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te, cur.L, cur.start, bl,
+                         hkv, cur.h);
+    } else {
+      ta = cursor_info<CB>(cur, sm, wave, bl, hkv);
+    }
+    cursor_next(cur, sm, wave);
+    if (!defer) issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
+
     // ---- batch prologue: block ids (into LDS) and query rows (into
-    // registers) are all requested before anything waits on them.
-    const int plane = pt & 63;
+    // registers) are all requested before anything waits on them
     uint32_t raw[QR];
     int idv[IDR];
 #pragma unroll
@@ -1072,25 +1088,28 @@ void decode_kernel(DecodeParams p) {
         raw[i] = load_qrow<D>(p.q + ((int64_t)b * p.hq + h * G + g) * D, plane);
       }
     }
-    // the wave's first tile goes out now, its block ids read from the table
-    // itself (scalar loads), so its data is on the way while the block ids
-    // and query rows above come back and the query pieces are made
-    Cursor cur;
-    cur.ls = 0;
-    cur.li = 0;
-    cur.nseg = nseg;
-    cursor_seek(cur, sm, wave);
-    TileInfo ta;
-    if (cur.ls < nseg) {
-      const int b0 = __builtin_amdgcn_readfirstlane(sm.seg[cur.ls].b);
-      const int32_t* trow = p.tables + (int64_t)(p.headwise ? b0 * hkv + cur.h : b0) * p.max_blocks;
-      ta = tile_info<CB>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te, cur.L, cur.start, bl,
-                         hkv, cur.h);
-    } else {
-      ta = cursor_info<CB>(cur, sm, wave, bl, hkv);
+
+    // ---- fused step: the new token of every pair whose last tile is in
+    // this batch is quantized and stored (K and V rows, one lane group of the
+    // writer wave each), and the writer waits for its stores before the
+    // barrier below, after which the tile holding it may be read.  Only this
+    // workgroup reads that tile, so no other workgroup has to wait for it.
+    if (writer) {
+      constexpr int LPR = D / 8;
+      for (int g0 = 0; g0 < 2 * nseg; g0 += 64 / LPR) {
+        const int grp = g0 + plane / LPR;
+        if (grp < 2 * nseg) {
+          const SegRec& sr = sm.seg[grp >> 1];
+          if (sr.L > 0 && sr.te - 1 == (sr.L - 1) >> 6) {
+            const int64_t slot = p.wp.slot_hw ? p.wp.slot_hw[(int64_t)sr.b * hkv + sr.h] : p.wp.slot[sr.b];
+            write_row<MODE, D, ROT>(p.wp, sr.b, sr.h, grp & 1, slot, plane % LPR);
+          }
+        }
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
-    cursor_next(cur, sm, wave);
-    issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
 
 #pragma unroll
     for (int u = 0; u < IDR; ++u) {
@@ -1098,6 +1117,7 @@ void decode_kernel(DecodeParams p) {
       if (j < ids_used) sm.ids[j] = idv[u];
     }
     __syncthreads();
+    if (defer) issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
 
 #pragma unroll
     for (int i = 0; i < QR; ++i) {
