@@ -47,7 +47,7 @@ MALL_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc")
 # sources that define the decode and prefill kernels (a counter summary is
 # tied to them)
-DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h")]
+DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h", "kvq_write_row.h")]
 PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")]
 
 
