@@ -120,6 +120,34 @@ def test_decode_validation(lib):
         assert _decode(lib, d, ws=None) == _lib.KVQ_EINVAL
 
 
+def _step(lib, d, **kw):
+    P = ctypes.c_void_p(4096)
+    a = dict(out=P, odt=0, q=P, B=2, Hq=8, key=P, value=P, ks=512, vs=512, sm=P, smh=None, kc=P, km=P, vc=P,
+             vm=P, bt=P, bth=None, mb=4, sl=P, msl=200, win=None, scale=0.125, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.kvq_decode_step(ctypes.byref(d), a["out"], a["odt"], a["q"], a["B"], a["Hq"], a["key"], a["value"],
+                               a["ks"], a["vs"], a["sm"], a["smh"], a["kc"], a["km"], a["vc"], a["vm"], a["bt"],
+                               a["bth"], a["mb"], a["sl"], a["msl"], a["win"], a["scale"], a["ws"], a["wsb"], None)
+
+
+def test_decode_step_validation(lib):
+    d = desc(H=4, bs=64)                                           # D 128: token stride >= 512
+    P = ctypes.c_void_p(4096)
+    assert _step(lib, d, sm=None, smh=None) == _lib.KVQ_EINVAL      # no slot mapping
+    assert "slot_mapping" in lib.kvq_last_error().decode()
+    assert _step(lib, d, sm=P, smh=P) == _lib.KVQ_EINVAL            # both slot mappings
+    assert _step(lib, d, key=None) == _lib.KVQ_EINVAL
+    assert _step(lib, d, ks=100) == _lib.KVQ_EINVAL                 # stride below Hkv*D
+    assert "stride" in lib.kvq_last_error().decode()
+    assert _step(lib, d, vs=516) == _lib.KVQ_EINVAL                 # stride not a multiple of 8
+    assert _step(lib, d, value=ctypes.c_void_p(4098)) == _lib.KVQ_EINVAL   # misaligned
+    assert _step(lib, d, Hq=6) == _lib.KVQ_EINVAL                   # decode checks apply too
+    assert _step(lib, d, bt=None, bth=None) == _lib.KVQ_EINVAL
+    assert _step(lib, d, kc=None) == _lib.KVQ_EINVAL
+    assert _step(lib, d, wsb=16) == _lib.KVQ_ENOSPACE
+    assert _step(lib, d, B=0, sm=None, key=None) == _lib.KVQ_OK     # nothing to do
+
+
 def _prefill(lib, d, **kw):
     P = ctypes.c_void_p(4096)
     a = dict(out=P, odt=0, q=P, cu=P, B=2, Hq=8, mq=64, kc=P, km=P, vc=P, vm=P, bt=P, bth=None, mb=4, sl=P,
