@@ -21,7 +21,7 @@ stream it runs on, divided by ``steps``; its algorithmic bytes add the new
 tokens' write (bf16 rows read, codes + meta + slots).  ``decode_only`` is
 kvq_paged_decode_attention timed the same way, ``write.step_write_us`` the
 step's write alone.  ``write`` also reports quantize-write tokens/s on a
-whole-cache fill.  ``cpu_baseline`` times the oracle on a bounded sample.
+whole-cache fill, ``gather`` the dequantize-gather of the whole cache.  ``cpu_baseline`` times the oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -49,6 +49,7 @@ CSRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc")
 # tied to them)
 DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h", "kvq_write_row.h")]
 PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")]
+GATHER_SRC = [os.path.join(CSRC, f) for f in ("kvq_gather.hip", "kvq_device.h", "kvq_internal.h")]
 
 
 def sha(paths):
@@ -130,6 +131,57 @@ def write_bytes_per_token(spec):
     M = 1 if spec.mode == 0 else 2
     slot = 8 * (spec.Hkv if spec.headwise else 1)
     return spec.Hkv * 2 * (spec.D * 2 + P + 4 * M) + slot
+
+
+def gather_bytes(spec, case):
+    """Algorithmic bytes of a whole-cache dequantize-gather: per (position,
+    kv head) row of K and of V, the packed codes and fp32 meta read (rows in
+    present blocks) and the bf16 row written; plus the block-table entries and
+    cu_seq_lens read."""
+    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
+    M = 1 if spec.mode == 0 else 2
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    present = 0
+    entries = 0
+    for b, L in enumerate(lens):
+        nblk = -(-int(L) // spec.bs)
+        for h in range(spec.Hkv):
+            if case.block_tables_headwise is not None:
+                row = case.tables.block_tables_headwise[b * spec.Hkv + h, :nblk]
+            else:
+                row = case.tables.block_tables[b, :nblk]
+            pos_ok = np.repeat(row >= 0, spec.bs)[:L]
+            present += int(pos_ok.sum())
+            entries += nblk
+    rows = int(lens.sum()) * spec.Hkv
+    return 2 * present * (P + 4 * M) + 2 * rows * 2 * spec.D + 4 * entries + 4 * (len(lens) + 1)
+
+
+def gather_cpu(spec, case, planes, lens, seconds):
+    """The oracle's gather on the host cores: (sequence, kv head) pairs until
+    ~`seconds` have passed, as bytes of the same accounting per second."""
+    import oracle
+    pl = [p.cpu().numpy() for p in planes]
+    signs = None if case.rot_signs is None else case.rot_signs.cpu().numpy()
+    bt = case.tables.block_tables
+    bth = case.tables.block_tables_headwise
+    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
+    M = 1 if spec.mode == 0 else 2
+    done, nbytes = 0, 0
+    t0 = time.perf_counter()
+    for b in range(spec.B):
+        for h in range(spec.Hkv):
+            oracle.gather_head(b, h, int(lens[b]), spec.mode, spec.D, spec.bs, spec.Hkv, *pl, signs=signs,
+                               block_tables=bt, block_tables_headwise=bth)
+            done += 1
+            nbytes += 2 * int(lens[b]) * (P + 4 * M + 2 * spec.D)
+            if time.perf_counter() - t0 > seconds:
+                break
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"GBps": round(nbytes / dt / 1e9, 4), "sample": f"{done} of {spec.B * spec.Hkv} (sequence, kv head) "
+            f"pairs in {dt:.1f} s", "cores": int(torch.get_num_threads()), "kind": "oracle"}
 
 
 def build_workload(spec, dev):
@@ -358,6 +410,26 @@ def run_mixed(args, spec, dev):
     wb = write_bytes_per_token(spec)
     p_tf = flops / (p_ms * 1e-3) / 1e12
     d_gbs = d_algo / (d_ms * 1e-3) / 1e9
+    # dequantize-gather of the whole cache (every sequence, positions 0 ..
+    # L - 1, bf16 rows [T, Hkv, D] for K and for V), cycling the replicas
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    cu_np = np.concatenate([[0], np.cumsum(lens)])
+    cu = torch.as_tensor(cu_np.astype(np.int32), device=dev)
+    g_tot = int(cu_np[-1])
+    g_out = [torch.empty((g_tot, spec.Hkv, spec.D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+
+    def gather(i):
+        kvq.kvq_gather_dequant(d, *replicas[i % R], cu, max_len, g_tot, block_tables=case.block_tables,
+                               block_tables_headwise=case.block_tables_headwise,
+                               key_out=g_out[0], value_out=g_out[1])
+
+    gather(0)
+    g_ms = time_events(gather, 5)
+    g_avg = float(np.mean(g_ms))
+    g_bytes = gather_bytes(spec, case)
+    g_cpu = None if args.no_cpu_baseline else gather_cpu(spec, case, planes, lens, 3.0)
+    del g_out
+
     result = {
         "metric": "decode-attn effective KV GB/s (% HBM peak); quantize-write tokens/s",
         "value": round(d_gbs, 2),
@@ -525,6 +597,26 @@ def main():
     fill_ms = time_events(fill, 5)
     fill_avg = float(np.mean(fill_ms))
 
+    # dequantize-gather of the whole cache (every sequence, positions 0 ..
+    # L - 1, bf16 rows [T, Hkv, D] for K and for V), cycling the replicas
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    cu_np = np.concatenate([[0], np.cumsum(lens)])
+    cu = torch.as_tensor(cu_np.astype(np.int32), device=dev)
+    g_tot = int(cu_np[-1])
+    g_out = [torch.empty((g_tot, spec.Hkv, spec.D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+
+    def gather(i):
+        kvq.kvq_gather_dequant(d, *replicas[i % R], cu, max_len, g_tot, block_tables=case.block_tables,
+                               block_tables_headwise=case.block_tables_headwise,
+                               key_out=g_out[0], value_out=g_out[1])
+
+    gather(0)
+    g_ms = time_events(gather, 5)
+    g_avg = float(np.mean(g_ms))
+    g_bytes = gather_bytes(spec, case)
+    g_cpu = None if args.no_cpu_baseline else gather_cpu(spec, case, planes, lens, 3.0)
+    del g_out
+
     result = {
         "metric": "decode-attn effective KV GB/s (% HBM peak); quantize-write tokens/s",
         "value": round(algo / (ms_step * 1e-3) / 1e9, 2),
@@ -560,6 +652,12 @@ def main():
                   "tokens_per_s": round(T / (fill_avg * 1e-3), 1),
                   "bytes_per_token": wb, "GBps": round(T * wb / (fill_avg * 1e-3) / 1e9, 2),
                   "frac": round(T * wb / (fill_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "gather": {"kernel": "gather_kernel (dequantize-gather, bf16 out)", "rows": int(g_tot) * spec.Hkv * 2,
+                   "avg_launch_us": round(g_avg * 1e3, 2), "algorithmic_bytes_per_launch": int(g_bytes),
+                   "GBps": round(g_bytes / (g_avg * 1e-3) / 1e9, 2),
+                   "frac": round(g_bytes / (g_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "traffic": load_traffic(f"gather_{spec.name}_counters.json", GATHER_SRC),
+                   "cpu_oracle": g_cpu},
         "setup_s": round(setup_s, 1),
     }
     if not args.no_cpu_baseline:

@@ -257,6 +257,36 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc,
                                        float softmax_scale,
                                        void* stream);
 
+/* Dequantize-gather (the cache-fetch-and-dequantize operator of FastDeploy
+ * PR 5173, review thread; the gather-and-dequantize of the paged cache that
+ * prefill uses in the vllm-ascend-quantized-kv-cache package, 运行机制).
+ * Sequence b's positions j = 0 .. n_b - 1, n_b = cu_seq_lens[b+1] -
+ * cu_seq_lens[b], are written to row cu_seq_lens[b] + j of key_out and
+ * value_out: for every kv head h the dequantized row x_hat = c*s (+ z) of the
+ * block the table gives, rotated back (R^T x_hat) when the cache has a
+ * rotation.  A position in an evicted (-1) block gives a zero row.
+ *   key_out, value_out (device) [total_tokens, Hkv, D] float32 (KVQ_OUT_F32)
+ *                or bf16 (KVQ_OUT_BF16, round to nearest even), 16-byte aligned
+ *   block_tables / block_tables_headwise, max_blocks_per_seq: as for
+ *                kvq_paged_decode_attention (exactly one non-NULL)
+ *   cu_seq_lens  (device) int32 [num_seqs + 1], non-decreasing from 0,
+ *                cu_seq_lens[num_seqs] <= total_tokens, every n_b <= max_seq_len
+ *   max_seq_len  host upper bound on every n_b (sizes the grid: positions at
+ *                or past it are not written), <= max_blocks_per_seq*block_size
+ * Rows past total_tokens are never written.  No workspace; one kernel launch.
+ * The outputs must not overlap the cache planes. */
+kvq_status kvq_gather_dequant(const kvq_cache_desc* desc,
+                              void* key_out, void* value_out, int32_t out_dtype,
+                              const uint8_t* k_codes, const float* k_meta,
+                              const uint8_t* v_codes, const float* v_meta,
+                              const int32_t* block_tables,
+                              const int32_t* block_tables_headwise,
+                              int32_t max_blocks_per_seq,
+                              const int32_t* cu_seq_lens,
+                              int32_t num_seqs, int32_t total_tokens,
+                              int32_t max_seq_len,
+                              void* stream);
+
 /* Thread-local message for the last non-OK status ("" if none). */
 const char* kvq_last_error(void);
 

@@ -325,6 +325,33 @@ def gather_head(b: int, h: int, n_pos: int, mode: int, head_dim: int,
     return K, V, present
 
 
+def gather_dequant(cu_seq_lens, mode: int, head_dim: int, block_size: int,
+                   num_kv_heads: int, k_codes, k_meta, v_codes, v_meta, signs=None,
+                   block_tables=None, block_tables_headwise=None):
+    """Dequantize-gather: the custom op that fetches K/V out of the quantized
+    cache and dequantizes them ([P1] review thread, the cache-fetch operator
+    with its composed-op test version; [P4] 运行机制: prefill gathers and
+    dequantizes the paged cache when it needs dense K/V).
+
+    Sequence b's positions 0 .. n_b - 1, n_b = cu_seq_lens[b+1] -
+    cu_seq_lens[b], become rows cu_seq_lens[b] .. cu_seq_lens[b+1] - 1 of the
+    float64 outputs K, V [cu_seq_lens[-1], Hkv, D], dequantized and
+    un-rotated.  Positions in an evicted (-1) block are zero rows."""
+    cu = np.asarray(cu_seq_lens, np.int64)
+    n_tok = int(cu[-1])
+    K = np.zeros((n_tok, num_kv_heads, head_dim))
+    V = np.zeros((n_tok, num_kv_heads, head_dim))
+    for b in range(len(cu) - 1):
+        n = int(cu[b + 1] - cu[b])
+        for h in range(num_kv_heads):
+            Kb, Vb, _ = gather_head(b, h, n, mode, head_dim, block_size, num_kv_heads,
+                                    k_codes, k_meta, v_codes, v_meta, signs,
+                                    block_tables, block_tables_headwise)
+            K[cu[b]:cu[b + 1], h] = Kb
+            V[cu[b]:cu[b + 1], h] = Vb
+    return K, V
+
+
 def _attend(qs: np.ndarray, K: np.ndarray, V: np.ndarray, allowed: np.ndarray,
             scale: float) -> np.ndarray:
     """Plain softmax attention in float64.  qs [n, D]; allowed [n, Lk] bool.

@@ -46,6 +46,7 @@ SIGNATURES = {
                                _P, _P, _I32, _P, _I32, _P, ctypes.c_float, _P, _SZ, _P]),
     "kvq_paged_prefill_attention": (_I32, [_DESC, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                            _I32, _P, _I32, _P, ctypes.c_float, _P]),
+    "kvq_gather_dequant": (_I32, [_DESC, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _P]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_version": (_I32, []),
 }

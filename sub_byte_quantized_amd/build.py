@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_host.cpp", "kvq_write.hip", "kvq_decode.hip", "kvq_prefill.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_write.hip", "kvq_decode.hip", "kvq_prefill.hip", "kvq_gather.hip"]
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 

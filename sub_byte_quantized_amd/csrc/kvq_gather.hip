@@ -1,0 +1,189 @@
+// Dequantize-gather: materialize the un-rotated K and V of given sequences
+// out of the quantized paged cache, as dense [token, kv head, D] rows.
+//
+// The operation is the cache-fetch-and-dequantize custom operator named in the
+// review thread of FastDeploy PR 5173 ("[Feature] support dynamic int2
+// quantization cache kv"), and the gather-and-dequantize that prefill applies
+// to the paged cache in the vllm-ascend-quantized-kv-cache package (运行机制).
+// Per row (position j of sequence b, kv head h, K or V):
+//   x_hat = c*s (+ z)             float32, product then sum (no contraction)
+//   out   = R^T x_hat = (1/sqrt(D)) d .* (H x_hat)   when the cache is rotated
+// with the block id read from the uniform table row b or the head-wise row
+// b*Hkv + h; a -1 entry (an evicted sliding-window block, FastDeploy PR 7718)
+// gives a zero row and no cache address is formed.
+//
+// Work split: HBM streaming.  D/8 lanes own a row, 8 elements per lane: the
+// lane's packed bytes (8 INT8, 4 INT4, 2 INT2) and the row's meta in one load
+// each, 16 (bf16) or 32 (float32) bytes stored.  A 256-thread workgroup takes
+// ITER groups of 16 (D 128) or 32 (D 64) consecutive rows of one sequence, in
+// (position, kv head, K/V) order, and issues all its loads before the first
+// use.  grid.y is the sequence; grid.x covers max_seq_len positions.
+#pragma clang fp contract(off)
+
+#include "kvq_internal.h"
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kGatherIter = 4;
+
+template <int MODE, int D, bool ROT, bool BF16>
+__global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
+  constexpr int LPR = D / 8;                    // lanes per row
+  constexpr int RPW = 64 / LPR;                 // rows per wave
+  constexpr int RPB = 4 * RPW;                  // rows per workgroup and iteration
+  constexpr int P = row_bytes(MODE, D);
+  constexpr int M = mode_meta(MODE);
+  constexpr int BPL = P / LPR;                  // packed bytes per lane
+
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & (LPR - 1);
+  const int hkv = p.hkv;
+  const int c0 = p.cu[b];
+  const int n = min(p.cu[b + 1] - c0, p.max_blocks << p.block_size_log2);
+  const int64_t rows = (int64_t)n * hkv * 2;
+  const int64_t r0 = (int64_t)blockIdx.x * RPB * kGatherIter + (threadIdx.x >> 6) * RPW + lane / LPR;
+  if (r0 >= rows) return;
+
+  uint32_t raw[kGatherIter][BPL >= 4 ? BPL / 4 : 1];
+  float s[kGatherIter], z[kGatherIter];
+  bool present[kGatherIter];
+  int64_t orow[kGatherIter];
+  int hh[kGatherIter], kvs[kGatherIter];
+#pragma unroll
+  for (int it = 0; it < kGatherIter; ++it) {
+    const int64_t r = r0 + (int64_t)it * RPB;
+    const bool in = r < rows;
+    const int pos = (int)(r / (2 * hkv));
+    const int rem = (int)(r - (int64_t)pos * 2 * hkv);
+    const int h = rem >> 1, kv = rem & 1;
+    hh[it] = h;
+    kvs[it] = kv;
+    orow[it] = in ? (int64_t)c0 + pos : -1;
+    int id = -1;
+    if (in) {
+      const int32_t* trow = p.tables + (int64_t)(p.headwise ? b * hkv + h : b) * p.max_blocks;
+      id = trow[pos >> p.block_size_log2];
+    }
+    present[it] = in && id >= 0 && id < p.num_blocks && orow[it] < p.total_tokens;
+    const int64_t src = present[it]
+                            ? (((int64_t)id * hkv + h) << p.block_size_log2) + (pos & ((1 << p.block_size_log2) - 1))
+                            : 0;
+    const uint8_t* codes = (kv ? p.v_codes : p.k_codes) + src * P + lr * BPL;
+    const float* meta = (kv ? p.v_meta : p.k_meta) + src * M;
+    if (present[it]) {
+      load_bytes<BPL>(raw[it], codes);
+      if constexpr (M == 2) {
+        const float2 sz = *reinterpret_cast<const float2*>(meta);
+        s[it] = sz.x;
+        z[it] = sz.y;
+      } else {
+        s[it] = meta[0];
+        z[it] = 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < (BPL >= 4 ? BPL / 4 : 1); ++w) raw[it][w] = 0;
+      s[it] = 0.0f;
+      z[it] = 0.0f;
+    }
+  }
+
+#pragma unroll
+  for (int it = 0; it < kGatherIter; ++it) {
+    if (orow[it] < 0 || orow[it] >= p.total_tokens) continue;
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int c;
+      if constexpr (MODE == 0) c = (int)(int8_t)((raw[it][i >> 2] >> (8 * (i & 3))) & 0xffu);
+      else if constexpr (MODE == 1) c = (int)((raw[it][0] >> (4 * i)) & 0xFu);
+      else c = (int)((raw[it][0] >> (2 * i)) & 0x3u);
+      const float cs = (float)c * s[it];
+      x[i] = M == 2 ? cs + z[it] : cs;
+    }
+    if (!present[it]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+    }
+    if constexpr (ROT) {
+      // H x: in-lane butterflies (element strides 1, 2, 4), then across the
+      // row's lanes (element stride 8m lives m lanes away)
+#pragma unroll
+      for (int hs = 1; hs < 8; hs <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (!(i & hs)) {
+            const float a = x[i], c = x[i + hs];
+            x[i] = a + c;
+            x[i + hs] = a - c;
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < LPR; m <<= 1) {
+        const bool upper = (lr & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float o = __shfl_xor(x[i], m);
+          x[i] = upper ? (o - x[i]) : (x[i] + o);
+        }
+      }
+      const float4 s0 = *reinterpret_cast<const float4*>(p.signs + lr * 8);
+      const float4 s1 = *reinterpret_cast<const float4*>(p.signs + lr * 8 + 4);
+      const float sg[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = x[i] * sg[i] * p.inv_sqrt_d;
+    }
+    const int64_t e0 = (orow[it] * hkv + hh[it]) * D + lr * 8;
+    void* out = kvs[it] ? p.v_out : p.k_out;
+    if constexpr (BF16) {
+      uint4 w;
+      w.x = pack_bf16(x[0], x[1]);
+      w.y = pack_bf16(x[2], x[3]);
+      w.z = pack_bf16(x[4], x[5]);
+      w.w = pack_bf16(x[6], x[7]);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) = w;
+    } else {
+      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
+      o[0] = make_float4(x[0], x[1], x[2], x[3]);
+      o[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+  }
+}
+
+template <int MODE, int D, bool ROT>
+hipError_t launch_gather_t(const GatherParams& p, hipStream_t s) {
+  constexpr int RPB = 4 * (64 / (D / 8)) * kGatherIter;
+  const int64_t rows = (int64_t)p.max_seq_len * p.hkv * 2;
+  const int64_t gx = (rows + RPB - 1) / RPB;
+  if (gx == 0 || p.num_seqs == 0) return hipSuccess;
+  const dim3 grid((unsigned)gx, (unsigned)p.num_seqs);
+  if (p.out_bf16)
+    hipLaunchKernelGGL((gather_kernel<MODE, D, ROT, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((gather_kernel<MODE, D, ROT, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_gather_m(int d, bool rot, const GatherParams& p, hipStream_t s) {
+  if (d == 64) return rot ? launch_gather_t<MODE, 64, true>(p, s) : launch_gather_t<MODE, 64, false>(p, s);
+  return rot ? launch_gather_t<MODE, 128, true>(p, s) : launch_gather_t<MODE, 128, false>(p, s);
+}
+
+}  // namespace
+
+int64_t gather_rows_per_workgroup(int d) { return 4LL * (64 / (d / 8)) * kGatherIter; }
+
+hipError_t launch_gather(int mode, int d, bool rot, const GatherParams& p, hipStream_t s) {
+  switch (mode) {
+    case 0: return launch_gather_m<0>(d, rot, p, s);
+    case 1: return launch_gather_m<1>(d, rot, p, s);
+    default: return launch_gather_m<2>(d, rot, p, s);
+  }
+}
+
+}  // namespace kvq

@@ -413,6 +413,64 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
   return ok();
 }
 
+kvq_status kvq_gather_dequant(const kvq_cache_desc* desc, void* key_out, void* value_out, int32_t out_dtype,
+                              const uint8_t* k_codes, const float* k_meta, const uint8_t* v_codes,
+                              const float* v_meta, const int32_t* block_tables,
+                              const int32_t* block_tables_headwise, int32_t max_blocks_per_seq,
+                              const int32_t* cu_seq_lens, int32_t num_seqs, int32_t total_tokens,
+                              int32_t max_seq_len, void* stream) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (num_seqs < 0) return fail(KVQ_EINVAL, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > 65535) return fail(KVQ_EUNSUPPORTED, "num_seqs %d > 65535", num_seqs);
+  if (total_tokens < 0) return fail(KVQ_EINVAL, "total_tokens %d < 0", total_tokens);
+  if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len %d < 0", max_seq_len);
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16)
+    return fail(KVQ_EINVAL, "out_dtype %d is not a kvq_out_dtype", out_dtype);
+  if ((block_tables == nullptr) == (block_tables_headwise == nullptr))
+    return fail(KVQ_EINVAL, "exactly one of block_tables and block_tables_headwise must be non-NULL");
+  if (max_blocks_per_seq < 1) return fail(KVQ_EINVAL, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * desc->block_size)
+    return fail(KVQ_EINVAL, "max_seq_len %d exceeds max_blocks_per_seq*block_size = %lld", max_seq_len,
+                (long long)max_blocks_per_seq * desc->block_size);
+  const long long gx = ((long long)max_seq_len * desc->num_kv_heads * 2 +
+                        kvq::gather_rows_per_workgroup(desc->head_dim) - 1) /
+                       kvq::gather_rows_per_workgroup(desc->head_dim);
+  if (gx > 0x7fffffffLL) return fail(KVQ_EUNSUPPORTED, "gather grid of %lld workgroups per sequence", gx);
+  if ((long long)total_tokens * desc->num_kv_heads * desc->head_dim > (1LL << 40))
+    return fail(KVQ_EUNSUPPORTED, "outputs of %lld rows are too large", (long long)total_tokens);
+  if (num_seqs == 0 || total_tokens == 0 || max_seq_len == 0) return ok();
+  if (!key_out || !value_out || !cu_seq_lens) return fail(KVQ_EINVAL, "key_out, value_out or cu_seq_lens is NULL");
+  if (!aligned(key_out, 16) || !aligned(value_out, 16))
+    return fail(KVQ_EINVAL, "key_out and value_out must be 16-byte aligned");
+  st = check_planes(k_codes, k_meta, v_codes, v_meta);
+  if (st != KVQ_OK) return st;
+  kvq::GatherParams p{};
+  p.k_codes = k_codes;
+  p.k_meta = k_meta;
+  p.v_codes = v_codes;
+  p.v_meta = v_meta;
+  p.k_out = key_out;
+  p.v_out = value_out;
+  p.headwise = block_tables_headwise != nullptr;
+  p.tables = p.headwise ? block_tables_headwise : block_tables;
+  p.cu = cu_seq_lens;
+  p.signs = desc->rot_signs;
+  p.num_blocks = desc->num_blocks;
+  p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
+  p.max_blocks = max_blocks_per_seq;
+  p.block_size_log2 = __builtin_ctz((unsigned)desc->block_size);
+  p.hkv = desc->num_kv_heads;
+  p.num_seqs = num_seqs;
+  p.max_seq_len = max_seq_len;
+  p.total_tokens = total_tokens;
+  p.out_bf16 = out_dtype == KVQ_OUT_BF16;
+  hipError_t e = kvq::launch_gather(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_EHIP, "gather launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* kvq_last_error(void) { return g_err; }
 
 int32_t kvq_version(void) { return 100; }

@@ -100,7 +100,32 @@ struct PrefillParams {
   int32_t out_bf16;
 };
 
+struct GatherParams {
+  const uint8_t* k_codes;
+  const float* k_meta;
+  const uint8_t* v_codes;
+  const float* v_meta;
+  void* k_out;                  // [total_tokens, Hkv, D] float32 or bf16
+  void* v_out;
+  const int32_t* tables;        // [B, max_blocks] or [B*Hkv, max_blocks]
+  const int32_t* cu;            // [B + 1] output row offsets
+  const float* signs;           // [D] or nullptr
+  int64_t num_blocks;
+  float inv_sqrt_d;
+  int32_t headwise;
+  int32_t max_blocks;
+  int32_t block_size_log2;
+  int32_t hkv;
+  int32_t num_seqs;
+  int32_t max_seq_len;          // positions the grid covers per sequence
+  int32_t total_tokens;         // rows of the outputs
+  int32_t out_bf16;
+};
+
 hipError_t launch_write(int mode, int d, bool rot, const WriteParams& p, hipStream_t s);
+hipError_t launch_gather(int mode, int d, bool rot, const GatherParams& p, hipStream_t s);
+// Rows one dequantize-gather workgroup covers (grid.x = ceil(rows / this)).
+int64_t gather_rows_per_workgroup(int d);
 // Resident decode workgroups per CU for this variant (its waves per SIMD).
 int decode_wgs_per_cu(int mode, int d, int group);
 hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, hipStream_t s);

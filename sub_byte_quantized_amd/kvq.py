@@ -281,3 +281,44 @@ def kvq_paged_prefill_attention(desc: CacheDesc, query: torch.Tensor, cu_seqlens
         _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
         _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale), _stream(dev)))
     return out
+
+
+def kvq_gather_dequant(desc: CacheDesc, k_codes: torch.Tensor, k_meta: torch.Tensor,
+                       v_codes: torch.Tensor, v_meta: torch.Tensor,
+                       cu_seq_lens: torch.Tensor, max_seq_len: int, total_tokens: int,
+                       block_tables: Optional[torch.Tensor] = None,
+                       block_tables_headwise: Optional[torch.Tensor] = None,
+                       key_out: Optional[torch.Tensor] = None,
+                       value_out: Optional[torch.Tensor] = None,
+                       out_dtype: torch.dtype = torch.bfloat16):
+    """Dequantized, un-rotated K and V [total_tokens, Hkv, D] of the
+    sequences' positions 0 .. n_b - 1 (n_b = cu_seq_lens[b+1] -
+    cu_seq_lens[b]) at rows cu_seq_lens[b] ..; evicted positions are zero.
+    Returns (key_out, value_out)."""
+    dev = k_codes.device
+    _need(cu_seq_lens, "cu_seq_lens", torch.int32, dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(block_tables_headwise, "block_tables_headwise", torch.int32, dev)
+    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (v_codes, "v_codes", torch.uint8),
+                     (k_meta, "k_meta", torch.float32), (v_meta, "v_meta", torch.float32)):
+        _need(t, n, dt, dev)
+    shape = (int(total_tokens), desc.num_kv_heads, desc.head_dim)
+    if key_out is None:
+        key_out = torch.empty(shape, dtype=out_dtype, device=dev)
+    if value_out is None:
+        value_out = torch.empty(shape, dtype=key_out.dtype, device=dev)
+    for t, n in ((key_out, "key_out"), (value_out, "value_out")):
+        _need(t, n, key_out.dtype, dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{n} must be {shape}, got {tuple(t.shape)}")
+    odt = {torch.float32: KVQ_OUT_F32, torch.bfloat16: KVQ_OUT_BF16}[key_out.dtype]
+    tab = block_tables if block_tables is not None else block_tables_headwise
+    max_blocks = int(tab.shape[1]) if tab is not None else 0
+    B = int(cu_seq_lens.shape[0]) - 1
+    d = desc.c()
+    _check(_lib.load().kvq_gather_dequant(
+        ctypes.byref(d), _ptr(key_out), _ptr(value_out), odt,
+        _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
+        _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
+        _ptr(cu_seq_lens), B, int(total_tokens), int(max_seq_len), _stream(dev)))
+    return key_out, value_out

@@ -260,6 +260,71 @@ def check_gather_matches_dense(o):
                 assert np.allclose(got, xh @ R, atol=1e-12)
 
 
+def _grid_rows(mode, n, D, seed):
+    """Rows x = c*s + z whose quantization is exact: s a power of two, z
+    bf16-exact, codes drawn in [lo, L] with both ends present in every row, so
+    the row's min/max (or absmax) give back s and z, 1/s is exact, and every
+    code and x_hat = c*s + z come back without rounding.  Returns (x float32
+    [n, D], codes int [n, D])."""
+    r = np.random.default_rng(seed)
+    L = {0: 127, 1: 15, 2: 3}[mode]
+    lo = -L if mode == 0 else 0
+    c = r.integers(lo, L + 1, (n, D))
+    c[:, 0] = L
+    c[:, 1] = lo
+    s = 2.0 ** -r.integers(2, 6, (n, 1))
+    z = 0.0 if mode == 0 else r.choice([-1.5, -0.75, 0.25, 1.0], (n, 1))
+    return (c * s + z).astype(F32), c
+
+
+def check_gather_dequant_grid(o):
+    """Dequantize-gather of rows whose quantization is exact returns them bit
+    for bit at rows cu[b] + j (shuffled table, a zero-length sequence, every
+    mode); an evicted block gives zero rows and leaves the rest; with a
+    rotation the result is the dense float64 R^T of the rotated-space gather."""
+    D, bs, Hkv = 64, 16, 3
+    lens = np.array([21, 0, 40])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    nblk = [(L + bs - 1) // bs for L in lens]
+    nb = sum(nblk) + 2
+    perm = np.random.default_rng(11).permutation(nb)
+    bt = np.full((len(lens), max(nblk)), -1, np.int64)
+    k0 = 0
+    for b, n in enumerate(nblk):
+        bt[b, :n] = perm[k0:k0 + n]
+        k0 += n
+    tok_seq = np.repeat(np.arange(len(lens)), lens)
+    tok_pos = np.concatenate([np.arange(L) for L in lens])
+    slots = bt[tok_seq, tok_pos // bs] * bs + tok_pos % bs
+    T = int(lens.sum())
+    for mode in MODES:
+        xk, _ = _grid_rows(mode, T * Hkv, D, 20 + mode)
+        xv, _ = _grid_rows(mode, T * Hkv, D, 30 + mode)
+        k, v = xk.reshape(T, Hkv, D), xv.reshape(T, Hkv, D)
+        cs, ms = o.plane_shapes(mode, D, Hkv, bs, nb)
+        planes = [np.full(cs, 0xFF, np.uint8), np.full(ms, np.nan, F32),
+                  np.full(cs, 0xFF, np.uint8), np.full(ms, np.nan, F32)]
+        o.write_cache(k, v, mode, bs, *planes, slot_mapping=slots)
+        K, V = o.gather_dequant(cu, mode, D, bs, Hkv, *planes, block_tables=bt)
+        assert K.shape == (T, Hkv, D)
+        assert np.array_equal(K, k.astype(np.float64)) and np.array_equal(V, v.astype(np.float64)), mode
+        # evict block 1 of sequence 2: its 16 positions read as zero rows
+        ev = bt.copy()
+        ev[2, 1] = -1
+        Ke, Ve = o.gather_dequant(cu, mode, D, bs, Hkv, *planes, block_tables=ev)
+        gone = np.zeros(T, bool)
+        gone[cu[2] + bs:cu[2] + 2 * bs] = True
+        assert np.all(Ke[gone] == 0) and np.all(Ve[gone] == 0)
+        assert np.array_equal(Ke[~gone], K[~gone]) and np.array_equal(Ve[~gone], V[~gone])
+        # head-wise rows equal to the uniform row: same result
+        Kh, _ = o.gather_dequant(cu, mode, D, bs, Hkv, *planes, block_tables_headwise=np.repeat(bt, Hkv, axis=0))
+        assert np.array_equal(Kh, K)
+    signs = np.where(np.random.default_rng(12).integers(0, 2, D) == 1, 1.0, -1.0).astype(F32)
+    R = scipy.linalg.hadamard(D) * signs.astype(float)[None, :] / math.sqrt(D)
+    Kr, Vr = o.gather_dequant(cu, mode, D, bs, Hkv, *planes, signs=signs, block_tables=bt)
+    assert np.allclose(Kr, K @ R, atol=1e-12) and np.allclose(Vr, V @ R, atol=1e-12)
+
+
 # --------------------------------------------------------------- attention ---
 def _sdpa64(q, K, V, mask, scale):
     qt = torch.as_tensor(q, dtype=torch.float64)[None, None]

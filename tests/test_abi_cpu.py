@@ -34,7 +34,7 @@ def test_header_lists_entry_points():
     names = header_functions()
     for n in ("kvq_query_layout", "kvq_reshape_and_cache", "kvq_paged_decode_attention",
               "kvq_decode_workspace_size", "kvq_workspace_init", "kvq_paged_prefill_attention",
-              "kvq_decode_step", "kvq_last_error"):
+              "kvq_decode_step", "kvq_gather_dequant", "kvq_last_error"):
         assert n in names
 
 
@@ -197,3 +197,34 @@ def test_workspace_init_validation(lib):
 
 def test_version(lib):
     assert lib.kvq_version() >= 100
+
+
+def _gather(lib, d, **kw):
+    P = ctypes.c_void_p(4096)
+    a = dict(ko=P, vo=P, odt=1, kc=P, km=P, vc=P, vm=P, bt=P, bth=None, mb=4, cu=P, B=2, tot=300, msl=200)
+    a.update(kw)
+    return lib.kvq_gather_dequant(ctypes.byref(d), a["ko"], a["vo"], a["odt"], a["kc"], a["km"], a["vc"], a["vm"],
+                                  a["bt"], a["bth"], a["mb"], a["cu"], a["B"], a["tot"], a["msl"], None)
+
+
+def test_gather_validation(lib):
+    d = desc(H=4, bs=64)
+    P = ctypes.c_void_p(4096)
+    assert _gather(lib, d, bt=None, bth=None) == _lib.KVQ_EINVAL     # no table
+    assert "exactly one" in lib.kvq_last_error().decode()
+    assert _gather(lib, d, bt=P, bth=P) == _lib.KVQ_EINVAL           # both tables
+    assert _gather(lib, d, msl=4 * 64 + 1) == _lib.KVQ_EINVAL        # beyond the table
+    assert _gather(lib, d, odt=3) == _lib.KVQ_EINVAL
+    assert _gather(lib, d, ko=None) == _lib.KVQ_EINVAL
+    assert _gather(lib, d, cu=None) == _lib.KVQ_EINVAL
+    assert _gather(lib, d, km=None) == _lib.KVQ_EINVAL
+    assert _gather(lib, d, vo=ctypes.c_void_p(4100)) == _lib.KVQ_EINVAL   # misaligned
+    assert _gather(lib, d, B=-1) == _lib.KVQ_EINVAL
+    assert _gather(lib, d, B=70000) == _lib.KVQ_EUNSUPPORTED
+    assert _gather(lib, d, tot=-5) == _lib.KVQ_EINVAL
+    assert _gather(lib, d, mb=0) == _lib.KVQ_EINVAL
+    assert _gather(lib, desc(D=96)) == _lib.KVQ_EINVAL
+    # nothing to do: OK, nothing launched (no GPU here)
+    assert _gather(lib, d, B=0) == _lib.KVQ_OK
+    assert _gather(lib, d, tot=0, ko=None, vo=None) == _lib.KVQ_OK
+    assert _gather(lib, d, msl=0) == _lib.KVQ_OK

@@ -31,6 +31,8 @@ MUTATIONS = {
     "evicted_read": ("present = ids >= 0", "present = ids >= -1"),
     "headwise_row": ("return np.asarray(block_tables_headwise)[b * num_kv_heads + h]", "return np.asarray(block_tables_headwise)[h * num_kv_heads + b]"),
     "scale_dropped": ("logits = scale * (np.asarray(qs, np.float64) @ K.T)", "logits = np.asarray(qs, np.float64) @ K.T"),
+    "gather_head_index": ("K[cu[b]:cu[b + 1], h] = Kb", "K[cu[b]:cu[b + 1], num_kv_heads - 1 - h] = Kb"),
+    "gather_row_offset": ("n = int(cu[b + 1] - cu[b])", "n = int(cu[b + 1] - cu[b]) - (b > 0)"),
     "slot_offset": ("blk, off = sl // block_size, sl % block_size", "blk, off = sl // block_size, (sl + 1) % block_size"),
 }
 
