@@ -621,7 +621,7 @@ struct Smem {
       float ml[NWV][GM][2];
     } comb;                             // per-wave (m, l, acc) of a segment
     struct {
-      float fin[GM][D];                 // normalized rows before R^T
+      float fin[2][GM][D];              // normalized rows before R^T (up to two pairs)
     } fw;
     float qrow[NWV][D];                 // query prologue scratch, one row per wave
   };
@@ -647,23 +647,10 @@ __device__ __forceinline__ int pair_geo(const DecodeParams& p, int pair, int* t0
 }
 
 // The share partition: workgroup w takes tiles [start(w), start(w + 1)) of
-// the T concatenated tiles.  Workgroups of dispatch round r (ids r*ncu ..
-// r*ncu + ncu - 1, one per CU) start streaming a few microseconds after the
-// rounds before them on the same CU (their prologues queue behind the older
-// waves), so round r's shares are K*r tiles shorter than round 0's, the
-// average kept at T / nw: share_r = T/nw + K (nr - 1)/2 - K r.  Equal shares
-// (K = 0) when nw is not a whole number of rounds or the shares would get
-// short.
+// the T concatenated tiles, equal shares (nw <= T, so none is empty).
 struct Part {
-  int T, nw, ncu, nr, K;
-  __device__ int start(int w) const {
-    if (K == 0) return (int)(((int64_t)T * w) / nw);
-    // 2 nw * (sum of the shares before w), exact in int64
-    const int r = w / ncu;
-    const int64_t c2 = 2LL * w * T +
-                       (int64_t)K * nw * ((int64_t)w * (nr - 1) - (int64_t)ncu * r * (r - 1) - 2LL * (w - r * ncu) * r);
-    return (int)(c2 / (2LL * nw));
-  }
+  int T, nw;
+  __device__ int start(int w) const { return (int)(((int64_t)T * w) / nw); }
   // workgroup whose share holds tile x (0 <= x < T)
   __device__ int owner(int x) const {
     int lo = 0, hi = nw - 1;
@@ -757,50 +744,85 @@ __device__ __forceinline__ float load_dev(const float* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merge the published pieces of one pair (slots slot0 .. slot0 + n - 1),
-// normalize, R^T and store.  All threads.  Each thread folds its (head, d)
-// values over the pieces in slot order with the online-softmax update,
-// requesting eight pieces' (m, l, acc) at a time, so a merge of up to eight
-// pieces waits on memory once.
-template <int D, int PHI, int NWV, bool ROT>
-__device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI, NWV>& sm, int slot0, int n,
-                                             int64_t orow0, int tid) {
+// Merge the published pieces of up to two pairs (pair i: slots s0[i] ..
+// s0[i] + n[i] - 1, output rows o0[i] ..), normalize, R^T and store.  All
+// threads.  Each pass gives every thread U (head, d) values of both pairs;
+// the thread folds each over its pieces in slot order with the online-softmax
+// update, and requests the (m, l, acc) of KP pieces of every value at once,
+// so a pass over pairs of at most KP pieces waits on memory once.
+template <int D, int PHI, int NWV, bool ROT, int KP>
+__device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI, NWV>& sm, int np, int s0a, int na,
+                                             int64_t o0a, int s0b, int nb, int64_t o0b, int tid) {
   constexpr int NT = 64 * NWV;
+  // values per thread and pass: enough to cover the largest group in one
+  // pass where the threads are few, at most two (registers)
+  constexpr int U = (Smem<D, PHI, NWV>::GM * D + NT - 1) / NT >= 2 ? 2 : 1;
   const int G = p.group;
+  const int GD = G * D;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t stride = (int64_t)G * (D + 4);   // floats between consecutive pieces
-  for (int e = tid; e < G * D; e += NT) {
-    const int g = e / D, d = e - g * D;
-    const float* base = p.partials + ((int64_t)slot0 * G + g) * (D + 4);
-    float M = kNegInf, l = 0.0f, v = 0.0f;
-    for (int s = 0; s < n; s += 8) {
-      const int c = min(8, n - s);
-      float pm[8], pl[8], pa[8];
+  const int nmax = max(na, np > 1 ? nb : 0);
+  for (int e0 = 0; e0 < GD; e0 += U * NT) {
+    float M[2][U], l[2][U], v[2][U];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (u < c) {
-          const float* rec = base + (s + u) * stride;
-          pm[u] = load_dev(rec);
-          pl[u] = load_dev(rec + 1);
-          pa[u] = load_dev(rec + 4 + d);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int u = 0; u < U; ++u) { M[i][u] = kNegInf; l[i][u] = 0.0f; v[i][u] = 0.0f; }
+    for (int s = 0; s < nmax; s += KP) {
+      float pm[2][U][KP], pl[2][U][KP], pa[2][U][KP];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int n = i ? nb : na;
+        const int slot0 = i ? s0b : s0a;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = e0 + u * NT + tid;
+          const int g = e / D, d = e - g * D;
+          const float* base = p.partials + ((int64_t)slot0 * G + g) * (D + 4);
+#pragma unroll
+          for (int k = 0; k < KP; ++k) {
+            if (i < np && e < GD && s + k < n) {
+              const float* rec = base + (s + k) * stride;
+              pm[i][u][k] = load_dev(rec);
+              pl[i][u][k] = load_dev(rec + 1);
+              pa[i][u][k] = load_dev(rec + 4 + d);
+            }
+          }
         }
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (u < c) {
-          const float mn = fmaxf(M, pm[u]);
-          const float fo = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - mn);
-          const float fn = pm[u] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(pm[u] - mn);
-          v = v * fo + pa[u] * fn;
-          l = l * fo + pl[u] * fn;
-          M = mn;
+      for (int i = 0; i < 2; ++i) {
+        const int n = i ? nb : na;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = e0 + u * NT + tid;
+#pragma unroll
+          for (int k = 0; k < KP; ++k) {
+            if (i < np && e < GD && s + k < n) {
+              const float mn = fmaxf(M[i][u], pm[i][u][k]);
+              const float fo = M[i][u] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M[i][u] - mn);
+              const float fn = pm[i][u][k] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(pm[i][u][k] - mn);
+              v[i][u] = v[i][u] * fo + pa[i][u][k] * fn;
+              l[i][u] = l[i][u] * fo + pl[i][u][k] * fn;
+              M[i][u] = mn;
+            }
+          }
         }
       }
     }
-    sm.fw.fin[g][d] = l > 0.0f ? v / l : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * NT + tid;
+        if (i < np && e < GD) sm.fw.fin[i][e / D][e % D] = l[i][u] > 0.0f ? v[i][u] / l[i][u] : 0.0f;
+      }
   }
   __syncthreads();
-  for (int g = wave; g < G; g += NWV) finish_row<D, ROT>(p, sm.fw.fin[g], orow0 + g, lane);
+  for (int g = wave; g < G; g += NWV) {
+    finish_row<D, ROT>(p, sm.fw.fin[0][g], o0a + g, lane);
+    if (np > 1) finish_row<D, ROT>(p, sm.fw.fin[1][g], o0b + g, lane);
+  }
 }
 
 // Inclusive tile prefix of pairs [c0, c0 + cn) into pref[1 .. cn] (pref[0] =
@@ -910,13 +932,9 @@ void decode_kernel(DecodeParams p) {
   Part part;
   part.T = T;
   part.nw = active_wgs(gridDim.x, T);
-  part.ncu = p.ncu;
-  part.nr = part.nw / p.ncu;
-  part.K = (part.nw % p.ncu == 0 && part.nr > 1 && (int64_t)T >= (int64_t)part.nw * (p.share_skew * part.nr + 1))
-               ? p.share_skew : 0;
   const int nw = part.nw;
   if (w >= nw) return;
-  const int a_my = part.start(w), e_my = part.start(w + 1);
+  const int e_my = part.start(w + 1);
 
   // ---- pairs without tiles (an empty sequence) get zero rows; pair i falls
   // to workgroup i % nw
@@ -945,10 +963,9 @@ void decode_kernel(DecodeParams p) {
   // chunk of pairs whose prefix is in LDS: pairs [c0, c0 + cn), cbase tiles
   // before it, ci the next pair to look at
   int c0 = 0, cbase = 0;
-  int x = a_my;          // next tile of the share
+  int x = part.start(w);  // next tile of the share
   int ci = first_after(sm.pref, cn, cbase, x);
   int npend = 0;
-  Buf<MODE, D, PHI> ba, bb;
   // rotating wave priority (see set_prio)
   // (rounds: the workgroup's own waves per SIMD, waves i, i + 4, ... sharing
   // SIMD i % 4, or else the grid's dispatch rounds)
@@ -1023,6 +1040,9 @@ void decode_kernel(DecodeParams p) {
     int pt = threadIdx.x;   // thread index opaque to the compiler, as in the segment epilogue
     asm volatile("" : "+v"(pt));
     const int plane = pt & 63;
+    // the tile buffers live within one batch (each batch loads its first
+    // tile afresh), so nothing holds them across the share's merges
+    Buf<MODE, D, PHI> ba, bb;
 
     // fused step: does this batch hold the last tile of a pair (the tile with
     // the new token at position L - 1)?
@@ -1035,35 +1055,13 @@ void decode_kernel(DecodeParams p) {
       }
     }
 
-    // ---- the wave's first tile goes out first, its block ids read from the
-    // table itself (scalar loads), so its data is on the way while the rest
-    // of the prologue runs; a tile holding a new token waits until after the
-    // barrier that follows the token's store
-    Cursor cur;
-    cur.ls = 0;
-    cur.li = 0;
-    cur.nseg = nseg;
-    cursor_seek(cur, sm, wave);
-    TileInfo ta;
-    // the last wave writes the new tokens, so only it waits on stores; its
-    // first tile, and any wave's first tile that holds a new token, go out
-    // after the barrier
-    const bool writer = wr && wave == NWV - 1;
-    const bool defer = writer ||
-                       (wr && cur.ls < nseg && cur.L > 0 && cur.tb + wave + NWV * cur.li == (cur.L - 1) >> 6);
-    if (cur.ls < nseg) {
-      const int b0 = __builtin_amdgcn_readfirstlane(sm.seg[cur.ls].b);
-      const int32_t* trow = p.tables + (int64_t)(p.headwise ? b0 * hkv + cur.h : b0) * p.max_blocks;
-      ta = tile_info<CB>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te, cur.L, cur.start, bl,
-                         hkv, cur.h);
-    } else {
-      ta = cursor_info<CB>(cur, sm, wave, bl, hkv);
-    }
-    cursor_next(cur, sm, wave);
-    if (!defer) issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
-
-    // ---- batch prologue: block ids (into LDS) and query rows (into
-    // registers) are all requested before anything waits on them
+    // ---- batch prologue: the block ids (into LDS) and the query rows (into
+    // registers) are requested first, then the block id of the wave's first
+    // tile (from the table itself), and that tile's loads go out as soon as
+    // the id is back.  Vector loads complete in order, so the waits for the
+    // ids and the queries below never wait for tile data: the first tiles
+    // stream while the prologue finishes.  A tile holding a new token waits
+    // until after the barrier that follows the token's store.
     uint32_t raw[QR];
     int idv[IDR];
 #pragma unroll
@@ -1089,6 +1087,41 @@ void decode_kernel(DecodeParams p) {
       }
     }
 
+    Cursor cur;
+    cur.ls = 0;
+    cur.li = 0;
+    cur.nseg = nseg;
+    cursor_seek(cur, sm, wave);
+    TileInfo ta;
+    // the last wave writes the new tokens, so only it waits on stores; its
+    // first tile, and any wave's first tile that holds a new token, go out
+    // after the barrier
+    const bool writer = wr && wave == NWV - 1;
+    const bool defer = writer ||
+                       (wr && cur.ls < nseg && cur.L > 0 && cur.tb + wave + NWV * cur.li == (cur.L - 1) >> 6);
+    if (cur.ls < nseg) {
+      const int b0 = __builtin_amdgcn_readfirstlane(sm.seg[cur.ls].b);
+      const int32_t* trow = p.tables + (int64_t)(p.headwise ? b0 * hkv + cur.h : b0) * p.max_blocks;
+      ta = tile_info<CB>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te, cur.L, cur.start, bl,
+                         hkv, cur.h);
+    } else {
+      ta = cursor_info<CB>(cur, sm, wave, bl, hkv);
+    }
+    cursor_next(cur, sm, wave);
+    // the ids and query rows are back (the table read above waited for all
+    // older loads): consume them before the tile loads go out, so no later
+    // wait has to count those loads (a deferred tile would otherwise make the
+    // compiler wait for every load at the join)
+#pragma unroll
+    for (int u = 0; u < IDR; ++u) {
+      const int j = pt + u * NT;
+      if (j < ids_used) sm.ids[j] = idv[u];
+    }
+#pragma unroll
+    for (int i = 0; i < QR; ++i) asm volatile("" : "+v"(raw[i]));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // keep those stores above the tile loads
+    if (!defer) issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
+
     // ---- fused step: the new token of every pair whose last tile is in
     // this batch is quantized and stored (K and V rows, one lane group of the
     // writer wave each), and the writer waits for its stores before the
@@ -1111,11 +1144,6 @@ void decode_kernel(DecodeParams p) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
 
-#pragma unroll
-    for (int u = 0; u < IDR; ++u) {
-      const int j = pt + u * NT;
-      if (j < ids_used) sm.ids[j] = idv[u];
-    }
     __syncthreads();
     if (defer) issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
 
@@ -1242,10 +1270,10 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
           const int e = et + j * NT;
-          if (e < G * D) sm.fw.fin[e / D][e % D] = lsum[j] > 0.0f ? val[j] / lsum[j] : 0.0f;
+          if (e < G * D) sm.fw.fin[0][e / D][e % D] = lsum[j] > 0.0f ? val[j] / lsum[j] : 0.0f;
         }
         __syncthreads();
-        for (int g = wave; g < G; g += NWV) finish_row<D, ROT>(p, sm.fw.fin[g], orow0 + g, elane);
+        for (int g = wave; g < G; g += NWV) finish_row<D, ROT>(p, sm.fw.fin[0][g], orow0 + g, elane);
       } else {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -1277,16 +1305,29 @@ void decode_kernel(DecodeParams p) {
       sm.pflag[tid] = atomicAdd(p.counters + sm.pend[tid][0], 1) == lw - fw;
     }
     __syncthreads();
+    // the pairs this workgroup completes (at most two), merged together
+    int np = 0, s0a = 0, na = 0, s0b = 0, nb = 0, pa = 0, pb = 0;
+    int64_t o0a = 0, o0b = 0;
     for (int i = 0; i < npend; ++i) {
       if (__builtin_amdgcn_readfirstlane(sm.pflag[i])) {
         const int pair = __builtin_amdgcn_readfirstlane(sm.pend[i][0]);
         const int fw = part.owner(__builtin_amdgcn_readfirstlane(sm.pend[i][1]));
         const int lw = part.owner(__builtin_amdgcn_readfirstlane(sm.pend[i][2]) - 1);
         const int b = pair / hkv, h = pair - b * hkv;
-        merge_pieces<D, PHI, NWV, ROT>(p, sm, pair + fw, lw - fw + 1, (int64_t)b * p.hq + h * G, tid);
-        if (tid == 0) atomicExch(p.counters + pair, 0);
-        __syncthreads();
+        if (np == 0) {
+          s0a = pair + fw; na = lw - fw + 1; o0a = (int64_t)b * p.hq + h * G; pa = pair;
+        } else {
+          s0b = pair + fw; nb = lw - fw + 1; o0b = (int64_t)b * p.hq + h * G; pb = pair;
+        }
+        ++np;
       }
+    }
+    if (np > 0) {
+      // eight pieces per round trip, four in the variants with three waves per
+      // SIMD (168 registers)
+      constexpr int KP = decode_waves_per_simd<MODE, D, PHI>() >= 3 ? 4 : 8;
+      merge_pieces<D, PHI, NWV, ROT, KP>(p, sm, np, s0a, na, o0a, s0b, nb, o0b, tid);
+      if (tid < np) atomicExch(p.counters + (tid ? pb : pa), 0);
     }
   }
 }

@@ -191,8 +191,7 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
   p.num_pairs = num_seqs * desc->num_kv_heads;
   p.n_wgs = pl.n_wgs;
   p.ncu = num_cus();
-  p.prio_rot = env_flag("KVQ_DECODE_PRIO", 1);
-  p.share_skew = env_flag("KVQ_DECODE_SKEW", 0);
+  p.prio_rot = env_flag("KVQ_DECODE_PRIO", 0);
   p.out_bf16 = out_dtype == KVQ_OUT_BF16;
   p.bits_magic = 0x43004300u;
   p.bits_n4 = 0x000F000Fu;

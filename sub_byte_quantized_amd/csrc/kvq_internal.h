@@ -65,7 +65,6 @@ struct DecodeParams {
   int32_t n_wgs;                // persistent decode workgroups
   int32_t ncu;                  // compute units (workgroups of one dispatch round)
   int32_t prio_rot;             // 1: dispatch rounds take turns at the top wave priority
-  int32_t share_skew;           // tiles each later dispatch round's shares give up
   int32_t out_bf16;
   uint32_t bits_magic;          // 0x43004300: bf16 128.0 in both halves
   uint32_t bits_n4;             // 0x000F000F
