@@ -69,6 +69,20 @@ __device__ __forceinline__ float quad_xor(float x) {
   return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), sel, 0xF, 0xF, false));
 }
 
+// x from lane l ^ m, m = 1, 2, 4 or 8, partners inside aligned 16-lane rows
+// (m a constant after unrolling): DPP quad permutes for 1 and 2, a rotate by
+// 8 within the 16-lane DPP row for 8 (equal to xor 8 there), a bitmask
+// swizzle for 4; none goes through LDS memory.  Both lanes of a pair must be
+// active.
+__device__ __forceinline__ float xor_in_row(float x, int m) {
+  switch (m) {
+    case 1: return quad_xor<1>(x);
+    case 2: return quad_xor<2>(x);
+    case 4: return __uint_as_float(__builtin_amdgcn_ds_swizzle(__float_as_uint(x), 0x101F));
+    default: return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
+  }
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);

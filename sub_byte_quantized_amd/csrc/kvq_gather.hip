@@ -47,17 +47,34 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
   const int64_t r0 = (int64_t)blockIdx.x * RPB * kGatherIter + (threadIdx.x >> 6) * RPW + lane / LPR;
   if (r0 >= rows) return;
 
+  // the lane's rotation signs, read before any store (so not reloaded per row)
+  float sg[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+  if constexpr (ROT) {
+    const float4 s0 = *reinterpret_cast<const float4*>(p.signs + lr * 8);
+    const float4 s1 = *reinterpret_cast<const float4*>(p.signs + lr * 8 + 4);
+    sg[0] = s0.x; sg[1] = s0.y; sg[2] = s0.z; sg[3] = s0.w;
+    sg[4] = s1.x; sg[5] = s1.y; sg[6] = s1.z; sg[7] = s1.w;
+  }
   uint32_t raw[kGatherIter][BPL >= 4 ? BPL / 4 : 1];
   float s[kGatherIter], z[kGatherIter];
   bool present[kGatherIter];
   int64_t orow[kGatherIter];
   int hh[kGatherIter], kvs[kGatherIter];
+  // r = pos * 2 Hkv + 2 h + kv: one division for the first row, then steps
+  // of RPB rows
+  int pos = (int)(r0 / (2 * hkv));
+  int rem = (int)(r0 - (int64_t)pos * 2 * hkv);
 #pragma unroll
   for (int it = 0; it < kGatherIter; ++it) {
     const int64_t r = r0 + (int64_t)it * RPB;
+    if (it > 0) {
+      rem += RPB;
+      while (rem >= 2 * hkv) {
+        rem -= 2 * hkv;
+        ++pos;
+      }
+    }
     const bool in = r < rows;
-    const int pos = (int)(r / (2 * hkv));
-    const int rem = (int)(r - (int64_t)pos * 2 * hkv);
     const int h = rem >> 1, kv = rem & 1;
     hh[it] = h;
     kvs[it] = kv;
@@ -124,16 +141,12 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
       }
 #pragma unroll
       for (int m = 1; m < LPR; m <<= 1) {
-        const bool upper = (lr & m) != 0;
+        // x + o in the lower lane, o - x in the upper one, as one fma with a
+        // +-1 factor (the product is exact, so the single rounding is the sum's)
+        const float sgn = (lr & m) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float o = __shfl_xor(x[i], m);
-          x[i] = upper ? (o - x[i]) : (x[i] + o);
-        }
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], sgn, xor_in_row(x[i], m));
       }
-      const float4 s0 = *reinterpret_cast<const float4*>(p.signs + lr * 8);
-      const float4 s1 = *reinterpret_cast<const float4*>(p.signs + lr * 8 + 4);
-      const float sg[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = x[i] * sg[i] * p.inv_sqrt_d;
     }

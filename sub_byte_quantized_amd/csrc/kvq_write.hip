@@ -16,7 +16,9 @@
 //
 // Work split: one row = one (token, kv head) of K or of V.  D/8 lanes own a
 // row, 8 elements per lane (one 16-byte load), so a wave64 handles 128/D*4
-// rows and a 256-thread workgroup 16 (D=128) or 32 (D=64) rows.  The FWHT
+// rows at once; each lane group takes four rows 16 (D=128) or 32 (D=64) rows
+// apart, their slots and loads all requested before the first is used, so a
+// 256-thread workgroup writes 64 or 128 rows.  The FWHT
 // runs in registers for the three in-lane stages and across lanes for the
 // rest; min/max/absmax are lane reductions.  Stores are the lane's slice of
 // the packed row (4 bytes for INT4, 8 for INT8, 2 for INT2) plus one meta
@@ -29,23 +31,50 @@
 namespace kvq {
 namespace {
 
+constexpr int kWriteIter = 4;   // rows per lane group, their loads in flight together
+
 template <int MODE, int D, bool ROT>
 __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
   constexpr int LPR = D / 8;             // lanes per row
   constexpr int RPW = 64 / LPR;          // rows per wave
-  constexpr int RPB = 4 * RPW;           // rows per workgroup
+  constexpr int RPB = 4 * RPW;           // rows per workgroup and iteration
 
   const int lane = threadIdx.x & 63;
   const int lr = lane & (LPR - 1);
-  const int64_t row = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6) * RPW + lane / LPR;
+  const int64_t row0 = (int64_t)blockIdx.x * RPB * kWriteIter + (threadIdx.x >> 6) * RPW + lane / LPR;
   const int hkv = p.hkv;
-  const int64_t t = row / (2 * hkv);
-  const int h = (int)((row >> 1) % hkv);
-  const int kv = (int)(row & 1);
 
-  int64_t slot = -1;
-  if (row < p.total_rows) slot = p.slot_hw ? p.slot_hw[t * hkv + h] : p.slot[t];
-  write_row<MODE, D, ROT>(p, t, h, kv, slot, lr);
+  float sg[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+  if constexpr (ROT) write_row_signs(p, lr, sg);
+  int64_t slot[kWriteIter];
+  uint4 raw[kWriteIter];
+  int hs[kWriteIter];
+  // row = t * 2 Hkv + 2 h + kv: one division for the first row, then steps
+  // of RPB rows
+  int64_t t = row0 / (2 * hkv);
+  int rem = (int)(row0 - t * 2 * hkv);
+#pragma unroll
+  for (int it = 0; it < kWriteIter; ++it) {
+    const int64_t row = row0 + (int64_t)it * RPB;
+    if (it > 0) {
+      rem += RPB;
+      while (rem >= 2 * hkv) {
+        rem -= 2 * hkv;
+        ++t;
+      }
+    }
+    const int h = rem >> 1;
+    hs[it] = rem;
+    slot[it] = -1;
+    raw[it] = make_uint4(0, 0, 0, 0);
+    if (row < p.total_rows) {
+      slot[it] = p.slot_hw ? p.slot_hw[t * hkv + h] : p.slot[t];
+      raw[it] = write_row_load<D>(p, t, h, rem & 1, lr);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kWriteIter; ++it)
+    write_row_store<MODE, D, ROT>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, slot[it], lr);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
@@ -56,7 +85,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
 
 template <int MODE, int D, bool ROT>
 hipError_t launch_write_t(const WriteParams& p, hipStream_t s) {
-  constexpr int RPB = 4 * (64 / (D / 8));
+  constexpr int RPB = 4 * (64 / (D / 8)) * kWriteIter;
   const int64_t blocks = (p.total_rows + RPB - 1) / RPB;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((write_kernel<MODE, D, ROT>), dim3((unsigned)blocks), dim3(256), 0, s, p);

@@ -7,16 +7,38 @@
 // (converged: the FWHT and the statistics are shuffles within the group);
 // each lane owns 8 consecutive elements.  Row (token t, kv head h, K if kv =
 // 0 else V) goes to `slot` (block * block_size + offset); slot < 0 computes
-// nothing visible.
+// nothing visible.  The load and the rest are separate steps, so a caller
+// can have the loads of several rows in flight before the first is used.
 #pragma once
 
 #include "kvq_internal.h"
+#include "kvq_device.h"
 
 namespace kvq {
 namespace {
 
+// The lane's 8 bf16 elements of row (token t, kv head h, K if kv = 0 else
+// V): one 16-byte load.
+template <int D>
+__device__ __forceinline__ uint4 write_row_load(const WriteParams& p, int64_t t, int h, int kv, int lr) {
+  const uint16_t* src = kv ? p.value + t * p.value_stride : p.key + t * p.key_stride;
+  return *reinterpret_cast<const uint4*>(src + (int64_t)h * D + lr * 8);
+}
+
+// The lane's 8 rotation signs (read before any store of the caller, so they
+// are not reloaded after each row's stores).
+__device__ __forceinline__ void write_row_signs(const WriteParams& p, int lr, float (&sg)[8]) {
+  const float4 s0 = *reinterpret_cast<const float4*>(p.signs + lr * 8);
+  const float4 s1 = *reinterpret_cast<const float4*>(p.signs + lr * 8 + 4);
+  sg[0] = s0.x; sg[1] = s0.y; sg[2] = s0.z; sg[3] = s0.w;
+  sg[4] = s1.x; sg[5] = s1.y; sg[6] = s1.z; sg[7] = s1.w;
+}
+
+// Everything after the load: rotation (lane signs sg), scale (and zero),
+// codes, packed and paged stores of the row whose lane elements `raw` holds.
 template <int MODE, int D, bool ROT>
-__device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h, int kv, int64_t slot, int lr) {
+__device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw, const float (&sg)[8], int h, int kv,
+                                                int64_t slot, int lr) {
 #pragma clang fp contract(off)
   constexpr int LPR = D / 8;             // lanes per row
   constexpr int P = row_bytes(MODE, D);  // packed bytes per row
@@ -28,8 +50,6 @@ __device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h
 
   float x[8];
   if (active) {
-    const uint16_t* src = kv ? p.value + t * p.value_stride : p.key + t * p.key_stride;
-    const uint4 raw = *reinterpret_cast<const uint4*>(src + (int64_t)h * D + lr * 8);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -42,10 +62,8 @@ __device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h
   }
 
   if constexpr (ROT) {
-    const float4 s0 = *reinterpret_cast<const float4*>(p.signs + lr * 8);
-    const float4 s1 = *reinterpret_cast<const float4*>(p.signs + lr * 8 + 4);
-    x[0] *= s0.x; x[1] *= s0.y; x[2] *= s0.z; x[3] *= s0.w;
-    x[4] *= s1.x; x[5] *= s1.y; x[6] *= s1.z; x[7] *= s1.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] *= sg[i];
     // in-lane butterflies, pairs (i, i + hh) with bit hh of i clear
 #pragma unroll
     for (int hh = 1; hh < 8; hh <<= 1) {
@@ -61,12 +79,11 @@ __device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h
     // cross-lane butterflies: element stride 8*m lives m lanes away
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) {
-      const bool upper = (lr & m) != 0;
+      // x + o in the lower lane, o - x in the upper one, as one fma with a
+      // +-1 factor (the product is exact, so the single rounding is the sum's)
+      const float sgn = (lr & m) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float o = __shfl_xor(x[i], m);
-        x[i] = upper ? (o - x[i]) : (x[i] + o);
-      }
+      for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], sgn, xor_in_row(x[i], m));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = x[i] * p.inv_sqrt_d;
@@ -78,7 +95,7 @@ __device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h
 #pragma unroll
     for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) a = fmaxf(a, __shfl_xor(a, m));
+    for (int m = 1; m < LPR; m <<= 1) a = fmaxf(a, xor_in_row(a, m));
     s = a / kLevels;
     z = 0.0f;
   } else {
@@ -90,8 +107,8 @@ __device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h
     }
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, m));
-      mx = fmaxf(mx, __shfl_xor(mx, m));
+      mn = fminf(mn, xor_in_row(mn, m));
+      mx = fmaxf(mx, xor_in_row(mx, m));
     }
     s = (mx - mn) / kLevels;
     z = mn;
@@ -139,6 +156,15 @@ __device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h
       *reinterpret_cast<float2*>(meta) = make_float2(s, z);
     }
   }
+}
+
+// The whole row: load, then compute and store (slot < 0 reads nothing).
+template <int MODE, int D, bool ROT>
+__device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h, int kv, int64_t slot, int lr) {
+  const uint4 raw = slot >= 0 ? write_row_load<D>(p, t, h, kv, lr) : make_uint4(0, 0, 0, 0);
+  float sg[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+  if constexpr (ROT) write_row_signs(p, lr, sg);
+  write_row_store<MODE, D, ROT>(p, raw, sg, h, kv, slot, lr);
 }
 
 }  // namespace
