@@ -50,6 +50,7 @@ CSRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc")
 DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h", "kvq_write_row.h")]
 PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")]
 GATHER_SRC = [os.path.join(CSRC, f) for f in ("kvq_gather.hip", "kvq_device.h", "kvq_internal.h")]
+WRITE_SRC = [os.path.join(CSRC, f) for f in ("kvq_write.hip", "kvq_write_row.h", "kvq_device.h", "kvq_internal.h")]
 
 
 def sha(paths):
@@ -133,14 +134,14 @@ def write_bytes_per_token(spec):
     return spec.Hkv * 2 * (spec.D * 2 + P + 4 * M) + slot
 
 
-def gather_bytes(spec, case):
-    """Algorithmic bytes of a whole-cache dequantize-gather: per (position,
-    kv head) row of K and of V, the packed codes and fp32 meta read (rows in
-    present blocks) and the bf16 row written; plus the block-table entries and
-    cu_seq_lens read."""
+def gather_bytes(spec, case, nseq=None):
+    """Algorithmic bytes of a dequantize-gather of the first `nseq` sequences'
+    whole contexts (all by default): per (position, kv head) row of K and of
+    V, the packed codes and fp32 meta read (rows in present blocks) and the
+    bf16 row written; plus the block-table entries and cu_seq_lens read."""
     P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
     M = 1 if spec.mode == 0 else 2
-    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)[:nseq]
     present = 0
     entries = 0
     for b, L in enumerate(lens):
@@ -410,24 +411,21 @@ def run_mixed(args, spec, dev):
     wb = write_bytes_per_token(spec)
     p_tf = flops / (p_ms * 1e-3) / 1e12
     d_gbs = d_algo / (d_ms * 1e-3) / 1e9
-    # dequantize-gather of the whole cache (every sequence, positions 0 ..
-    # L - 1, bf16 rows [T, Hkv, D] for K and for V), cycling the replicas
-    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    # the prefill fallback: dequantize-gather of the prefill sequences' whole
+    # contexts (positions 0 .. L - 1, head-wise table, bf16 rows [T, Hkv, D])
+    lens = psl.cpu().numpy().astype(np.int64)
     cu_np = np.concatenate([[0], np.cumsum(lens)])
     cu = torch.as_tensor(cu_np.astype(np.int32), device=dev)
     g_tot = int(cu_np[-1])
     g_out = [torch.empty((g_tot, spec.Hkv, spec.D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
 
     def gather(i):
-        kvq.kvq_gather_dequant(d, *replicas[i % R], cu, max_len, g_tot, block_tables=case.block_tables,
-                               block_tables_headwise=case.block_tables_headwise,
+        kvq.kvq_gather_dequant(d, *planes, cu, max_len, g_tot, block_tables=pbt, block_tables_headwise=pbth,
                                key_out=g_out[0], value_out=g_out[1])
 
     gather(0)
-    g_ms = time_events(gather, 5)
-    g_avg = float(np.mean(g_ms))
-    g_bytes = gather_bytes(spec, case)
-    g_cpu = None if args.no_cpu_baseline else gather_cpu(spec, case, planes, lens, 3.0)
+    g_avg = float(np.mean(time_events(gather, 5)))
+    g_bytes = gather_bytes(spec, case, npf)
     del g_out
 
     result = {
@@ -461,6 +459,11 @@ def run_mixed(args, spec, dev):
         "write": {"step_tokens": T, "step_write_us": round(w_ms * 1e3, 2),
                   "tokens_per_s": round(T / (w_ms * 1e-3), 1), "bytes_per_token": wb,
                   "GBps": round(T * wb / (w_ms * 1e-3) / 1e9, 2)},
+        "gather": {"kernel": "gather_kernel (dequantize-gather of the prefill contexts, bf16 out)",
+                   "rows": int(g_tot) * spec.Hkv * 2, "avg_launch_us": round(g_avg * 1e3, 2),
+                   "algorithmic_bytes_per_launch": int(g_bytes),
+                   "GBps": round(g_bytes / (g_avg * 1e-3) / 1e9, 2),
+                   "frac": round(g_bytes / (g_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "setup_s": round(setup_s, 1),
     }
     if not args.no_cpu_baseline:
@@ -651,7 +654,8 @@ def main():
                   "fill_tokens": int(T), "fill_us": round(fill_avg * 1e3, 2),
                   "tokens_per_s": round(T / (fill_avg * 1e-3), 1),
                   "bytes_per_token": wb, "GBps": round(T * wb / (fill_avg * 1e-3) / 1e9, 2),
-                  "frac": round(T * wb / (fill_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                  "frac": round(T * wb / (fill_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "traffic": load_traffic(f"write_{spec.name}_counters.json", WRITE_SRC)},
         "gather": {"kernel": "gather_kernel (dequantize-gather, bf16 out)", "rows": int(g_tot) * spec.Hkv * 2,
                    "avg_launch_us": round(g_avg * 1e3, 2), "algorithmic_bytes_per_launch": int(g_bytes),
                    "GBps": round(g_bytes / (g_avg * 1e-3) / 1e9, 2),
