@@ -75,11 +75,12 @@ __device__ __forceinline__ float quad_xor(float x) {
 // swizzle for 4; none goes through LDS memory.  Both lanes of a pair must be
 // active.
 __device__ __forceinline__ float xor_in_row(float x, int m) {
+  // plain DPP moves (no old value to merge, so no zeroed destination first)
   switch (m) {
-    case 1: return quad_xor<1>(x);
-    case 2: return quad_xor<2>(x);
+    case 1: return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0xB1, 0xF, 0xF, true));
+    case 2: return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x4E, 0xF, 0xF, true));
     case 4: return __uint_as_float(__builtin_amdgcn_ds_swizzle(__float_as_uint(x), 0x101F));
-    default: return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
+    default: return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x128, 0xF, 0xF, true));
   }
 }
 

@@ -127,8 +127,10 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   }
 
   if (!active) return;
-  const int64_t blk = slot / p.block_size;
-  const int64_t off = slot - blk * p.block_size;
+  // block_size is a power of two (checked on the host)
+  const int bsl = __builtin_ctz((unsigned)p.block_size);
+  const int64_t blk = slot >> bsl;
+  const int64_t off = slot & (p.block_size - 1);
   const int64_t ridx = (blk * hkv + h) * p.block_size + off;
   uint8_t* codes = (kv ? p.v_codes : p.k_codes) + ridx * P + lr * BPL;
   float* meta = (kv ? p.v_meta : p.k_meta) + ridx * M;
