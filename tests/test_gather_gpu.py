@@ -137,25 +137,32 @@ def test_gather_repeatable():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_gather_full_config_sampled(cfg):
-    """The whole cache of the INT8 (batch 32) and INT4 + rotation (batch 96)
-    workloads gathered in one bf16 call, as the bench times it; sampled
-    (sequence, kv head) pairs checked against the oracle."""
+    """The whole cache of the INT8 (batch 32), INT4 + rotation (batch 96) and
+    INT2 + rotation (4 x 131072) workloads, and the 16 prefill contexts of the
+    mixed step (head-wise table with -1 entries), gathered in one bf16 call
+    each, as the bench times them; sampled (sequence, kv head) pairs checked
+    against the oracle."""
     spec = synth.CONFIGS[cfg]
     print(f"[case] gather full {spec.name}", flush=True)
     case, d, planes = gh.build(spec)
-    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    nseq = spec.n_prefill or spec.B
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)[:nseq]
     cu_np = np.concatenate([[0], np.cumsum(lens)])
     cu = torch.as_tensor(cu_np.astype(np.int32), device=gh.dev())
-    K, V = run_gather(spec, case, d, planes, cu, int(lens.max()), int(lens.sum()), torch.bfloat16)
+    bt = None if case.block_tables is None else case.block_tables[:nseq].contiguous()
+    bth = None if case.block_tables_headwise is None else case.block_tables_headwise[:nseq * spec.Hkv].contiguous()
+    K, V = kvq.kvq_gather_dequant(d, *planes, cu, int(lens.max()), int(lens.sum()), block_tables=bt,
+                                  block_tables_headwise=bth, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     pl = gh.host_planes(planes)
     r = np.random.default_rng(cfg)
-    for b in r.choice(spec.B, 3, replace=False):
+    for b in r.choice(nseq, 3, replace=False):
         h = int(r.integers(spec.Hkv))
         Kr, Vr, _ = oracle.gather_head(int(b), h, int(lens[b]), spec.mode, spec.D, spec.bs, spec.Hkv, *pl,
-                                       signs=gh.host(case.rot_signs), block_tables=gh.host(case.block_tables))
+                                       signs=gh.host(case.rot_signs), block_tables=gh.host(bt),
+                                       block_tables_headwise=gh.host(bth))
         rows = slice(int(cu_np[b]), int(cu_np[b + 1]))
         check_gather(K[rows, h].float().cpu().numpy(), Kr, spec.D, True, f"{spec.name} b{b} h{h} K")
         check_gather(V[rows, h].float().cpu().numpy(), Vr, spec.D, True, f"{spec.name} b{b} h{h} V")
