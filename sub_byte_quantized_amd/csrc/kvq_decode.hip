@@ -937,10 +937,12 @@ void decode_kernel(DecodeParams p) {
   const int e_my = part.start(w + 1);
 
   // ---- pairs without tiles (an empty sequence) get zero rows; pair i falls
-  // to workgroup i % nw
+  // to workgroup i % nw.  Pairs of the first prefix chunk take their length
+  // from LDS (the scan's), so only batches of more than kPrefChunk pairs
+  // read seq_lens again here.
   for (int i = w + tid * nw; i < P; i += NT * nw) {
     int t0, L, s;
-    if (pair_geo(p, i, &t0, &L, &s) == 0) {
+    if (i < cn ? sm.plen[i] <= 0 : pair_geo(p, i, &t0, &L, &s) == 0) {
       const int b = i / hkv, h = i - b * hkv;
       const int64_t o = ((int64_t)b * p.hq + h * G) * D;
       for (int e = 0; e < G * D; ++e) {
