@@ -186,6 +186,132 @@ def check_quant_degenerate(o):
         assert np.all(c == 0)
 
 
+# ------------------------------------------- exact model of the fp32 steps ---
+# The write's codes are decided by a fixed sequence of float32 operations
+# (s = fl(fl(max - min) / L), inv = fl(1 / s), base = fl(y - z), t = fl(base * inv),
+# c = round-half-even(t), clamped).  The pins below model that sequence with
+# exact rationals and an explicit round-to-nearest-even onto the 24-bit
+# float32 significand, independent of numpy's float32 arithmetic, and feed it
+# rows built to sit on or next to rounding ties, where any other reading
+# (round half up or away, a float64 t, a division instead of the reciprocal,
+# an unrounded subtraction) gives a different code.
+from fractions import Fraction as _Fr
+
+
+def _f32r(x):
+    """Round a rational to the nearest float32 (ties to even), normal range."""
+    x = _Fr(x)
+    if x == 0:
+        return _Fr(0)
+    sgn = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if _Fr(2) ** e > a:
+        e -= 1
+    assert _Fr(2) ** e <= a < _Fr(2) ** (e + 1)
+    assert -126 <= e <= 127, "outside the normal float32 range"
+    ulp = _Fr(2) ** (e - 23)
+    n = _rne_int(a / ulp)
+    return sgn * n * ulp
+
+
+def _rne_int(t):
+    """Nearest integer to a rational, ties to even."""
+    t = _Fr(t)
+    f = t.numerator // t.denominator
+    r = t - f
+    if r > _Fr(1, 2) or (r == _Fr(1, 2) and f % 2 == 1):
+        return f + 1
+    return f
+
+
+def _model_codes(row, mode):
+    """Codes, s, z of one float32 row by the exact model of the steps."""
+    L = {0: 127, 1: 15, 2: 3}[mode]
+    y = [_Fr(float(v)) for v in row]
+    if mode == 0:
+        s = _f32r(max(abs(v) for v in y) / L)
+        z = _Fr(0)
+        base = y
+        lo = -L
+    else:
+        mn, mx = min(y), max(y)
+        s = _f32r(_f32r(mx - mn) / L)
+        z = mn
+        base = [_f32r(v - mn) for v in y]
+        lo = 0
+    if s < _Fr(2) ** -126:
+        return [0] * len(y), s, z
+    inv = _f32r(1 / s)
+    return [min(max(_rne_int(_f32r(b * inv)), lo), L) for b in base], s, z
+
+
+def _tie_rows():
+    """Rows (mode, float32 row) whose exact (y - z) / s lands on or beside
+    k + 1/2:
+      * s = 2^-e: every code step is exact, t = k + 1/2 exactly;
+      * INT4 s = 3 (z = 0, max 45): fl(1/3) = (2^25 + 1) / (3 2^25), so
+        (k + 1/2) fl(1/3) lies within half an ulp of k + 1/2 and rounds back
+        onto the tie;
+      * INT4 s = 7/64 (max 105/64): fl(64/7) exceeds 64/7 by 4.5e-8
+        relative, so (k + 1/2) fl(64/7) rounds up past the tie for k = 6,
+        12, 14, where the exact quotient would round to the even neighbour;
+      * float32 rows with a non-dyadic z and scale, y placed a few ulps either
+        side of fl((k + 1/2) s + z), where the rounding of y - z decides."""
+    rows = []
+    for e in (0, 3, -2):
+        u = 2.0 ** -e
+        rows.append((0, np.array([127 * u, -127 * u] + [(k + 0.5) * u for k in range(-127, 127)], F32)))
+        for mode, L in ((1, 15), (2, 3)):
+            z = -1.25 * u
+            rows.append((mode, np.array([z, z + L * u] + [z + (k + 0.5) * u for k in range(L)] * 4, F32)))
+    rows.append((1, np.array([0.0, 45.0] + [3 * (k + 0.5) for k in range(15)], F32)))
+    rows.append((1, np.array([0.0, 105 / 64] + [(k + 0.5) * 7 / 64 for k in range(15)], F32)))
+    r = np.random.default_rng(17)
+    for mode, L in ((1, 15), (2, 3), (1, 15)):
+        for _ in range(6):
+            s = F32(int(r.integers(1, 1 << 12)) * 2.0 ** -12)
+            z = F32(-int(r.integers(1, 1 << 20)) * 2.0 ** -24)
+            ys = [z, F32(z + F32(L) * s)]
+            for k in range(L):
+                c = F32(F32(k + 0.5) * s + z)
+                for d in (-2, -1, 0, 1, 2):
+                    v = c
+                    for _ in range(abs(d)):
+                        v = np.nextafter(v, F32(np.inf) if d > 0 else F32(-np.inf))
+                    ys.append(F32(v))
+            rows.append((mode, np.array(ys, F32)))
+    return rows
+
+
+def check_quant_exact_model_ties(o):
+    """Codes, scales and zero points of rows on and beside rounding ties equal
+    the exact model of the float32 steps (round half to even; one correctly
+    rounded reciprocal; rounded subtraction; rounded product)."""
+    for mode, row in _tie_rows():
+        c, s, z = o.quantize_rows(row[None, :], mode)
+        mc, ms, mz = _model_codes(row, mode)
+        assert _Fr(float(s[0])) == ms and _Fr(float(z[0])) == mz, (mode, row[:4])
+        assert [int(v) for v in c[0]] == mc, (mode, row[:4], [int(v) for v in c[0]], mc)
+
+
+def check_quant_ties_to_even(o):
+    """On a power-of-two grid every t is exactly k + 1/2: the codes are the
+    even neighbours (0.5 -> 0, 1.5 -> 2, -0.5 -> 0, -1.5 -> -2)."""
+    for mode, L in ((0, 127), (1, 15), (2, 3)):
+        if mode == 0:
+            ks = np.arange(-127, 127)
+            row = np.concatenate([[127.0, -127.0], ks + 0.5]).astype(F32)
+            exp = np.where(ks % 2 == 0, ks, ks + 1)
+        else:
+            ks = np.arange(L)
+            row = np.concatenate([[0.0, float(L)], ks + 0.5]).astype(F32)
+            exp = np.where(ks % 2 == 0, ks, ks + 1)
+        c, s, z = o.quantize_rows(row[None, :], mode)
+        assert s[0] == 1.0
+        assert np.array_equal(c[0, 2:], exp), mode
+
+
 # ------------------------------------------------------------------ layout ---
 def check_layout_facts(o):
     with open(os.path.join(HERE, "golden", "layout_facts.json")) as f:
@@ -239,6 +365,49 @@ def check_paged_roundtrip(o):
                     assert np.array_equal(pm[blk, h, off, 1], z.reshape(T, Hkv)[:, h])
         unused = np.setdiff1d(np.arange(t["nb"]), t["used"])
         assert np.all(kc[unused] == 0xFF) and np.all(np.isnan(km[unused]))
+
+
+def check_write_headwise_slot_map(o):
+    """A head-wise slot map [T, Hkv] sends row (t, h) to its own slot: with
+    independent per-head block permutations, the (block, h) slice named by
+    slot_hw[t, h] holds the encoding of k[t, h] and v[t, h] and nothing else
+    changes; reading each head back through its own head-wise table row gives
+    the tokens in order."""
+    D, bs, Hkv, T = 64, 4, 3, 10          # T != Hkv, so a transposed map reads wrong slots
+    nblk = (T + bs - 1) // bs
+    nb = nblk + 2
+    r = np.random.default_rng(21)
+    bth = np.full((Hkv, nblk), -1, np.int64)
+    for h in range(Hkv):
+        bth[h] = r.permutation(nb)[:nblk]
+    pos = np.arange(T)
+    slot_hw = np.stack([bth[h, pos // bs] * bs + pos % bs for h in range(Hkv)], axis=1)   # [T, Hkv]
+    assert not np.array_equal(slot_hw[:, 0], slot_hw[:, 1])
+    k = _bf16_rows((T, Hkv, D), 61)
+    v = _bf16_rows((T, Hkv, D), 62, offset=0.25)
+    for mode in MODES:
+        cs, ms = o.plane_shapes(mode, D, Hkv, bs, nb)
+        planes = [np.full(cs, 0xFF, np.uint8), np.full(ms, np.nan, F32),
+                  np.full(cs, 0xFF, np.uint8), np.full(ms, np.nan, F32)]
+        o.write_cache(k, v, mode, bs, *planes, slot_mapping_headwise=slot_hw)
+        touched = np.zeros((nb, Hkv, bs), bool)
+        for src, pc, pm in ((k, planes[0], planes[1]), (v, planes[2], planes[3])):
+            for t in range(T):
+                for h in range(Hkv):
+                    packed, sc, z, _ = o.encode_rows(src[t, h][None], mode)
+                    blk, off = divmod(int(slot_hw[t, h]), bs)
+                    touched[blk, h, off] = True
+                    assert np.array_equal(pc[blk, h, off], packed[0]), (mode, t, h)
+                    assert pm[blk, h, off, 0] == sc[0]
+                    if mode != 0:
+                        assert pm[blk, h, off, 1] == z[0]
+            assert np.all(pc[~touched] == 0xFF) and np.all(np.isnan(pm[~touched]))
+        table = np.repeat(bth[None], 1, axis=0).reshape(Hkv, nblk)   # rows b*Hkv + h with b = 0
+        for h in range(Hkv):
+            K, V, pres = o.gather_head(0, h, T, mode, D, bs, Hkv, *planes, block_tables_headwise=table)
+            assert pres.all()
+            ck, sk, zk = o.quantize_rows(k[:, h], mode)
+            assert np.array_equal(K, o.dequant_rows_f64(ck, sk, zk)), (mode, h)
 
 
 def check_gather_matches_dense(o):

@@ -34,6 +34,15 @@ MUTATIONS = {
     "gather_head_index": ("K[cu[b]:cu[b + 1], h] = Kb", "K[cu[b]:cu[b + 1], num_kv_heads - 1 - h] = Kb"),
     "gather_row_offset": ("n = int(cu[b + 1] - cu[b])", "n = int(cu[b + 1] - cu[b]) - (b > 0)"),
     "slot_offset": ("blk, off = sl // block_size, sl % block_size", "blk, off = sl // block_size, (sl + 1) % block_size"),
+    # rounding and the float32 operation order of the code decision
+    "round_half_up": ("c = np.clip(np.rint(t), lo, hi)", "c = np.clip(np.floor(t + 0.5), lo, hi)"),
+    "round_half_away": ("c = np.clip(np.rint(t), lo, hi)", "c = np.clip(np.sign(t) * np.floor(np.abs(t) + 0.5), lo, hi)"),
+    "t_float64": ("t = (base * inv[..., None]).astype(_F32)", "t = base.astype(np.float64) * inv[..., None].astype(np.float64)"),
+    "t_divide": ("t = (base * inv[..., None]).astype(_F32)", "t = (base / np.where(ok, s, _F32(1.0))[..., None]).astype(_F32)"),
+    "sub_unrounded": ("base = (y - mn[..., None]).astype(_F32)", "base = y.astype(np.float64) - mn[..., None].astype(np.float64)"),
+    "range_unrounded": ("s = ((mx - mn) / L).astype(_F32)", "s = ((mx.astype(np.float64) - mn) / L).astype(_F32)"),
+    "headwise_slots_transposed": ("slots = np.asarray(slot_mapping_headwise, np.int64).reshape(T, Hkv)",
+                                  "slots = np.asarray(slot_mapping_headwise, np.int64).reshape(Hkv, T).T"),
 }
 
 
