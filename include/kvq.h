@@ -35,8 +35,13 @@
  *    then returns a message (thread-local, valid until the next call on the
  *    same thread).  The library never aborts.
  *  - Values the host cannot see (device-side seq_lens, block ids, slots) are
- *    the caller's contract: block ids must be < num_blocks or negative (table
- *    entries) and slots < num_blocks*block_size or negative (slot mappings).
+ *    the caller's contract: block ids should be < num_blocks or negative
+ *    (table entries) and slots < num_blocks*block_size or negative (slot
+ *    mappings).  A violation never makes a kernel touch memory outside the
+ *    planes: a table entry >= num_blocks is treated like -1 (an evicted
+ *    block, never read), a slot >= num_blocks*block_size like a negative one
+ *    (the row is not written), and seq_lens entries are clamped to
+ *    max_seq_len.  Results for such inputs are what those rules give.
  *
  * Cache layout (one code plane and one meta plane each for K and for V):
  *    codes: uint8   [num_blocks, num_kv_heads, block_size, P]
@@ -90,6 +95,16 @@ typedef struct {
   const float* rot_signs;
 } kvq_cache_desc;
 
+/* Options of a decode launch.  Pass NULL for the defaults. */
+typedef struct {
+  /* Workgroups of the persistent decode grid; 0 = as many as the device
+   * holds resident at once (the default and the fastest).  Any positive count
+   * gives the same result up to floating-point summation order (each count's
+   * result is deterministic); the workspace size depends on it, so the same
+   * options must be given to kvq_decode_workspace_size. */
+  int32_t num_workgroups;
+} kvq_decode_options;
+
 typedef struct {
   uint64_t code_bytes;       /* bytes of one code plane (the K plane; V is equal) */
   uint64_t meta_bytes;       /* bytes of one meta plane */
@@ -127,14 +142,16 @@ kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc,
                                  uint8_t* v_codes, float* v_meta,
                                  void* stream);
 
-/* Workspace bytes kvq_paged_decode_attention needs for these sizes (host
- * only).  max_seq_len is the largest seq_lens entry the call will see.  The
- * workspace holds one counter per (sequence, kv head) and the partial
- * softmax states of pairs that several workgroups share; its size grows with
- * num_seqs * kv heads and the GQA group, not with max_seq_len (except for
- * very long batches). */
+/* Workspace bytes kvq_paged_decode_attention and kvq_decode_step need for
+ * these sizes and options (host only; options NULL = defaults, and the same
+ * options must then be passed to the decode call).  max_seq_len is the
+ * largest seq_lens entry the call will see.  The workspace holds one counter
+ * per (sequence, kv head) and the partial softmax states of pairs that
+ * several workgroups share; its size grows with num_seqs * kv heads and the
+ * GQA group, not with max_seq_len (except for very long batches). */
 kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t num_seqs,
                                      int32_t num_q_heads, int32_t max_seq_len,
+                                     const kvq_decode_options* options,
                                      size_t* bytes /* host */);
 
 /* Zero a workspace (asynchronous on `stream`; 256-byte aligned, size a
@@ -157,10 +174,12 @@ kvq_status kvq_workspace_init(void* workspace, size_t workspace_bytes, void* str
  *                exactly one is non-NULL; row b*Hkv + h serves kv head h;
  *                an entry < 0 marks an evicted block (never read)
  *   seq_lens     (device) int32 [B], positions cached for each sequence
- *                (the current token included), each <= max_seq_len
+ *                (the current token included), each <= max_seq_len (larger
+ *                entries are clamped to it)
  *   max_seq_len  host upper bound on seq_lens, <= max_blocks_per_seq*block_size
  *   window       (device) int32 [Hkv], <= 0 = full context; or NULL
  *   softmax_scale  logits scale (usually 1/sqrt(D)); finite
+ *   options      NULL, or the options given to kvq_decode_workspace_size
  *   workspace    (device) >= kvq_decode_workspace_size bytes, 256-byte
  *                aligned, zeroed before its first use (kvq_workspace_init);
  *                holds per-pair counters, zero again when the call ends, and
@@ -178,6 +197,7 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc,
                                       const int32_t* seq_lens, int32_t max_seq_len,
                                       const int32_t* window,
                                       float softmax_scale,
+                                      const kvq_decode_options* options,
                                       void* workspace, size_t workspace_bytes,
                                       void* stream);
 
@@ -218,6 +238,7 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc,
                            const int32_t* seq_lens, int32_t max_seq_len,
                            const int32_t* window,
                            float softmax_scale,
+                           const kvq_decode_options* options,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
@@ -239,8 +260,11 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc,
  *                are not computed)
  *   seq_lens     (device) int32 [num_seqs], each >= n_b and <= max_seq_len
  *   block tables, window, softmax_scale and the cache planes as for
- *   kvq_paged_decode_attention.  No workspace: every launch covers the whole
- *   key range of its rows.  GQA groups up to 128. */
+ *   kvq_paged_decode_attention
+ *   workspace    (device) kvq_prefill_workspace_size bytes; may be NULL when
+ *                that size is 0 (it is for every shape this library builds:
+ *                each workgroup covers the whole key range of its rows)
+ * GQA groups up to 128.  One kernel launch. */
 kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc,
                                        void* out, int32_t out_dtype,
                                        const void* query,
@@ -255,7 +279,16 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc,
                                        const int32_t* seq_lens, int32_t max_seq_len,
                                        const int32_t* window,
                                        float softmax_scale,
+                                       void* workspace, size_t workspace_bytes,
                                        void* stream);
+
+/* Workspace bytes kvq_paged_prefill_attention needs for these sizes (host
+ * only): 0 for every shape this library builds, since a workgroup owns the
+ * whole key range of its query rows and merges nothing across workgroups.
+ * Validates the same sizes as the prefill call. */
+kvq_status kvq_prefill_workspace_size(const kvq_cache_desc* desc, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_q_len,
+                                      int32_t max_seq_len, size_t* bytes /* host */);
 
 /* Dequantize-gather (the cache-fetch-and-dequantize operator of FastDeploy
  * PR 5173, review thread; the gather-and-dequantize of the paged cache that

@@ -23,6 +23,10 @@ class CacheDesc(ctypes.Structure):
                 ("num_blocks", ctypes.c_int64), ("rot_signs", ctypes.c_void_p)]
 
 
+class DecodeOptions(ctypes.Structure):
+    _fields_ = [("num_workgroups", ctypes.c_int32)]
+
+
 class Layout(ctypes.Structure):
     _fields_ = [("code_bytes", ctypes.c_uint64), ("meta_bytes", ctypes.c_uint64),
                 ("row_code_bytes", ctypes.c_uint32), ("row_meta_floats", ctypes.c_uint32)]
@@ -33,19 +37,21 @@ _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _DESC = ctypes.POINTER(CacheDesc)
+_OPT = ctypes.POINTER(DecodeOptions)
 
 # name -> (restype, argtypes); the symbols include/kvq.h declares
 SIGNATURES = {
     "kvq_query_layout": (_I32, [_DESC, ctypes.POINTER(Layout)]),
     "kvq_reshape_and_cache": (_I32, [_DESC, _P, _P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _P]),
-    "kvq_decode_workspace_size": (_I32, [_DESC, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "kvq_decode_workspace_size": (_I32, [_DESC, _I32, _I32, _I32, _OPT, ctypes.POINTER(_SZ)]),
     "kvq_workspace_init": (_I32, [_P, _SZ, _P]),
     "kvq_paged_decode_attention": (_I32, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                          _I32, _P, _I32, _P, ctypes.c_float, _P, _SZ, _P]),
+                                          _I32, _P, _I32, _P, ctypes.c_float, _OPT, _P, _SZ, _P]),
     "kvq_decode_step": (_I32, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P,
-                               _P, _P, _I32, _P, _I32, _P, ctypes.c_float, _P, _SZ, _P]),
+                               _P, _P, _I32, _P, _I32, _P, ctypes.c_float, _OPT, _P, _SZ, _P]),
     "kvq_paged_prefill_attention": (_I32, [_DESC, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                           _I32, _P, _I32, _P, ctypes.c_float, _P]),
+                                           _I32, _P, _I32, _P, ctypes.c_float, _P, _SZ, _P]),
+    "kvq_prefill_workspace_size": (_I32, [_DESC, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "kvq_gather_dequant": (_I32, [_DESC, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _P]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_version": (_I32, []),

@@ -17,9 +17,10 @@
 //   sum_t w_t v_hat_t = sum_t (p_t s_t) c_t + (sum_t p_t z_t) 1 .
 // q'.c runs on v_mfma_i32_16x16x64_i8: the codes are int8 operands as they
 // are (INT8) or after two or three bit operations per 16 codes (INT4/INT2),
-// and q' is split into two int8 pieces (scale S: q' ~ S (a + b/2^7),
-// |a| <= 127, |b| <= 64, within 2^-15 of max|q'|), so the products
-// accumulate exactly in int32.  sum_t w_t c_t runs on v_mfma_f32_16x16x32_bf16 with the codes as
+// and q' is split into three int8 pieces (scale S: q' ~ S (a + b/2^7 +
+// c/2^14), |a| <= 127, |b|, |c| <= 64, within 2^-22 of max|q'|), so the
+// products accumulate exactly in int32.  Two pieces (2^-15) were measured
+// too coarse for a peaked softmax over x10 outlier channels.  sum_t w_t c_t runs on v_mfma_f32_16x16x32_bf16 with the codes as
 // exact bf16 integers 128 + c (one and-or per two codes) and w split into
 // bf16 hi + lo; one extra MFMA per d-tile, a constant -128 operand against the
 // weight sum in three bf16 pieces, cancels the 128 offset.
@@ -78,6 +79,12 @@ struct Geo {
   static constexpr bool NARROW = VB < 4;
   static constexpr int DT = D / 16;              // V-pass d-tiles
 };
+
+// Bytes between consecutive query-piece planes of the decode LDS (Smem::qp:
+// 32 rows of a batch's (segment, head) pieces plus one zero row, D + 16
+// bytes each).
+template <int D, int PHI>
+constexpr int kQPlane = (32 / (16 / PHI) * (16 / PHI) + 1) * (D + 16);
 
 // d held by byte j (0..15) of the int8 operand of k-step s for lane-group
 // d-range `sub` (K pass); the query pieces in LDS are laid out in this order.
@@ -182,18 +189,19 @@ struct TileInfo {
 };
 
 // CB: block_size >= 64, so a tile lies in one block and its sub-tile rows
-// are row0 + 16 s (one block id per tile; an evicted block reads rows 0..63,
-// which exist because every block slice has at least 64 rows).
+// are row0 + 16 s (one block id per tile).  A block id that is negative
+// (evicted) or at or past num_blocks makes its sub-tiles invalid: no row is
+// formed for them and issue_loads reads nothing for them.
 template <bool CB>
 __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int tile, int te, int L, int start,
-                                              int bs_log2, int hkv, int h) {
+                                              int bs_log2, int hkv, int h, int nblk) {
   TileInfo t;
   t.pos0 = tile * 64;
   t.valid = 0;
   if constexpr (CB) {
     const bool in = tile < te;
     const int id = __builtin_amdgcn_readfirstlane(ids[in ? (t.pos0 >> bs_log2) - blk0 : 0]);
-    const bool okb = in && id >= 0;
+    const bool okb = in && id >= 0 && id < nblk;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int pos = t.pos0 + 16 * s;
@@ -209,7 +217,7 @@ __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int 
     const int pos = t.pos0 + 16 * s;
     const bool in = tile < te && pos < L && pos + 15 >= start;
     const int id = __builtin_amdgcn_readfirstlane(ids[in ? (pos >> bs_log2) - blk0 : 0]);
-    const bool ok = in && id >= 0;
+    const bool ok = in && id >= 0 && id < nblk;
     t.valid |= ok ? 1u << s : 0u;
     row[s] = ok ? ((id * hkv + h) << bs_log2) + (pos & ((1 << bs_log2) - 1)) : 0;
   }
@@ -217,9 +225,8 @@ __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int 
   return t;
 }
 
-// Row of sub-tile sigma (sigma may differ per lane).  An invalid sub-tile
-// reads row 0, which is always addressable; its data is masked out of the
-// scores and gets zero weight.
+// Row of sub-tile sigma (sigma may differ per lane); 0 for an invalid
+// sub-tile, whose loads are not issued.
 __device__ __forceinline__ int pick_row(const TileInfo& t, int sigma) {
   return sigma == 0 ? t.row0 : (sigma == 1 ? t.row1 : (sigma == 2 ? t.row2 : t.row3));
 }
@@ -240,7 +247,12 @@ __device__ __forceinline__ void issue_loads(Buf<MODE, D, PHI>& b, const TileInfo
   constexpr int P = Gm::P, M = Gm::M;
   const int phi_grp = q * PHI / 4;          // phase of this lane group (K pass)
   const int sub = q % (4 / PHI);            // d-range of this lane group (K pass)
+  // An invalid sub-tile (evicted block, id out of range, or wholly outside
+  // [start, L)) is not read: its registers keep whatever they held, which the
+  // compute masks (score -inf, weight and V meta zero) and never lets reach a
+  // result, since the codes are integers and every use is a select.
   if constexpr (CB) {
+    if (t.valid == 0) return;   // one block per tile: all four sub-tiles or none
     // uniform tile bases (scalar) + per-lane constant 32-bit offsets
     const uint8_t* kb = p.k_codes + (int64_t)t.row0 * P;
     const uint8_t* vb = p.v_codes + (int64_t)t.row0 * P;
@@ -268,20 +280,27 @@ __device__ __forceinline__ void issue_loads(Buf<MODE, D, PHI>& b, const TileInfo
   }
 #pragma unroll
   for (int tau = 0; tau < Gm::NKT; ++tau) {
-    const int kr = pick_row(t, tau * PHI + phi_grp) + r;
-    load_bytes<Gm::KB>(b.k[tau], p.k_codes + (int64_t)kr * P + sub * Gm::KB);
-    const int mr = pick_row(t, tau * PHI + phi_col) + 4 * q;
+    const int sk = tau * PHI + phi_grp;     // per lane group
+    if ((t.valid >> sk) & 1u) {
+      const int kr = pick_row(t, sk) + r;
+      load_bytes<Gm::KB>(b.k[tau], p.k_codes + (int64_t)kr * P + sub * Gm::KB);
+    }
+    const int sm = tau * PHI + phi_col;     // per lane
+    if ((t.valid >> sm) & 1u) {
+      const int mr = pick_row(t, sm) + 4 * q;
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const float4 a = reinterpret_cast<const float4*>(p.k_meta + (int64_t)mr * M)[i];
-      const float4 c = reinterpret_cast<const float4*>(p.v_meta + (int64_t)mr * M)[i];
-      b.km[tau][4 * i] = a.x; b.km[tau][4 * i + 1] = a.y; b.km[tau][4 * i + 2] = a.z; b.km[tau][4 * i + 3] = a.w;
-      b.vm[tau][4 * i] = c.x; b.vm[tau][4 * i + 1] = c.y; b.vm[tau][4 * i + 2] = c.z; b.vm[tau][4 * i + 3] = c.w;
+      for (int i = 0; i < M; ++i) {
+        const float4 a = reinterpret_cast<const float4*>(p.k_meta + (int64_t)mr * M)[i];
+        const float4 c = reinterpret_cast<const float4*>(p.v_meta + (int64_t)mr * M)[i];
+        b.km[tau][4 * i] = a.x; b.km[tau][4 * i + 1] = a.y; b.km[tau][4 * i + 2] = a.z; b.km[tau][4 * i + 3] = a.w;
+        b.vm[tau][4 * i] = c.x; b.vm[tau][4 * i + 1] = c.y; b.vm[tau][4 * i + 2] = c.z; b.vm[tau][4 * i + 3] = c.w;
+      }
     }
   }
   const int voff = 4 * q * P + ((r * Gm::VB) & ~3);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
+    if (!((t.valid >> s) & 1u)) continue;   // wave-uniform
     const int row = s == 0 ? t.row0 : (s == 1 ? t.row1 : (s == 2 ? t.row2 : t.row3));
     const uint8_t* base = p.v_codes + (int64_t)row * P;
 #pragma unroll
@@ -296,10 +315,10 @@ struct WaveState {
 };
 
 struct LaneConst {
-  const int8_t* qa;    // query pieces of this lane's B operand rows (LDS)
-  const int8_t* qb;
+  const int8_t* qa;    // query piece a of this lane's B operand row (LDS); pieces b
+                       // and c sit kQPlane and 2 kQPlane bytes further
   float sp;            // log2 logit per unit of x (S/128 of the column's head)
-  float q1r;           // sum of the column head's pieces, 128 a + b
+  float q1r;           // sum of the column head's pieces, 2^14 a + 2^7 b + c
   int q;
   int phi_col;
   bool head_ok;
@@ -315,23 +334,28 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
   using Gm = Geo<MODE, D, PHI>;
   constexpr int M = Gm::M;
   const int q = lc.q, phi_col = lc.phi_col;
-  // ---- K pass: int32 (a, b) dot products of the query pieces with the codes;
-  // x = s_K (128 a + b).c + z_K q1r, the log2 logit being sp * x
+  // ---- K pass: int32 (a, b, c) dot products of the query pieces with the
+  // codes; x = s_K (2^14 a + 2^7 b + c).code + z_K q1r, the log2 logit
+  // being sp * x
   float sc[Gm::NKT][4];
 #pragma unroll
   for (int tau = 0; tau < Gm::NKT; ++tau) {
-    i32x4_t ia = {0, 0, 0, 0}, ib = {0, 0, 0, 0};
+    i32x4_t ia = {0, 0, 0, 0}, ib = {0, 0, 0, 0}, ic = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < Gm::KS; ++s) {
       const u32x4_t a = unpack_k<MODE, Gm::KSW>(b.k[tau], s, 0x0F0F0F0Fu, 0x03030303u);
+      // one address, three immediate offsets
       const uint4 xa = *reinterpret_cast<const uint4*>(lc.qa + 16 * s);
-      const uint4 xb = *reinterpret_cast<const uint4*>(lc.qb + 16 * s);
+      const uint4 xb = *reinterpret_cast<const uint4*>(lc.qa + kQPlane<D, PHI> + 16 * s);
+      const uint4 xc = *reinterpret_cast<const uint4*>(lc.qa + 2 * kQPlane<D, PHI> + 16 * s);
       ia = mfma_i8(a, u32x4_t{xa.x, xa.y, xa.z, xa.w}, ia);
       ib = mfma_i8(a, u32x4_t{xb.x, xb.y, xb.z, xb.w}, ib);
+      ic = mfma_i8(a, u32x4_t{xc.x, xc.y, xc.z, xc.w}, ic);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float raw = (float)((ia[i] << 7) + ib[i]);
+      // 2^7 a + b is exact in int32 (|.| < 2^29); one rounding joins c
+      const float raw = __builtin_fmaf((float)((ia[i] << 7) + ib[i]), 128.0f, (float)ic[i]);
       const float s = M == 2 ? b.km[tau][2 * i] : b.km[tau][i];
       const float z = M == 2 ? b.km[tau][2 * i + 1] : 0.0f;
       sc[tau][i] = __builtin_fmaf(raw, s, z * lc.q1r);
@@ -472,7 +496,7 @@ constexpr int decode_waves_per_simd() {
 
 // Waves per workgroup.  INT4 and INT2: all of a CU's waves in one
 // workgroup (one per SIMD per round), so no two workgroups on a CU compete
-// and the waves of a SIMD take turns at the top priority; INT8, whose tiles
+// for issue; INT8, whose tiles
 // are the heaviest in bytes: four-wave workgroups, several per CU, so one
 // workgroup's segment barriers and prologue overlap another's loads
 // (measured faster for each).
@@ -512,13 +536,14 @@ __device__ __forceinline__ uint32_t load_qrow(const uint16_t* src, int lane) {
   else return src[lane];
 }
 
-// One query row: q' = R q * scale * log2(e), then its two int8 pieces in
-// k-slot order (q' ~ (S/128)(128 a + b), S = max|q'|/127, |a| <= 127,
-// |b| <= 64), sp = S/128 and q1r = sum(128 a + b).  `scratch` is the wave's
-// own D floats of LDS (written and read back by the same wave, in order).
+// One query row: q' = R q * scale * log2(e), then its three int8 pieces in
+// k-slot order (q' ~ (S/2^14)(2^14 a + 2^7 b + c), S = max|q'|/127,
+// |a| <= 127, |b|, |c| <= 64), sp = S/2^14 and q1r = sum(2^14 a + 2^7 b + c).
+// `scratch` is the wave's own D floats of LDS (written and read back by the
+// same wave, in order).
 template <int MODE, int D, int PHI, bool ROT>
 __device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, float* scratch, int8_t* qa,
-                                           int8_t* qb, float* qs, float* q1, int lane) {
+                                           int8_t* qb, int8_t* qc, float* qs, float* q1, int lane) {
   using Gm = Geo<MODE, D, PHI>;
   constexpr int E = D / 64;
   float x[E];
@@ -552,15 +577,18 @@ __device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, 
     const float v = scratch[kmap<MODE, D, PHI>(sub, rem >> 4, rem & 15)];
     const float t = fminf(fmaxf(v * invS, -127.0f), 127.0f);
     const float a = __builtin_rintf(t);
-    const float bq = __builtin_rintf((t - a) * 128.0f);
+    const float r1 = (t - a) * 128.0f;          // exact, |r1| <= 64
+    const float bq = __builtin_rintf(r1);
+    const float cq = __builtin_rintf((r1 - bq) * 128.0f);
     qa[pos] = (int8_t)a;
     qb[pos] = (int8_t)bq;
-    sab += 128.0f * a + bq;           // exact: |sum| < 2^24
+    qc[pos] = (int8_t)cq;
+    sab += __builtin_fmaf(16384.0f, a, __builtin_fmaf(128.0f, bq, cq));   // each term exact (< 2^22)
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) sab += __shfl_xor(sab, m);
   if (lane == 0) {
-    *qs = mx > 0.0f ? (mx / 127.0f) * 0.0078125f : 1.0f;
+    *qs = mx > 0.0f ? (mx / 127.0f) * 6.103515625e-05f : 1.0f;   // S / 2^14
     *q1 = sab;
   }
 }
@@ -608,11 +636,13 @@ struct Smem {
   static constexpr int GM = 16 / PHI;   // most heads of a kv head's group (G * PHI <= 16)
   static constexpr int NS = 32 / GM;    // segments of one batch (their pieces stay in LDS)
   static constexpr int QW = D + 16;     // piece row stride: 16 bytes of padding spread banks
-  alignas(16) int8_t qa[NS][GM][QW];    // query pieces in k-slot order
-  alignas(16) int8_t qb[NS][GM][QW];
-  alignas(16) int8_t qzero[QW];         // B rows of columns without work
-  float qs[NS][GM];                     // sp: (max|q'| / 127) / 128
-  float q1[NS][GM];                     // q1r: sum over d of 128 a + b
+  // query pieces a, b, c in k-slot order: piece p of row (segment k, head
+  // g) at qp[p][k GM + g]; row NS GM of every piece is zero (the B rows of
+  // columns without work)
+  alignas(16) int8_t qp[3][NS * GM + 1][QW];
+  static_assert(sizeof(qp[0]) == (size_t)kQPlane<D, PHI>, "query plane stride");
+  float qs[NS][GM];                     // sp: (max|q'| / 127) / 2^14
+  float q1[NS][GM];                     // q1r: sum over d of 2^14 a + 2^7 b + c
   SegRec seg[NS];
   int32_t ids[kMaxSplitBlocks];         // block ids of the batch's segments
   union {
@@ -637,7 +667,7 @@ struct Smem {
 // (or 0) to seq_len; *t0 = first tile, *L = attended end, *start = begin.
 __device__ __forceinline__ int pair_geo(const DecodeParams& p, int pair, int* t0, int* L, int* start) {
   const int b = pair / p.hkv, h = pair - b * p.hkv;
-  const int l = min(p.seq_lens[b], p.max_blocks << p.block_size_log2);
+  const int l = min(p.seq_lens[b], p.max_seq_len);   // host checked max_seq_len <= max_blocks * bs
   const int W = p.window ? p.window[h] : 0;
   const int s = (W > 0 && l > W) ? l - W : 0;
   *t0 = s / 64;
@@ -661,21 +691,6 @@ struct Part {
     return lo;
   }
 };
-
-// Wave priority for the rounds of a persistent grid: with several
-// workgroups per CU (dispatch rounds of ncu workgroups), the SIMDs' issue
-// arbitration favours the oldest waves, so the last round's shares would
-// finish well after the first's.  Instead, while streaming tiles, each
-// wave's priority rotates (0, 1, 2, ... per tile pair), offset by its round,
-// so the rounds take turns at the top; the short latency-bound phases
-// (prologue, segment epilogues, merging) run at priority 3, above any
-// streaming wave, so they never wait behind another workgroup's tiles.
-__device__ __forceinline__ void set_prio(int k) {
-  if (k == 0) __builtin_amdgcn_s_setprio(0);
-  else if (k == 1) __builtin_amdgcn_s_setprio(1);
-  else if (k == 2) __builtin_amdgcn_s_setprio(2);
-  else __builtin_amdgcn_s_setprio(3);
-}
 
 // Workgroups in the partition: never more than tiles.
 __device__ __forceinline__ int active_wgs(int grid, int T) { return max(1, min(grid, T)); }
@@ -716,13 +731,13 @@ __device__ __forceinline__ void cursor_seek(Cursor& c, const Smem<D, PHI, NWV>& 
 
 template <bool CB, int D, int PHI, int NWV>
 __device__ __forceinline__ TileInfo cursor_info(const Cursor& c, const Smem<D, PHI, NWV>& sm, int wave, int bl,
-                                                int hkv) {
+                                                int hkv, int nblk) {
   if (c.ls >= c.nseg) {
     TileInfo t;
     t.pos0 = 0; t.row0 = 0; t.row1 = 0; t.row2 = 0; t.row3 = 0; t.valid = 0;
     return t;
   }
-  return tile_info<CB>(sm.ids + c.off, c.blk0, c.tb + wave + NWV * c.li, c.te, c.L, c.start, bl, hkv, c.h);
+  return tile_info<CB>(sm.ids + c.off, c.blk0, c.tb + wave + NWV * c.li, c.te, c.L, c.start, bl, hkv, c.h, nblk);
 }
 
 template <int D, int PHI, int NWV>
@@ -906,12 +921,11 @@ void decode_kernel(DecodeParams p) {
   const int lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = p.num_pairs, G = p.group, hkv = p.hkv, bl = p.block_size_log2;
+  const int nblk = (int)p.num_blocks;   // < 2^31 (checked on the host)
   const int w = blockIdx.x;
 
-  if (p.prio_rot) set_prio(3);
-
   // ---- tile prefix of the first chunk of pairs; total tiles
-  for (int i = tid; i < Sm::QW; i += NT) sm.qzero[i] = 0;
+  for (int i = tid; i < 3 * Sm::QW; i += NT) sm.qp[i / Sm::QW][NS * Sm::GM][i % Sm::QW] = 0;
   int cn = min(kPrefChunk, P);
   int ctot = scan_chunk<NWV>(p, sm.pref, sm.plen, sm.pst, sm.part, 0, cn, tid);
   int T = ctot;
@@ -968,11 +982,6 @@ void decode_kernel(DecodeParams p) {
   int x = part.start(w);  // next tile of the share
   int ci = first_after(sm.pref, cn, cbase, x);
   int npend = 0;
-  // rotating wave priority (see set_prio)
-  // (rounds: the workgroup's own waves per SIMD, waves i, i + 4, ... sharing
-  // SIMD i % 4, or else the grid's dispatch rounds)
-  const int prio_rounds = !p.prio_rot ? 1 : (NWV > 4 ? NWV / 4 : min(3, (int)(gridDim.x / p.ncu)));
-  int prio_phase = prio_rounds > 1 ? (NWV > 4 ? wave / 4 : w / p.ncu) % prio_rounds : 0;
 
   while (x < e_my) {
     // ---- a batch: up to NS segments whose block ids fit the LDS table
@@ -1105,9 +1114,9 @@ void decode_kernel(DecodeParams p) {
       const int b0 = __builtin_amdgcn_readfirstlane(sm.seg[cur.ls].b);
       const int32_t* trow = p.tables + (int64_t)(p.headwise ? b0 * hkv + cur.h : b0) * p.max_blocks;
       ta = tile_info<CB>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te, cur.L, cur.start, bl,
-                         hkv, cur.h);
+                         hkv, cur.h, nblk);
     } else {
-      ta = cursor_info<CB>(cur, sm, wave, bl, hkv);
+      ta = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk);
     }
     cursor_next(cur, sm, wave);
     // the ids and query rows are back (the table read above waited for all
@@ -1154,7 +1163,8 @@ void decode_kernel(DecodeParams p) {
       const int rr = wave + i * NWV;
       if (rr < nseg * G) {
         const int k = rr / G, g = rr - k * G;
-        prep_query<MODE, D, PHI, ROT>(p, raw[i], sm.qrow[wave], sm.qa[k][g], sm.qb[k][g], &sm.qs[k][g],
+        prep_query<MODE, D, PHI, ROT>(p, raw[i], sm.qrow[wave], sm.qp[0][k * Sm::GM + g], sm.qp[1][k * Sm::GM + g],
+                                      sm.qp[2][k * Sm::GM + g], &sm.qs[k][g],
                                       &sm.q1[k][g], plane);
       }
     }
@@ -1172,8 +1182,7 @@ void decode_kernel(DecodeParams p) {
       lc.phi_col = phi_col;
       lc.head_ok = g_col < G;
       const bool brow = lc.head_ok && phi_grp == phi_col;
-      lc.qa = brow ? &sm.qa[k][g_col][sub * Gm::SUBD] : &sm.qzero[sub * Gm::SUBD];
-      lc.qb = brow ? &sm.qb[k][g_col][sub * Gm::SUBD] : &sm.qzero[sub * Gm::SUBD];
+      lc.qa = &sm.qp[0][brow ? k * Sm::GM + g_col : NS * Sm::GM][sub * Gm::SUBD];
       lc.sp = lc.head_ok ? sm.qs[k][g_col] : 1.0f;
       lc.q1r = lc.head_ok ? sm.q1[k][g_col] : 0.0f;
       lc.magic = magic;
@@ -1187,22 +1196,16 @@ void decode_kernel(DecodeParams p) {
       for (int i = 0; i < Gm::DT; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
       for (int it = 0; it < n2; it += 2) {
-        if (prio_rounds > 1) {
-          set_prio(prio_phase);
-          prio_phase = prio_phase + 1 == prio_rounds ? 0 : prio_phase + 1;
-        }
-        const TileInfo tn = cursor_info<CB>(cur, sm, wave, bl, hkv);
+        const TileInfo tn = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk);
         cursor_next(cur, sm, wave);
         issue_loads<MODE, D, PHI, CB>(bb, tn, p, r, q, phi_col);
         run_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
-        const TileInfo t2 = cursor_info<CB>(cur, sm, wave, bl, hkv);
+        const TileInfo t2 = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk);
         cursor_next(cur, sm, wave);
         issue_loads<MODE, D, PHI, CB>(ba, t2, p, r, q, phi_col);
         run_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
         ta = t2;
       }
-
-      if (prio_rounds > 1) set_prio(3);
 
       // ---- segment epilogue: sum the phases of a head, then l and z over
       // lane groups; combine the waves in LDS

@@ -11,7 +11,6 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 
 #include "kvq.h"
@@ -77,11 +76,6 @@ int num_cus() {
   return n;
 }
 
-int env_flag(const char* name, int dflt) {
-  const char* e = std::getenv(name);
-  return e ? std::atoi(e) : dflt;
-}
-
 struct DecodePlan {
   int n_wgs;
   size_t counter_bytes;
@@ -92,22 +86,20 @@ struct DecodePlan {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Stream-K plan: a persistent grid of as many workgroups as fit on the
-// MI355X at once (256 CUs times the variant's resident workgroups per CU)
-// shares all pairs' tiles equally; more workgroups only when a
-// share could span more blocks than one segment's LDS table holds.  The
-// workspace holds one piece counter per pair (zero between calls) and one
-// (m, l, acc) record per (piece, head): at most n_wgs + pairs pieces.
+// MI355X at once (256 CUs times the variant's resident workgroups per CU),
+// or the caller's count, shares all pairs' tiles equally; more workgroups
+// only when a share could span more blocks than one segment's LDS table
+// holds.  The workspace holds one piece counter per pair (zero between calls)
+// and one (m, l, acc) record per (piece, head): at most n_wgs + pairs pieces.
 // Deterministic in its inputs.
-DecodePlan plan_decode(const kvq_cache_desc* d, int num_seqs, int num_q_heads, int max_seq_len) {
+DecodePlan plan_decode(const kvq_cache_desc* d, int num_seqs, int num_q_heads, int max_seq_len,
+                       const kvq_decode_options* opt) {
   DecodePlan pl{};
   const long long max_tiles = (max_seq_len + kvq::kTile - 1) / kvq::kTile;
   const long long pairs = (long long)num_seqs * d->num_kv_heads;
   const long long seg_cap = ((long long)(kvq::kMaxSplitBlocks - 1) * d->block_size) / kvq::kTile - 1;
   long long nw = (long long)num_cus() * kvq::decode_wgs_per_cu(d->mode, d->head_dim, num_q_heads / d->num_kv_heads);
-  if (const char* e = std::getenv("KVQ_DECODE_WGS")) {
-    const long long t = std::atoll(e);
-    if (t > 0) nw = t;
-  }
+  if (opt && opt->num_workgroups > 0) nw = opt->num_workgroups;
   const long long need = (pairs * max_tiles + seg_cap - 1) / seg_cap + 1;
   if (nw < need) nw = need;
   pl.n_wgs = (int)nw;
@@ -115,6 +107,14 @@ DecodePlan plan_decode(const kvq_cache_desc* d, int num_seqs, int num_q_heads, i
   pl.counter_bytes = round_up((size_t)pairs * sizeof(int32_t), 256);
   pl.partial_bytes = round_up((size_t)(nw + pairs) * G * (d->head_dim + 4) * sizeof(float), 256);
   return pl;
+}
+
+kvq_status check_options(const kvq_decode_options* opt) {
+  if (opt && opt->num_workgroups < 0)
+    return fail(KVQ_EINVAL, "options->num_workgroups %d < 0", opt->num_workgroups);
+  if (opt && opt->num_workgroups > (1 << 20))
+    return fail(KVQ_EUNSUPPORTED, "options->num_workgroups %d > 2^20", opt->num_workgroups);
+  return KVQ_OK;
 }
 
 kvq_status check_decode_sizes(const kvq_cache_desc* d, int num_seqs, int num_q_heads, int max_seq_len) {
@@ -141,11 +141,14 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
                                       const int32_t* block_tables, const int32_t* block_tables_headwise,
                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
                                       int32_t max_seq_len, const int32_t* window, float softmax_scale,
+                                      const kvq_decode_options* options,
                                       void* workspace, size_t workspace_bytes, void* stream,
                                       const kvq::WriteParams* wp) {
   kvq_status st = check_desc(desc);
   if (st != KVQ_OK) return st;
   st = check_decode_sizes(desc, num_seqs, num_q_heads, max_seq_len);
+  if (st != KVQ_OK) return st;
+  st = check_options(options);
   if (st != KVQ_OK) return st;
   if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16)
     return fail(KVQ_EINVAL, "out_dtype %d is not a kvq_out_dtype", out_dtype);
@@ -161,7 +164,7 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
   if (!aligned(out, 16)) return fail(KVQ_EINVAL, "out must be 16-byte aligned");
   st = check_planes(k_codes, k_meta, v_codes, v_meta);
   if (st != KVQ_OK) return st;
-  const DecodePlan pl = plan_decode(desc, num_seqs, num_q_heads, max_seq_len);
+  const DecodePlan pl = plan_decode(desc, num_seqs, num_q_heads, max_seq_len, options);
   if (!workspace) return fail(KVQ_EINVAL, "workspace is NULL (%zu bytes needed)", pl.total());
   if (workspace_bytes < pl.total())
     return fail(KVQ_ENOSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total());
@@ -182,7 +185,9 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
   p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counter_bytes);
   p.qscale = softmax_scale * 1.4426950408889634f;
   p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
+  p.num_blocks = desc->num_blocks;
   p.max_blocks = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
   p.block_size = desc->block_size;
   p.block_size_log2 = __builtin_ctz((unsigned)desc->block_size);
   p.hq = num_q_heads;
@@ -190,8 +195,6 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
   p.group = num_q_heads / desc->num_kv_heads;
   p.num_pairs = num_seqs * desc->num_kv_heads;
   p.n_wgs = pl.n_wgs;
-  p.ncu = num_cus();
-  p.prio_rot = env_flag("KVQ_DECODE_PRIO", 0);
   p.out_bf16 = out_dtype == KVQ_OUT_BF16;
   p.bits_magic = 0x43004300u;
   p.bits_n4 = 0x000F000Fu;
@@ -205,6 +208,7 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
     p.wp.v_meta = const_cast<float*>(v_meta);
     p.wp.hkv = desc->num_kv_heads;
     p.wp.block_size = desc->block_size;
+    p.wp.slot_cap = desc->num_blocks * desc->block_size;
     p.wp.signs = desc->rot_signs;
     p.wp.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
     p.wp.total_rows = 2 * (int64_t)num_seqs * desc->num_kv_heads;
@@ -213,6 +217,25 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_EHIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+kvq_status check_prefill_sizes(const kvq_cache_desc* desc, int num_seqs, int num_q_heads, int max_q_len,
+                               int max_seq_len) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (num_seqs < 0) return fail(KVQ_EINVAL, "num_seqs %d < 0", num_seqs);
+  if (num_q_heads < 1) return fail(KVQ_EINVAL, "num_q_heads %d < 1", num_q_heads);
+  if (num_q_heads % desc->num_kv_heads != 0)
+    return fail(KVQ_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                desc->num_kv_heads);
+  const int group = num_q_heads / desc->num_kv_heads;
+  if (group > 128) return fail(KVQ_EUNSUPPORTED, "GQA group %d > 128 is not built", group);
+  if (max_q_len < 0) return fail(KVQ_EINVAL, "max_q_len %d < 0", max_q_len);
+  if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len %d < 0", max_seq_len);
+  const int tq = 128 / group;
+  const long long n_work = (((long long)max_q_len + tq - 1) / tq) * desc->num_kv_heads * (long long)num_seqs;
+  if (n_work > 0x7fffff00LL) return fail(KVQ_EUNSUPPORTED, "prefill grid of %lld workgroups", n_work);
+  return KVQ_OK;
 }
 
 }  // namespace
@@ -263,6 +286,7 @@ kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc, const void* key, co
   p.slot = slot_mapping;
   p.slot_hw = slot_mapping_headwise;
   p.total_rows = 2 * (int64_t)num_tokens * H;
+  p.slot_cap = desc->num_blocks * desc->block_size;
   p.hkv = H;
   p.block_size = desc->block_size;
   p.k_codes = k_codes;
@@ -278,13 +302,15 @@ kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc, const void* key, co
 }
 
 kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t num_seqs, int32_t num_q_heads,
-                                     int32_t max_seq_len, size_t* bytes) {
+                                     int32_t max_seq_len, const kvq_decode_options* options, size_t* bytes) {
   kvq_status st = check_desc(desc);
   if (st != KVQ_OK) return st;
   st = check_decode_sizes(desc, num_seqs, num_q_heads, max_seq_len);
   if (st != KVQ_OK) return st;
+  st = check_options(options);
+  if (st != KVQ_OK) return st;
   if (!bytes) return fail(KVQ_EINVAL, "bytes is NULL");
-  *bytes = plan_decode(desc, num_seqs, num_q_heads, max_seq_len).total();
+  *bytes = plan_decode(desc, num_seqs, num_q_heads, max_seq_len, options).total();
   return ok();
 }
 
@@ -305,10 +331,11 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
                                       const int32_t* block_tables, const int32_t* block_tables_headwise,
                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
                                       int32_t max_seq_len, const int32_t* window, float softmax_scale,
+                                      const kvq_decode_options* options,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(desc, out, out_dtype, query, num_seqs, num_q_heads, k_codes, k_meta, v_codes, v_meta,
                      block_tables, block_tables_headwise, max_blocks_per_seq, seq_lens, max_seq_len, window,
-                     softmax_scale, workspace, workspace_bytes, stream, nullptr);
+                     softmax_scale, options, workspace, workspace_bytes, stream, nullptr);
 }
 
 kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* out, int32_t out_dtype, const void* query,
@@ -318,7 +345,8 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* out, int32_t out_dt
                            uint8_t* v_codes, float* v_meta, const int32_t* block_tables,
                            const int32_t* block_tables_headwise, int32_t max_blocks_per_seq,
                            const int32_t* seq_lens, int32_t max_seq_len, const int32_t* window,
-                           float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                           float softmax_scale, const kvq_decode_options* options, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   kvq_status st = check_desc(desc);
   if (st != KVQ_OK) return st;
   if (num_seqs > 0) {
@@ -341,7 +369,7 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* out, int32_t out_dt
   w.slot_hw = slot_mapping_headwise;
   return decode_impl(desc, out, out_dtype, query, num_seqs, num_q_heads, k_codes, k_meta, v_codes, v_meta,
                      block_tables, block_tables_headwise, max_blocks_per_seq, seq_lens, max_seq_len, window,
-                     softmax_scale, workspace, workspace_bytes, stream, &w);
+                     softmax_scale, options, workspace, workspace_bytes, stream, &w);
 }
 
 kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
@@ -352,18 +380,10 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
                                        const int32_t* block_tables, const int32_t* block_tables_headwise,
                                        int32_t max_blocks_per_seq, const int32_t* seq_lens,
                                        int32_t max_seq_len, const int32_t* window, float softmax_scale,
-                                       void* stream) {
-  kvq_status st = check_desc(desc);
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  kvq_status st = check_prefill_sizes(desc, num_seqs, num_q_heads, max_q_len, max_seq_len);
   if (st != KVQ_OK) return st;
-  if (num_seqs < 0) return fail(KVQ_EINVAL, "num_seqs %d < 0", num_seqs);
-  if (num_q_heads < 1) return fail(KVQ_EINVAL, "num_q_heads %d < 1", num_q_heads);
-  if (num_q_heads % desc->num_kv_heads != 0)
-    return fail(KVQ_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
-                desc->num_kv_heads);
   const int group = num_q_heads / desc->num_kv_heads;
-  if (group > 128) return fail(KVQ_EUNSUPPORTED, "GQA group %d > 128 is not built", group);
-  if (max_q_len < 0) return fail(KVQ_EINVAL, "max_q_len %d < 0", max_q_len);
-  if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len %d < 0", max_seq_len);
   if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16)
     return fail(KVQ_EINVAL, "out_dtype %d is not a kvq_out_dtype", out_dtype);
   if ((block_tables == nullptr) == (block_tables_headwise == nullptr))
@@ -373,6 +393,10 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
     return fail(KVQ_EINVAL, "max_seq_len %d exceeds max_blocks_per_seq*block_size = %lld", max_seq_len,
                 (long long)max_blocks_per_seq * desc->block_size);
   if (!std::isfinite(softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is not finite");
+  // no shape this library builds needs a prefill workspace (the size query
+  // returns 0), so any workspace, NULL included, is enough
+  (void)workspace;
+  (void)workspace_bytes;
   if (num_seqs == 0 || max_q_len == 0) return ok();
   if (!out || !query || !cu_seqlens_q || !seq_lens)
     return fail(KVQ_EINVAL, "out, query, cu_seqlens_q or seq_lens is NULL");
@@ -381,7 +405,6 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
   const int tq = 128 / group;
   const long long n_qtiles = ((long long)max_q_len + tq - 1) / tq;
   const long long n_work = n_qtiles * desc->num_kv_heads * (long long)num_seqs;
-  if (n_work > 0x7fffff00LL) return fail(KVQ_EUNSUPPORTED, "prefill grid of %lld workgroups", n_work);
   kvq::PrefillParams p{};
   p.k_codes = k_codes;
   p.k_meta = k_meta;
@@ -397,7 +420,9 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
   p.signs = desc->rot_signs;
   p.qscale = softmax_scale * 1.4426950408889634f;
   p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
+  p.num_blocks = desc->num_blocks;
   p.max_blocks = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
   p.block_size_log2 = __builtin_ctz((unsigned)desc->block_size);
   p.hq = num_q_heads;
   p.hkv = desc->num_kv_heads;
@@ -409,6 +434,15 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
   hipError_t e = kvq::launch_prefill(desc->mode, desc->head_dim, desc->rot_signs != nullptr, p,
                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_EHIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvq_status kvq_prefill_workspace_size(const kvq_cache_desc* desc, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t max_q_len, int32_t max_seq_len, size_t* bytes) {
+  kvq_status st = check_prefill_sizes(desc, num_seqs, num_q_heads, max_q_len, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (!bytes) return fail(KVQ_EINVAL, "bytes is NULL");
+  *bytes = 0;
   return ok();
 }
 

@@ -29,6 +29,7 @@ struct WriteParams {
   const int64_t* slot;      // [T] or nullptr
   const int64_t* slot_hw;   // [T, Hkv] or nullptr
   int64_t total_rows;       // 2 * T * Hkv
+  int64_t slot_cap;         // num_blocks * block_size: slots at or past it are skipped
   int32_t hkv;
   int32_t block_size;
   uint8_t* k_codes;
@@ -54,8 +55,10 @@ struct DecodeParams {
   int32_t* counters;            // [num_pairs] pieces counted in; zero between calls
   float qscale;                 // softmax_scale * log2(e)
   float inv_sqrt_d;
+  int64_t num_blocks;           // ids at or past it are treated as evicted
   int32_t headwise;
   int32_t max_blocks;
+  int32_t max_seq_len;          // seq_lens entries are clamped to it
   int32_t block_size;
   int32_t block_size_log2;
   int32_t hq;
@@ -63,8 +66,6 @@ struct DecodeParams {
   int32_t group;                // Hq / Hkv
   int32_t num_pairs;            // B * Hkv
   int32_t n_wgs;                // persistent decode workgroups
-  int32_t ncu;                  // compute units (workgroups of one dispatch round)
-  int32_t prio_rot;             // 1: dispatch rounds take turns at the top wave priority
   int32_t out_bf16;
   uint32_t bits_magic;          // 0x43004300: bf16 128.0 in both halves
   uint32_t bits_n4;             // 0x000F000F
@@ -87,8 +88,10 @@ struct PrefillParams {
   const float* signs;           // [D] or nullptr
   float qscale;                 // softmax_scale * log2(e)
   float inv_sqrt_d;
+  int64_t num_blocks;           // ids at or past it are treated as evicted
   int32_t headwise;
   int32_t max_blocks;
+  int32_t max_seq_len;          // seq_lens entries are clamped to it
   int32_t block_size_log2;
   int32_t hq;
   int32_t hkv;

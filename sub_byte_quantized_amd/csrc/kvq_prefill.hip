@@ -31,8 +31,8 @@
 //   S^T = K Q^T on v_mfma_i32_16x16x64_i8
 //     A  codes [16 positions x 64 k] from LDS, position 16 kb + r
 //     B  query pieces [64 k x 16 rows] in registers; q' * scale * log2(e) is
-//        split into two int8 pieces (q' ~ S (a + b / 2^7), |a| <= 127,
-//        |b| <= 64) that accumulate exactly in int32
+//        split into three int8 pieces (q' ~ S (a + b / 2^7 + c / 2^14),
+//        |a| <= 127, |b|, |c| <= 64) that accumulate exactly in int32
 //     C  lane (row r, positions 16 kb + 4 q + i)
 //   O += W V on v_mfma_f32_16x16x32_bf16, W = p * s_V as bf16 hi + lo
 //     A  W [16 rows x 32 positions]: the C registers of two key blocks
@@ -102,7 +102,7 @@ struct PSmem {
     PBuf<MODE, D> buf[2];
   };
   float rs[kPRows];                  // max |q' * scale * log2(e)| of each row
-  float r1[kPRows];                  // sum of the row's represented q'
+  float r1[kPRows];                  // sum over d of the row's 2^14 a + 2^7 b + c
 };
 
 // Registers a staging thread carries from the global loads to the LDS stores.
@@ -115,46 +115,53 @@ struct Stage {
   int ok;
 };
 
+// Plane row of position j (<= khi) of the walked table row, or -1 when the
+// position is absent: past khi, in an evicted (-1) block, or in a block id at
+// or past num_blocks.
 __device__ __forceinline__ int plane_row(const int32_t* trow, int j, int khi, int bs_log2, int hkv, int h,
-                                         int* ok) {
+                                         int nblk) {
   int id = -1;
   if (j <= khi) id = trow[j >> bs_log2];
-  *ok = id >= 0;
-  return id >= 0 ? ((id * hkv + h) << bs_log2) + (j & ((1 << bs_log2) - 1)) : 0;
+  return (id >= 0 && id < nblk) ? ((id * hkv + h) << bs_log2) + (j & ((1 << bs_log2) - 1)) : -1;
 }
 
 // Global loads of key tile `tau` into registers.  Thread t stages K codes of
 // position t / 4, d-chunk t % 4 (and the meta of the position when t % 4 ==
 // 0) and V codes of positions 4 (t % 16) .. +3, d = DPT (t / 16) .. +DPT-1.
-// A position that is absent (evicted block, past the range) reads row 0,
-// which always exists; it is masked by `ok`.
+// An absent position is not read: its codes stage as zeros and `ok` masks it
+// (score -inf, weight 0).
 template <int MODE, int D>
 __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillParams& p, const int32_t* trow,
                                            int tau, int khi, int h, int tid) {
   using Gp = PGeo<MODE, D>;
   const int n = tid >> 2, qd = tid & 3;
-  int ok;
-  const int row = plane_row(trow, tau * kPKeys + n, khi, p.block_size_log2, p.hkv, h, &ok);
-  load_bytes<Gp::KNW * 4>(st.k, p.k_codes + (int64_t)row * Gp::P + qd * (Gp::KNW * 4));
-  st.ok = ok;
-  if (qd == 0) {
-    st.sk = p.k_meta[(int64_t)row * Gp::M];
-    st.zk = Gp::M == 2 ? p.k_meta[(int64_t)row * Gp::M + 1] : 0.0f;
-    st.sv = p.v_meta[(int64_t)row * Gp::M];
-    st.zv = Gp::M == 2 ? p.v_meta[(int64_t)row * Gp::M + 1] : 0.0f;
+  const int nblk = (int)p.num_blocks;   // < 2^31 (checked on the host)
+  const int row = plane_row(trow, tau * kPKeys + n, khi, p.block_size_log2, p.hkv, h, nblk);
+  st.ok = row >= 0;
+#pragma unroll
+  for (int i = 0; i < Gp::KNW; ++i) st.k[i] = 0u;
+  st.sk = 0.0f; st.zk = 0.0f; st.sv = 0.0f; st.zv = 0.0f;
+  if (row >= 0) {
+    load_bytes<Gp::KNW * 4>(st.k, p.k_codes + (int64_t)row * Gp::P + qd * (Gp::KNW * 4));
+    if (qd == 0) {
+      st.sk = p.k_meta[(int64_t)row * Gp::M];
+      st.zk = Gp::M == 2 ? p.k_meta[(int64_t)row * Gp::M + 1] : 0.0f;
+      st.sv = p.v_meta[(int64_t)row * Gp::M];
+      st.zv = Gp::M == 2 ? p.v_meta[(int64_t)row * Gp::M + 1] : 0.0f;
+    }
   }
   // V: positions 4 kq .. 4 kq + 3 (one block: block sizes are >= 16),
   // d = DPT wd .. DPT wd + DPT - 1, with kq = t % 16 so that the 16 lanes of
   // a group write one whole V^T row in LDS (no bank conflicts).
   const int kq = tid & 15, wd = tid >> 4;
   const int j0 = tau * kPKeys + 4 * kq;
-  const int bs_log2 = p.block_size_log2;
-  const int vid = j0 <= khi ? trow[j0 >> bs_log2] : -1;
-  const int vrow0 = ((max(vid, 0) * p.hkv + h) << bs_log2) + (j0 & ((1 << bs_log2) - 1));
+  const int vrow0 = plane_row(trow, j0, khi, p.block_size_log2, p.hkv, h, nblk);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int vr = (vid >= 0 && j0 + i <= khi) ? vrow0 + i : 0;
-    load_bytes<Gp::VNB>(st.v[i], p.v_codes + (int64_t)vr * Gp::P + wd * Gp::VNB);
+#pragma unroll
+    for (int w = 0; w < Gp::VNW; ++w) st.v[i][w] = 0u;
+    if (vrow0 >= 0 && j0 + i <= khi)
+      load_bytes<Gp::VNB>(st.v[i], p.v_codes + (int64_t)(vrow0 + i) * Gp::P + wd * Gp::VNB);
   }
 }
 
@@ -186,9 +193,13 @@ __device__ __forceinline__ void stage_store(const Stage<MODE, D>& st, PBuf<MODE,
   if (qd == 0) {
     // The PV product also yields the row sums l = sum p and Z = sum p z_V
     // through four extra V^T rows holding 1/s_V and z_V/s_V as bf16 hi + lo
-    // (W = p s_V).  A row with a zero or subnormal scale has all-zero codes,
-    // so any s_V reconstructs it; 1 keeps the extra rows finite.
-    const float sv = st.sv >= 1.17549435e-38f ? st.sv : 1.0f;
+    // (W = p s_V).  s_V enters both as max(s_V, 2^-96): below that, the lo
+    // half of W would fall under bf16's subnormal range and W / s_V would
+    // carry up to 2^-8 of error into l.  A row with a zero or subnormal scale
+    // has all-zero codes, so any s_V reconstructs it; a row with a scale in
+    // [2^-126, 2^-96) has entries below 127 * 2^-96, and the clamp moves its
+    // share of the output by less than 2^-89 p.
+    const float sv = fmaxf(st.sv, 0x1p-96f);
     const float u = st.ok ? __builtin_amdgcn_rcpf(sv) : 0.0f;
     const float t = st.ok ? st.zv * u : 0.0f;
     const __bf16 uh = (__bf16)u, th = (__bf16)t;
@@ -241,10 +252,10 @@ __device__ __forceinline__ void stage_store(const Stage<MODE, D>& st, PBuf<MODE,
 template <int MODE, int D>
 struct WaveCtx {
   using Gp = PGeo<MODE, D>;
-  u32x4_t qa[2][Gp::KS], qb[2][Gp::KS];   // query pieces, B-operand layout
+  u32x4_t qa[2][Gp::KS], qb[2][Gp::KS], qc[2][Gp::KS];   // query pieces, B-operand layout
   f32x4_t o[2][Gp::DB + 1];               // output accumulators (C layout); block DB: l, Z
   float m[2];                             // reference max (log2 units)
-  float sp[2], qp[2];                     // logit = sp * (s_K raw + z_K qp)
+  float sp[2], qp[2];                     // logit = sp * (s_K raw + z_K qp), raw = 2^14 A + 2^7 B + C
   int rpos[2], rlo[2];                    // row position and window start
   int W, wpos_lo, wpos_hi;
   bool wave_live;
@@ -267,11 +278,12 @@ __device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& 
     if (active) {
       const bool all_ok = __all(cb.ok[wc.lane >> 2][wc.lane & 3] != 0);
       const bool full = all_ok && pos0 + kPKeys - 1 <= wc.wpos_lo && (W <= 0 || pos0 >= wc.wpos_hi - W + 1);
-      // ---- S^T = K Q^T, two int32 accumulators (pieces a and b)
+      // ---- S^T = K Q^T, three int32 accumulators (pieces a, b and c)
       float x[4][2][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         i32x4_t ia[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, ib[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+        i32x4_t ic[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
         for (int ks = 0; ks < Gp::KS; ++ks) {
           const u32x4_t a = cb.k[16 * kb + r][4 * ks + q];
@@ -279,6 +291,7 @@ __device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& 
           for (int rb = 0; rb < 2; ++rb) {
             ia[rb] = mfma_i8(a, wc.qa[rb][ks], ia[rb]);
             ib[rb] = mfma_i8(a, wc.qb[rb][ks], ib[rb]);
+            ic[rb] = mfma_i8(a, wc.qc[rb][ks], ic[rb]);
           }
         }
         const f32x4_t skv = cb.sk[4 * kb + q];
@@ -287,7 +300,8 @@ __device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& 
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float raw = (float)((ia[rb][i] << 7) + ib[rb][i]);
+            // 2^7 A + B is exact in int32 (|.| < 2^29); one rounding joins C
+            const float raw = __builtin_fmaf((float)((ia[rb][i] << 7) + ib[rb][i]), 128.0f, (float)ic[rb][i]);
             x[kb][rb][i] = __builtin_fmaf(raw, skv[i], zkv[i] * wc.qp[rb]);
           }
       }
@@ -415,7 +429,7 @@ void prefill_kernel(PrefillParams p) {
   if (tok0 >= nq) return;
   const int ntok = min(tq, nq - tok0);
   const int nrows = ntok * G;
-  const int L = min(p.seq_lens[b], p.max_blocks << p.block_size_log2);
+  const int L = min(p.seq_lens[b], p.max_seq_len);   // host checked max_seq_len <= max_blocks * bs
   const int W = p.window ? p.window[h] : 0;
   const int pbase = L - nq + tok0;                // position of the tile's first token
   const int khi = pbase + ntok - 1;               // last position any row may see
@@ -467,26 +481,25 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
     const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
-    float sa = 0.0f, sb = 0.0f;
+    float sq = 0.0f;
     for (int d = lane; d < D; d += 64) {
       const float t = fminf(fmaxf(sm.qf[row][d] * qmul * invS, -127.0f), 127.0f);
       const float a = __builtin_rintf(t);
-      sa += a;
-      sb += __builtin_rintf((t - a) * 128.0f);
+      const float r1 = (t - a) * 128.0f;
+      const float b = __builtin_rintf(r1);
+      const float c = __builtin_rintf((r1 - b) * 128.0f);
+      sq += __builtin_fmaf(16384.0f, a, __builtin_fmaf(128.0f, b, c));   // each term exact (< 2^22)
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      sa += __shfl_xor(sa, m);
-      sb += __shfl_xor(sb, m);
-    }
+    for (int m = 32; m >= 1; m >>= 1) sq += __shfl_xor(sq, m);
     if (lane == 0) {
       sm.rs[row] = mx;
-      sm.r1[row] = (mx / 127.0f) * (sa + sb * 0.0078125f);
+      sm.r1[row] = sq;
     }
   }
   __syncthreads();
   // B operands: lane (row r of block rb, k-slots 64 ks + 16 q .. +15)
-  u32x4_t qa[2][Gp::KS], qb[2][Gp::KS];
+  u32x4_t qa[2][Gp::KS], qb[2][Gp::KS], qc[2][Gp::KS];
   float sp[2], qp[2];
   int rpos[2], rlo[2];
 #pragma unroll
@@ -497,28 +510,33 @@ void prefill_kernel(PrefillParams p) {
     const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;   // as in the pass above
 #pragma unroll
     for (int ks = 0; ks < Gp::KS; ++ks) {
-      uint32_t wa[4], wb[4];
+      uint32_t wa[4], wb[4], wcc[4];
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
-        uint32_t pa = 0, pb = 0;
+        uint32_t pa = 0, pb = 0, pc = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = kslot_d<MODE, D>(64 * ks + 16 * q + 4 * j4 + j);
           const float t = fminf(fmaxf(sm.qf[row][d] * qmul * invS, -127.0f), 127.0f);
           const float a = __builtin_rintf(t);
-          const float c = __builtin_rintf((t - a) * 128.0f);
+          const float r1 = (t - a) * 128.0f;
+          const float b = __builtin_rintf(r1);
+          const float c = __builtin_rintf((r1 - b) * 128.0f);
           pa |= ((uint32_t)(int32_t)a & 0xffu) << (8 * j);
-          pb |= ((uint32_t)(int32_t)c & 0xffu) << (8 * j);
+          pb |= ((uint32_t)(int32_t)b & 0xffu) << (8 * j);
+          pc |= ((uint32_t)(int32_t)c & 0xffu) << (8 * j);
         }
         wa[j4] = pa;
         wb[j4] = pb;
+        wcc[j4] = pc;
       }
       qa[rb][ks] = u32x4_t{wa[0], wa[1], wa[2], wa[3]};
       qb[rb][ks] = u32x4_t{wb[0], wb[1], wb[2], wb[3]};
+      qc[rb][ks] = u32x4_t{wcc[0], wcc[1], wcc[2], wcc[3]};
     }
-    // logit (log2 units) = sp * x, x = s_K raw + z_K qp, raw = 128 A + B
-    sp[rb] = S > 0.0f ? S * 0.0078125f : 1.0f;
-    qp[rb] = S > 0.0f ? sm.r1[row] / sp[rb] : 0.0f;
+    // logit (log2 units) = sp * x, x = s_K raw + z_K qp, raw = 2^14 A + 2^7 B + C
+    sp[rb] = S > 0.0f ? S * 6.103515625e-05f : 1.0f;   // S / 2^14
+    qp[rb] = S > 0.0f ? sm.r1[row] : 0.0f;
     const bool live = row < nrows;
     rpos[rb] = live ? pbase + row / G : -1;
     rlo[rb] = W > 0 ? rpos[rb] - W + 1 : INT32_MIN;
@@ -544,7 +562,9 @@ void prefill_kernel(PrefillParams p) {
     wc.m[rb] = kNegInf;
     wc.sp[rb] = sp[rb]; wc.qp[rb] = qp[rb]; wc.rpos[rb] = rpos[rb]; wc.rlo[rb] = rlo[rb];
 #pragma unroll
-    for (int ks = 0; ks < Gp::KS; ++ks) { wc.qa[rb][ks] = qa[rb][ks]; wc.qb[rb][ks] = qb[rb][ks]; }
+    for (int ks = 0; ks < Gp::KS; ++ks) {
+      wc.qa[rb][ks] = qa[rb][ks]; wc.qb[rb][ks] = qb[rb][ks]; wc.qc[rb][ks] = qc[rb][ks];
+    }
 #pragma unroll
     for (int db = 0; db <= Gp::DB; ++db) wc.o[rb][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }

@@ -6,8 +6,8 @@
 // The D/8 lanes lr = 0 .. D/8-1 of one aligned lane group call it together
 // (converged: the FWHT and the statistics are shuffles within the group);
 // each lane owns 8 consecutive elements.  Row (token t, kv head h, K if kv =
-// 0 else V) goes to `slot` (block * block_size + offset); slot < 0 computes
-// nothing visible.  The load and the rest are separate steps, so a caller
+// 0 else V) goes to `slot` (block * block_size + offset); a slot < 0 or at
+// or past the planes' capacity computes nothing visible.  The load and the rest are separate steps, so a caller
 // can have the loads of several rows in flight before the first is used.
 #pragma once
 
@@ -46,7 +46,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   constexpr int M = mode_meta(MODE);
   constexpr float kLevels = (float)mode_levels(MODE);
   const int hkv = p.hkv;
-  const bool active = slot >= 0;
+  const bool active = slot >= 0 && slot < p.slot_cap;
 
   float x[8];
   if (active) {
@@ -160,10 +160,10 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   }
 }
 
-// The whole row: load, then compute and store (slot < 0 reads nothing).
+// The whole row: load, then compute and store (a skipped slot reads nothing).
 template <int MODE, int D, bool ROT>
 __device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h, int kv, int64_t slot, int lr) {
-  const uint4 raw = slot >= 0 ? write_row_load<D>(p, t, h, kv, lr) : make_uint4(0, 0, 0, 0);
+  const uint4 raw = (slot >= 0 && slot < p.slot_cap) ? write_row_load<D>(p, t, h, kv, lr) : make_uint4(0, 0, 0, 0);
   float sg[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (ROT) write_row_signs(p, lr, sg);
   write_row_store<MODE, D, ROT>(p, raw, sg, h, kv, slot, lr);

@@ -46,6 +46,71 @@ def _need(t, name, dtype, device=None, contiguous=True):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _opts(num_workgroups: int):
+    """kvq_decode_options for a workgroup count (0 = the library's choice)."""
+    return ctypes.byref(_lib.DecodeOptions(int(num_workgroups))) if num_workgroups else None
+
+
+def _check_planes(desc, k_codes, k_meta, v_codes, v_meta):
+    """The four planes: dtype, device, contiguity, and at least the bytes the
+    layout query gives for ``desc`` (a larger allocation is allowed: the
+    kernels address only the first num_blocks blocks)."""
+    lay = kvq_query_layout(desc)
+    dev = k_codes.device
+    for t, n, dt, need in ((k_codes, "k_codes", torch.uint8, lay["code_bytes"]),
+                           (v_codes, "v_codes", torch.uint8, lay["code_bytes"]),
+                           (k_meta, "k_meta", torch.float32, lay["meta_bytes"]),
+                           (v_meta, "v_meta", torch.float32, lay["meta_bytes"])):
+        if t is None:
+            raise ValueError(f"{n} is None")
+        _need(t, n, dt, dev)
+        if t.numel() * t.element_size() < need:
+            raise ValueError(f"{n} holds {t.numel() * t.element_size()} bytes, the layout needs {need}")
+    return dev
+
+
+def _check_tables(desc, B, block_tables, block_tables_headwise, dev):
+    """Exactly one table, int32 on the device, B (uniform) or B*Hkv
+    (head-wise) rows; returns its row length."""
+    if (block_tables is None) == (block_tables_headwise is None):
+        raise ValueError("exactly one of block_tables and block_tables_headwise must be given")
+    tab = block_tables if block_tables is not None else block_tables_headwise
+    name = "block_tables" if block_tables is not None else "block_tables_headwise"
+    _need(tab, name, torch.int32, dev)
+    rows = B if block_tables is not None else B * desc.num_kv_heads
+    if tab.dim() != 2 or tab.shape[0] < rows:
+        raise ValueError(f"{name} must be [>= {rows}, max_blocks], got {tuple(tab.shape)}")
+    return int(tab.shape[1])
+
+
+def _check_lens_window(desc, B, seq_lens, window, dev):
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    if seq_lens is None or seq_lens.dim() != 1 or seq_lens.shape[0] < B:
+        raise ValueError(f"seq_lens must be int32 [>= {B}]")
+    _need(window, "window", torch.int32, dev)
+    if window is not None and (window.dim() != 1 or window.shape[0] < desc.num_kv_heads):
+        raise ValueError(f"window must be int32 [>= {desc.num_kv_heads}]")
+
+
+def _check_query(desc, query, name="query"):
+    dev = query.device
+    _need(query, name, torch.bfloat16, dev)
+    if query.dim() != 3 or query.shape[2] != desc.head_dim:
+        raise ValueError(f"{name} must be [N, Hq, {desc.head_dim}], got {tuple(query.shape)}")
+    return dev
+
+
+def _out_for(out, shape, out_dtype, dev):
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"out must be float32 or bfloat16, got {out.dtype}")
+    _need(out, "out", out.dtype, dev)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must be {tuple(shape)}, got {tuple(out.shape)}")
+    return out, {torch.float32: KVQ_OUT_F32, torch.bfloat16: KVQ_OUT_BF16}[out.dtype]
+
+
 def _stream(device) -> ctypes.c_void_p:
     if device.type != "cuda":
         raise ValueError(f"tensors must be on a HIP device, got {device}")
@@ -110,11 +175,17 @@ def kvq_reshape_and_cache(desc: CacheDesc, key: torch.Tensor, value: torch.Tenso
             raise ValueError(f"{n} must be [T, Hkv, D] with heads and D contiguous")
     if key.shape != value.shape:
         raise ValueError("key and value shapes differ")
+    _check_planes(desc, k_codes, k_meta, v_codes, v_meta)
+    T = int(key.shape[0])
+    if key.shape[1] != desc.num_kv_heads or key.shape[2] != desc.head_dim:
+        raise ValueError(f"key must be [T, {desc.num_kv_heads}, {desc.head_dim}], got {tuple(key.shape)}")
     _need(slot_mapping, "slot_mapping", torch.int64, dev)
     _need(slot_mapping_headwise, "slot_mapping_headwise", torch.int64, dev)
-    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (v_codes, "v_codes", torch.uint8),
-                     (k_meta, "k_meta", torch.float32), (v_meta, "v_meta", torch.float32)):
-        _need(t, n, dt, dev)
+    if slot_mapping is not None and tuple(slot_mapping.shape) != (T,):
+        raise ValueError(f"slot_mapping must be [{T}], got {tuple(slot_mapping.shape)}")
+    if slot_mapping_headwise is not None and tuple(slot_mapping_headwise.shape) != (T, desc.num_kv_heads):
+        raise ValueError(f"slot_mapping_headwise must be [{T}, {desc.num_kv_heads}], "
+                         f"got {tuple(slot_mapping_headwise.shape)}")
     d = desc.c()
     _check(_lib.load().kvq_reshape_and_cache(
         ctypes.byref(d), _ptr(key), _ptr(value), key.stride(0), value.stride(0),
@@ -123,11 +194,22 @@ def kvq_reshape_and_cache(desc: CacheDesc, key: torch.Tensor, value: torch.Tenso
 
 
 def kvq_decode_workspace_size(desc: CacheDesc, num_seqs: int, num_q_heads: int,
-                              max_seq_len: int) -> int:
+                              max_seq_len: int, num_workgroups: int = 0) -> int:
+    """Workspace bytes of a decode call with these sizes; ``num_workgroups``
+    (0 = the library's choice) must match the decode call's."""
     n = ctypes.c_size_t(0)
     d = desc.c()
     _check(_lib.load().kvq_decode_workspace_size(ctypes.byref(d), int(num_seqs), int(num_q_heads),
-                                                 int(max_seq_len), ctypes.byref(n)))
+                                                 int(max_seq_len), _opts(num_workgroups), ctypes.byref(n)))
+    return int(n.value)
+
+
+def kvq_prefill_workspace_size(desc: CacheDesc, num_seqs: int, num_q_heads: int, max_q_len: int,
+                               max_seq_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    d = desc.c()
+    _check(_lib.load().kvq_prefill_workspace_size(ctypes.byref(d), int(num_seqs), int(num_q_heads),
+                                                  int(max_q_len), int(max_seq_len), ctypes.byref(n)))
     return int(n.value)
 
 
@@ -155,32 +237,26 @@ def kvq_paged_decode_attention(desc: CacheDesc, query: torch.Tensor,
                                softmax_scale: Optional[float] = None,
                                out: Optional[torch.Tensor] = None,
                                out_dtype: torch.dtype = torch.float32,
-                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                               workspace: Optional[torch.Tensor] = None,
+                               num_workgroups: int = 0) -> torch.Tensor:
     """Decode attention for query [B, Hq, D] (bf16); returns out [B, Hq, D]."""
-    dev = query.device
-    _need(query, "query", torch.bfloat16, dev)
+    dev = _check_query(desc, query)
     B, Hq, D = query.shape
-    _need(seq_lens, "seq_lens", torch.int32, dev)
-    _need(block_tables, "block_tables", torch.int32, dev)
-    _need(block_tables_headwise, "block_tables_headwise", torch.int32, dev)
-    _need(window, "window", torch.int32, dev)
-    tab = block_tables if block_tables is not None else block_tables_headwise
-    max_blocks = int(tab.shape[1]) if tab is not None else 0
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
-    _need(out, "out", out.dtype, dev)
-    odt = {torch.float32: KVQ_OUT_F32, torch.bfloat16: KVQ_OUT_BF16}[out.dtype]
+    _check_planes(desc, k_codes, k_meta, v_codes, v_meta)
+    max_blocks = _check_tables(desc, B, block_tables, block_tables_headwise, dev)
+    _check_lens_window(desc, B, seq_lens, window, dev)
+    out, odt = _out_for(out, (B, Hq, D), out_dtype, dev)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if workspace is None:
-        workspace = alloc_workspace(kvq_decode_workspace_size(desc, B, Hq, max_seq_len), dev)
+        workspace = alloc_workspace(kvq_decode_workspace_size(desc, B, Hq, max_seq_len, num_workgroups), dev)
     _need(workspace, "workspace", torch.uint8, dev)
     d = desc.c()
     _check(_lib.load().kvq_paged_decode_attention(
         ctypes.byref(d), _ptr(out), odt, _ptr(query), int(B), int(Hq),
         _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
         _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
-        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale),
+        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale), _opts(num_workgroups),
         _ptr(workspace), workspace.numel(), _stream(dev)))
     return out
 
@@ -197,37 +273,33 @@ def kvq_decode_step(desc: CacheDesc, query: torch.Tensor, key: torch.Tensor, val
                     softmax_scale: Optional[float] = None,
                     out: Optional[torch.Tensor] = None,
                     out_dtype: torch.dtype = torch.float32,
-                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    workspace: Optional[torch.Tensor] = None,
+                    num_workgroups: int = 0) -> torch.Tensor:
     """One decode step in one launch: quantize-on-write of each sequence's
     new token (key/value [B, Hkv, D] bf16, token b at slot_mapping[b], which
     must be position seq_lens[b] - 1 of sequence b's table), then decode
     attention of query [B, Hq, D]; returns out [B, Hq, D]."""
-    dev = query.device
-    _need(query, "query", torch.bfloat16, dev)
+    dev = _check_query(desc, query)
     B, Hq, D = query.shape
     for t, n in ((key, "key"), (value, "value")):
         _need(t, n, torch.bfloat16, dev, contiguous=False)
-        if t.dim() != 3 or t.shape[0] != B or t.stride(2) != 1 or t.stride(1) != desc.head_dim:
-            raise ValueError(f"{n} must be [B, Hkv, D] with heads and D contiguous")
+        if t.dim() != 3 or tuple(t.shape) != (B, desc.num_kv_heads, D) or t.stride(2) != 1 \
+                or t.stride(1) != desc.head_dim:
+            raise ValueError(f"{n} must be [{B}, {desc.num_kv_heads}, {D}] with heads and D contiguous")
     _need(slot_mapping, "slot_mapping", torch.int64, dev)
     _need(slot_mapping_headwise, "slot_mapping_headwise", torch.int64, dev)
-    _need(seq_lens, "seq_lens", torch.int32, dev)
-    _need(block_tables, "block_tables", torch.int32, dev)
-    _need(block_tables_headwise, "block_tables_headwise", torch.int32, dev)
-    _need(window, "window", torch.int32, dev)
-    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (v_codes, "v_codes", torch.uint8),
-                     (k_meta, "k_meta", torch.float32), (v_meta, "v_meta", torch.float32)):
-        _need(t, n, dt, dev)
-    tab = block_tables if block_tables is not None else block_tables_headwise
-    max_blocks = int(tab.shape[1]) if tab is not None else 0
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
-    _need(out, "out", out.dtype, dev)
-    odt = {torch.float32: KVQ_OUT_F32, torch.bfloat16: KVQ_OUT_BF16}[out.dtype]
+    if slot_mapping is not None and tuple(slot_mapping.shape) != (B,):
+        raise ValueError(f"slot_mapping must be [{B}]")
+    if slot_mapping_headwise is not None and tuple(slot_mapping_headwise.shape) != (B, desc.num_kv_heads):
+        raise ValueError(f"slot_mapping_headwise must be [{B}, {desc.num_kv_heads}]")
+    _check_planes(desc, k_codes, k_meta, v_codes, v_meta)
+    max_blocks = _check_tables(desc, B, block_tables, block_tables_headwise, dev)
+    _check_lens_window(desc, B, seq_lens, window, dev)
+    out, odt = _out_for(out, (B, Hq, D), out_dtype, dev)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if workspace is None:
-        workspace = alloc_workspace(kvq_decode_workspace_size(desc, B, Hq, max_seq_len), dev)
+        workspace = alloc_workspace(kvq_decode_workspace_size(desc, B, Hq, max_seq_len, num_workgroups), dev)
     _need(workspace, "workspace", torch.uint8, dev)
     d = desc.c()
     _check(_lib.load().kvq_decode_step(
@@ -236,7 +308,7 @@ def kvq_decode_step(desc: CacheDesc, query: torch.Tensor, key: torch.Tensor, val
         _ptr(slot_mapping), _ptr(slot_mapping_headwise),
         _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
         _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
-        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale),
+        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale), _opts(num_workgroups),
         _ptr(workspace), workspace.numel(), _stream(dev)))
     return out
 
@@ -251,35 +323,35 @@ def kvq_paged_prefill_attention(desc: CacheDesc, query: torch.Tensor, cu_seqlens
                                 window: Optional[torch.Tensor] = None,
                                 softmax_scale: Optional[float] = None,
                                 out: Optional[torch.Tensor] = None,
-                                out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+                                out_dtype: torch.dtype = torch.float32,
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Chunked-prefill attention for query [total_q, Hq, D] (bf16) with
     sequence b owning rows cu_seqlens_q[b]..cu_seqlens_q[b+1]-1; returns out
     [total_q, Hq, D]."""
-    dev = query.device
-    _need(query, "query", torch.bfloat16, dev)
+    dev = _check_query(desc, query)
     Tq, Hq, D = query.shape
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
-    _need(seq_lens, "seq_lens", torch.int32, dev)
-    _need(block_tables, "block_tables", torch.int32, dev)
-    _need(block_tables_headwise, "block_tables_headwise", torch.int32, dev)
-    _need(window, "window", torch.int32, dev)
     B = int(seq_lens.shape[0])
     if cu_seqlens_q.shape[0] != B + 1:
         raise KvqError(1, f"cu_seqlens_q has {cu_seqlens_q.shape[0]} entries, {B + 1} expected")
-    tab = block_tables if block_tables is not None else block_tables_headwise
-    max_blocks = int(tab.shape[1]) if tab is not None else 0
-    if out is None:
-        out = torch.empty((Tq, Hq, D), dtype=out_dtype, device=dev)
-    _need(out, "out", out.dtype, dev)
-    odt = {torch.float32: KVQ_OUT_F32, torch.bfloat16: KVQ_OUT_BF16}[out.dtype]
+    _check_planes(desc, k_codes, k_meta, v_codes, v_meta)
+    max_blocks = _check_tables(desc, B, block_tables, block_tables_headwise, dev)
+    _check_lens_window(desc, B, seq_lens, window, dev)
+    out, odt = _out_for(out, (Tq, Hq, D), out_dtype, dev)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
+    need = kvq_prefill_workspace_size(desc, B, Hq, max_q_len, max_seq_len)
+    if workspace is None and need:
+        workspace = alloc_workspace(need, dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
     d = desc.c()
     _check(_lib.load().kvq_paged_prefill_attention(
         ctypes.byref(d), _ptr(out), odt, _ptr(query), _ptr(cu_seqlens_q), B, int(Hq), int(max_q_len),
         _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
         _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
-        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale), _stream(dev)))
+        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)))
     return out
 
 
@@ -295,13 +367,9 @@ def kvq_gather_dequant(desc: CacheDesc, k_codes: torch.Tensor, k_meta: torch.Ten
     sequences' positions 0 .. n_b - 1 (n_b = cu_seq_lens[b+1] -
     cu_seq_lens[b]) at rows cu_seq_lens[b] ..; evicted positions are zero.
     Returns (key_out, value_out)."""
-    dev = k_codes.device
+    dev = _check_planes(desc, k_codes, k_meta, v_codes, v_meta)
     _need(cu_seq_lens, "cu_seq_lens", torch.int32, dev)
-    _need(block_tables, "block_tables", torch.int32, dev)
-    _need(block_tables_headwise, "block_tables_headwise", torch.int32, dev)
-    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (v_codes, "v_codes", torch.uint8),
-                     (k_meta, "k_meta", torch.float32), (v_meta, "v_meta", torch.float32)):
-        _need(t, n, dt, dev)
+    _check_tables(desc, int(cu_seq_lens.shape[0]) - 1, block_tables, block_tables_headwise, dev)
     shape = (int(total_tokens), desc.num_kv_heads, desc.head_dim)
     if key_out is None:
         key_out = torch.empty(shape, dtype=out_dtype, device=dev)

@@ -34,7 +34,7 @@ def test_header_lists_entry_points():
     names = header_functions()
     for n in ("kvq_query_layout", "kvq_reshape_and_cache", "kvq_paged_decode_attention",
               "kvq_decode_workspace_size", "kvq_workspace_init", "kvq_paged_prefill_attention",
-              "kvq_decode_step", "kvq_gather_dequant", "kvq_last_error"):
+              "kvq_decode_step", "kvq_gather_dequant", "kvq_last_error", "kvq_prefill_workspace_size"):
         assert n in names
 
 
@@ -90,11 +90,12 @@ def test_write_validation(lib):
 def _decode(lib, d, **kw):
     P = ctypes.c_void_p(4096)
     a = dict(out=P, odt=0, q=P, B=2, Hq=8, kc=P, km=P, vc=P, vm=P, bt=P, bth=None, mb=4, sl=P, msl=200,
-             win=None, scale=0.125, ws=P, wsb=1 << 20)
+             win=None, scale=0.125, opt=None, ws=P, wsb=1 << 20)
     a.update(kw)
     return lib.kvq_paged_decode_attention(ctypes.byref(d), a["out"], a["odt"], a["q"], a["B"], a["Hq"],
                                           a["kc"], a["km"], a["vc"], a["vm"], a["bt"], a["bth"], a["mb"],
-                                          a["sl"], a["msl"], a["win"], a["scale"], a["ws"], a["wsb"], None)
+                                          a["sl"], a["msl"], a["win"], a["scale"], a["opt"], a["ws"], a["wsb"],
+                                          None)
 
 
 def test_decode_validation(lib):
@@ -114,20 +115,34 @@ def test_decode_validation(lib):
     assert _decode(lib, d, out=ctypes.c_void_p(4098)) == _lib.KVQ_EINVAL   # misaligned
     assert _decode(lib, d, B=0) == _lib.KVQ_OK                      # nothing to do
     need = ctypes.c_size_t()
-    assert lib.kvq_decode_workspace_size(ctypes.byref(d), 2, 8, 200, ctypes.byref(need)) == 0
+    assert lib.kvq_decode_workspace_size(ctypes.byref(d), 2, 8, 200, None, ctypes.byref(need)) == 0
     if need.value:
         assert _decode(lib, d, wsb=need.value - 1) == _lib.KVQ_ENOSPACE
         assert _decode(lib, d, ws=None) == _lib.KVQ_EINVAL
+    # options: a negative workgroup count is rejected; an explicit count
+    # changes the workspace size, and the decode call checks it with its own
+    bad = _lib.DecodeOptions(-1)
+    assert _decode(lib, d, opt=ctypes.byref(bad)) == _lib.KVQ_EINVAL
+    assert lib.kvq_decode_workspace_size(ctypes.byref(d), 2, 8, 200, ctypes.byref(bad), ctypes.byref(need)) \
+        == _lib.KVQ_EINVAL
+    big = _lib.DecodeOptions(5000)
+    n_big = ctypes.c_size_t()
+    assert lib.kvq_decode_workspace_size(ctypes.byref(d), 2, 8, 200, ctypes.byref(big), ctypes.byref(n_big)) == 0
+    n_def = ctypes.c_size_t()
+    assert lib.kvq_decode_workspace_size(ctypes.byref(d), 2, 8, 200, None, ctypes.byref(n_def)) == 0
+    assert n_big.value > n_def.value
+    assert _decode(lib, d, opt=ctypes.byref(big), wsb=n_def.value) == _lib.KVQ_ENOSPACE
 
 
 def _step(lib, d, **kw):
     P = ctypes.c_void_p(4096)
     a = dict(out=P, odt=0, q=P, B=2, Hq=8, key=P, value=P, ks=512, vs=512, sm=P, smh=None, kc=P, km=P, vc=P,
-             vm=P, bt=P, bth=None, mb=4, sl=P, msl=200, win=None, scale=0.125, ws=P, wsb=1 << 20)
+             vm=P, bt=P, bth=None, mb=4, sl=P, msl=200, win=None, scale=0.125, opt=None, ws=P, wsb=1 << 20)
     a.update(kw)
     return lib.kvq_decode_step(ctypes.byref(d), a["out"], a["odt"], a["q"], a["B"], a["Hq"], a["key"], a["value"],
                                a["ks"], a["vs"], a["sm"], a["smh"], a["kc"], a["km"], a["vc"], a["vm"], a["bt"],
-                               a["bth"], a["mb"], a["sl"], a["msl"], a["win"], a["scale"], a["ws"], a["wsb"], None)
+                               a["bth"], a["mb"], a["sl"], a["msl"], a["win"], a["scale"], a["opt"], a["ws"],
+                               a["wsb"], None)
 
 
 def test_decode_step_validation(lib):
@@ -151,11 +166,12 @@ def test_decode_step_validation(lib):
 def _prefill(lib, d, **kw):
     P = ctypes.c_void_p(4096)
     a = dict(out=P, odt=0, q=P, cu=P, B=2, Hq=8, mq=64, kc=P, km=P, vc=P, vm=P, bt=P, bth=None, mb=4, sl=P,
-             msl=200, win=None, scale=0.125)
+             msl=200, win=None, scale=0.125, ws=None, wsb=0)
     a.update(kw)
     return lib.kvq_paged_prefill_attention(ctypes.byref(d), a["out"], a["odt"], a["q"], a["cu"], a["B"], a["Hq"],
                                            a["mq"], a["kc"], a["km"], a["vc"], a["vm"], a["bt"], a["bth"],
-                                           a["mb"], a["sl"], a["msl"], a["win"], a["scale"], None)
+                                           a["mb"], a["sl"], a["msl"], a["win"], a["scale"], a["ws"], a["wsb"],
+                                           None)
 
 
 def test_prefill_validation(lib):
@@ -178,12 +194,25 @@ def test_prefill_validation(lib):
     assert _prefill(lib, desc(D=96)) == _lib.KVQ_EINVAL
 
 
+def test_prefill_workspace_size(lib):
+    d = desc(H=4, bs=64)
+    n = ctypes.c_size_t(123)
+    assert lib.kvq_prefill_workspace_size(ctypes.byref(d), 16, 16, 512, 32768, ctypes.byref(n)) == _lib.KVQ_OK
+    assert n.value == 0
+    # the same size checks as the prefill call
+    assert lib.kvq_prefill_workspace_size(ctypes.byref(d), 16, 6, 512, 32768, ctypes.byref(n)) == _lib.KVQ_EINVAL
+    assert lib.kvq_prefill_workspace_size(ctypes.byref(d), -1, 16, 512, 32768, ctypes.byref(n)) == _lib.KVQ_EINVAL
+    assert lib.kvq_prefill_workspace_size(ctypes.byref(d), 16, 16, -2, 32768, ctypes.byref(n)) == _lib.KVQ_EINVAL
+    assert lib.kvq_prefill_workspace_size(ctypes.byref(d), 16, 16, 512, 32768, None) == _lib.KVQ_EINVAL
+    assert lib.kvq_prefill_workspace_size(None, 16, 16, 512, 32768, ctypes.byref(n)) == _lib.KVQ_EINVAL
+
+
 def test_workspace_size_grows_with_work(lib):
     d = desc(H=8, bs=64)
     sizes = []
     for msl in (64, 4096, 131072):
         n = ctypes.c_size_t()
-        assert lib.kvq_decode_workspace_size(ctypes.byref(d), 4, 32, msl, ctypes.byref(n)) == 0
+        assert lib.kvq_decode_workspace_size(ctypes.byref(d), 4, 32, msl, None, ctypes.byref(n)) == 0
         sizes.append(n.value)
         assert n.value % 16 == 0
     assert sizes[0] <= sizes[1] <= sizes[2]

@@ -4,8 +4,6 @@ planes, element by element (float32 output within max-abs 2e-3 and mean-abs
 head-wise rows equal to the uniform row (FastDeploy PR 7718 correctness
 gates), repeated calls; and ones that hold within tolerance: split count,
 -1 entries for blocks outside the window."""
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -80,20 +78,18 @@ def test_decode_bf16_output():
     assert np.all(np.abs(a - b) <= ulp)
 
 
-def test_decode_repeatable_and_split_invariant(monkeypatch):
+def test_decode_repeatable_and_split_invariant():
     spec = synth.small_spec(name="splits", cfg=463, mode=2, rotate=True, lens=[2000, 45, 700], B=3)
     case, d, planes = gh.build(spec)
     outs = []
     # workgroup counts: one share per pair or fewer, shares cutting pairs at
     # odd places, more workgroups than tiles (the partition then shrinks)
-    for nwg in ("1", "3", "7", "1000"):
-        monkeypatch.setenv("KVQ_DECODE_WGS", nwg)
-        o1 = gh.gpu_decode(spec, case, d, planes)
-        o2 = gh.gpu_decode(spec, case, d, planes)
+    for nwg in (1, 3, 7, 1000):
+        o1 = gh.gpu_decode(spec, case, d, planes, num_workgroups=nwg)
+        o2 = gh.gpu_decode(spec, case, d, planes, num_workgroups=nwg)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2), f"repeat differs at {nwg} workgroups"
         outs.append(o1.cpu().numpy())
-    monkeypatch.delenv("KVQ_DECODE_WGS")
     ref = gh.oracle_decode(spec, case, gh.host_planes(planes))
     for o in outs:
         gh.assert_close(o, ref, "split-count")
@@ -220,7 +216,7 @@ def _many_pair_lens(seed, n):
 
 
 @pytest.mark.parametrize("mode,bs", [(1, 16), (0, 64), (2, 64)])
-def test_decode_many_pairs_chunks_and_batches(monkeypatch, mode, bs):
+def test_decode_many_pairs_chunks_and_batches(mode, bs):
     """1200 pairs (several prefix chunks), shares holding hundreds of
     segments (many segment batches, some cut short by the block-id table),
     empty sequences in between; default grid and a 7-workgroup grid."""
@@ -229,17 +225,12 @@ def test_decode_many_pairs_chunks_and_batches(monkeypatch, mode, bs):
     print(f"[case] decode {spec.name}", flush=True)
     case, d, planes = gh.build(spec)
     ref = gh.oracle_decode(spec, case, gh.host_planes(planes))
-    for nwg in (None, "7"):
-        if nwg is None:
-            monkeypatch.delenv("KVQ_DECODE_WGS", raising=False)
-        else:
-            monkeypatch.setenv("KVQ_DECODE_WGS", nwg)
-        o1 = gh.gpu_decode(spec, case, d, planes)
-        o2 = gh.gpu_decode(spec, case, d, planes)
+    for nwg in (0, 7):
+        o1 = gh.gpu_decode(spec, case, d, planes, num_workgroups=nwg)
+        o2 = gh.gpu_decode(spec, case, d, planes, num_workgroups=nwg)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2), f"repeat differs ({nwg} workgroups)"
         o = o1.cpu().numpy()
         lens = np.asarray(spec.lens)
         assert np.all(o[lens == 0] == 0)
         gh.assert_close(o, ref, f"{spec.name} wgs={nwg}")
-    monkeypatch.delenv("KVQ_DECODE_WGS", raising=False)
