@@ -201,6 +201,39 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc,
                                       void* workspace, size_t workspace_bytes,
                                       void* stream);
 
+/* Largest workspace kvq_paged_decode_attention_noalloc can serve (bytes). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* Paged decode attention without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Arguments, result and errors are
+ * those of kvq_paged_decode_attention with the default options; the
+ * workspace is instead a device array inside the library of
+ * KVQ_NOALLOC_SCRATCH_BYTES bytes per GPU, held until the process ends.
+ *  - A call whose workspace (kvq_decode_workspace_size with NULL options)
+ *    exceeds KVQ_NOALLOC_SCRATCH_BYTES returns KVQ_ENOSPACE and launches
+ *    nothing.
+ *  - Each call launches a small fill kernel that zeroes the array's counters,
+ *    then the decode kernel, both on `stream`; nothing is allocated (no
+ *    hipMalloc, no memset node).  The calling thread's current device must be
+ *    the one that `stream` and the buffers belong to.
+ *  - Every call on a GPU shares that GPU's array: calls that overlap in time
+ *    on one GPU (on different streams, or from different threads) race and
+ *    give undefined results. */
+kvq_status kvq_paged_decode_attention_noalloc(const kvq_cache_desc* desc,
+                                              void* out, int32_t out_dtype,
+                                              const void* query,
+                                              int32_t num_seqs, int32_t num_q_heads,
+                                              const uint8_t* k_codes, const float* k_meta,
+                                              const uint8_t* v_codes, const float* v_meta,
+                                              const int32_t* block_tables,
+                                              const int32_t* block_tables_headwise,
+                                              int32_t max_blocks_per_seq,
+                                              const int32_t* seq_lens, int32_t max_seq_len,
+                                              const int32_t* window,
+                                              float softmax_scale,
+                                              void* stream);
+
 /* One decode step in one launch: the quantize-on-write of each sequence's
  * new token followed by paged decode attention (the decoder's cache write and
  * attention of FastDeploy PR 5173, Modifications, and the append-then-attend

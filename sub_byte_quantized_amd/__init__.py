@@ -5,7 +5,7 @@ The Python layer marshals arguments only; every step runs in HIP kernels.
 """
 from .kvq import (CacheDesc, KvqError, alloc_cache, alloc_workspace,  # noqa: F401
                   kvq_decode_step, kvq_decode_workspace_size, kvq_gather_dequant,
-                  kvq_paged_decode_attention,
+                  kvq_paged_decode_attention, kvq_paged_decode_attention_noalloc,
                   kvq_paged_prefill_attention, kvq_prefill_workspace_size,
                   kvq_query_layout,
                   kvq_reshape_and_cache, kvq_workspace_init, KVQ_INT8_SYM, KVQ_INT4_ASYM,

@@ -47,6 +47,8 @@ SIGNATURES = {
     "kvq_workspace_init": (_I32, [_P, _SZ, _P]),
     "kvq_paged_decode_attention": (_I32, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                           _I32, _P, _I32, _P, ctypes.c_float, _OPT, _P, _SZ, _P]),
+    "kvq_paged_decode_attention_noalloc": (_I32, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                                  _I32, _P, _I32, _P, ctypes.c_float, _P]),
     "kvq_decode_step": (_I32, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P,
                                _P, _P, _I32, _P, _I32, _P, ctypes.c_float, _OPT, _P, _SZ, _P]),
     "kvq_paged_prefill_attention": (_I32, [_DESC, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,

@@ -12,9 +12,17 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kvq.h"
 #include "kvq_internal.h"
+
+// Device scratch of kvq_paged_decode_attention_noalloc: the decode
+// workspace (piece counters, then partial softmax states) of callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never uses this name as an address: it takes
+// the device address from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -134,6 +142,32 @@ kvq_status check_decode_sizes(const kvq_cache_desc* d, int num_seqs, int num_q_h
   return KVQ_OK;
 }
 
+// Device address of `scratch` on the current device: looked up once per
+// device (with that device current) and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+kvq_status scratch_address(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVQ_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_EUNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KVQ_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return KVQ_OK;
+}
+
+// use_scratch: the workspace is the library's device scratch (workspace and
+// workspace_bytes are ignored); its counters are cleared by a fill kernel
+// before the decode launch.
 kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
                                       const void* query, int32_t num_seqs, int32_t num_q_heads,
                                       const uint8_t* k_codes, const float* k_meta,
@@ -143,7 +177,7 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
                                       int32_t max_seq_len, const int32_t* window, float softmax_scale,
                                       const kvq_decode_options* options,
                                       void* workspace, size_t workspace_bytes, void* stream,
-                                      const kvq::WriteParams* wp) {
+                                      const kvq::WriteParams* wp, bool use_scratch = false) {
   kvq_status st = check_desc(desc);
   if (st != KVQ_OK) return st;
   st = check_decode_sizes(desc, num_seqs, num_q_heads, max_seq_len);
@@ -165,6 +199,17 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
   st = check_planes(k_codes, k_meta, v_codes, v_meta);
   if (st != KVQ_OK) return st;
   const DecodePlan pl = plan_decode(desc, num_seqs, num_q_heads, max_seq_len, options);
+  if (use_scratch) {
+    if (pl.total() > (size_t)KVQ_NOALLOC_SCRATCH_BYTES)
+      return fail(KVQ_ENOSPACE, "this decode needs %zu bytes of workspace; the allocation-free call has %zu",
+                  pl.total(), (size_t)KVQ_NOALLOC_SCRATCH_BYTES);
+    st = scratch_address(&workspace);
+    if (st != KVQ_OK) return st;
+    workspace_bytes = KVQ_NOALLOC_SCRATCH_BYTES;
+    // the counters must start at zero: a fill kernel, not a memset node
+    hipError_t e = kvq::launch_fill_zero(workspace, pl.counter_bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVQ_EHIP, "scratch clear: %s", hipGetErrorString(e));
+  }
   if (!workspace) return fail(KVQ_EINVAL, "workspace is NULL (%zu bytes needed)", pl.total());
   if (workspace_bytes < pl.total())
     return fail(KVQ_ENOSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total());
@@ -336,6 +381,20 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
   return decode_impl(desc, out, out_dtype, query, num_seqs, num_q_heads, k_codes, k_meta, v_codes, v_meta,
                      block_tables, block_tables_headwise, max_blocks_per_seq, seq_lens, max_seq_len, window,
                      softmax_scale, options, workspace, workspace_bytes, stream, nullptr);
+}
+
+kvq_status kvq_paged_decode_attention_noalloc(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
+                                              const void* query, int32_t num_seqs, int32_t num_q_heads,
+                                              const uint8_t* k_codes, const float* k_meta,
+                                              const uint8_t* v_codes, const float* v_meta,
+                                              const int32_t* block_tables,
+                                              const int32_t* block_tables_headwise,
+                                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                              int32_t max_seq_len, const int32_t* window,
+                                              float softmax_scale, void* stream) {
+  return decode_impl(desc, out, out_dtype, query, num_seqs, num_q_heads, k_codes, k_meta, v_codes, v_meta,
+                     block_tables, block_tables_headwise, max_blocks_per_seq, seq_lens, max_seq_len, window,
+                     softmax_scale, nullptr, nullptr, 0, stream, nullptr, true);
 }
 
 kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* out, int32_t out_dtype, const void* query,

@@ -261,6 +261,36 @@ def kvq_paged_decode_attention(desc: CacheDesc, query: torch.Tensor,
     return out
 
 
+def kvq_paged_decode_attention_noalloc(desc: CacheDesc, query: torch.Tensor,
+                                       k_codes: torch.Tensor, k_meta: torch.Tensor,
+                                       v_codes: torch.Tensor, v_meta: torch.Tensor,
+                                       seq_lens: torch.Tensor, max_seq_len: int,
+                                       block_tables: Optional[torch.Tensor] = None,
+                                       block_tables_headwise: Optional[torch.Tensor] = None,
+                                       window: Optional[torch.Tensor] = None,
+                                       softmax_scale: Optional[float] = None,
+                                       out: Optional[torch.Tensor] = None,
+                                       out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Decode attention with the library's device scratch as workspace (no
+    workspace argument; nothing is allocated when ``out`` is given)."""
+    dev = _check_query(desc, query)
+    B, Hq, D = query.shape
+    _check_planes(desc, k_codes, k_meta, v_codes, v_meta)
+    max_blocks = _check_tables(desc, B, block_tables, block_tables_headwise, dev)
+    _check_lens_window(desc, B, seq_lens, window, dev)
+    out, odt = _out_for(out, (B, Hq, D), out_dtype, dev)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    d = desc.c()
+    with torch.cuda.device(dev):
+        _check(_lib.load().kvq_paged_decode_attention_noalloc(
+            ctypes.byref(d), _ptr(out), odt, _ptr(query), int(B), int(Hq),
+            _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
+            _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
+            _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale), _stream(dev)))
+    return out
+
+
 def kvq_decode_step(desc: CacheDesc, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                     k_codes: torch.Tensor, k_meta: torch.Tensor,
                     v_codes: torch.Tensor, v_meta: torch.Tensor,

@@ -145,6 +145,29 @@ def _step(lib, d, **kw):
                                a["wsb"], None)
 
 
+def test_noalloc_rejects_oversize_and_validates(lib):
+    """The allocation-free decode validates like the decode call and refuses
+    a plan larger than its device scratch before touching the GPU."""
+    d = desc(H=8, bs=64)
+    P = ctypes.c_void_p(4096)
+
+    def call(**kw):
+        a = dict(out=P, odt=0, q=P, B=2, Hq=32, kc=P, km=P, vc=P, vm=P, bt=P, bth=None, mb=4, sl=P, msl=200,
+                 win=None, scale=0.125)
+        a.update(kw)
+        return lib.kvq_paged_decode_attention_noalloc(ctypes.byref(d), a["out"], a["odt"], a["q"], a["B"], a["Hq"],
+                                                      a["kc"], a["km"], a["vc"], a["vm"], a["bt"], a["bth"],
+                                                      a["mb"], a["sl"], a["msl"], a["win"], a["scale"], None)
+    need = ctypes.c_size_t()
+    assert lib.kvq_decode_workspace_size(ctypes.byref(d), 4096, 128, 64, None, ctypes.byref(need)) == 0
+    assert need.value > 8 << 20
+    assert call(B=4096, Hq=128, msl=64, mb=1) == _lib.KVQ_ENOSPACE
+    assert "allocation-free" in lib.kvq_last_error().decode()
+    assert call(Hq=12) == _lib.KVQ_EINVAL                 # GQA divisibility
+    assert call(bt=None) == _lib.KVQ_EINVAL               # no table
+    assert call(B=0) == _lib.KVQ_OK                       # nothing to do
+
+
 def test_decode_step_validation(lib):
     d = desc(H=4, bs=64)                                           # D 128: token stride >= 512
     P = ctypes.c_void_p(4096)
