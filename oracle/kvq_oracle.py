@@ -52,6 +52,11 @@ Readings where the pages are silent (each also listed in the design doc):
 * A token position p of sequence b attends (decode) to positions j < L_b that
   lie in a non-evicted block and, for a windowed kv head, j >= L_b - W.
   kv head = q head // (Hq/Hkv).  An empty allowed set gives output 0.
+* Attention sinks ([P3] Modifications: a sink_size parameter threaded into the
+  attention op, semantics unstated): a windowed kv head also attends the
+  first sink_size positions of the sequence (when present in the table), as
+  in sliding-window attention with sink tokens; heads without a window see
+  everything anyway.
 """
 from __future__ import annotations
 
@@ -373,12 +378,13 @@ def _attend(qs: np.ndarray, K: np.ndarray, V: np.ndarray, allowed: np.ndarray,
 def decode_attention(q, seq_lens, mode: int, head_dim: int, block_size: int,
                      num_kv_heads: int, k_codes, k_meta, v_codes, v_meta,
                      softmax_scale: float, signs=None, block_tables=None,
-                     block_tables_headwise=None, window=None, pairs=None):
+                     block_tables_headwise=None, window=None, pairs=None, sink_size=0):
     """Step O9: one query token per sequence, q [B, Hq, D] (float images of
     bf16).  Returns float64 [B, Hq, D].
 
     If ``pairs`` is given (list of (b, kv_head)), only those are computed and
-    the rest of the output stays NaN.
+    the rest of the output stays NaN.  ``sink_size``: a windowed head also
+    attends positions j < sink_size.
     """
     q = np.asarray(q, np.float64)
     B, Hq, D = q.shape
@@ -393,7 +399,8 @@ def decode_attention(q, seq_lens, mode: int, head_dim: int, block_size: int,
         allowed = present.copy()
         W = int(window[h]) if window is not None else 0
         if W > 0:
-            allowed &= np.arange(L) >= L - W
+            j = np.arange(L)
+            allowed &= (j >= L - W) | (j < sink_size)
         qs = q[b, h * G:(h + 1) * G]
         out[b, h * G:(h + 1) * G] = _attend(qs, K, V, np.broadcast_to(allowed, (G, L)),
                                              softmax_scale)
@@ -404,14 +411,15 @@ def prefill_attention(q, cu_seqlens_q, seq_lens, mode: int, head_dim: int,
                       block_size: int, num_kv_heads: int, k_codes, k_meta, v_codes,
                       v_meta, softmax_scale: float, signs=None, block_tables=None,
                       block_tables_headwise=None, window=None, pairs=None,
-                      rows=None):
+                      rows=None, sink_size=0):
     """Step O10: chunked prefill.  q [Tq, Hq, D]; sequence b owns query rows
     cu[b]..cu[b+1]-1, which sit at positions L_b - n_b + i (n_b = new tokens).
     Query at position p attends to keys j <= p that are present and, for a
     windowed kv head, j >= p - W + 1.  Returns float64 [Tq, Hq, D].
 
     ``pairs`` restricts the (b, kv_head) pairs computed; ``rows`` (an int array
-    of query indices within each sequence) restricts the query rows.
+    of query indices within each sequence) restricts the query rows;
+    ``sink_size``: a windowed head also attends positions j < sink_size.
     """
     q = np.asarray(q, np.float64)
     Tq, Hq, D = q.shape
@@ -436,7 +444,7 @@ def prefill_attention(q, cu_seqlens_q, seq_lens, mode: int, head_dim: int,
         allowed = (j <= pos) & present[None, :]
         W = int(window[h]) if window is not None else 0
         if W > 0:
-            allowed &= j >= pos - W + 1
+            allowed &= (j >= pos - W + 1) | (j < sink_size)
         for g in range(G):
             hq = h * G + g
             out[q0 + idx, hq] = _attend(q[q0 + idx, hq], K, V, allowed, softmax_scale)

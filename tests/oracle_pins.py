@@ -665,4 +665,51 @@ def check_prefill_vs_bruteforce(o):
     assert np.allclose(dec, out[cu[1:] - 1], atol=1e-13)
 
 
+def check_sinks(o):
+    """Attention sinks: a windowed head attends the window and the first
+    sink_size positions, checked against float64 SDPA with that union mask
+    for decode and (per query row) for prefill; sink_size 0 is the window
+    alone; sink_size >= L is the whole context."""
+    t = _tiny_cache(o, 1, seed=8)
+    kc, km, vc, vm = t["planes"]
+    D, bs, Hkv = t["D"], t["bs"], t["Hkv"]
+    q = _bf16_rows((2, 4, D), 81)
+    win = np.array([20, 0], np.int32)
+    for sink in (0, 3, 17):
+        out = o.decode_attention(q, t["lens"], 1, D, bs, Hkv, kc, km, vc, vm, 0.125, signs=t["signs"],
+                                 block_tables=t["bt"], window=win, sink_size=sink)
+        for b, L in enumerate(t["lens"]):
+            for hq in range(4):
+                h = hq // 2
+                K, V, _ = o.gather_head(b, h, int(L), 1, D, bs, Hkv, kc, km, vc, vm, t["signs"],
+                                        block_tables=t["bt"])
+                mask = np.ones((1, L), bool)
+                if win[h] > 0:
+                    mask[0, :L - win[h]] = False
+                    mask[0, :min(sink, L)] = True
+                ref = _sdpa64(q[b, hq][None], K, V, mask, 0.125)[0]
+                assert np.allclose(out[b, hq], ref, atol=1e-12), (sink, b, hq)
+    base = o.decode_attention(q, t["lens"], 1, D, bs, Hkv, kc, km, vc, vm, 0.125, signs=t["signs"],
+                              block_tables=t["bt"])
+    allsink = o.decode_attention(q, t["lens"], 1, D, bs, Hkv, kc, km, vc, vm, 0.125, signs=t["signs"],
+                                 block_tables=t["bt"], window=win, sink_size=1000)
+    assert np.allclose(base, allsink, atol=1e-13)
+    # prefill: row i at position p sees j <= p with j >= p - W + 1 or j < sink
+    n_new = np.array([9, 30])
+    cu = np.concatenate([[0], np.cumsum(n_new)])
+    qp = _bf16_rows((int(cu[-1]), 4, D), 82)
+    sink = 5
+    outp = o.prefill_attention(qp, cu, t["lens"], 1, D, bs, Hkv, kc, km, vc, vm, 0.125, signs=t["signs"],
+                               block_tables=t["bt"], window=win, sink_size=sink)
+    for b, L in enumerate(t["lens"]):
+        K, V, _ = o.gather_head(b, 0, int(L), 1, D, bs, Hkv, kc, km, vc, vm, t["signs"], block_tables=t["bt"])
+        for i in range(n_new[b]):
+            pos = L - n_new[b] + i
+            mask = np.zeros((1, L), bool)
+            mask[0, max(0, pos - win[0] + 1):pos + 1] = True
+            mask[0, :min(sink, pos + 1)] = True
+            ref = _sdpa64(qp[cu[b] + i, 0][None], K, V, mask, 0.125)[0]
+            assert np.allclose(outp[cu[b] + i, 0], ref, atol=1e-12), (b, i)
+
+
 ALL = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -25,9 +25,10 @@ MUTATIONS = {
     "dequant_wrong": ("return (np.asarray(codes, np.float64) * np.asarray(s, np.float64)[..., None]\n            + np.asarray(z, np.float64)[..., None])",
                       "return ((np.asarray(codes, np.float64) + np.asarray(z, np.float64)[..., None])\n            * np.asarray(s, np.float64)[..., None])"),
     "gqa_map": ("qs = q[b, h * G:(h + 1) * G]", "qs = q[b, h::num_kv_heads]"),
-    "window_off_by_one": ("allowed &= np.arange(L) >= L - W", "allowed &= np.arange(L) > L - W"),
+    "window_off_by_one": ("allowed &= (j >= L - W) | (j < sink_size)", "allowed &= (j > L - W) | (j < sink_size)"),
     "causal_strict": ("allowed = (j <= pos) & present[None, :]", "allowed = (j < pos) & present[None, :]"),
-    "prefill_window_off_by_one": ("allowed &= j >= pos - W + 1", "allowed &= j >= pos - W"),
+    "prefill_window_off_by_one": ("allowed &= (j >= pos - W + 1) | (j < sink_size)",
+                                  "allowed &= (j >= pos - W) | (j < sink_size)"),
     "evicted_read": ("present = ids >= 0", "present = ids >= -1"),
     "headwise_row": ("return np.asarray(block_tables_headwise)[b * num_kv_heads + h]", "return np.asarray(block_tables_headwise)[h * num_kv_heads + b]"),
     "scale_dropped": ("logits = scale * (np.asarray(qs, np.float64) @ K.T)", "logits = np.asarray(qs, np.float64) @ K.T"),
@@ -41,6 +42,8 @@ MUTATIONS = {
     "t_divide": ("t = (base * inv[..., None]).astype(_F32)", "t = (base / np.where(ok, s, _F32(1.0))[..., None]).astype(_F32)"),
     "sub_unrounded": ("base = (y - mn[..., None]).astype(_F32)", "base = y.astype(np.float64) - mn[..., None].astype(np.float64)"),
     "range_unrounded": ("s = ((mx - mn) / L).astype(_F32)", "s = ((mx.astype(np.float64) - mn) / L).astype(_F32)"),
+    "sink_off_by_one": ("allowed &= (j >= L - W) | (j < sink_size)", "allowed &= (j >= L - W) | (j <= sink_size)"),
+    "prefill_sink_dropped": ("allowed &= (j >= pos - W + 1) | (j < sink_size)", "allowed &= (j >= pos - W + 1)"),
     "headwise_slots_transposed": ("slots = np.asarray(slot_mapping_headwise, np.int64).reshape(T, Hkv)",
                                   "slots = np.asarray(slot_mapping_headwise, np.int64).reshape(Hkv, T).T"),
 }
