@@ -166,7 +166,8 @@ kvq_status kvq_workspace_init(void* workspace, size_t workspace_bytes, void* str
  * head h = hq / (Hq/Hkv) the output is softmax attention of query[b, hq] over
  * the dequantized, un-rotated keys/values of positions j < seq_lens[b] that
  * lie in a non-evicted block and, if window && window[h] > 0, satisfy
- * j >= seq_lens[b] - window[h].  No allowed position => output 0.
+ * j >= seq_lens[b] - window[h] or j < sink_size.  No allowed position =>
+ * output 0.
  *   out          (device) [B, Hq, D] float32 (KVQ_OUT_F32) or bf16 (KVQ_OUT_BF16)
  *   query        (device) bf16 [B, Hq, D]
  *   block_tables (device) int32 [B, max_blocks_per_seq], or NULL
@@ -178,6 +179,11 @@ kvq_status kvq_workspace_init(void* workspace, size_t workspace_bytes, void* str
  *                entries are clamped to it)
  *   max_seq_len  host upper bound on seq_lens, <= max_blocks_per_seq*block_size
  *   window       (device) int32 [Hkv], <= 0 = full context; or NULL
+ *   sink_size    (host) attention sinks: a windowed kv head also attends
+ *                positions j < sink_size (FastDeploy PR 7718, Modifications,
+ *                threads a sink_size into the attention op); <= 0 = none.
+ *                With sinks, a windowed head's walk starts at position 0 and
+ *                the tiles between the sinks and the window read nothing.
  *   softmax_scale  logits scale (usually 1/sqrt(D)); finite
  *   options      NULL, or the options given to kvq_decode_workspace_size
  *   workspace    (device) >= kvq_decode_workspace_size bytes, 256-byte
@@ -195,7 +201,7 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc,
                                       const int32_t* block_tables_headwise,
                                       int32_t max_blocks_per_seq,
                                       const int32_t* seq_lens, int32_t max_seq_len,
-                                      const int32_t* window,
+                                      const int32_t* window, int32_t sink_size,
                                       float softmax_scale,
                                       const kvq_decode_options* options,
                                       void* workspace, size_t workspace_bytes,
@@ -230,7 +236,7 @@ kvq_status kvq_paged_decode_attention_noalloc(const kvq_cache_desc* desc,
                                               const int32_t* block_tables_headwise,
                                               int32_t max_blocks_per_seq,
                                               const int32_t* seq_lens, int32_t max_seq_len,
-                                              const int32_t* window,
+                                              const int32_t* window, int32_t sink_size,
                                               float softmax_scale,
                                               void* stream);
 
@@ -269,7 +275,7 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc,
                            const int32_t* block_tables_headwise,
                            int32_t max_blocks_per_seq,
                            const int32_t* seq_lens, int32_t max_seq_len,
-                           const int32_t* window,
+                           const int32_t* window, int32_t sink_size,
                            float softmax_scale,
                            const kvq_decode_options* options,
                            void* workspace, size_t workspace_bytes,
@@ -285,15 +291,16 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc,
  * seq_lens[b].  Row (i, q head hq) attends, over kv head h = hq / (Hq/Hkv), to
  * the dequantized, un-rotated keys/values of positions j <= L_b - n_b + i that
  * lie in a non-evicted block and, if window && window[h] > 0, satisfy
- * j >= L_b - n_b + i - window[h] + 1.  No allowed position => output 0.
+ * j >= L_b - n_b + i - window[h] + 1 or j < sink_size.  No allowed position
+ * => output 0.
  *   out          (device) [total_q, Hq, D] float32 or bf16 (out_dtype)
  *   query        (device) bf16 [total_q, Hq, D]
  *   cu_seqlens_q (device) int32 [num_seqs + 1], non-decreasing, from 0
  *   max_q_len    host upper bound on every n_b (sizes the grid; rows past it
  *                are not computed)
  *   seq_lens     (device) int32 [num_seqs], each >= n_b and <= max_seq_len
- *   block tables, window, softmax_scale and the cache planes as for
- *   kvq_paged_decode_attention
+ *   block tables, window, sink_size, softmax_scale and the cache planes as
+ *   for kvq_paged_decode_attention
  *   workspace    (device) kvq_prefill_workspace_size bytes; may be NULL when
  *                that size is 0 (it is for every shape this library builds:
  *                each workgroup covers the whole key range of its rows)
@@ -310,7 +317,7 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc,
                                        const int32_t* block_tables_headwise,
                                        int32_t max_blocks_per_seq,
                                        const int32_t* seq_lens, int32_t max_seq_len,
-                                       const int32_t* window,
+                                       const int32_t* window, int32_t sink_size,
                                        float softmax_scale,
                                        void* workspace, size_t workspace_bytes,
                                        void* stream);

@@ -46,13 +46,13 @@ SIGNATURES = {
     "kvq_decode_workspace_size": (_I32, [_DESC, _I32, _I32, _I32, _OPT, ctypes.POINTER(_SZ)]),
     "kvq_workspace_init": (_I32, [_P, _SZ, _P]),
     "kvq_paged_decode_attention": (_I32, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                          _I32, _P, _I32, _P, ctypes.c_float, _OPT, _P, _SZ, _P]),
+                                          _I32, _P, _I32, _P, _I32, ctypes.c_float, _OPT, _P, _SZ, _P]),
     "kvq_paged_decode_attention_noalloc": (_I32, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                                  _I32, _P, _I32, _P, ctypes.c_float, _P]),
+                                                  _I32, _P, _I32, _P, _I32, ctypes.c_float, _P]),
     "kvq_decode_step": (_I32, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P,
-                               _P, _P, _I32, _P, _I32, _P, ctypes.c_float, _OPT, _P, _SZ, _P]),
+                               _P, _P, _I32, _P, _I32, _P, _I32, ctypes.c_float, _OPT, _P, _SZ, _P]),
     "kvq_paged_prefill_attention": (_I32, [_DESC, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                           _I32, _P, _I32, _P, ctypes.c_float, _P, _SZ, _P]),
+                                           _I32, _P, _I32, _P, _I32, ctypes.c_float, _P, _SZ, _P]),
     "kvq_prefill_workspace_size": (_I32, [_DESC, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "kvq_gather_dequant": (_I32, [_DESC, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _P]),
     "kvq_last_error": (ctypes.c_char_p, []),

@@ -192,9 +192,11 @@ struct TileInfo {
 // are row0 + 16 s (one block id per tile).  A block id that is negative
 // (evicted) or at or past num_blocks makes its sub-tiles invalid: no row is
 // formed for them and issue_loads reads nothing for them.
+// Attended positions of a pair: [start, L), plus [0, sink) when the head is
+// windowed (sink is 0 otherwise).
 template <bool CB>
 __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int tile, int te, int L, int start,
-                                              int bs_log2, int hkv, int h, int nblk) {
+                                              int sink, int bs_log2, int hkv, int h, int nblk) {
   TileInfo t;
   t.pos0 = tile * 64;
   t.valid = 0;
@@ -205,7 +207,7 @@ __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int pos = t.pos0 + 16 * s;
-      t.valid |= (okb && pos < L && pos + 15 >= start) ? 1u << s : 0u;
+      t.valid |= (okb && pos < L && (pos + 15 >= start || pos < sink)) ? 1u << s : 0u;
     }
     t.row0 = okb ? ((id * hkv + h) << bs_log2) + (t.pos0 & ((1 << bs_log2) - 1)) : 0;
     t.row1 = t.row0 + 16; t.row2 = t.row0 + 32; t.row3 = t.row0 + 48;
@@ -215,7 +217,7 @@ __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int 
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int pos = t.pos0 + 16 * s;
-    const bool in = tile < te && pos < L && pos + 15 >= start;
+    const bool in = tile < te && pos < L && (pos + 15 >= start || pos < sink);
     const int id = __builtin_amdgcn_readfirstlane(ids[in ? (pos >> bs_log2) - blk0 : 0]);
     const bool ok = in && id >= 0 && id < nblk;
     t.valid |= ok ? 1u << s : 0u;
@@ -330,7 +332,8 @@ struct LaneConst {
 // score needs a mask (wave-uniform; the masking sits behind a branch).
 template <int MODE, int D, int PHI>
 __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const TileInfo& t, WaveState& st,
-                                             f32x4_t* acc, const LaneConst& lc, int L, int start, bool full) {
+                                             f32x4_t* acc, const LaneConst& lc, int L, int start, int sink,
+                                             bool full) {
   using Gm = Geo<MODE, D, PHI>;
   constexpr int M = Gm::M;
   const int q = lc.q, phi_col = lc.phi_col;
@@ -385,7 +388,7 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pos = t.pos0 + 16 * sg + 4 * qm + i;
-        const bool keep = tv && pos < L && pos >= start;
+        const bool keep = tv && pos < L && (pos >= start || pos < sink);
         sc[tau][i] = keep ? sc[tau][i] : kNegInf;
         svv[tau][i] = keep ? svv[tau][i] : 0.0f;
         zvv[tau][i] = keep ? zvv[tau][i] : 0.0f;
@@ -479,10 +482,10 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
 
 template <int MODE, int D, int PHI>
 __device__ __forceinline__ void run_tile(const Buf<MODE, D, PHI>& b, const TileInfo& t, WaveState& st,
-                                         f32x4_t* acc, const LaneConst& lc, int L, int start) {
+                                         f32x4_t* acc, const LaneConst& lc, int L, int start, int sink) {
   if (!t.valid) return;
-  const bool full = t.valid == 0xFu && t.pos0 >= start && t.pos0 + 64 <= L;
-  compute_tile<MODE, D, PHI>(b, t, st, acc, lc, L, start, full);
+  const bool full = t.valid == 0xFu && (t.pos0 >= start || t.pos0 + 64 <= sink) && t.pos0 + 64 <= L;
+  compute_tile<MODE, D, PHI>(b, t, st, acc, lc, L, start, sink, full);
 }
 
 // Waves per SIMD, i.e. resident four-wave workgroups per CU: two where the
@@ -664,16 +667,20 @@ struct Smem {
 };
 
 // Tiles of (sequence b, kv head h): 64-position tiles from the window start
-// (or 0) to seq_len; *t0 = first tile, *L = attended end, *start = begin.
+// (or 0; or 0 as well when the window cuts and sinks are on, the tiles in
+// between then reading nothing) to seq_len; *t0 = first tile, *L = attended
+// end, *start = window start.
+__device__ __forceinline__ int first_tile(int start, int sink) { return (start > 0 && sink > 0) ? 0 : start / 64; }
+
 __device__ __forceinline__ int pair_geo(const DecodeParams& p, int pair, int* t0, int* L, int* start) {
   const int b = pair / p.hkv, h = pair - b * p.hkv;
   const int l = min(p.seq_lens[b], p.max_seq_len);   // host checked max_seq_len <= max_blocks * bs
   const int W = p.window ? p.window[h] : 0;
   const int s = (W > 0 && l > W) ? l - W : 0;
-  *t0 = s / 64;
+  *t0 = first_tile(s, p.sink);
   *L = l;
   *start = s;
-  return l > 0 ? (l + 63) / 64 - s / 64 : 0;
+  return l > 0 ? (l + 63) / 64 - *t0 : 0;
 }
 
 // The share partition: workgroup w takes tiles [start(w), start(w + 1)) of
@@ -731,13 +738,14 @@ __device__ __forceinline__ void cursor_seek(Cursor& c, const Smem<D, PHI, NWV>& 
 
 template <bool CB, int D, int PHI, int NWV>
 __device__ __forceinline__ TileInfo cursor_info(const Cursor& c, const Smem<D, PHI, NWV>& sm, int wave, int bl,
-                                                int hkv, int nblk) {
+                                                int hkv, int nblk, int sink) {
   if (c.ls >= c.nseg) {
     TileInfo t;
     t.pos0 = 0; t.row0 = 0; t.row1 = 0; t.row2 = 0; t.row3 = 0; t.valid = 0;
     return t;
   }
-  return tile_info<CB>(sm.ids + c.off, c.blk0, c.tb + wave + NWV * c.li, c.te, c.L, c.start, bl, hkv, c.h, nblk);
+  return tile_info<CB>(sm.ids + c.off, c.blk0, c.tb + wave + NWV * c.li, c.te, c.L, c.start,
+                       c.start > 0 ? sink : 0, bl, hkv, c.h, nblk);
 }
 
 template <int D, int PHI, int NWV>
@@ -1010,7 +1018,7 @@ void decode_kernel(DecodeParams p) {
       const int pair = c0 + ci;
       const int L = __builtin_amdgcn_readfirstlane(sm.plen[ci]);
       const int start = __builtin_amdgcn_readfirstlane(sm.pst[ci]);
-      const int t0 = start / 64;
+      const int t0 = first_tile(start, p.sink);
       const int e = min(s1, e_my);
       const int tb = t0 + (x - s0), te = t0 + (e - s0);
       const int blk0 = (tb * 64) >> bl;
@@ -1113,10 +1121,10 @@ void decode_kernel(DecodeParams p) {
     if (cur.ls < nseg) {
       const int b0 = __builtin_amdgcn_readfirstlane(sm.seg[cur.ls].b);
       const int32_t* trow = p.tables + (int64_t)(p.headwise ? b0 * hkv + cur.h : b0) * p.max_blocks;
-      ta = tile_info<CB>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te, cur.L, cur.start, bl,
-                         hkv, cur.h, nblk);
+      ta = tile_info<CB>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te, cur.L, cur.start,
+                         cur.start > 0 ? p.sink : 0, bl, hkv, cur.h, nblk);
     } else {
-      ta = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk);
+      ta = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk, p.sink);
     }
     cursor_next(cur, sm, wave);
     // the ids and query rows are back (the table read above waited for all
@@ -1175,6 +1183,7 @@ void decode_kernel(DecodeParams p) {
       const SegRec& sr = sm.seg[k];
       const int L = __builtin_amdgcn_readfirstlane(sr.L);
       const int start = __builtin_amdgcn_readfirstlane(sr.start);
+      const int sinkE = start > 0 ? p.sink : 0;
       const int n2 = wave_tiles2<NWV>(__builtin_amdgcn_readfirstlane(sr.te) -
                                       __builtin_amdgcn_readfirstlane(sr.tb), wave);
       LaneConst lc;
@@ -1196,14 +1205,14 @@ void decode_kernel(DecodeParams p) {
       for (int i = 0; i < Gm::DT; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
       for (int it = 0; it < n2; it += 2) {
-        const TileInfo tn = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk);
+        const TileInfo tn = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk, p.sink);
         cursor_next(cur, sm, wave);
         issue_loads<MODE, D, PHI, CB>(bb, tn, p, r, q, phi_col);
-        run_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start);
-        const TileInfo t2 = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk);
+        run_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start, sinkE);
+        const TileInfo t2 = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk, p.sink);
         cursor_next(cur, sm, wave);
         issue_loads<MODE, D, PHI, CB>(ba, t2, p, r, q, phi_col);
-        run_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start);
+        run_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start, sinkE);
         ta = t2;
       }
 

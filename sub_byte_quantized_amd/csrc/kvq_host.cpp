@@ -174,8 +174,8 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
                                       const uint8_t* v_codes, const float* v_meta,
                                       const int32_t* block_tables, const int32_t* block_tables_headwise,
                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                      int32_t max_seq_len, const int32_t* window, float softmax_scale,
-                                      const kvq_decode_options* options,
+                                      int32_t max_seq_len, const int32_t* window, int32_t sink_size,
+                                      float softmax_scale, const kvq_decode_options* options,
                                       void* workspace, size_t workspace_bytes, void* stream,
                                       const kvq::WriteParams* wp, bool use_scratch = false) {
   kvq_status st = check_desc(desc);
@@ -233,6 +233,7 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
   p.num_blocks = desc->num_blocks;
   p.max_blocks = max_blocks_per_seq;
   p.max_seq_len = max_seq_len;
+  p.sink = sink_size > 0 ? sink_size : 0;
   p.block_size = desc->block_size;
   p.block_size_log2 = __builtin_ctz((unsigned)desc->block_size);
   p.hq = num_q_heads;
@@ -375,12 +376,12 @@ kvq_status kvq_paged_decode_attention(const kvq_cache_desc* desc, void* out, int
                                       const uint8_t* v_codes, const float* v_meta,
                                       const int32_t* block_tables, const int32_t* block_tables_headwise,
                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                      int32_t max_seq_len, const int32_t* window, float softmax_scale,
-                                      const kvq_decode_options* options,
+                                      int32_t max_seq_len, const int32_t* window, int32_t sink_size,
+                                      float softmax_scale, const kvq_decode_options* options,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(desc, out, out_dtype, query, num_seqs, num_q_heads, k_codes, k_meta, v_codes, v_meta,
                      block_tables, block_tables_headwise, max_blocks_per_seq, seq_lens, max_seq_len, window,
-                     softmax_scale, options, workspace, workspace_bytes, stream, nullptr);
+                     sink_size, softmax_scale, options, workspace, workspace_bytes, stream, nullptr);
 }
 
 kvq_status kvq_paged_decode_attention_noalloc(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
@@ -390,11 +391,11 @@ kvq_status kvq_paged_decode_attention_noalloc(const kvq_cache_desc* desc, void* 
                                               const int32_t* block_tables,
                                               const int32_t* block_tables_headwise,
                                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                              int32_t max_seq_len, const int32_t* window,
+                                              int32_t max_seq_len, const int32_t* window, int32_t sink_size,
                                               float softmax_scale, void* stream) {
   return decode_impl(desc, out, out_dtype, query, num_seqs, num_q_heads, k_codes, k_meta, v_codes, v_meta,
                      block_tables, block_tables_headwise, max_blocks_per_seq, seq_lens, max_seq_len, window,
-                     softmax_scale, nullptr, nullptr, 0, stream, nullptr, true);
+                     sink_size, softmax_scale, nullptr, nullptr, 0, stream, nullptr, true);
 }
 
 kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* out, int32_t out_dtype, const void* query,
@@ -404,8 +405,8 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* out, int32_t out_dt
                            uint8_t* v_codes, float* v_meta, const int32_t* block_tables,
                            const int32_t* block_tables_headwise, int32_t max_blocks_per_seq,
                            const int32_t* seq_lens, int32_t max_seq_len, const int32_t* window,
-                           float softmax_scale, const kvq_decode_options* options, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           int32_t sink_size, float softmax_scale, const kvq_decode_options* options,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   kvq_status st = check_desc(desc);
   if (st != KVQ_OK) return st;
   if (num_seqs > 0) {
@@ -428,7 +429,7 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* out, int32_t out_dt
   w.slot_hw = slot_mapping_headwise;
   return decode_impl(desc, out, out_dtype, query, num_seqs, num_q_heads, k_codes, k_meta, v_codes, v_meta,
                      block_tables, block_tables_headwise, max_blocks_per_seq, seq_lens, max_seq_len, window,
-                     softmax_scale, options, workspace, workspace_bytes, stream, &w);
+                     sink_size, softmax_scale, options, workspace, workspace_bytes, stream, &w);
 }
 
 kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
@@ -438,8 +439,9 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
                                        const uint8_t* v_codes, const float* v_meta,
                                        const int32_t* block_tables, const int32_t* block_tables_headwise,
                                        int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                       int32_t max_seq_len, const int32_t* window, float softmax_scale,
-                                       void* workspace, size_t workspace_bytes, void* stream) {
+                                       int32_t max_seq_len, const int32_t* window, int32_t sink_size,
+                                       float softmax_scale, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
   kvq_status st = check_prefill_sizes(desc, num_seqs, num_q_heads, max_q_len, max_seq_len);
   if (st != KVQ_OK) return st;
   const int group = num_q_heads / desc->num_kv_heads;
@@ -482,6 +484,7 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
   p.num_blocks = desc->num_blocks;
   p.max_blocks = max_blocks_per_seq;
   p.max_seq_len = max_seq_len;
+  p.sink = sink_size > 0 ? sink_size : 0;
   p.block_size_log2 = __builtin_ctz((unsigned)desc->block_size);
   p.hq = num_q_heads;
   p.hkv = desc->num_kv_heads;

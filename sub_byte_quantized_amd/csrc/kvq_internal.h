@@ -59,6 +59,7 @@ struct DecodeParams {
   int32_t headwise;
   int32_t max_blocks;
   int32_t max_seq_len;          // seq_lens entries are clamped to it
+  int32_t sink;                 // windowed heads also attend positions < sink (>= 0)
   int32_t block_size;
   int32_t block_size_log2;
   int32_t hq;
@@ -92,6 +93,7 @@ struct PrefillParams {
   int32_t headwise;
   int32_t max_blocks;
   int32_t max_seq_len;          // seq_lens entries are clamped to it
+  int32_t sink;                 // windowed heads also attend positions < sink (>= 0)
   int32_t block_size_log2;
   int32_t hq;
   int32_t hkv;

@@ -115,13 +115,22 @@ struct Stage {
   int ok;
 };
 
-// Plane row of position j (<= khi) of the walked table row, or -1 when the
-// position is absent: past khi, in an evicted (-1) block, or in a block id at
-// or past num_blocks.
-__device__ __forceinline__ int plane_row(const int32_t* trow, int j, int khi, int bs_log2, int hkv, int h,
-                                         int nblk) {
+// Plane row of position j of the walked table row, or -1 when no row of the
+// workgroup sees the position or it is absent: past khi, in the gap between
+// the sinks and the earliest window start [sink, klo), in an evicted (-1)
+// block, or in a block id at or past num_blocks.
+struct KeyRange {
+  int klo, khi, sink;   // positions the workgroup's rows may see: [0, sink) and [klo, khi]
+};
+
+__device__ __forceinline__ bool key_seen(const KeyRange& kr, int j) {
+  return j <= kr.khi && (j >= kr.klo || j < kr.sink);
+}
+
+__device__ __forceinline__ int plane_row(const int32_t* trow, int j, const KeyRange& kr, int bs_log2, int hkv,
+                                         int h, int nblk) {
   int id = -1;
-  if (j <= khi) id = trow[j >> bs_log2];
+  if (key_seen(kr, j)) id = trow[j >> bs_log2];
   return (id >= 0 && id < nblk) ? ((id * hkv + h) << bs_log2) + (j & ((1 << bs_log2) - 1)) : -1;
 }
 
@@ -132,11 +141,11 @@ __device__ __forceinline__ int plane_row(const int32_t* trow, int j, int khi, in
 // (score -inf, weight 0).
 template <int MODE, int D>
 __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillParams& p, const int32_t* trow,
-                                           int tau, int khi, int h, int tid) {
+                                           int tau, const KeyRange& kr, int h, int tid) {
   using Gp = PGeo<MODE, D>;
   const int n = tid >> 2, qd = tid & 3;
   const int nblk = (int)p.num_blocks;   // < 2^31 (checked on the host)
-  const int row = plane_row(trow, tau * kPKeys + n, khi, p.block_size_log2, p.hkv, h, nblk);
+  const int row = plane_row(trow, tau * kPKeys + n, kr, p.block_size_log2, p.hkv, h, nblk);
   st.ok = row >= 0;
 #pragma unroll
   for (int i = 0; i < Gp::KNW; ++i) st.k[i] = 0u;
@@ -155,12 +164,14 @@ __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillPara
   // a group write one whole V^T row in LDS (no bank conflicts).
   const int kq = tid & 15, wd = tid >> 4;
   const int j0 = tau * kPKeys + 4 * kq;
-  const int vrow0 = plane_row(trow, j0, khi, p.block_size_log2, p.hkv, h, nblk);
+  // the four positions share a block (block sizes are >= 16)
+  const KeyRange all = {0, kr.khi, 0};
+  const int vrow0 = plane_row(trow, j0, all, p.block_size_log2, p.hkv, h, nblk);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int w = 0; w < Gp::VNW; ++w) st.v[i][w] = 0u;
-    if (vrow0 >= 0 && j0 + i <= khi)
+    if (vrow0 >= 0 && key_seen(kr, j0 + i))
       load_bytes<Gp::VNB>(st.v[i], p.v_codes + (int64_t)(vrow0 + i) * Gp::P + wd * Gp::VNB);
   }
 }
@@ -258,6 +269,7 @@ struct WaveCtx {
   float sp[2], qp[2];                     // logit = sp * (s_K raw + z_K qp), raw = 2^14 A + 2^7 B + C
   int rpos[2], rlo[2];                    // row position and window start
   int W, wpos_lo, wpos_hi;
+  int sink;                               // windowed head: positions < sink are seen too (else 0)
   bool wave_live;
   int lane, r, q;
 };
@@ -266,18 +278,20 @@ struct WaveCtx {
 // buffer PAR, the next tile's LDS stores into the other buffer, barrier.
 template <int MODE, int D, int PAR>
 __device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& wc, Stage<MODE, D>& stg,
-                                          const PrefillParams& p, const int32_t* trow, int tau, int tau1,
-                                          int khi, int h, int tid) {
+                                          const PrefillParams& p, const int32_t* trow, int tau, int tau_next,
+                                          const KeyRange& kr, int h, int tid) {
   using Gp = PGeo<MODE, D>;
   const PBuf<MODE, D>& cb = sm.buf[PAR];
-  const bool more = tau < tau1;
-  if (more) stage_load<MODE, D>(stg, p, trow, tau + 1, khi, h, tid);
+  const bool more = tau_next >= 0;
+  if (more) stage_load<MODE, D>(stg, p, trow, tau_next, kr, h, tid);
   const int W = wc.W, r = wc.r, q = wc.q;
     const int pos0 = tau * kPKeys;
-    const bool active = wc.wave_live && pos0 <= wc.wpos_hi && (W <= 0 || pos0 + kPKeys - 1 >= wc.wpos_lo - W + 1);
+    const bool active = wc.wave_live && pos0 <= wc.wpos_hi &&
+                        (W <= 0 || pos0 + kPKeys - 1 >= wc.wpos_lo - W + 1 || pos0 < wc.sink);
     if (active) {
       const bool all_ok = __all(cb.ok[wc.lane >> 2][wc.lane & 3] != 0);
-      const bool full = all_ok && pos0 + kPKeys - 1 <= wc.wpos_lo && (W <= 0 || pos0 >= wc.wpos_hi - W + 1);
+      const bool full = all_ok && pos0 + kPKeys - 1 <= wc.wpos_lo &&
+                        (W <= 0 || pos0 >= wc.wpos_hi - W + 1 || pos0 + kPKeys <= wc.sink);
       // ---- S^T = K Q^T, three int32 accumulators (pieces a, b and c)
       float x[4][2][4];
 #pragma unroll
@@ -314,7 +328,7 @@ __device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& 
             const int j = pos0 + 16 * kb + 4 * q + i;
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-              const bool keep = okv[i] != 0 && j <= wc.rpos[rb] && j >= wc.rlo[rb];
+              const bool keep = okv[i] != 0 && j <= wc.rpos[rb] && (j >= wc.rlo[rb] || j < wc.sink);
               x[kb][rb][i] = keep ? x[kb][rb][i] : kNegInf;
             }
           }
@@ -434,7 +448,11 @@ void prefill_kernel(PrefillParams p) {
   const int pbase = L - nq + tok0;                // position of the tile's first token
   const int khi = pbase + ntok - 1;               // last position any row may see
   const int klo = W > 0 ? max(0, pbase - W + 1) : 0;
-  const int tau0 = klo / kPKeys;
+  // sinks: a windowed head also sees positions < sink; the key tiles walked
+  // are those of [0, sink) then those of [klo, khi] (a tile in both counts once)
+  const int sinkE = (W > 0 && klo > 0) ? min(p.sink, klo) : 0;
+  const int ns_tiles = (sinkE + kPKeys - 1) / kPKeys;       // tiles 0 .. ns_tiles - 1
+  const int tau0 = max(klo / kPKeys, ns_tiles);
   const int tau1 = khi >= 0 ? khi / kPKeys : -1;  // inclusive; none when khi < 0
   const int32_t* trow = p.tables + (int64_t)(p.headwise ? b * p.hkv + h : b) * p.max_blocks;
 
@@ -446,7 +464,13 @@ void prefill_kernel(PrefillParams p) {
 
   // ---- first key tile's loads overlap the query prologue
   Stage<MODE, D> stg;
-  if (tau0 <= tau1) stage_load<MODE, D>(stg, p, trow, tau0, khi, h, tid);
+  const KeyRange kr = {klo, khi, sinkE};
+  // the walk: k = 0 .. nwalk - 1 visits tile walk_tile(k)
+  const int nwin = tau1 >= tau0 ? tau1 - tau0 + 1 : 0;
+  const int nwalk = (khi >= 0 ? min(ns_tiles, khi / kPKeys + 1) : 0) + nwin;
+  const int nsw = nwalk - nwin;                               // sink tiles walked
+  auto walk_tile = [&](int k) { return k < nsw ? k : tau0 + (k - nsw); };
+  if (nwalk > 0) stage_load<MODE, D>(stg, p, trow, walk_tile(0), kr, h, tid);
 
   // ---- query prologue: rows (token t, head g) -> R q
   for (int e = tid; e < kPRows * D; e += 64 * kPWaves) {
@@ -553,7 +577,7 @@ void prefill_kernel(PrefillParams p) {
     sm.buf[bsel].vt[D + 4 + rem / (Gp::VROW / 16)][rem % (Gp::VROW / 16)] = u32x4_t{0u, 0u, 0u, 0u};
   }
 
-  if (tau0 <= tau1) stage_store<MODE, D>(stg, sm.buf[0], tid);
+  if (nwalk > 0) stage_store<MODE, D>(stg, sm.buf[0], tid);
   __syncthreads();
 
   WaveCtx<MODE, D> wc{};
@@ -568,14 +592,15 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int db = 0; db <= Gp::DB; ++db) wc.o[rb][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  wc.W = W; wc.wave_live = wave_live; wc.wpos_lo = wpos_lo; wc.wpos_hi = wpos_hi;
+  wc.W = W; wc.wave_live = wave_live; wc.wpos_lo = wpos_lo; wc.wpos_hi = wpos_hi; wc.sink = sinkE;
   wc.lane = lane; wc.r = r; wc.q = q;
 
   // two tiles per iteration so that each buffer's LDS offsets are constants
-  for (int tau = tau0; tau <= tau1; tau += 2) {
-    tile_step<MODE, D, 0>(sm, wc, stg, p, trow, tau, tau1, khi, h, tid);
-    if (tau + 1 > tau1) break;
-    tile_step<MODE, D, 1>(sm, wc, stg, p, trow, tau + 1, tau1, khi, h, tid);
+  for (int k = 0; k < nwalk; k += 2) {
+    tile_step<MODE, D, 0>(sm, wc, stg, p, trow, walk_tile(k), k + 1 < nwalk ? walk_tile(k + 1) : -1, kr, h, tid);
+    if (k + 1 >= nwalk) break;
+    tile_step<MODE, D, 1>(sm, wc, stg, p, trow, walk_tile(k + 1), k + 2 < nwalk ? walk_tile(k + 2) : -1, kr, h,
+                          tid);
   }
 
   // ---- epilogue: normalize into LDS rows, R^T, store

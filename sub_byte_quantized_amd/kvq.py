@@ -238,7 +238,7 @@ def kvq_paged_decode_attention(desc: CacheDesc, query: torch.Tensor,
                                out: Optional[torch.Tensor] = None,
                                out_dtype: torch.dtype = torch.float32,
                                workspace: Optional[torch.Tensor] = None,
-                               num_workgroups: int = 0) -> torch.Tensor:
+                               num_workgroups: int = 0, sink_size: int = 0) -> torch.Tensor:
     """Decode attention for query [B, Hq, D] (bf16); returns out [B, Hq, D]."""
     dev = _check_query(desc, query)
     B, Hq, D = query.shape
@@ -256,7 +256,7 @@ def kvq_paged_decode_attention(desc: CacheDesc, query: torch.Tensor,
         ctypes.byref(d), _ptr(out), odt, _ptr(query), int(B), int(Hq),
         _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
         _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
-        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale), _opts(num_workgroups),
+        _ptr(seq_lens), int(max_seq_len), _ptr(window), int(sink_size), float(softmax_scale), _opts(num_workgroups),
         _ptr(workspace), workspace.numel(), _stream(dev)))
     return out
 
@@ -270,7 +270,8 @@ def kvq_paged_decode_attention_noalloc(desc: CacheDesc, query: torch.Tensor,
                                        window: Optional[torch.Tensor] = None,
                                        softmax_scale: Optional[float] = None,
                                        out: Optional[torch.Tensor] = None,
-                                       out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+                                       out_dtype: torch.dtype = torch.float32,
+                                       sink_size: int = 0) -> torch.Tensor:
     """Decode attention with the library's device scratch as workspace (no
     workspace argument; nothing is allocated when ``out`` is given)."""
     dev = _check_query(desc, query)
@@ -287,7 +288,7 @@ def kvq_paged_decode_attention_noalloc(desc: CacheDesc, query: torch.Tensor,
             ctypes.byref(d), _ptr(out), odt, _ptr(query), int(B), int(Hq),
             _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
             _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
-            _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale), _stream(dev)))
+            _ptr(seq_lens), int(max_seq_len), _ptr(window), int(sink_size), float(softmax_scale), _stream(dev)))
     return out
 
 
@@ -304,7 +305,7 @@ def kvq_decode_step(desc: CacheDesc, query: torch.Tensor, key: torch.Tensor, val
                     out: Optional[torch.Tensor] = None,
                     out_dtype: torch.dtype = torch.float32,
                     workspace: Optional[torch.Tensor] = None,
-                    num_workgroups: int = 0) -> torch.Tensor:
+                    num_workgroups: int = 0, sink_size: int = 0) -> torch.Tensor:
     """One decode step in one launch: quantize-on-write of each sequence's
     new token (key/value [B, Hkv, D] bf16, token b at slot_mapping[b], which
     must be position seq_lens[b] - 1 of sequence b's table), then decode
@@ -338,7 +339,7 @@ def kvq_decode_step(desc: CacheDesc, query: torch.Tensor, key: torch.Tensor, val
         _ptr(slot_mapping), _ptr(slot_mapping_headwise),
         _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
         _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
-        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale), _opts(num_workgroups),
+        _ptr(seq_lens), int(max_seq_len), _ptr(window), int(sink_size), float(softmax_scale), _opts(num_workgroups),
         _ptr(workspace), workspace.numel(), _stream(dev)))
     return out
 
@@ -354,7 +355,7 @@ def kvq_paged_prefill_attention(desc: CacheDesc, query: torch.Tensor, cu_seqlens
                                 softmax_scale: Optional[float] = None,
                                 out: Optional[torch.Tensor] = None,
                                 out_dtype: torch.dtype = torch.float32,
-                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                                workspace: Optional[torch.Tensor] = None, sink_size: int = 0) -> torch.Tensor:
     """Chunked-prefill attention for query [total_q, Hq, D] (bf16) with
     sequence b owning rows cu_seqlens_q[b]..cu_seqlens_q[b+1]-1; returns out
     [total_q, Hq, D]."""
@@ -380,7 +381,7 @@ def kvq_paged_prefill_attention(desc: CacheDesc, query: torch.Tensor, cu_seqlens
         ctypes.byref(d), _ptr(out), odt, _ptr(query), _ptr(cu_seqlens_q), B, int(Hq), int(max_q_len),
         _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta),
         _ptr(block_tables), _ptr(block_tables_headwise), max_blocks,
-        _ptr(seq_lens), int(max_seq_len), _ptr(window), float(softmax_scale),
+        _ptr(seq_lens), int(max_seq_len), _ptr(window), int(sink_size), float(softmax_scale),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)))
     return out
 

@@ -94,7 +94,7 @@ def _decode(lib, d, **kw):
     a.update(kw)
     return lib.kvq_paged_decode_attention(ctypes.byref(d), a["out"], a["odt"], a["q"], a["B"], a["Hq"],
                                           a["kc"], a["km"], a["vc"], a["vm"], a["bt"], a["bth"], a["mb"],
-                                          a["sl"], a["msl"], a["win"], a["scale"], a["opt"], a["ws"], a["wsb"],
+                                          a["sl"], a["msl"], a["win"], 0, a["scale"], a["opt"], a["ws"], a["wsb"],
                                           None)
 
 
@@ -141,7 +141,7 @@ def _step(lib, d, **kw):
     a.update(kw)
     return lib.kvq_decode_step(ctypes.byref(d), a["out"], a["odt"], a["q"], a["B"], a["Hq"], a["key"], a["value"],
                                a["ks"], a["vs"], a["sm"], a["smh"], a["kc"], a["km"], a["vc"], a["vm"], a["bt"],
-                               a["bth"], a["mb"], a["sl"], a["msl"], a["win"], a["scale"], a["opt"], a["ws"],
+                               a["bth"], a["mb"], a["sl"], a["msl"], a["win"], 0, a["scale"], a["opt"], a["ws"],
                                a["wsb"], None)
 
 
@@ -157,7 +157,7 @@ def test_noalloc_rejects_oversize_and_validates(lib):
         a.update(kw)
         return lib.kvq_paged_decode_attention_noalloc(ctypes.byref(d), a["out"], a["odt"], a["q"], a["B"], a["Hq"],
                                                       a["kc"], a["km"], a["vc"], a["vm"], a["bt"], a["bth"],
-                                                      a["mb"], a["sl"], a["msl"], a["win"], a["scale"], None)
+                                                      a["mb"], a["sl"], a["msl"], a["win"], 0, a["scale"], None)
     need = ctypes.c_size_t()
     assert lib.kvq_decode_workspace_size(ctypes.byref(d), 4096, 128, 64, None, ctypes.byref(need)) == 0
     assert need.value > 8 << 20
@@ -193,7 +193,7 @@ def _prefill(lib, d, **kw):
     a.update(kw)
     return lib.kvq_paged_prefill_attention(ctypes.byref(d), a["out"], a["odt"], a["q"], a["cu"], a["B"], a["Hq"],
                                            a["mq"], a["kc"], a["km"], a["vc"], a["vm"], a["bt"], a["bth"],
-                                           a["mb"], a["sl"], a["msl"], a["win"], a["scale"], a["ws"], a["wsb"],
+                                           a["mb"], a["sl"], a["msl"], a["win"], 0, a["scale"], a["ws"], a["wsb"],
                                            None)
 
 
