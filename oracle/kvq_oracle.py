@@ -52,6 +52,13 @@ Readings where the pages are silent (each also listed in the design doc):
 * A token position p of sequence b attends (decode) to positions j < L_b that
   lie in a non-evicted block and, for a windowed kv head, j >= L_b - W.
   kv head = q head // (Hq/Hkv).  An empty allowed set gives output 0.
+* Dynamic per-channel INT8 ([P4] 运行机制: the INT8 scales are computed along
+  the token axis the first time a layer receives K/V, symmetric, per channel,
+  separately for K and V): s[h, d] = max_t |x[t, h, d]| / 127 over that first
+  batch, in float32; every row written later is quantized with those fixed
+  scales, c = clamp(rint(x * fl(1/s_d)), -127, 127) (values beyond the
+  calibrated range saturate), a channel with a zero or subnormal scale gets
+  code 0, and x_hat = c * s_d.  No rotation and no per-token metadata.
 * Attention sinks ([P3] Modifications: a sink_size parameter threaded into the
   attention op, semantics unstated): a windowed kv head also attends the
   first sink_size positions of the sequence (when present in the table), as
@@ -67,11 +74,12 @@ import numpy as np
 INT8_SYM = 0
 INT4_ASYM = 1
 INT2_ASYM = 2
-MODES = (INT8_SYM, INT4_ASYM, INT2_ASYM)
-BITS = {INT8_SYM: 8, INT4_ASYM: 4, INT2_ASYM: 2}
+INT8_CHANNEL = 3
+MODES = (INT8_SYM, INT4_ASYM, INT2_ASYM)          # the per-token-head modes
+BITS = {INT8_SYM: 8, INT4_ASYM: 4, INT2_ASYM: 2, INT8_CHANNEL: 8}
 # number of quantization steps: codes span [0, L] (asymmetric) or [-L, L]
-LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3}
-META_FLOATS = {INT8_SYM: 1, INT4_ASYM: 2, INT2_ASYM: 2}
+LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3, INT8_CHANNEL: 127}
+META_FLOATS = {INT8_SYM: 1, INT4_ASYM: 2, INT2_ASYM: 2, INT8_CHANNEL: 0}
 
 _F32 = np.float32
 _FLT_MIN = _F32(2.0 ** -126)
@@ -219,7 +227,7 @@ def dequant_rows_f64(codes: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndar
 def pack_codes(codes: np.ndarray, mode: int) -> np.ndarray:
     """codes [..., D] -> uint8 [..., D*b/8]."""
     c = np.asarray(codes, np.int64)
-    if mode == INT8_SYM:
+    if BITS[mode] == 8:
         return (c & 0xFF).astype(np.uint8)
     b = BITS[mode]
     per = 8 // b
@@ -234,7 +242,7 @@ def pack_codes(codes: np.ndarray, mode: int) -> np.ndarray:
 def unpack_codes(packed: np.ndarray, mode: int, head_dim: int) -> np.ndarray:
     """uint8 [..., D*b/8] -> int32 codes [..., D] (INT8 sign-extended)."""
     p = np.asarray(packed, np.uint8).astype(np.int64)
-    if mode == INT8_SYM:
+    if BITS[mode] == 8:
         return np.where(p >= 128, p - 256, p).astype(np.int32)
     b = BITS[mode]
     per = 8 // b
@@ -242,6 +250,32 @@ def unpack_codes(packed: np.ndarray, mode: int, head_dim: int) -> np.ndarray:
     out = np.stack(parts, axis=-1).reshape(p.shape[:-1] + (p.shape[-1] * per,))
     assert out.shape[-1] == head_dim
     return out.astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Dynamic per-channel INT8 ([P4] 运行机制: scales from the first K/V a layer
+# receives, along the token axis, symmetric, per channel, K and V separately)
+# --------------------------------------------------------------------------
+def calibrate_channel_scales(x: np.ndarray) -> np.ndarray:
+    """Scales of one of K or V from the first batch x [T, Hkv, D] (float32
+    images of bf16): s[h, d] = max_t |x[t, h, d]| / 127, one correctly rounded
+    float32 division."""
+    a = np.max(np.abs(np.asarray(x, _F32)), axis=0)
+    return (a / _F32(127.0)).astype(_F32)
+
+
+def quantize_rows_channel(y: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Codes of rows y [R, D] against fixed per-channel scales [D] (or [R, D]):
+    c = clamp(rint(y * fl(1/s)), -127, 127) in float32; a channel whose scale
+    is zero, subnormal or NaN gets code 0."""
+    y = np.asarray(y, _F32)
+    s = np.broadcast_to(np.asarray(scales, _F32), y.shape)
+    ok = s >= _FLT_MIN
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        inv = np.where(ok, _F32(1.0) / np.where(ok, s, _F32(1.0)), _F32(0.0)).astype(_F32)
+        t = (y * inv).astype(_F32)
+    c = np.clip(np.rint(t), -127, 127)
+    return np.where(ok, c, 0).astype(np.int32)
 
 
 # --------------------------------------------------------------------------
@@ -263,13 +297,14 @@ def encode_rows(x_bf16_as_f32: np.ndarray, mode: int, signs=None):
 def write_cache(k: np.ndarray, v: np.ndarray, mode: int, block_size: int,
                 k_codes: np.ndarray, k_meta: np.ndarray,
                 v_codes: np.ndarray, v_meta: np.ndarray,
-                slot_mapping=None, slot_mapping_headwise=None, signs=None):
+                slot_mapping=None, slot_mapping_headwise=None, signs=None, channel_scales=None):
     """Quantize the rows of k, v [T, Hkv, D] (float32 images of bf16) and store
     them at their slots (step O6).
 
     slot_mapping [T] (the same slot for every kv head) or slot_mapping_headwise
     [T, Hkv]; slot = block * block_size + offset; a negative slot skips the row.
-    Planes are modified in place.
+    Planes are modified in place.  INT8_CHANNEL takes channel_scales [2, Hkv, D]
+    (K then V) and writes no metadata.
     """
     T, Hkv, D = k.shape
     if (slot_mapping is None) == (slot_mapping_headwise is None):
@@ -278,14 +313,19 @@ def write_cache(k: np.ndarray, v: np.ndarray, mode: int, block_size: int,
         slots = np.repeat(np.asarray(slot_mapping, np.int64)[:, None], Hkv, axis=1)
     else:
         slots = np.asarray(slot_mapping_headwise, np.int64).reshape(T, Hkv)
-    for src, codes_pl, meta_pl in ((k, k_codes, k_meta), (v, v_codes, v_meta)):
+    tt, hh = np.nonzero(slots >= 0)           # rows written: token tt, kv head hh
+    sl = slots[tt, hh]
+    blk, off = sl // block_size, sl % block_size
+    for kv, (src, codes_pl, meta_pl) in enumerate(((k, k_codes, k_meta), (v, v_codes, v_meta))):
+        if mode == INT8_CHANNEL:
+            sc = np.asarray(channel_scales, _F32)[kv]                         # [Hkv, D]
+            packed = pack_codes(quantize_rows_channel(np.asarray(src, _F32), sc[None]), mode)
+            codes_pl[blk, hh, off, :] = packed[tt, hh]
+            continue
         packed, s, z, _ = encode_rows(np.asarray(src, _F32).reshape(T * Hkv, D), mode, signs)
         packed = packed.reshape(T, Hkv, -1)
         s = s.reshape(T, Hkv)
         z = z.reshape(T, Hkv)
-        tt, hh = np.nonzero(slots >= 0)
-        sl = slots[tt, hh]
-        blk, off = sl // block_size, sl % block_size
         codes_pl[blk, hh, off, :] = packed[tt, hh]
         meta_pl[blk, hh, off, 0] = s[tt, hh]
         if mode != INT8_SYM:
@@ -308,7 +348,7 @@ def table_row(b: int, h: int, num_kv_heads: int, block_tables=None,
 def gather_head(b: int, h: int, n_pos: int, mode: int, head_dim: int,
                 block_size: int, num_kv_heads: int,
                 k_codes, k_meta, v_codes, v_meta, signs=None,
-                block_tables=None, block_tables_headwise=None):
+                block_tables=None, block_tables_headwise=None, channel_scales=None):
     """Dequantized, un-rotated K and V (float64 [n_pos, D]) of positions
     0..n_pos-1 of (b, h), plus a bool [n_pos] that is False for positions in an
     evicted (-1) block.  Evicted rows are returned as zeros and never read."""
@@ -321,8 +361,11 @@ def gather_head(b: int, h: int, n_pos: int, mode: int, head_dim: int,
     if np.any(present):
         bi = ids[present]
         off = pos[present] % block_size
-        for pl_c, pl_m, out in ((k_codes, k_meta, K), (v_codes, v_meta, V)):
+        for kv, (pl_c, pl_m, out) in enumerate(((k_codes, k_meta, K), (v_codes, v_meta, V))):
             codes = unpack_codes(pl_c[bi, h, off, :], mode, head_dim)
+            if mode == INT8_CHANNEL:
+                out[present] = codes * np.asarray(channel_scales, np.float64)[kv, h][None, :]
+                continue
             s = pl_m[bi, h, off, 0]
             z = pl_m[bi, h, off, 1] if mode != INT8_SYM else np.zeros_like(s)
             xhat = dequant_rows_f64(codes, s, z)
@@ -332,7 +375,7 @@ def gather_head(b: int, h: int, n_pos: int, mode: int, head_dim: int,
 
 def gather_dequant(cu_seq_lens, mode: int, head_dim: int, block_size: int,
                    num_kv_heads: int, k_codes, k_meta, v_codes, v_meta, signs=None,
-                   block_tables=None, block_tables_headwise=None):
+                   block_tables=None, block_tables_headwise=None, channel_scales=None):
     """Dequantize-gather: the custom op that fetches K/V out of the quantized
     cache and dequantizes them ([P1] review thread, the cache-fetch operator
     with its composed-op test version; [P4] 运行机制: prefill gathers and
@@ -351,7 +394,7 @@ def gather_dequant(cu_seq_lens, mode: int, head_dim: int, block_size: int,
         for h in range(num_kv_heads):
             Kb, Vb, _ = gather_head(b, h, n, mode, head_dim, block_size, num_kv_heads,
                                     k_codes, k_meta, v_codes, v_meta, signs,
-                                    block_tables, block_tables_headwise)
+                                    block_tables, block_tables_headwise, channel_scales)
             K[cu[b]:cu[b + 1], h] = Kb
             V[cu[b]:cu[b + 1], h] = Vb
     return K, V
@@ -378,7 +421,8 @@ def _attend(qs: np.ndarray, K: np.ndarray, V: np.ndarray, allowed: np.ndarray,
 def decode_attention(q, seq_lens, mode: int, head_dim: int, block_size: int,
                      num_kv_heads: int, k_codes, k_meta, v_codes, v_meta,
                      softmax_scale: float, signs=None, block_tables=None,
-                     block_tables_headwise=None, window=None, pairs=None, sink_size=0):
+                     block_tables_headwise=None, window=None, pairs=None, sink_size=0,
+                     channel_scales=None):
     """Step O9: one query token per sequence, q [B, Hq, D] (float images of
     bf16).  Returns float64 [B, Hq, D].
 
@@ -395,7 +439,7 @@ def decode_attention(q, seq_lens, mode: int, head_dim: int, block_size: int,
         L = int(seq_lens[b])
         K, V, present = gather_head(b, h, L, mode, head_dim, block_size, num_kv_heads,
                                     k_codes, k_meta, v_codes, v_meta, signs,
-                                    block_tables, block_tables_headwise)
+                                    block_tables, block_tables_headwise, channel_scales)
         allowed = present.copy()
         W = int(window[h]) if window is not None else 0
         if W > 0:
@@ -411,7 +455,7 @@ def prefill_attention(q, cu_seqlens_q, seq_lens, mode: int, head_dim: int,
                       block_size: int, num_kv_heads: int, k_codes, k_meta, v_codes,
                       v_meta, softmax_scale: float, signs=None, block_tables=None,
                       block_tables_headwise=None, window=None, pairs=None,
-                      rows=None, sink_size=0):
+                      rows=None, sink_size=0, channel_scales=None):
     """Step O10: chunked prefill.  q [Tq, Hq, D]; sequence b owns query rows
     cu[b]..cu[b+1]-1, which sit at positions L_b - n_b + i (n_b = new tokens).
     Query at position p attends to keys j <= p that are present and, for a
@@ -435,7 +479,7 @@ def prefill_attention(q, cu_seqlens_q, seq_lens, mode: int, head_dim: int,
             continue
         K, V, present = gather_head(b, h, L, mode, head_dim, block_size, num_kv_heads,
                                     k_codes, k_meta, v_codes, v_meta, signs,
-                                    block_tables, block_tables_headwise)
+                                    block_tables, block_tables_headwise, channel_scales)
         idx = np.arange(n) if rows is None else np.asarray([r for r in rows if r < n], np.int64)
         if idx.size == 0:
             continue

@@ -712,4 +712,80 @@ def check_sinks(o):
             assert np.allclose(outp[cu[b] + i, 0], ref, atol=1e-12), (b, i)
 
 
+# --------------------------------------------------- per-channel INT8 ------
+def _channel_batch(r, T, Hkv, D, exps):
+    """[T, Hkv, D] rows whose per-(head, channel) absolute maximum over tokens
+    is exactly 127 * 2^-e (e from `exps`), other entries k * 2^-e with |k| <=
+    127 integer, so the scales are 2^-e exactly and every code is k."""
+    e = r.choice(exps, size=(Hkv, D))
+    k = r.integers(-127, 128, size=(T, Hkv, D))
+    k[0] = np.where(r.integers(0, 2, size=(Hkv, D)) == 1, 127, -127)   # the maximum
+    return (k * 2.0 ** -e[None]).astype(F32), k, (2.0 ** -e).astype(F32)
+
+
+def check_channel_calibration_and_codes(o):
+    """Per-channel INT8: the calibrated scale of each (head, channel) is its
+    maximum |x| over the first batch / 127 (2^-e exactly on power-of-two
+    grids); rows on the grid quantize to their integers; later values beyond
+    the calibrated range saturate at +-127; an all-zero channel has scale 0
+    and codes 0; exact .5 steps round half to even."""
+    r = np.random.default_rng(31)
+    T, Hkv, D = 9, 3, 64
+    x, k, sexp = _channel_batch(r, T, Hkv, D, [0, 3, 7])
+    x[:, 1, 5] = 0.0
+    k[:, 1, 5] = 0
+    sexp[1, 5] = 0.0
+    sc = o.calibrate_channel_scales(x)
+    assert sc.shape == (Hkv, D) and sc.dtype == F32
+    assert np.array_equal(sc, sexp)
+    c = o.quantize_rows_channel(x, sc[None])
+    assert np.array_equal(c, k)
+    # saturation of later tokens beyond the calibrated maximum
+    big = (np.array([300.0, -1000.0, 128.0, -127.6]) * sexp[0, :4]).astype(F32)
+    cb = o.quantize_rows_channel(big[None], sc[0, :4][None])
+    assert np.array_equal(cb[0], [127, -127, 127, -127])
+    # ties: t = k + 1/2 exactly on the grid -> even neighbour
+    ks = np.arange(-10, 10)
+    ties = ((ks + 0.5) * sexp[2, 0]).astype(F32)
+    ct = o.quantize_rows_channel(ties[:, None], np.full((len(ks), 1), sc[2, 0], F32))[:, 0]
+    assert np.array_equal(ct, np.where(ks % 2 == 0, ks, ks + 1))
+    # a zero-scale channel gives code 0 whatever the later value
+    assert o.quantize_rows_channel(np.array([[5.0]], F32), np.array([[0.0]], F32))[0, 0] == 0
+
+
+def check_channel_write_gather_and_attention(o):
+    """Per-channel INT8 through the paged layout: grid rows written with their
+    own calibrated scales come back exactly from the gather (shuffled table,
+    K and V scales distinct); decode equals float64 SDPA over those rows."""
+    r = np.random.default_rng(32)
+    D, bs, Hkv, L = 64, 16, 2, 40
+    k, _, _ = _channel_batch(r, L, Hkv, D, [1, 4])
+    v, _, _ = _channel_batch(r, L, Hkv, D, [0, 2, 5])
+    sc = np.stack([o.calibrate_channel_scales(k), o.calibrate_channel_scales(v)])
+    assert not np.array_equal(sc[0], sc[1])
+    nblk = (L + bs - 1) // bs
+    nb = nblk + 2
+    bt = r.permutation(nb)[:nblk][None].astype(np.int64)
+    pos = np.arange(L)
+    slots = bt[0, pos // bs] * bs + pos % bs
+    cs, ms = o.plane_shapes(o.INT8_CHANNEL, D, Hkv, bs, nb)
+    assert ms[-1] == 0 and cs[-1] == D
+    kc = np.full(cs, 0xFF, np.uint8)
+    vc = np.full(cs, 0xFF, np.uint8)
+    km = np.zeros(ms, F32)
+    vm = np.zeros(ms, F32)
+    o.write_cache(k, v, o.INT8_CHANNEL, bs, kc, km, vc, vm, slot_mapping=slots, channel_scales=sc)
+    K, V = o.gather_dequant(np.array([0, L]), o.INT8_CHANNEL, D, bs, Hkv, kc, km, vc, vm, block_tables=bt,
+                            channel_scales=sc)
+    assert np.array_equal(K, k.astype(np.float64)) and np.array_equal(V, v.astype(np.float64))
+    q = _bf16_rows((1, 4, D), 91)
+    out = o.decode_attention(q, np.array([L]), o.INT8_CHANNEL, D, bs, Hkv, kc, km, vc, vm, 0.125,
+                             block_tables=bt, channel_scales=sc)
+    for hq in range(4):
+        h = hq // 2
+        ref = _sdpa64(q[0, hq][None], k[:, h].astype(np.float64), v[:, h].astype(np.float64),
+                      np.ones((1, L), bool), 0.125)[0]
+        assert np.allclose(out[0, hq], ref, atol=1e-12), hq
+
+
 ALL = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

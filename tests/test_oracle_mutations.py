@@ -18,8 +18,10 @@ MUTATIONS = {
     "unrotate_no_signs": ("return fwht(x) * np.asarray(signs, np.float64) / math.sqrt(D)", "return fwht(x) / math.sqrt(D)"),
     "floor_not_rint": ("c = np.clip(np.rint(t), lo, hi)", "c = np.clip(np.floor(t), lo, hi)"),
     "zero_is_max": ("z = mn.astype(_F32)", "z = mx.astype(_F32)"),
-    "int4_levels_16": ("LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3}", "LEVELS = {INT8_SYM: 127, INT4_ASYM: 16, INT2_ASYM: 3}"),
-    "int8_levels_128": ("LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3}", "LEVELS = {INT8_SYM: 128, INT4_ASYM: 15, INT2_ASYM: 3}"),
+    "int4_levels_16": ("LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3, INT8_CHANNEL: 127}",
+                       "LEVELS = {INT8_SYM: 127, INT4_ASYM: 16, INT2_ASYM: 3, INT8_CHANNEL: 127}"),
+    "int8_levels_128": ("LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3, INT8_CHANNEL: 127}",
+                        "LEVELS = {INT8_SYM: 128, INT4_ASYM: 15, INT2_ASYM: 3, INT8_CHANNEL: 127}"),
     "nibble_order": ("out |= g[..., k] << (b * k)", "out |= g[..., k] << (b * (per - 1 - k))"),
     "int8_no_sign_extend": ("return np.where(p >= 128, p - 256, p).astype(np.int32)", "return p.astype(np.int32)"),
     "dequant_wrong": ("return (np.asarray(codes, np.float64) * np.asarray(s, np.float64)[..., None]\n            + np.asarray(z, np.float64)[..., None])",
@@ -44,6 +46,12 @@ MUTATIONS = {
     "range_unrounded": ("s = ((mx - mn) / L).astype(_F32)", "s = ((mx.astype(np.float64) - mn) / L).astype(_F32)"),
     "sink_off_by_one": ("allowed &= (j >= L - W) | (j < sink_size)", "allowed &= (j >= L - W) | (j <= sink_size)"),
     "prefill_sink_dropped": ("allowed &= (j >= pos - W + 1) | (j < sink_size)", "allowed &= (j >= pos - W + 1)"),
+    "channel_axis": ("a = np.max(np.abs(np.asarray(x, _F32)), axis=0)", "a = np.max(np.abs(np.asarray(x, _F32)), axis=1)"),
+    "channel_no_saturation": ("c = np.clip(np.rint(t), -127, 127)", "c = np.rint(t)"),
+    "channel_kv_swapped": ("out[present] = codes * np.asarray(channel_scales, np.float64)[kv, h][None, :]",
+                           "out[present] = codes * np.asarray(channel_scales, np.float64)[1 - kv, h][None, :]"),
+    "channel_scale_head": ("out[present] = codes * np.asarray(channel_scales, np.float64)[kv, h][None, :]",
+                           "out[present] = codes * np.asarray(channel_scales, np.float64)[kv, 0][None, :]"),
     "headwise_slots_transposed": ("slots = np.asarray(slot_mapping_headwise, np.int64).reshape(T, Hkv)",
                                   "slots = np.asarray(slot_mapping_headwise, np.int64).reshape(Hkv, T).T"),
 }
