@@ -47,7 +47,9 @@
  *    codes: uint8   [num_blocks, num_kv_heads, block_size, P]
  *           P = head_dim * b / 8, b = 8, 4, 2 bits
  *    meta : float32 [num_blocks, num_kv_heads, block_size, M]
- *           M = 1 (INT8: scale) or 2 (INT4/INT2: scale, zero point)
+ *           M = 1 (INT8: scale), 2 (INT4/INT2: scale, zero point) or 0
+ *           (INT8_CHANNEL: the scales are per channel, in
+ *           desc->channel_scales; meta pointers may then be NULL)
  *  A (token, kv head) row of codes is contiguous.  INT4 puts element 2j in the
  *  low nibble of byte j; INT2 puts element 4j+k in bits 2k..2k+1 of byte j;
  *  INT8 stores two's complement codes in [-127, 127].  Reconstruction:
@@ -76,8 +78,14 @@ typedef enum {
  * INT4 / INT2: per-token-head asymmetric, s = (max y - min y) / L,
  * z = min y, L = 15 / 3, codes = clamp(rint((y - z) / s), 0, L), computed as
  * (y - z) * (1/s) in float32 with round-half-to-even.  A row whose scale is
- * zero or subnormal gets all-zero codes. */
-typedef enum { KVQ_INT8_SYM = 0, KVQ_INT4_ASYM = 1, KVQ_INT2_ASYM = 2 } kvq_mode;
+ * zero or subnormal gets all-zero codes.
+ * INT8_CHANNEL: dynamic per-channel symmetric INT8 (the
+ * vllm-ascend-quantized-kv-cache package, 运行机制): one scale per (K or V,
+ * kv head, channel), s_d = max_t |x_d| / 127 over the first K/V a layer
+ * receives (kvq_calibrate_channel_scales), then fixed; codes
+ * clamp(rint(x_d * (1/s_d)), -127, 127), saturating; x_hat = c * s_d.  No
+ * rotation and no per-row metadata (the meta planes are empty). */
+typedef enum { KVQ_INT8_SYM = 0, KVQ_INT4_ASYM = 1, KVQ_INT2_ASYM = 2, KVQ_INT8_CHANNEL = 3 } kvq_mode;
 
 typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 } kvq_out_dtype;
 
@@ -91,8 +99,13 @@ typedef struct {
    * With signs d, every K and V row x is stored as the codes of
    * y = (1/sqrt(D)) * H_D (d .* x), H_D the Sylvester Hadamard matrix in
    * natural order; attention pre-rotates the query with the same matrix and
-   * rotates its output back, so results are in the original basis. */
+   * rotates its output back, so results are in the original basis.  Must be
+   * NULL for KVQ_INT8_CHANNEL. */
   const float* rot_signs;
+  /* (device) KVQ_INT8_CHANNEL only: float32 [2][num_kv_heads][head_dim]
+   * scales, K then V (from kvq_calibrate_channel_scales); ignored by the
+   * other modes.  Required by every call that quantizes or reads codes. */
+  const float* channel_scales;
 } kvq_cache_desc;
 
 /* Options of a decode launch.  Pass NULL for the defaults. */
@@ -141,6 +154,21 @@ kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc,
                                  uint8_t* k_codes, float* k_meta,
                                  uint8_t* v_codes, float* v_meta,
                                  void* stream);
+
+/* Per-channel scales of KVQ_INT8_CHANNEL from a layer's first K/V (the
+ * vllm-ascend-quantized-kv-cache package, 运行机制: computed along the token
+ * axis the first time the layer receives K/V, symmetric, K and V apart):
+ * scales_out[0][h][d] = max_t |key[t, h, d]| / 127 and scales_out[1][h][d]
+ * from value, in float32 (correctly rounded division), over t < num_tokens.
+ * A channel whose maximum is 0 gets scale 0 (its codes are then 0).
+ *   key, value, *_tok_stride: as for kvq_reshape_and_cache
+ *   scales_out   (device) float32 [2, Hkv, D], 16-byte aligned; written, not read
+ * desc->mode must be KVQ_INT8_CHANNEL (desc->channel_scales is not read).
+ * num_tokens == 0 writes zeros.  One kernel launch. */
+kvq_status kvq_calibrate_channel_scales(const kvq_cache_desc* desc,
+                                        const void* key, const void* value,
+                                        int64_t key_tok_stride, int64_t value_tok_stride,
+                                        int32_t num_tokens, float* scales_out, void* stream);
 
 /* Workspace bytes kvq_paged_decode_attention and kvq_decode_step need for
  * these sizes and options (host only; options NULL = defaults, and the same

@@ -13,14 +13,15 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE, KVQ_EHIP = range(5)
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_EUNSUPPORTED", 3: "KVQ_ENOSPACE", 4: "KVQ_EHIP"}
-KVQ_INT8_SYM, KVQ_INT4_ASYM, KVQ_INT2_ASYM = 0, 1, 2
+KVQ_INT8_SYM, KVQ_INT4_ASYM, KVQ_INT2_ASYM, KVQ_INT8_CHANNEL = 0, 1, 2, 3
 KVQ_OUT_F32, KVQ_OUT_BF16 = 0, 1
 
 
 class CacheDesc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("num_blocks", ctypes.c_int64), ("rot_signs", ctypes.c_void_p)]
+                ("num_blocks", ctypes.c_int64), ("rot_signs", ctypes.c_void_p),
+                ("channel_scales", ctypes.c_void_p)]
 
 
 class DecodeOptions(ctypes.Structure):
@@ -43,6 +44,7 @@ _OPT = ctypes.POINTER(DecodeOptions)
 SIGNATURES = {
     "kvq_query_layout": (_I32, [_DESC, ctypes.POINTER(Layout)]),
     "kvq_reshape_and_cache": (_I32, [_DESC, _P, _P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _P]),
+    "kvq_calibrate_channel_scales": (_I32, [_DESC, _P, _P, _I64, _I64, _I32, _P, _P]),
     "kvq_decode_workspace_size": (_I32, [_DESC, _I32, _I32, _I32, _OPT, ctypes.POINTER(_SZ)]),
     "kvq_workspace_init": (_I32, [_P, _SZ, _P]),
     "kvq_paged_decode_attention": (_I32, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,

@@ -238,8 +238,8 @@ struct Buf {
   using Gm = Geo<MODE, D, PHI>;
   uint32_t k[Gm::NKT][Gm::KW];
   uint32_t v[16][Gm::VW];
-  float km[Gm::NKT][4 * Gm::M];
-  float vm[Gm::NKT][4 * Gm::M];
+  float km[Gm::NKT][4 * (Gm::M > 0 ? Gm::M : 1)];   // unused without per-row metadata
+  float vm[Gm::NKT][4 * (Gm::M > 0 ? Gm::M : 1)];
 };
 
 template <int MODE, int D, int PHI, bool CB>
@@ -359,7 +359,8 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
     for (int i = 0; i < 4; ++i) {
       // 2^7 a + b is exact in int32 (|.| < 2^29); one rounding joins c
       const float raw = __builtin_fmaf((float)((ia[i] << 7) + ib[i]), 128.0f, (float)ic[i]);
-      const float s = M == 2 ? b.km[tau][2 * i] : b.km[tau][i];
+      // per-channel INT8: the K scales are folded into the query pieces
+      const float s = M == 0 ? 1.0f : (M == 2 ? b.km[tau][2 * i] : b.km[tau][i]);
       const float z = M == 2 ? b.km[tau][2 * i + 1] : 0.0f;
       sc[tau][i] = __builtin_fmaf(raw, s, z * lc.q1r);
     }
@@ -371,7 +372,7 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
   for (int tau = 0; tau < Gm::NKT; ++tau)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      svv[tau][i] = M == 2 ? b.vm[tau][2 * i] : b.vm[tau][i];
+      svv[tau][i] = M == 0 ? 1.0f : (M == 2 ? b.vm[tau][2 * i] : b.vm[tau][i]);
       zvv[tau][i] = M == 2 ? b.vm[tau][2 * i + 1] : 0.0f;
     }
   if (__builtin_expect(!full, 0)) {
@@ -494,7 +495,7 @@ __device__ __forceinline__ void run_tile(const Buf<MODE, D, PHI>& b, const TileI
 // the lightest; one where a tile needs the whole register file.
 template <int MODE, int D, int PHI>
 constexpr int decode_waves_per_simd() {
-  return (PHI == 1 || (MODE == 0 && D == 128 && PHI < 4)) ? 1 : ((MODE == 2 && PHI == 4) ? 3 : 2);
+  return (PHI == 1 || (mode_bits(MODE) == 8 && D == 128 && PHI < 4)) ? 1 : ((MODE == 2 && PHI == 4) ? 3 : 2);
 }
 
 // Waves per workgroup.  INT4 and INT2: all of a CU's waves in one
@@ -504,7 +505,7 @@ constexpr int decode_waves_per_simd() {
 // workgroup's segment barriers and prologue overlap another's loads
 // (measured faster for each).
 template <int MODE, int D, int PHI>
-constexpr int decode_wg_waves() { return MODE != 0 ? 4 * decode_waves_per_simd<MODE, D, PHI>() : 4; }
+constexpr int decode_wg_waves() { return mode_bits(MODE) != 8 ? 4 * decode_waves_per_simd<MODE, D, PHI>() : 4; }
 
 // ---------------------------------------------------------------------------
 // Whole rows of D values, one row per wave: lane holds d = E*lane + e with
@@ -546,7 +547,7 @@ __device__ __forceinline__ uint32_t load_qrow(const uint16_t* src, int lane) {
 // same wave, in order).
 template <int MODE, int D, int PHI, bool ROT>
 __device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, float* scratch, int8_t* qa,
-                                           int8_t* qb, int8_t* qc, float* qs, float* q1, int lane) {
+                                           int8_t* qb, int8_t* qc, float* qs, float* q1, int h, int lane) {
   using Gm = Geo<MODE, D, PHI>;
   constexpr int E = D / 64;
   float x[E];
@@ -560,6 +561,10 @@ __device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, 
 #pragma unroll
     for (int e = 0; e < E; ++e) x[e] *= p.signs[E * lane + e];
     wave_fwht<D>(x, lane);
+  }
+  if constexpr (MODE == kChannelMode) {   // q . (c (.) s_K) = (q (.) s_K) . c
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] *= p.chs[(int64_t)h * D + E * lane + e];
   }
   const float qmul = ROT ? p.qscale * p.inv_sqrt_d : p.qscale;
   float mx = 0.0f;
@@ -597,13 +602,19 @@ __device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, 
 }
 
 // One output row from its D normalized values in LDS: R^T (FWHT, signs,
-// 1/sqrt(D)) when rotated, then float32 or bf16 stores.
-template <int D, bool ROT>
+// 1/sqrt(D)) when rotated, the V channel scales for per-channel INT8, then
+// float32 or bf16 stores.
+template <int MODE, int D, bool ROT>
 __device__ __forceinline__ void finish_row(const DecodeParams& p, const float* src, int64_t orow, int lane) {
   constexpr int E = D / 64;
   float x[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) x[e] = src[E * lane + e];
+  if constexpr (MODE == kChannelMode) {   // sum_t p_t c_t (.) s_V
+    const int h = (int)((orow % p.hq) / p.group);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] *= p.chs[((int64_t)p.hkv + h) * D + E * lane + e];
+  }
   if constexpr (ROT) {
     wave_fwht<D>(x, lane);
 #pragma unroll
@@ -773,7 +784,7 @@ __device__ __forceinline__ float load_dev(const float* a) {
 // the thread folds each over its pieces in slot order with the online-softmax
 // update, and requests the (m, l, acc) of KP pieces of every value at once,
 // so a pass over pairs of at most KP pieces waits on memory once.
-template <int D, int PHI, int NWV, bool ROT, int KP>
+template <int MODE, int D, int PHI, int NWV, bool ROT, int KP>
 __device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI, NWV>& sm, int np, int s0a, int na,
                                              int64_t o0a, int s0b, int nb, int64_t o0b, int tid) {
   constexpr int NT = 64 * NWV;
@@ -843,8 +854,8 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI,
   }
   __syncthreads();
   for (int g = wave; g < G; g += NWV) {
-    finish_row<D, ROT>(p, sm.fw.fin[0][g], o0a + g, lane);
-    if (np > 1) finish_row<D, ROT>(p, sm.fw.fin[1][g], o0b + g, lane);
+    finish_row<MODE, D, ROT>(p, sm.fw.fin[0][g], o0a + g, lane);
+    if (np > 1) finish_row<MODE, D, ROT>(p, sm.fw.fin[1][g], o0b + g, lane);
   }
 }
 
@@ -1172,8 +1183,8 @@ void decode_kernel(DecodeParams p) {
       if (rr < nseg * G) {
         const int k = rr / G, g = rr - k * G;
         prep_query<MODE, D, PHI, ROT>(p, raw[i], sm.qrow[wave], sm.qp[0][k * Sm::GM + g], sm.qp[1][k * Sm::GM + g],
-                                      sm.qp[2][k * Sm::GM + g], &sm.qs[k][g],
-                                      &sm.q1[k][g], plane);
+                                      sm.qp[2][k * Sm::GM + g], &sm.qs[k][g], &sm.q1[k][g],
+                                      __builtin_amdgcn_readfirstlane(sm.seg[k].h), plane);
       }
     }
     __syncthreads();
@@ -1287,7 +1298,7 @@ void decode_kernel(DecodeParams p) {
           if (e < G * D) sm.fw.fin[0][e / D][e % D] = lsum[j] > 0.0f ? val[j] / lsum[j] : 0.0f;
         }
         __syncthreads();
-        for (int g = wave; g < G; g += NWV) finish_row<D, ROT>(p, sm.fw.fin[0][g], orow0 + g, elane);
+        for (int g = wave; g < G; g += NWV) finish_row<MODE, D, ROT>(p, sm.fw.fin[0][g], orow0 + g, elane);
       } else {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -1340,7 +1351,7 @@ void decode_kernel(DecodeParams p) {
       // eight pieces per round trip, four in the variants with three waves per
       // SIMD (168 registers)
       constexpr int KP = decode_waves_per_simd<MODE, D, PHI>() >= 3 ? 4 : 8;
-      merge_pieces<D, PHI, NWV, ROT, KP>(p, sm, np, s0a, na, o0a, s0b, nb, o0b, tid);
+      merge_pieces<MODE, D, PHI, NWV, ROT, KP>(p, sm, np, s0a, na, o0a, s0b, nb, o0b, tid);
       if (tid < np) atomicExch(p.counters + (tid ? pb : pa), 0);
     }
   }
@@ -1365,8 +1376,12 @@ hipError_t launch_decode_p(const DecodeParams& p, hipStream_t s) {
 
 template <int MODE>
 hipError_t launch_decode_m(int d, bool rot, const DecodeParams& p, hipStream_t s) {
-  if (d == 64) return rot ? launch_decode_p<MODE, 64, true>(p, s) : launch_decode_p<MODE, 64, false>(p, s);
-  return rot ? launch_decode_p<MODE, 128, true>(p, s) : launch_decode_p<MODE, 128, false>(p, s);
+  if constexpr (MODE == kChannelMode) {   // no rotation in this mode (checked on the host)
+    return d == 64 ? launch_decode_p<MODE, 64, false>(p, s) : launch_decode_p<MODE, 128, false>(p, s);
+  } else {
+    if (d == 64) return rot ? launch_decode_p<MODE, 64, true>(p, s) : launch_decode_p<MODE, 64, false>(p, s);
+    return rot ? launch_decode_p<MODE, 128, true>(p, s) : launch_decode_p<MODE, 128, false>(p, s);
+  }
 }
 
 }  // namespace
@@ -1377,6 +1392,7 @@ int decode_wgs_per_cu(int mode, int d, int group) {
   KVQ_W(0, 64, 4) KVQ_W(0, 64, 2) KVQ_W(0, 64, 1) KVQ_W(0, 128, 4) KVQ_W(0, 128, 2) KVQ_W(0, 128, 1)
   KVQ_W(1, 64, 4) KVQ_W(1, 64, 2) KVQ_W(1, 64, 1) KVQ_W(1, 128, 4) KVQ_W(1, 128, 2) KVQ_W(1, 128, 1)
   KVQ_W(2, 64, 4) KVQ_W(2, 64, 2) KVQ_W(2, 64, 1) KVQ_W(2, 128, 4) KVQ_W(2, 128, 2) KVQ_W(2, 128, 1)
+  KVQ_W(3, 64, 4) KVQ_W(3, 64, 2) KVQ_W(3, 64, 1) KVQ_W(3, 128, 4) KVQ_W(3, 128, 2) KVQ_W(3, 128, 1)
 #undef KVQ_W
   return 4;
 }
@@ -1385,7 +1401,8 @@ hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, hipSt
   switch (mode) {
     case 0: return launch_decode_m<0>(d, rot, p, s);
     case 1: return launch_decode_m<1>(d, rot, p, s);
-    default: return launch_decode_m<2>(d, rot, p, s);
+    case 2: return launch_decode_m<2>(d, rot, p, s);
+    default: return launch_decode_m<kChannelMode>(d, rot, p, s);
   }
 }
 

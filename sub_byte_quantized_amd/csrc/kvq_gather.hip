@@ -89,10 +89,13 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
                             ? (((int64_t)id * hkv + h) << p.block_size_log2) + (pos & ((1 << p.block_size_log2) - 1))
                             : 0;
     const uint8_t* codes = (kv ? p.v_codes : p.k_codes) + src * P + lr * BPL;
-    const float* meta = (kv ? p.v_meta : p.k_meta) + src * M;
+    const float* meta = (kv ? p.v_meta : p.k_meta) + src * M;   // unused when M == 0
     if (present[it]) {
       load_bytes<BPL>(raw[it], codes);
-      if constexpr (M == 2) {
+      if constexpr (M == 0) {   // per-channel scales, read below
+        s[it] = 1.0f;
+        z[it] = 0.0f;
+      } else if constexpr (M == 2) {
         const float2 sz = *reinterpret_cast<const float2*>(meta);
         s[it] = sz.x;
         z[it] = sz.y;
@@ -111,14 +114,23 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
 #pragma unroll
   for (int it = 0; it < kGatherIter; ++it) {
     if (orow[it] < 0 || orow[it] >= p.total_tokens) continue;
+    // per-channel INT8: the lane's 8 channel scales of (K or V, kv head)
+    float sc[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (MODE == kChannelMode) {
+      const float* cs = p.chs + ((int64_t)kvs[it] * hkv + hh[it]) * D + lr * 8;
+      const float4 s0 = *reinterpret_cast<const float4*>(cs);
+      const float4 s1 = *reinterpret_cast<const float4*>(cs + 4);
+      sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
+      sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+    }
     float x[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int c;
-      if constexpr (MODE == 0) c = (int)(int8_t)((raw[it][i >> 2] >> (8 * (i & 3))) & 0xffu);
+      if constexpr (MODE == 0 || MODE == kChannelMode) c = (int)(int8_t)((raw[it][i >> 2] >> (8 * (i & 3))) & 0xffu);
       else if constexpr (MODE == 1) c = (int)((raw[it][0] >> (4 * i)) & 0xFu);
       else c = (int)((raw[it][0] >> (2 * i)) & 0x3u);
-      const float cs = (float)c * s[it];
+      const float cs = (float)c * (MODE == kChannelMode ? sc[i] : s[it]);
       x[i] = M == 2 ? cs + z[it] : cs;
     }
     if (!present[it]) {
@@ -183,8 +195,12 @@ hipError_t launch_gather_t(const GatherParams& p, hipStream_t s) {
 
 template <int MODE>
 hipError_t launch_gather_m(int d, bool rot, const GatherParams& p, hipStream_t s) {
-  if (d == 64) return rot ? launch_gather_t<MODE, 64, true>(p, s) : launch_gather_t<MODE, 64, false>(p, s);
-  return rot ? launch_gather_t<MODE, 128, true>(p, s) : launch_gather_t<MODE, 128, false>(p, s);
+  if constexpr (MODE == kChannelMode) {   // no rotation in this mode (checked on the host)
+    return d == 64 ? launch_gather_t<MODE, 64, false>(p, s) : launch_gather_t<MODE, 128, false>(p, s);
+  } else {
+    if (d == 64) return rot ? launch_gather_t<MODE, 64, true>(p, s) : launch_gather_t<MODE, 64, false>(p, s);
+    return rot ? launch_gather_t<MODE, 128, true>(p, s) : launch_gather_t<MODE, 128, false>(p, s);
+  }
 }
 
 }  // namespace
@@ -195,7 +211,8 @@ hipError_t launch_gather(int mode, int d, bool rot, const GatherParams& p, hipSt
   switch (mode) {
     case 0: return launch_gather_m<0>(d, rot, p, s);
     case 1: return launch_gather_m<1>(d, rot, p, s);
-    default: return launch_gather_m<2>(d, rot, p, s);
+    case 2: return launch_gather_m<2>(d, rot, p, s);
+    default: return launch_gather_m<kChannelMode>(d, rot, p, s);
   }
 }
 

@@ -45,7 +45,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 kvq_status check_desc(const kvq_cache_desc* d) {
   if (!d) return fail(KVQ_EINVAL, "desc is NULL");
-  if (d->mode < KVQ_INT8_SYM || d->mode > KVQ_INT2_ASYM)
+  if (d->mode < KVQ_INT8_SYM || d->mode > KVQ_INT8_CHANNEL)
     return fail(KVQ_EINVAL, "mode %d is not a kvq_mode", d->mode);
   if (d->head_dim != 64 && d->head_dim != 128) {
     if (d->head_dim > 0 && (d->head_dim & (d->head_dim - 1)) == 0)
@@ -60,12 +60,24 @@ kvq_status check_desc(const kvq_cache_desc* d) {
     return fail(KVQ_EUNSUPPORTED, "num_blocks*num_kv_heads*block_size must stay below 2^31 rows");
   if (d->rot_signs && !aligned(d->rot_signs, 16))
     return fail(KVQ_EINVAL, "rot_signs must be 16-byte aligned");
+  if (d->mode == KVQ_INT8_CHANNEL && d->rot_signs)
+    return fail(KVQ_EUNSUPPORTED, "KVQ_INT8_CHANNEL takes no rotation (rot_signs must be NULL)");
   return KVQ_OK;
 }
 
-kvq_status check_planes(const uint8_t* kc, const float* km, const uint8_t* vc, const float* vm) {
-  if (!kc || !km || !vc || !vm) return fail(KVQ_EINVAL, "a cache plane pointer is NULL");
-  if (!aligned(kc, 16) || !aligned(km, 16) || !aligned(vc, 16) || !aligned(vm, 16))
+// The per-channel scales a KVQ_INT8_CHANNEL call reads.
+kvq_status check_channel(const kvq_cache_desc* d) {
+  if (d->mode != KVQ_INT8_CHANNEL) return KVQ_OK;
+  if (!d->channel_scales) return fail(KVQ_EINVAL, "KVQ_INT8_CHANNEL needs desc->channel_scales");
+  if (!aligned(d->channel_scales, 16)) return fail(KVQ_EINVAL, "channel_scales must be 16-byte aligned");
+  return KVQ_OK;
+}
+
+// Code planes always; meta planes unless the mode has no per-row metadata.
+kvq_status check_planes(int mode, const uint8_t* kc, const float* km, const uint8_t* vc, const float* vm) {
+  const bool meta = kvq::mode_meta(mode) > 0;
+  if (!kc || !vc || (meta && (!km || !vm))) return fail(KVQ_EINVAL, "a cache plane pointer is NULL");
+  if (!aligned(kc, 16) || !aligned(vc, 16) || (meta && (!aligned(km, 16) || !aligned(vm, 16))))
     return fail(KVQ_EINVAL, "cache planes must be 16-byte aligned");
   return KVQ_OK;
 }
@@ -196,7 +208,9 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
   if (num_seqs == 0) return ok();
   if (!out || !query || !seq_lens) return fail(KVQ_EINVAL, "out, query or seq_lens is NULL");
   if (!aligned(out, 16)) return fail(KVQ_EINVAL, "out must be 16-byte aligned");
-  st = check_planes(k_codes, k_meta, v_codes, v_meta);
+  st = check_planes(desc->mode, k_codes, k_meta, v_codes, v_meta);
+  if (st != KVQ_OK) return st;
+  st = check_channel(desc);
   if (st != KVQ_OK) return st;
   const DecodePlan pl = plan_decode(desc, num_seqs, num_q_heads, max_seq_len, options);
   if (use_scratch) {
@@ -226,6 +240,7 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
   p.seq_lens = seq_lens;
   p.window = window;
   p.signs = desc->rot_signs;
+  p.chs = desc->channel_scales;
   p.counters = static_cast<int32_t*>(workspace);
   p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counter_bytes);
   p.qscale = softmax_scale * 1.4426950408889634f;
@@ -256,6 +271,7 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
     p.wp.block_size = desc->block_size;
     p.wp.slot_cap = desc->num_blocks * desc->block_size;
     p.wp.signs = desc->rot_signs;
+    p.wp.chs = desc->channel_scales;
     p.wp.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
     p.wp.total_rows = 2 * (int64_t)num_seqs * desc->num_kv_heads;
   }
@@ -313,7 +329,9 @@ kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc, const void* key, co
   if (num_tokens == 0) return ok();  // nothing is read or written
   if ((slot_mapping == nullptr) == (slot_mapping_headwise == nullptr))
     return fail(KVQ_EINVAL, "exactly one of slot_mapping and slot_mapping_headwise must be non-NULL");
-  st = check_planes(k_codes, k_meta, v_codes, v_meta);
+  st = check_planes(desc->mode, k_codes, k_meta, v_codes, v_meta);
+  if (st != KVQ_OK) return st;
+  st = check_channel(desc);
   if (st != KVQ_OK) return st;
   const int D = desc->head_dim, H = desc->num_kv_heads;
   {
@@ -340,10 +358,40 @@ kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc, const void* key, co
   p.v_codes = v_codes;
   p.v_meta = v_meta;
   p.signs = desc->rot_signs;
+  p.chs = desc->channel_scales;
   p.inv_sqrt_d = inv_sqrt_f32(D);
   hipError_t e = kvq::launch_write(desc->mode, D, desc->rot_signs != nullptr, p,
                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_EHIP, "write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvq_status kvq_calibrate_channel_scales(const kvq_cache_desc* desc, const void* key, const void* value,
+                                        int64_t key_tok_stride, int64_t value_tok_stride, int32_t num_tokens,
+                                        float* scales_out, void* stream) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (desc->mode != KVQ_INT8_CHANNEL)
+    return fail(KVQ_EINVAL, "kvq_calibrate_channel_scales needs mode KVQ_INT8_CHANNEL (got %d)", desc->mode);
+  if (num_tokens < 0) return fail(KVQ_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (!scales_out || !aligned(scales_out, 16)) return fail(KVQ_EINVAL, "scales_out must be non-NULL, 16-byte aligned");
+  const int D = desc->head_dim, H = desc->num_kv_heads;
+  if (num_tokens > 0) {
+    if (!key || !value) return fail(KVQ_EINVAL, "key or value is NULL");
+    if (key_tok_stride < (int64_t)H * D || value_tok_stride < (int64_t)H * D)
+      return fail(KVQ_EINVAL, "token strides (%lld, %lld) must be >= num_kv_heads*head_dim = %d",
+                  (long long)key_tok_stride, (long long)value_tok_stride, H * D);
+    if (key_tok_stride % 8 != 0 || value_tok_stride % 8 != 0 || !aligned(key, 16) || !aligned(value, 16))
+      return fail(KVQ_EINVAL, "key/value must be 16-byte aligned with token strides a multiple of 8");
+  }
+  kvq::WriteParams p{};
+  p.key = static_cast<const uint16_t*>(key);
+  p.value = static_cast<const uint16_t*>(value);
+  p.key_stride = key_tok_stride;
+  p.value_stride = value_tok_stride;
+  p.hkv = H;
+  hipError_t e = kvq::launch_calibrate(D, p, num_tokens, scales_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_EHIP, "calibrate launch: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -461,7 +509,9 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
   if (num_seqs == 0 || max_q_len == 0) return ok();
   if (!out || !query || !cu_seqlens_q || !seq_lens)
     return fail(KVQ_EINVAL, "out, query, cu_seqlens_q or seq_lens is NULL");
-  st = check_planes(k_codes, k_meta, v_codes, v_meta);
+  st = check_planes(desc->mode, k_codes, k_meta, v_codes, v_meta);
+  if (st != KVQ_OK) return st;
+  st = check_channel(desc);
   if (st != KVQ_OK) return st;
   const int tq = 128 / group;
   const long long n_qtiles = ((long long)max_q_len + tq - 1) / tq;
@@ -479,6 +529,7 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
   p.tables = p.headwise ? block_tables_headwise : block_tables;
   p.window = window;
   p.signs = desc->rot_signs;
+  p.chs = desc->channel_scales;
   p.qscale = softmax_scale * 1.4426950408889634f;
   p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
   p.num_blocks = desc->num_blocks;
@@ -538,7 +589,9 @@ kvq_status kvq_gather_dequant(const kvq_cache_desc* desc, void* key_out, void* v
   if (!key_out || !value_out || !cu_seq_lens) return fail(KVQ_EINVAL, "key_out, value_out or cu_seq_lens is NULL");
   if (!aligned(key_out, 16) || !aligned(value_out, 16))
     return fail(KVQ_EINVAL, "key_out and value_out must be 16-byte aligned");
-  st = check_planes(k_codes, k_meta, v_codes, v_meta);
+  st = check_planes(desc->mode, k_codes, k_meta, v_codes, v_meta);
+  if (st != KVQ_OK) return st;
+  st = check_channel(desc);
   if (st != KVQ_OK) return st;
   kvq::GatherParams p{};
   p.k_codes = k_codes;
@@ -551,6 +604,7 @@ kvq_status kvq_gather_dequant(const kvq_cache_desc* desc, void* key_out, void* v
   p.tables = p.headwise ? block_tables_headwise : block_tables;
   p.cu = cu_seq_lens;
   p.signs = desc->rot_signs;
+  p.chs = desc->channel_scales;
   p.num_blocks = desc->num_blocks;
   p.inv_sqrt_d = inv_sqrt_f32(desc->head_dim);
   p.max_blocks = max_blocks_per_seq;

@@ -7,10 +7,14 @@
 
 namespace kvq {
 
-// Codes per byte and metadata floats per row, by mode (0 INT8, 1 INT4, 2 INT2).
-__host__ __device__ constexpr int mode_bits(int mode) { return mode == 0 ? 8 : (mode == 1 ? 4 : 2); }
-__host__ __device__ constexpr int mode_meta(int mode) { return mode == 0 ? 1 : 2; }
-__host__ __device__ constexpr int mode_levels(int mode) { return mode == 0 ? 127 : (mode == 1 ? 15 : 3); }
+// Code bits, metadata floats per row and levels, by mode (0 INT8 per token
+// and head, 1 INT4, 2 INT2, 3 INT8 with per-channel scales and no per-row
+// metadata).
+__host__ __device__ constexpr int mode_bits(int mode) { return (mode == 0 || mode == 3) ? 8 : (mode == 1 ? 4 : 2); }
+__host__ __device__ constexpr int mode_meta(int mode) { return mode == 0 ? 1 : (mode == 3 ? 0 : 2); }
+__host__ __device__ constexpr int mode_levels(int mode) { return (mode == 0 || mode == 3) ? 127 : (mode == 1 ? 15 : 3); }
+// Per-channel scales: [2][Hkv][D] float32, K then V.
+constexpr int kChannelMode = 3;
 __host__ __device__ constexpr int row_bytes(int mode, int d) { return d * mode_bits(mode) / 8; }
 
 // Positions the decode kernel processes as one tile (four 16-token MFMA tiles).
@@ -37,6 +41,7 @@ struct WriteParams {
   uint8_t* v_codes;
   float* v_meta;
   const float* signs;       // [D] or nullptr
+  const float* chs;         // per-channel mode: [2][Hkv][D] scales, K then V
   float inv_sqrt_d;         // float32 rounding of 1/sqrt(D)
 };
 
@@ -51,6 +56,7 @@ struct DecodeParams {
   const int32_t* seq_lens;      // [B]
   const int32_t* window;        // [Hkv] or nullptr
   const float* signs;           // [D] or nullptr
+  const float* chs;             // per-channel mode: [2][Hkv][D] scales, K then V
   float* partials;              // [n_wgs + num_pairs][group][D + 4] pieces (m, l, pad, pad, acc)
   int32_t* counters;            // [num_pairs] pieces counted in; zero between calls
   float qscale;                 // softmax_scale * log2(e)
@@ -87,6 +93,7 @@ struct PrefillParams {
   const int32_t* tables;        // [B, max_blocks] or [B*Hkv, max_blocks]
   const int32_t* window;        // [Hkv] or nullptr
   const float* signs;           // [D] or nullptr
+  const float* chs;             // per-channel mode: [2][Hkv][D] scales, K then V
   float qscale;                 // softmax_scale * log2(e)
   float inv_sqrt_d;
   int64_t num_blocks;           // ids at or past it are treated as evicted
@@ -114,6 +121,7 @@ struct GatherParams {
   const int32_t* tables;        // [B, max_blocks] or [B*Hkv, max_blocks]
   const int32_t* cu;            // [B + 1] output row offsets
   const float* signs;           // [D] or nullptr
+  const float* chs;             // per-channel mode: [2][Hkv][D] scales, K then V
   int64_t num_blocks;
   float inv_sqrt_d;
   int32_t headwise;
@@ -135,5 +143,7 @@ int decode_wgs_per_cu(int mode, int d, int group);
 hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, hipStream_t s);
 hipError_t launch_prefill(int mode, int d, bool rot, const PrefillParams& p, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+// Per-channel scales of a first batch: out[kv][h][d] = max_t |x| / 127.
+hipError_t launch_calibrate(int d, const WriteParams& p, int32_t num_tokens, float* out, hipStream_t s);
 
 }  // namespace kvq

@@ -153,10 +153,15 @@ __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillPara
   if (row >= 0) {
     load_bytes<Gp::KNW * 4>(st.k, p.k_codes + (int64_t)row * Gp::P + qd * (Gp::KNW * 4));
     if (qd == 0) {
-      st.sk = p.k_meta[(int64_t)row * Gp::M];
-      st.zk = Gp::M == 2 ? p.k_meta[(int64_t)row * Gp::M + 1] : 0.0f;
-      st.sv = p.v_meta[(int64_t)row * Gp::M];
-      st.zv = Gp::M == 2 ? p.v_meta[(int64_t)row * Gp::M + 1] : 0.0f;
+      if constexpr (Gp::M == 0) {   // per-channel INT8: scales live in the query and the output
+        st.sk = 1.0f;
+        st.sv = 1.0f;
+      } else {
+        st.sk = p.k_meta[(int64_t)row * Gp::M];
+        st.zk = Gp::M == 2 ? p.k_meta[(int64_t)row * Gp::M + 1] : 0.0f;
+        st.sv = p.v_meta[(int64_t)row * Gp::M];
+        st.zv = Gp::M == 2 ? p.v_meta[(int64_t)row * Gp::M + 1] : 0.0f;
+      }
     }
   }
   // V: positions 4 kq .. 4 kq + 3 (one block: block sizes are >= 16),
@@ -245,12 +250,12 @@ __device__ __forceinline__ void stage_store(const Stage<MODE, D>& st, PBuf<MODE,
     for (int w = 0; w < NW; ++w)
 #pragma unroll
       for (int pl = 0; pl < NPL; ++pl) {
-        const uint32_t x = MODE == 0 ? (st.v[i][w] ^ 0x80808080u)
+        const uint32_t x = BITS == 8 ? (st.v[i][w] ^ 0x80808080u)
                                      : ((st.v[i][w] >> (BITS * pl)) & (MODE == 1 ? 0x0F0F0F0Fu : 0x03030303u));
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int e = (32 / BITS) * w + NPL * bb + pl;
-          if (e < Gp::DPT) c[i][e] = MODE == 0 ? (float)((x >> (8 * bb)) & 0xffu) - 128.0f
+          if (e < Gp::DPT) c[i][e] = BITS == 8 ? (float)((x >> (8 * bb)) & 0xffu) - 128.0f
                                                : (float)((x >> (8 * bb)) & 0xffu);
         }
       }
@@ -480,6 +485,7 @@ void prefill_kernel(PrefillParams p) {
       const int t = row / G, g = row - t * G;
       v = __uint_as_float((uint32_t)p.q[((int64_t)(q0 + tok0 + t) * p.hq + h * G + g) * D + d] << 16);
       if constexpr (ROT) v *= p.signs[d];
+      if constexpr (MODE == kChannelMode) v *= p.chs[(int64_t)h * D + d];   // q . (c (.) s_K)
     }
     sm.qf[row][d] = v;
   }
@@ -635,6 +641,7 @@ void prefill_kernel(PrefillParams p) {
     const int t = row / G, g = row - t * G;
     float v = sm.qf[row][d];
     if constexpr (ROT) v = v * p.signs[d] * p.inv_sqrt_d;
+    if constexpr (MODE == kChannelMode) v *= p.chs[((int64_t)p.hkv + h) * D + d];   // (sum_j p_j c_j) (.) s_V
     const int64_t o_idx = ((int64_t)(q0 + tok0 + t) * p.hq + h * G + g) * D + d;
     if (p.out_bf16)
       reinterpret_cast<__bf16*>(p.out)[o_idx] = (__bf16)v;
@@ -663,6 +670,9 @@ hipError_t launch_prefill(int mode, int d, bool rot, const PrefillParams& p, hip
   KVQ_PREFILL_CASE(2, 64)
   KVQ_PREFILL_CASE(2, 128)
 #undef KVQ_PREFILL_CASE
+  // per-channel INT8 has no rotation (checked on the host)
+  if (mode == kChannelMode && d == 64) return launch_prefill_t<kChannelMode, 64, false>(p, s);
+  if (mode == kChannelMode && d == 128) return launch_prefill_t<kChannelMode, 128, false>(p, s);
   return hipErrorInvalidValue;
 }
 

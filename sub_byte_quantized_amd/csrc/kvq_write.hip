@@ -77,6 +77,34 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
     write_row_store<MODE, D, ROT>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, slot[it], lr);
 }
 
+// Per-channel scales of a first batch (dynamic per-channel INT8, the
+// vllm-ascend-quantized-kv-cache package, 运行机制): workgroup (kv, h)
+// reduces max_t |x[t, h, d]| over the tokens for every channel d, then
+// divides by 127 (correctly rounded).  Thread i takes channel i % D and
+// tokens i / D, i / D + 256 / D, ...; the partial maxima meet in LDS.  The
+// maximum of absolute values is exact and order-free.
+template <int D>
+__global__ __launch_bounds__(256) void calibrate_kernel(WriteParams p, int32_t num_tokens, float* out) {
+  constexpr int TPS = 256 / D;             // token lanes per channel
+  __shared__ float part[TPS][D];
+  const int kv = blockIdx.x & 1, h = blockIdx.x >> 1;
+  const int d = threadIdx.x % D, t0 = threadIdx.x / D;
+  const uint16_t* src = kv ? p.value : p.key;
+  const int64_t stride = kv ? p.value_stride : p.key_stride;
+  float m = 0.0f;
+  for (int64_t t = t0; t < num_tokens; t += TPS) {
+    const uint16_t raw = src[t * stride + (int64_t)h * D + d];
+    m = fmaxf(m, fabsf(__uint_as_float((uint32_t)raw << 16)));
+  }
+  part[t0][d] = m;
+  __syncthreads();
+  if (t0 == 0) {
+#pragma unroll
+    for (int i = 1; i < TPS; ++i) m = fmaxf(m, part[i][d]);
+    out[((int64_t)kv * p.hkv + h) * D + d] = m / 127.0f;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
        i += (size_t)gridDim.x * blockDim.x)
@@ -94,8 +122,12 @@ hipError_t launch_write_t(const WriteParams& p, hipStream_t s) {
 
 template <int MODE>
 hipError_t launch_write_m(int d, bool rot, const WriteParams& p, hipStream_t s) {
-  if (d == 64) return rot ? launch_write_t<MODE, 64, true>(p, s) : launch_write_t<MODE, 64, false>(p, s);
-  return rot ? launch_write_t<MODE, 128, true>(p, s) : launch_write_t<MODE, 128, false>(p, s);
+  if constexpr (MODE == kChannelMode) {   // no rotation in this mode (checked on the host)
+    return d == 64 ? launch_write_t<MODE, 64, false>(p, s) : launch_write_t<MODE, 128, false>(p, s);
+  } else {
+    if (d == 64) return rot ? launch_write_t<MODE, 64, true>(p, s) : launch_write_t<MODE, 64, false>(p, s);
+    return rot ? launch_write_t<MODE, 128, true>(p, s) : launch_write_t<MODE, 128, false>(p, s);
+  }
 }
 
 }  // namespace
@@ -104,8 +136,16 @@ hipError_t launch_write(int mode, int d, bool rot, const WriteParams& p, hipStre
   switch (mode) {
     case 0: return launch_write_m<0>(d, rot, p, s);
     case 1: return launch_write_m<1>(d, rot, p, s);
-    default: return launch_write_m<2>(d, rot, p, s);
+    case 2: return launch_write_m<2>(d, rot, p, s);
+    default: return launch_write_m<kChannelMode>(d, rot, p, s);
   }
+}
+
+hipError_t launch_calibrate(int d, const WriteParams& p, int32_t num_tokens, float* out, hipStream_t s) {
+  const dim3 grid((unsigned)(2 * p.hkv));
+  if (d == 64) hipLaunchKernelGGL(calibrate_kernel<64>, grid, dim3(256), 0, s, p, num_tokens, out);
+  else hipLaunchKernelGGL(calibrate_kernel<128>, grid, dim3(256), 0, s, p, num_tokens, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {

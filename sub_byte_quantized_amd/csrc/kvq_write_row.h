@@ -89,7 +89,24 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     for (int i = 0; i < 8; ++i) x[i] = x[i] * p.inv_sqrt_d;
   }
 
-  float s, z;
+  // per-channel INT8: fixed scales of the (K or V, kv head) channels, codes
+  // clamp(rint(x * (1/s_d)), -127, 127), one correctly rounded reciprocal per
+  // channel; a zero or subnormal scale gives code 0; no row metadata
+  uint32_t c[8];
+  if constexpr (MODE == kChannelMode) {
+    const float* cs = p.chs + ((int64_t)kv * hkv + h) * D + lr * 8;
+    const float4 s0 = *reinterpret_cast<const float4*>(cs);
+    const float4 s1 = *reinterpret_cast<const float4*>(cs + 4);
+    const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool okc = sc[i] >= 1.17549435e-38f;
+      const float invc = okc ? 1.0f / sc[i] : 0.0f;
+      const float r = fminf(fmaxf(__builtin_rintf(x[i] * invc), -kLevels), kLevels);
+      c[i] = okc ? (uint32_t)(int32_t)r : 0u;
+    }
+  }
+  float s = 0.0f, z = 0.0f;   // per-row scale and zero (not for per-channel INT8)
   if constexpr (MODE == 0) {
     float a = 0.0f;
 #pragma unroll
@@ -98,7 +115,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     for (int m = 1; m < LPR; m <<= 1) a = fmaxf(a, xor_in_row(a, m));
     s = a / kLevels;
     z = 0.0f;
-  } else {
+  } else if constexpr (MODE != kChannelMode) {
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) {
@@ -114,16 +131,17 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     z = mn;
   }
 
-  // zero, subnormal or NaN scale: all-zero codes
-  const bool ok = s >= 1.17549435e-38f;
-  const float inv = ok ? 1.0f / s : 0.0f;
-  constexpr float lo = MODE == 0 ? -kLevels : 0.0f;
-  uint32_t c[8];
+  if constexpr (MODE != kChannelMode) {
+    // zero, subnormal or NaN scale: all-zero codes
+    const bool ok = s >= 1.17549435e-38f;
+    const float inv = ok ? 1.0f / s : 0.0f;
+    constexpr float lo = MODE == 0 ? -kLevels : 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float tq = MODE == 0 ? x[i] * inv : (x[i] - z) * inv;
-    const float r = fminf(fmaxf(__builtin_rintf(tq), lo), kLevels);
-    c[i] = ok ? (uint32_t)(int32_t)r : 0u;
+    for (int i = 0; i < 8; ++i) {
+      const float tq = MODE == 0 ? x[i] * inv : (x[i] - z) * inv;
+      const float r = fminf(fmaxf(__builtin_rintf(tq), lo), kLevels);
+      c[i] = ok ? (uint32_t)(int32_t)r : 0u;
+    }
   }
 
   if (!active) return;
@@ -133,9 +151,9 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   const int64_t off = slot & (p.block_size - 1);
   const int64_t ridx = (blk * hkv + h) * p.block_size + off;
   uint8_t* codes = (kv ? p.v_codes : p.k_codes) + ridx * P + lr * BPL;
-  float* meta = (kv ? p.v_meta : p.k_meta) + ridx * M;
+  float* meta = (kv ? p.v_meta : p.k_meta) + ridx * M;   // unused when M == 0
 
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == 0 || MODE == kChannelMode) {
     uint2 w;
     w.x = (c[0] & 0xffu) | ((c[1] & 0xffu) << 8) | ((c[2] & 0xffu) << 16) | ((c[3] & 0xffu) << 24);
     w.y = (c[4] & 0xffu) | ((c[5] & 0xffu) << 8) | ((c[6] & 0xffu) << 16) | ((c[7] & 0xffu) << 24);
@@ -151,7 +169,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     for (int i = 0; i < 8; ++i) w |= c[i] << (2 * i);
     *reinterpret_cast<uint16_t*>(codes) = (uint16_t)w;
   }
-  if (lr == 0) {
+  if (M > 0 && lr == 0) {
     if constexpr (M == 1) {
       meta[0] = s;
     } else {

@@ -16,8 +16,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (KVQ_INT2_ASYM, KVQ_INT4_ASYM, KVQ_INT8_SYM, KVQ_OUT_BF16,  # noqa: F401
-                   KVQ_OUT_F32)
+from ._lib import (KVQ_INT2_ASYM, KVQ_INT4_ASYM, KVQ_INT8_CHANNEL, KVQ_INT8_SYM,  # noqa: F401
+                   KVQ_OUT_BF16, KVQ_OUT_F32)
 
 
 class KvqError(RuntimeError):
@@ -125,13 +125,20 @@ class CacheDesc:
     block_size: int
     num_blocks: int
     rot_signs: Optional[torch.Tensor] = None   # float32 [head_dim] of +-1, on the device
+    # KVQ_INT8_CHANNEL: float32 [2, Hkv, D] per-channel scales (K then V)
+    channel_scales: Optional[torch.Tensor] = None
 
     def c(self) -> _lib.CacheDesc:
         if self.rot_signs is not None:
             _need(self.rot_signs, "rot_signs", torch.float32)
+        if self.channel_scales is not None:
+            _need(self.channel_scales, "channel_scales", torch.float32)
+            if tuple(self.channel_scales.shape) != (2, self.num_kv_heads, self.head_dim):
+                raise ValueError(f"channel_scales must be [2, {self.num_kv_heads}, {self.head_dim}]")
         return _lib.CacheDesc(int(self.mode), int(self.head_dim), int(self.num_kv_heads),
                               int(self.block_size), int(self.num_blocks),
-                              None if self.rot_signs is None else self.rot_signs.data_ptr())
+                              None if self.rot_signs is None else self.rot_signs.data_ptr(),
+                              None if self.channel_scales is None else self.channel_scales.data_ptr())
 
 
 def kvq_query_layout(desc: CacheDesc) -> dict:
@@ -191,6 +198,29 @@ def kvq_reshape_and_cache(desc: CacheDesc, key: torch.Tensor, value: torch.Tenso
         ctypes.byref(d), _ptr(key), _ptr(value), key.stride(0), value.stride(0),
         _ptr(slot_mapping), _ptr(slot_mapping_headwise), int(key.shape[0]),
         _ptr(k_codes), _ptr(k_meta), _ptr(v_codes), _ptr(v_meta), _stream(dev)))
+
+
+def kvq_calibrate_channel_scales(desc: CacheDesc, key: torch.Tensor, value: torch.Tensor,
+                                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-channel INT8 scales [2, Hkv, D] (K then V) of a layer's first
+    K/V, key/value bf16 [T, Hkv, D]: max over tokens of |x| / 127."""
+    dev = key.device
+    for t, n in ((key, "key"), (value, "value")):
+        _need(t, n, torch.bfloat16, dev, contiguous=False)
+        if t.dim() != 3 or tuple(t.shape[1:]) != (desc.num_kv_heads, desc.head_dim) or t.stride(2) != 1 \
+                or t.stride(1) != desc.head_dim:
+            raise ValueError(f"{n} must be [T, {desc.num_kv_heads}, {desc.head_dim}] with heads and D contiguous")
+    if key.shape != value.shape:
+        raise ValueError("key and value shapes differ")
+    if out is None:
+        out = torch.empty((2, desc.num_kv_heads, desc.head_dim), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev)
+    if tuple(out.shape) != (2, desc.num_kv_heads, desc.head_dim):
+        raise ValueError(f"out must be [2, {desc.num_kv_heads}, {desc.head_dim}]")
+    d = desc.c()
+    _check(_lib.load().kvq_calibrate_channel_scales(ctypes.byref(d), _ptr(key), _ptr(value), key.stride(0),
+                                                    value.stride(0), int(key.shape[0]), _ptr(out), _stream(dev)))
+    return out
 
 
 def kvq_decode_workspace_size(desc: CacheDesc, num_seqs: int, num_q_heads: int,

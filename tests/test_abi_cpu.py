@@ -27,7 +27,7 @@ def lib():
 
 
 def desc(mode=1, D=128, H=4, bs=64, nb=10, signs=None):
-    return _lib.CacheDesc(mode, D, H, bs, nb, signs)
+    return _lib.CacheDesc(mode, D, H, bs, nb, signs, None)
 
 
 def test_header_lists_entry_points():
@@ -44,21 +44,22 @@ def test_exports_every_header_symbol(lib):
         assert name in _lib.SIGNATURES, f"binding lacks {name}"
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
 @pytest.mark.parametrize("D", [64, 128])
 def test_layout_matches_formula(lib, mode, D):
     d = desc(mode, D, H=3, bs=32, nb=7)
     out = _lib.Layout()
     assert lib.kvq_query_layout(ctypes.byref(d), ctypes.byref(out)) == 0
     cshape, mshape = oracle.plane_shapes(mode, D, 3, 32, 7)
-    assert out.row_code_bytes == cshape[-1] == D * {0: 8, 1: 4, 2: 2}[mode] // 8
+    assert out.row_code_bytes == cshape[-1] == D * {0: 8, 1: 4, 2: 2, 3: 8}[mode] // 8
     assert out.row_meta_floats == mshape[-1]
     assert out.code_bytes == 7 * 3 * 32 * cshape[-1]
     assert out.meta_bytes == 7 * 3 * 32 * mshape[-1] * 4
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(mode=3), _lib.KVQ_EINVAL), (dict(mode=-1), _lib.KVQ_EINVAL),
+    (dict(mode=4), _lib.KVQ_EINVAL), (dict(mode=-1), _lib.KVQ_EINVAL),
+    (dict(mode=3, signs=4096), _lib.KVQ_EUNSUPPORTED),
     (dict(D=96), _lib.KVQ_EINVAL), (dict(D=256), _lib.KVQ_EUNSUPPORTED), (dict(D=0), _lib.KVQ_EINVAL),
     (dict(H=0), _lib.KVQ_EINVAL), (dict(bs=8), _lib.KVQ_EINVAL), (dict(bs=40), _lib.KVQ_EINVAL), (dict(bs=48), _lib.KVQ_EINVAL),
     (dict(nb=0), _lib.KVQ_EINVAL)])
@@ -68,6 +69,27 @@ def test_layout_rejects(lib, kw, status):
     assert lib.kvq_query_layout(ctypes.byref(d), ctypes.byref(out)) == status
     assert lib.kvq_last_error().decode()
     assert lib.kvq_query_layout(None, ctypes.byref(out)) == _lib.KVQ_EINVAL
+
+
+def test_channel_mode_validation(lib):
+    """KVQ_INT8_CHANNEL: no rotation, channel scales required by calls that
+    read or write codes, meta planes optional; calibration only in that mode."""
+    P = ctypes.c_void_p(4096)
+    d = _lib.CacheDesc(3, 128, 4, 64, 10, None, None)
+    # write without channel scales
+    assert lib.kvq_reshape_and_cache(ctypes.byref(d), P, P, 512, 512, P, None, 4, P, None, P, None, None) \
+        == _lib.KVQ_EINVAL
+    assert "channel_scales" in lib.kvq_last_error().decode()
+    # misaligned scales
+    d2 = _lib.CacheDesc(3, 128, 4, 64, 10, None, 4100)
+    assert lib.kvq_reshape_and_cache(ctypes.byref(d2), P, P, 512, 512, P, None, 4, P, None, P, None, None) \
+        == _lib.KVQ_EINVAL
+    # calibration: wrong mode, null output, bad stride
+    d0 = _lib.CacheDesc(0, 128, 4, 64, 10, None, None)
+    assert lib.kvq_calibrate_channel_scales(ctypes.byref(d0), P, P, 512, 512, 8, P, None) == _lib.KVQ_EINVAL
+    assert lib.kvq_calibrate_channel_scales(ctypes.byref(d), P, P, 512, 512, 8, None, None) == _lib.KVQ_EINVAL
+    assert lib.kvq_calibrate_channel_scales(ctypes.byref(d), P, P, 100, 512, 8, P, None) == _lib.KVQ_EINVAL
+    assert lib.kvq_calibrate_channel_scales(ctypes.byref(d), P, P, 512, 512, -1, P, None) == _lib.KVQ_EINVAL
 
 
 def test_write_validation(lib):
