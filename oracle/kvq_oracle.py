@@ -59,6 +59,12 @@ Readings where the pages are silent (each also listed in the design doc):
   scales, c = clamp(rint(x * fl(1/s_d)), -127, 127) (values beyond the
   calibrated range saturate), a channel with a zero or subnormal scale gets
   code 0, and x_hat = c * s_d.  No rotation and no per-token metadata.
+* FP8 per-token-head ([P2] 功能与动机: the INT8/FP8 per-token-head schemes the
+  INT4 mode extends): OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+  mantissa bits, no infinities, largest finite 448, subnormal step 2^-9),
+  symmetric per (token, kv head): s = max|y| / 448, t = clamp(y * fl(1/s),
+  -448, 448) in float32, code = t rounded to the nearest E4M3 value, ties to
+  even; x_hat = E4M3(code) * s.  The same optional rotation as INT4/INT2.
 * Attention sinks ([P3] Modifications: a sink_size parameter threaded into the
   attention op, semantics unstated): a windowed kv head also attends the
   first sink_size positions of the sequence (when present in the table), as
@@ -75,11 +81,13 @@ INT8_SYM = 0
 INT4_ASYM = 1
 INT2_ASYM = 2
 INT8_CHANNEL = 3
-MODES = (INT8_SYM, INT4_ASYM, INT2_ASYM)          # the per-token-head modes
-BITS = {INT8_SYM: 8, INT4_ASYM: 4, INT2_ASYM: 2, INT8_CHANNEL: 8}
+FP8_E4M3 = 4
+MODES = (INT8_SYM, INT4_ASYM, INT2_ASYM)          # the integer per-token-head modes
+BITS = {INT8_SYM: 8, INT4_ASYM: 4, INT2_ASYM: 2, INT8_CHANNEL: 8, FP8_E4M3: 8}
 # number of quantization steps: codes span [0, L] (asymmetric) or [-L, L]
 LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3, INT8_CHANNEL: 127}
-META_FLOATS = {INT8_SYM: 1, INT4_ASYM: 2, INT2_ASYM: 2, INT8_CHANNEL: 0}
+META_FLOATS = {INT8_SYM: 1, INT4_ASYM: 2, INT2_ASYM: 2, INT8_CHANNEL: 0, FP8_E4M3: 1}
+E4M3_MAX = 448.0
 
 _F32 = np.float32
 _FLT_MIN = _F32(2.0 ** -126)
@@ -253,6 +261,61 @@ def unpack_codes(packed: np.ndarray, mode: int, head_dim: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# FP8 (OCP E4M3) per-token-head ([P2] 功能与动机: INT8/FP8 per-token-head)
+# --------------------------------------------------------------------------
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each E4M3 byte (float64): exponent field e, mantissa m, sign s;
+    e > 0: (-1)^s 2^(e-7) (1 + m/8); e = 0: (-1)^s 2^-6 m/8; 0x7F / 0xFF: NaN."""
+    c = np.asarray(codes, np.int64)
+    sgn = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    v = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))
+    v = sgn * v
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def e4m3_encode(t: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 byte to each finite |t| <= 448 (ties to even mantissa;
+    -0 keeps its sign bit).  Below 2^-6 the grid is 2^-9 (subnormals);
+    above, 8 steps per binade.  Computed in float64, where every step here is
+    exact."""
+    t = np.asarray(t, np.float64)
+    assert np.all(np.isfinite(t)) and np.all(np.abs(t) <= E4M3_MAX)
+    a = np.abs(t)
+    sub = a < 2.0 ** -6
+    q_sub = np.rint(a / 2.0 ** -9)                     # 0 .. 8 (8 is the first normal)
+    e = np.floor(np.log2(np.where(sub, 1.0, a)))
+    # log2 may be off by one ulp at exact powers of two: fix e so 2^e <= a < 2^(e+1)
+    e = np.where(np.ldexp(1.0, e.astype(np.int64)) > a, e - 1, e)
+    e = np.where(np.ldexp(1.0, (e + 1).astype(np.int64)) <= a, e + 1, e)
+    q = np.rint(a / np.ldexp(1.0, (e - 3).astype(np.int64)))   # 8 .. 16
+    e = np.where(q == 16, e + 1, e)
+    q = np.where(q == 16, 8, q)
+    normal = ((e + 7).astype(np.int64) << 3) | (q.astype(np.int64) - 8)
+    code = np.where(sub, q_sub.astype(np.int64), normal)
+    code = np.where(np.signbit(t), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def quantize_rows_fp8(y: np.ndarray):
+    """FP8 rows y [R, D] float32 -> (codes uint8 [R, D], s f32 [R]):
+    s = max|y| / 448, t = clamp(y * fl(1/s), -448, 448) in float32, codes
+    the nearest E4M3 values; rows with a zero, subnormal or NaN scale get
+    code 0."""
+    y = np.asarray(y, _F32)
+    a = np.max(np.abs(y), axis=-1)
+    s = (a / _F32(E4M3_MAX)).astype(_F32)
+    ok = s >= _FLT_MIN
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        inv = np.where(ok, _F32(1.0) / np.where(ok, s, _F32(1.0)), _F32(0.0)).astype(_F32)
+        t = (y * inv[..., None]).astype(_F32)
+    t = np.clip(np.where(ok[..., None], t, _F32(0.0)), -E4M3_MAX, E4M3_MAX)
+    codes = e4m3_encode(t)
+    return np.where(ok[..., None], codes, np.uint8(0)).astype(np.uint8), s
+
+
+# --------------------------------------------------------------------------
 # Dynamic per-channel INT8 ([P4] 运行机制: scales from the first K/V a layer
 # receives, along the token axis, symmetric, per channel, K and V separately)
 # --------------------------------------------------------------------------
@@ -290,6 +353,9 @@ def encode_rows(x_bf16_as_f32: np.ndarray, mode: int, signs=None):
     """
     x = np.asarray(x_bf16_as_f32, dtype=_F32)
     y = rotate_f32(x, signs) if signs is not None else x
+    if mode == FP8_E4M3:
+        codes, s = quantize_rows_fp8(y)
+        return codes, s, np.zeros_like(s), codes
     codes, s, z = quantize_rows(y, mode)
     return pack_codes(codes, mode), s, z, codes
 
@@ -328,7 +394,7 @@ def write_cache(k: np.ndarray, v: np.ndarray, mode: int, block_size: int,
         z = z.reshape(T, Hkv)
         codes_pl[blk, hh, off, :] = packed[tt, hh]
         meta_pl[blk, hh, off, 0] = s[tt, hh]
-        if mode != INT8_SYM:
+        if META_FLOATS[mode] == 2:
             meta_pl[blk, hh, off, 1] = z[tt, hh]
 
 
@@ -362,6 +428,10 @@ def gather_head(b: int, h: int, n_pos: int, mode: int, head_dim: int,
         bi = ids[present]
         off = pos[present] % block_size
         for kv, (pl_c, pl_m, out) in enumerate(((k_codes, k_meta, K), (v_codes, v_meta, V))):
+            if mode == FP8_E4M3:
+                xhat = e4m3_decode(pl_c[bi, h, off, :]) * np.asarray(pl_m[bi, h, off, 0], np.float64)[:, None]
+                out[present] = unrotate_f64(xhat, signs) if signs is not None else xhat
+                continue
             codes = unpack_codes(pl_c[bi, h, off, :], mode, head_dim)
             if mode == INT8_CHANNEL:
                 out[present] = codes * np.asarray(channel_scales, np.float64)[kv, h][None, :]

@@ -712,6 +712,85 @@ def check_sinks(o):
             assert np.allclose(outp[cu[b] + i, 0], ref, atol=1e-12), (b, i)
 
 
+# ------------------------------------------------------------- FP8 E4M3 ----
+def _e4m3_probe_inputs():
+    """Every bf16 value with |x| <= 448, the midpoints between consecutive
+    E4M3 values and their float32 neighbours."""
+    b = np.arange(0, 1 << 16, dtype=np.uint32) << 16
+    x = b.view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) <= 448.0)]
+    fin = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    fin = np.sort(np.unique(fin[np.isfinite(fin)]))
+    mids = ((fin[:-1].astype(np.float64) + fin[1:]) / 2).astype(F32)
+    return np.concatenate([x, mids, np.nextafter(mids, F32(np.inf)), np.nextafter(mids, F32(-np.inf))]).astype(F32)
+
+
+def check_e4m3_codec(o):
+    """The E4M3 codec equals torch's float8_e4m3fn (a library routine): the
+    value of every byte, and the nearest-even encoding of every bf16 value in
+    [-448, 448] and of every midpoint between neighbouring E4M3 values (and
+    one float32 step either side of it); encode(decode(c)) = c."""
+    c = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).float().numpy()
+    v = o.e4m3_decode(c)
+    fin = np.isfinite(ref)
+    assert np.array_equal(v[fin], ref[fin]) and np.all(np.isnan(v[~fin]))
+    assert np.array_equal(np.signbit(v[fin]), np.signbit(ref[fin]))
+    x = _e4m3_probe_inputs()
+    assert np.array_equal(o.e4m3_encode(x), torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert np.array_equal(o.e4m3_encode(v[fin]), c[fin])
+
+
+def check_fp8_quantize(o):
+    """FP8 rows: on a grid y = v 2^-e with v E4M3 values and +-448 present,
+    s = 2^-e, the codes are the E4M3 bytes of v and x_hat = y exactly;
+    otherwise |y - x_hat| <= max(|y| 2^-4, s 2^-10) (half a step of three
+    mantissa bits, or of the subnormal grid); a zero row has scale 0 and
+    codes 0."""
+    r = np.random.default_rng(41)
+    fin = o.e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = fin[np.isfinite(fin)]
+    for e in (0, 3, -5):
+        v = r.choice(fin, size=(30, 128))
+        v[:, 0] = np.where(r.integers(0, 2, 30) == 1, 448.0, -448.0)
+        y = (v * 2.0 ** -e).astype(F32)
+        packed, s, z, codes = o.encode_rows(y, o.FP8_E4M3)
+        assert np.all(s == F32(2.0 ** -e)) and np.all(z == 0)
+        assert np.array_equal(codes, o.e4m3_encode(v.astype(F32)))
+        assert np.array_equal(o.e4m3_decode(codes) * s[:, None].astype(np.float64), y.astype(np.float64))
+    y = _bf16_rows((200, 64), 42, scale=3.0)
+    packed, s, z, codes = o.encode_rows(y, o.FP8_E4M3)
+    xh = o.e4m3_decode(codes) * s[:, None].astype(np.float64)
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, s[:, None] * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(np.abs(xh - y) <= bound)
+    assert np.all(np.abs(o.e4m3_decode(codes)) <= 448.0)
+    zero = np.zeros((1, 64), F32)
+    _, s0, _, c0 = o.encode_rows(zero, o.FP8_E4M3)
+    assert s0[0] == 0 and np.all(c0 == 0)
+
+
+def check_fp8_attention(o):
+    """FP8 decode through a shuffled table (with rotation) equals float64 SDPA
+    over the gathered, un-rotated rows."""
+    t = _tiny_cache(o, o.FP8_E4M3, seed=9)
+    kc, km, vc, vm = t["planes"]
+    D, bs, Hkv = t["D"], t["bs"], t["Hkv"]
+    q = _bf16_rows((2, 4, D), 93)
+    out = o.decode_attention(q, t["lens"], o.FP8_E4M3, D, bs, Hkv, kc, km, vc, vm, 0.125, signs=t["signs"],
+                             block_tables=t["bt"])
+    R = scipy.linalg.hadamard(D) * t["signs"].astype(float)[None, :] / math.sqrt(D)
+    for b, L in enumerate(t["lens"]):
+        for hq in range(4):
+            h = hq // 2
+            rows = np.nonzero(t["tok_seq"] == b)[0]
+            K = o.e4m3_decode(o.encode_rows(t["k"][rows, h], o.FP8_E4M3, t["signs"])[3]) * \
+                o.encode_rows(t["k"][rows, h], o.FP8_E4M3, t["signs"])[1][:, None].astype(np.float64)
+            V = o.e4m3_decode(o.encode_rows(t["v"][rows, h], o.FP8_E4M3, t["signs"])[3]) * \
+                o.encode_rows(t["v"][rows, h], o.FP8_E4M3, t["signs"])[1][:, None].astype(np.float64)
+            ref = _sdpa64(q[b, hq][None], K @ R, V @ R, np.ones((1, L), bool), 0.125)[0]
+            assert np.allclose(out[b, hq], ref, atol=1e-12), (b, hq)
+
+
 # --------------------------------------------------- per-channel INT8 ------
 def _channel_batch(r, T, Hkv, D, exps):
     """[T, Hkv, D] rows whose per-(head, channel) absolute maximum over tokens

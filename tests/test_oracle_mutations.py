@@ -52,6 +52,12 @@ MUTATIONS = {
                            "out[present] = codes * np.asarray(channel_scales, np.float64)[1 - kv, h][None, :]"),
     "channel_scale_head": ("out[present] = codes * np.asarray(channel_scales, np.float64)[kv, h][None, :]",
                            "out[present] = codes * np.asarray(channel_scales, np.float64)[kv, 0][None, :]"),
+    "fp8_bias": ("v = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))",
+                 "v = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 8), np.ldexp(m / 8.0, -7))"),
+    "fp8_max": ("s = (a / _F32(E4M3_MAX)).astype(_F32)", "s = (a / _F32(240.0)).astype(_F32)"),
+    "fp8_ties_up": ("q = np.rint(a / np.ldexp(1.0, (e - 3).astype(np.int64)))   # 8 .. 16",
+                    "q = np.floor(a / np.ldexp(1.0, (e - 3).astype(np.int64)) + 0.5)"),
+    "fp8_subnormal_step": ("q_sub = np.rint(a / 2.0 ** -9)", "q_sub = np.rint(a / 2.0 ** -10)"),
     "headwise_slots_transposed": ("slots = np.asarray(slot_mapping_headwise, np.int64).reshape(T, Hkv)",
                                   "slots = np.asarray(slot_mapping_headwise, np.int64).reshape(Hkv, T).T"),
 }
