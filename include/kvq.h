@@ -47,12 +47,13 @@
  *    codes: uint8   [num_blocks, num_kv_heads, block_size, P]
  *           P = head_dim * b / 8, b = 8, 4, 2 bits
  *    meta : float32 [num_blocks, num_kv_heads, block_size, M]
- *           M = 1 (INT8: scale), 2 (INT4/INT2: scale, zero point) or 0
+ *           M = 1 (INT8, FP8: scale), 2 (INT4/INT2: scale, zero point) or 0
  *           (INT8_CHANNEL: the scales are per channel, in
  *           desc->channel_scales; meta pointers may then be NULL)
  *  A (token, kv head) row of codes is contiguous.  INT4 puts element 2j in the
  *  low nibble of byte j; INT2 puts element 4j+k in bits 2k..2k+1 of byte j;
- *  INT8 stores two's complement codes in [-127, 127].  Reconstruction:
+ *  INT8 stores two's complement codes in [-127, 127]; FP8 one E4M3 byte per
+ *  element.  Reconstruction:
  *  x_hat = c*s (INT8) or c*s + z (INT4/INT2), in the rotated basis when the
  *  cache has a rotation.
  */
@@ -84,8 +85,16 @@ typedef enum {
  * kv head, channel), s_d = max_t |x_d| / 127 over the first K/V a layer
  * receives (kvq_calibrate_channel_scales), then fixed; codes
  * clamp(rint(x_d * (1/s_d)), -127, 127), saturating; x_hat = c * s_d.  No
- * rotation and no per-row metadata (the meta planes are empty). */
-typedef enum { KVQ_INT8_SYM = 0, KVQ_INT4_ASYM = 1, KVQ_INT2_ASYM = 2, KVQ_INT8_CHANNEL = 3 } kvq_mode;
+ * rotation and no per-row metadata (the meta planes are empty).
+ * FP8_E4M3: per-token-head FP8 (the INT8/FP8 per-token-head schemes of the
+ * vLLM PR 40835 summary, 功能与动机): OCP E4M3 codes (bias 7, largest 448),
+ * s = max|y| / 448, code = y * (1/s) clamped to +-448 and rounded to the
+ * nearest E4M3 value (ties to even); x_hat = E4M3(code) * s; one meta float
+ * (s); optional rotation.  Chunked prefill is not built for this mode
+ * (KVQ_EUNSUPPORTED; kvq_gather_dequant gives the dense rows). */
+typedef enum {
+  KVQ_INT8_SYM = 0, KVQ_INT4_ASYM = 1, KVQ_INT2_ASYM = 2, KVQ_INT8_CHANNEL = 3, KVQ_FP8_E4M3 = 4
+} kvq_mode;
 
 typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 } kvq_out_dtype;
 

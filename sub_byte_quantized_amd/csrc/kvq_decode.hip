@@ -81,10 +81,14 @@ struct Geo {
 };
 
 // Bytes between consecutive query-piece planes of the decode LDS (Smem::qp:
-// 32 rows of a batch's (segment, head) pieces plus one zero row, D + 16
-// bytes each).
-template <int D, int PHI>
-constexpr int kQPlane = (32 / (16 / PHI) * (16 / PHI) + 1) * (D + 16);
+// 32 rows of a batch's (segment, head) pieces plus one zero row, QB D + 16
+// bytes each; QB = 1 for the int8 pieces, 2 for the bf16 pieces of FP8).
+template <int D, int PHI, int QB = 1>
+constexpr int kQPlane = (32 / (16 / PHI) * (16 / PHI) + 1) * (QB * D + 16);
+
+// Query bytes per element in the decode LDS.
+template <int MODE>
+constexpr int q_elem_bytes() { return MODE == kFp8Mode ? 2 : 1; }
 
 // d held by byte j (0..15) of the int8 operand of k-step s for lane-group
 // d-range `sub` (K pass); the query pieces in LDS are laid out in this order.
@@ -124,7 +128,17 @@ template <int MODE, int VW, int DTI, bool NARROW>
 __device__ __forceinline__ u32x4_t unpack_v(const uint32_t (*vc)[VW], uint32_t magic, uint32_t n4,
                                             uint32_t n2, uint32_t vsel) {
   u32x4_t a;
-  if constexpr (NARROW) {
+  if constexpr (MODE == kFp8Mode) {
+    // E4M3 byte of tokens 2p and 2p + 1 side by side, then both to bf16
+    // (every E4M3 value is a bf16 value)
+    constexpr int w = DTI >> 2;
+    constexpr uint32_t sel = (uint32_t)(DTI & 3) | ((4u + (DTI & 3)) << 8) | 0x0C0C0000u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t y = __builtin_amdgcn_perm(vc[2 * p + 1][w], vc[2 * p][w], sel);
+      a[p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)y, 1.0f, false));
+    }
+  } else if constexpr (NARROW) {
     // vsel picks byte 0 of the lane's bytes in each of the two dwords; byte
     // b of them is vsel + b in both selector fields
     constexpr uint32_t b = MODE == 1 ? DTI >> 1 : DTI >> 2;
@@ -328,21 +342,88 @@ struct LaneConst {
   uint32_t vsel;            // NARROW V rows: byte selector of the lane's first byte
 };
 
+// FP8 codes of masked rows set to zero.  A masked row may be unwritten or
+// stale (an absent sub-tile keeps the registers of an earlier tile), and an
+// E4M3 NaN byte (0x7F, 0xFF) there would reach every MFMA column through the
+// products with zero that the integer modes rely on (the K pass mixes the
+// phases' rows, the V pass sums over tokens).  Rows as issue_loads assigns
+// them: K-tile tau of lane group q holds token 16 (tau PHI + phase) + r, V
+// slot 4 s + i holds token 16 s + 4 q + i.
+template <int MODE, int D, int PHI>
+__device__ __forceinline__ void clear_masked_rows(Buf<MODE, D, PHI>& b, const TileInfo& t, int L, int start,
+                                                  int sink) {
+  using Gm = Geo<MODE, D, PHI>;
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  const int rr = ln & 15, qq = ln >> 4, pg = qq * PHI / 4;
+#pragma unroll
+  for (int tau = 0; tau < Gm::NKT; ++tau) {
+    const int sk = tau * PHI + pg;
+    const int pos = t.pos0 + 16 * sk + rr;
+    const bool keep = ((t.valid >> sk) & 1u) && pos < L && (pos >= start || pos < sink);
+#pragma unroll
+    for (int w = 0; w < Gm::KW; ++w) b.k[tau][w] = keep ? b.k[tau][w] : 0u;
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = t.pos0 + 16 * s + 4 * qq + i;
+      const bool keep = ((t.valid >> s) & 1u) && pos < L && (pos >= start || pos < sink);
+#pragma unroll
+      for (int w = 0; w < Gm::VW; ++w) b.v[4 * s + i][w] = keep ? b.v[4 * s + i][w] : 0u;
+    }
+}
+
 // full: every position of the tile is present and inside [start, L), so no
 // score needs a mask (wave-uniform; the masking sits behind a branch).
 template <int MODE, int D, int PHI>
-__device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const TileInfo& t, WaveState& st,
+__device__ __forceinline__ void compute_tile(Buf<MODE, D, PHI>& b, const TileInfo& t, WaveState& st,
                                              f32x4_t* acc, const LaneConst& lc, int L, int start, int sink,
                                              bool full) {
   using Gm = Geo<MODE, D, PHI>;
   constexpr int M = Gm::M;
   const int q = lc.q, phi_col = lc.phi_col;
+  if constexpr (MODE == kFp8Mode) {
+    if (__builtin_expect(!full, 0)) clear_masked_rows<MODE, D, PHI>(b, t, L, start, sink);
+  }
   // ---- K pass: int32 (a, b, c) dot products of the query pieces with the
   // codes; x = s_K (2^14 a + 2^7 b + c).code + z_K q1r, the log2 logit
   // being sp * x
   float sc[Gm::NKT][4];
 #pragma unroll
-  for (int tau = 0; tau < Gm::NKT; ++tau) {
+  for (int tau = 0; tau < Gm::NKT && MODE == kFp8Mode; ++tau) {
+    // FP8: E4M3 codes to bf16 (exact), bf16 MFMA against the query's three
+    // bf16 pieces (hi, mid, lo) into one float32 accumulator; x = s_K q'.code
+    constexpr int QP = kQPlane<D, PHI, 2>;
+    f32x4_t fa = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < Gm::KS; ++s) {
+      const u32x4_t c8 = unpack_k<MODE, Gm::KSW>(b.k[tau], s, 0u, 0u);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4_t a;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          a[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c8[2 * hh + w],
+                                                                                           1.0f, false));
+          a[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c8[2 * hh + w],
+                                                                                               1.0f, true));
+        }
+        const int8_t* qp = lc.qa + 32 * s + 16 * hh;
+        const uint4 xh = *reinterpret_cast<const uint4*>(qp);
+        const uint4 xm = *reinterpret_cast<const uint4*>(qp + QP);
+        const uint4 xl = *reinterpret_cast<const uint4*>(qp + 2 * QP);
+        fa = mfma(a, u32x4_t{xh.x, xh.y, xh.z, xh.w}, fa);
+        fa = mfma(a, u32x4_t{xm.x, xm.y, xm.z, xm.w}, fa);
+        fa = mfma(a, u32x4_t{xl.x, xl.y, xl.z, xl.w}, fa);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[tau][i] = fa[i] * b.km[tau][i];
+  }
+#pragma unroll
+  for (int tau = 0; tau < Gm::NKT && MODE != kFp8Mode; ++tau) {
     i32x4_t ia = {0, 0, 0, 0}, ib = {0, 0, 0, 0}, ic = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < Gm::KS; ++s) {
@@ -439,13 +520,14 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
       const uint32_t lo = pack_bf16(w2[0] - h0, w2[1] - h1);
       wh[tau][i / 2] = hi;
       wl[tau][i / 2] = lo;
-      wsum += (h0 + bf16_lo(lo)) + (h1 + bf16_hi(lo));
+      if constexpr (MODE != kFp8Mode) wsum += (h0 + bf16_lo(lo)) + (h1 + bf16_hi(lo));
     }
   }
   // ---- offset: acc -= 128 * (sum of the column's weights), as one MFMA per
-  // d-tile against the sum split into three bf16 pieces
-  wsum = add_xor32(add_xor16(wsum));
-  {
+  // d-tile against the sum split into three bf16 pieces (not for FP8, whose
+  // codes enter the V pass as their own values)
+  if constexpr (MODE != kFp8Mode) {
+    wsum = add_xor32(add_xor16(wsum));
     const __bf16 w0 = (__bf16)wsum;
     const float r1 = wsum - (float)w0;
     const __bf16 w1 = (__bf16)r1;
@@ -482,7 +564,7 @@ __device__ __forceinline__ void compute_tile(const Buf<MODE, D, PHI>& b, const T
 }
 
 template <int MODE, int D, int PHI>
-__device__ __forceinline__ void run_tile(const Buf<MODE, D, PHI>& b, const TileInfo& t, WaveState& st,
+__device__ __forceinline__ void run_tile(Buf<MODE, D, PHI>& b, const TileInfo& t, WaveState& st,
                                          f32x4_t* acc, const LaneConst& lc, int L, int start, int sink) {
   if (!t.valid) return;
   const bool full = t.valid == 0xFu && (t.pos0 >= start || t.pos0 + 64 <= sink) && t.pos0 + 64 <= L;
@@ -567,6 +649,30 @@ __device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, 
     for (int e = 0; e < E; ++e) x[e] *= p.chs[(int64_t)h * D + E * lane + e];
   }
   const float qmul = ROT ? p.qscale * p.inv_sqrt_d : p.qscale;
+  if constexpr (MODE == kFp8Mode) {
+    // three bf16 pieces hi + mid + lo of q' (each residual exact in float32,
+    // the sum within 2^-24 of q' relative); sp = 1, q1r = 0
+#pragma unroll
+    for (int e = 0; e < E; ++e) scratch[E * lane + e] = x[e] * qmul;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int pos = lane + 64 * j;
+      const int sub = pos / Gm::SUBD, rem = pos - sub * Gm::SUBD;
+      const float v = scratch[kmap<MODE, D, PHI>(sub, rem >> 4, rem & 15)];
+      const __bf16 hi = (__bf16)v;
+      const float r1 = v - (float)hi;
+      const __bf16 mid = (__bf16)r1;
+      const __bf16 lo = (__bf16)(r1 - (float)mid);
+      reinterpret_cast<__bf16*>(qa)[pos] = hi;
+      reinterpret_cast<__bf16*>(qb)[pos] = mid;
+      reinterpret_cast<__bf16*>(qc)[pos] = lo;
+    }
+    if (lane == 0) {
+      *qs = 1.0f;
+      *q1 = 0.0f;
+    }
+    return;
+  }
   float mx = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -645,16 +751,16 @@ struct SegRec {
   int pad[2];
 };
 
-template <int D, int PHI, int NWV>
+template <int D, int PHI, int NWV, int QB>
 struct Smem {
   static constexpr int GM = 16 / PHI;   // most heads of a kv head's group (G * PHI <= 16)
   static constexpr int NS = 32 / GM;    // segments of one batch (their pieces stay in LDS)
-  static constexpr int QW = D + 16;     // piece row stride: 16 bytes of padding spread banks
-  // query pieces a, b, c in k-slot order: piece p of row (segment k, head
-  // g) at qp[p][k GM + g]; row NS GM of every piece is zero (the B rows of
-  // columns without work)
+  static constexpr int QW = QB * D + 16;   // piece row stride: 16 bytes of padding spread banks
+  // query pieces a, b, c (int8; FP8: bf16 hi, mid, lo) in k-slot order:
+  // piece p of row (segment k, head g) at qp[p][k GM + g]; row NS GM of every
+  // piece is zero (the B rows of columns without work)
   alignas(16) int8_t qp[3][NS * GM + 1][QW];
-  static_assert(sizeof(qp[0]) == (size_t)kQPlane<D, PHI>, "query plane stride");
+  static_assert(sizeof(qp[0]) == (size_t)kQPlane<D, PHI, QB>, "query plane stride");
   float qs[NS][GM];                     // sp: (max|q'| / 127) / 2^14
   float q1[NS][GM];                     // q1r: sum over d of 2^14 a + 2^7 b + c
   SegRec seg[NS];
@@ -729,8 +835,8 @@ struct Cursor {
   int tb, te, off, blk0, L, start, h, n2;
 };
 
-template <int D, int PHI, int NWV>
-__device__ __forceinline__ void cursor_seek(Cursor& c, const Smem<D, PHI, NWV>& sm, int wave) {
+template <int D, int PHI, int NWV, int QB>
+__device__ __forceinline__ void cursor_seek(Cursor& c, const Smem<D, PHI, NWV, QB>& sm, int wave) {
   for (; c.ls < c.nseg; ++c.ls) {
     const SegRec& s = sm.seg[c.ls];
     c.tb = __builtin_amdgcn_readfirstlane(s.tb);
@@ -747,8 +853,8 @@ __device__ __forceinline__ void cursor_seek(Cursor& c, const Smem<D, PHI, NWV>& 
   }
 }
 
-template <bool CB, int D, int PHI, int NWV>
-__device__ __forceinline__ TileInfo cursor_info(const Cursor& c, const Smem<D, PHI, NWV>& sm, int wave, int bl,
+template <bool CB, int D, int PHI, int NWV, int QB>
+__device__ __forceinline__ TileInfo cursor_info(const Cursor& c, const Smem<D, PHI, NWV, QB>& sm, int wave, int bl,
                                                 int hkv, int nblk, int sink) {
   if (c.ls >= c.nseg) {
     TileInfo t;
@@ -759,8 +865,8 @@ __device__ __forceinline__ TileInfo cursor_info(const Cursor& c, const Smem<D, P
                        c.start > 0 ? sink : 0, bl, hkv, c.h, nblk);
 }
 
-template <int D, int PHI, int NWV>
-__device__ __forceinline__ void cursor_next(Cursor& c, const Smem<D, PHI, NWV>& sm, int wave) {
+template <int D, int PHI, int NWV, int QB>
+__device__ __forceinline__ void cursor_next(Cursor& c, const Smem<D, PHI, NWV, QB>& sm, int wave) {
   if (++c.li < c.n2) return;
   c.li = 0;
   ++c.ls;
@@ -784,13 +890,13 @@ __device__ __forceinline__ float load_dev(const float* a) {
 // the thread folds each over its pieces in slot order with the online-softmax
 // update, and requests the (m, l, acc) of KP pieces of every value at once,
 // so a pass over pairs of at most KP pieces waits on memory once.
-template <int MODE, int D, int PHI, int NWV, bool ROT, int KP>
-__device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI, NWV>& sm, int np, int s0a, int na,
+template <int MODE, int D, int PHI, int NWV, bool ROT, int KP, int QB>
+__device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI, NWV, QB>& sm, int np, int s0a, int na,
                                              int64_t o0a, int s0b, int nb, int64_t o0b, int tid) {
   constexpr int NT = 64 * NWV;
   // values per thread and pass: enough to cover the largest group in one
   // pass where the threads are few, at most two (registers)
-  constexpr int U = (Smem<D, PHI, NWV>::GM * D + NT - 1) / NT >= 2 ? 2 : 1;
+  constexpr int U = (Smem<D, PHI, NWV, QB>::GM * D + NT - 1) / NT >= 2 ? 2 : 1;
   const int G = p.group;
   const int GD = G * D;
   const int lane = tid & 63, wave = tid >> 6;
@@ -930,7 +1036,7 @@ __device__ __forceinline__ int first_after(const int32_t* pref, int cn, int cbas
 template <int MODE, int D, int PHI, bool ROT, bool CB, int NWV>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<MODE, D, PHI>())))
 void decode_kernel(DecodeParams p) {
-  using Sm = Smem<D, PHI, NWV>;
+  using Sm = Smem<D, PHI, NWV, q_elem_bytes<MODE>()>;
   using Gm = Geo<MODE, D, PHI>;
   constexpr int NT = 64 * NWV, NS = Sm::NS;
   constexpr int QR = (NS * Sm::GM + NWV - 1) / NWV;      // query rows per wave in a batch prologue
@@ -1202,7 +1308,7 @@ void decode_kernel(DecodeParams p) {
       lc.phi_col = phi_col;
       lc.head_ok = g_col < G;
       const bool brow = lc.head_ok && phi_grp == phi_col;
-      lc.qa = &sm.qp[0][brow ? k * Sm::GM + g_col : NS * Sm::GM][sub * Gm::SUBD];
+      lc.qa = &sm.qp[0][brow ? k * Sm::GM + g_col : NS * Sm::GM][q_elem_bytes<MODE>() * sub * Gm::SUBD];
       lc.sp = lc.head_ok ? sm.qs[k][g_col] : 1.0f;
       lc.q1r = lc.head_ok ? sm.q1[k][g_col] : 0.0f;
       lc.magic = magic;
@@ -1393,6 +1499,7 @@ int decode_wgs_per_cu(int mode, int d, int group) {
   KVQ_W(1, 64, 4) KVQ_W(1, 64, 2) KVQ_W(1, 64, 1) KVQ_W(1, 128, 4) KVQ_W(1, 128, 2) KVQ_W(1, 128, 1)
   KVQ_W(2, 64, 4) KVQ_W(2, 64, 2) KVQ_W(2, 64, 1) KVQ_W(2, 128, 4) KVQ_W(2, 128, 2) KVQ_W(2, 128, 1)
   KVQ_W(3, 64, 4) KVQ_W(3, 64, 2) KVQ_W(3, 64, 1) KVQ_W(3, 128, 4) KVQ_W(3, 128, 2) KVQ_W(3, 128, 1)
+  KVQ_W(4, 64, 4) KVQ_W(4, 64, 2) KVQ_W(4, 64, 1) KVQ_W(4, 128, 4) KVQ_W(4, 128, 2) KVQ_W(4, 128, 1)
 #undef KVQ_W
   return 4;
 }
@@ -1402,7 +1509,8 @@ hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, hipSt
     case 0: return launch_decode_m<0>(d, rot, p, s);
     case 1: return launch_decode_m<1>(d, rot, p, s);
     case 2: return launch_decode_m<2>(d, rot, p, s);
-    default: return launch_decode_m<kChannelMode>(d, rot, p, s);
+    case kChannelMode: return launch_decode_m<kChannelMode>(d, rot, p, s);
+    default: return launch_decode_m<kFp8Mode>(d, rot, p, s);
   }
 }
 

@@ -124,8 +124,17 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
       sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
     }
     float x[8];
+    if constexpr (MODE == kFp8Mode) {   // E4M3 values, exact in float32, times the row scale
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+      for (int w = 0; w < 2; ++w) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[it][w], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[it][w], true);
+        x[4 * w] = lo[0] * s[it]; x[4 * w + 1] = lo[1] * s[it];
+        x[4 * w + 2] = hi[0] * s[it]; x[4 * w + 3] = hi[1] * s[it];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8 && MODE != kFp8Mode; ++i) {
       int c;
       if constexpr (MODE == 0 || MODE == kChannelMode) c = (int)(int8_t)((raw[it][i >> 2] >> (8 * (i & 3))) & 0xffu);
       else if constexpr (MODE == 1) c = (int)((raw[it][0] >> (4 * i)) & 0xFu);
@@ -212,7 +221,8 @@ hipError_t launch_gather(int mode, int d, bool rot, const GatherParams& p, hipSt
     case 0: return launch_gather_m<0>(d, rot, p, s);
     case 1: return launch_gather_m<1>(d, rot, p, s);
     case 2: return launch_gather_m<2>(d, rot, p, s);
-    default: return launch_gather_m<kChannelMode>(d, rot, p, s);
+    case kChannelMode: return launch_gather_m<kChannelMode>(d, rot, p, s);
+    default: return launch_gather_m<kFp8Mode>(d, rot, p, s);
   }
 }
 

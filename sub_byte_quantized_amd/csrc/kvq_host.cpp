@@ -45,7 +45,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 kvq_status check_desc(const kvq_cache_desc* d) {
   if (!d) return fail(KVQ_EINVAL, "desc is NULL");
-  if (d->mode < KVQ_INT8_SYM || d->mode > KVQ_INT8_CHANNEL)
+  if (d->mode < KVQ_INT8_SYM || d->mode > KVQ_FP8_E4M3)
     return fail(KVQ_EINVAL, "mode %d is not a kvq_mode", d->mode);
   if (d->head_dim != 64 && d->head_dim != 128) {
     if (d->head_dim > 0 && (d->head_dim & (d->head_dim - 1)) == 0)
@@ -285,6 +285,9 @@ kvq_status check_prefill_sizes(const kvq_cache_desc* desc, int num_seqs, int num
                                int max_seq_len) {
   kvq_status st = check_desc(desc);
   if (st != KVQ_OK) return st;
+  if (desc->mode == KVQ_FP8_E4M3)
+    return fail(KVQ_EUNSUPPORTED, "chunked prefill is not built for KVQ_FP8_E4M3 (kvq_gather_dequant gives the "
+                "dense rows)");
   if (num_seqs < 0) return fail(KVQ_EINVAL, "num_seqs %d < 0", num_seqs);
   if (num_q_heads < 1) return fail(KVQ_EINVAL, "num_q_heads %d < 1", num_q_heads);
   if (num_q_heads % desc->num_kv_heads != 0)

@@ -9,12 +9,17 @@ namespace kvq {
 
 // Code bits, metadata floats per row and levels, by mode (0 INT8 per token
 // and head, 1 INT4, 2 INT2, 3 INT8 with per-channel scales and no per-row
-// metadata).
-__host__ __device__ constexpr int mode_bits(int mode) { return (mode == 0 || mode == 3) ? 8 : (mode == 1 ? 4 : 2); }
-__host__ __device__ constexpr int mode_meta(int mode) { return mode == 0 ? 1 : (mode == 3 ? 0 : 2); }
-__host__ __device__ constexpr int mode_levels(int mode) { return (mode == 0 || mode == 3) ? 127 : (mode == 1 ? 15 : 3); }
+// metadata, 4 FP8 E4M3 per token and head: one scale, codes up to 448).
+__host__ __device__ constexpr int mode_bits(int mode) {
+  return (mode == 0 || mode == 3 || mode == 4) ? 8 : (mode == 1 ? 4 : 2);
+}
+__host__ __device__ constexpr int mode_meta(int mode) { return (mode == 0 || mode == 4) ? 1 : (mode == 3 ? 0 : 2); }
+__host__ __device__ constexpr int mode_levels(int mode) {
+  return (mode == 0 || mode == 3) ? 127 : (mode == 1 ? 15 : (mode == 4 ? 448 : 3));
+}
 // Per-channel scales: [2][Hkv][D] float32, K then V.
 constexpr int kChannelMode = 3;
+constexpr int kFp8Mode = 4;
 __host__ __device__ constexpr int row_bytes(int mode, int d) { return d * mode_bits(mode) / 8; }
 
 // Positions the decode kernel processes as one tile (four 16-token MFMA tiles).

@@ -107,7 +107,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     }
   }
   float s = 0.0f, z = 0.0f;   // per-row scale and zero (not for per-channel INT8)
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == 0 || MODE == kFp8Mode) {
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
@@ -131,7 +131,22 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     z = mn;
   }
 
-  if constexpr (MODE != kChannelMode) {
+  if constexpr (MODE == kFp8Mode) {
+    // FP8: t = clamp(x * (1/s), -448, 448), nearest E4M3 (ties to even) by
+    // the hardware conversion, two values per instruction; zero, subnormal or
+    // NaN scale: all-zero codes
+    const bool ok = s >= 1.17549435e-38f;
+    const float inv = ok ? 1.0f / s : 0.0f;
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = ok ? fminf(fmaxf(x[i] * inv, -kLevels), kLevels) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[4 * j], t[4 * j + 1], 0, false);
+      w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[4 * j + 2], t[4 * j + 3], (int)w, true);
+      c[4 * j] = w & 0xffu; c[4 * j + 1] = (w >> 8) & 0xffu; c[4 * j + 2] = (w >> 16) & 0xffu; c[4 * j + 3] = w >> 24;
+    }
+  } else if constexpr (MODE != kChannelMode) {
     // zero, subnormal or NaN scale: all-zero codes
     const bool ok = s >= 1.17549435e-38f;
     const float inv = ok ? 1.0f / s : 0.0f;
@@ -153,7 +168,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   uint8_t* codes = (kv ? p.v_codes : p.k_codes) + ridx * P + lr * BPL;
   float* meta = (kv ? p.v_meta : p.k_meta) + ridx * M;   // unused when M == 0
 
-  if constexpr (MODE == 0 || MODE == kChannelMode) {
+  if constexpr (mode_bits(MODE) == 8) {
     uint2 w;
     w.x = (c[0] & 0xffu) | ((c[1] & 0xffu) << 8) | ((c[2] & 0xffu) << 16) | ((c[3] & 0xffu) << 24);
     w.y = (c[4] & 0xffu) | ((c[5] & 0xffu) << 8) | ((c[6] & 0xffu) << 16) | ((c[7] & 0xffu) << 24);

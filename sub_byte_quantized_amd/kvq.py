@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (KVQ_INT2_ASYM, KVQ_INT4_ASYM, KVQ_INT8_CHANNEL, KVQ_INT8_SYM,  # noqa: F401
+from ._lib import (KVQ_FP8_E4M3, KVQ_INT2_ASYM, KVQ_INT4_ASYM, KVQ_INT8_CHANNEL, KVQ_INT8_SYM,  # noqa: F401
                    KVQ_OUT_BF16, KVQ_OUT_F32)
 
 

@@ -77,14 +77,24 @@ def assert_close(got, ref, what=""):
     assert mx <= ATOL_MAX and mean <= ATOL_MEAN, f"{what}: max-abs {mx:.3e} mean-abs {mean:.3e}"
 
 
+def code_ordinals(packed, mode, D):
+    """Codes as integers in value order: the codes themselves, or for FP8 the
+    E4M3 byte's magnitude bits with its sign (adjacent E4M3 values differ by
+    one; +0 and -0 are both 0)."""
+    if mode == oracle.FP8_E4M3:
+        c = np.asarray(packed, np.int64)
+        return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+    return oracle.unpack_codes(packed, mode, D).astype(np.int64)
+
+
 def compare_codes(spec, got_codes, ref_codes, rotated, what=""):
     """Packed codes: bit-exact without rotation; with rotation at most 0.01 %
     of elements may differ, each by one step."""
     if not rotated:
         assert np.array_equal(got_codes, ref_codes), f"{what}: codes differ"
         return
-    g = oracle.unpack_codes(got_codes, spec.mode, spec.D).astype(np.int64)
-    r = oracle.unpack_codes(ref_codes, spec.mode, spec.D).astype(np.int64)
+    g = code_ordinals(got_codes, spec.mode, spec.D)
+    r = code_ordinals(ref_codes, spec.mode, spec.D)
     diff = np.abs(g - r)
     n_bad = int((diff > 0).sum())
     print(f"[parity] {what}: {n_bad} of {diff.size} codes differ (max step {int(diff.max())})")

@@ -44,21 +44,21 @@ def test_exports_every_header_symbol(lib):
         assert name in _lib.SIGNATURES, f"binding lacks {name}"
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("D", [64, 128])
 def test_layout_matches_formula(lib, mode, D):
     d = desc(mode, D, H=3, bs=32, nb=7)
     out = _lib.Layout()
     assert lib.kvq_query_layout(ctypes.byref(d), ctypes.byref(out)) == 0
     cshape, mshape = oracle.plane_shapes(mode, D, 3, 32, 7)
-    assert out.row_code_bytes == cshape[-1] == D * {0: 8, 1: 4, 2: 2, 3: 8}[mode] // 8
+    assert out.row_code_bytes == cshape[-1] == D * {0: 8, 1: 4, 2: 2, 3: 8, 4: 8}[mode] // 8
     assert out.row_meta_floats == mshape[-1]
     assert out.code_bytes == 7 * 3 * 32 * cshape[-1]
     assert out.meta_bytes == 7 * 3 * 32 * mshape[-1] * 4
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(mode=4), _lib.KVQ_EINVAL), (dict(mode=-1), _lib.KVQ_EINVAL),
+    (dict(mode=5), _lib.KVQ_EINVAL), (dict(mode=-1), _lib.KVQ_EINVAL),
     (dict(mode=3, signs=4096), _lib.KVQ_EUNSUPPORTED),
     (dict(D=96), _lib.KVQ_EINVAL), (dict(D=256), _lib.KVQ_EUNSUPPORTED), (dict(D=0), _lib.KVQ_EINVAL),
     (dict(H=0), _lib.KVQ_EINVAL), (dict(bs=8), _lib.KVQ_EINVAL), (dict(bs=40), _lib.KVQ_EINVAL), (dict(bs=48), _lib.KVQ_EINVAL),
@@ -237,6 +237,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, d, B=0) == _lib.KVQ_OK                      # nothing to do
     assert _prefill(lib, d, mq=0) == _lib.KVQ_OK
     assert _prefill(lib, desc(D=96)) == _lib.KVQ_EINVAL
+    assert _prefill(lib, desc(mode=4, H=4, bs=64)) == _lib.KVQ_EUNSUPPORTED   # no FP8 prefill
+    assert "FP8" in lib.kvq_last_error().decode()
 
 
 def test_prefill_workspace_size(lib):
@@ -250,6 +252,9 @@ def test_prefill_workspace_size(lib):
     assert lib.kvq_prefill_workspace_size(ctypes.byref(d), 16, 16, -2, 32768, ctypes.byref(n)) == _lib.KVQ_EINVAL
     assert lib.kvq_prefill_workspace_size(ctypes.byref(d), 16, 16, 512, 32768, None) == _lib.KVQ_EINVAL
     assert lib.kvq_prefill_workspace_size(None, 16, 16, 512, 32768, ctypes.byref(n)) == _lib.KVQ_EINVAL
+    d4 = desc(mode=4, H=4, bs=64)
+    assert lib.kvq_prefill_workspace_size(ctypes.byref(d4), 16, 16, 512, 32768, ctypes.byref(n)) \
+        == _lib.KVQ_EUNSUPPORTED
 
 
 def test_workspace_size_grows_with_work(lib):

@@ -28,7 +28,7 @@ def run_and_check(spec, what=None, pairs=None, **kw):
 
 
 SPECS = []
-for mode in (0, 1, 2):
+for mode in (0, 1, 2, 4):
     for D in (64, 128):
         for rot in (False, True):
             SPECS.append(synth.small_spec(name=f"m{mode}-d{D}-r{int(rot)}", cfg=400 + 10 * mode + D // 64 + 5 * rot,

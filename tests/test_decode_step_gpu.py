@@ -43,6 +43,7 @@ CASES = [
     dict(name="m1-b16-rot", mode=1, rotate=True, bs=16, D=128, lens=[0, 17, 129, 700, 1500], B=5, Hkv=2, Hq=10),
     dict(name="m2-b64-rot", mode=2, rotate=True, bs=64, D=128, lens=[5, 4000, 63, 128], B=4, Hkv=4, Hq=16),
     dict(name="m1-d64-rot", mode=1, rotate=True, bs=16, D=64, lens=[3, 200, 1000], B=3, Hkv=2, Hq=4),
+    dict(name="m4-b16-rot", mode=4, rotate=True, bs=16, D=128, lens=[1, 64, 300, 1000], B=4, Hkv=2, Hq=8),
     dict(name="m1-headwise-window", mode=1, rotate=True, bs=64, D=128, lens=[300, 1000, 129], B=3, Hkv=4, Hq=16,
          window=[100, 64, 0, 0], headwise=True, evict_outside_window=True),
 ]

@@ -172,6 +172,8 @@ PEAKED = [
                      lens=[300, 1000, 77]),
     synth.small_spec(name="peaked-int2-rot", cfg=722, mode=2, rotate=True, outliers=4, B=3, Hkv=2, Hq=8,
                      lens=[300, 1000, 77]),
+    synth.small_spec(name="peaked-fp8", cfg=723, mode=4, rotate=False, outliers=4, B=3, Hkv=2, Hq=8,
+                     lens=[300, 1000, 77]),
 ]
 
 
@@ -189,6 +191,8 @@ def test_peaked_softmax_decode_and_prefill(spec):
     # the softmax really is peaked: the largest weight of most (sequence, head)
     # rows is above 0.5 in the oracle's float64 softmax
     gh.assert_close(out.cpu().numpy(), ref, f"{spec.name} decode")
+    if spec.mode == oracle.FP8_E4M3:   # no chunked prefill for FP8
+        return
     n_new = [40, 64, 77]
     q, cu = gh.prefill_inputs(spec, n_new, stream=61)
     q = (q.float() * 8.0).to(torch.bfloat16)

@@ -59,7 +59,7 @@ def oracle_gather(spec, case, planes_np, cu):
 
 
 SPECS = []
-for mode in (0, 1, 2):
+for mode in (0, 1, 2, 4):
     for D in (64, 128):
         for rot in (False, True):
             SPECS.append(synth.small_spec(name=f"m{mode}-d{D}-r{int(rot)}", cfg=700 + 10 * mode + D // 64 + 5 * rot,
