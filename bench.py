@@ -1,37 +1,47 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized paged KV cache on one MI355X.
 
-A step is one decode step of the workload: quantize-on-write of the step's
-new token of every sequence, then paged decode attention of every sequence
-over its whole cache, both in one launch (kvq_decode_step; ``--unfused``
-runs kvq_reshape_and_cache then kvq_paged_decode_attention instead).
-The default workload is the INT8 per-token-head symmetric decode (batch 32,
-32 q / 8 kv heads, head_dim 128, block 64, seq_lens ~U[1024, 8192], 4 outlier
-channels x10); --config selects the others.  The cache is built once (untimed)
-and copied into enough replicas (>= 1.2 GB in total) that steps cycle through
-memory larger than the 256 MB Infinity Cache.
+The headline workload (default, ``--config 4``) is the largest one: INT2
+asymmetric + Hadamard decode, batch 4 x 131 072 positions, 32 q / 8 kv
+heads, head_dim 128, block 64, with 48 layers' caches held as separate
+buffers.  A step is one decode step of the whole model: for every layer in
+turn, one launch of kvq_decode_step (quantize-on-write of each sequence's
+new token, then paged decode attention over the layer's cache), 48 launches
+back to back.  ``--config 2`` / ``3`` time one-layer workloads whose step is
+one launch, cycling cache replicas (>= 1.2 GB in all) so that steps stream
+from HBM rather than the 256 MB Infinity Cache; ``--config 5`` is the mixed
+step (write, chunked prefill, decode).  With the default config the INT8,
+INT4 and mixed-step workloads, and the INT8 workload's shapes held as FP8
+E4M3 and as per-channel INT8 ("2:fp8", "2:chan"), are measured in the same
+run and reported as sub-objects under ``configs``.
 
-Prints ONE JSON line.  ``value`` is decode effective KV GB/s of the whole
-step: the algorithmic bytes decode reads (packed codes + fp32 scale/zero of
-attended tokens, plus queries, outputs and block-table entries) divided by
-the step time, steps launched back to back (``--graph`` replays each from a
-HIP graph instead).  ``roofline`` is the step's kernel alone: after the
-timed steps, ``steps`` back-to-back launches between two HIP events on the
-stream it runs on, divided by ``steps``; its algorithmic bytes add the new
-tokens' write (bf16 rows read, codes + meta + slots).  ``decode_only`` is
-kvq_paged_decode_attention timed the same way, ``write.step_write_us`` the
-step's write alone.  ``write`` also reports quantize-write tokens/s on a
-whole-cache fill, ``gather`` the dequantize-gather of the whole cache.
-Fractions are against the 8 TB/s nominal and, as ``frac_of_measured_copy``,
-against a 1 GiB device copy timed in the same run.  ``cpu_baseline`` times the oracle on a bounded sample.
+Prints ONE JSON line.  Timing: after ``warmup`` untimed steps, ``repeats``
+(>= 5) timed regions of exactly ``steps`` steps, each bracketed by
+synchronize + wall clock and by two HIP events on the stream the kernels
+run on; ``ms_per_step`` and ``value`` come from the median region.
+``value`` is decode effective KV GB/s of the whole step: the algorithmic
+bytes decode reads (packed codes + fp32 scale/zero of attended tokens, plus
+queries, outputs and block-table entries; all layers) over the step time.
+``roofline`` is the step's kernel: its average launch time is the median
+region's event span divided by the launches in it, so it can never exceed
+the step time; its algorithmic bytes add the new tokens' write.  ``write``
+reports quantize-write tokens/s on a whole-cache fill of one layer,
+``gather`` the dequantize-gather of one layer's cache.  Fractions are
+against the 8 TB/s nominal and against a 1 GiB device copy and a 4 GiB
+streaming read (a read-only HIP kernel, libkvq_bench.so) timed in the same
+run.  ``cpu_baseline`` times the oracle on a
+bounded sample, with all host threads and with one, median of 3 each.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import dataclasses
 import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -44,15 +54,40 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 import sub_byte_quantized_amd as kvq  # noqa: E402
 
+METRIC = "decode-attn effective KV GB/s (% HBM peak); quantize-write tokens/s"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFS = 2500.0
 MALL_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc")
-# sources that define the decode and prefill kernels (a counter summary is
-# tied to them)
+# sources that define each kernel (a counter summary is tied to them)
 DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h", "kvq_write_row.h")]
 PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")]
 GATHER_SRC = [os.path.join(CSRC, f) for f in ("kvq_gather.hip", "kvq_device.h", "kvq_internal.h")]
 WRITE_SRC = [os.path.join(CSRC, f) for f in ("kvq_write.hip", "kvq_write_row.h", "kvq_device.h", "kvq_internal.h")]
+MODE_NAMES = ["int8_sym", "int4_asym", "int2_asym", "int8_channel", "fp8_e4m3"]
+# per-mode decode contraction types
+MODE_DTYPES = {0: "int8 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
+               1: "int4 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
+               2: "int2 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
+               3: "int8 codes (per-channel scales); int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
+               4: "fp8 e4m3 codes; bf16 mfma (q.k, p.v), fp32 accumulate"}
+# workload variants a sub-object may name as "<config>:<variant>": the
+# config's shapes and inputs with another cache mode
+VARIANTS = {"fp8": dict(mode=4, rotate=False, suffix="fp8-e4m3"),
+            "chan": dict(mode=3, rotate=False, suffix="int8-channel")}
+
+
+def spec_of(key):
+    """synth.CONFIGS[c] for "c"; for "c:variant" the same workload with the
+    variant's cache mode (one-layer workloads only)."""
+    c, _, var = str(key).partition(":")
+    spec = synth.CONFIGS[int(c)]
+    if not var:
+        return spec
+    v = VARIANTS[var]
+    if spec.layers > 1 or spec.n_prefill:
+        raise SystemExit(f"variant {var} is for one-layer decode workloads")
+    return dataclasses.replace(spec, name=f"{spec.name}-{v['suffix']}", mode=v["mode"], rotate=v["rotate"])
 
 
 def sha(paths):
@@ -63,13 +98,20 @@ def sha(paths):
     return h.hexdigest()[:16]
 
 
+def row_layout(spec):
+    """(packed code bytes, fp32 meta floats) of one (token, kv head) row:
+    INT8 8 bits + scale, INT4 4 bits + scale and zero, INT2 2 bits + scale
+    and zero, per-channel INT8 8 bits and no meta, FP8 8 bits + scale."""
+    bits = {0: 8, 1: 4, 2: 2, 3: 8, 4: 8}[spec.mode]
+    return spec.D * bits // 8, {0: 1, 1: 2, 2: 2, 3: 0, 4: 1}[spec.mode]
+
+
 def decode_algo_bytes(spec, case, first=0):
     """Algorithmic bytes one decode launch over sequences first..B-1 reads and
     writes: codes + meta of every attended token (positions inside the
     window, in non-evicted blocks, below seq_len), the block-table entries
     walked, queries and outputs."""
-    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
-    M = 1 if spec.mode == 0 else 2
+    P, M = row_layout(spec)
     row = 2 * (P + 4 * M)
     lens = case.seq_lens.cpu().numpy().astype(np.int64)
     win = None if case.window is None else case.window.cpu().numpy()
@@ -95,7 +137,8 @@ def decode_algo_bytes(spec, case, first=0):
     kv = tokens * row
     q = nb * spec.Hq * spec.D * 2
     out = nb * spec.Hq * spec.D * 4
-    return kv + q + out + 4 * entries + 4 * nb, kv, tokens
+    chs = 2 * spec.Hkv * spec.D * 4 if spec.mode == 3 else 0   # per-channel scales
+    return kv + q + out + 4 * entries + 4 * nb + chs, kv, tokens
 
 
 def prefill_work(spec, case):
@@ -104,8 +147,7 @@ def prefill_work(spec, case):
     p = L - n + i sees keys j <= p in present blocks and, for a windowed kv
     head, j >= p - W + 1), times the G q heads; flops = 4 D per pair (q.k and
     p.v); KV bytes = codes + meta of the positions any row of the chunk sees."""
-    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
-    M = 1 if spec.mode == 0 else 2
+    P, M = row_layout(spec)
     row = 2 * (P + 4 * M)
     G = spec.Hq // spec.Hkv
     lens = case.seq_lens.cpu().numpy().astype(np.int64)
@@ -130,8 +172,7 @@ def prefill_work(spec, case):
 
 
 def write_bytes_per_token(spec):
-    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
-    M = 1 if spec.mode == 0 else 2
+    P, M = row_layout(spec)
     slot = 8 * (spec.Hkv if spec.headwise else 1)
     return spec.Hkv * 2 * (spec.D * 2 + P + 4 * M) + slot
 
@@ -141,8 +182,7 @@ def gather_bytes(spec, case, nseq=None):
     whole contexts (all by default): per (position, kv head) row of K and of
     V, the packed codes and fp32 meta read (rows in present blocks) and the
     bf16 row written; plus the block-table entries and cu_seq_lens read."""
-    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
-    M = 1 if spec.mode == 0 else 2
+    P, M = row_layout(spec)
     lens = case.seq_lens.cpu().numpy().astype(np.int64)[:nseq]
     present = 0
     entries = 0
@@ -160,63 +200,38 @@ def gather_bytes(spec, case, nseq=None):
     return 2 * present * (P + 4 * M) + 2 * rows * 2 * spec.D + 4 * entries + 4 * (len(lens) + 1)
 
 
-def gather_cpu(spec, case, planes, lens, seconds):
-    """The oracle's gather on the host cores: (sequence, kv head) pairs until
-    ~`seconds` have passed, as bytes of the same accounting per second."""
-    import oracle
-    pl = [p.cpu().numpy() for p in planes]
-    signs = None if case.rot_signs is None else case.rot_signs.cpu().numpy()
-    bt = case.tables.block_tables
-    bth = case.tables.block_tables_headwise
-    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
-    M = 1 if spec.mode == 0 else 2
-    done, nbytes = 0, 0
-    t0 = time.perf_counter()
-    for b in range(spec.B):
-        for h in range(spec.Hkv):
-            oracle.gather_head(b, h, int(lens[b]), spec.mode, spec.D, spec.bs, spec.Hkv, *pl, signs=signs,
-                               block_tables=bt, block_tables_headwise=bth)
-            done += 1
-            nbytes += 2 * int(lens[b]) * (P + 4 * M + 2 * spec.D)
-            if time.perf_counter() - t0 > seconds:
-                break
-        if time.perf_counter() - t0 > seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"GBps": round(nbytes / dt / 1e9, 4), "sample": f"{done} of {spec.B * spec.Hkv} (sequence, kv head) "
-            f"pairs in {dt:.1f} s", "cores": int(torch.get_num_threads()), "kind": "oracle"}
+# ---------------------------------------------------------------- timing ---
+def timed_regions(step, steps, launches, repeats):
+    """`repeats` timed regions of exactly `steps` calls of step(i), each
+    bracketed by synchronize + wall clock and by two HIP events on the
+    current stream (the kernels' own).  Returns per region (ms per step by
+    the wall clock, us per launch by the events); the event span lies inside
+    the wall-clock span, so launch time x launches <= step time."""
+    walls, launch_us = [], []
+    for _ in range(repeats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        walls.append((t1 - t0) * 1e3 / steps)
+        launch_us.append(e0.elapsed_time(e1) * 1e3 / (steps * launches))
+    return walls, launch_us
 
 
-def build_workload(spec, dev):
-    case = synth.make_case(spec, dev)
-    d = kvq.CacheDesc(spec.mode, spec.D, spec.Hkv, spec.bs, case.tables.num_blocks, case.rot_signs)
-    planes = kvq.alloc_cache(d, dev, poison=True)
-    kvq.kvq_reshape_and_cache(d, case.k, case.v, *planes, slot_mapping=case.slot_mapping,
-                              slot_mapping_headwise=case.slot_mapping_headwise)
-    # the step's new tokens: the last n_b positions of sequence b (one for a
-    # decode sequence, the chunk for a prefill sequence)
-    lens = case.seq_lens.cpu().numpy().astype(np.int64)
-    n_new = synth.new_tokens_of(spec)
-    ends = np.cumsum(lens)
-    last = np.concatenate([np.arange(e - n, e) for e, n in zip(ends, n_new)])
-    li = torch.as_tensor(last, device=dev)
-    new = dict(k=case.k[li].contiguous(), v=case.v[li].contiguous(),
-               sm=None if case.slot_mapping is None else case.slot_mapping[li].contiguous(),
-               smh=None if case.slot_mapping_headwise is None else case.slot_mapping_headwise[li].contiguous())
-    torch.cuda.synchronize()
-    return case, d, planes, new
+def median_region(walls, launch_us):
+    """Index of the median region by wall time."""
+    order = sorted(range(len(walls)), key=lambda i: walls[i])
+    return order[len(order) // 2]
 
 
-def measured_copy_gbs(dev, reps=5):
-    """Device-copy rate: 2 x 1 GiB moved per copy_ (read + write), best of
-    `reps` launches."""
-    n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    ms = min(time_events(lambda i: dst.copy_(src), reps))
-    del src, dst
-    return 2 * n / (ms * 1e-3) / 1e9
+def spread(x):
+    return [round(min(x), 4), round(max(x), 4)]
 
 
 def time_events(fn, reps):
@@ -230,71 +245,54 @@ def time_events(fn, reps):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
-def time_span(fn, reps):
-    """Mean duration of `reps` back-to-back calls: one HIP event before the
-    first and one after the last, on the current stream (the kernels' own)."""
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(reps):
-        fn(i)
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / reps
+def stream_read_lib():
+    """The benchmark's read-ceiling kernel (libkvq_bench.so, built beside
+    libkvq.so)."""
+    path = os.path.join(ROOT, "sub_byte_quantized_amd", "libkvq_bench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build first (python __graft_entry__.py)")
+    lib = ctypes.CDLL(path)
+    lib.kvq_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.kvq_bench_stream_read.restype = ctypes.c_int
+    return lib
 
 
-def cpu_baseline(spec, case, planes, seconds, min_seconds=10.0):
-    """The oracle, as it stands, on a bounded sample of the same decode: as
-    many (sequence, kv head) pairs as fit in ``seconds``; a workload whose
-    pairs all finish sooner is passed over again until ``min_seconds``."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    host_planes = [p.cpu().numpy() for p in planes]
-    q = case.q.float().cpu().numpy()
-    lens = case.seq_lens.cpu().numpy()
-    bt = None if case.block_tables is None else case.block_tables.cpu().numpy()
-    bth = None if case.block_tables_headwise is None else case.block_tables_headwise.cpu().numpy()
-    win = None if case.window is None else case.window.cpu().numpy()
-    signs = None if case.rot_signs is None else case.rot_signs.cpu().numpy()
-    P = spec.D * {0: 8, 1: 4, 2: 2}[spec.mode] // 8
-    M = 1 if spec.mode == 0 else 2
-    r = np.random.default_rng(0)
-    order = [(int(b), int(h)) for b, h in zip(r.permutation(np.repeat(np.arange(spec.B), spec.Hkv)),
-                                                np.tile(np.arange(spec.Hkv), spec.B))]
-    done, nbytes, passes = 0, 0, 0
-    t0 = time.perf_counter()
-    while True:
-        for b, h in order:
-            oracle.decode_attention(q, lens, spec.mode, spec.D, spec.bs, spec.Hkv, *host_planes,
-                                    case.softmax_scale, signs=signs, block_tables=bt,
-                                    block_tables_headwise=bth, window=win, pairs=[(b, h)])
-            W = int(win[h]) if win is not None else 0
-            L = int(lens[b])
-            nbytes += (min(L, W) if W > 0 else L) * 2 * (P + 4 * M)
-            done += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        passes += 1
-        if time.perf_counter() - t0 >= min(seconds, min_seconds):
-            break
-    dt = time.perf_counter() - t0
-    # oracle write on a token sample
-    tw0 = time.perf_counter()
-    nt = 2048
-    k = case.k[:nt].float().cpu().numpy()
-    v = case.v[:nt].float().cpu().numpy()
-    for src in (k, v):
-        oracle.encode_rows(src.reshape(-1, spec.D), spec.mode, signs)
-    tw = time.perf_counter() - tw0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} (sequence, kv head) decode pairs of {spec.B * spec.Hkv} ({passes} pass(es)) in {dt:.1f} s "
-                      f"(float64 attention over the GPU's stored planes); write: {nt} tokens in {tw:.2f} s",
-            "write_tokens_per_s": round(nt / tw, 1)}
+# (waves per CU, loads in flight per lane) tried for the read ceiling
+READ_SHAPES = ((4, 8), (8, 4), (12, 2), (16, 1), (32, 1))
+
+
+def measured_ceilings(dev, reps=5):
+    """Practical HBM ceilings timed in this run: a 1 GiB device copy (2 x 1
+    GiB moved per copy_) and a 4 GiB streaming read by a read-only HIP kernel
+    (best launch shape of READ_SHAPES), best of `reps` each, GB/s."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copy_ms = min(time_events(lambda i: dst.copy_(src), reps))
+    del src, dst
+    lib = stream_read_lib()
+    nb = 4 << 30
+    big = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)   # XOR of every 16-byte load is 0
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = float("inf")
+    for wpc, unroll in READ_SHAPES:
+        blocks = cus * wpc // 4
+
+        def rd(i, blocks=blocks, unroll=unroll):
+            rc = lib.kvq_bench_stream_read(big.data_ptr(), nb, 0x12345678, sink.data_ptr(), blocks, unroll, stream)
+            if rc != 0:
+                raise RuntimeError(f"kvq_bench_stream_read failed ({rc})")
+        rd(0)
+        best = min(best, min(time_events(rd, reps)))
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    del big, sink
+    torch.cuda.empty_cache()
+    return 2 * n / (copy_ms * 1e-3) / 1e9, nb / (best * 1e-3) / 1e9
 
 
 def load_traffic(name, srcs=DECODE_SRC):
@@ -308,6 +306,265 @@ def load_traffic(name, srcs=DECODE_SRC):
     if j.get("kernel_source_sha") != sha(srcs):
         return None
     return j.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------- workloads ---
+def new_token_index(spec, case):
+    """Token rows (into case.k / case.v) of each sequence's step tokens: the
+    last n_b positions of sequence b."""
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    n_new = synth.new_tokens_of(spec)
+    ends = np.cumsum(lens)
+    return np.concatenate([np.arange(e - n, e) for e, n in zip(ends, n_new)])
+
+
+def build_buffers(spec, dev, n_bufs, layers):
+    """The workload's caches.  layers: `n_bufs` layers, each written from its
+    own seeded K/V draws with its own queries; otherwise `n_bufs` replicas
+    (device copies) of one cache sharing one batch of queries.  Returns
+    (case of layer 0, desc, [dict(planes, q, new)])."""
+    case = synth.make_case(spec, dev)
+    d = kvq.CacheDesc(spec.mode, spec.D, spec.Hkv, spec.bs, case.tables.num_blocks, case.rot_signs)
+    if spec.mode == 3:
+        # per-channel INT8: scales from the layer's first K/V, here the whole
+        # cached context (one layer; the step's new tokens saturate if beyond)
+        assert not layers or n_bufs == 1
+        d.channel_scales = kvq.kvq_calibrate_channel_scales(d, case.k, case.v)
+    li = torch.as_tensor(new_token_index(spec, case), device=dev)
+    T = int(case.k.shape[0])
+
+    def new_of(k, v):
+        return dict(k=k[li].contiguous(), v=v[li].contiguous(),
+                    sm=None if case.slot_mapping is None else case.slot_mapping[li].contiguous(),
+                    smh=None if case.slot_mapping_headwise is None else case.slot_mapping_headwise[li].contiguous())
+
+    bufs = []
+    for l in range(n_bufs):
+        if l == 0 or not layers:
+            k, v, q = case.k, case.v, case.q
+        else:
+            k = synth.kv_values(spec, T, synth.S_K, dev, layer=l)
+            v = synth.kv_values(spec, T, synth.S_V, dev, layer=l)
+            q = synth.bf16_normal((spec.B, spec.Hq, spec.D), spec.cfg, synth.S_Q + 100 * l, dev)
+        if l == 0 or layers:
+            planes = kvq.alloc_cache(d, dev, poison=True)
+            kvq.kvq_reshape_and_cache(d, k, v, *planes, slot_mapping=case.slot_mapping,
+                                      slot_mapping_headwise=case.slot_mapping_headwise)
+        else:
+            planes = tuple(p.clone() for p in bufs[0]["planes"])
+        bufs.append(dict(planes=planes, q=q, new=new_of(k, v) if (l == 0 or layers) else bufs[0]["new"]))
+        if l > 0 and layers:
+            del k, v
+    torch.cuda.synchronize()
+    return case, d, bufs
+
+
+def cpu_baseline(spec, case, planes, seconds):
+    """The oracle, as it stands, on a bounded sample of the same decode:
+    (sequence, kv head) pairs in a seeded order until `seconds` have passed,
+    as algorithmic KV bytes per second.  Run three times with every host
+    thread the BLAS may use and three times with one; the medians are
+    reported."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+    host_planes = [p.cpu().numpy() for p in planes]
+    q = case.q.float().cpu().numpy()
+    lens = case.seq_lens.cpu().numpy()
+    bt = None if case.block_tables is None else case.block_tables.cpu().numpy()
+    bth = None if case.block_tables_headwise is None else case.block_tables_headwise.cpu().numpy()
+    win = None if case.window is None else case.window.cpu().numpy()
+    signs = None if case.rot_signs is None else case.rot_signs.cpu().numpy()
+    P, M = row_layout(spec)
+    r = np.random.default_rng(0)
+    order = [(int(b), int(h)) for b, h in zip(r.permutation(np.repeat(np.arange(spec.B), spec.Hkv)),
+                                                np.tile(np.arange(spec.Hkv), spec.B))]
+
+    def one_run():
+        done, nbytes = 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            b, h = order[done % len(order)]
+            oracle.decode_attention(q, lens, spec.mode, spec.D, spec.bs, spec.Hkv, *host_planes,
+                                    case.softmax_scale, signs=signs, block_tables=bt,
+                                    block_tables_headwise=bth, window=win, pairs=[(b, h)])
+            W = int(win[h]) if win is not None else 0
+            L = int(lens[b])
+            nbytes += (min(L, W) if W > 0 else L) * 2 * (P + 4 * M)
+            done += 1
+        return nbytes / (time.perf_counter() - t0) / 1e9, done
+
+    all_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    runs_all = [one_run() for _ in range(3)]
+    with threadpool_limits(limits=1):
+        runs_one = [one_run() for _ in range(3)]
+    med_all = statistics.median(v for v, _ in runs_all)
+    med_one = statistics.median(v for v, _ in runs_one)
+    # write: the oracle's encode of a token sample
+    nt = min(2048, int(case.k.shape[0]))
+    k = case.k[:nt].float().cpu().numpy()
+    v = case.v[:nt].float().cpu().numpy()
+    tw0 = time.perf_counter()
+    for src in (k, v):
+        oracle.encode_rows(src.reshape(-1, spec.D), spec.mode, signs)
+    tw = time.perf_counter() - tw0
+    pairs = [n for _, n in runs_all]
+    return {"value": round(med_all, 4), "unit": "GB/s", "cores": int(all_threads), "kind": "oracle",
+            "sample": f"(sequence, kv head) decode pairs of one layer's cache, {seconds:.0f} s per run "
+                      f"({min(pairs)}-{max(pairs)} pairs of {spec.B * spec.Hkv}), float64 attention over the "
+                      f"GPU's stored planes; median of 3 runs",
+            "one_core": {"value": round(med_one, 4), "unit": "GB/s", "cores": 1},
+            "write_tokens_per_s": round(nt / tw, 1)}
+
+
+def run_decode(args, spec, dev, ceilings, headline):
+    """A decode workload: the step is kvq_decode_step over every layer
+    (multi-layer workloads) or over one cache replica (one-layer ones)."""
+    t_setup = time.perf_counter()
+    layered = spec.layers > 1
+    case, d, bufs = build_buffers(spec, dev, spec.layers if layered else 1, layered)
+    n_bufs = len(bufs)
+    if not layered:
+        cache_bytes = sum(p.numel() * p.element_size() for p in bufs[0]["planes"])
+        R = args.replicas or max(1, min(16, math.ceil(max(1.2e9, 4 * MALL_BYTES) / cache_bytes)))
+        for _ in range(R - 1):
+            bufs.append(dict(planes=tuple(p.clone() for p in bufs[0]["planes"]), q=bufs[0]["q"], new=bufs[0]["new"]))
+        n_bufs = R
+    max_len = int(case.seq_lens.max().item())
+    ws = kvq.alloc_workspace(kvq.kvq_decode_workspace_size(d, spec.B, spec.Hq, max_len), dev)
+    out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
+    algo, kv_bytes, tokens = decode_algo_bytes(spec, case)
+    wb = write_bytes_per_token(spec)
+    step_write_bytes = spec.B * wb
+    setup_s = time.perf_counter() - t_setup
+
+    def fused(buf):
+        kvq.kvq_decode_step(d, buf["q"], buf["new"]["k"], buf["new"]["v"], *buf["planes"], case.seq_lens, max_len,
+                            slot_mapping=buf["new"]["sm"], slot_mapping_headwise=buf["new"]["smh"],
+                            block_tables=case.block_tables, block_tables_headwise=case.block_tables_headwise,
+                            window=case.window, softmax_scale=case.softmax_scale, out=out, workspace=ws)
+
+    def decode_only(buf):
+        kvq.kvq_paged_decode_attention(d, buf["q"], *buf["planes"], case.seq_lens, max_len,
+                                       block_tables=case.block_tables,
+                                       block_tables_headwise=case.block_tables_headwise,
+                                       window=case.window, softmax_scale=case.softmax_scale, out=out, workspace=ws)
+
+    if layered:
+        def step(i):
+            for b in bufs:
+                fused(b)
+        launches = n_bufs
+    else:
+        def step(i):
+            fused(bufs[i % n_bufs])
+        launches = 1
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    walls, lus = timed_regions(step, args.steps, launches, args.repeats)
+    mi = median_region(walls, lus)
+    ms_step, launch_us = walls[mi], lus[mi]
+    step_algo = algo * launches                     # decode bytes of the whole step
+    k_algo = algo + step_write_bytes                # one launch of the fused kernel
+    k_gbs = k_algo / (launch_us * 1e-6) / 1e9
+    copy_gbs, read_gbs = ceilings
+
+    skip = set(args.skip.split(",")) if args.skip else set()
+    # decode alone (no new-token write), same regions over the same buffers
+    if layered:
+        def dstep(i):
+            for b in bufs:
+                decode_only(b)
+    else:
+        def dstep(i):
+            decode_only(bufs[i % n_bufs])
+    d_us = float("nan")
+    if "decode_only" not in skip:
+        dw, dl = timed_regions(dstep, max(5, args.steps // 2), launches, 3)
+        d_us = dl[median_region(dw, dl)]
+
+    # quantize-write throughput: whole-cache fill of one layer into fresh planes
+    T = int(case.k.shape[0])
+    scratch = kvq.alloc_cache(d, dev)
+    fill = lambda i: kvq.kvq_reshape_and_cache(d, case.k, case.v, *scratch, slot_mapping=case.slot_mapping,
+                                               slot_mapping_headwise=case.slot_mapping_headwise)
+    fill_ms = float("nan")
+    if "fill" not in skip:
+        fill(0)
+        fill_ms = statistics.median(time_events(fill, 5))
+    del scratch
+
+    # dequantize-gather of one layer's whole cache (bf16 rows [T, Hkv, D])
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    cu_np = np.concatenate([[0], np.cumsum(lens)])
+    cu = torch.as_tensor(cu_np.astype(np.int32), device=dev)
+    g_tot = int(cu_np[-1])
+    g_out = [torch.empty((g_tot, spec.Hkv, spec.D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    gather = lambda i: kvq.kvq_gather_dequant(d, *bufs[i % n_bufs]["planes"], cu, max_len, g_tot,
+                                              block_tables=case.block_tables,
+                                              block_tables_headwise=case.block_tables_headwise,
+                                              key_out=g_out[0], value_out=g_out[1])
+    g_ms = float("nan")
+    if "gather" not in skip:
+        gather(0)
+        g_ms = statistics.median(time_events(gather, 5))
+    g_bytes = gather_bytes(spec, case)
+    del g_out
+
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(gbs(step_algo, ms_step), 2),
+        "unit": "GB/s",
+        "ms_per_step": round(ms_step, 5),
+        "dtype": MODE_DTYPES[spec.mode],
+        "config": {"workload": spec.name, "batch": spec.B, "q_heads": spec.Hq, "kv_heads": spec.Hkv,
+                   "head_dim": spec.D, "block_size": spec.bs, "mode": MODE_NAMES[spec.mode],
+                   "rotation": spec.rotate, "seq_len_max": max_len, "tokens_cached_per_layer": T,
+                   "kv_tokens_attended_per_layer": tokens,
+                   "layers": spec.layers if layered else 1,
+                   "cache_buffers": n_bufs,
+                   "buffers": "separate per layer, each written from its own K/V draws" if layered
+                   else "device copies of one cache, cycled (>= 1.2 GB in all)",
+                   "step": f"kvq_decode_step (new-token write + decode, one launch) x {launches}",
+                   "parallelism": "single GPU"},
+        "repeats": {"n": args.repeats, "ms_per_step": [round(w, 4) for w in walls],
+                    "launch_us": [round(x, 3) for x in lus]},
+        "hbm_frac_of_step": round(gbs(step_algo, ms_step) / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel (fused step: new-token write + decode)",
+                     "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(f"decode_{spec.name}_counters.json"),
+                     "algorithmic_bytes_per_launch": int(k_algo), "kv_bytes_per_launch": int(kv_bytes),
+                     "avg_launch_us": round(launch_us, 3), "launch_us_spread": spread(lus),
+                     "launches": args.steps * launches,
+                     "measured_copy_GBps": round(copy_gbs, 1), "measured_read_GBps": round(read_gbs, 1),
+                     "frac_of_measured_copy": round(k_gbs / copy_gbs, 4),
+                     "frac_of_measured_read": round(k_gbs / read_gbs, 4)},
+        "decode_only": {"avg_launch_us": round(d_us, 3), "achieved": round(gbs(algo, d_us * 1e-3), 2),
+                        "frac": round(gbs(algo, d_us * 1e-3) / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes_per_launch": int(algo)},
+        "write": {"kernel": "write_kernel (whole-cache fill of one layer)", "fill_tokens": T,
+                  "fill_us": round(fill_ms * 1e3, 2), "tokens_per_s": round(T / (fill_ms * 1e-3), 1),
+                  "bytes_per_token": wb, "GBps": round(gbs(T * wb, fill_ms), 2),
+                  "frac": round(gbs(T * wb, fill_ms) / HBM_PEAK_GBS, 4),
+                  "frac_of_measured_copy": round(gbs(T * wb, fill_ms) / copy_gbs, 4),
+                  "traffic": load_traffic(f"write_{spec.name}_counters.json", WRITE_SRC)},
+        "gather": {"kernel": "gather_kernel (dequantize-gather of one layer, bf16 out)", "rows": g_tot * spec.Hkv * 2,
+                   "avg_launch_us": round(g_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(g_bytes),
+                   "GBps": round(gbs(g_bytes, g_ms), 2), "frac": round(gbs(g_bytes, g_ms) / HBM_PEAK_GBS, 4),
+                   "frac_of_measured_copy": round(gbs(g_bytes, g_ms) / copy_gbs, 4),
+                   "traffic": load_traffic(f"gather_{spec.name}_counters.json", GATHER_SRC)},
+        "setup_s": round(setup_s, 1),
+    }
+    if headline and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(spec, case, bufs[0]["planes"], args.cpu_seconds)
+        if layered:
+            res["cpu_baseline"]["sample"] += f" (one layer of {spec.layers}; the rate is per byte, so it holds for all)"
+    del bufs, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def oracle_prefill_sample(spec, case, planes, seconds):
@@ -353,25 +610,24 @@ def oracle_prefill_sample(spec, case, planes, seconds):
                       f"prefill in {dt:.1f} s (float64 attention over the GPU's stored planes)"}
 
 
-def run_mixed(args, spec, dev):
+def run_mixed(args, spec, dev, ceilings, headline):
     """The mixed step: quantize-write of every sequence's new tokens (the
     chunk of each prefill sequence, one token of each decode sequence),
     chunked-prefill attention of the prefill sequences, decode attention of
-    the others.  Prefill is MFMA work, so its roofline is TFLOP/s against the
-    dense bf16 peak; decode is reported as effective KV GB/s."""
+    the others, three launches.  Prefill is MFMA work, so its roofline is
+    TFLOP/s against the dense bf16 peak; decode is effective KV GB/s."""
     t_setup = time.perf_counter()
-    case, d, planes, new = build_workload(spec, dev)
+    case, d, bufs = build_buffers(spec, dev, 1, False)
+    planes, new = bufs[0]["planes"], bufs[0]["new"]
     npf = spec.n_prefill
     Hkv = spec.Hkv
     max_len = int(case.seq_lens.max().item())
-    # decode part: sequences npf..B-1
     dq = case.q[npf:].contiguous()
     dsl = case.seq_lens[npf:].contiguous()
     dbt = None if case.block_tables is None else case.block_tables[npf:].contiguous()
     dbth = None if case.block_tables_headwise is None else case.block_tables_headwise[npf * Hkv:].contiguous()
     ws = kvq.alloc_workspace(kvq.kvq_decode_workspace_size(d, spec.B - npf, spec.Hq, max_len), dev)
     dout = torch.empty((spec.B - npf, spec.Hq, spec.D), dtype=torch.float32, device=dev)
-    # prefill part: sequences 0..npf-1
     psl = case.seq_lens[:npf].contiguous()
     pbt = None if case.block_tables is None else case.block_tables[:npf].contiguous()
     pbth = None if case.block_tables_headwise is None else case.block_tables_headwise[:npf * Hkv].contiguous()
@@ -395,41 +651,29 @@ def run_mixed(args, spec, dev):
                                        block_tables_headwise=dbth, window=case.window,
                                        softmax_scale=case.softmax_scale, out=dout, workspace=ws)
 
+    def step(i):
+        write(i)
+        prefill(i)
+        decode(i)
+
     for i in range(args.warmup):
-        write(i)
-        prefill(i)
-        decode(i)
+        step(i)
     torch.cuda.synchronize()
-    # timed region: exactly `steps` steps, the three kernels back to back
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        write(i)
-        prefill(i)
-        decode(i)
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    # the kernels inside a step, bracketed by events
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record()
-        write(i)
-        ev[i][1].record()
-        prefill(i)
-        ev[i][2].record()
-        decode(i)
-        ev[i][3].record()
-    torch.cuda.synchronize()
-    w_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    p_step_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    d_step_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    # each kernel alone: back-to-back launches between two HIP events
-    p_ms = time_span(prefill, args.steps)
-    d_ms = time_span(decode, args.steps)
+    n = max(5, args.steps // 2)
+    walls, _ = timed_regions(step, n, 3, args.repeats)
+    ms_step = statistics.median(walls)
+    # each kernel alone: median of regions of back-to-back launches
+    pw, pl = timed_regions(prefill, n, 1, args.repeats)
+    p_us = pl[median_region(pw, pl)]
+    dw, dl = timed_regions(decode, n, 1, args.repeats)
+    d_us = dl[median_region(dw, dl)]
+    ww, wl = timed_regions(write, n, 1, args.repeats)
+    w_us = wl[median_region(ww, wl)]
     T = int(new["k"].shape[0])
     wb = write_bytes_per_token(spec)
-    p_tf = flops / (p_ms * 1e-3) / 1e12
-    d_gbs = d_algo / (d_ms * 1e-3) / 1e9
+    p_tf = flops / (p_us * 1e-6) / 1e12
+    d_gbs = d_algo / (d_us * 1e-6) / 1e9
+
     # the prefill fallback: dequantize-gather of the prefill sequences' whole
     # contexts (positions 0 .. L - 1, head-wise table, bf16 rows [T, Hkv, D])
     lens = psl.cpu().numpy().astype(np.int64)
@@ -437,57 +681,48 @@ def run_mixed(args, spec, dev):
     cu = torch.as_tensor(cu_np.astype(np.int32), device=dev)
     g_tot = int(cu_np[-1])
     g_out = [torch.empty((g_tot, spec.Hkv, spec.D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
-
-    def gather(i):
-        kvq.kvq_gather_dequant(d, *planes, cu, max_len, g_tot, block_tables=pbt, block_tables_headwise=pbth,
-                               key_out=g_out[0], value_out=g_out[1])
-
+    gather = lambda i: kvq.kvq_gather_dequant(d, *planes, cu, max_len, g_tot, block_tables=pbt,
+                                              block_tables_headwise=pbth, key_out=g_out[0], value_out=g_out[1])
     gather(0)
-    g_avg = float(np.mean(time_events(gather, 5)))
+    g_ms = statistics.median(time_events(gather, 5))
     g_bytes = gather_bytes(spec, case, npf)
     del g_out
 
-    result = {
-        "metric": "decode-attn effective KV GB/s (% HBM peak); quantize-write tokens/s",
+    res = {
+        "metric": METRIC,
         "value": round(d_gbs, 2),
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "int4 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
-        "data": "synthetic (seeded)",
         "config": {"workload": spec.name, "batch": spec.B, "prefill_seqs": npf, "prefill_new_tokens": max_q,
                    "decode_seqs": spec.B - npf, "q_heads": spec.Hq, "kv_heads": spec.Hkv, "head_dim": spec.D,
-                   "block_size": spec.bs, "mode": ["int8_sym", "int4_asym", "int2_asym"][spec.mode],
-                   "rotation": spec.rotate, "window": list(spec.window or []), "headwise_table": spec.headwise,
-                   "seq_len": max_len, "parallelism": "single GPU"},
+                   "block_size": spec.bs, "mode": MODE_NAMES[spec.mode], "rotation": spec.rotate,
+                   "window": list(spec.window or []), "headwise_table": spec.headwise, "seq_len": max_len,
+                   "step": "write + prefill + decode, three launches", "parallelism": "single GPU"},
+        "repeats": {"n": args.repeats, "ms_per_step": [round(w, 4) for w in walls]},
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(p_tf, 2),
-                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(p_tf / 2500.0, 4),
+                     "peak": BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(p_tf / BF16_PEAK_TFS, 4),
                      "traffic": load_traffic(f"prefill_{spec.name}_counters.json", PREFILL_SRC),
                      "useful_pairs": pairs, "flops_per_launch": flops, "kv_bytes_per_launch": p_kv,
-                     "avg_launch_us": round(p_ms * 1e3, 2), "launches": args.steps,
-                     "in_step_launch_us": round(p_step_ms * 1e3, 2)},
+                     "avg_launch_us": round(p_us, 2), "launch_us_spread": spread(pl), "launches": n * args.repeats},
         "decode": {"kernel": "decode_kernel", "achieved_GBps": round(d_gbs, 2),
                    "frac": round(d_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": int(d_algo),
-                   "kv_tokens_attended": d_tokens, "avg_launch_us": round(d_ms * 1e3, 2),
-                   "in_step_launch_us": round(d_step_ms * 1e3, 2)},
-        "write": {"step_tokens": T, "step_write_us": round(w_ms * 1e3, 2),
-                  "tokens_per_s": round(T / (w_ms * 1e-3), 1), "bytes_per_token": wb,
-                  "GBps": round(T * wb / (w_ms * 1e-3) / 1e9, 2)},
+                   "kv_tokens_attended": d_tokens, "avg_launch_us": round(d_us, 2),
+                   "traffic": load_traffic(f"decode_{spec.name}_counters.json")},
+        "write": {"step_tokens": T, "step_write_us": round(w_us, 2), "tokens_per_s": round(T / (w_us * 1e-6), 1),
+                  "bytes_per_token": wb, "GBps": round(T * wb / (w_us * 1e-6) / 1e9, 2)},
         "gather": {"kernel": "gather_kernel (dequantize-gather of the prefill contexts, bf16 out)",
-                   "rows": int(g_tot) * spec.Hkv * 2, "avg_launch_us": round(g_avg * 1e3, 2),
+                   "rows": g_tot * spec.Hkv * 2, "avg_launch_us": round(g_ms * 1e3, 2),
                    "algorithmic_bytes_per_launch": int(g_bytes),
-                   "GBps": round(g_bytes / (g_avg * 1e-3) / 1e9, 2),
-                   "frac": round(g_bytes / (g_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                   "GBps": round(g_bytes / (g_ms * 1e-3) / 1e9, 2),
+                   "frac": round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "setup_s": round(setup_s, 1),
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = oracle_prefill_sample(spec, case, planes, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    if headline and not args.no_cpu_baseline:
+        res["cpu_baseline"] = oracle_prefill_sample(spec, case, planes, args.cpu_seconds)
+    del bufs, planes, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -495,19 +730,23 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--replicas", type=int, default=0, help="cache replicas cycled (0 = enough for 1.2 GB)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--repeats", type=int, default=5, help="timed regions of `steps` steps (median reported)")
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--subs", default=None,
+                    help="comma-separated workloads reported as sub-objects, a config or config:variant "
+                         "(variants: fp8, chan); default 2,3,5,2:fp8,2:chan with --config 4; 'none' for none")
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas of a one-layer workload (0 = >= 1.2 GB)")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0, help="seconds of each of the oracle's six runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="replay the step from a HIP graph instead of launching it")
-    ap.add_argument("--unfused", action="store_true", help="run the step as write then decode (two launches)")
+    ap.add_argument("--skip", default="", help="comma-separated parts not to run: decode_only, fill, gather "
+                    "(for profiling one kernel)")
     ap.add_argument("--mode", choices=["step", "copy"], default="step",
                     help="copy: time a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build measures the kernel "
-              "on one GPU's share; see DESIGN.md for how the path shards.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): it measures each kernel on one GPU's "
+              "share; DESIGN.md describes how the path would shard.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -523,185 +762,36 @@ def main():
         print(json.dumps({"mode": "copy", "bytes": n, "ms": ms, "GBps": [2 * n / (m * 1e6) for m in ms]}))
         return
 
-    spec = synth.CONFIGS[args.config]
-    if spec.n_prefill:
-        return run_mixed(args, spec, dev)
-    t_setup = time.perf_counter()
-    case, d, planes, new = build_workload(spec, dev)
-    cache_bytes = sum(p.numel() * p.element_size() for p in planes)
-    R = args.replicas or max(1, min(16, math.ceil(max(1.2e9, 4 * MALL_BYTES) / cache_bytes)))
-    replicas = [planes] + [tuple(p.clone() for p in planes) for _ in range(R - 1)]
-    max_len = int(case.seq_lens.max().item())
-    ws = kvq.alloc_workspace(kvq.kvq_decode_workspace_size(d, spec.B, spec.Hq, max_len), dev)
-    out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
-    algo, kv_bytes, tokens = decode_algo_bytes(spec, case)
-    setup_s = time.perf_counter() - t_setup
+    if args.subs is None:
+        subs = ["2", "3", "5", "2:fp8", "2:chan"] if args.config == 4 else []
+    elif args.subs in ("", "none"):
+        subs = []
+    else:
+        subs = args.subs.split(",")
+    ceilings = measured_ceilings(dev)
 
-    def write(i):
-        rp = replicas[i % R]
-        kvq.kvq_reshape_and_cache(d, new["k"], new["v"], *rp, slot_mapping=new["sm"],
-                                  slot_mapping_headwise=new["smh"])
+    def run(key, headline):
+        spec = spec_of(key)
+        return (run_mixed if spec.n_prefill else run_decode)(args, spec, dev, ceilings, headline)
 
-    def decode(i):
-        rp = replicas[i % R]
-        kvq.kvq_paged_decode_attention(d, case.q, *rp, case.seq_lens, max_len,
-                                       block_tables=case.block_tables,
-                                       block_tables_headwise=case.block_tables_headwise,
-                                       window=case.window, softmax_scale=case.softmax_scale,
-                                       out=out, workspace=ws)
-
-    def fused(i):
-        rp = replicas[i % R]
-        kvq.kvq_decode_step(d, case.q, new["k"], new["v"], *rp, case.seq_lens, max_len,
-                            slot_mapping=new["sm"], slot_mapping_headwise=new["smh"],
-                            block_tables=case.block_tables, block_tables_headwise=case.block_tables_headwise,
-                            window=case.window, softmax_scale=case.softmax_scale, out=out, workspace=ws)
-
-    def two_calls(i):
-        write(i)
-        decode(i)
-
-    one = two_calls if args.unfused else fused
-    for i in range(args.warmup):
-        one(i)
-    torch.cuda.synchronize()
-
-    # --graph: one HIP graph per cache replica holding the step, replayed
-    # (measured slower than eager launches for the two-kernel step)
-    graphs = None
-    if args.graph:
-        graphs = []
-        for k in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                one(k)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % R].replay()
-        torch.cuda.synchronize()
-
-    def step(i):
-        if graphs is not None:
-            graphs[i % R].replay()
-        else:
-            one(i)
-
-    # timed region: exactly `steps` steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    # the step's kernel alone (the fused write + decode; with --unfused the
-    # decode): `steps` back-to-back launches over the replicas between two
-    # HIP events on the stream it runs on (the host stays ahead of the GPU,
-    # so the span is the kernels and the gaps between them)
-    step_kernel = decode if args.unfused else fused
-    dec_avg = time_span(step_kernel, args.steps)
-    # for reference: decode alone and the step's write alone, same way
-    dec_only_avg = time_span(decode, args.steps)
-    step_write_avg = time_span(write, args.steps)
-    wb = write_bytes_per_token(spec)
-    step_write_bytes = spec.B * wb
-    k_algo = algo if args.unfused else algo + step_write_bytes
-
-    # measured device-copy bandwidth (1 GiB read + 1 GiB written), the
-    # practical ceiling the fractions are also quoted against
-    copy_gbs = measured_copy_gbs(dev)
-
-    # quantize-write throughput: whole-cache fill into a scratch replica
-    T = case.k.shape[0]
-    scratch = replicas[-1]
-
-    def fill(i):
-        kvq.kvq_reshape_and_cache(d, case.k, case.v, *scratch, slot_mapping=case.slot_mapping,
-                                  slot_mapping_headwise=case.slot_mapping_headwise)
-
-    fill(0)
-    fill_ms = time_events(fill, 5)
-    fill_avg = float(np.mean(fill_ms))
-
-    # dequantize-gather of the whole cache (every sequence, positions 0 ..
-    # L - 1, bf16 rows [T, Hkv, D] for K and for V), cycling the replicas
-    lens = case.seq_lens.cpu().numpy().astype(np.int64)
-    cu_np = np.concatenate([[0], np.cumsum(lens)])
-    cu = torch.as_tensor(cu_np.astype(np.int32), device=dev)
-    g_tot = int(cu_np[-1])
-    g_out = [torch.empty((g_tot, spec.Hkv, spec.D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
-
-    def gather(i):
-        kvq.kvq_gather_dequant(d, *replicas[i % R], cu, max_len, g_tot, block_tables=case.block_tables,
-                               block_tables_headwise=case.block_tables_headwise,
-                               key_out=g_out[0], value_out=g_out[1])
-
-    gather(0)
-    g_ms = time_events(gather, 5)
-    g_avg = float(np.mean(g_ms))
-    g_bytes = gather_bytes(spec, case)
-    g_cpu = None if args.no_cpu_baseline else gather_cpu(spec, case, planes, lens, 3.0)
-    del g_out
-
-    result = {
-        "metric": "decode-attn effective KV GB/s (% HBM peak); quantize-write tokens/s",
-        "value": round(algo / (ms_step * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {0: "int8 codes, bf16 mfma, fp32 accumulate", 1: "int4 codes, bf16 mfma, fp32 accumulate",
-                  2: "int2 codes, bf16 mfma, fp32 accumulate"}[spec.mode],
-        "data": "synthetic (seeded)",
-        "config": {"workload": spec.name, "batch": spec.B, "q_heads": spec.Hq, "kv_heads": spec.Hkv,
-                   "head_dim": spec.D, "block_size": spec.bs, "mode": ["int8_sym", "int4_asym", "int2_asym"][spec.mode],
-                   "rotation": spec.rotate, "tokens_cached": int(T), "kv_tokens_attended": tokens,
-                   "cache_replicas": R, "parallelism": "single GPU",
-                   "step": "write + decode, two launches" if args.unfused else "fused write + decode, one launch",
-                   "step_launch": "eager" if graphs is None else "hip graph per replica"},
-        "hbm_frac_of_step": round(algo / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel" + ("" if args.unfused else " (fused step: new-token write + decode)"),
-                     "achieved": round(k_algo / (dec_avg * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k_algo / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(f"decode_{spec.name}_counters.json"),
-                     "algorithmic_bytes_per_launch": int(k_algo), "kv_bytes_per_launch": int(kv_bytes),
-                     "avg_launch_us": round(dec_avg * 1e3, 3), "launches": args.steps,
-                     "measured_copy_GBps": round(copy_gbs, 1),
-                     "frac_of_measured_copy": round(k_algo / (dec_avg * 1e-3) / 1e9 / copy_gbs, 4)},
-        "decode_only": {"avg_launch_us": round(dec_only_avg * 1e3, 3),
-                        "achieved": round(algo / (dec_only_avg * 1e-3) / 1e9, 2),
-                        "algorithmic_bytes_per_launch": int(algo)},
-        "write": {"step_write_us": round(step_write_avg * 1e3, 3), "step_tokens": spec.B,
-                  "fill_tokens": int(T), "fill_us": round(fill_avg * 1e3, 2),
-                  "tokens_per_s": round(T / (fill_avg * 1e-3), 1),
-                  "bytes_per_token": wb, "GBps": round(T * wb / (fill_avg * 1e-3) / 1e9, 2),
-                  "frac": round(T * wb / (fill_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                  "frac_of_measured_copy": round(T * wb / (fill_avg * 1e-3) / 1e9 / copy_gbs, 4),
-                  "traffic": load_traffic(f"write_{spec.name}_counters.json", WRITE_SRC)},
-        "gather": {"kernel": "gather_kernel (dequantize-gather, bf16 out)", "rows": int(g_tot) * spec.Hkv * 2,
-                   "avg_launch_us": round(g_avg * 1e3, 2), "algorithmic_bytes_per_launch": int(g_bytes),
-                   "GBps": round(g_bytes / (g_avg * 1e-3) / 1e9, 2),
-                   "frac": round(g_bytes / (g_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                   "frac_of_measured_copy": round(g_bytes / (g_avg * 1e-3) / 1e9 / copy_gbs, 4),
-                   "traffic": load_traffic(f"gather_{spec.name}_counters.json", GATHER_SRC),
-                   "cpu_oracle": g_cpu},
-        "setup_s": round(setup_s, 1),
-    }
-    if spec.layers > 1:
-        # the workload is `layers` layers' caches run back to back; one layer's
-        # buffers (cycled over the replicas) are timed, the step scales by layers
-        result["config"]["layers"] = spec.layers
-        result["config"]["timed"] = "one layer's cache per step"
-        result["ms_per_step_all_layers"] = round(ms_step * spec.layers, 4)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(spec, case, planes, args.cpu_seconds)
-        if spec.layers > 1:
-            result["cpu_baseline"]["sample"] += f"; one layer (x{spec.layers} for all layers)"
-    print(json.dumps(result), flush=True)
+    result = run(args.config, True)
+    head = {"metric": result.pop("metric"), "value": result.pop("value"), "unit": result.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": result.pop("ms_per_step"),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": result.pop("dtype"),
+            "data": "synthetic (seeded)", "config": result.pop("config")}
+    line = dict(head)
+    line["roofline"] = result.pop("roofline")
+    if "cpu_baseline" in result:
+        line["cpu_baseline"] = result.pop("cpu_baseline")
+    line.update(result)
+    if subs:
+        line["configs"] = {}
+        for c in subs:
+            sub = run(c, False)
+            line["configs"][sub["config"]["workload"]] = sub
+            print(f"[bench] {sub['config']['workload']}: {sub['value']} GB/s, roofline "
+                  f"{sub['roofline']['frac']}", file=sys.stderr, flush=True)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -3,7 +3,8 @@
     python -m sub_byte_quantized_amd.build [--jobs N]
 
 Each source is compiled to an object in parallel, then linked into
-sub_byte_quantized_amd/libkvq.so.  Always rebuilds.
+sub_byte_quantized_amd/libkvq.so.  The benchmark's read-ceiling kernel is
+linked on its own into libkvq_bench.so.  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -20,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 SOURCES = ["kvq_host.cpp", "kvq_write.hip", "kvq_decode.hip", "kvq_prefill.hip", "kvq_gather.hip"]
+BENCH_LIB = os.path.join(PKG, "libkvq_bench.so")
+BENCH_SOURCES = ["bench_stream_read.hip"]
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 
@@ -49,18 +52,23 @@ def compile_one(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+def link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 4, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + BENCH_SOURCES))
+    link(objs[:len(SOURCES)], LIB)
+    link(objs[len(SOURCES):], BENCH_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {BENCH_LIB}")
     return LIB
 
 
