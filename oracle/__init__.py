@@ -5,5 +5,5 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 share no code.
 """
 from .kvq_oracle import *  # noqa: F401,F403
-from .kvq_oracle import (INT8_SYM, INT4_ASYM, INT2_ASYM, INT8_CHANNEL, FP8_E4M3, MODES, BITS, LEVELS,  # noqa: F401
-                         META_FLOATS)
+from .kvq_oracle import (INT8_SYM, INT4_ASYM, INT2_ASYM, INT8_CHANNEL, FP8_E4M3, INT4_INLINE, MODES, BITS,  # noqa: F401
+                         LEVELS, META_FLOATS)

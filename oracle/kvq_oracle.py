@@ -70,6 +70,20 @@ Readings where the pages are silent (each also listed in the design doc):
   first sink_size positions of the sequence (when present in the table), as
   in sliding-window attention with sink tokens; heads without a window see
   everything anyway.
+* INT4 inline layout ([P2] 关键源码片段: the cache shape (num_blocks, 2,
+  block_size, num_kv_heads, head_size // 2 + scale_pad) with the float32
+  scale in the last 4 bytes of each row; 评论区精华: the 4-bit zero point is
+  kept in the scale's low 4 bits).  One uint8 tensor [nb, 2, bs, Hkv, D/2 +
+  4], index 1 = 0 for K and 1 for V; row = D/2 nibble bytes (INT4 order)
+  then the 4 little-endian bytes of the stored scale st.  The zero point is
+  an integer zp in [0, 15] (the textbook asymmetric scheme, zero exactly
+  representable): mn = min(min y, 0), mx = max(max y, 0) in float32, s =
+  (mx - mn) / 15, zp = clamp(rint(-mn / s), 0, 15), st = the float32 whose
+  bits are those of s with the low 4 replaced by zp (|st - s| <= 15 ulp(s),
+  so st is the scale a reader that ignores the zero point still gets), then
+  c = clamp(rint(y * fl(1/st)) + zp, 0, 15) and x_hat = (c - zp) * st.  A
+  row whose s is zero, subnormal or NaN stores st = 0 and codes 0.  The
+  same optional rotation as INT4.
 """
 from __future__ import annotations
 
@@ -82,11 +96,14 @@ INT4_ASYM = 1
 INT2_ASYM = 2
 INT8_CHANNEL = 3
 FP8_E4M3 = 4
+INT4_INLINE = 5
 MODES = (INT8_SYM, INT4_ASYM, INT2_ASYM)          # the integer per-token-head modes
-BITS = {INT8_SYM: 8, INT4_ASYM: 4, INT2_ASYM: 2, INT8_CHANNEL: 8, FP8_E4M3: 8}
+BITS = {INT8_SYM: 8, INT4_ASYM: 4, INT2_ASYM: 2, INT8_CHANNEL: 8, FP8_E4M3: 8, INT4_INLINE: 4}
 # number of quantization steps: codes span [0, L] (asymmetric) or [-L, L]
 LEVELS = {INT8_SYM: 127, INT4_ASYM: 15, INT2_ASYM: 3, INT8_CHANNEL: 127}
-META_FLOATS = {INT8_SYM: 1, INT4_ASYM: 2, INT2_ASYM: 2, INT8_CHANNEL: 0, FP8_E4M3: 1}
+# meta floats in a separate plane (the inline layout keeps its scale in the row)
+META_FLOATS = {INT8_SYM: 1, INT4_ASYM: 2, INT2_ASYM: 2, INT8_CHANNEL: 0, FP8_E4M3: 1, INT4_INLINE: 0}
+INLINE_LEVELS = 15
 E4M3_MAX = 448.0
 
 _F32 = np.float32
@@ -109,10 +126,19 @@ def plane_shapes(mode: int, head_dim: int, num_kv_heads: int, block_size: int,
     codes: uint8 [num_blocks, Hkv, block_size, P]
     meta : float32 [num_blocks, Hkv, block_size, M], M = 1 (s) or 2 (s, z)
     """
+    if mode == INT4_INLINE:
+        raise ValueError("the inline layout is one tensor: inline_cache_shape")
     P = row_code_bytes(mode, head_dim)
     M = META_FLOATS[mode]
     return ((num_blocks, num_kv_heads, block_size, P),
             (num_blocks, num_kv_heads, block_size, M))
+
+
+def inline_cache_shape(head_dim: int, num_kv_heads: int, block_size: int, num_blocks: int):
+    """The INT4 inline cache: uint8 [num_blocks, 2 (K, V), block_size, Hkv,
+    D/2 + 4] ([P2] 关键源码片段: head_size // 2 + scale_pad, scale_pad = 4
+    bytes of float32 scale)."""
+    return (num_blocks, 2, block_size, num_kv_heads, head_dim // 2 + 4)
 
 
 # --------------------------------------------------------------------------
@@ -342,6 +368,61 @@ def quantize_rows_channel(y: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# INT4 with the zero point in the scale's low bits ([P2] 关键源码片段 and
+# 评论区精华: 4-bit zero point hidden in the low 4 bits of the float32 scale)
+# --------------------------------------------------------------------------
+def embed_zero(s: np.ndarray, zp: np.ndarray) -> np.ndarray:
+    """float32 whose bits are those of s with the low 4 replaced by zp."""
+    bits = np.asarray(s, _F32).view(np.uint32)
+    return ((bits & np.uint32(0xFFFFFFF0)) | np.asarray(zp, np.uint32)).astype(np.uint32).view(_F32)
+
+
+def hidden_zero(st: np.ndarray) -> np.ndarray:
+    """The zero point kept in a stored scale: its low 4 bits."""
+    return (np.asarray(st, _F32).view(np.uint32) & np.uint32(0xF)).astype(np.int32)
+
+
+def quantize_rows_inline(y: np.ndarray):
+    """float32 rows y [R, D] -> (codes int32 [R, D] in [0, 15], st f32 [R]).
+
+    mn = min(min y, 0), mx = max(max y, 0); s = (mx - mn) / 15; zp =
+    clamp(rint(-mn / s), 0, 15); st = s with zp in its low 4 bits; c =
+    clamp(rint(y * fl(1/st)) + zp, 0, 15).  Rows with a zero, subnormal or
+    NaN s store st = 0 and codes 0."""
+    y = np.asarray(y, dtype=_F32)
+    mn = np.minimum(np.min(y, axis=-1), _F32(0.0)).astype(_F32)
+    mx = np.maximum(np.max(y, axis=-1), _F32(0.0)).astype(_F32)
+    s = ((mx - mn) / _F32(INLINE_LEVELS)).astype(_F32)
+    ok = s >= _FLT_MIN
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        s1 = np.where(ok, s, _F32(1.0)).astype(_F32)
+        zp = np.clip(np.rint((-mn / s1).astype(_F32)), 0, INLINE_LEVELS).astype(np.int64)
+        zp = np.where(ok, zp, 0)
+        st = np.where(ok, embed_zero(s1, zp), _F32(0.0)).astype(_F32)
+        inv = (_F32(1.0) / np.where(ok, st, _F32(1.0))).astype(_F32)
+        t = (y * inv[..., None]).astype(_F32)
+    c = np.clip(np.rint(t) + zp[..., None], 0, INLINE_LEVELS)
+    c = np.where(ok[..., None], c, 0).astype(np.int32)
+    return c, st
+
+
+def inline_rows(packed: np.ndarray, st: np.ndarray) -> np.ndarray:
+    """Stored rows: the packed nibbles [R, D/2] then st's 4 little-endian bytes."""
+    tail = np.asarray(st, '<f4').reshape(-1, 1).view(np.uint8)
+    return np.concatenate([np.asarray(packed, np.uint8).reshape(len(tail), -1), tail], axis=1)
+
+
+def dequant_inline_rows_f64(rows: np.ndarray, head_dim: int) -> np.ndarray:
+    """x_hat = (c - zp) * st in float64 from stored inline rows [R, D/2 + 4]."""
+    rows = np.asarray(rows, np.uint8)
+    P = head_dim // 2
+    codes = unpack_codes(rows[:, :P], INT4_ASYM, head_dim).astype(np.float64)
+    st = np.ascontiguousarray(rows[:, P:P + 4]).view('<f4')[:, 0].astype(_F32)
+    zp = hidden_zero(st).astype(np.float64)
+    return (codes - zp[:, None]) * st.astype(np.float64)[:, None]
+
+
+# --------------------------------------------------------------------------
 # Quantize-on-write into the paged layout  ([P2] 实现拆解 item 2: RHT, then
 # scale and zero per token and head, then pack and store; [P3] Motivation:
 # per-head block rows)
@@ -356,6 +437,9 @@ def encode_rows(x_bf16_as_f32: np.ndarray, mode: int, signs=None):
     if mode == FP8_E4M3:
         codes, s = quantize_rows_fp8(y)
         return codes, s, np.zeros_like(s), codes
+    if mode == INT4_INLINE:
+        codes, st = quantize_rows_inline(y)
+        return pack_codes(codes, INT4_ASYM), st, np.zeros_like(st), codes
     codes, s, z = quantize_rows(y, mode)
     return pack_codes(codes, mode), s, z, codes
 
@@ -370,7 +454,8 @@ def write_cache(k: np.ndarray, v: np.ndarray, mode: int, block_size: int,
     slot_mapping [T] (the same slot for every kv head) or slot_mapping_headwise
     [T, Hkv]; slot = block * block_size + offset; a negative slot skips the row.
     Planes are modified in place.  INT8_CHANNEL takes channel_scales [2, Hkv, D]
-    (K then V) and writes no metadata.
+    (K then V) and writes no metadata.  INT4_INLINE takes its one cache tensor
+    (inline_cache_shape) as k_codes; the other three are None.
     """
     T, Hkv, D = k.shape
     if (slot_mapping is None) == (slot_mapping_headwise is None):
@@ -389,6 +474,10 @@ def write_cache(k: np.ndarray, v: np.ndarray, mode: int, block_size: int,
             codes_pl[blk, hh, off, :] = packed[tt, hh]
             continue
         packed, s, z, _ = encode_rows(np.asarray(src, _F32).reshape(T * Hkv, D), mode, signs)
+        if mode == INT4_INLINE:
+            rows = inline_rows(packed, s).reshape(T, Hkv, -1)
+            k_codes[blk, kv, off, hh, :] = rows[tt, hh]
+            continue
         packed = packed.reshape(T, Hkv, -1)
         s = s.reshape(T, Hkv)
         z = z.reshape(T, Hkv)
@@ -428,6 +517,10 @@ def gather_head(b: int, h: int, n_pos: int, mode: int, head_dim: int,
         bi = ids[present]
         off = pos[present] % block_size
         for kv, (pl_c, pl_m, out) in enumerate(((k_codes, k_meta, K), (v_codes, v_meta, V))):
+            if mode == INT4_INLINE:   # one tensor, passed as k_codes
+                xhat = dequant_inline_rows_f64(k_codes[bi, kv, off, h, :], head_dim)
+                out[present] = unrotate_f64(xhat, signs) if signs is not None else xhat
+                continue
             if mode == FP8_E4M3:
                 xhat = e4m3_decode(pl_c[bi, h, off, :]) * np.asarray(pl_m[bi, h, off, 0], np.float64)[:, None]
                 out[present] = unrotate_f64(xhat, signs) if signs is not None else xhat

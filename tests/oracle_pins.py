@@ -867,4 +867,170 @@ def check_channel_write_gather_and_attention(o):
         assert np.allclose(out[0, hq], ref, atol=1e-12), hq
 
 
+# ------------------------------------- INT4 with the zero in the scale -----
+def _f32_bits(x):
+    """Bits of a float32-representable rational."""
+    return int(np.array([float(x)], F32).view(np.uint32)[0])
+
+
+def _inline_model(row):
+    """Codes and stored-scale bits of one float32 row by the exact model of
+    the inline INT4 steps: zero-including range, s = (mx - mn) / 15 (two
+    float32 roundings), zp = rint(-mn / s) clamped to [0, 15], st = s with zp
+    in its low 4 bits, c = clamp(rint(fl(y fl(1/st))) + zp, 0, 15)."""
+    y = [_Fr(float(v)) for v in row]
+    mn, mx = min(min(y), _Fr(0)), max(max(y), _Fr(0))
+    s = _f32r(_f32r(mx - mn) / 15)
+    if s < _Fr(2) ** -126:
+        return [0] * len(y), 0
+    zp = min(max(_rne_int(_f32r(-mn / s)), 0), 15)
+    bits = (_f32_bits(s) & ~0xF) | zp
+    st = _Fr(float(np.array([bits], np.uint32).view(F32)[0]))
+    inv = _f32r(1 / st)
+    return [min(max(_rne_int(_f32r(v * inv)) + zp, 0), 15) for v in y], bits
+
+
+def _inline_rows_for_pins():
+    """Float32 rows: grids (c - zp) 2^-e, exact ties with zp = 0 and with odd
+    zp, values half a step from the grid with zp = 15, one-signed rows, and
+    random rows."""
+    rows = []
+    r = np.random.default_rng(51)
+    for zp, e in ((0, 4), (3, 0), (5, 7), (15, 2)):
+        c = r.permutation(np.tile(np.arange(16), 2))
+        c[:2] = (0, 15)
+        rows.append(((c - zp) * 2.0 ** -e).astype(F32))
+    # zp = 0, s = 2^-4 exactly: ties at t = k + 1/2 go to the even code
+    tie = np.zeros(32, F32)
+    tie[:2] = (0.0, 15 / 16)
+    tie[2:12] = (np.arange(10) + 0.5) / 16
+    rows.append(tie)
+    # zp = 1 (st = 2^-4 (1 + 2^-23)): y near 2.5 st whose product with
+    # fl(1/st) rounds to exactly 2.5 (an odd zero point then decides the
+    # order of the rounding and the zero's addition)
+    st1 = np.array([0x3D800001], np.uint32).view(F32)[0]
+    inv1 = F32(1.0) / st1
+    cand = [F32(2.5 / 16) + F32(k) * F32(2.0 ** -26) for k in range(-8, 9)]
+    hit = [v for v in cand if F32(v * inv1) == F32(2.5)]
+    assert hit, "no exact tie found"
+    odd = np.zeros(32, F32)
+    odd[:3] = (-1 / 16, 14 / 16, hit[0])
+    rows.append(odd)
+    # zp = 15 (largest perturbation of the scale): y = fl((k + 1/2) st)
+    st15 = np.array([0x3D80000F], np.uint32).view(F32)[0]
+    half = np.zeros(32, F32)
+    half[:2] = (-15 / 16, 0.0)
+    half[2:16] = (-(np.arange(14) + 0.5) * np.float64(st15)).astype(F32)
+    rows.append(half)
+    rows.append(np.abs(_bf16_rows((32,), 52)) + F32(1.0))     # all positive: zp = 0
+    rows.append(-np.abs(_bf16_rows((32,), 53)) - F32(1.0))    # all negative: zp = 15
+    rows.extend(_bf16_rows((40, 32), 54, scale=2.0, offset=0.3))
+    return np.stack(rows).astype(F32)
+
+
+def check_inline_exact_model(o):
+    """Inline INT4 codes and stored scales equal the exact rational model of
+    the steps on grid rows, exact ties (zp = 0 and odd zp), half-step values
+    under the largest scale perturbation, one-signed and random rows."""
+    y = _inline_rows_for_pins()
+    codes, st = o.quantize_rows_inline(y)
+    bits = st.view(np.uint32)
+    for i, row in enumerate(y):
+        mc, mb = _inline_model(row)
+        assert list(codes[i]) == mc, (i, list(codes[i]), mc)
+        assert int(bits[i]) == mb, (i, hex(int(bits[i])), hex(mb))
+    # the grid rows: zp and codes as built, st = 2^-e with zp in the low bits
+    r = np.random.default_rng(51)
+    for i, (zp, e) in enumerate(((0, 4), (3, 0), (5, 7), (15, 2))):
+        c = r.permutation(np.tile(np.arange(16), 2))
+        c[:2] = (0, 15)
+        assert np.array_equal(codes[i], c)
+        assert int(bits[i]) == (_f32_bits(_Fr(2) ** -e) | zp)
+    assert list(codes[4][2:12]) == [0, 2, 2, 4, 4, 6, 6, 8, 8, 10]   # ties to even, zp = 0
+    assert codes[5][2] == 3                                          # rint(2.5) = 2, plus zp = 1
+    assert o.hidden_zero(st[7:8])[0] == 0 and o.hidden_zero(st[8:9])[0] == 15
+
+
+def check_inline_bounds_and_degenerate(o):
+    """|x_hat - y| <= st/2 (plus float32 rounding of the product) on random
+    and one-signed rows; st within 15 ulp of the unperturbed scale, same
+    upper 28 bits; zero and subnormal-range rows store st = 0 and codes 0,
+    and dequantize to 0."""
+    y = np.concatenate([_bf16_rows((300, 64), 55, scale=3.0, offset=-0.7),
+                        np.abs(_bf16_rows((20, 64), 56)) + F32(0.5)]).astype(F32)
+    codes, st = o.quantize_rows_inline(y)
+    rows = o.inline_rows(o.pack_codes(codes, o.INT4_ASYM), st)
+    xh = o.dequant_inline_rows_f64(rows, 64)
+    mn = np.minimum(y.min(1), 0).astype(F32)
+    mx = np.maximum(y.max(1), 0).astype(F32)
+    s = ((mx - mn) / F32(15)).astype(F32)
+    assert np.all((st.view(np.uint32) >> 4) == (s.view(np.uint32) >> 4))
+    assert np.all(np.abs(st.astype(np.float64) - s) <= 15 * 2.0 ** -23 * s)
+    bound = 0.5 * st.astype(np.float64)[:, None] * (1 + 2.0 ** -16) + 2.0 ** -22 * np.abs(y)
+    assert np.all(np.abs(xh - y) <= bound)
+    for row in (np.zeros((1, 64), F32), np.full((1, 64), F32(1e-40))):
+        c0, s0 = o.quantize_rows_inline(row)
+        assert s0.view(np.uint32)[0] == 0 and not c0.any()
+        r0 = o.inline_rows(o.pack_codes(c0, o.INT4_ASYM), s0)
+        assert not o.dequant_inline_rows_f64(r0, 64).any()
+
+
+def check_inline_layout_write_gather_attention(o):
+    """The inline cache: shape (nb, 2, bs, Hkv, D/2 + 4); a written row holds
+    the nibbles (element 2j low) then the little-endian float32 stored
+    scale, K at index 0 and V at index 1 of the second axis; unwritten rows
+    keep their bytes; gather through a shuffled table (with rotation) is the
+    un-rotated (c - zp) st, and decode equals float64 SDPA over it."""
+    D, bs, Hkv, lens = 64, 16, 2, (37, 100)
+    assert o.inline_cache_shape(128, 4, 16, 3) == (3, 2, 16, 4, 68)
+    r = np.random.default_rng(57)
+    nblk = [(L + bs - 1) // bs for L in lens]
+    nb = sum(nblk) + 3
+    perm = r.permutation(nb)
+    bt = np.full((2, max(nblk)), -1, np.int64)
+    bt[0, :nblk[0]] = perm[:nblk[0]]
+    bt[1, :nblk[1]] = perm[nblk[0]:sum(nblk)]
+    tok_seq = np.repeat([0, 1], lens)
+    tok_pos = np.concatenate([np.arange(L) for L in lens])
+    slots = bt[tok_seq, tok_pos // bs] * bs + tok_pos % bs
+    T = sum(lens)
+    k = _bf16_rows((T, Hkv, D), 58)
+    v = _bf16_rows((T, Hkv, D), 59, offset=0.5)
+    signs = np.where(r.integers(0, 2, D) == 1, 1.0, -1.0).astype(F32)
+    for sg in (None, signs):
+        cache = np.full(o.inline_cache_shape(D, Hkv, bs, nb), 0xFF, np.uint8)
+        o.write_cache(k, v, o.INT4_INLINE, bs, cache, None, None, None, slot_mapping=slots, signs=sg)
+        written = np.zeros(cache.shape[:4], bool)
+        for t in range(T):
+            blk, off = divmod(int(slots[t]), bs)
+            for h in range(Hkv):
+                for kv, src in ((0, k), (1, v)):
+                    written[blk, kv, off, h] = True
+                    if sg is not None:
+                        continue
+                    c, bits = _inline_model(src[t, h])
+                    row = cache[blk, kv, off, h]
+                    nib = [int(row[j // 2]) >> (4 * (j % 2)) & 15 for j in range(D)]
+                    assert nib == c, (t, h, kv)
+                    assert bytes(row[D // 2:]) == int(bits).to_bytes(4, "little"), (t, h, kv)
+        assert np.all(cache[~written] == 0xFF)
+        K, V = o.gather_dequant(np.array([0, lens[0], T]), o.INT4_INLINE, D, bs, Hkv, cache, None, None, None,
+                                signs=sg, block_tables=bt)
+        R = np.eye(D) if sg is None else scipy.linalg.hadamard(D) * sg.astype(float)[None, :] / math.sqrt(D)
+        for src, G_ in ((k, K), (v, V)):
+            y = src.reshape(T * Hkv, D) if sg is None else o.rotate_f32(src.reshape(T * Hkv, D), sg)
+            c, st = o.quantize_rows_inline(y)
+            xh = (c - o.hidden_zero(st)[:, None]) * st.astype(np.float64)[:, None]
+            assert np.allclose(G_.reshape(T * Hkv, D), xh @ R, atol=1e-12)
+        q = _bf16_rows((2, 4, D), 60)
+        out = o.decode_attention(q, np.array(lens), o.INT4_INLINE, D, bs, Hkv, cache, None, None, None, 0.125,
+                                 signs=sg, block_tables=bt)
+        for b, L in enumerate(lens):
+            rows = np.nonzero(tok_seq == b)[0]
+            for hq in range(4):
+                h = hq // 2
+                ref = _sdpa64(q[b, hq][None], K[rows, h], V[rows, h], np.ones((1, L), bool), 0.125)[0]
+                assert np.allclose(out[b, hq], ref, atol=1e-12), (b, hq)
+
+
 ALL = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -60,6 +60,21 @@ MUTATIONS = {
     "fp8_subnormal_step": ("q_sub = np.rint(a / 2.0 ** -9)", "q_sub = np.rint(a / 2.0 ** -10)"),
     "headwise_slots_transposed": ("slots = np.asarray(slot_mapping_headwise, np.int64).reshape(T, Hkv)",
                                   "slots = np.asarray(slot_mapping_headwise, np.int64).reshape(Hkv, T).T"),
+    # INT4 with the zero point in the scale's low bits
+    "inline_zero_high_bits": ("return ((bits & np.uint32(0xFFFFFFF0)) | np.asarray(zp, np.uint32))",
+                              "return ((bits & np.uint32(0xFFFFFF0F)) | (np.asarray(zp, np.uint32) << np.uint32(4)))"),
+    "inline_range_without_zero": ("mn = np.minimum(np.min(y, axis=-1), _F32(0.0)).astype(_F32)",
+                                  "mn = np.min(y, axis=-1).astype(_F32)"),
+    "inline_round_after_add": ("c = np.clip(np.rint(t) + zp[..., None], 0, INLINE_LEVELS)",
+                               "c = np.clip(np.rint(t + zp[..., None]), 0, INLINE_LEVELS)"),
+    "inline_unperturbed_scale": ("inv = (_F32(1.0) / np.where(ok, st, _F32(1.0))).astype(_F32)",
+                                 "inv = (_F32(1.0) / np.where(ok, s1, _F32(1.0))).astype(_F32)"),
+    "inline_dequant_no_zero": ("return (codes - zp[:, None]) * st.astype(np.float64)[:, None]",
+                               "return codes * st.astype(np.float64)[:, None]"),
+    "inline_v_from_k_half": ("xhat = dequant_inline_rows_f64(k_codes[bi, kv, off, h, :], head_dim)",
+                             "xhat = dequant_inline_rows_f64(k_codes[bi, 0, off, h, :], head_dim)"),
+    "inline_zero_truncated": ("zp = np.clip(np.rint((-mn / s1).astype(_F32)), 0, INLINE_LEVELS).astype(np.int64)",
+                              "zp = np.clip(np.floor((-mn / s1).astype(_F32)), 0, INLINE_LEVELS).astype(np.int64)"),
 }
 
 
