@@ -12,8 +12,9 @@ one launch, cycling cache replicas (>= 1.2 GB in all) so that steps stream
 from HBM rather than the 256 MB Infinity Cache; ``--config 5`` is the mixed
 step (write, chunked prefill, decode).  With the default config the INT8,
 INT4 and mixed-step workloads, and the INT8 workload's shapes held as FP8
-E4M3 and as per-channel INT8 ("2:fp8", "2:chan"), are measured in the same
-run and reported as sub-objects under ``configs``.
+E4M3 and as per-channel INT8 ("2:fp8", "2:chan"), and the INT4 workload in
+the inline layout ("3:inline"), are measured in the same run and reported as
+sub-objects under ``configs``.
 
 Prints ONE JSON line.  Timing: after ``warmup`` untimed steps, ``repeats``
 (>= 5) timed regions of exactly ``steps`` steps, each bracketed by
@@ -64,17 +65,20 @@ DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", 
 PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")]
 GATHER_SRC = [os.path.join(CSRC, f) for f in ("kvq_gather.hip", "kvq_device.h", "kvq_internal.h")]
 WRITE_SRC = [os.path.join(CSRC, f) for f in ("kvq_write.hip", "kvq_write_row.h", "kvq_device.h", "kvq_internal.h")]
-MODE_NAMES = ["int8_sym", "int4_asym", "int2_asym", "int8_channel", "fp8_e4m3"]
+MODE_NAMES = ["int8_sym", "int4_asym", "int2_asym", "int8_channel", "fp8_e4m3", "int4_inline"]
 # per-mode decode contraction types
 MODE_DTYPES = {0: "int8 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
                1: "int4 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
                2: "int2 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
                3: "int8 codes (per-channel scales); int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
-               4: "fp8 e4m3 codes; bf16 mfma (q.k, p.v), fp32 accumulate"}
+               4: "fp8 e4m3 codes; bf16 mfma (q.k, p.v), fp32 accumulate",
+               5: "int4 codes (inline rows, zero point in the scale); int8 mfma (q.k), bf16 mfma (p.v), "
+                  "fp32 accumulate"}
 # workload variants a sub-object may name as "<config>:<variant>": the
 # config's shapes and inputs with another cache mode
 VARIANTS = {"fp8": dict(mode=4, rotate=False, suffix="fp8-e4m3"),
-            "chan": dict(mode=3, rotate=False, suffix="int8-channel")}
+            "chan": dict(mode=3, rotate=False, suffix="int8-channel"),
+            "inline": dict(mode=5, rotate=True, suffix="inline")}
 
 
 def spec_of(key):
@@ -101,7 +105,10 @@ def sha(paths):
 def row_layout(spec):
     """(packed code bytes, fp32 meta floats) of one (token, kv head) row:
     INT8 8 bits + scale, INT4 4 bits + scale and zero, INT2 2 bits + scale
-    and zero, per-channel INT8 8 bits and no meta, FP8 8 bits + scale."""
+    and zero, per-channel INT8 8 bits and no meta, FP8 8 bits + scale,
+    inline INT4 4 bits + the 4-byte stored scale in the row."""
+    if spec.mode == 5:
+        return spec.D // 2 + 4, 0
     bits = {0: 8, 1: 4, 2: 2, 3: 8, 4: 8}[spec.mode]
     return spec.D * bits // 8, {0: 1, 1: 2, 2: 2, 3: 0, 4: 1}[spec.mode]
 
@@ -351,7 +358,7 @@ def build_buffers(spec, dev, n_bufs, layers):
             kvq.kvq_reshape_and_cache(d, k, v, *planes, slot_mapping=case.slot_mapping,
                                       slot_mapping_headwise=case.slot_mapping_headwise)
         else:
-            planes = tuple(p.clone() for p in bufs[0]["planes"])
+            planes = tuple(None if p is None else p.clone() for p in bufs[0]["planes"])
         bufs.append(dict(planes=planes, q=q, new=new_of(k, v) if (l == 0 or layers) else bufs[0]["new"]))
         if l > 0 and layers:
             del k, v
@@ -367,7 +374,7 @@ def cpu_baseline(spec, case, planes, seconds):
     reported."""
     import oracle
     from threadpoolctl import threadpool_info, threadpool_limits
-    host_planes = [p.cpu().numpy() for p in planes]
+    host_planes = [None if p is None else p.cpu().numpy() for p in planes]
     q = case.q.float().cpu().numpy()
     lens = case.seq_lens.cpu().numpy()
     bt = None if case.block_tables is None else case.block_tables.cpu().numpy()
@@ -424,10 +431,11 @@ def run_decode(args, spec, dev, ceilings, headline):
     case, d, bufs = build_buffers(spec, dev, spec.layers if layered else 1, layered)
     n_bufs = len(bufs)
     if not layered:
-        cache_bytes = sum(p.numel() * p.element_size() for p in bufs[0]["planes"])
+        cache_bytes = sum(p.numel() * p.element_size() for p in bufs[0]["planes"] if p is not None)
         R = args.replicas or max(1, min(16, math.ceil(max(1.2e9, 4 * MALL_BYTES) / cache_bytes)))
         for _ in range(R - 1):
-            bufs.append(dict(planes=tuple(p.clone() for p in bufs[0]["planes"]), q=bufs[0]["q"], new=bufs[0]["new"]))
+            bufs.append(dict(planes=tuple(None if p is None else p.clone() for p in bufs[0]["planes"]),
+                             q=bufs[0]["q"], new=bufs[0]["new"]))
         n_bufs = R
     max_len = int(case.seq_lens.max().item())
     ws = kvq.alloc_workspace(kvq.kvq_decode_workspace_size(d, spec.B, spec.Hq, max_len), dev)
@@ -734,7 +742,8 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--subs", default=None,
                     help="comma-separated workloads reported as sub-objects, a config or config:variant "
-                         "(variants: fp8, chan); default 2,3,5,2:fp8,2:chan with --config 4; 'none' for none")
+                         "(variants: fp8, chan, inline); default 2,3,5,2:fp8,2:chan,3:inline with --config 4; "
+                         "'none' for none")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas of a one-layer workload (0 = >= 1.2 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=4.0, help="seconds of each of the oracle's six runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -763,7 +772,7 @@ def main():
         return
 
     if args.subs is None:
-        subs = ["2", "3", "5", "2:fp8", "2:chan"] if args.config == 4 else []
+        subs = ["2", "3", "5", "2:fp8", "2:chan", "3:inline"] if args.config == 4 else []
     elif args.subs in ("", "none"):
         subs = []
     else:

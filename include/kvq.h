@@ -91,9 +91,24 @@ typedef enum {
  * s = max|y| / 448, code = y * (1/s) clamped to +-448 and rounded to the
  * nearest E4M3 value (ties to even); x_hat = E4M3(code) * s; one meta float
  * (s); optional rotation.  Chunked prefill is not built for this mode
- * (KVQ_EUNSUPPORTED; kvq_gather_dequant gives the dense rows). */
+ * (KVQ_EUNSUPPORTED; kvq_gather_dequant gives the dense rows).
+ * INT4_INLINE: the vLLM-shaped inline layout (vLLM PR 40835 summary,
+ * 关键源码片段: cache shape (num_blocks, 2, block_size, num_kv_heads,
+ * head_size // 2 + scale_pad), the float32 scale at the end of each row;
+ * 评论区精华: the 4-bit zero point kept in the scale's low 4 bits).  ONE
+ * uint8 tensor [num_blocks][2][block_size][num_kv_heads][D/2 + 4], index 0
+ * of the second axis K, 1 V; a row is D/2 bytes of nibbles (element 2j in
+ * the low nibble of byte j) then the 4 little-endian bytes of the stored
+ * scale st.  Per row: mn = min(min y, 0), mx = max(max y, 0), s = (mx - mn)
+ * / 15, zp = clamp(rint(-mn / s), 0, 15), st = s with its low 4 bits
+ * replaced by zp (within 15 ulp of s), c = clamp(rint(y * (1/st)) + zp, 0,
+ * 15), x_hat = (c - zp) * st; a zero, subnormal or NaN s stores st = 0 and
+ * codes 0.  Optional rotation.  Calls take the tensor as k_codes and NULL
+ * for k_meta, v_codes and v_meta (KVQ_EINVAL otherwise).  Chunked prefill
+ * is not built for this mode (KVQ_EUNSUPPORTED). */
 typedef enum {
-  KVQ_INT8_SYM = 0, KVQ_INT4_ASYM = 1, KVQ_INT2_ASYM = 2, KVQ_INT8_CHANNEL = 3, KVQ_FP8_E4M3 = 4
+  KVQ_INT8_SYM = 0, KVQ_INT4_ASYM = 1, KVQ_INT2_ASYM = 2, KVQ_INT8_CHANNEL = 3, KVQ_FP8_E4M3 = 4,
+  KVQ_INT4_INLINE = 5
 } kvq_mode;
 
 typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 } kvq_out_dtype;
@@ -103,7 +118,9 @@ typedef struct {
   int32_t head_dim;        /* D: 64 or 128 */
   int32_t num_kv_heads;    /* Hkv >= 1 */
   int32_t block_size;      /* tokens per block: a power of two, 16..1024 */
-  int64_t num_blocks;      /* physical blocks in each plane, >= 1 */
+  int64_t num_blocks;      /* physical blocks in each plane, >= 1; rows
+                              num_blocks * num_kv_heads * block_size < 2^31
+                              (< 2^30 for KVQ_INT4_INLINE) */
   /* (device) [head_dim] float32 of +1.0f / -1.0f, or NULL for no rotation.
    * With signs d, every K and V row x is stored as the codes of
    * y = (1/sqrt(D)) * H_D (d .* x), H_D the Sylvester Hadamard matrix in
@@ -128,9 +145,10 @@ typedef struct {
 } kvq_decode_options;
 
 typedef struct {
-  uint64_t code_bytes;       /* bytes of one code plane (the K plane; V is equal) */
-  uint64_t meta_bytes;       /* bytes of one meta plane */
-  uint32_t row_code_bytes;   /* P */
+  uint64_t code_bytes;       /* bytes of one code plane (the K plane; V is equal);
+                                KVQ_INT4_INLINE: of the one cache tensor (K and V) */
+  uint64_t meta_bytes;       /* bytes of one meta plane (0 for INLINE) */
+  uint32_t row_code_bytes;   /* P; KVQ_INT4_INLINE: D/2 + 4, the whole inline row */
   uint32_t row_meta_floats;  /* M */
 } kvq_layout;
 

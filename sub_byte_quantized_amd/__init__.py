@@ -9,5 +9,6 @@ from .kvq import (CacheDesc, KvqError, alloc_cache, alloc_workspace, kvq_calibra
                   kvq_paged_prefill_attention, kvq_prefill_workspace_size,
                   kvq_query_layout,
                   kvq_reshape_and_cache, kvq_workspace_init, KVQ_INT8_SYM, KVQ_INT4_ASYM,
-                  KVQ_INT2_ASYM, KVQ_INT8_CHANNEL, KVQ_FP8_E4M3, KVQ_OUT_F32, KVQ_OUT_BF16)
+                  KVQ_INT2_ASYM, KVQ_INT8_CHANNEL, KVQ_FP8_E4M3, KVQ_INT4_INLINE, KVQ_OUT_F32,
+                  KVQ_OUT_BF16)
 from ._lib import LIB_PATH, load as load_library  # noqa: F401

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE, KVQ_EHIP = range(5)
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_EUNSUPPORTED", 3: "KVQ_ENOSPACE", 4: "KVQ_EHIP"}
-KVQ_INT8_SYM, KVQ_INT4_ASYM, KVQ_INT2_ASYM, KVQ_INT8_CHANNEL, KVQ_FP8_E4M3 = 0, 1, 2, 3, 4
+KVQ_INT8_SYM, KVQ_INT4_ASYM, KVQ_INT2_ASYM, KVQ_INT8_CHANNEL, KVQ_FP8_E4M3, KVQ_INT4_INLINE = 0, 1, 2, 3, 4, 5
 KVQ_OUT_F32, KVQ_OUT_BF16 = 0, 1
 
 

@@ -63,7 +63,12 @@ namespace {
 template <int MODE, int D, int PHI>
 struct Geo {
   static constexpr int P = row_bytes(MODE, D);   // packed bytes per row
-  static constexpr int M = mode_meta(MODE);      // meta floats per row
+  static constexpr int M = mode_meta(MODE);      // meta floats per row (meta planes)
+  // inline INT4: rows of RS bytes (codes, then the stored scale), tokens
+  // Hkv rows apart; the scale and the zero point come from one word
+  static constexpr bool INL = MODE == kInlineMode;
+  static constexpr int RS = INL ? inline_row_bytes(D) : P;
+  static constexpr bool MZ = M == 2 || INL;      // rows carry a zero point
   static constexpr int NKT = 4 / PHI;            // K-tiles per 64-position tile
   static constexpr int SUBD = D * PHI / 4;       // d values per lane group per K-tile
   static constexpr int KS = SUBD / 16;           // int8 MFMA k-steps per K-tile
@@ -95,7 +100,7 @@ constexpr int q_elem_bytes() { return MODE == kFp8Mode ? 2 : 1; }
 template <int MODE, int D, int PHI>
 __device__ __forceinline__ int kmap(int sub, int s, int j) {
   const int base = sub * Geo<MODE, D, PHI>::SUBD + 16 * s;
-  if constexpr (MODE == 1) return base + 8 * ((j >> 2) >> 1) + 2 * (j & 3) + ((j >> 2) & 1);
+  if constexpr (code_mode(MODE) == 1) return base + 8 * ((j >> 2) >> 1) + 2 * (j & 3) + ((j >> 2) & 1);
   else if constexpr (MODE == 2) return base + 4 * (j & 3) + (j >> 2);
   else return base + j;
 }
@@ -104,7 +109,7 @@ __device__ __forceinline__ int kmap(int sub, int s, int j) {
 template <int MODE, int KSW>
 __device__ __forceinline__ u32x4_t unpack_k(const uint32_t* kc, int s, uint32_t m4, uint32_t m2) {
   u32x4_t a;
-  if constexpr (MODE == 1) {
+  if constexpr (code_mode(MODE) == 1) {
     const uint32_t x0 = kc[2 * s], x1 = kc[2 * s + 1];
     a[0] = x0 & m4;
     a[1] = (x0 >> 4) & m4;
@@ -141,15 +146,16 @@ __device__ __forceinline__ u32x4_t unpack_v(const uint32_t (*vc)[VW], uint32_t m
   } else if constexpr (NARROW) {
     // vsel picks byte 0 of the lane's bytes in each of the two dwords; byte
     // b of them is vsel + b in both selector fields
-    constexpr uint32_t b = MODE == 1 ? DTI >> 1 : DTI >> 2;
-    constexpr int sh = MODE == 1 ? 4 * (DTI & 1) : 2 * (DTI & 3);
+    constexpr bool I4 = code_mode(MODE) == 1;
+    constexpr uint32_t b = I4 ? DTI >> 1 : DTI >> 2;
+    constexpr int sh = I4 ? 4 * (DTI & 1) : 2 * (DTI & 3);
     const uint32_t sel = vsel + b * 0x00010001u;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint32_t y = __builtin_amdgcn_perm(vc[2 * p + 1][0], vc[2 * p][0], sel);
-      a[p] = and_or(sh ? (y >> sh) : y, MODE == 1 ? n4 : n2, magic);
+      a[p] = and_or(sh ? (y >> sh) : y, I4 ? n4 : n2, magic);
     }
-  } else if constexpr (MODE == 1) {
+  } else if constexpr (code_mode(MODE) == 1) {
     constexpr uint32_t b = DTI >> 1;
     constexpr uint32_t sel = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);
 #pragma unroll
@@ -208,7 +214,9 @@ struct TileInfo {
 // formed for them and issue_loads reads nothing for them.
 // Attended positions of a pair: [start, L), plus [0, sink) when the head is
 // windowed (sink is 0 otherwise).
-template <bool CB>
+// INL: rows of the inline layout, ((id 2 bs + offset) Hkv + h), tokens Hkv
+// rows apart (the V rows use the same index from the V base).
+template <bool CB, bool INL>
 __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int tile, int te, int L, int start,
                                               int sink, int bs_log2, int hkv, int h, int nblk) {
   TileInfo t;
@@ -223,7 +231,13 @@ __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int 
       const int pos = t.pos0 + 16 * s;
       t.valid |= (okb && pos < L && (pos + 15 >= start || pos < sink)) ? 1u << s : 0u;
     }
-    t.row0 = okb ? ((id * hkv + h) << bs_log2) + (t.pos0 & ((1 << bs_log2) - 1)) : 0;
+    const int pin = t.pos0 & ((1 << bs_log2) - 1);
+    if constexpr (INL) {
+      t.row0 = okb ? ((id << (bs_log2 + 1)) + pin) * hkv + h : 0;
+      t.row1 = t.row0 + 16 * hkv; t.row2 = t.row0 + 32 * hkv; t.row3 = t.row0 + 48 * hkv;
+      return t;
+    }
+    t.row0 = okb ? ((id * hkv + h) << bs_log2) + pin : 0;
     t.row1 = t.row0 + 16; t.row2 = t.row0 + 32; t.row3 = t.row0 + 48;
     return t;
   }
@@ -235,7 +249,8 @@ __device__ __forceinline__ TileInfo tile_info(const int32_t* ids, int blk0, int 
     const int id = __builtin_amdgcn_readfirstlane(ids[in ? (pos >> bs_log2) - blk0 : 0]);
     const bool ok = in && id >= 0 && id < nblk;
     t.valid |= ok ? 1u << s : 0u;
-    row[s] = ok ? ((id * hkv + h) << bs_log2) + (pos & ((1 << bs_log2) - 1)) : 0;
+    const int pin = pos & ((1 << bs_log2) - 1);
+    row[s] = !ok ? 0 : (INL ? ((id << (bs_log2 + 1)) + pin) * hkv + h : ((id * hkv + h) << bs_log2) + pin);
   }
   t.row0 = row[0]; t.row1 = row[1]; t.row2 = row[2]; t.row3 = row[3];
   return t;
@@ -267,6 +282,58 @@ __device__ __forceinline__ void issue_loads(Buf<MODE, D, PHI>& b, const TileInfo
   // [start, L)) is not read: its registers keep whatever they held, which the
   // compute masks (score -inf, weight and V meta zero) and never lets reach a
   // result, since the codes are integers and every use is a select.
+  if constexpr (Gm::INL) {
+    // inline rows (4-byte aligned): tokens TS bytes apart, the stored scale
+    // word at byte P of each row
+    constexpr int RS = Gm::RS;
+    const int TS = p.hkv * RS;
+    if constexpr (CB) {
+      if (t.valid == 0) return;
+      const uint8_t* kb = p.k_codes + (int64_t)t.row0 * RS;
+      const uint8_t* vb = p.v_codes + (int64_t)t.row0 * RS;
+#pragma unroll
+      for (int tau = 0; tau < Gm::NKT; ++tau) {
+        load_bytes_a4<Gm::KB>(b.k[tau], kb + (16 * (tau * PHI + phi_grp) + r) * TS + sub * Gm::KB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int mo = (16 * (tau * PHI + phi_col) + 4 * q + i) * TS + P;
+          b.km[tau][i] = *reinterpret_cast<const float*>(kb + mo);
+          b.vm[tau][i] = *reinterpret_cast<const float*>(vb + mo);
+        }
+      }
+      const int vo = 4 * q * TS + ((r * Gm::VB) & ~3);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_bytes_a4<Gm::NARROW ? 4 : Gm::VB>(b.v[4 * s + i], vb + vo + (16 * s + i) * TS);
+      return;
+    }
+#pragma unroll
+    for (int tau = 0; tau < Gm::NKT; ++tau) {
+      const int sk = tau * PHI + phi_grp;
+      if ((t.valid >> sk) & 1u)
+        load_bytes_a4<Gm::KB>(b.k[tau], p.k_codes + (int64_t)pick_row(t, sk) * RS + r * TS + sub * Gm::KB);
+      const int sm = tau * PHI + phi_col;
+      if ((t.valid >> sm) & 1u) {
+        const int64_t mb = (int64_t)pick_row(t, sm) * RS + P;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b.km[tau][i] = *reinterpret_cast<const float*>(p.k_codes + mb + (4 * q + i) * TS);
+          b.vm[tau][i] = *reinterpret_cast<const float*>(p.v_codes + mb + (4 * q + i) * TS);
+        }
+      }
+    }
+    const int vo = 4 * q * TS + ((r * Gm::VB) & ~3);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (!((t.valid >> s) & 1u)) continue;   // wave-uniform
+      const int row = s == 0 ? t.row0 : (s == 1 ? t.row1 : (s == 2 ? t.row2 : t.row3));
+      const uint8_t* base = p.v_codes + (int64_t)row * RS + vo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_bytes_a4<Gm::NARROW ? 4 : Gm::VB>(b.v[4 * s + i], base + i * TS);
+    }
+    return;
+  }
   if constexpr (CB) {
     if (t.valid == 0) return;   // one block per tile: all four sub-tiles or none
     // uniform tile bases (scalar) + per-lane constant 32-bit offsets
@@ -441,8 +508,9 @@ __device__ __forceinline__ void compute_tile(Buf<MODE, D, PHI>& b, const TileInf
       // 2^7 a + b is exact in int32 (|.| < 2^29); one rounding joins c
       const float raw = __builtin_fmaf((float)((ia[i] << 7) + ib[i]), 128.0f, (float)ic[i]);
       // per-channel INT8: the K scales are folded into the query pieces
-      const float s = M == 0 ? 1.0f : (M == 2 ? b.km[tau][2 * i] : b.km[tau][i]);
-      const float z = M == 2 ? b.km[tau][2 * i + 1] : 0.0f;
+      // inline: the stored scale st, z = -zp st with zp its low 4 bits
+      const float s = (M == 0 && !Gm::INL) ? 1.0f : (M == 2 ? b.km[tau][2 * i] : b.km[tau][i]);
+      const float z = Gm::INL ? -(float)(__float_as_uint(s) & 0xFu) * s : (M == 2 ? b.km[tau][2 * i + 1] : 0.0f);
       sc[tau][i] = __builtin_fmaf(raw, s, z * lc.q1r);
     }
   }
@@ -453,8 +521,9 @@ __device__ __forceinline__ void compute_tile(Buf<MODE, D, PHI>& b, const TileInf
   for (int tau = 0; tau < Gm::NKT; ++tau)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      svv[tau][i] = M == 0 ? 1.0f : (M == 2 ? b.vm[tau][2 * i] : b.vm[tau][i]);
-      zvv[tau][i] = M == 2 ? b.vm[tau][2 * i + 1] : 0.0f;
+      svv[tau][i] = (M == 0 && !Gm::INL) ? 1.0f : (M == 2 ? b.vm[tau][2 * i] : b.vm[tau][i]);
+      zvv[tau][i] = Gm::INL ? -(float)(__float_as_uint(svv[tau][i]) & 0xFu) * svv[tau][i]
+                            : (M == 2 ? b.vm[tau][2 * i + 1] : 0.0f);
     }
   if (__builtin_expect(!full, 0)) {
     // the lane index re-derived here (mbcnt, from no register), so this rare
@@ -509,7 +578,7 @@ __device__ __forceinline__ void compute_tile(Buf<MODE, D, PHI>& b, const TileInf
       for (int e = 0; e < 2; ++e) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[tau][i + e], lc.sp, -mu));
         st.l += pr;
-        if constexpr (M == 2) st.z = __builtin_fmaf(pr, zvv[tau][i + e], st.z);
+        if constexpr (Gm::MZ) st.z = __builtin_fmaf(pr, zvv[tau][i + e], st.z);
         w2[e] = pr * svv[tau][i + e];
       }
       // hi = w with the low 16 bits cleared (exact bf16), lo = w - hi (exact)
@@ -853,7 +922,7 @@ __device__ __forceinline__ void cursor_seek(Cursor& c, const Smem<D, PHI, NWV, Q
   }
 }
 
-template <bool CB, int D, int PHI, int NWV, int QB>
+template <bool CB, bool INL, int D, int PHI, int NWV, int QB>
 __device__ __forceinline__ TileInfo cursor_info(const Cursor& c, const Smem<D, PHI, NWV, QB>& sm, int wave, int bl,
                                                 int hkv, int nblk, int sink) {
   if (c.ls >= c.nseg) {
@@ -861,7 +930,7 @@ __device__ __forceinline__ TileInfo cursor_info(const Cursor& c, const Smem<D, P
     t.pos0 = 0; t.row0 = 0; t.row1 = 0; t.row2 = 0; t.row3 = 0; t.valid = 0;
     return t;
   }
-  return tile_info<CB>(sm.ids + c.off, c.blk0, c.tb + wave + NWV * c.li, c.te, c.L, c.start,
+  return tile_info<CB, INL>(sm.ids + c.off, c.blk0, c.tb + wave + NWV * c.li, c.te, c.L, c.start,
                        c.start > 0 ? sink : 0, bl, hkv, c.h, nblk);
 }
 
@@ -1238,10 +1307,11 @@ void decode_kernel(DecodeParams p) {
     if (cur.ls < nseg) {
       const int b0 = __builtin_amdgcn_readfirstlane(sm.seg[cur.ls].b);
       const int32_t* trow = p.tables + (int64_t)(p.headwise ? b0 * hkv + cur.h : b0) * p.max_blocks;
-      ta = tile_info<CB>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te, cur.L, cur.start,
+      ta = tile_info<CB, MODE == kInlineMode>(trow + cur.blk0, cur.blk0, cur.tb + wave + NWV * cur.li, cur.te,
+                                              cur.L, cur.start,
                          cur.start > 0 ? p.sink : 0, bl, hkv, cur.h, nblk);
     } else {
-      ta = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk, p.sink);
+      ta = cursor_info<CB, MODE == kInlineMode>(cur, sm, wave, bl, hkv, nblk, p.sink);
     }
     cursor_next(cur, sm, wave);
     // the ids and query rows are back (the table read above waited for all
@@ -1322,11 +1392,11 @@ void decode_kernel(DecodeParams p) {
       for (int i = 0; i < Gm::DT; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
       for (int it = 0; it < n2; it += 2) {
-        const TileInfo tn = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk, p.sink);
+        const TileInfo tn = cursor_info<CB, MODE == kInlineMode>(cur, sm, wave, bl, hkv, nblk, p.sink);
         cursor_next(cur, sm, wave);
         issue_loads<MODE, D, PHI, CB>(bb, tn, p, r, q, phi_col);
         run_tile<MODE, D, PHI>(ba, ta, st, acc, lc, L, start, sinkE);
-        const TileInfo t2 = cursor_info<CB>(cur, sm, wave, bl, hkv, nblk, p.sink);
+        const TileInfo t2 = cursor_info<CB, MODE == kInlineMode>(cur, sm, wave, bl, hkv, nblk, p.sink);
         cursor_next(cur, sm, wave);
         issue_loads<MODE, D, PHI, CB>(ba, t2, p, r, q, phi_col);
         run_tile<MODE, D, PHI>(bb, tn, st, acc, lc, L, start, sinkE);
@@ -1500,6 +1570,7 @@ int decode_wgs_per_cu(int mode, int d, int group) {
   KVQ_W(2, 64, 4) KVQ_W(2, 64, 2) KVQ_W(2, 64, 1) KVQ_W(2, 128, 4) KVQ_W(2, 128, 2) KVQ_W(2, 128, 1)
   KVQ_W(3, 64, 4) KVQ_W(3, 64, 2) KVQ_W(3, 64, 1) KVQ_W(3, 128, 4) KVQ_W(3, 128, 2) KVQ_W(3, 128, 1)
   KVQ_W(4, 64, 4) KVQ_W(4, 64, 2) KVQ_W(4, 64, 1) KVQ_W(4, 128, 4) KVQ_W(4, 128, 2) KVQ_W(4, 128, 1)
+  KVQ_W(5, 64, 4) KVQ_W(5, 64, 2) KVQ_W(5, 64, 1) KVQ_W(5, 128, 4) KVQ_W(5, 128, 2) KVQ_W(5, 128, 1)
 #undef KVQ_W
   return 4;
 }
@@ -1510,7 +1581,8 @@ hipError_t launch_decode(int mode, int d, bool rot, const DecodeParams& p, hipSt
     case 1: return launch_decode_m<1>(d, rot, p, s);
     case 2: return launch_decode_m<2>(d, rot, p, s);
     case kChannelMode: return launch_decode_m<kChannelMode>(d, rot, p, s);
-    default: return launch_decode_m<kFp8Mode>(d, rot, p, s);
+    case kFp8Mode: return launch_decode_m<kFp8Mode>(d, rot, p, s);
+    default: return launch_decode_m<kInlineMode>(d, rot, p, s);
   }
 }
 

@@ -97,6 +97,27 @@ __device__ __forceinline__ uint32_t pack_exact(float a, float b) {
   return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
+// N bytes from an address that is only 4-byte aligned (rows of the inline
+// layout): dword vectors declared with 4-byte alignment.
+typedef uint32_t u32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2a4_t __attribute__((ext_vector_type(2), aligned(4)));
+template <int N>
+__device__ __forceinline__ void load_bytes_a4(uint32_t* dst, const uint8_t* src) {
+  static_assert(N % 4 == 0, "whole dwords");
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int i = 0; i < N / 16; ++i) {
+      const u32x4a4_t a = reinterpret_cast<const u32x4a4_t*>(src)[i];
+      dst[4 * i] = a[0]; dst[4 * i + 1] = a[1]; dst[4 * i + 2] = a[2]; dst[4 * i + 3] = a[3];
+    }
+  } else if constexpr (N == 8) {
+    const u32x2a4_t a = *reinterpret_cast<const u32x2a4_t*>(src);
+    dst[0] = a[0]; dst[1] = a[1];
+  } else {
+    dst[0] = *reinterpret_cast<const uint32_t*>(src);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src) {
   if constexpr (N >= 16) {

@@ -85,14 +85,21 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
       id = trow[pos >> p.block_size_log2];
     }
     present[it] = in && id >= 0 && id < p.num_blocks && orow[it] < p.total_tokens;
-    const int64_t src = present[it]
-                            ? (((int64_t)id * hkv + h) << p.block_size_log2) + (pos & ((1 << p.block_size_log2) - 1))
-                            : 0;
-    const uint8_t* codes = (kv ? p.v_codes : p.k_codes) + src * P + lr * BPL;
+    const int64_t pin = pos & ((1 << p.block_size_log2) - 1);
+    // plane row (id Hkv + h) bs + offset; inline row (id 2 bs + offset) Hkv + h
+    const int64_t src = !present[it] ? 0
+                        : MODE == kInlineMode ? ((((int64_t)id << (p.block_size_log2 + 1)) + pin) * hkv + h)
+                                              : ((((int64_t)id * hkv + h) << p.block_size_log2) + pin);
+    const uint8_t* codes = (kv ? p.v_codes : p.k_codes) + src * (MODE == kInlineMode ? inline_row_bytes(D) : P) +
+                           lr * BPL;
     const float* meta = (kv ? p.v_meta : p.k_meta) + src * M;   // unused when M == 0
     if (present[it]) {
       load_bytes<BPL>(raw[it], codes);
-      if constexpr (M == 0) {   // per-channel scales, read below
+      if constexpr (MODE == kInlineMode) {   // stored scale st; zero point = its low 4 bits
+        const uint32_t sb = *reinterpret_cast<const uint32_t*>(codes - lr * BPL + P);
+        s[it] = __uint_as_float(sb);
+        z[it] = (float)(sb & 0xFu);
+      } else if constexpr (M == 0) {   // per-channel scales, read below
         s[it] = 1.0f;
         z[it] = 0.0f;
       } else if constexpr (M == 2) {
@@ -137,8 +144,12 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
     for (int i = 0; i < 8 && MODE != kFp8Mode; ++i) {
       int c;
       if constexpr (MODE == 0 || MODE == kChannelMode) c = (int)(int8_t)((raw[it][i >> 2] >> (8 * (i & 3))) & 0xffu);
-      else if constexpr (MODE == 1) c = (int)((raw[it][0] >> (4 * i)) & 0xFu);
+      else if constexpr (code_mode(MODE) == 1) c = (int)((raw[it][0] >> (4 * i)) & 0xFu);
       else c = (int)((raw[it][0] >> (2 * i)) & 0x3u);
+      if constexpr (MODE == kInlineMode) {   // (c - zp) st: an exact small integer times st
+        x[i] = ((float)c - z[it]) * s[it];
+        continue;
+      }
       const float cs = (float)c * (MODE == kChannelMode ? sc[i] : s[it]);
       x[i] = M == 2 ? cs + z[it] : cs;
     }
@@ -222,7 +233,8 @@ hipError_t launch_gather(int mode, int d, bool rot, const GatherParams& p, hipSt
     case 1: return launch_gather_m<1>(d, rot, p, s);
     case 2: return launch_gather_m<2>(d, rot, p, s);
     case kChannelMode: return launch_gather_m<kChannelMode>(d, rot, p, s);
-    default: return launch_gather_m<kFp8Mode>(d, rot, p, s);
+    case kFp8Mode: return launch_gather_m<kFp8Mode>(d, rot, p, s);
+    default: return launch_gather_m<kInlineMode>(d, rot, p, s);
   }
 }
 

@@ -45,7 +45,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 kvq_status check_desc(const kvq_cache_desc* d) {
   if (!d) return fail(KVQ_EINVAL, "desc is NULL");
-  if (d->mode < KVQ_INT8_SYM || d->mode > KVQ_FP8_E4M3)
+  if (d->mode < KVQ_INT8_SYM || d->mode > KVQ_INT4_INLINE)
     return fail(KVQ_EINVAL, "mode %d is not a kvq_mode", d->mode);
   if (d->head_dim != 64 && d->head_dim != 128) {
     if (d->head_dim > 0 && (d->head_dim & (d->head_dim - 1)) == 0)
@@ -56,8 +56,10 @@ kvq_status check_desc(const kvq_cache_desc* d) {
   if (d->block_size < 16 || d->block_size > 1024 || (d->block_size & (d->block_size - 1)) != 0)
     return fail(KVQ_EINVAL, "block_size %d must be a power of two in [16, 1024]", d->block_size);
   if (d->num_blocks < 1) return fail(KVQ_EINVAL, "num_blocks %lld < 1", (long long)d->num_blocks);
-  if ((long long)d->num_blocks * d->num_kv_heads * d->block_size > 0x7fffffffLL)
-    return fail(KVQ_EUNSUPPORTED, "num_blocks*num_kv_heads*block_size must stay below 2^31 rows");
+  if ((long long)d->num_blocks * d->num_kv_heads * d->block_size * (d->mode == KVQ_INT4_INLINE ? 2 : 1) >
+      0x7fffffffLL)
+    return fail(KVQ_EUNSUPPORTED, "num_blocks*num_kv_heads*block_size must stay below 2^31 rows (2^30 for the "
+                "inline layout, which holds K and V rows in one tensor)");
   if (d->rot_signs && !aligned(d->rot_signs, 16))
     return fail(KVQ_EINVAL, "rot_signs must be 16-byte aligned");
   if (d->mode == KVQ_INT8_CHANNEL && d->rot_signs)
@@ -74,12 +76,31 @@ kvq_status check_channel(const kvq_cache_desc* d) {
 }
 
 // Code planes always; meta planes unless the mode has no per-row metadata.
+// The inline layout is one tensor passed as k_codes, the other three NULL.
 kvq_status check_planes(int mode, const uint8_t* kc, const float* km, const uint8_t* vc, const float* vm) {
+  if (mode == KVQ_INT4_INLINE) {
+    if (!kc) return fail(KVQ_EINVAL, "k_codes (the inline cache) is NULL");
+    if (km || vc || vm) return fail(KVQ_EINVAL, "KVQ_INT4_INLINE takes one tensor as k_codes; k_meta, v_codes and "
+                                    "v_meta must be NULL");
+    if (!aligned(kc, 16)) return fail(KVQ_EINVAL, "the inline cache must be 16-byte aligned");
+    return KVQ_OK;
+  }
   const bool meta = kvq::mode_meta(mode) > 0;
   if (!kc || !vc || (meta && (!km || !vm))) return fail(KVQ_EINVAL, "a cache plane pointer is NULL");
   if (!aligned(kc, 16) || !aligned(vc, 16) || (meta && (!aligned(km, 16) || !aligned(vm, 16))))
     return fail(KVQ_EINVAL, "cache planes must be 16-byte aligned");
   return KVQ_OK;
+}
+
+// The four plane pointers the kernels take: for the inline layout the V
+// base is the V half of block 0 (block_size * num_kv_heads rows in), so K and
+// V rows share one row index, and there are no meta planes.
+template <typename C, typename F>
+void resolve_planes(const kvq_cache_desc* d, C*& kc, F*& km, C*& vc, F*& vm) {
+  if (d->mode != KVQ_INT4_INLINE) return;
+  vc = kc + (size_t)d->block_size * d->num_kv_heads * kvq::inline_row_bytes(d->head_dim);
+  km = nullptr;
+  vm = nullptr;
 }
 
 float inv_sqrt_f32(int d) { return (float)(1.0 / std::sqrt((double)d)); }
@@ -210,6 +231,7 @@ kvq_status decode_impl(const kvq_cache_desc* desc, void* out, int32_t out_dtype,
   if (!aligned(out, 16)) return fail(KVQ_EINVAL, "out must be 16-byte aligned");
   st = check_planes(desc->mode, k_codes, k_meta, v_codes, v_meta);
   if (st != KVQ_OK) return st;
+  resolve_planes(desc, k_codes, k_meta, v_codes, v_meta);
   st = check_channel(desc);
   if (st != KVQ_OK) return st;
   const DecodePlan pl = plan_decode(desc, num_seqs, num_q_heads, max_seq_len, options);
@@ -285,9 +307,9 @@ kvq_status check_prefill_sizes(const kvq_cache_desc* desc, int num_seqs, int num
                                int max_seq_len) {
   kvq_status st = check_desc(desc);
   if (st != KVQ_OK) return st;
-  if (desc->mode == KVQ_FP8_E4M3)
-    return fail(KVQ_EUNSUPPORTED, "chunked prefill is not built for KVQ_FP8_E4M3 (kvq_gather_dequant gives the "
-                "dense rows)");
+  if (desc->mode == KVQ_FP8_E4M3 || desc->mode == KVQ_INT4_INLINE)
+    return fail(KVQ_EUNSUPPORTED, "chunked prefill is not built for %s (kvq_gather_dequant gives the dense rows)",
+                desc->mode == KVQ_FP8_E4M3 ? "KVQ_FP8_E4M3" : "KVQ_INT4_INLINE");
   if (num_seqs < 0) return fail(KVQ_EINVAL, "num_seqs %d < 0", num_seqs);
   if (num_q_heads < 1) return fail(KVQ_EINVAL, "num_q_heads %d < 1", num_q_heads);
   if (num_q_heads % desc->num_kv_heads != 0)
@@ -314,6 +336,13 @@ kvq_status kvq_query_layout(const kvq_cache_desc* desc, kvq_layout* out) {
   const uint32_t P = (uint32_t)kvq::row_bytes(desc->mode, desc->head_dim);
   const uint32_t M = (uint32_t)kvq::mode_meta(desc->mode);
   const uint64_t rows = (uint64_t)desc->num_blocks * desc->num_kv_heads * desc->block_size;
+  if (desc->mode == KVQ_INT4_INLINE) {   // one tensor: K and V rows of D/2 + 4 bytes
+    out->row_code_bytes = (uint32_t)kvq::inline_row_bytes(desc->head_dim);
+    out->row_meta_floats = 0;
+    out->code_bytes = 2 * rows * out->row_code_bytes;
+    out->meta_bytes = 0;
+    return ok();
+  }
   out->row_code_bytes = P;
   out->row_meta_floats = M;
   out->code_bytes = rows * P;
@@ -334,6 +363,7 @@ kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc, const void* key, co
     return fail(KVQ_EINVAL, "exactly one of slot_mapping and slot_mapping_headwise must be non-NULL");
   st = check_planes(desc->mode, k_codes, k_meta, v_codes, v_meta);
   if (st != KVQ_OK) return st;
+  resolve_planes(desc, k_codes, k_meta, v_codes, v_meta);
   st = check_channel(desc);
   if (st != KVQ_OK) return st;
   const int D = desc->head_dim, H = desc->num_kv_heads;
@@ -514,6 +544,7 @@ kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc, void* out, in
     return fail(KVQ_EINVAL, "out, query, cu_seqlens_q or seq_lens is NULL");
   st = check_planes(desc->mode, k_codes, k_meta, v_codes, v_meta);
   if (st != KVQ_OK) return st;
+  resolve_planes(desc, k_codes, k_meta, v_codes, v_meta);
   st = check_channel(desc);
   if (st != KVQ_OK) return st;
   const int tq = 128 / group;
@@ -594,6 +625,7 @@ kvq_status kvq_gather_dequant(const kvq_cache_desc* desc, void* key_out, void* v
     return fail(KVQ_EINVAL, "key_out and value_out must be 16-byte aligned");
   st = check_planes(desc->mode, k_codes, k_meta, v_codes, v_meta);
   if (st != KVQ_OK) return st;
+  resolve_planes(desc, k_codes, k_meta, v_codes, v_meta);
   st = check_channel(desc);
   if (st != KVQ_OK) return st;
   kvq::GatherParams p{};

@@ -7,19 +7,31 @@
 
 namespace kvq {
 
-// Code bits, metadata floats per row and levels, by mode (0 INT8 per token
-// and head, 1 INT4, 2 INT2, 3 INT8 with per-channel scales and no per-row
-// metadata, 4 FP8 E4M3 per token and head: one scale, codes up to 448).
+// Code bits, metadata floats per row (in separate meta planes) and levels,
+// by mode: 0 INT8 per token and head, 1 INT4, 2 INT2, 3 INT8 with
+// per-channel scales and no per-row metadata, 4 FP8 E4M3 per token and head
+// (one scale, codes up to 448), 5 INT4 in the inline layout (codes and the
+// float32 stored scale in one row, the integer zero point in the scale's low
+// 4 bits, no meta planes).
 __host__ __device__ constexpr int mode_bits(int mode) {
-  return (mode == 0 || mode == 3 || mode == 4) ? 8 : (mode == 1 ? 4 : 2);
+  return (mode == 0 || mode == 3 || mode == 4) ? 8 : ((mode == 1 || mode == 5) ? 4 : 2);
 }
-__host__ __device__ constexpr int mode_meta(int mode) { return (mode == 0 || mode == 4) ? 1 : (mode == 3 ? 0 : 2); }
+__host__ __device__ constexpr int mode_meta(int mode) {
+  return (mode == 0 || mode == 4) ? 1 : ((mode == 3 || mode == 5) ? 0 : 2);
+}
 __host__ __device__ constexpr int mode_levels(int mode) {
-  return (mode == 0 || mode == 3) ? 127 : (mode == 1 ? 15 : (mode == 4 ? 448 : 3));
+  return (mode == 0 || mode == 3) ? 127 : ((mode == 1 || mode == 5) ? 15 : (mode == 4 ? 448 : 3));
 }
 // Per-channel scales: [2][Hkv][D] float32, K then V.
 constexpr int kChannelMode = 3;
 constexpr int kFp8Mode = 4;
+// Inline INT4: one uint8 tensor [nb][2][bs][Hkv][D/2 + 4]; K rows at index 0
+// of the second axis, V rows at 1 (the host passes the V half of block 0 as
+// the V base, so both use one row index ((blk * 2 bs + offset) Hkv + h)).
+constexpr int kInlineMode = 5;
+__host__ __device__ constexpr int inline_row_bytes(int d) { return d / 2 + 4; }
+// How a mode packs its codes (the inline mode packs like INT4).
+__host__ __device__ constexpr int code_mode(int mode) { return mode == 5 ? 1 : mode; }
 __host__ __device__ constexpr int row_bytes(int mode, int d) { return d * mode_bits(mode) / 8; }
 
 // Positions the decode kernel processes as one tile (four 16-token MFMA tiles).

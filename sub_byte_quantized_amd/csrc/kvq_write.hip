@@ -138,7 +138,8 @@ hipError_t launch_write(int mode, int d, bool rot, const WriteParams& p, hipStre
     case 1: return launch_write_m<1>(d, rot, p, s);
     case 2: return launch_write_m<2>(d, rot, p, s);
     case kChannelMode: return launch_write_m<kChannelMode>(d, rot, p, s);
-    default: return launch_write_m<kFp8Mode>(d, rot, p, s);
+    case kFp8Mode: return launch_write_m<kFp8Mode>(d, rot, p, s);
+    default: return launch_write_m<kInlineMode>(d, rot, p, s);
   }
 }
 

@@ -107,6 +107,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     }
   }
   float s = 0.0f, z = 0.0f;   // per-row scale and zero (not for per-channel INT8)
+  uint32_t stbits = 0;        // inline INT4: bits of the stored scale
   if constexpr (MODE == 0 || MODE == kFp8Mode) {
     float a = 0.0f;
 #pragma unroll
@@ -127,6 +128,10 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
       mn = fminf(mn, xor_in_row(mn, m));
       mx = fmaxf(mx, xor_in_row(mx, m));
     }
+    if constexpr (MODE == kInlineMode) {   // the range holds zero (integer zero point)
+      mn = fminf(mn, 0.0f);
+      mx = fmaxf(mx, 0.0f);
+    }
     s = (mx - mn) / kLevels;
     z = mn;
   }
@@ -146,6 +151,19 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
       w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[4 * j + 2], t[4 * j + 3], (int)w, true);
       c[4 * j] = w & 0xffu; c[4 * j + 1] = (w >> 8) & 0xffu; c[4 * j + 2] = (w >> 16) & 0xffu; c[4 * j + 3] = w >> 24;
     }
+  } else if constexpr (MODE == kInlineMode) {
+    // zp = clamp(rint(-mn / s), 0, 15) into the low 4 bits of s (the stored
+    // scale st), then c = clamp(rint(x * (1/st)) + zp, 0, 15); a zero,
+    // subnormal or NaN s stores st = 0 and codes 0
+    const bool ok = s >= 1.17549435e-38f;
+    const float zp = ok ? fminf(fmaxf(__builtin_rintf(-z / s), 0.0f), kLevels) : 0.0f;
+    stbits = ok ? ((__float_as_uint(s) & ~0xFu) | (uint32_t)zp) : 0u;
+    const float inv = ok ? 1.0f / __uint_as_float(stbits) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float r = fminf(fmaxf(__builtin_rintf(x[i] * inv) + zp, 0.0f), kLevels);
+      c[i] = ok ? (uint32_t)(int32_t)r : 0u;
+    }
   } else if constexpr (MODE != kChannelMode) {
     // zero, subnormal or NaN scale: all-zero codes
     const bool ok = s >= 1.17549435e-38f;
@@ -164,6 +182,17 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   const int bsl = __builtin_ctz((unsigned)p.block_size);
   const int64_t blk = slot >> bsl;
   const int64_t off = slot & (p.block_size - 1);
+  if constexpr (MODE == kInlineMode) {
+    // row ((blk * 2 bs + off) Hkv + h) from the K or V base: nibbles, then
+    // the stored scale
+    uint8_t* row = (kv ? p.v_codes : p.k_codes) + (((blk << (bsl + 1)) + off) * hkv + h) * inline_row_bytes(D);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= c[i] << (4 * i);
+    *reinterpret_cast<uint32_t*>(row + lr * BPL) = w;
+    if (lr == 0) *reinterpret_cast<uint32_t*>(row + P) = stbits;
+    return;
+  }
   const int64_t ridx = (blk * hkv + h) * p.block_size + off;
   uint8_t* codes = (kv ? p.v_codes : p.k_codes) + ridx * P + lr * BPL;
   float* meta = (kv ? p.v_meta : p.k_meta) + ridx * M;   // unused when M == 0

@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (KVQ_FP8_E4M3, KVQ_INT2_ASYM, KVQ_INT4_ASYM, KVQ_INT8_CHANNEL, KVQ_INT8_SYM,  # noqa: F401
+from ._lib import (KVQ_FP8_E4M3, KVQ_INT2_ASYM, KVQ_INT4_ASYM, KVQ_INT4_INLINE, KVQ_INT8_CHANNEL,  # noqa: F401
+                   KVQ_INT8_SYM,
                    KVQ_OUT_BF16, KVQ_OUT_F32)
 
 
@@ -54,9 +55,17 @@ def _opts(num_workgroups: int):
 def _check_planes(desc, k_codes, k_meta, v_codes, v_meta):
     """The four planes: dtype, device, contiguity, and at least the bytes the
     layout query gives for ``desc`` (a larger allocation is allowed: the
-    kernels address only the first num_blocks blocks)."""
+    kernels address only the first num_blocks blocks).  KVQ_INT4_INLINE: the
+    one cache tensor as k_codes, the other three None."""
     lay = kvq_query_layout(desc)
     dev = k_codes.device
+    if desc.mode == KVQ_INT4_INLINE:
+        if k_meta is not None or v_codes is not None or v_meta is not None:
+            raise ValueError("KVQ_INT4_INLINE takes the cache as k_codes; k_meta, v_codes, v_meta must be None")
+        _need(k_codes, "k_codes", torch.uint8, dev)
+        if k_codes.numel() < lay["code_bytes"]:
+            raise ValueError(f"k_codes holds {k_codes.numel()} bytes, the layout needs {lay['code_bytes']}")
+        return dev
     for t, n, dt, need in ((k_codes, "k_codes", torch.uint8, lay["code_bytes"]),
                            (v_codes, "v_codes", torch.uint8, lay["code_bytes"]),
                            (k_meta, "k_meta", torch.float32, lay["meta_bytes"]),
@@ -152,9 +161,18 @@ def kvq_query_layout(desc: CacheDesc) -> dict:
 def alloc_cache(desc: CacheDesc, device, poison: bool = False):
     """Allocate (k_codes, k_meta, v_codes, v_meta) at the sizes
     kvq_query_layout reports: uint8 [nb, Hkv, bs, P] and float32
-    [nb, Hkv, bs, M].  ``poison`` fills codes with 0xFF and meta with NaN."""
+    [nb, Hkv, bs, M].  ``poison`` fills codes with 0xFF and meta with NaN.
+    KVQ_INT4_INLINE: (cache, None, None, None), cache uint8 [nb, 2, bs, Hkv,
+    D/2 + 4]."""
     lay = kvq_query_layout(desc)
     P, M = lay["row_code_bytes"], lay["row_meta_floats"]
+    if desc.mode == KVQ_INT4_INLINE:
+        c = torch.empty((desc.num_blocks, 2, desc.block_size, desc.num_kv_heads, P), dtype=torch.uint8,
+                        device=device)
+        assert c.numel() == lay["code_bytes"]
+        if poison:
+            c.fill_(0xFF)
+        return c, None, None, None
     shape_c = (desc.num_blocks, desc.num_kv_heads, desc.block_size, P)
     shape_m = (desc.num_blocks, desc.num_kv_heads, desc.block_size, M)
     planes = []

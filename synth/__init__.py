@@ -38,8 +38,9 @@ import torch
 INT8_SYM, INT4_ASYM, INT2_ASYM = 0, 1, 2
 INT8_CHANNEL = 3
 FP8_E4M3 = 4
-_BITS = {INT8_SYM: 8, INT4_ASYM: 4, INT2_ASYM: 2, INT8_CHANNEL: 8, FP8_E4M3: 8}
-_META = {INT8_SYM: 1, INT4_ASYM: 2, INT2_ASYM: 2, INT8_CHANNEL: 0, FP8_E4M3: 1}
+INT4_INLINE = 5
+_BITS = {INT8_SYM: 8, INT4_ASYM: 4, INT2_ASYM: 2, INT8_CHANNEL: 8, FP8_E4M3: 8, INT4_INLINE: 4}
+_META = {INT8_SYM: 1, INT4_ASYM: 2, INT2_ASYM: 2, INT8_CHANNEL: 0, FP8_E4M3: 1, INT4_INLINE: 0}
 
 S_LENS, S_K, S_V, S_Q, S_SIGNS, S_PERM, S_OUTLIER, S_OFFSET = range(8)
 

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -58,7 +59,7 @@ def test_layout_matches_formula(lib, mode, D):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(mode=5), _lib.KVQ_EINVAL), (dict(mode=-1), _lib.KVQ_EINVAL),
+    (dict(mode=6), _lib.KVQ_EINVAL), (dict(mode=-1), _lib.KVQ_EINVAL),
     (dict(mode=3, signs=4096), _lib.KVQ_EUNSUPPORTED),
     (dict(D=96), _lib.KVQ_EINVAL), (dict(D=256), _lib.KVQ_EUNSUPPORTED), (dict(D=0), _lib.KVQ_EINVAL),
     (dict(H=0), _lib.KVQ_EINVAL), (dict(bs=8), _lib.KVQ_EINVAL), (dict(bs=40), _lib.KVQ_EINVAL), (dict(bs=48), _lib.KVQ_EINVAL),
@@ -118,6 +119,30 @@ def _decode(lib, d, **kw):
                                           a["kc"], a["km"], a["vc"], a["vm"], a["bt"], a["bth"], a["mb"],
                                           a["sl"], a["msl"], a["win"], 0, a["scale"], a["opt"], a["ws"], a["wsb"],
                                           None)
+
+
+def test_inline_layout_and_planes(lib):
+    """KVQ_INT4_INLINE: one tensor [nb, 2, bs, Hkv, D/2 + 4] passed as k_codes;
+    k_meta, v_codes and v_meta must be NULL; no chunked prefill; rows of the
+    tensor stay below 2^31."""
+    d = desc(mode=5, D=128, H=4, bs=32, nb=7)
+    out = _lib.Layout()
+    assert lib.kvq_query_layout(ctypes.byref(d), ctypes.byref(out)) == 0
+    assert out.row_code_bytes == 68 and out.row_meta_floats == 0 and out.meta_bytes == 0
+    assert out.code_bytes == int(np.prod(oracle.inline_cache_shape(128, 4, 32, 7)))
+    P = ctypes.c_void_p(4096)
+    assert _decode(lib, d, km=P, vc=None, vm=None, msl=4 * 32) == _lib.KVQ_EINVAL
+    assert "must be NULL" in lib.kvq_last_error().decode()
+    assert _decode(lib, d, km=None, vc=P, vm=None, msl=4 * 32) == _lib.KVQ_EINVAL
+    assert _decode(lib, d, kc=None, km=None, vc=None, vm=None, msl=4 * 32) == _lib.KVQ_EINVAL
+    assert lib.kvq_reshape_and_cache(ctypes.byref(d), P, P, 512, 512, P, None, 4, P, None, P, None, None) \
+        == _lib.KVQ_EINVAL
+    assert _prefill(lib, d, km=None, vc=None, vm=None) == _lib.KVQ_EUNSUPPORTED
+    assert "INLINE" in lib.kvq_last_error().decode()
+    big = desc(mode=5, D=128, H=8, bs=1024, nb=1 << 17)   # 2^30 rows per half: 2^31 in the tensor
+    assert lib.kvq_query_layout(ctypes.byref(big), ctypes.byref(out)) == _lib.KVQ_EUNSUPPORTED
+    half = desc(mode=1, D=128, H=8, bs=1024, nb=1 << 17)  # the same rows in separate planes fit
+    assert lib.kvq_query_layout(ctypes.byref(half), ctypes.byref(out)) == _lib.KVQ_OK
 
 
 def test_decode_validation(lib):
