@@ -104,8 +104,7 @@ typedef enum {
  * replaced by zp (within 15 ulp of s), c = clamp(rint(y * (1/st)) + zp, 0,
  * 15), x_hat = (c - zp) * st; a zero, subnormal or NaN s stores st = 0 and
  * codes 0.  Optional rotation.  Calls take the tensor as k_codes and NULL
- * for k_meta, v_codes and v_meta (KVQ_EINVAL otherwise).  Chunked prefill
- * is not built for this mode (KVQ_EUNSUPPORTED). */
+ * for k_meta, v_codes and v_meta (KVQ_EINVAL otherwise). */
 typedef enum {
   KVQ_INT8_SYM = 0, KVQ_INT4_ASYM = 1, KVQ_INT2_ASYM = 2, KVQ_INT8_CHANNEL = 3, KVQ_FP8_E4M3 = 4,
   KVQ_INT4_INLINE = 5

@@ -307,9 +307,9 @@ kvq_status check_prefill_sizes(const kvq_cache_desc* desc, int num_seqs, int num
                                int max_seq_len) {
   kvq_status st = check_desc(desc);
   if (st != KVQ_OK) return st;
-  if (desc->mode == KVQ_FP8_E4M3 || desc->mode == KVQ_INT4_INLINE)
-    return fail(KVQ_EUNSUPPORTED, "chunked prefill is not built for %s (kvq_gather_dequant gives the dense rows)",
-                desc->mode == KVQ_FP8_E4M3 ? "KVQ_FP8_E4M3" : "KVQ_INT4_INLINE");
+  if (desc->mode == KVQ_FP8_E4M3)
+    return fail(KVQ_EUNSUPPORTED, "chunked prefill is not built for KVQ_FP8_E4M3 (kvq_gather_dequant gives the "
+                "dense rows)");
   if (num_seqs < 0) return fail(KVQ_EINVAL, "num_seqs %d < 0", num_seqs);
   if (num_q_heads < 1) return fail(KVQ_EINVAL, "num_q_heads %d < 1", num_q_heads);
   if (num_q_heads % desc->num_kv_heads != 0)

@@ -73,7 +73,7 @@ template <int MODE, int D>
 __device__ __forceinline__ int kslot_d(int s) {
   constexpr int DC = PGeo<MODE, D>::DC;
   const int base = (s / DC) * DC, c = s % DC;
-  if constexpr (MODE == 1) {
+  if constexpr (code_mode(MODE) == 1) {
     const int pl = c / (DC / 2), rem = c % (DC / 2);
     return base + 8 * (rem >> 2) + 2 * (rem & 3) + pl;
   } else if constexpr (MODE == 2) {
@@ -127,11 +127,16 @@ __device__ __forceinline__ bool key_seen(const KeyRange& kr, int j) {
   return j <= kr.khi && (j >= kr.klo || j < kr.sink);
 }
 
+// INL: the row of the inline layout, ((id 2 bs + offset) Hkv + h), read
+// from the K or the V base (consecutive positions are Hkv rows apart).
+template <bool INL>
 __device__ __forceinline__ int plane_row(const int32_t* trow, int j, const KeyRange& kr, int bs_log2, int hkv,
                                          int h, int nblk) {
   int id = -1;
   if (key_seen(kr, j)) id = trow[j >> bs_log2];
-  return (id >= 0 && id < nblk) ? ((id * hkv + h) << bs_log2) + (j & ((1 << bs_log2) - 1)) : -1;
+  if (id < 0 || id >= nblk) return -1;
+  const int pin = j & ((1 << bs_log2) - 1);
+  return INL ? ((id << (bs_log2 + 1)) + pin) * hkv + h : ((id * hkv + h) << bs_log2) + pin;
 }
 
 // Global loads of key tile `tau` into registers.  Thread t stages K codes of
@@ -145,14 +150,31 @@ __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillPara
   using Gp = PGeo<MODE, D>;
   const int n = tid >> 2, qd = tid & 3;
   const int nblk = (int)p.num_blocks;   // < 2^31 (checked on the host)
-  const int row = plane_row(trow, tau * kPKeys + n, kr, p.block_size_log2, p.hkv, h, nblk);
+  constexpr bool INL = MODE == kInlineMode;
+  constexpr int RS = INL ? inline_row_bytes(D) : Gp::P;   // bytes between rows
+  const int row = plane_row<INL>(trow, tau * kPKeys + n, kr, p.block_size_log2, p.hkv, h, nblk);
   st.ok = row >= 0;
 #pragma unroll
   for (int i = 0; i < Gp::KNW; ++i) st.k[i] = 0u;
   st.sk = 0.0f; st.zk = 0.0f; st.sv = 0.0f; st.zv = 0.0f;
   if (row >= 0) {
-    load_bytes<Gp::KNW * 4>(st.k, p.k_codes + (int64_t)row * Gp::P + qd * (Gp::KNW * 4));
-    if (qd == 0) {
+    if constexpr (INL) {
+      // 4-byte aligned rows; the stored scale st at byte P, zero point = its
+      // low 4 bits (z = -zp st)
+      const uint8_t* kr8 = p.k_codes + (int64_t)row * RS;
+      load_bytes_a4<Gp::KNW * 4>(st.k, kr8 + qd * (Gp::KNW * 4));
+      if (qd == 0) {
+        const uint32_t kb = *reinterpret_cast<const uint32_t*>(kr8 + Gp::P);
+        const uint32_t vb = *reinterpret_cast<const uint32_t*>(p.v_codes + (int64_t)row * RS + Gp::P);
+        st.sk = __uint_as_float(kb);
+        st.zk = -(float)(kb & 0xFu) * st.sk;
+        st.sv = __uint_as_float(vb);
+        st.zv = -(float)(vb & 0xFu) * st.sv;
+      }
+    } else {
+      load_bytes<Gp::KNW * 4>(st.k, p.k_codes + (int64_t)row * Gp::P + qd * (Gp::KNW * 4));
+    }
+    if (qd == 0 && !INL) {
       if constexpr (Gp::M == 0) {   // per-channel INT8: scales live in the query and the output
         st.sk = 1.0f;
         st.sv = 1.0f;
@@ -171,13 +193,14 @@ __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillPara
   const int j0 = tau * kPKeys + 4 * kq;
   // the four positions share a block (block sizes are >= 16)
   const KeyRange all = {0, kr.khi, 0};
-  const int vrow0 = plane_row(trow, j0, all, p.block_size_log2, p.hkv, h, nblk);
+  const int vrow0 = plane_row<INL>(trow, j0, all, p.block_size_log2, p.hkv, h, nblk);
+  const int vstep = INL ? p.hkv : 1;   // rows between consecutive positions
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int w = 0; w < Gp::VNW; ++w) st.v[i][w] = 0u;
     if (vrow0 >= 0 && key_seen(kr, j0 + i))
-      load_bytes<Gp::VNB>(st.v[i], p.v_codes + (int64_t)(vrow0 + i) * Gp::P + wd * Gp::VNB);
+      load_bytes<Gp::VNB>(st.v[i], p.v_codes + (int64_t)(vrow0 + i * vstep) * RS + wd * Gp::VNB);
   }
 }
 
@@ -188,7 +211,7 @@ __device__ __forceinline__ void stage_store(const Stage<MODE, D>& st, PBuf<MODE,
   const int n = tid >> 2, qd = tid & 3;
   // K: int8 codes, k-slot order
   uint32_t kc[Gp::DC / 4];
-  if constexpr (MODE == 1) {
+  if constexpr (code_mode(MODE) == 1) {
 #pragma unroll
     for (int i = 0; i < Gp::KNW; ++i) {
       kc[i] = st.k[i] & 0x0F0F0F0Fu;
@@ -251,7 +274,8 @@ __device__ __forceinline__ void stage_store(const Stage<MODE, D>& st, PBuf<MODE,
 #pragma unroll
       for (int pl = 0; pl < NPL; ++pl) {
         const uint32_t x = BITS == 8 ? (st.v[i][w] ^ 0x80808080u)
-                                     : ((st.v[i][w] >> (BITS * pl)) & (MODE == 1 ? 0x0F0F0F0Fu : 0x03030303u));
+                                     : ((st.v[i][w] >> (BITS * pl)) &
+                                        (code_mode(MODE) == 1 ? 0x0F0F0F0Fu : 0x03030303u));
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int e = (32 / BITS) * w + NPL * bb + pl;
@@ -598,7 +622,9 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int db = 0; db <= Gp::DB; ++db) wc.o[rb][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  wc.W = W; wc.wave_live = wave_live; wc.wpos_lo = wpos_lo; wc.wpos_hi = wpos_hi; wc.sink = sinkE;
+  // the rows' masks take the whole sink range: a later row's window starts
+  // after klo, so positions in [min(sink, klo), sink) are sinks for it
+  wc.W = W; wc.wave_live = wave_live; wc.wpos_lo = wpos_lo; wc.wpos_hi = wpos_hi; wc.sink = W > 0 ? p.sink : 0;
   wc.lane = lane; wc.r = r; wc.q = q;
 
   // two tiles per iteration so that each buffer's LDS offsets are constants
@@ -669,6 +695,8 @@ hipError_t launch_prefill(int mode, int d, bool rot, const PrefillParams& p, hip
   KVQ_PREFILL_CASE(1, 128)
   KVQ_PREFILL_CASE(2, 64)
   KVQ_PREFILL_CASE(2, 128)
+  KVQ_PREFILL_CASE(kInlineMode, 64)
+  KVQ_PREFILL_CASE(kInlineMode, 128)
 #undef KVQ_PREFILL_CASE
   // per-channel INT8 has no rotation (checked on the host)
   if (mode == kChannelMode && d == 64) return launch_prefill_t<kChannelMode, 64, false>(p, s);

@@ -4,8 +4,8 @@ against the oracle: the written tensor byte for byte without rotation (with
 rotation at most 0.01 % of codes one step off and stored scales within 1e-6
 relative), rows no slot names untouched; decode and the fused step within
 max-abs 2e-3 / mean-abs 2e-4 over tables, windows, head-wise rows and
-evicted blocks; the gather within float32 rounding; chunked prefill
-refused."""
+evicted blocks, and chunked prefill likewise; the gather within float32
+rounding."""
 import numpy as np
 import pytest
 import torch
@@ -117,10 +117,9 @@ def test_inline_fused_step_matches_write_then_decode():
     gh.assert_close(out_b.cpu().numpy(), ref, "inline fused step")
 
 
-def test_inline_degenerate_rows_and_prefill_refused():
+def test_inline_degenerate_rows():
     """Zero rows store st = 0 and codes 0; one-signed rows get zp 0 or 15;
-    the HIP bytes equal the oracle's.  Chunked prefill returns
-    KVQ_EUNSUPPORTED."""
+    the HIP bytes equal the oracle's."""
     spec = synth.small_spec(name="inl-degenerate", cfg=890, mode=5, rotate=False, D=64, bs=16, B=1, Hkv=2,
                             Hq=4, lens=[48])
     case = synth.make_case(spec, gh.dev())
@@ -140,7 +139,41 @@ def test_inline_degenerate_rows_and_prefill_refused():
             assert np.all(st == 0) and not got[blk, kv, off, :, :P].any()
         else:
             assert np.all(st & 0xF == want), (t, kv, st)
-    q, cu = gh.prefill_inputs(spec, [8])
-    with pytest.raises(kvq.KvqError) as e:
-        gh.gpu_prefill(spec, case, d, planes, q, cu)
-    assert "INLINE" in str(e.value)
+
+
+PREFILL = [synth.small_spec(name=f"inl-pre-d{D}-r{int(rot)}-b{bs}-g{G}", cfg=895 + D // 64 + 2 * rot + G, mode=5,
+                            D=D, rotate=rot, bs=bs, B=3, Hkv=2, Hq=2 * G, lens=[300, 45, 1000])
+           for D, rot, bs, G in ((128, True, 64, 4), (64, False, 16, 1), (128, False, 16, 5), (64, True, 64, 16))]
+
+
+@pytest.mark.parametrize("spec", PREFILL, ids=lambda s: s.name)
+def test_inline_prefill(spec):
+    """Chunked prefill over the inline cache: the last 50 positions of every
+    sequence (fewer for short ones) against the oracle."""
+    print(f"[case] inline prefill {spec.name}", flush=True)
+    case, d, planes = gh.build(spec)
+    got = planes[0].cpu().numpy()
+    n_new = [min(50, int(L)) for L in gh.host(case.seq_lens)]
+    q, cu = gh.prefill_inputs(spec, n_new, stream=66)
+    out = gh.gpu_prefill(spec, case, d, planes, q, cu)
+    torch.cuda.synchronize()
+    ref = gh.oracle_prefill(spec, case, [got, None, None, None], q, cu)
+    gh.assert_close(out.cpu().numpy(), ref, f"{spec.name} prefill")
+
+
+def test_inline_prefill_windows_headwise():
+    spec = synth.small_spec(name="inl-pre-swa", cfg=899, mode=5, rotate=True, B=3, Hkv=4, Hq=16,
+                            lens=[300, 1000, 129], window=[128, 0, 256, 0], headwise=True,
+                            evict_outside_window=True)
+    case, d, planes = gh.build(spec)
+    got = planes[0].cpu().numpy()
+    q, cu = gh.prefill_inputs(spec, [40, 64, 1], stream=67)
+    for sink in (0, 16):
+        out = gh.gpu_prefill(spec, case, d, planes, q, cu, sink_size=sink)
+        torch.cuda.synchronize()
+        bt, bth, sl = gh.prefill_tables(case, 3)
+        ref = oracle.prefill_attention(gh.f32(q), gh.host(cu), gh.host(sl), 5, spec.D, spec.bs, spec.Hkv, got, None,
+                                       None, None, case.softmax_scale, signs=gh.host(case.rot_signs),
+                                       block_tables_headwise=gh.host(bth), window=gh.host(case.window),
+                                       sink_size=sink)
+        gh.assert_close(out.cpu().numpy(), ref, f"inline prefill windows sink {sink}")

@@ -82,3 +82,23 @@ def test_sink_zero_is_window_only_bitexact():
     e = gh.gpu_decode(spec, case, d, planes)
     torch.cuda.synchronize()
     gh.assert_close(c.cpu().numpy(), e.cpu().numpy().astype(np.float64), "sink >= L")
+
+
+def test_sinks_overlapping_window_starts_in_prefill():
+    """Chunks whose rows' window starts straddle the sink range: the earliest
+    row's window starts inside [0, sink) or at 0, and later rows' starts move
+    past it, so positions between a row's window start and the sink end are
+    seen only as sinks (two query tiles per sequence; windows 256 and 128)."""
+    spec = synth.small_spec(name="sinks-straddle", cfg=795, mode=1, rotate=True, B=3, Hkv=4, Hq=16,
+                            lens=[300, 330, 160], window=[256, 0, 128, 300])
+    case, d, planes = gh.build(spec)
+    hp = gh.host_planes(planes)
+    q, cu = gh.prefill_inputs(spec, [40, 64, 50], stream=68)
+    for sink in (16, 40, 100):
+        outp = gh.gpu_prefill(spec, case, d, planes, q, cu, sink_size=sink)
+        torch.cuda.synchronize()
+        bt, bth, sl = gh.prefill_tables(case, 3)
+        refp = oracle.prefill_attention(gh.f32(q), gh.host(cu), gh.host(sl), spec.mode, spec.D, spec.bs, spec.Hkv,
+                                        *hp, case.softmax_scale, signs=gh.host(case.rot_signs),
+                                        block_tables=gh.host(bt), window=gh.host(case.window), sink_size=sink)
+        gh.assert_close(outp.cpu().numpy(), refp, f"straddling sinks {sink}")
