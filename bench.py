@@ -739,7 +739,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--repeats", type=int, default=5, help="timed regions of `steps` steps (median reported)")
-    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", default="4",
+                    help="workload: 1..5, or config:variant (variants: fp8, chan, inline; one-layer decode configs)")
     ap.add_argument("--subs", default=None,
                     help="comma-separated workloads reported as sub-objects, a config or config:variant "
                          "(variants: fp8, chan, inline); default 2,3,5,2:fp8,2:chan,3:inline with --config 4; "
@@ -772,7 +773,7 @@ def main():
         return
 
     if args.subs is None:
-        subs = ["2", "3", "5", "2:fp8", "2:chan", "3:inline"] if args.config == 4 else []
+        subs = ["2", "3", "5", "2:fp8", "2:chan", "3:inline"] if args.config == "4" else []
     elif args.subs in ("", "none"):
         subs = []
     else:
