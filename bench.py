@@ -416,6 +416,7 @@ def cpu_baseline(spec, case, planes, seconds):
     tw = time.perf_counter() - tw0
     pairs = [n for _, n in runs_all]
     return {"value": round(med_all, 4), "unit": "GB/s", "cores": int(all_threads), "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)),
             "sample": f"(sequence, kv head) decode pairs of one layer's cache, {seconds:.0f} s per run "
                       f"({min(pairs)}-{max(pairs)} pairs of {spec.B * spec.Hkv}), float64 attention over the "
                       f"GPU's stored planes; median of 3 runs",

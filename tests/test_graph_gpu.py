@@ -12,7 +12,7 @@ from tests import gpu_helpers as gh
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2, 4, 5])
 def test_step_graph_replays_match_eager(mode):
     spec = synth.small_spec(name=f"graph-m{mode}", cfg=480 + mode, mode=mode, rotate=mode != 0, B=6, Hkv=2, Hq=8,
                             lens=[1, 70, 300, 1000, 2049, 4000])

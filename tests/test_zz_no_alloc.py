@@ -26,7 +26,8 @@ def _sub_case(case, spec, nseq):
     return sub, c
 
 
-@pytest.mark.parametrize("mode,rotate,headwise", [(1, True, False), (0, False, True), (2, True, False)])
+@pytest.mark.parametrize("mode,rotate,headwise", [(1, True, False), (0, False, True), (2, True, False),
+                                                   (4, True, False), (5, True, True)])
 def test_noalloc_matches_decode_twice(mode, rotate, headwise):
     spec = synth.small_spec(name=f"noalloc-m{mode}", cfg=760 + mode, mode=mode, rotate=rotate, B=5, Hkv=2, Hq=8,
                             lens=[700, 1, 2100, 64, 333], headwise=headwise)
