@@ -54,8 +54,10 @@
  *  low nibble of byte j; INT2 puts element 4j+k in bits 2k..2k+1 of byte j;
  *  INT8 stores two's complement codes in [-127, 127]; FP8 one E4M3 byte per
  *  element.  Reconstruction:
- *  x_hat = c*s (INT8) or c*s + z (INT4/INT2), in the rotated basis when the
- *  cache has a rotation.
+ *  x_hat = c*s (INT8), c*s + z (INT4/INT2), E4M3(c)*s (FP8), c*s_d
+ *  (INT8_CHANNEL), in the rotated basis when the cache has a rotation.
+ *  KVQ_INT4_INLINE keeps codes and scale in one tensor instead (see kvq_mode):
+ *  x_hat = (c - zp)*st.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -358,7 +360,8 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc,
  *   workspace    (device) kvq_prefill_workspace_size bytes; may be NULL when
  *                that size is 0 (it is for every shape this library builds:
  *                each workgroup covers the whole key range of its rows)
- * GQA groups up to 128.  One kernel launch. */
+ * GQA groups up to 128.  One kernel launch.  KVQ_FP8_E4M3 returns
+ * KVQ_EUNSUPPORTED (not built; kvq_gather_dequant gives its dense rows). */
 kvq_status kvq_paged_prefill_attention(const kvq_cache_desc* desc,
                                        void* out, int32_t out_dtype,
                                        const void* query,
