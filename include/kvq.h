@@ -166,13 +166,15 @@ kvq_status kvq_query_layout(const kvq_cache_desc* desc, kvq_layout* out /* host 
  * slot_mapping_headwise[t*Hkv + h]): block = slot / block_size,
  * offset = slot % block_size.  A negative slot skips the row.
  *   key, value       (device) bf16, row (t, h) at t*tok_stride + h*D elements
- *   *_tok_stride     elements between consecutive tokens, >= Hkv*D
+ *   *_tok_stride     elements between consecutive tokens, >= Hkv*D, a
+ *                    multiple of 8 and below 2^31 (KVQ_EUNSUPPORTED past it)
  *   slot_mapping     (device) int64 [num_tokens], or NULL
  *   slot_mapping_headwise (device) int64 [num_tokens, Hkv], or NULL;
  *                    exactly one of the two slot mappings is non-NULL
  *                    (num_tokens == 0 is a no-op that reads no argument)
  *   k_codes, v_codes (device) uint8 planes; k_meta, v_meta (device) float32
- * Two tokens mapped to the same (slot, head) in one call race. */
+ * Two tokens mapped to the same (slot, head) in one call race.  One call
+ * writes at most 2^31 rows (2 * num_tokens * Hkv; KVQ_EUNSUPPORTED past it). */
 kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc,
                                  const void* key, const void* value,
                                  int64_t key_tok_stride, int64_t value_tok_stride,

@@ -43,8 +43,10 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
   const int hkv = p.hkv;
   const int c0 = p.cu[b];
   const int n = min(p.cu[b + 1] - c0, p.max_blocks << p.block_size_log2);
-  const int64_t rows = (int64_t)n * hkv * 2;
-  const int64_t r0 = (int64_t)blockIdx.x * RPB * kGatherIter + (threadIdx.x >> 6) * RPW + lane / LPR;
+  // row, table and output indices stay below 2^31 (checked on the host), so
+  // the index math is 32-bit and each address one 32 x 32 -> 64-bit product
+  const int rows = n * hkv * 2;
+  const int r0 = blockIdx.x * RPB * kGatherIter + (threadIdx.x >> 6) * RPW + lane / LPR;
   if (r0 >= rows) return;
 
   // the lane's rotation signs, read before any store (so not reloaded per row)
@@ -58,15 +60,15 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
   uint32_t raw[kGatherIter][BPL >= 4 ? BPL / 4 : 1];
   float s[kGatherIter], z[kGatherIter];
   bool present[kGatherIter];
-  int64_t orow[kGatherIter];
+  int orow[kGatherIter];
   int hh[kGatherIter], kvs[kGatherIter];
   // r = pos * 2 Hkv + 2 h + kv: one division for the first row, then steps
   // of RPB rows
-  int pos = (int)(r0 / (2 * hkv));
-  int rem = (int)(r0 - (int64_t)pos * 2 * hkv);
+  int pos = r0 / (2 * hkv);
+  int rem = r0 - pos * 2 * hkv;
 #pragma unroll
   for (int it = 0; it < kGatherIter; ++it) {
-    const int64_t r = r0 + (int64_t)it * RPB;
+    const int r = r0 + it * RPB;
     if (it > 0) {
       rem += RPB;
       while (rem >= 2 * hkv) {
@@ -78,21 +80,21 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
     const int h = rem >> 1, kv = rem & 1;
     hh[it] = h;
     kvs[it] = kv;
-    orow[it] = in ? (int64_t)c0 + pos : -1;
+    orow[it] = in ? c0 + pos : -1;
     int id = -1;
     if (in) {
-      const int32_t* trow = p.tables + (int64_t)(p.headwise ? b * hkv + h : b) * p.max_blocks;
+      const int32_t* trow = p.tables + (uint32_t)(p.headwise ? b * hkv + h : b) * (uint32_t)p.max_blocks;
       id = trow[pos >> p.block_size_log2];
     }
     present[it] = in && id >= 0 && id < p.num_blocks && orow[it] < p.total_tokens;
-    const int64_t pin = pos & ((1 << p.block_size_log2) - 1);
+    const uint32_t pin = pos & ((1 << p.block_size_log2) - 1);
     // plane row (id Hkv + h) bs + offset; inline row (id 2 bs + offset) Hkv + h
-    const int64_t src = !present[it] ? 0
-                        : MODE == kInlineMode ? ((((int64_t)id << (p.block_size_log2 + 1)) + pin) * hkv + h)
-                                              : ((((int64_t)id * hkv + h) << p.block_size_log2) + pin);
-    const uint8_t* codes = (kv ? p.v_codes : p.k_codes) + src * (MODE == kInlineMode ? inline_row_bytes(D) : P) +
-                           lr * BPL;
-    const float* meta = (kv ? p.v_meta : p.k_meta) + src * M;   // unused when M == 0
+    const uint32_t src = !present[it] ? 0u
+                         : MODE == kInlineMode ? ((((uint32_t)id << (p.block_size_log2 + 1)) + pin) * hkv + h)
+                                               : ((((uint32_t)id * hkv + h) << p.block_size_log2) + pin);
+    const uint8_t* codes = (kv ? p.v_codes : p.k_codes) +
+                           (uint64_t)src * (MODE == kInlineMode ? inline_row_bytes(D) : P) + lr * BPL;
+    const float* meta = (kv ? p.v_meta : p.k_meta) + (uint64_t)src * M;   // unused when M == 0
     if (present[it]) {
       load_bytes<BPL>(raw[it], codes);
       if constexpr (MODE == kInlineMode) {   // stored scale st; zero point = its low 4 bits
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = x[i] * sg[i] * p.inv_sqrt_d;
     }
-    const int64_t e0 = (orow[it] * hkv + hh[it]) * D + lr * 8;
+    const uint64_t e0 = (uint64_t)(uint32_t)(orow[it] * hkv + hh[it]) * D + lr * 8;
     void* out = kvs[it] ? p.v_out : p.k_out;
     if constexpr (BF16) {
       uint4 w;

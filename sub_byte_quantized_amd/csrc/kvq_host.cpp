@@ -374,6 +374,10 @@ kvq_status kvq_reshape_and_cache(const kvq_cache_desc* desc, const void* key, co
                   (long long)key_tok_stride, (long long)value_tok_stride, H * D);
     if (key_tok_stride % 8 != 0 || value_tok_stride % 8 != 0 || !aligned(key, 16) || !aligned(value, 16))
       return fail(KVQ_EINVAL, "key/value must be 16-byte aligned with token strides a multiple of 8");
+    if (key_tok_stride > 0x7fffffffLL || value_tok_stride > 0x7fffffffLL)
+      return fail(KVQ_EUNSUPPORTED, "token strides must stay below 2^31 elements");
+    if (2LL * num_tokens * H > 0x7fffffffLL)
+      return fail(KVQ_EUNSUPPORTED, "2*num_tokens*num_kv_heads rows must stay below 2^31 per call");
   }
   kvq::WriteParams p{};
   p.key = static_cast<const uint16_t*>(key);
@@ -416,6 +420,10 @@ kvq_status kvq_calibrate_channel_scales(const kvq_cache_desc* desc, const void* 
                   (long long)key_tok_stride, (long long)value_tok_stride, H * D);
     if (key_tok_stride % 8 != 0 || value_tok_stride % 8 != 0 || !aligned(key, 16) || !aligned(value, 16))
       return fail(KVQ_EINVAL, "key/value must be 16-byte aligned with token strides a multiple of 8");
+    if (key_tok_stride > 0x7fffffffLL || value_tok_stride > 0x7fffffffLL)
+      return fail(KVQ_EUNSUPPORTED, "token strides must stay below 2^31 elements");
+    if (2LL * num_tokens * H > 0x7fffffffLL)
+      return fail(KVQ_EUNSUPPORTED, "2*num_tokens*num_kv_heads rows must stay below 2^31 per call");
   }
   kvq::WriteParams p{};
   p.key = static_cast<const uint16_t*>(key);
@@ -500,6 +508,8 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* out, int32_t out_dt
                   (long long)key_tok_stride, (long long)value_tok_stride, H * D);
     if (key_tok_stride % 8 != 0 || value_tok_stride % 8 != 0 || !aligned(key, 16) || !aligned(value, 16))
       return fail(KVQ_EINVAL, "key/value must be 16-byte aligned with token strides a multiple of 8");
+    if (key_tok_stride > 0x7fffffffLL || value_tok_stride > 0x7fffffffLL)
+      return fail(KVQ_EUNSUPPORTED, "token strides must stay below 2^31 elements");
   }
   kvq::WriteParams w{};
   w.key = static_cast<const uint16_t*>(key);
@@ -617,8 +627,13 @@ kvq_status kvq_gather_dequant(const kvq_cache_desc* desc, void* key_out, void* v
                         kvq::gather_rows_per_workgroup(desc->head_dim) - 1) /
                        kvq::gather_rows_per_workgroup(desc->head_dim);
   if (gx > 0x7fffffffLL) return fail(KVQ_EUNSUPPORTED, "gather grid of %lld workgroups per sequence", gx);
-  if ((long long)total_tokens * desc->num_kv_heads * desc->head_dim > (1LL << 40))
-    return fail(KVQ_EUNSUPPORTED, "outputs of %lld rows are too large", (long long)total_tokens);
+  if ((long long)total_tokens * desc->num_kv_heads > 0x7fffffffLL)
+    return fail(KVQ_EUNSUPPORTED, "outputs of %lld rows are too large (total_tokens*num_kv_heads must stay below "
+                "2^31)", (long long)total_tokens);
+  if ((long long)max_blocks_per_seq * desc->block_size * desc->num_kv_heads * 2 > 0x7fffffffLL ||
+      (long long)num_seqs * desc->num_kv_heads * max_blocks_per_seq > 0x7fffffffLL)
+    return fail(KVQ_EUNSUPPORTED, "block tables of %d x %d entries are too large for one gather", num_seqs,
+                max_blocks_per_seq);
   if (num_seqs == 0 || total_tokens == 0 || max_seq_len == 0) return ok();
   if (!key_out || !value_out || !cu_seq_lens) return fail(KVQ_EINVAL, "key_out, value_out or cu_seq_lens is NULL");
   if (!aligned(key_out, 16) || !aligned(value_out, 16))

@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
 
   const int lane = threadIdx.x & 63;
   const int lr = lane & (LPR - 1);
-  const int64_t row0 = (int64_t)blockIdx.x * RPB * kWriteIter + (threadIdx.x >> 6) * RPW + lane / LPR;
+  // rows, tokens and slot-map indices stay below 2^31 (checked on the host)
+  const int row0 = blockIdx.x * RPB * kWriteIter + (threadIdx.x >> 6) * RPW + lane / LPR;
   const int hkv = p.hkv;
 
   float sg[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
@@ -51,11 +52,11 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
   int hs[kWriteIter];
   // row = t * 2 Hkv + 2 h + kv: one division for the first row, then steps
   // of RPB rows
-  int64_t t = row0 / (2 * hkv);
-  int rem = (int)(row0 - t * 2 * hkv);
+  int t = row0 / (2 * hkv);
+  int rem = row0 - t * 2 * hkv;
 #pragma unroll
   for (int it = 0; it < kWriteIter; ++it) {
-    const int64_t row = row0 + (int64_t)it * RPB;
+    const int row = row0 + it * RPB;
     if (it > 0) {
       rem += RPB;
       while (rem >= 2 * hkv) {
@@ -69,12 +70,12 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
     raw[it] = make_uint4(0, 0, 0, 0);
     if (row < p.total_rows) {
       slot[it] = p.slot_hw ? p.slot_hw[t * hkv + h] : p.slot[t];
-      raw[it] = write_row_load<D>(p, t, h, rem & 1, lr);
+      raw[it] = write_row_load<D, true>(p, t, h, rem & 1, lr);
     }
   }
 #pragma unroll
   for (int it = 0; it < kWriteIter; ++it)
-    write_row_store<MODE, D, ROT>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, slot[it], lr);
+    write_row_store<MODE, D, ROT, true>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, slot[it], lr);
 }
 
 // Per-channel scales of a first batch (dynamic per-channel INT8, the

@@ -18,9 +18,17 @@ namespace kvq {
 namespace {
 
 // The lane's 8 bf16 elements of row (token t, kv head h, K if kv = 0 else
-// V): one 16-byte load.
-template <int D>
+// V): one 16-byte load.  I32: tokens and strides are below 2^31 (checked on
+// the host for the write kernel), so the token offset is one 32 x 32 ->
+// 64-bit multiply.  The fused decode step keeps the 64-bit form, whose
+// register use the decode kernel's allocation is tuned around.
+template <int D, bool I32 = false>
 __device__ __forceinline__ uint4 write_row_load(const WriteParams& p, int64_t t, int h, int kv, int lr) {
+  if constexpr (I32) {
+    const uint64_t tt = (uint32_t)t;
+    const uint16_t* src = kv ? p.value + tt * (uint32_t)p.value_stride : p.key + tt * (uint32_t)p.key_stride;
+    return *reinterpret_cast<const uint4*>(src + (uint32_t)(h * D + lr * 8));
+  }
   const uint16_t* src = kv ? p.value + t * p.value_stride : p.key + t * p.key_stride;
   return *reinterpret_cast<const uint4*>(src + (int64_t)h * D + lr * 8);
 }
@@ -36,7 +44,7 @@ __device__ __forceinline__ void write_row_signs(const WriteParams& p, int lr, fl
 
 // Everything after the load: rotation (lane signs sg), scale (and zero),
 // codes, packed and paged stores of the row whose lane elements `raw` holds.
-template <int MODE, int D, bool ROT>
+template <int MODE, int D, bool ROT, bool I32 = false>
 __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw, const float (&sg)[8], int h, int kv,
                                                 int64_t slot, int lr) {
 #pragma clang fp contract(off)
@@ -178,14 +186,20 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   }
 
   if (!active) return;
-  // block_size is a power of two (checked on the host)
+  // block_size is a power of two (checked on the host); an active slot is
+  // below num_blocks * block_size and every row index below 2^31 (host
+  // check), so with I32 the index math is 32-bit
   const int bsl = __builtin_ctz((unsigned)p.block_size);
   const int64_t blk = slot >> bsl;
   const int64_t off = slot & (p.block_size - 1);
+  const uint32_t blk32 = (uint32_t)slot >> bsl, off32 = (uint32_t)slot & (uint32_t)(p.block_size - 1);
   if constexpr (MODE == kInlineMode) {
     // row ((blk * 2 bs + off) Hkv + h) from the K or V base: nibbles, then
     // the stored scale
-    uint8_t* row = (kv ? p.v_codes : p.k_codes) + (((blk << (bsl + 1)) + off) * hkv + h) * inline_row_bytes(D);
+    uint8_t* row = (kv ? p.v_codes : p.k_codes) +
+                   (I32 ? (uint64_t)(((blk32 << (bsl + 1)) + off32) * (uint32_t)hkv + (uint32_t)h) *
+                              inline_row_bytes(D)
+                        : (((blk << (bsl + 1)) + off) * hkv + h) * inline_row_bytes(D));
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) w |= c[i] << (4 * i);
@@ -193,7 +207,8 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     if (lr == 0) *reinterpret_cast<uint32_t*>(row + P) = stbits;
     return;
   }
-  const int64_t ridx = (blk * hkv + h) * p.block_size + off;
+  const int64_t ridx = I32 ? (int64_t)(((blk32 * (uint32_t)hkv + (uint32_t)h) << bsl) + off32)
+                           : (blk * hkv + h) * p.block_size + off;
   uint8_t* codes = (kv ? p.v_codes : p.k_codes) + ridx * P + lr * BPL;
   float* meta = (kv ? p.v_meta : p.k_meta) + ridx * M;   // unused when M == 0
 
