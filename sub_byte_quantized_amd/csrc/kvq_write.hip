@@ -32,6 +32,7 @@ namespace kvq {
 namespace {
 
 constexpr int kWriteIter = 4;   // rows per lane group, their loads in flight together
+constexpr int kChanInvMax = 4096;   // per-channel reciprocals a workgroup keeps in LDS (2 Hkv D)
 
 template <int MODE, int D, bool ROT>
 __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
@@ -47,6 +48,22 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
 
   float sg[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (ROT) write_row_signs(p, lr, sg);
+  // per-channel INT8: the workgroup's rows span all (K or V, kv head)
+  // channels, so their correctly rounded reciprocals are computed once into
+  // LDS (when they fit) instead of once per row
+  const float* chinv = nullptr;
+  if constexpr (MODE == kChannelMode) {
+    __shared__ __align__(16) float inv_lds[kChanInvMax];
+    const int n = 2 * hkv * D;
+    if (n <= kChanInvMax) {
+      for (int i = threadIdx.x; i < n; i += 256) {
+        const float s = p.chs[i];
+        inv_lds[i] = s >= 1.17549435e-38f ? 1.0f / s : 0.0f;
+      }
+      __syncthreads();
+      chinv = inv_lds;
+    }
+  }
   int64_t slot[kWriteIter];
   uint4 raw[kWriteIter];
   int hs[kWriteIter];
@@ -75,7 +92,7 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
   }
 #pragma unroll
   for (int it = 0; it < kWriteIter; ++it)
-    write_row_store<MODE, D, ROT, true>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, slot[it], lr);
+    write_row_store<MODE, D, ROT, true>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, slot[it], lr, chinv);
 }
 
 // Per-channel scales of a first batch (dynamic per-channel INT8, the

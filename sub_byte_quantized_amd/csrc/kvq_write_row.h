@@ -46,7 +46,7 @@ __device__ __forceinline__ void write_row_signs(const WriteParams& p, int lr, fl
 // codes, packed and paged stores of the row whose lane elements `raw` holds.
 template <int MODE, int D, bool ROT, bool I32 = false>
 __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw, const float (&sg)[8], int h, int kv,
-                                                int64_t slot, int lr) {
+                                                int64_t slot, int lr, const float* chinv = nullptr) {
 #pragma clang fp contract(off)
   constexpr int LPR = D / 8;             // lanes per row
   constexpr int P = row_bytes(MODE, D);  // packed bytes per row
@@ -99,19 +99,30 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
 
   // per-channel INT8: fixed scales of the (K or V, kv head) channels, codes
   // clamp(rint(x * (1/s_d)), -127, 127), one correctly rounded reciprocal per
-  // channel; a zero or subnormal scale gives code 0; no row metadata
+  // channel (0 for a zero or subnormal scale, which gives code 0); no row
+  // metadata.  chinv: the reciprocals already in LDS ([2][Hkv][D]), else
+  // computed here
   uint32_t c[8];
   if constexpr (MODE == kChannelMode) {
-    const float* cs = p.chs + ((int64_t)kv * hkv + h) * D + lr * 8;
-    const float4 s0 = *reinterpret_cast<const float4*>(cs);
-    const float4 s1 = *reinterpret_cast<const float4*>(cs + 4);
-    const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    float inv[8];
+    if (chinv) {
+      const float* ci = chinv + (kv * hkv + h) * D + lr * 8;
+      const float4 i0 = *reinterpret_cast<const float4*>(ci);
+      const float4 i1 = *reinterpret_cast<const float4*>(ci + 4);
+      inv[0] = i0.x; inv[1] = i0.y; inv[2] = i0.z; inv[3] = i0.w;
+      inv[4] = i1.x; inv[5] = i1.y; inv[6] = i1.z; inv[7] = i1.w;
+    } else {
+      const float* cs = p.chs + ((int64_t)kv * hkv + h) * D + lr * 8;
+      const float4 s0 = *reinterpret_cast<const float4*>(cs);
+      const float4 s1 = *reinterpret_cast<const float4*>(cs + 4);
+      const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) inv[i] = sc[i] >= 1.17549435e-38f ? 1.0f / sc[i] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bool okc = sc[i] >= 1.17549435e-38f;
-      const float invc = okc ? 1.0f / sc[i] : 0.0f;
-      const float r = fminf(fmaxf(__builtin_rintf(x[i] * invc), -kLevels), kLevels);
-      c[i] = okc ? (uint32_t)(int32_t)r : 0u;
+      const float r = fminf(fmaxf(__builtin_rintf(x[i] * inv[i]), -kLevels), kLevels);
+      c[i] = inv[i] != 0.0f ? (uint32_t)(int32_t)r : 0u;   // 1/s of a normal scale is never 0
     }
   }
   float s = 0.0f, z = 0.0f;   // per-row scale and zero (not for per-channel INT8)
