@@ -724,7 +724,8 @@ def run_mixed(args, spec, dev, ceilings, headline):
                    "rows": g_tot * spec.Hkv * 2, "avg_launch_us": round(g_ms * 1e3, 2),
                    "algorithmic_bytes_per_launch": int(g_bytes),
                    "GBps": round(g_bytes / (g_ms * 1e-3) / 1e9, 2),
-                   "frac": round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                   "frac": round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "traffic": load_traffic(f"gather_{spec.name}_counters.json", GATHER_SRC)},
         "setup_s": round(setup_s, 1),
     }
     if headline and not args.no_cpu_baseline:
