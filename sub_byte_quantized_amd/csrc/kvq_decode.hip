@@ -662,35 +662,6 @@ constexpr int decode_wg_waves() { return mode_bits(MODE) != 8 ? 4 * decode_waves
 // Whole rows of D values, one row per wave: lane holds d = E*lane + e with
 // E = D/64.
 
-// In-register Sylvester FWHT of one row (natural order, unnormalized).  The
-// stages h = 1, 2, ..., D/2 run in that order: stage h maps the pair
-// (d, d + h), bit h of d clear, to (x_d + x_{d+h}, x_d - x_{d+h}); within the
-// lane for h < E, across lanes (lane ^ h/E) otherwise.
-template <int D>
-__device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane) {
-  constexpr int E = D / 64;
-  if constexpr (E == 2) {
-    const float a = x[0], b = x[1];
-    x[0] = a + b;
-    x[1] = a - b;
-  }
-#pragma unroll
-  for (int hl = 1; hl < 64; hl <<= 1) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float y = __shfl_xor(x[e], hl);
-      x[e] = (lane & hl) ? y - x[e] : x[e] + y;
-    }
-  }
-}
-
-// The lane's E bf16 values of a query row, as loaded (one dword or one short).
-template <int D>
-__device__ __forceinline__ uint32_t load_qrow(const uint16_t* src, int lane) {
-  if constexpr (D == 128) return reinterpret_cast<const uint32_t*>(src)[lane];
-  else return src[lane];
-}
-
 // One query row: q' = R q * scale * log2(e), then its three int8 pieces in
 // k-slot order (q' ~ (S/2^14)(2^14 a + 2^7 b + c), S = max|q'|/127,
 // |a| <= 127, |b|, |c| <= 64), sp = S/2^14 and q1r = sum(2^14 a + 2^7 b + c).

@@ -1,5 +1,6 @@
 // Device helpers shared by the libkvq HIP kernels (gfx950): MFMA wrappers,
-// cross-lane reductions, bf16 packing and raw byte loads.
+// cross-lane reductions, bf16 packing, raw byte loads and the in-register
+// query rotation.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -136,6 +137,35 @@ __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src) {
   } else {
     dst[0] = *src;
   }
+}
+
+// In-register Sylvester FWHT of one row (natural order, unnormalized).  The
+// stages h = 1, 2, ..., D/2 run in that order: stage h maps the pair
+// (d, d + h), bit h of d clear, to (x_d + x_{d+h}, x_d - x_{d+h}); within the
+// lane for h < E, across lanes (lane ^ h/E) otherwise.
+template <int D>
+__device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane) {
+  constexpr int E = D / 64;
+  if constexpr (E == 2) {
+    const float a = x[0], b = x[1];
+    x[0] = a + b;
+    x[1] = a - b;
+  }
+#pragma unroll
+  for (int hl = 1; hl < 64; hl <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float y = __shfl_xor(x[e], hl);
+      x[e] = (lane & hl) ? y - x[e] : x[e] + y;
+    }
+  }
+}
+
+// The lane's E bf16 values of a query row, as loaded (one dword or one short).
+template <int D>
+__device__ __forceinline__ uint32_t load_qrow(const uint16_t* src, int lane) {
+  if constexpr (D == 128) return reinterpret_cast<const uint32_t*>(src)[lane];
+  else return src[lane];
 }
 
 }  // namespace

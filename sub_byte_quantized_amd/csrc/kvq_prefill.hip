@@ -88,7 +88,7 @@ template <int MODE, int D>
 struct PBuf {
   using Gp = PGeo<MODE, D>;
   u32x4_t k[kPKeys][Gp::KROW / 16];    // int8 codes, k-slot order
-  u32x4_t vt[D + 16][Gp::VROW / 16];   // bf16 c, [d][position slot]; rows D..D+3: see stage_store
+  u32x4_t vt[D + 16][Gp::VROW / 16];   // bf16 c, [d][position slot]; rows D..D+3: see stage_part
   f32x4_t sk[kPKeys / 4];              // per position, four to a vector
   f32x4_t zk[kPKeys / 4];
   f32x4_t sv[kPKeys / 4];
@@ -113,6 +113,7 @@ struct Stage {
   uint32_t v[4][Gp::VNW];
   float sk, zk, sv, zv;
   int ok;
+  int kid, vid;   // block ids of the tile staged next (K position, V positions), read a tile ahead
 };
 
 // Plane row of position j of the walked table row, or -1 when no row of the
@@ -127,54 +128,65 @@ __device__ __forceinline__ bool key_seen(const KeyRange& kr, int j) {
   return j <= kr.khi && (j >= kr.klo || j < kr.sink);
 }
 
-// INL: the row of the inline layout, ((id 2 bs + offset) Hkv + h), read
-// from the K or the V base (consecutive positions are Hkv rows apart).
+// Plane row of position j in block `id` (-1: evicted, or at or past
+// num_blocks: no row).  INL: the row of the inline layout,
+// ((id 2 bs + offset) Hkv + h), read from the K or the V base (consecutive
+// positions are Hkv rows apart).
 template <bool INL>
-__device__ __forceinline__ int plane_row(const int32_t* trow, int j, const KeyRange& kr, int bs_log2, int hkv,
-                                         int h, int nblk) {
-  int id = -1;
-  if (key_seen(kr, j)) id = trow[j >> bs_log2];
+__device__ __forceinline__ int plane_row(int id, int j, int bs_log2, int hkv, int h, int nblk) {
   if (id < 0 || id >= nblk) return -1;
   const int pin = j & ((1 << bs_log2) - 1);
   return INL ? ((id << (bs_log2 + 1)) + pin) * hkv + h : ((id * hkv + h) << bs_log2) + pin;
 }
 
-// Global loads of key tile `tau` into registers.  Thread t stages K codes of
-// position t / 4, d-chunk t % 4 (and the meta of the position when t % 4 ==
-// 0) and V codes of positions 4 (t % 16) .. +3, d = DPT (t / 16) .. +DPT-1.
-// An absent position is not read: its codes stage as zeros and `ok` masks it
-// (score -inf, weight 0).
+// Block ids of key tile `tau` for this thread's K position t / 4 (-1 when no
+// row of the workgroup sees it) and V positions 4 (t % 16) .. +3 (one block:
+// block sizes are >= 16; -1 past khi).  They are read one tile ahead, so the
+// code loads of a tile never wait on the table.
 template <int MODE, int D>
-__device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillParams& p, const int32_t* trow,
-                                           int tau, const KeyRange& kr, int h, int tid) {
+__device__ __forceinline__ void stage_ids(Stage<MODE, D>& st, const int32_t* trow, int tau, const KeyRange& kr,
+                                          int bs_log2, int tid) {
+  const int j = tau * kPKeys + (tid >> 2), j0 = tau * kPKeys + 4 * (tid & 15);
+  st.kid = key_seen(kr, j) ? trow[j >> bs_log2] : -1;
+  st.vid = j0 <= kr.khi ? trow[j0 >> bs_log2] : -1;
+}
+
+// Global loads of key tile `tau` into registers, from the block ids
+// stage_ids read.  Thread t stages K codes of position t / 4, d-chunk t % 4,
+// the meta of that position and V codes of positions 4 (t % 16) .. +3,
+// d = DPT (t / 16) .. +DPT-1.  An absent position is not
+// read: its codes stage as zeros and `ok` masks it (score -inf, weight 0).
+template <int MODE, int D>
+__device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillParams& p, int tau, const KeyRange& kr,
+                                           int h, int tid) {
   using Gp = PGeo<MODE, D>;
   const int n = tid >> 2, qd = tid & 3;
   const int nblk = (int)p.num_blocks;   // < 2^31 (checked on the host)
   constexpr bool INL = MODE == kInlineMode;
   constexpr int RS = INL ? inline_row_bytes(D) : Gp::P;   // bytes between rows
-  const int row = plane_row<INL>(trow, tau * kPKeys + n, kr, p.block_size_log2, p.hkv, h, nblk);
+  const int row = plane_row<INL>(st.kid, tau * kPKeys + n, p.block_size_log2, p.hkv, h, nblk);
   st.ok = row >= 0;
 #pragma unroll
   for (int i = 0; i < Gp::KNW; ++i) st.k[i] = 0u;
   st.sk = 0.0f; st.zk = 0.0f; st.sv = 0.0f; st.zv = 0.0f;
   if (row >= 0) {
+    // the four lanes of a position all read its meta (one request per
+    // address): each stores one field of it, with no branch in the store
     if constexpr (INL) {
       // 4-byte aligned rows; the stored scale st at byte P, zero point = its
       // low 4 bits (z = -zp st)
       const uint8_t* kr8 = p.k_codes + (int64_t)row * RS;
       load_bytes_a4<Gp::KNW * 4>(st.k, kr8 + qd * (Gp::KNW * 4));
-      if (qd == 0) {
-        const uint32_t kb = *reinterpret_cast<const uint32_t*>(kr8 + Gp::P);
-        const uint32_t vb = *reinterpret_cast<const uint32_t*>(p.v_codes + (int64_t)row * RS + Gp::P);
-        st.sk = __uint_as_float(kb);
-        st.zk = -(float)(kb & 0xFu) * st.sk;
-        st.sv = __uint_as_float(vb);
-        st.zv = -(float)(vb & 0xFu) * st.sv;
-      }
+      const uint32_t kb = *reinterpret_cast<const uint32_t*>(kr8 + Gp::P);
+      const uint32_t vb = *reinterpret_cast<const uint32_t*>(p.v_codes + (int64_t)row * RS + Gp::P);
+      st.sk = __uint_as_float(kb);
+      st.zk = -(float)(kb & 0xFu) * st.sk;
+      st.sv = __uint_as_float(vb);
+      st.zv = -(float)(vb & 0xFu) * st.sv;
     } else {
       load_bytes<Gp::KNW * 4>(st.k, p.k_codes + (int64_t)row * Gp::P + qd * (Gp::KNW * 4));
     }
-    if (qd == 0 && !INL) {
+    if constexpr (!INL) {
       if constexpr (Gp::M == 0) {   // per-channel INT8: scales live in the query and the output
         st.sk = 1.0f;
         st.sv = 1.0f;
@@ -192,8 +204,7 @@ __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillPara
   const int kq = tid & 15, wd = tid >> 4;
   const int j0 = tau * kPKeys + 4 * kq;
   // the four positions share a block (block sizes are >= 16)
-  const KeyRange all = {0, kr.khi, 0};
-  const int vrow0 = plane_row<INL>(trow, j0, all, p.block_size_log2, p.hkv, h, nblk);
+  const int vrow0 = plane_row<INL>(st.vid, j0, p.block_size_log2, p.hkv, h, nblk);
   const int vstep = INL ? p.hkv : 1;   // rows between consecutive positions
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -204,89 +215,107 @@ __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillPara
   }
 }
 
-// Unpack the staged registers into LDS buffer `b`.
+// Unpacking the staged registers into LDS buffer `b` goes in parts that the
+// tile loop spreads between the MFMAs of the PV product (part 0: K codes,
+// parts 1 .. DPT: V^T columns, part DPT + 1: the per-position meta); none
+// branches.  Parts 1 .. DPT read the V codes through `vp`: INT4 keeps its
+// two nibble planes there, formed in part 0.
 template <int MODE, int D>
-__device__ __forceinline__ void stage_store(const Stage<MODE, D>& st, PBuf<MODE, D>& b, int tid) {
+struct VPlanes {
+  uint32_t x[4][2];
+};
+
+// V code of position 4 kq + i, d = DPT wd + e, as a float (exact).
+template <int MODE, int D>
+__device__ __forceinline__ float v_code(const Stage<MODE, D>& st, const VPlanes<MODE, D>& vp, int i, int e) {
+  if constexpr (code_mode(MODE) == 1) {   // byte b of plane pl: d = 2 b + pl
+    return (float)((vp.x[i][e & 1] >> (8 * (e >> 1))) & 0xffu);
+  } else if constexpr (MODE == 2) {       // byte b, crumb pl: d = 4 b + pl
+    return (float)((st.v[i][0] >> (8 * (e >> 2) + 2 * (e & 3))) & 3u);
+  } else {                                // INT8: byte e % 4 of word e / 4, signed
+    return (float)(int8_t)(st.v[i][e >> 2] >> (8 * (e & 3)));
+  }
+}
+
+template <int MODE, int D>
+__device__ __forceinline__ void stage_part(const Stage<MODE, D>& st, VPlanes<MODE, D>& vp, PBuf<MODE, D>& b,
+                                           int tid, int part) {
   using Gp = PGeo<MODE, D>;
   const int n = tid >> 2, qd = tid & 3;
-  // K: int8 codes, k-slot order
-  uint32_t kc[Gp::DC / 4];
-  if constexpr (code_mode(MODE) == 1) {
+  if (part == 0) {
+    // K: int8 codes, k-slot order
+    uint32_t kc[Gp::DC / 4];
+    if constexpr (code_mode(MODE) == 1) {
 #pragma unroll
-    for (int i = 0; i < Gp::KNW; ++i) {
-      kc[i] = st.k[i] & 0x0F0F0F0Fu;
-      kc[Gp::KNW + i] = (st.k[i] >> 4) & 0x0F0F0F0Fu;
+      for (int i = 0; i < Gp::KNW; ++i) {
+        kc[i] = st.k[i] & 0x0F0F0F0Fu;
+        kc[Gp::KNW + i] = (st.k[i] >> 4) & 0x0F0F0F0Fu;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vp.x[i][0] = st.v[i][0] & 0x0F0F0F0Fu;
+        vp.x[i][1] = (st.v[i][0] >> 4) & 0x0F0F0F0Fu;
+      }
+    } else if constexpr (MODE == 2) {
+#pragma unroll
+      for (int pl = 0; pl < 4; ++pl)
+#pragma unroll
+        for (int i = 0; i < Gp::KNW; ++i) kc[pl * Gp::KNW + i] = (st.k[i] >> (2 * pl)) & 0x03030303u;
+    } else {
+#pragma unroll
+      for (int i = 0; i < Gp::KNW; ++i) kc[i] = st.k[i];
     }
-  } else if constexpr (MODE == 2) {
 #pragma unroll
-    for (int pl = 0; pl < 4; ++pl)
-#pragma unroll
-      for (int i = 0; i < Gp::KNW; ++i) kc[pl * Gp::KNW + i] = (st.k[i] >> (2 * pl)) & 0x03030303u;
+    for (int i = 0; i < Gp::DC / 16; ++i)
+      b.k[n][qd * (Gp::DC / 16) + i] = u32x4_t{kc[4 * i], kc[4 * i + 1], kc[4 * i + 2], kc[4 * i + 3]};
+  } else if (part <= Gp::DPT) {
+    // V: positions 4 kq .. 4 kq + 3 -> slots of the PV operand order, as
+    // exact bf16 integers c (no offset: the accumulator then holds only the
+    // signal, whose fp32 rounding does not grow with an offset over long
+    // contexts)
+    const int e = part - 1;
+    const int kq = tid & 15, wd = tid >> 4;
+    const int kq7 = kq & 7;
+    const int slot = 32 * (kq >> 3) + 8 * (kq7 & 3) + 4 * (kq7 >> 2);
+    reinterpret_cast<uint2*>(&b.vt[Gp::DPT * wd + e][0])[slot >> 2] =
+        make_uint2(pack_exact(v_code(st, vp, 0, e), v_code(st, vp, 1, e)),
+                   pack_exact(v_code(st, vp, 2, e), v_code(st, vp, 3, e)));
   } else {
-#pragma unroll
-    for (int i = 0; i < Gp::KNW; ++i) kc[i] = st.k[i];
-  }
-#pragma unroll
-  for (int i = 0; i < Gp::DC / 16; ++i)
-    b.k[n][qd * (Gp::DC / 16) + i] = u32x4_t{kc[4 * i], kc[4 * i + 1], kc[4 * i + 2], kc[4 * i + 3]};
-  if (qd == 0) {
     // The PV product also yields the row sums l = sum p and Z = sum p z_V
     // through four extra V^T rows holding 1/s_V and z_V/s_V as bf16 hi + lo
-    // (W = p s_V).  s_V enters both as max(s_V, 2^-96): below that, the lo
-    // half of W would fall under bf16's subnormal range and W / s_V would
-    // carry up to 2^-8 of error into l.  A row with a zero or subnormal scale
-    // has all-zero codes, so any s_V reconstructs it; a row with a scale in
-    // [2^-126, 2^-96) has entries below 127 * 2^-96, and the clamp moves its
-    // share of the output by less than 2^-89 p.
+    // (W = p s_V); lane qd of a position writes row D + qd and one of its
+    // s_K, z_K, s_V, present flags.  s_V enters both as max(s_V, 2^-96):
+    // below that, the lo half of W would fall under bf16's subnormal range
+    // and W / s_V would carry up to 2^-8 of error into l.  A row with a zero
+    // or subnormal scale has all-zero codes, so any s_V reconstructs it; a
+    // row with a scale in [2^-126, 2^-96) has entries below 127 * 2^-96, and
+    // the clamp moves its share of the output by less than 2^-89 p.
     const float sv = fmaxf(st.sv, 0x1p-96f);
     const float u = st.ok ? __builtin_amdgcn_rcpf(sv) : 0.0f;
     const float t = st.ok ? st.zv * u : 0.0f;
-    const __bf16 uh = (__bf16)u, th = (__bf16)t;
-    const __bf16 ul = (__bf16)(u - (float)uh), tl = (__bf16)(t - (float)th);
+    const float val = qd < 2 ? u : t;
+    const __bf16 hi = (__bf16)val;
+    const __bf16 lo = (__bf16)(val - (float)hi);
     const int kq7 = (n >> 2) & 7;
     const int nslot = 32 * (n >> 5) + 8 * (kq7 & 3) + 4 * (kq7 >> 2) + (n & 3);
-    reinterpret_cast<__bf16*>(&b.vt[D + 0][0])[nslot] = uh;
-    reinterpret_cast<__bf16*>(&b.vt[D + 1][0])[nslot] = ul;
-    reinterpret_cast<__bf16*>(&b.vt[D + 2][0])[nslot] = th;
-    reinterpret_cast<__bf16*>(&b.vt[D + 3][0])[nslot] = tl;
-    b.sk[n >> 2][n & 3] = st.ok ? st.sk : 0.0f;
-    b.zk[n >> 2][n & 3] = st.ok ? st.zk : 0.0f;
-    b.sv[n >> 2][n & 3] = st.ok ? sv : 0.0f;
-    b.ok[n >> 2][n & 3] = st.ok;
+    reinterpret_cast<__bf16*>(&b.vt[D + qd][0])[nslot] = (qd & 1) ? lo : hi;
+    // sk, zk, sv and ok are consecutive arrays of kPKeys words
+    using PB = PBuf<MODE, D>;
+    static_assert(offsetof(PB, zk) == offsetof(PB, sk) + 4 * kPKeys &&
+                      offsetof(PB, sv) == offsetof(PB, sk) + 8 * kPKeys &&
+                      offsetof(PB, ok) == offsetof(PB, sk) + 12 * kPKeys,
+                  "per-position meta arrays must be consecutive");
+    const float f = qd == 0 ? st.sk : qd == 1 ? st.zk : sv;
+    reinterpret_cast<uint32_t*>(&b.sk[0])[qd * kPKeys + n] =
+        qd == 3 ? (uint32_t)st.ok : (st.ok ? __float_as_uint(f) : 0u);
   }
-  // V: positions 4 kq .. 4 kq + 3 -> slots of the PV operand order, as exact
-  // bf16 integers c (no offset: the accumulator then holds only the signal,
-  // whose fp32 rounding does not grow with an offset over long contexts)
-  const int kq = tid & 15, wd = tid >> 4;
-  const int kq7 = kq & 7;
-  const int slot = 32 * (kq >> 3) + 8 * (kq7 & 3) + 4 * (kq7 >> 2);
-  // codes into bytes, then one v_cvt_f32_ubyte per code: byte b of plane
-  // word pw[pl][w] holds the code of d = DPT*wd + e with (INT8) e = 4 w + b,
-  // (INT4) e = 8 w + 2 b + pl, (INT2) e = 16 w + 4 b + pl
-  constexpr int BITS = mode_bits(MODE);
-  constexpr int NPL = 8 / BITS;                       // code planes per byte
-  constexpr int NW = (Gp::DPT * BITS + 31) / 32;      // dwords per position
-  float c[4][Gp::DPT];
+}
+
+template <int MODE, int D>
+__device__ __forceinline__ void stage_store(const Stage<MODE, D>& st, PBuf<MODE, D>& b, int tid) {
+  VPlanes<MODE, D> vp;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int pl = 0; pl < NPL; ++pl) {
-        const uint32_t x = BITS == 8 ? (st.v[i][w] ^ 0x80808080u)
-                                     : ((st.v[i][w] >> (BITS * pl)) &
-                                        (code_mode(MODE) == 1 ? 0x0F0F0F0Fu : 0x03030303u));
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int e = (32 / BITS) * w + NPL * bb + pl;
-          if (e < Gp::DPT) c[i][e] = BITS == 8 ? (float)((x >> (8 * bb)) & 0xffu) - 128.0f
-                                               : (float)((x >> (8 * bb)) & 0xffu);
-        }
-      }
-#pragma unroll
-  for (int e = 0; e < Gp::DPT; ++e)
-    reinterpret_cast<uint2*>(&b.vt[Gp::DPT * wd + e][0])[slot >> 2] =
-        make_uint2(pack_exact(c[0][e], c[1][e]), pack_exact(c[2][e], c[3][e]));
+  for (int part = 0; part <= PGeo<MODE, D>::DPT + 1; ++part) stage_part<MODE, D>(st, vp, b, tid, part);
 }
 
 template <int MODE, int D>
@@ -308,11 +337,17 @@ struct WaveCtx {
 template <int MODE, int D, int PAR>
 __device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& wc, Stage<MODE, D>& stg,
                                           const PrefillParams& p, const int32_t* trow, int tau, int tau_next,
-                                          const KeyRange& kr, int h, int tid) {
+                                          int tau_next2, const KeyRange& kr, int h, int tid) {
   using Gp = PGeo<MODE, D>;
   const PBuf<MODE, D>& cb = sm.buf[PAR];
   const bool more = tau_next >= 0;
-  if (more) stage_load<MODE, D>(stg, p, trow, tau_next, kr, h, tid);
+  // the ids of tile tau_next2 are read only on the path that has consumed
+  // the previous ids (a write on a path that had not would make the compiler
+  // wait for every load in flight, this tile's codes included)
+  if (more) {
+    stage_load<MODE, D>(stg, p, tau_next, kr, h, tid);
+    if (tau_next2 >= 0) stage_ids<MODE, D>(stg, trow, tau_next2, kr, p.block_size_log2, tid);
+  }
   const int W = wc.W, r = wc.r, q = wc.q;
     const int pos0 = tau * kPKeys;
     const bool active = wc.wave_live && pos0 <= wc.wpos_hi &&
@@ -392,55 +427,65 @@ __device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& 
         }
       }
       // ---- p = 2^(logit - m), W = p s_V as bf16 hi + lo in PV A-operand
-      // order (slab s = positions 32 s .. 32 s + 31)
+      // order (slab s = positions 32 s .. 32 s + 31), and O += W V.  The
+      // MFMAs of slab 0 run while slab 1's weights are formed, and those of
+      // slab 1 while the next tile is unpacked into LDS: the source order
+      // below, fenced per d-block, is the issue order.  Every accumulator
+      // still sums slab 0's hi, lo, then slab 1's hi, lo.
+      float mu[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) mu[rb] = wc.m[rb] == kNegInf ? 0.0f : wc.m[rb];
       u32x4_t wh[2][2], wl[2][2];
+      // weights of positions 16 kb + 4 q + 2 h2 + {0, 1}, rows of block rb:
+      // hi = w with the low 16 bits cleared (exact bf16), lo = w - hi (exact
+      // in fp32) rounded to bf16: together 16 significant bits
+      auto wpair = [&](int kb, int rb, int h2) {
+        const f32x4_t svv = cb.sv[4 * kb + q];
+        const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][rb][2 * h2], wc.sp[rb], -mu[rb])) *
+                         svv[2 * h2];
+        const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][rb][2 * h2 + 1], wc.sp[rb], -mu[rb])) *
+                         svv[2 * h2 + 1];
+        const float t0 = __uint_as_float(__float_as_uint(w0) & 0xffff0000u);
+        const float t1 = __uint_as_float(__float_as_uint(w1) & 0xffff0000u);
+        const int s = kb >> 1, hf = 2 * (kb & 1) + h2;
+        wh[s][rb][hf] = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x07060302u);
+        wl[s][rb][hf] = pack_bf16(w0 - t0, w1 - t1);
+      };
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float mu = wc.m[rb] == kNegInf ? 0.0f : wc.m[rb];
+      for (int k = 0; k < 8; ++k) wpair(k >> 2, (k >> 1) & 1, k & 1);
+      constexpr int NST = Gp::DB + 1;   // d-blocks, one fenced step each
+      VPlanes<MODE, D> vp;
+      u32x4_t bv = cb.vt[r][q];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const f32x4_t svv = cb.sv[4 * kb + q];
-          float wv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            wv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][rb][i], wc.sp[rb], -mu)) * svv[i];
-          // hi = w with the low 16 bits cleared (exact bf16), lo = w - hi
-          // (exact in fp32) rounded to bf16: together 16 significant bits
-          float th[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) th[i] = __uint_as_float(__float_as_uint(wv[i]) & 0xffff0000u);
-          const int s = kb >> 1, hf = 2 * (kb & 1);
-          wh[s][rb][hf] = __builtin_amdgcn_perm(__float_as_uint(th[1]), __float_as_uint(th[0]), 0x07060302u);
-          wh[s][rb][hf + 1] = __builtin_amdgcn_perm(__float_as_uint(th[3]), __float_as_uint(th[2]), 0x07060302u);
-          wl[s][rb][hf] = pack_bf16(wv[0] - th[0], wv[1] - th[1]);
-          wl[s][rb][hf + 1] = pack_bf16(wv[2] - th[2], wv[3] - th[3]);
+      for (int st2 = 0; st2 < 2 * NST; ++st2) {
+        const int sl = st2 / NST, db = st2 % NST;
+        // the operand of the next step, read one step ahead
+        u32x4_t nb = bv;
+        if (st2 + 1 < 2 * NST) {
+          const int sl1 = (st2 + 1) / NST, db1 = (st2 + 1) % NST;
+          nb = cb.vt[16 * db1 + r][4 * sl1 + q];
         }
-      }
-      // ---- O += W V, V operands read one d-block ahead of their MFMAs
-      u32x4_t b0 = cb.vt[r][q], b1 = cb.vt[r][4 + q];
-#pragma unroll
-      for (int db = 0; db <= Gp::DB; ++db) {
-        u32x4_t n0 = b0, n1 = b1;
-        if (db < Gp::DB) {
-          n0 = cb.vt[16 * (db + 1) + r][q];
-          n1 = cb.vt[16 * (db + 1) + r][4 + q];
-        }
-        // keep the next operands' reads ahead of this block's MFMAs (the
-        // scheduler otherwise sinks them next to their use and exposes the
-        // LDS latency)
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          wc.o[rb][db] = mfma(wh[0][rb], b0, wc.o[rb][db]);
-          wc.o[rb][db] = mfma(wl[0][rb], b0, wc.o[rb][db]);
-          wc.o[rb][db] = mfma(wh[1][rb], b1, wc.o[rb][db]);
-          wc.o[rb][db] = mfma(wl[1][rb], b1, wc.o[rb][db]);
+          wc.o[rb][db] = mfma(wh[sl][rb], bv, wc.o[rb][db]);
+          wc.o[rb][db] = mfma(wl[sl][rb], bv, wc.o[rb][db]);
         }
-        b0 = n0;
-        b1 = n1;
+        if (sl == 0) {
+          // slab 1's eight weight pairs over the NST steps
+#pragma unroll
+          for (int k = db * 8 / NST; k < (db + 1) * 8 / NST; ++k) wpair(2 + (k >> 2), (k >> 1) & 1, k & 1);
+        } else {
+          // the next tile's LDS stores (stale data after the last tile, into
+          // the buffer no wave reads before the barrier)
+          stage_part<MODE, D>(stg, vp, sm.buf[PAR ^ 1], tid, db);
+          if (db == NST - 1) stage_part<MODE, D>(stg, vp, sm.buf[PAR ^ 1], tid, Gp::DPT + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bv = nb;
       }
+    } else if (more) {
+      stage_store<MODE, D>(stg, sm.buf[PAR ^ 1], tid);
     }
-  if (more) stage_store<MODE, D>(stg, sm.buf[PAR ^ 1], tid);
   __syncthreads();
 }
 
@@ -499,56 +544,71 @@ void prefill_kernel(PrefillParams p) {
   const int nwalk = (khi >= 0 ? min(ns_tiles, khi / kPKeys + 1) : 0) + nwin;
   const int nsw = nwalk - nwin;                               // sink tiles walked
   auto walk_tile = [&](int k) { return k < nsw ? k : tau0 + (k - nsw); };
-  if (nwalk > 0) stage_load<MODE, D>(stg, p, trow, walk_tile(0), kr, h, tid);
+  if (nwalk > 0) {
+    stage_ids<MODE, D>(stg, trow, walk_tile(0), kr, p.block_size_log2, tid);
+    stage_load<MODE, D>(stg, p, walk_tile(0), kr, h, tid);
+    if (nwalk > 1) stage_ids<MODE, D>(stg, trow, walk_tile(1), kr, p.block_size_log2, tid);
+  }
 
-  // ---- query prologue: rows (token t, head g) -> R q
-  for (int e = tid; e < kPRows * D; e += 64 * kPWaves) {
-    const int row = e / D, d = e - row * D;
-    float v = 0.0f;
-    if (row < nrows) {
-      const int t = row / G, g = row - t * G;
-      v = __uint_as_float((uint32_t)p.q[((int64_t)(q0 + tok0 + t) * p.hq + h * G + g) * D + d] << 16);
-      if constexpr (ROT) v *= p.signs[d];
-      if constexpr (MODE == kChannelMode) v *= p.chs[(int64_t)h * D + d];   // q . (c (.) s_K)
-    }
-    sm.qf[row][d] = v;
-  }
-  __syncthreads();
-  if constexpr (ROT) {
-    for (int hh = 1; hh < D; hh <<= 1) {
-      for (int e = tid; e < kPRows * (D / 2); e += 64 * kPWaves) {
-        const int g = e / (D / 2), k = e - g * (D / 2);
-        const int i = (k / hh) * 2 * hh + (k % hh);
-        const float a = sm.qf[g][i], c = sm.qf[g][i + hh];
-        sm.qf[g][i] = a + c;
-        sm.qf[g][i + hh] = a - c;
-      }
-      __syncthreads();
-    }
-  }
+  // ---- query prologue: each wave its 32 rows (token t, head g): one
+  // lane-contiguous load per row, all in flight together, then in registers
+  // q' = R q * qmul (Sylvester FWHT across the wave, stages h = 1 .. D/2 in
+  // order), its maximum |q'| and the sum of its pieces; q' goes to LDS for
+  // the B-operand gather below.  Lane l holds d = E l .. E l + E - 1.
+  constexpr int E = D / 64;
   const float qmul = ROT ? p.qscale * p.inv_sqrt_d : p.qscale;
-  // piece scale and represented sum per row (each wave its own 32 rows)
-  for (int i = 0; i < 32; ++i) {
-    const int row = 32 * wave + i;
-    float mx = 0.0f;
-    for (int d = lane; d < D; d += 64) mx = fmaxf(mx, fabsf(sm.qf[row][d] * qmul));
+  float sg[E], chk[E];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
-    float sq = 0.0f;
-    for (int d = lane; d < D; d += 64) {
-      const float t = fminf(fmaxf(sm.qf[row][d] * qmul * invS, -127.0f), 127.0f);
-      const float a = __builtin_rintf(t);
-      const float r1 = (t - a) * 128.0f;
-      const float b = __builtin_rintf(r1);
-      const float c = __builtin_rintf((r1 - b) * 128.0f);
-      sq += __builtin_fmaf(16384.0f, a, __builtin_fmaf(128.0f, b, c));   // each term exact (< 2^22)
+  for (int e = 0; e < E; ++e) {
+    sg[e] = ROT ? p.signs[E * lane + e] : 1.0f;
+    chk[e] = MODE == kChannelMode ? p.chs[(int64_t)h * D + E * lane + e] : 1.0f;   // q . (c (.) s_K)
+  }
+  {
+    uint32_t raw[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int row = 32 * wave + i;
+      const int t = row / G, g = row - t * G;
+      raw[i] = row < nrows ? load_qrow<D>(p.q + ((int64_t)(q0 + tok0 + t) * p.hq + h * G + g) * D, lane) : 0u;
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) sq += __shfl_xor(sq, m);
-    if (lane == 0) {
-      sm.rs[row] = mx;
-      sm.r1[row] = sq;
+    for (int i = 0; i < 32; ++i) {
+      const int row = 32 * wave + i;
+      float x[E];
+      x[0] = __uint_as_float(raw[i] << 16);
+      if constexpr (E == 2) x[1] = __uint_as_float(raw[i] & 0xffff0000u);
+      if constexpr (ROT) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] *= sg[e];
+        wave_fwht<D>(x, lane);
+      }
+      float mx = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if constexpr (MODE == kChannelMode) x[e] *= chk[e];
+        x[e] *= qmul;
+        mx = fmaxf(mx, fabsf(x[e]));
+        sm.qf[row][E * lane + e] = x[e];
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+      const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
+      float sq = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float tt = fminf(fmaxf(x[e] * invS, -127.0f), 127.0f);
+        const float a = __builtin_rintf(tt);
+        const float r1 = (tt - a) * 128.0f;
+        const float b = __builtin_rintf(r1);
+        const float c = __builtin_rintf((r1 - b) * 128.0f);
+        sq += __builtin_fmaf(16384.0f, a, __builtin_fmaf(128.0f, b, c));   // each term exact (< 2^22)
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) sq += __shfl_xor(sq, m);
+      if (lane == 0) {
+        sm.rs[row] = mx;
+        sm.r1[row] = sq;
+      }
     }
   }
   __syncthreads();
@@ -571,7 +631,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = kslot_d<MODE, D>(64 * ks + 16 * q + 4 * j4 + j);
-          const float t = fminf(fmaxf(sm.qf[row][d] * qmul * invS, -127.0f), 127.0f);
+          const float t = fminf(fmaxf(sm.qf[row][d] * invS, -127.0f), 127.0f);
           const float a = __builtin_rintf(t);
           const float r1 = (t - a) * 128.0f;
           const float b = __builtin_rintf(r1);
@@ -628,10 +688,11 @@ void prefill_kernel(PrefillParams p) {
   wc.lane = lane; wc.r = r; wc.q = q;
 
   // two tiles per iteration so that each buffer's LDS offsets are constants
+  auto walk_or_none = [&](int k) { return k < nwalk ? walk_tile(k) : -1; };
   for (int k = 0; k < nwalk; k += 2) {
-    tile_step<MODE, D, 0>(sm, wc, stg, p, trow, walk_tile(k), k + 1 < nwalk ? walk_tile(k + 1) : -1, kr, h, tid);
+    tile_step<MODE, D, 0>(sm, wc, stg, p, trow, walk_tile(k), walk_or_none(k + 1), walk_or_none(k + 2), kr, h, tid);
     if (k + 1 >= nwalk) break;
-    tile_step<MODE, D, 1>(sm, wc, stg, p, trow, walk_tile(k + 1), k + 2 < nwalk ? walk_tile(k + 2) : -1, kr, h,
+    tile_step<MODE, D, 1>(sm, wc, stg, p, trow, walk_tile(k + 1), walk_or_none(k + 2), walk_or_none(k + 3), kr, h,
                           tid);
   }
 
@@ -650,29 +711,42 @@ void prefill_kernel(PrefillParams p) {
     }
   }
   __syncthreads();
-  if constexpr (ROT) {
-    for (int hh = 1; hh < D; hh <<= 1) {
-      for (int e = tid; e < nrows * (D / 2); e += 64 * kPWaves) {
-        const int g = e / (D / 2), k = e - g * (D / 2);
-        const int i = (k / hh) * 2 * hh + (k % hh);
-        const float a = sm.qf[g][i], c = sm.qf[g][i + hh];
-        sm.qf[g][i] = a + c;
-        sm.qf[g][i + hh] = a - c;
-      }
-      __syncthreads();
-    }
+  // R^T (FWHT across the wave, signs, 1/sqrt(D)), the V channel scales for
+  // per-channel INT8, and lane-contiguous stores: each wave its own rows.
+  // The lane index is opaque here, so the prologue's sign loads are not kept
+  // live across the tile loop.
+  int el = lane;
+  asm volatile("" : "+v"(el));
+  float so[E], chv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    so[e] = ROT ? p.signs[E * el + e] : 1.0f;
+    chv[e] = MODE == kChannelMode ? p.chs[((int64_t)p.hkv + h) * D + E * el + e] : 1.0f;   // (sum_j p_j c_j) (.) s_V
   }
-  for (int e = tid; e < nrows * D; e += 64 * kPWaves) {
-    const int row = e / D, d = e - row * D;
+  for (int i = 0; i < 32; ++i) {
+    const int row = 32 * wave + i;
+    if (row >= nrows) break;
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = sm.qf[row][E * el + e];
+    if constexpr (ROT) {
+      wave_fwht<D>(x, el);
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = x[e] * so[e] * p.inv_sqrt_d;
+    }
+    if constexpr (MODE == kChannelMode) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] *= chv[e];
+    }
     const int t = row / G, g = row - t * G;
-    float v = sm.qf[row][d];
-    if constexpr (ROT) v = v * p.signs[d] * p.inv_sqrt_d;
-    if constexpr (MODE == kChannelMode) v *= p.chs[((int64_t)p.hkv + h) * D + d];   // (sum_j p_j c_j) (.) s_V
-    const int64_t o_idx = ((int64_t)(q0 + tok0 + t) * p.hq + h * G + g) * D + d;
-    if (p.out_bf16)
-      reinterpret_cast<__bf16*>(p.out)[o_idx] = (__bf16)v;
-    else
-      reinterpret_cast<float*>(p.out)[o_idx] = v;
+    const int64_t o_idx = ((int64_t)(q0 + tok0 + t) * p.hq + h * G + g) * D + E * el;
+    if (p.out_bf16) {
+      if constexpr (E == 2) reinterpret_cast<uint32_t*>(p.out)[o_idx / 2] = pack_bf16(x[0], x[1]);
+      else reinterpret_cast<__bf16*>(p.out)[o_idx] = (__bf16)x[0];
+    } else {
+      if constexpr (E == 2) reinterpret_cast<float2*>(p.out)[o_idx / 2] = make_float2(x[0], x[1]);
+      else reinterpret_cast<float*>(p.out)[o_idx] = x[0];
+    }
   }
 }
 
