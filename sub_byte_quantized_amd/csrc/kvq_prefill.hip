@@ -154,11 +154,11 @@ __device__ __forceinline__ void stage_ids(Stage<MODE, D>& st, const int32_t* tro
 // Global loads of key tile `tau` into registers, from the block ids
 // stage_ids read.  Thread t stages K codes of position t / 4, d-chunk t % 4,
 // the meta of that position and V codes of positions 4 (t % 16) .. +3,
-// d = DPT (t / 16) .. +DPT-1.  An absent position is not
-// read: its codes stage as zeros and `ok` masks it (score -inf, weight 0).
+// d = DPT (t / 16) .. +DPT-1.  Nothing of an absent block (-1, or an id at
+// or past num_blocks) is read, nor a K position that no row sees: their
+// codes stage as zeros and `ok` masks them (score -inf, weight 0).
 template <int MODE, int D>
-__device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillParams& p, int tau, const KeyRange& kr,
-                                           int h, int tid) {
+__device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillParams& p, int tau, int h, int tid) {
   using Gp = PGeo<MODE, D>;
   const int n = tid >> 2, qd = tid & 3;
   const int nblk = (int)p.num_blocks;   // < 2^31 (checked on the host)
@@ -204,14 +204,19 @@ __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillPara
   const int kq = tid & 15, wd = tid >> 4;
   const int j0 = tau * kPKeys + 4 * kq;
   // the four positions share a block (block sizes are >= 16)
+  // All four are read when the block is present: a position outside the
+  // rows' range has zero weight (p = 0 and s_V = 0 staged), and integer
+  // codes are finite, so its codes add exactly nothing.
   const int vrow0 = plane_row<INL>(st.vid, j0, p.block_size_log2, p.hkv, h, nblk);
-  const int vstep = INL ? p.hkv : 1;   // rows between consecutive positions
+  const int64_t vstep = INL ? (int64_t)p.hkv * RS : RS;   // bytes between consecutive positions
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int w = 0; w < Gp::VNW; ++w) st.v[i][w] = 0u;
-    if (vrow0 >= 0 && key_seen(kr, j0 + i))
-      load_bytes<Gp::VNB>(st.v[i], p.v_codes + (int64_t)(vrow0 + i * vstep) * RS + wd * Gp::VNB);
+  if (vrow0 >= 0) {
+    const uint8_t* vb = p.v_codes + (int64_t)vrow0 * RS + wd * Gp::VNB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_bytes<Gp::VNB>(st.v[i], vb + i * vstep);
   }
 }
 
@@ -345,7 +350,7 @@ __device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& 
   // the previous ids (a write on a path that had not would make the compiler
   // wait for every load in flight, this tile's codes included)
   if (more) {
-    stage_load<MODE, D>(stg, p, tau_next, kr, h, tid);
+    stage_load<MODE, D>(stg, p, tau_next, h, tid);
     if (tau_next2 >= 0) stage_ids<MODE, D>(stg, trow, tau_next2, kr, p.block_size_log2, tid);
   }
   const int W = wc.W, r = wc.r, q = wc.q;
@@ -546,7 +551,7 @@ void prefill_kernel(PrefillParams p) {
   auto walk_tile = [&](int k) { return k < nsw ? k : tau0 + (k - nsw); };
   if (nwalk > 0) {
     stage_ids<MODE, D>(stg, trow, walk_tile(0), kr, p.block_size_log2, tid);
-    stage_load<MODE, D>(stg, p, walk_tile(0), kr, h, tid);
+    stage_load<MODE, D>(stg, p, walk_tile(0), h, tid);
     if (nwalk > 1) stage_ids<MODE, D>(stg, trow, walk_tile(1), kr, p.block_size_log2, tid);
   }
 
