@@ -139,16 +139,18 @@ __device__ __forceinline__ int plane_row(int id, int j, int bs_log2, int hkv, in
   return INL ? ((id << (bs_log2 + 1)) + pin) * hkv + h : ((id * hkv + h) << bs_log2) + pin;
 }
 
-// Block ids of key tile `tau` for this thread's K position t / 4 (-1 when no
-// row of the workgroup sees it) and V positions 4 (t % 16) .. +3 (one block:
-// block sizes are >= 16; -1 past khi).  They are read one tile ahead, so the
-// code loads of a tile never wait on the table.
+// Block ids of key tile `tau` for this thread's K position t / 4 and V
+// positions 4 (t % 16) .. +3 (one block: block sizes are >= 16).  They are
+// read one tile ahead, so the code loads of a tile never wait on the table.
 template <int MODE, int D>
 __device__ __forceinline__ void stage_ids(Stage<MODE, D>& st, const int32_t* trow, int tau, const KeyRange& kr,
                                           int bs_log2, int tid) {
+  // entries at positions clamped to khi (< L, inside the table row) are read
+  // with no branch around the loads; stage_load discards those of positions
+  // no row sees (testing them here would wait for the loads at once)
   const int j = tau * kPKeys + (tid >> 2), j0 = tau * kPKeys + 4 * (tid & 15);
-  st.kid = key_seen(kr, j) ? trow[j >> bs_log2] : -1;
-  st.vid = j0 <= kr.khi ? trow[j0 >> bs_log2] : -1;
+  st.kid = trow[min(j, kr.khi) >> bs_log2];
+  st.vid = trow[min(j0, kr.khi) >> bs_log2];
 }
 
 // Global loads of key tile `tau` into registers, from the block ids
@@ -158,13 +160,15 @@ __device__ __forceinline__ void stage_ids(Stage<MODE, D>& st, const int32_t* tro
 // or past num_blocks) is read, nor a K position that no row sees: their
 // codes stage as zeros and `ok` masks them (score -inf, weight 0).
 template <int MODE, int D>
-__device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillParams& p, int tau, int h, int tid) {
+__device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillParams& p, int tau, const KeyRange& kr,
+                                           int h, int tid) {
   using Gp = PGeo<MODE, D>;
   const int n = tid >> 2, qd = tid & 3;
   const int nblk = (int)p.num_blocks;   // < 2^31 (checked on the host)
   constexpr bool INL = MODE == kInlineMode;
   constexpr int RS = INL ? inline_row_bytes(D) : Gp::P;   // bytes between rows
-  const int row = plane_row<INL>(st.kid, tau * kPKeys + n, p.block_size_log2, p.hkv, h, nblk);
+  const int jk = tau * kPKeys + n;
+  const int row = plane_row<INL>(key_seen(kr, jk) ? st.kid : -1, jk, p.block_size_log2, p.hkv, h, nblk);
   st.ok = row >= 0;
 #pragma unroll
   for (int i = 0; i < Gp::KNW; ++i) st.k[i] = 0u;
@@ -207,7 +211,7 @@ __device__ __forceinline__ void stage_load(Stage<MODE, D>& st, const PrefillPara
   // All four are read when the block is present: a position outside the
   // rows' range has zero weight (p = 0 and s_V = 0 staged), and integer
   // codes are finite, so its codes add exactly nothing.
-  const int vrow0 = plane_row<INL>(st.vid, j0, p.block_size_log2, p.hkv, h, nblk);
+  const int vrow0 = plane_row<INL>(j0 <= kr.khi ? st.vid : -1, j0, p.block_size_log2, p.hkv, h, nblk);
   const int64_t vstep = INL ? (int64_t)p.hkv * RS : RS;   // bytes between consecutive positions
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -350,7 +354,7 @@ __device__ __forceinline__ void tile_step(PSmem<MODE, D>& sm, WaveCtx<MODE, D>& 
   // the previous ids (a write on a path that had not would make the compiler
   // wait for every load in flight, this tile's codes included)
   if (more) {
-    stage_load<MODE, D>(stg, p, tau_next, h, tid);
+    stage_load<MODE, D>(stg, p, tau_next, kr, h, tid);
     if (tau_next2 >= 0) stage_ids<MODE, D>(stg, trow, tau_next2, kr, p.block_size_log2, tid);
   }
   const int W = wc.W, r = wc.r, q = wc.q;
@@ -551,7 +555,7 @@ void prefill_kernel(PrefillParams p) {
   auto walk_tile = [&](int k) { return k < nsw ? k : tau0 + (k - nsw); };
   if (nwalk > 0) {
     stage_ids<MODE, D>(stg, trow, walk_tile(0), kr, p.block_size_log2, tid);
-    stage_load<MODE, D>(stg, p, walk_tile(0), h, tid);
+    stage_load<MODE, D>(stg, p, walk_tile(0), kr, h, tid);
     if (nwalk > 1) stage_ids<MODE, D>(stg, trow, walk_tile(1), kr, p.block_size_log2, tid);
   }
 
@@ -660,11 +664,12 @@ void prefill_kernel(PrefillParams p) {
     rpos[rb] = live ? pbase + row / G : -1;
     rlo[rb] = W > 0 ? rpos[rb] - W + 1 : INT32_MIN;
   }
-  // wave-uniform position range of the wave's live rows
+  // wave-uniform position range of the wave's live rows (kept in scalar
+  // registers, so the per-tile tests below are scalar branches)
   const int wrow0 = 32 * wave;
   const bool wave_live = wrow0 < nrows;
-  const int wpos_lo = pbase + wrow0 / G;
-  const int wpos_hi = pbase + (min(wrow0 + 31, nrows - 1)) / G;
+  const int wpos_lo = __builtin_amdgcn_readfirstlane(pbase + wrow0 / G);
+  const int wpos_hi = __builtin_amdgcn_readfirstlane(pbase + (min(wrow0 + 31, nrows - 1)) / G);
   __syncthreads();   // qf is dead; the buffers may be written
   // extra V^T rows D+4 .. D+15 feed unused output columns: keep them zero
   for (int e = tid; e < 2 * 12 * (Gp::VROW / 16); e += 64 * kPWaves) {
