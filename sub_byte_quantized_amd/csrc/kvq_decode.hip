@@ -721,7 +721,7 @@ __device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, 
     scratch[E * lane + e] = x[e];
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, lane_xor(mx, m));
   const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
   float sab = 0.0f;
 #pragma unroll
@@ -740,7 +740,7 @@ __device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, 
     sab += __builtin_fmaf(16384.0f, a, __builtin_fmaf(128.0f, bq, cq));   // each term exact (< 2^22)
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) sab += __shfl_xor(sab, m);
+  for (int m = 32; m >= 1; m >>= 1) sab += lane_xor(sab, m);
   if (lane == 0) {
     *qs = mx > 0.0f ? (mx / 127.0f) * 6.103515625e-05f : 1.0f;   // S / 2^14
     *q1 = sab;

@@ -85,6 +85,18 @@ __device__ __forceinline__ float xor_in_row(float x, int m) {
   }
 }
 
+// x from lane l ^ m for m = 1 .. 32 (a constant after unrolling), with no
+// LDS round trip: xor_in_row below 16; for 16 and 32 a permlane swap of
+// (x, x), whose two results are x and the partner's value in a lane-dependent
+// order, so the partner's bits are r0 ^ r1 ^ x.  All 64 lanes must be active.
+__device__ __forceinline__ float lane_xor(float x, int m) {
+  if (m < 16) return xor_in_row(x, m);
+  const uint32_t b = __float_as_uint(x);
+  const auto r = m == 16 ? __builtin_amdgcn_permlane16_swap(b, b, false, false)
+                         : __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __uint_as_float(r[0] ^ r[1] ^ b);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
@@ -142,7 +154,8 @@ __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src) {
 // In-register Sylvester FWHT of one row (natural order, unnormalized).  The
 // stages h = 1, 2, ..., D/2 run in that order: stage h maps the pair
 // (d, d + h), bit h of d clear, to (x_d + x_{d+h}, x_d - x_{d+h}); within the
-// lane for h < E, across lanes (lane ^ h/E) otherwise.
+// lane for h < E, across lanes (lane ^ h/E) otherwise, with DPP and
+// permlane moves (all 64 lanes active).
 template <int D>
 __device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane) {
   constexpr int E = D / 64;
@@ -155,7 +168,7 @@ __device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane) {
   for (int hl = 1; hl < 64; hl <<= 1) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const float y = __shfl_xor(x[e], hl);
+      const float y = lane_xor(x[e], hl);
       x[e] = (lane & hl) ? y - x[e] : x[e] + y;
     }
   }

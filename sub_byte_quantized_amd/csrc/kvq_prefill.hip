@@ -600,7 +600,7 @@ void prefill_kernel(PrefillParams p) {
         sm.qf[row][E * lane + e] = x[e];
       }
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+      for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, lane_xor(mx, m));
       const float invS = mx > 0.0f ? 127.0f / mx : 0.0f;
       float sq = 0.0f;
 #pragma unroll
@@ -613,7 +613,7 @@ void prefill_kernel(PrefillParams p) {
         sq += __builtin_fmaf(16384.0f, a, __builtin_fmaf(128.0f, b, c));   // each term exact (< 2^22)
       }
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) sq += __shfl_xor(sq, m);
+      for (int m = 32; m >= 1; m >>= 1) sq += lane_xor(sq, m);
       if (lane == 0) {
         sm.rs[row] = mx;
         sm.r1[row] = sq;
