@@ -16,8 +16,8 @@
 // lane's packed bytes (8 INT8, 4 INT4, 2 INT2) and the row's meta in one load
 // each, 16 (bf16) or 32 (float32) bytes stored.  A 256-thread workgroup takes
 // ITER groups of 16 (D 128) or 32 (D 64) consecutive rows of one sequence, in
-// (position, kv head, K/V) order, and issues all its loads before the first
-// use.  grid.y is the sequence; grid.x covers max_seq_len positions.
+// (position, kv head, K/V) order: all their table entries are read, then all
+// their codes and meta, before the first use.  grid.y is the sequence; grid.x covers max_seq_len positions.
 #pragma clang fp contract(off)
 
 #include "kvq_internal.h"
@@ -60,10 +60,12 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
   uint32_t raw[kGatherIter][BPL >= 4 ? BPL / 4 : 1];
   float s[kGatherIter], z[kGatherIter];
   bool present[kGatherIter];
-  int orow[kGatherIter];
+  int orow[kGatherIter], pins[kGatherIter], ids[kGatherIter];
   int hh[kGatherIter], kvs[kGatherIter];
-  // r = pos * 2 Hkv + 2 h + kv: one division for the first row, then steps
-  // of RPB rows
+  // Three phases, so each wait covers one kind of load: every row's table
+  // entry, then (one wait) every row's codes and meta, then the
+  // dequantization and stores.  r = pos * 2 Hkv + 2 h + kv: one division for
+  // the first row, then steps of RPB rows.
   int pos = r0 / (2 * hkv);
   int rem = r0 - pos * 2 * hkv;
 #pragma unroll
@@ -77,17 +79,22 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
       }
     }
     const bool in = r < rows;
-    const int h = rem >> 1, kv = rem & 1;
+    const int h = rem >> 1;
     hh[it] = h;
-    kvs[it] = kv;
+    kvs[it] = rem & 1;
     orow[it] = in ? c0 + pos : -1;
-    int id = -1;
+    pins[it] = pos & ((1 << p.block_size_log2) - 1);
+    ids[it] = -1;
     if (in) {
       const int32_t* trow = p.tables + (uint32_t)(p.headwise ? b * hkv + h : b) * (uint32_t)p.max_blocks;
-      id = trow[pos >> p.block_size_log2];
+      ids[it] = trow[pos >> p.block_size_log2];
     }
-    present[it] = in && id >= 0 && id < p.num_blocks && orow[it] < p.total_tokens;
-    const uint32_t pin = pos & ((1 << p.block_size_log2) - 1);
+  }
+#pragma unroll
+  for (int it = 0; it < kGatherIter; ++it) {
+    const int id = ids[it], h = hh[it], kv = kvs[it];
+    present[it] = orow[it] >= 0 && id >= 0 && id < p.num_blocks && orow[it] < p.total_tokens;
+    const uint32_t pin = (uint32_t)pins[it];
     // plane row (id Hkv + h) bs + offset; inline row (id 2 bs + offset) Hkv + h
     const uint32_t src = !present[it] ? 0u
                          : MODE == kInlineMode ? ((((uint32_t)id << (p.block_size_log2 + 1)) + pin) * hkv + h)
