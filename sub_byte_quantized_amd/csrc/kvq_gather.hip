@@ -191,19 +191,18 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = x[i] * sg[i] * p.inv_sqrt_d;
     }
+    // non-temporal stores: the dense rows are written once and not read back
+    // by this kernel, so they need not stay in the caches
     const uint64_t e0 = (uint64_t)(uint32_t)(orow[it] * hkv + hh[it]) * D + lr * 8;
     void* out = kvs[it] ? p.v_out : p.k_out;
     if constexpr (BF16) {
-      uint4 w;
-      w.x = pack_bf16(x[0], x[1]);
-      w.y = pack_bf16(x[2], x[3]);
-      w.z = pack_bf16(x[4], x[5]);
-      w.w = pack_bf16(x[6], x[7]);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) = w;
+      const u32x4_t w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + e0));
     } else {
-      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
-      o[0] = make_float4(x[0], x[1], x[2], x[3]);
-      o[1] = make_float4(x[4], x[5], x[6], x[7]);
+      f32x4_t* o = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + e0);
+      const f32x4_t a = {x[0], x[1], x[2], x[3]}, c = {x[4], x[5], x[6], x[7]};
+      __builtin_nontemporal_store(a, o);
+      __builtin_nontemporal_store(c, o + 1);
     }
   }
 }
