@@ -665,11 +665,14 @@ constexpr int decode_wg_waves() { return mode_bits(MODE) != 8 ? 4 * decode_waves
 // One query row: q' = R q * scale * log2(e), then its three int8 pieces in
 // k-slot order (q' ~ (S/2^14)(2^14 a + 2^7 b + c), S = max|q'|/127,
 // |a| <= 127, |b|, |c| <= 64), sp = S/2^14 and q1r = sum(2^14 a + 2^7 b + c).
-// `scratch` is the wave's own D floats of LDS (written and read back by the
-// same wave, in order).
+// sg and ch are the lane's rotation signs and K channel scales (d = E lane ..
+// E lane + E - 1), read with the query row so that nothing here waits on a
+// load.  `scratch` is the wave's own D floats of LDS (written and read back
+// by the same wave, in order).
 template <int MODE, int D, int PHI, bool ROT>
-__device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, float* scratch, int8_t* qa,
-                                           int8_t* qb, int8_t* qc, float* qs, float* q1, int h, int lane) {
+__device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, const float (&sg)[D / 64],
+                                           const float (&ch)[D / 64], float* scratch, int8_t* qa, int8_t* qb,
+                                           int8_t* qc, float* qs, float* q1, int lane) {
   using Gm = Geo<MODE, D, PHI>;
   constexpr int E = D / 64;
   float x[E];
@@ -681,12 +684,12 @@ __device__ __forceinline__ void prep_query(const DecodeParams& p, uint32_t raw, 
   }
   if constexpr (ROT) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] *= p.signs[E * lane + e];
+    for (int e = 0; e < E; ++e) x[e] *= sg[e];
     wave_fwht<D>(x, lane);
   }
   if constexpr (MODE == kChannelMode) {   // q . (c (.) s_K) = (q (.) s_K) . c
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] *= p.chs[(int64_t)h * D + E * lane + e];
+    for (int e = 0; e < E; ++e) x[e] *= ch[e];
   }
   const float qmul = ROT ? p.qscale * p.inv_sqrt_d : p.qscale;
   if constexpr (MODE == kFp8Mode) {
@@ -1239,6 +1242,8 @@ void decode_kernel(DecodeParams p) {
     // stream while the prologue finishes.  A tile holding a new token waits
     // until after the barrier that follows the token's store.
     uint32_t raw[QR];
+    float qch[QR][D / 64];
+    float qsg[D / 64];
     int idv[IDR];
 #pragma unroll
     for (int u = 0; u < IDR; ++u) {
@@ -1253,16 +1258,24 @@ void decode_kernel(DecodeParams p) {
       }
     }
 #pragma unroll
+    for (int e = 0; e < D / 64; ++e) qsg[e] = ROT ? p.signs[(D / 64) * plane + e] : 1.0f;
+#pragma unroll
     for (int i = 0; i < QR; ++i) {
       const int rr = wave + i * NWV;
       raw[i] = 0;
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) qch[i][e] = 1.0f;
       if (rr < nseg * G) {
         const int k = rr / G, g = rr - k * G;
         const int b = __builtin_amdgcn_readfirstlane(sm.seg[k].b), h = __builtin_amdgcn_readfirstlane(sm.seg[k].h);
         raw[i] = load_qrow<D>(p.q + ((int64_t)b * p.hq + h * G + g) * D, plane);
+        if constexpr (MODE == kChannelMode) {
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e) qch[i][e] = p.chs[(int64_t)h * D + (D / 64) * plane + e];
+        }
       }
     }
-
+    const bool writer = wr && wave == NWV - 1;
     Cursor cur;
     cur.ls = 0;
     cur.li = 0;
@@ -1272,7 +1285,6 @@ void decode_kernel(DecodeParams p) {
     // the last wave writes the new tokens, so only it waits on stores; its
     // first tile, and any wave's first tile that holds a new token, go out
     // after the barrier
-    const bool writer = wr && wave == NWV - 1;
     const bool defer = writer ||
                        (wr && cur.ls < nseg && cur.L > 0 && cur.tb + wave + NWV * cur.li == (cur.L - 1) >> 6);
     if (cur.ls < nseg) {
@@ -1285,8 +1297,9 @@ void decode_kernel(DecodeParams p) {
       ta = cursor_info<CB, MODE == kInlineMode>(cur, sm, wave, bl, hkv, nblk, p.sink);
     }
     cursor_next(cur, sm, wave);
-    // the ids and query rows are back (the table read above waited for all
-    // older loads): consume them before the tile loads go out, so no later
+    // the ids, query rows, signs and channel scales are back (the table read
+    // above waited for all older loads): consume them before the tile loads
+    // go out, so no later
     // wait has to count those loads (a deferred tile would otherwise make the
     // compiler wait for every load at the join)
 #pragma unroll
@@ -1296,6 +1309,14 @@ void decode_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int i = 0; i < QR; ++i) asm volatile("" : "+v"(raw[i]));
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) {
+      if constexpr (ROT) asm volatile("" : "+v"(qsg[e]));
+      if constexpr (MODE == kChannelMode) {
+#pragma unroll
+        for (int i = 0; i < QR; ++i) asm volatile("" : "+v"(qch[i][e]));
+      }
+    }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);   // keep those stores above the tile loads
     if (!defer) issue_loads<MODE, D, PHI, CB>(ba, ta, p, r, q, phi_col);
 
@@ -1305,14 +1326,23 @@ void decode_kernel(DecodeParams p) {
     // barrier below, after which the tile holding it may be read.  Only this
     // workgroup reads that tile, so no other workgroup has to wait for it.
     if (writer) {
-      constexpr int LPR = D / 8;
-      for (int g0 = 0; g0 < 2 * nseg; g0 += 64 / LPR) {
-        const int grp = g0 + plane / LPR;
+      // the writer wave has no tile loads out yet, so each pass's loads (the
+      // slot, the row and the signs, none waiting on another) cost one round
+      // trip; a row without a slot stores nothing
+      constexpr int WLPR = D / 8;   // lanes per new-token row
+      float wsg[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+      if constexpr (ROT) write_row_signs(p.wp, plane % WLPR, wsg);
+      for (int g0 = 0; g0 < 2 * nseg; g0 += 64 / WLPR) {
+        const int grp = g0 + plane / WLPR;
         if (grp < 2 * nseg) {
           const SegRec& sr = sm.seg[grp >> 1];
           if (sr.L > 0 && sr.te - 1 == (sr.L - 1) >> 6) {
-            const int64_t slot = p.wp.slot_hw ? p.wp.slot_hw[(int64_t)sr.b * hkv + sr.h] : p.wp.slot[sr.b];
-            write_row<MODE, D, ROT>(p.wp, sr.b, sr.h, grp & 1, slot, plane % LPR);
+            int64_t slot = p.wp.slot_hw ? p.wp.slot_hw[(int64_t)sr.b * hkv + sr.h] : p.wp.slot[sr.b];
+            uint4 raw = write_row_load<D>(p.wp, sr.b, sr.h, grp & 1, plane % WLPR);
+            // both loads out before either is used (the compiler would
+            // otherwise sink the row load under the slot test)
+            asm volatile("" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z), "+v"(raw.w), "+v"(slot));
+            write_row_store<MODE, D, ROT>(p.wp, raw, wsg, sr.h, grp & 1, slot, plane % WLPR);
           }
         }
       }
@@ -1329,9 +1359,9 @@ void decode_kernel(DecodeParams p) {
       const int rr = wave + i * NWV;
       if (rr < nseg * G) {
         const int k = rr / G, g = rr - k * G;
-        prep_query<MODE, D, PHI, ROT>(p, raw[i], sm.qrow[wave], sm.qp[0][k * Sm::GM + g], sm.qp[1][k * Sm::GM + g],
-                                      sm.qp[2][k * Sm::GM + g], &sm.qs[k][g], &sm.q1[k][g],
-                                      __builtin_amdgcn_readfirstlane(sm.seg[k].h), plane);
+        prep_query<MODE, D, PHI, ROT>(p, raw[i], qsg, qch[i], sm.qrow[wave], sm.qp[0][k * Sm::GM + g],
+                                      sm.qp[1][k * Sm::GM + g], sm.qp[2][k * Sm::GM + g], &sm.qs[k][g],
+                                      &sm.q1[k][g], plane);
       }
     }
     __syncthreads();
