@@ -248,14 +248,5 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   }
 }
 
-// The whole row: load, then compute and store (a skipped slot reads nothing).
-template <int MODE, int D, bool ROT>
-__device__ __forceinline__ void write_row(const WriteParams& p, int64_t t, int h, int kv, int64_t slot, int lr) {
-  const uint4 raw = (slot >= 0 && slot < p.slot_cap) ? write_row_load<D>(p, t, h, kv, lr) : make_uint4(0, 0, 0, 0);
-  float sg[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
-  if constexpr (ROT) write_row_signs(p, lr, sg);
-  write_row_store<MODE, D, ROT>(p, raw, sg, h, kv, slot, lr);
-}
-
 }  // namespace
 }  // namespace kvq
