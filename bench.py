@@ -64,6 +64,13 @@ CSRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc")
 DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h", "kvq_write_row.h")]
 PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")]
 GATHER_SRC = [os.path.join(CSRC, f) for f in ("kvq_gather.hip", "kvq_device.h", "kvq_internal.h")]
+
+
+def gather_kernel_name(spec):
+    """The gather kernel a cache format runs: the rotated integer formats
+    un-rotate on the matrix cores (gather_rot_kernel), the rest stream
+    through gather_kernel."""
+    return "gather_rot_kernel" if spec.rotate and spec.mode != 4 else "gather_kernel"
 WRITE_SRC = [os.path.join(CSRC, f) for f in ("kvq_write.hip", "kvq_write_row.h", "kvq_device.h", "kvq_internal.h")]
 MODE_NAMES = ["int8_sym", "int4_asym", "int2_asym", "int8_channel", "fp8_e4m3", "int4_inline"]
 # per-mode decode contraction types
@@ -560,7 +567,7 @@ def run_decode(args, spec, dev, ceilings, headline):
                   "frac": round(gbs(T * wb, fill_ms) / HBM_PEAK_GBS, 4),
                   "frac_of_measured_copy": round(gbs(T * wb, fill_ms) / copy_gbs, 4),
                   "traffic": load_traffic(f"write_{spec.name}_counters.json", WRITE_SRC)},
-        "gather": {"kernel": "gather_kernel (dequantize-gather of one layer, bf16 out)", "rows": g_tot * spec.Hkv * 2,
+        "gather": {"kernel": gather_kernel_name(spec) + " (dequantize-gather of one layer, bf16 out)", "rows": g_tot * spec.Hkv * 2,
                    "avg_launch_us": round(g_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(g_bytes),
                    "GBps": round(gbs(g_bytes, g_ms), 2), "frac": round(gbs(g_bytes, g_ms) / HBM_PEAK_GBS, 4),
                    "frac_of_measured_copy": round(gbs(g_bytes, g_ms) / copy_gbs, 4),
@@ -720,7 +727,7 @@ def run_mixed(args, spec, dev, ceilings, headline):
                    "traffic": load_traffic(f"decode_{spec.name}_counters.json")},
         "write": {"step_tokens": T, "step_write_us": round(w_us, 2), "tokens_per_s": round(T / (w_us * 1e-6), 1),
                   "bytes_per_token": wb, "GBps": round(T * wb / (w_us * 1e-6) / 1e9, 2)},
-        "gather": {"kernel": "gather_kernel (dequantize-gather of the prefill contexts, bf16 out)",
+        "gather": {"kernel": gather_kernel_name(spec) + " (dequantize-gather of the prefill contexts, bf16 out)",
                    "rows": g_tot * spec.Hkv * 2, "avg_launch_us": round(g_ms * 1e3, 2),
                    "algorithmic_bytes_per_launch": int(g_bytes),
                    "GBps": round(g_bytes / (g_ms * 1e-3) / 1e9, 2),

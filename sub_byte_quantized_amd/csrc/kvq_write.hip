@@ -14,15 +14,17 @@
 //              c = clamp(rint((y - z) * (1/s)), 0, L)
 // with correctly rounded divisions and no fused multiply-adds.
 //
-// Work split: one row = one (token, kv head) of K or of V.  D/8 lanes own a
-// row, 8 elements per lane (one 16-byte load), so a wave64 handles 128/D*4
-// rows at once; each lane group takes four rows 16 (D=128) or 32 (D=64) rows
-// apart, their slots and loads all requested before the first is used, so a
-// 256-thread workgroup writes 64 or 128 rows.  The FWHT
-// runs in registers for the three in-lane stages and across lanes for the
-// rest; min/max/absmax are lane reductions.  Stores are the lane's slice of
-// the packed row (4 bytes for INT4, 8 for INT8, 2 for INT2) plus one meta
-// store per row.
+// Work split: one row = one (token, kv head) of K or of V.  D/16 lanes own a
+// row, 16 elements per lane (two 16-byte loads), so a wave64 handles 8 (D =
+// 128) or 16 (D = 64) rows at once; each lane group takes four rows 32 or 64
+// rows apart, their slots and loads all requested before the first is used,
+// so a 256-thread workgroup writes 128 or 256 rows.  The FWHT runs in
+// registers for the four in-lane stages and across lanes for the rest;
+// min/max/absmax are lane reductions.  Sixteen elements a lane (against the
+// fused decode step's eight) halve the per-row work each element carries: the
+// cross-lane reduction stages, the scale and zero divisions and the address
+// math.  Stores are the lane's slice of the packed row (16 bytes for INT8
+// and FP8, 8 for INT4, 4 for INT2) plus one meta store per row.
 #pragma clang fp contract(off)
 
 #include "kvq_internal.h"
@@ -36,7 +38,8 @@ constexpr int kChanInvMax = 4096;   // per-channel reciprocals a workgroup keeps
 
 template <int MODE, int D, bool ROT>
 __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
-  constexpr int LPR = D / 8;             // lanes per row
+  constexpr int EPL = 16;                // elements per lane
+  constexpr int LPR = D / EPL;           // lanes per row
   constexpr int RPW = 64 / LPR;          // rows per wave
   constexpr int RPB = 4 * RPW;           // rows per workgroup and iteration
 
@@ -46,8 +49,10 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
   const int row0 = blockIdx.x * RPB * kWriteIter + (threadIdx.x >> 6) * RPW + lane / LPR;
   const int hkv = p.hkv;
 
-  float sg[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
-  if constexpr (ROT) write_row_signs(p, lr, sg);
+  float sg[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) sg[i] = 1.0f;
+  if constexpr (ROT) write_row_signs_n<EPL>(p, lr, sg);
   // per-channel INT8: the workgroup's rows span all (K or V, kv head)
   // channels, so their correctly rounded reciprocals are computed once into
   // LDS (when they fit) instead of once per row
@@ -65,7 +70,7 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
     }
   }
   int64_t slot[kWriteIter];
-  uint4 raw[kWriteIter];
+  uint4 raw[kWriteIter][EPL / 8];
   int hs[kWriteIter];
   // row = t * 2 Hkv + 2 h + kv: one division for the first row, then steps
   // of RPB rows
@@ -84,15 +89,16 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
     const int h = rem >> 1;
     hs[it] = rem;
     slot[it] = -1;
-    raw[it] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < EPL / 8; ++v) raw[it][v] = make_uint4(0, 0, 0, 0);
     if (row < p.total_rows) {
       slot[it] = p.slot_hw ? p.slot_hw[t * hkv + h] : p.slot[t];
-      raw[it] = write_row_load<D, true>(p, t, h, rem & 1, lr);
+      write_row_load_n<D, EPL>(p, t, h, rem & 1, lr, raw[it]);
     }
   }
 #pragma unroll
   for (int it = 0; it < kWriteIter; ++it)
-    write_row_store<MODE, D, ROT, true>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, slot[it], lr, chinv);
+    write_row_store_n<MODE, D, ROT, true, EPL>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, slot[it], lr, chinv);
 }
 
 // Per-channel scales of a first batch (dynamic per-channel INT8, the
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
 
 template <int MODE, int D, bool ROT>
 hipError_t launch_write_t(const WriteParams& p, hipStream_t s) {
-  constexpr int RPB = 4 * (64 / (D / 8)) * kWriteIter;
+  constexpr int RPB = 4 * (64 / (D / 16)) * kWriteIter;
   const int64_t blocks = (p.total_rows + RPB - 1) / RPB;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((write_kernel<MODE, D, ROT>), dim3((unsigned)blocks), dim3(256), 0, s, p);

@@ -3,9 +3,11 @@
 // 2): bf16 row -> optional rotation -> scale (and zero) -> round -> pack ->
 // paged store.  Shared by the write kernel and the fused decode step.
 //
-// The D/8 lanes lr = 0 .. D/8-1 of one aligned lane group call it together
-// (converged: the FWHT and the statistics are shuffles within the group);
-// each lane owns 8 consecutive elements.  Row (token t, kv head h, K if kv =
+// The D/EPL lanes lr = 0 .. D/EPL-1 of one aligned lane group call it
+// together (converged: the FWHT and the statistics are shuffles within the
+// group); each lane owns EPL = 8 or 16 consecutive elements.  The element
+// split changes which butterfly stages run inside a lane and which across
+// lanes, not the stages or their order, so both splits store the same bits.  Row (token t, kv head h, K if kv =
 // 0 else V) goes to `slot` (block * block_size + offset); a slot < 0 or at
 // or past the planes' capacity computes nothing visible.  The load and the rest are separate steps, so a caller
 // can have the loads of several rows in flight before the first is used.
@@ -42,13 +44,36 @@ __device__ __forceinline__ void write_row_signs(const WriteParams& p, int lr, fl
   sg[4] = s1.x; sg[5] = s1.y; sg[6] = s1.z; sg[7] = s1.w;
 }
 
+// The same for EPL elements a lane: EPL / 8 16-byte loads of the row, and
+// the lane's EPL signs.
+template <int D, int EPL>
+__device__ __forceinline__ void write_row_load_n(const WriteParams& p, int64_t t, int h, int kv, int lr,
+                                                 uint4 (&raw)[EPL / 8]) {
+  const uint64_t tt = (uint32_t)t;   // tokens and strides below 2^31 (checked on the host)
+  const uint16_t* src = kv ? p.value + tt * (uint32_t)p.value_stride : p.key + tt * (uint32_t)p.key_stride;
+  const uint4* row = reinterpret_cast<const uint4*>(src + (uint32_t)(h * D + lr * EPL));
+#pragma unroll
+  for (int i = 0; i < EPL / 8; ++i) raw[i] = row[i];
+}
+
+template <int EPL>
+__device__ __forceinline__ void write_row_signs_n(const WriteParams& p, int lr, float (&sg)[EPL]) {
+#pragma unroll
+  for (int i = 0; i < EPL / 4; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(p.signs + lr * EPL + 4 * i);
+    sg[4 * i] = v.x; sg[4 * i + 1] = v.y; sg[4 * i + 2] = v.z; sg[4 * i + 3] = v.w;
+  }
+}
+
 // Everything after the load: rotation (lane signs sg), scale (and zero),
 // codes, packed and paged stores of the row whose lane elements `raw` holds.
-template <int MODE, int D, bool ROT, bool I32 = false>
-__device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw, const float (&sg)[8], int h, int kv,
-                                                int64_t slot, int lr, const float* chinv = nullptr) {
+template <int MODE, int D, bool ROT, bool I32, int EPL>
+__device__ __forceinline__ void write_row_store_n(const WriteParams& p, const uint4 (&raw)[EPL / 8],
+                                                  const float (&sg)[EPL], int h, int kv, int64_t slot, int lr,
+                                                  const float* chinv) {
 #pragma clang fp contract(off)
-  constexpr int LPR = D / 8;             // lanes per row
+  static_assert(EPL == 8 || EPL == 16, "8 or 16 elements a lane");
+  constexpr int LPR = D / EPL;           // lanes per row
   constexpr int P = row_bytes(MODE, D);  // packed bytes per row
   constexpr int BPL = P / LPR;           // packed bytes per lane
   constexpr int M = mode_meta(MODE);
@@ -56,27 +81,30 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   const int hkv = p.hkv;
   const bool active = slot >= 0 && slot < p.slot_cap;
 
-  float x[8];
+  float x[EPL];
   if (active) {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    for (int v = 0; v < EPL / 8; ++v) {
+      const uint32_t w[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * v + 2 * i] = __uint_as_float(w[i] << 16);
+        x[8 * v + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+    for (int i = 0; i < EPL; ++i) x[i] = 0.0f;
   }
 
   if constexpr (ROT) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] *= sg[i];
+    for (int i = 0; i < EPL; ++i) x[i] *= sg[i];
     // in-lane butterflies, pairs (i, i + hh) with bit hh of i clear
 #pragma unroll
-    for (int hh = 1; hh < 8; hh <<= 1) {
+    for (int hh = 1; hh < EPL; hh <<= 1) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < EPL; ++i) {
         if (!(i & hh)) {
           const float a = x[i], b = x[i + hh];
           x[i] = a + b;
@@ -84,17 +112,17 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
         }
       }
     }
-    // cross-lane butterflies: element stride 8*m lives m lanes away
+    // cross-lane butterflies: element stride EPL*m lives m lanes away
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) {
       // x + o in the lower lane, o - x in the upper one, as one fma with a
       // +-1 factor (the product is exact, so the single rounding is the sum's)
       const float sgn = (lr & m) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], sgn, xor_in_row(x[i], m));
+      for (int i = 0; i < EPL; ++i) x[i] = __builtin_fmaf(x[i], sgn, xor_in_row(x[i], m));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = x[i] * p.inv_sqrt_d;
+    for (int i = 0; i < EPL; ++i) x[i] = x[i] * p.inv_sqrt_d;
   }
 
   // per-channel INT8: fixed scales of the (K or V, kv head) channels, codes
@@ -102,25 +130,28 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   // channel (0 for a zero or subnormal scale, which gives code 0); no row
   // metadata.  chinv: the reciprocals already in LDS ([2][Hkv][D]), else
   // computed here
-  uint32_t c[8];
+  uint32_t c[EPL];
   if constexpr (MODE == kChannelMode) {
-    float inv[8];
+    float inv[EPL];
     if (chinv) {
-      const float* ci = chinv + (kv * hkv + h) * D + lr * 8;
-      const float4 i0 = *reinterpret_cast<const float4*>(ci);
-      const float4 i1 = *reinterpret_cast<const float4*>(ci + 4);
-      inv[0] = i0.x; inv[1] = i0.y; inv[2] = i0.z; inv[3] = i0.w;
-      inv[4] = i1.x; inv[5] = i1.y; inv[6] = i1.z; inv[7] = i1.w;
-    } else {
-      const float* cs = p.chs + ((int64_t)kv * hkv + h) * D + lr * 8;
-      const float4 s0 = *reinterpret_cast<const float4*>(cs);
-      const float4 s1 = *reinterpret_cast<const float4*>(cs + 4);
-      const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const float* ci = chinv + (kv * hkv + h) * D + lr * EPL;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) inv[i] = sc[i] >= 1.17549435e-38f ? 1.0f / sc[i] : 0.0f;
+      for (int v = 0; v < EPL / 4; ++v) {
+        const float4 iv = *reinterpret_cast<const float4*>(ci + 4 * v);
+        inv[4 * v] = iv.x; inv[4 * v + 1] = iv.y; inv[4 * v + 2] = iv.z; inv[4 * v + 3] = iv.w;
+      }
+    } else {
+      const float* cs = p.chs + ((int64_t)kv * hkv + h) * D + lr * EPL;
+#pragma unroll
+      for (int v = 0; v < EPL / 4; ++v) {
+        const float4 sv = *reinterpret_cast<const float4*>(cs + 4 * v);
+        const float sc[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) inv[4 * v + i] = sc[i] >= 1.17549435e-38f ? 1.0f / sc[i] : 0.0f;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       const float r = fminf(fmaxf(__builtin_rintf(x[i] * inv[i]), -kLevels), kLevels);
       c[i] = inv[i] != 0.0f ? (uint32_t)(int32_t)r : 0u;   // 1/s of a normal scale is never 0
     }
@@ -130,7 +161,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   if constexpr (MODE == 0 || MODE == kFp8Mode) {
     float a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+    for (int i = 0; i < EPL; ++i) a = fmaxf(a, fabsf(x[i]));
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) a = fmaxf(a, xor_in_row(a, m));
     s = a / kLevels;
@@ -138,7 +169,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   } else if constexpr (MODE != kChannelMode) {
     float mn = x[0], mx = x[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) {
+    for (int i = 1; i < EPL; ++i) {
       mn = fminf(mn, x[i]);
       mx = fmaxf(mx, x[i]);
     }
@@ -161,11 +192,11 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     // NaN scale: all-zero codes
     const bool ok = s >= 1.17549435e-38f;
     const float inv = ok ? 1.0f / s : 0.0f;
-    float t[8];
+    float t[EPL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = ok ? fminf(fmaxf(x[i] * inv, -kLevels), kLevels) : 0.0f;
+    for (int i = 0; i < EPL; ++i) t[i] = ok ? fminf(fmaxf(x[i] * inv, -kLevels), kLevels) : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < EPL / 4; ++j) {
       uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[4 * j], t[4 * j + 1], 0, false);
       w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[4 * j + 2], t[4 * j + 3], (int)w, true);
       c[4 * j] = w & 0xffu; c[4 * j + 1] = (w >> 8) & 0xffu; c[4 * j + 2] = (w >> 16) & 0xffu; c[4 * j + 3] = w >> 24;
@@ -179,7 +210,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     stbits = ok ? ((__float_as_uint(s) & ~0xFu) | (uint32_t)zp) : 0u;
     const float inv = ok ? 1.0f / __uint_as_float(stbits) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       const float r = fminf(fmaxf(__builtin_rintf(x[i] * inv) + zp, 0.0f), kLevels);
       c[i] = ok ? (uint32_t)(int32_t)r : 0u;
     }
@@ -189,7 +220,7 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
     const float inv = ok ? 1.0f / s : 0.0f;
     constexpr float lo = MODE == 0 ? -kLevels : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       const float tq = MODE == 0 ? x[i] * inv : (x[i] - z) * inv;
       const float r = fminf(fmaxf(__builtin_rintf(tq), lo), kLevels);
       c[i] = ok ? (uint32_t)(int32_t)r : 0u;
@@ -211,10 +242,12 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
                    (I32 ? (uint64_t)(((blk32 << (bsl + 1)) + off32) * (uint32_t)hkv + (uint32_t)h) *
                               inline_row_bytes(D)
                         : (((blk << (bsl + 1)) + off) * hkv + h) * inline_row_bytes(D));
-    uint32_t w = 0;
+    uint32_t w[EPL / 8] = {};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w |= c[i] << (4 * i);
-    *reinterpret_cast<uint32_t*>(row + lr * BPL) = w;
+    for (int i = 0; i < EPL; ++i) w[i >> 3] |= c[i] << (4 * (i & 7));
+    // inline rows are 4-byte aligned only
+    if constexpr (EPL == 8) *reinterpret_cast<uint32_t*>(row + lr * BPL) = w[0];
+    else *reinterpret_cast<u32x2a4_t*>(row + lr * BPL) = u32x2a4_t{w[0], w[1]};
     if (lr == 0) *reinterpret_cast<uint32_t*>(row + P) = stbits;
     return;
   }
@@ -224,20 +257,25 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
   float* meta = (kv ? p.v_meta : p.k_meta) + ridx * M;   // unused when M == 0
 
   if constexpr (mode_bits(MODE) == 8) {
-    uint2 w;
-    w.x = (c[0] & 0xffu) | ((c[1] & 0xffu) << 8) | ((c[2] & 0xffu) << 16) | ((c[3] & 0xffu) << 24);
-    w.y = (c[4] & 0xffu) | ((c[5] & 0xffu) << 8) | ((c[6] & 0xffu) << 16) | ((c[7] & 0xffu) << 24);
-    *reinterpret_cast<uint2*>(codes) = w;
-  } else if constexpr (MODE == 1) {
-    uint32_t w = 0;
+    uint32_t w[EPL / 4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w |= c[i] << (4 * i);
-    *reinterpret_cast<uint32_t*>(codes) = w;
+    for (int k = 0; k < EPL / 4; ++k)
+      w[k] = (c[4 * k] & 0xffu) | ((c[4 * k + 1] & 0xffu) << 8) | ((c[4 * k + 2] & 0xffu) << 16) |
+             ((c[4 * k + 3] & 0xffu) << 24);
+    if constexpr (EPL == 8) *reinterpret_cast<uint2*>(codes) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint4*>(codes) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (MODE == 1) {
+    uint32_t w[EPL / 8] = {};
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) w[i >> 3] |= c[i] << (4 * (i & 7));
+    if constexpr (EPL == 8) *reinterpret_cast<uint32_t*>(codes) = w[0];
+    else *reinterpret_cast<uint2*>(codes) = make_uint2(w[0], w[1]);
   } else {
     uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w |= c[i] << (2 * i);
-    *reinterpret_cast<uint16_t*>(codes) = (uint16_t)w;
+    for (int i = 0; i < EPL; ++i) w |= c[i] << (2 * i);
+    if constexpr (EPL == 8) *reinterpret_cast<uint16_t*>(codes) = (uint16_t)w;
+    else *reinterpret_cast<uint32_t*>(codes) = w;
   }
   if (M > 0 && lr == 0) {
     if constexpr (M == 1) {
@@ -246,6 +284,14 @@ __device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw,
       *reinterpret_cast<float2*>(meta) = make_float2(s, z);
     }
   }
+}
+
+// The 8-element form with one loaded vector (the fused decode step's).
+template <int MODE, int D, bool ROT, bool I32 = false>
+__device__ __forceinline__ void write_row_store(const WriteParams& p, uint4 raw, const float (&sg)[8], int h, int kv,
+                                                int64_t slot, int lr, const float* chinv = nullptr) {
+  const uint4 r[1] = {raw};
+  write_row_store_n<MODE, D, ROT, I32, 8>(p, r, sg, h, kv, slot, lr, chinv);
 }
 
 }  // namespace
