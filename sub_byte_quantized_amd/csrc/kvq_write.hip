@@ -14,17 +14,17 @@
 //              c = clamp(rint((y - z) * (1/s)), 0, L)
 // with correctly rounded divisions and no fused multiply-adds.
 //
-// Work split: one row = one (token, kv head) of K or of V.  D/16 lanes own a
-// row, 16 elements per lane (two 16-byte loads), so a wave64 handles 8 (D =
-// 128) or 16 (D = 64) rows at once; each lane group takes four rows 32 or 64
-// rows apart, their slots and loads all requested before the first is used,
-// so a 256-thread workgroup writes 128 or 256 rows.  The FWHT runs in
-// registers for the four in-lane stages and across lanes for the rest;
-// min/max/absmax are lane reductions.  Sixteen elements a lane (against the
-// fused decode step's eight) halve the per-row work each element carries: the
-// cross-lane reduction stages, the scale and zero divisions and the address
-// math.  Stores are the lane's slice of the packed row (16 bytes for INT8
-// and FP8, 8 for INT4, 4 for INT2) plus one meta store per row.
+// Work split: one row = one (token, kv head) of K or of V.  D/EPL lanes own a
+// row, EPL = 32 elements per lane with the rotation and 16 without (four or
+// two 16-byte loads), so a wave64 handles 64 EPL / D rows at once; each lane
+// group takes two (rotated) or four rows, their slots and loads all requested
+// before the first is used.  The FWHT runs in registers for the in-lane
+// stages (h < EPL) and across lanes for the rest; min/max/absmax are lane
+// reductions.  Long lane slices (against the fused decode step's eight
+// elements) cut the per-row work each element carries: the cross-lane
+// reduction stages, the scale and zero divisions and the address math.
+// Stores are the lane's slice of the packed row (EPL bytes for INT8 and FP8,
+// EPL/2 for INT4, EPL/4 for INT2) plus one meta store per row.
 #pragma clang fp contract(off)
 
 #include "kvq_internal.h"
@@ -33,12 +33,21 @@
 namespace kvq {
 namespace {
 
-constexpr int kWriteIter = 4;   // rows per lane group, their loads in flight together
+// Elements per lane: 32 with the rotation (its butterfly stages and the
+// per-row statistics make the kernel VALU-bound, and longer lane slices
+// carry less per-row work per element), 16 without (the 8-bit modes then
+// stream faster with more, shorter rows in flight).
+template <bool ROT>
+constexpr int write_epl() { return ROT ? 32 : 16; }
+// rows per lane group, their loads in flight together (64 bytes a lane)
+template <bool ROT>
+constexpr int write_iter() { return ROT ? 2 : 4; }
 constexpr int kChanInvMax = 4096;   // per-channel reciprocals a workgroup keeps in LDS (2 Hkv D)
 
 template <int MODE, int D, bool ROT>
 __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
-  constexpr int EPL = 16;                // elements per lane
+  constexpr int EPL = write_epl<ROT>();
+  constexpr int kWriteIter = write_iter<ROT>();
   constexpr int LPR = D / EPL;           // lanes per row
   constexpr int RPW = 64 / LPR;          // rows per wave
   constexpr int RPB = 4 * RPW;           // rows per workgroup and iteration
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
 
 template <int MODE, int D, bool ROT>
 hipError_t launch_write_t(const WriteParams& p, hipStream_t s) {
-  constexpr int RPB = 4 * (64 / (D / 16)) * kWriteIter;
+  constexpr int RPB = 4 * (64 / (D / write_epl<ROT>())) * write_iter<ROT>();
   const int64_t blocks = (p.total_rows + RPB - 1) / RPB;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((write_kernel<MODE, D, ROT>), dim3((unsigned)blocks), dim3(256), 0, s, p);

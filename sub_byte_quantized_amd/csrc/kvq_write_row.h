@@ -65,6 +65,27 @@ __device__ __forceinline__ void write_row_signs_n(const WriteParams& p, int lr, 
   }
 }
 
+// NW consecutive dwords to dst: one store of 4, 8 or 16 bytes a time (A4:
+// dst is only 4-byte aligned).
+template <int NW, bool A4>
+__device__ __forceinline__ void store_dwords(uint8_t* dst, const uint32_t (&w)[NW]) {
+  if constexpr (NW == 1) {
+    *reinterpret_cast<uint32_t*>(dst) = w[0];
+  } else if constexpr (NW == 2) {
+    if constexpr (A4) *reinterpret_cast<u32x2a4_t*>(dst) = u32x2a4_t{w[0], w[1]};
+    else *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      if constexpr (A4) {
+        *reinterpret_cast<u32x4a4_t*>(dst + 16 * i) = u32x4a4_t{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+      } else {
+        *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+      }
+    }
+  }
+}
+
 // Everything after the load: rotation (lane signs sg), scale (and zero),
 // codes, packed and paged stores of the row whose lane elements `raw` holds.
 template <int MODE, int D, bool ROT, bool I32, int EPL>
@@ -72,7 +93,7 @@ __device__ __forceinline__ void write_row_store_n(const WriteParams& p, const ui
                                                   const float (&sg)[EPL], int h, int kv, int64_t slot, int lr,
                                                   const float* chinv) {
 #pragma clang fp contract(off)
-  static_assert(EPL == 8 || EPL == 16, "8 or 16 elements a lane");
+  static_assert(EPL == 8 || EPL == 16 || EPL == 32, "8, 16 or 32 elements a lane");
   constexpr int LPR = D / EPL;           // lanes per row
   constexpr int P = row_bytes(MODE, D);  // packed bytes per row
   constexpr int BPL = P / LPR;           // packed bytes per lane
@@ -245,9 +266,7 @@ __device__ __forceinline__ void write_row_store_n(const WriteParams& p, const ui
     uint32_t w[EPL / 8] = {};
 #pragma unroll
     for (int i = 0; i < EPL; ++i) w[i >> 3] |= c[i] << (4 * (i & 7));
-    // inline rows are 4-byte aligned only
-    if constexpr (EPL == 8) *reinterpret_cast<uint32_t*>(row + lr * BPL) = w[0];
-    else *reinterpret_cast<u32x2a4_t*>(row + lr * BPL) = u32x2a4_t{w[0], w[1]};
+    store_dwords<EPL / 8, true>(row + lr * BPL, w);   // inline rows are 4-byte aligned only
     if (lr == 0) *reinterpret_cast<uint32_t*>(row + P) = stbits;
     return;
   }
@@ -262,20 +281,22 @@ __device__ __forceinline__ void write_row_store_n(const WriteParams& p, const ui
     for (int k = 0; k < EPL / 4; ++k)
       w[k] = (c[4 * k] & 0xffu) | ((c[4 * k + 1] & 0xffu) << 8) | ((c[4 * k + 2] & 0xffu) << 16) |
              ((c[4 * k + 3] & 0xffu) << 24);
-    if constexpr (EPL == 8) *reinterpret_cast<uint2*>(codes) = make_uint2(w[0], w[1]);
-    else *reinterpret_cast<uint4*>(codes) = make_uint4(w[0], w[1], w[2], w[3]);
+    store_dwords<EPL / 4, false>(codes, w);
   } else if constexpr (MODE == 1) {
     uint32_t w[EPL / 8] = {};
 #pragma unroll
     for (int i = 0; i < EPL; ++i) w[i >> 3] |= c[i] << (4 * (i & 7));
-    if constexpr (EPL == 8) *reinterpret_cast<uint32_t*>(codes) = w[0];
-    else *reinterpret_cast<uint2*>(codes) = make_uint2(w[0], w[1]);
-  } else {
+    store_dwords<EPL / 8, false>(codes, w);
+  } else if constexpr (EPL == 8) {
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) w |= c[i] << (2 * i);
-    if constexpr (EPL == 8) *reinterpret_cast<uint16_t*>(codes) = (uint16_t)w;
-    else *reinterpret_cast<uint32_t*>(codes) = w;
+    *reinterpret_cast<uint16_t*>(codes) = (uint16_t)w;
+  } else {
+    uint32_t w[EPL / 16] = {};
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) w[i >> 4] |= c[i] << (2 * (i & 15));
+    store_dwords<EPL / 16, false>(codes, w);
   }
   if (M > 0 && lr == 0) {
     if constexpr (M == 1) {
