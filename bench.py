@@ -64,6 +64,8 @@ CSRC = os.path.join(ROOT, "sub_byte_quantized_amd", "csrc")
 DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h", "kvq_write_row.h")]
 PREFILL_SRC = [os.path.join(CSRC, f) for f in ("kvq_prefill.hip", "kvq_device.h", "kvq_internal.h")]
 GATHER_SRC = [os.path.join(CSRC, f) for f in ("kvq_gather.hip", "kvq_device.h", "kvq_internal.h")]
+WRITE_SRC = [os.path.join(CSRC, f) for f in ("kvq_write.hip", "kvq_write_row.h", "kvq_device.h", "kvq_internal.h")]
+MODE_NAMES = ["int8_sym", "int4_asym", "int2_asym", "int8_channel", "fp8_e4m3", "int4_inline"]
 
 
 def gather_kernel_name(spec):
@@ -71,8 +73,8 @@ def gather_kernel_name(spec):
     un-rotate on the matrix cores (gather_rot_kernel), the rest stream
     through gather_kernel."""
     return "gather_rot_kernel" if spec.rotate and spec.mode != 4 else "gather_kernel"
-WRITE_SRC = [os.path.join(CSRC, f) for f in ("kvq_write.hip", "kvq_write_row.h", "kvq_device.h", "kvq_internal.h")]
-MODE_NAMES = ["int8_sym", "int4_asym", "int2_asym", "int8_channel", "fp8_e4m3", "int4_inline"]
+
+
 # per-mode decode contraction types
 MODE_DTYPES = {0: "int8 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",
                1: "int4 codes; int8 mfma (q.k), bf16 mfma (p.v), fp32 accumulate",

@@ -832,8 +832,30 @@ struct Smem {
 // end, *start = window start.
 __device__ __forceinline__ int first_tile(int start, int sink) { return (start > 0 && sink > 0) ? 0 : start / 64; }
 
+// Sequence b and kv head h of pair `pair`.  The planes layouts number the
+// pairs sequence-major (b Hkv + h).  The inline layout numbers them
+// head-major (h B + b): its rows interleave a token's heads, so a 128-byte
+// line holds parts of several heads' rows.  With equal shares over Hkv equal
+// head blocks, shares w, w + nw / Hkv, ... then walk the same positions of
+// one sequence's heads at the same time, and since workgroups go to the XCDs
+// round-robin they sit on one XCD (one L2) whenever nw / Hkv is a multiple of
+// the XCD count: a line is fetched once for all its heads, not once per head.
+template <bool HM>
+__device__ __forceinline__ void pair_bh(const DecodeParams& p, int hkv, int pair, int& b, int& h) {
+  if constexpr (HM) {
+    const int nb = p.num_pairs / hkv;
+    h = pair / nb;
+    b = pair - h * nb;
+  } else {
+    b = pair / hkv;
+    h = pair - b * hkv;
+  }
+}
+
+template <bool HM>
 __device__ __forceinline__ int pair_geo(const DecodeParams& p, int pair, int* t0, int* L, int* start) {
-  const int b = pair / p.hkv, h = pair - b * p.hkv;
+  int b, h;
+  pair_bh<HM>(p, p.hkv, pair, b, h);
   const int l = min(p.seq_lens[b], p.max_seq_len);   // host checked max_seq_len <= max_blocks * bs
   const int W = p.window ? p.window[h] : 0;
   const int s = (W > 0 && l > W) ? l - W : 0;
@@ -1012,7 +1034,7 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, Smem<D, PHI,
 // 0); returns the chunk's tile total.  All threads of the workgroup; each
 // thread takes a run of consecutive pairs, the runs are scanned within the
 // wave by shuffles and across the waves in LDS.  Ends with a barrier.
-template <int NWV>
+template <int NWV, bool HM>
 __device__ __forceinline__ int scan_chunk(const DecodeParams& p, int32_t* pref, int32_t* plen, int32_t* pst,
                                           int32_t* part, int c0, int cn, int tid) {
   constexpr int NT = 64 * NWV;
@@ -1024,7 +1046,7 @@ __device__ __forceinline__ int scan_chunk(const DecodeParams& p, int32_t* pref, 
     const int i = tid * per + k;
     if (i < cn) {
       int t0, L, s;
-      run += pair_geo(p, c0 + i, &t0, &L, &s);
+      run += pair_geo<HM>(p, c0 + i, &t0, &L, &s);
       pref[i + 1] = run;
       plen[i] = L;
       pst[i] = s;
@@ -1091,17 +1113,18 @@ void decode_kernel(DecodeParams p) {
   const int P = p.num_pairs, G = p.group, hkv = p.hkv, bl = p.block_size_log2;
   const int nblk = (int)p.num_blocks;   // < 2^31 (checked on the host)
   const int w = blockIdx.x;
+  constexpr bool HM = MODE == kInlineMode;   // pair order (pair_bh)
 
   // ---- tile prefix of the first chunk of pairs; total tiles
   for (int i = tid; i < 3 * Sm::QW; i += NT) sm.qp[i / Sm::QW][NS * Sm::GM][i % Sm::QW] = 0;
   int cn = min(kPrefChunk, P);
-  int ctot = scan_chunk<NWV>(p, sm.pref, sm.plen, sm.pst, sm.part, 0, cn, tid);
+  int ctot = scan_chunk<NWV, HM>(p, sm.pref, sm.plen, sm.pst, sm.part, 0, cn, tid);
   int T = ctot;
   if (P > cn) {
     int my = 0;
     for (int i = cn + tid; i < P; i += NT) {
       int t0, L, s;
-      my += pair_geo(p, i, &t0, &L, &s);
+      my += pair_geo<HM>(p, i, &t0, &L, &s);
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) my += __shfl_xor(my, m);
@@ -1124,8 +1147,9 @@ void decode_kernel(DecodeParams p) {
   // read seq_lens again here.
   for (int i = w + tid * nw; i < P; i += NT * nw) {
     int t0, L, s;
-    if (i < cn ? sm.plen[i] <= 0 : pair_geo(p, i, &t0, &L, &s) == 0) {
-      const int b = i / hkv, h = i - b * hkv;
+    if (i < cn ? sm.plen[i] <= 0 : pair_geo<HM>(p, i, &t0, &L, &s) == 0) {
+      int b, h;
+      pair_bh<HM>(p, hkv, i, b, h);
       const int64_t o = ((int64_t)b * p.hq + h * G) * D;
       for (int e = 0; e < G * D; ++e) {
         if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[o + e] = (__bf16)0.0f;
@@ -1165,7 +1189,7 @@ void decode_kernel(DecodeParams p) {
           break;
         }
         __syncthreads();   // earlier readers of pref / part are done
-        ctot = scan_chunk<NWV>(p, sm.pref, sm.plen, sm.pst, sm.part, c0, cn, tid);
+        ctot = scan_chunk<NWV, HM>(p, sm.pref, sm.plen, sm.pst, sm.part, c0, cn, tid);
         ci = first_after(sm.pref, cn, cbase, x);
         continue;
       }
@@ -1191,8 +1215,7 @@ void decode_kernel(DecodeParams p) {
       const bool whole = x == s0 && e == s1;
       if (tid == 0) {
         SegRec& s = sm.seg[nseg];
-        s.b = pair / hkv;
-        s.h = pair - s.b * hkv;
+        pair_bh<HM>(p, hkv, pair, s.b, s.h);
         s.tb = tb;
         s.te = te;
         s.L = L;
@@ -1515,7 +1538,8 @@ void decode_kernel(DecodeParams p) {
         const int pair = __builtin_amdgcn_readfirstlane(sm.pend[i][0]);
         const int fw = part.owner(__builtin_amdgcn_readfirstlane(sm.pend[i][1]));
         const int lw = part.owner(__builtin_amdgcn_readfirstlane(sm.pend[i][2]) - 1);
-        const int b = pair / hkv, h = pair - b * hkv;
+        int b, h;
+        pair_bh<HM>(p, hkv, pair, b, h);
         if (np == 0) {
           s0a = pair + fw; na = lw - fw + 1; o0a = (int64_t)b * p.hq + h * G; pa = pair;
         } else {
