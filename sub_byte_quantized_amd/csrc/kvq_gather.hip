@@ -46,7 +46,16 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
   // row, table and output indices stay below 2^31 (checked on the host), so
   // the index math is 32-bit and each address one 32 x 32 -> 64-bit product
   const int rows = n * hkv * 2;
-  const int r0 = blockIdx.x * RPB * kGatherIter + (threadIdx.x >> 6) * RPW + lane / LPR;
+  // Workgroups go to the 8 XCDs round-robin, and gridDim.x is a multiple of
+  // 8, so XCD x % 8 runs workgroups x, x + 8, ...  Of the nb8 workgroups
+  // (a multiple of 8) that cover this sequence's rows, those of XCD x % 8
+  // take the contiguous run (x % 8) nb8/8 .. of its row groups: neighbouring
+  // row groups share 128-byte lines of per-row meta, which one L2 then
+  // fetches once instead of once per XCD.
+  const int nb8 = ((rows + RPB * kGatherIter - 1) / (RPB * kGatherIter) + 7) & ~7;
+  if ((int)blockIdx.x >= nb8) return;
+  const int bx = (blockIdx.x & 7) * (nb8 >> 3) + (blockIdx.x >> 3);
+  const int r0 = bx * RPB * kGatherIter + (threadIdx.x >> 6) * RPW + lane / LPR;
   if (r0 >= rows) return;
 
   // the lane's rotation signs, read before any store (so not reloaded per row)
@@ -435,7 +444,7 @@ hipError_t launch_gather_t(const GatherParams& p, hipStream_t s) {
   }
   constexpr int RPB = 4 * (64 / (D / 8)) * kGatherIter;
   const int64_t rows = (int64_t)p.max_seq_len * p.hkv * 2;
-  const int64_t gx = (rows + RPB - 1) / RPB;
+  const int64_t gx = ((rows + RPB - 1) / RPB + 7) & ~7LL;   // a multiple of the XCD count
   if (gx == 0 || p.num_seqs == 0) return hipSuccess;
   const dim3 grid((unsigned)gx, (unsigned)p.num_seqs);
   if (p.out_bf16)
@@ -457,6 +466,8 @@ hipError_t launch_gather_m(int d, bool rot, const GatherParams& p, hipStream_t s
 
 }  // namespace
 
+// The fewest rows any gather workgroup covers (the host bounds the grid with
+// it; the launch pads grid.x to a multiple of 8 beyond that).
 int64_t gather_rows_per_workgroup(int d) { return 4LL * (64 / (d / 8)) * kGatherIter; }
 
 hipError_t launch_gather(int mode, int d, bool rot, const GatherParams& p, hipStream_t s) {
