@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
   int64_t slot[kWriteIter];
   uint4 raw[kWriteIter][EPL / 8];
   int hs[kWriteIter];
+  bool ins[kWriteIter];
   // row = t * 2 Hkv + 2 h + kv: one division for the first row, then steps
   // of RPB rows
   int t = row0 / (2 * hkv);
@@ -96,18 +97,20 @@ __global__ __launch_bounds__(256) void write_kernel(WriteParams p) {
       }
     }
     const int h = rem >> 1;
-    hs[it] = rem;
-    slot[it] = -1;
-#pragma unroll
-    for (int v = 0; v < EPL / 8; ++v) raw[it][v] = make_uint4(0, 0, 0, 0);
-    if (row < p.total_rows) {
-      slot[it] = p.slot_hw ? p.slot_hw[t * hkv + h] : p.slot[t];
-      write_row_load_n<D, EPL>(p, t, h, rem & 1, lr, raw[it]);
-    }
+    // a row past the end reads token 0's row and slot (always present, as a
+    // launch has rows) and stores nothing: no branch, no zeroing of its
+    // registers
+    const bool in = row < p.total_rows;
+    const int tc = in ? t : 0, hc = in ? h : 0;
+    hs[it] = in ? rem : (rem & 1);
+    ins[it] = in;
+    slot[it] = p.slot_hw ? p.slot_hw[tc * hkv + hc] : p.slot[tc];
+    write_row_load_n<D, EPL>(p, tc, hc, rem & 1, lr, raw[it]);
   }
 #pragma unroll
   for (int it = 0; it < kWriteIter; ++it)
-    write_row_store_n<MODE, D, ROT, true, EPL>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, slot[it], lr, chinv);
+    write_row_store_n<MODE, D, ROT, true, EPL>(p, raw[it], sg, hs[it] >> 1, hs[it] & 1, ins[it] ? slot[it] : -1, lr,
+                                               chinv);
 }
 
 // Per-channel scales of a first batch (dynamic per-channel INT8, the

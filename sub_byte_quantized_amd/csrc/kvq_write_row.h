@@ -102,8 +102,12 @@ __device__ __forceinline__ void write_row_store_n(const WriteParams& p, const ui
   const int hkv = p.hkv;
   const bool active = slot >= 0 && slot < p.slot_cap;
 
+  // An inactive row (all lanes of its group alike) computes on whatever its
+  // registers hold and stores nothing.  The 8-element form of the fused step
+  // zeroes them first (its register allocation is tuned around that), and so
+  // does per-channel INT8 (fewer instructions that way).
   float x[EPL];
-  if (active) {
+  if ((EPL > 8 && MODE != kChannelMode) || active) {
 #pragma unroll
     for (int v = 0; v < EPL / 8; ++v) {
       const uint32_t w[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
