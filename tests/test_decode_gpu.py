@@ -78,8 +78,12 @@ def test_decode_bf16_output():
     assert np.all(np.abs(a - b) <= ulp)
 
 
-def test_decode_repeatable_and_split_invariant():
-    spec = synth.small_spec(name="splits", cfg=463, mode=2, rotate=True, lens=[2000, 45, 700], B=3)
+@pytest.mark.parametrize("mode", [2, 5], ids=["int2", "inline"])
+def test_decode_repeatable_and_split_invariant(mode):
+    """The inline layout numbers its pairs head-major, so its cut pairs and
+    merges follow another order than the planes layouts'."""
+    spec = synth.small_spec(name=f"splits-m{mode}", cfg=463, mode=mode, rotate=True, lens=[2000, 45, 700], B=3)
+    print(f"[case] decode {spec.name}", flush=True)
     case, d, planes = gh.build(spec)
     outs = []
     # workgroup counts: one share per pair or fewer, shares cutting pairs at
@@ -215,7 +219,7 @@ def _many_pair_lens(seed, n):
     return [0 if k < 0.1 else int(r.integers(1, 201)) if k < 0.8 else int(r.integers(2000, 3001)) for k in kind]
 
 
-@pytest.mark.parametrize("mode,bs", [(1, 16), (0, 64), (2, 64)])
+@pytest.mark.parametrize("mode,bs", [(1, 16), (0, 64), (2, 64), (5, 16)])
 def test_decode_many_pairs_chunks_and_batches(mode, bs):
     """1200 pairs (several prefix chunks), shares holding hundreds of
     segments (many segment batches, some cut short by the block-id table),
