@@ -320,8 +320,10 @@ kvq_status check_prefill_sizes(const kvq_cache_desc* desc, int num_seqs, int num
   if (max_q_len < 0) return fail(KVQ_EINVAL, "max_q_len %d < 0", max_q_len);
   if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len %d < 0", max_seq_len);
   const int tq = 128 / group;
-  const long long n_work = (((long long)max_q_len + tq - 1) / tq) * desc->num_kv_heads * (long long)num_seqs;
-  if (n_work > 0x7fffff00LL) return fail(KVQ_EUNSUPPORTED, "prefill grid of %lld workgroups", n_work);
+  // the launch pads the (sequence, kv head) groups to a multiple of 8
+  const long long n_grid = (((long long)max_q_len + tq - 1) / tq) *
+                           (((long long)desc->num_kv_heads * num_seqs + 7) / 8 * 8);
+  if (n_grid > 0x7fffff00LL) return fail(KVQ_EUNSUPPORTED, "prefill grid of %lld workgroups", n_grid);
   return KVQ_OK;
 }
 

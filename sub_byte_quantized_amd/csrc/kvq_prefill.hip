@@ -507,16 +507,46 @@ void prefill_kernel(PrefillParams p) {
   using Gp = PGeo<MODE, D>;
   __shared__ PSmem<MODE, D> sm;
 
-  // ---- work item: consecutive items (the query tiles of one (sequence, kv
-  // head)) land on one XCD, whose L2 then serves their shared key tiles
-  const int nb = gridDim.x;                       // a multiple of 8
-  const int bid = blockIdx.x;
-  const int w_item = (bid & 7) * (nb >> 3) + (bid >> 3);
-  if (w_item >= p.n_work) return;
-  const int qt = w_item % p.n_qtiles;
-  const int hb = w_item / p.n_qtiles;
-  const int h = hb % p.hkv;
-  const int b = hb / p.hkv;
+  // ---- work item: (sequence, kv head) group and query tile.  The query
+  // tiles of a group run on one XCD, whose L2 then serves their shared key
+  // tiles; groups go to the XCDs round-robin, and on each XCD in group order
+  // (workgroups reach the XCDs round-robin in blockIdx order, grid.x = 8
+  // groups-per-XCD query-tile counts).  Groups are numbered heads without a
+  // window first: their key walks are the long ones, so every XCD starts its
+  // long items first and the short (windowed) ones fill in behind them.
+  int b, h, qt;
+  {
+    const int nqt = p.n_qtiles;
+    const int ng = p.n_work / nqt;                  // Hkv * num_seqs
+    const int bid = blockIdx.x;
+    const int k = bid >> 3;
+    const int lg = k / nqt;
+    qt = k - lg * nqt;
+    const int g = lg * 8 + (bid & 7);
+    if (g >= ng) return;
+    const int hkv = p.hkv, nseq = ng / hkv;
+    int nf = hkv;                                   // heads without a window
+    if (p.window) {
+      nf = 0;
+      for (int i = 0; i < hkv; ++i) nf += p.window[i] <= 0 ? 1 : 0;
+    }
+    // group g: the j-th head of its class, sequence b
+    const bool full = g < nf * nseq;
+    const int nc = full ? nf : hkv - nf;
+    const int gc = full ? g : g - nf * nseq;
+    b = gc / nc;
+    const int j = gc - b * nc;
+    h = j;
+    if (p.window) {
+      int seen = 0;
+      for (int i = 0; i < hkv; ++i) {
+        if ((p.window[i] <= 0) == full) {
+          if (seen == j) h = i;
+          ++seen;
+        }
+      }
+    }
+  }
 
   const int q0 = p.cu_q[b];
   const int nq = p.cu_q[b + 1] - q0;
@@ -762,7 +792,8 @@ void prefill_kernel(PrefillParams p) {
 
 template <int MODE, int D, bool ROT>
 hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
-  const int grid = (p.n_work + 7) / 8 * 8;
+  const int ng = p.n_work / p.n_qtiles;                // (sequence, kv head) groups
+  const int grid = (ng + 7) / 8 * 8 * p.n_qtiles;      // bounded on the host
   hipLaunchKernelGGL((prefill_kernel<MODE, D, ROT>), dim3(grid), dim3(64 * kPWaves), 0, s, p);
   return hipGetLastError();
 }
