@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
 // H c is exact in int32 (|.| <= 128 * 127) on v_mfma_i32_16x16x64_i8 with
 // A = diag(d) H (entries +-1, in LDS, built once per workgroup) and B = the
 // row's codes as int8, so each output is one conversion and one product
-// (plus the zero point in column 0) instead of seven butterfly stages.
+// (plus the zero point in column 0) instead of log2 D butterfly stages.
 //
 // Work split: a block is 16 rows of one sequence in (K/V, position, kv
 // head) order, which are 16 consecutive output rows; a wave takes NB blocks.
