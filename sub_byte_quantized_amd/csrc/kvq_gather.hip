@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
   const int lr = lane & (LPR - 1);
   const int hkv = p.hkv;
   const int c0 = p.cu[b];
-  const int n = min(p.cu[b + 1] - c0, p.max_blocks << p.block_size_log2);
+  // positions at or past max_seq_len (which sizes the grid) are not written
+  const int n = min(min(p.cu[b + 1] - c0, p.max_blocks << p.block_size_log2), p.max_seq_len);
   // row, table and output indices stay below 2^31 (checked on the host), so
   // the index math is 32-bit and each address one 32 x 32 -> 64-bit product
   const int rows = n * hkv * 2;
@@ -267,7 +268,8 @@ __global__ __launch_bounds__(256) void gather_rot_kernel(GatherParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hkv = p.hkv;
   const int c0 = p.cu[b];
-  const int n = min(p.cu[b + 1] - c0, p.max_blocks << p.block_size_log2);
+  // positions at or past max_seq_len (which sizes the grid) are not written
+  const int n = min(min(p.cu[b + 1] - c0, p.max_blocks << p.block_size_log2), p.max_seq_len);
   const int nh = n * hkv;                                 // rows of one of K, V (< 2^30, checked on the host)
   const int rows = 2 * nh;
   const int wbase = (blockIdx.x * 4 + wave) * 16 * NB;

@@ -126,6 +126,32 @@ def test_gather_total_tokens_bounds_rows():
     check_gather(vb[:total].cpu().numpy(), Vr[:total], spec.D, False, "bounded V")
 
 
+@pytest.mark.parametrize("idx", [2, 3], ids=["streaming", "rotated"])
+def test_gather_positions_past_max_seq_len_untouched(idx):
+    """max_seq_len below some sequences' n_b: their positions at or past it
+    keep the outputs' sentinel (the grid covers max_seq_len positions), the
+    others are the oracle's rows; both gather kernels."""
+    spec = SPECS[idx]
+    print(f"[case] gather max_seq_len cap {spec.name}", flush=True)
+    case, d, planes = gh.build(spec)
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device=gh.dev())
+    total, cap = int(lens.sum()), 200
+    assert lens.max() > cap
+    kb = torch.full((total, spec.Hkv, spec.D), 7.0, device=gh.dev())
+    vb = torch.full((total, spec.Hkv, spec.D), 7.0, device=gh.dev())
+    kvq.kvq_gather_dequant(d, *planes, cu, cap, total, block_tables=case.block_tables,
+                           key_out=kb, value_out=vb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Kr, Vr = oracle_gather(spec, case, gh.host_planes(planes), cu)
+    pos = np.concatenate([np.arange(n) for n in lens])
+    keep = pos < cap
+    K, V = kb.cpu().numpy(), vb.cpu().numpy()
+    assert np.all(K[~keep] == 7.0) and np.all(V[~keep] == 7.0)
+    check_gather(K[keep], Kr[keep], spec.D, False, "capped K")
+    check_gather(V[keep], Vr[keep], spec.D, False, "capped V")
+
+
 def test_gather_repeatable():
     spec = SPECS[9]
     case, d, planes = gh.build(spec)
